@@ -1,0 +1,204 @@
+"""Seeded synthetic inputs: model configurations, parameter sets and token streams.
+
+This module is the only code shared by the HIP path's callers and the oracle's
+callers. It holds sizes, parameter names/shapes, random draws and bf16 rounding
+of the drawn values; it holds none of the method's arithmetic (no norm, no
+projection, no attention, no merge).
+
+Parameter names and shapes follow the method's modules as the pages name them
+(greeksharifa summary page "Recurrent Looped Transformer 요약 설명", §2.1-§2.7
+and appendix A.1; jiphyeonjeon review page "Recurrent Looped Transformer",
+§2-§3, eq 2.1-2.2 and eq 2.9-2.11):
+
+  emb                    [V, d]        token embedding (encoder input)
+  enc.{l}.n1 / n2        [d]           pre-norm gains of encoder block l
+  enc.{l}.wq/wk/wv       [H*dh, d]     encoder self-attention projections
+  enc.{l}.wo             [d, H*dh]
+  enc.{l}.w1 / w3        [f, d]        SwiGLU gate / up projections
+  enc.{l}.w2             [d, f]        SwiGLU down projection
+  mem.nE                 [d]           RMSNorm_E gain (memory norm)
+  mem.{g}.wk / wv        [H*dh, d]     memory-group key / value projections
+  merge.ns               [d]           RMSNorm_s gain
+  merge.wg               [d, 2d]       gate weight over [e_t ; r_{t-1}]
+  merge.bg               [d]           gate bias
+  merge.ws               [d, d]        state projection
+  merge.s0               [d]           learned initial output s*
+  dec.{l}.m1 / m2 / m3   [d]           pre-norm gains (SWA, cross, FFN)
+  dec.{l}.wq/wk/wv/wo                  decoder SWA projections (absent when shared)
+  dec.{l}.xq             [H*dh, d]     cross-attention query projection
+  dec.{l}.xo             [d, H*dh]     cross-attention output projection
+  dec.{l}.w1 / w3 / w2                 decoder SwiGLU (absent when shared)
+  out.nO                 [d]           final norm gain
+  out.w                  [V, d]        readout
+
+Every matrix is [out_features, in_features].
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+V0, V1, V2 = 0, 1, 2  # RLT-0 (no feedback), RLT-1 (every token), RLT-2 (chunked)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    vocab: int
+    d: int
+    n_heads: int
+    d_head: int
+    L_E: int
+    L_D: int
+    ffn: int
+    window: int
+    groups: int
+    variant: int = V1
+    chunk: int = 1
+    share: bool = False
+    dtype: str = "bf16"          # "fp32" or "bf16" (storage of matrices, K/V, memory)
+    alpha: float = 0.1
+    rms_eps: float = 1e-6
+    rope_base: float = 10000.0
+    batch: int = 1
+    seq_len: int = 1             # tokens per sequence, BOS included
+    gen_len: int = 0             # extra tokens consumed one at a time after the prompt
+    token_dist: str = "uniform"  # "uniform" | "binary" | "zipf"
+    weight_seed: int = 0
+    token_seed: int = 0
+
+    @property
+    def bos(self) -> int:
+        return self.vocab - 1
+
+    @property
+    def hd(self) -> int:
+        return self.n_heads * self.d_head
+
+    def replace(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads (sizes as stated for each shape; f = 4d for the tiny shape).
+CONFIGS: Dict[str, Config] = {
+    "tiny_fp32": Config(name="tiny_fp32", vocab=32, d=64, n_heads=4, d_head=16, L_E=2, L_D=2,
+                        ffn=256, window=4, groups=1, variant=V1, dtype="fp32",
+                        batch=2, seq_len=16, token_dist="uniform", weight_seed=101, token_seed=201),
+    "algo_bf16": Config(name="algo_bf16", vocab=8, d=512, n_heads=8, d_head=64, L_E=4, L_D=4,
+                        ffn=2048, window=32, groups=1, variant=V1, dtype="bf16",
+                        batch=64, seq_len=257, token_dist="binary", weight_seed=102, token_seed=202),
+    "rlt2_bf16": Config(name="rlt2_bf16", vocab=8, d=512, n_heads=8, d_head=64, L_E=6, L_D=2,
+                        ffn=2048, window=32, groups=2, variant=V2, chunk=4, dtype="bf16",
+                        batch=128, seq_len=64, token_dist="uniform", weight_seed=103, token_seed=203),
+    "medium_lm": Config(name="medium_lm", vocab=32000, d=2048, n_heads=16, d_head=128, L_E=24, L_D=24,
+                        ffn=5632, window=512, groups=1, variant=V1, dtype="bf16",
+                        batch=32, seq_len=2048, gen_len=256, token_dist="zipf",
+                        weight_seed=104, token_seed=204),
+    "paper_shared": Config(name="paper_shared", vocab=32000, d=4096, n_heads=32, d_head=128, L_E=48,
+                           L_D=48, ffn=11008, window=1024, groups=1, variant=V1, share=True,
+                           dtype="bf16", batch=64, seq_len=8192, gen_len=512, token_dist="zipf",
+                           weight_seed=105, token_seed=205),
+}
+
+
+def manifest(cfg: Config) -> List[Tuple[str, Tuple[int, ...]]]:
+    """Parameter names and shapes in manifest order."""
+    d, hd, f, V = cfg.d, cfg.hd, cfg.ffn, cfg.vocab
+    out: List[Tuple[str, Tuple[int, ...]]] = [("emb", (V, d))]
+    for l in range(cfg.L_E):
+        out += [(f"enc.{l}.n1", (d,)), (f"enc.{l}.wq", (hd, d)), (f"enc.{l}.wk", (hd, d)),
+                (f"enc.{l}.wv", (hd, d)), (f"enc.{l}.wo", (d, hd)), (f"enc.{l}.n2", (d,)),
+                (f"enc.{l}.w1", (f, d)), (f"enc.{l}.w3", (f, d)), (f"enc.{l}.w2", (d, f))]
+    if cfg.L_D > 0:
+        out.append(("mem.nE", (d,)))
+        for g in range(cfg.groups):
+            out += [(f"mem.{g}.wk", (hd, d)), (f"mem.{g}.wv", (hd, d))]
+    if cfg.variant != V0:
+        out += [("merge.ns", (d,)), ("merge.wg", (d, 2 * d)), ("merge.bg", (d,)),
+                ("merge.ws", (d, d)), ("merge.s0", (d,))]
+    for l in range(cfg.L_D):
+        out.append((f"dec.{l}.m1", (d,)))
+        if not cfg.share:
+            out += [(f"dec.{l}.wq", (hd, d)), (f"dec.{l}.wk", (hd, d)), (f"dec.{l}.wv", (hd, d)),
+                    (f"dec.{l}.wo", (d, hd))]
+        out += [(f"dec.{l}.m2", (d,)), (f"dec.{l}.xq", (hd, d)), (f"dec.{l}.xo", (d, hd)),
+                (f"dec.{l}.m3", (d,))]
+        if not cfg.share:
+            out += [(f"dec.{l}.w1", (f, d)), (f"dec.{l}.w3", (f, d)), (f"dec.{l}.w2", (d, f))]
+    out += [("out.nO", (d,)), ("out.w", (V, d))]
+    return out
+
+
+def n_params(cfg: Config) -> int:
+    return int(sum(int(np.prod(s)) for _, s in manifest(cfg)))
+
+
+def is_gain(name: str) -> bool:
+    last = name.rsplit(".", 1)[-1]
+    return last in ("n1", "n2", "nE", "ns", "m1", "m2", "m3", "nO")
+
+
+def is_matrix(name: str, shape: Tuple[int, ...]) -> bool:
+    return len(shape) == 2
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = (rounded & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    nan = np.isnan(a)
+    if nan.any():
+        out = out.copy()
+        out[nan] = np.nan
+    return out.reshape(a.shape)
+
+
+def make_params(cfg: Config, seed: int | None = None, std: float = 0.02) -> Dict[str, np.ndarray]:
+    """Draw a parameter set in manifest order from numpy PCG64.
+
+    Matrices, embedding and gate bias ~ N(0, std); norm gains 1 + N(0, std);
+    s* ~ N(0, 1). For bf16 workloads the matrices are rounded to bf16 values
+    (vectors stay float32); both sides consume these same values.
+    """
+    rng = np.random.Generator(np.random.PCG64(cfg.weight_seed if seed is None else seed))
+    params: Dict[str, np.ndarray] = {}
+    for name, shape in manifest(cfg):
+        if name == "merge.s0":
+            a = rng.standard_normal(shape, dtype=np.float32)
+        elif is_gain(name):
+            a = (1.0 + std * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+        else:
+            a = (std * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+        if cfg.dtype == "bf16" and is_matrix(name, shape):
+            a = round_bf16(a)
+        params[name] = a
+    return params
+
+
+def zipf_ids(rng: np.random.Generator, n_ranks: int, s: float, size) -> np.ndarray:
+    """Ids whose rank k (1-based) has probability proportional to k^-s; id = k - 1."""
+    k = np.arange(1, n_ranks + 1, dtype=np.float64)
+    cdf = np.cumsum(k ** (-s))
+    cdf /= cdf[-1]
+    u = rng.random(size)
+    return np.minimum(np.searchsorted(cdf, u, side="right"), n_ranks - 1).astype(np.int32)
+
+
+def make_tokens(cfg: Config, batch: int | None = None, length: int | None = None,
+                seed: int | None = None) -> np.ndarray:
+    """int32 [B, T] token ids; position 1 is BOS (= V-1), the rest follow cfg.token_dist."""
+    B = cfg.batch if batch is None else batch
+    T = (cfg.seq_len + cfg.gen_len) if length is None else length
+    rng = np.random.Generator(np.random.PCG64(cfg.token_seed if seed is None else seed))
+    if cfg.token_dist == "binary":
+        body = rng.integers(0, 2, size=(B, T - 1), dtype=np.int32)
+    elif cfg.token_dist == "zipf":
+        body = zipf_ids(rng, cfg.vocab - 1, 1.1, (B, T - 1))
+    else:
+        body = rng.integers(0, cfg.vocab, size=(B, T - 1), dtype=np.int32)
+    bos = np.full((B, 1), cfg.bos, dtype=np.int32)
+    return np.ascontiguousarray(np.concatenate([bos, body], axis=1).astype(np.int32))
