@@ -1,0 +1,185 @@
+/*
+ * rlt.h - C ABI of the Recurrent Looped Transformer transition library (MI355X / gfx950).
+ *
+ * The library computes the method's forward pass on one GPU: the token-parallel
+ * causal encoder and its memory projection, the per-token decoder transition
+ * u_t = Merge(e_t, s_{t-1}), H_t = D_phi(u_t; M_<=t, C^D_{t-1}, t) batched over
+ * independent sequences, the RLT-2 chunked-feedback and RLT-0 variants, and the
+ * readout.  Sources (web pages about the method):
+ *   [S] greeksharifa.github.io, "Recurrent Looped Transformer 요약 설명":
+ *       §2.1-§2.7 (state, encoder/memory, transition, prefill/decoding, merge,
+ *       blocks, RLT-0/1/2), appendix A.1 (sharing), E (multi-turn), F
+ *       (execution procedures F.1 prefill, F.2 generation, F.4 replay), I (RLT-2).
+ *   [R] jiphyeonjeon.kr/blog/rlt, "Recurrent Looped Transformer":
+ *       §2 eq 2.1-2.2 (memory), §3.1 eq 2.7 (composition), §3.2 (E^step),
+ *       §3.3 eq 2.9-2.16 (merge, blocks, window), §4.2 eq 3.3 (storage),
+ *       §6.2 eq 5.5 (replay log-probabilities), §6.4-6.5 (stale caches, replay).
+ *
+ * Conventions
+ *  - Every function returns an rlt_status (0 = RLT_OK). No C++ exception crosses
+ *    the boundary. rlt_last_error() returns a thread-local message for the last
+ *    failure in the calling thread.
+ *  - Pointers marked "device" are HIP device memory on the model's device; the
+ *    caller owns them. The library owns the packed weights and all state
+ *    buffers (decoder state, rings, memory, encoder cache, workspaces).
+ *  - Calls enqueue work on the given stream and return without synchronising,
+ *    except rlt_create / rlt_update_weights / rlt_state_create, which
+ *    synchronise the stream before returning.
+ *  - Host-side validation (shapes, capacity, configuration, staleness) runs
+ *    before any launch; on error nothing is enqueued and the state is unchanged.
+ *  - Token ids must lie in [0, vocab); other ids are undefined behaviour.
+ *  - Batches are rectangular: every row of a state is at the same position.
+ *  - Positions are 1-based; position 1 holds BOS. Chunks of RLT-2 are anchored
+ *    at position 1 ([S] appendix I.1).
+ *  - A state is bound to the model that created it; it is stale after
+ *    rlt_update_weights until rlt_state_reset ([R] §6.4: caches computed with
+ *    old parameters are not current-policy values).
+ */
+#ifndef RLT_H
+#define RLT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RLT_OK = 0,
+  RLT_ERR_INVALID_ARG = -1,   /* null pointer, bad size, inconsistent config, unknown weight name */
+  RLT_ERR_UNSUPPORTED = -2,   /* a form the pages do not define (e.g. G not in {1, L_D}) or not built */
+  RLT_ERR_OOM = -3,           /* device allocation failed */
+  RLT_ERR_CAPACITY = -4,      /* positions would exceed the state's max_len */
+  RLT_ERR_STALE_STATE = -5,   /* state built under older weights; reset it */
+  RLT_ERR_HIP = -6,           /* a HIP runtime call failed */
+  RLT_ERR_ORDER = -7          /* decoder asked to consume positions not yet encoded */
+} rlt_status;
+
+typedef enum { RLT_FP32 = 0, RLT_BF16 = 1 } rlt_dtype;
+typedef enum { RLT_V0 = 0, RLT_V1 = 1, RLT_V2 = 2 } rlt_variant;
+
+/* Model configuration ([S] §2.1-§2.7, §3.1; [R] §2-§3). Plain old data. */
+typedef struct {
+  int vocab;          /* V */
+  int d;              /* residual width d (encoder output and recurrent output) */
+  int n_heads;        /* H: heads of every attention (encoder, SWA, cross) */
+  int d_head;         /* dh (even) */
+  int L_E;            /* encoder blocks */
+  int L_D;            /* decoder blocks (0 allowed: the model is the gated recurrence) */
+  int ffn;            /* SwiGLU hidden width f */
+  int window;         /* SWA window W >= 1, counting the current token */
+  int groups;         /* memory groups G: 1 (shared) or L_D (one per decoder layer) */
+  rlt_variant variant;/* RLT-0 (no feedback), RLT-1 (every token), RLT-2 (chunked) */
+  int chunk;          /* RLT-2 feedback interval K_c >= 1 (must be 1 unless RLT-2) */
+  int share_enc_dec;  /* 1: decoder SWA Q/K/V/O and FFN alias encoder layer l ([S] appendix A.1); needs L_E == L_D */
+  rlt_dtype dtype;    /* storage of matrices, GEMM inputs, K/V, rings and memory; accumulation,
+                         residual stream, s, norms, softmax and logits are fp32 */
+  float alpha;        /* feedback scale (0.1 in the pages' experiments) */
+  float rms_eps;      /* RMSNorm epsilon (1e-6) */
+  float rope_base;    /* rotary base (10000) */
+} rlt_config;
+
+/* One parameter tensor: fp32 values, row-major, in DEVICE memory, named as in the
+ * manifest (emb, enc.{l}.{n1,wq,wk,wv,wo,n2,w1,w3,w2}, mem.nE, mem.{g}.{wk,wv},
+ * merge.{ns,wg,bg,ws,s0}, dec.{l}.{m1,wq,wk,wv,wo,m2,xq,xo,m3,w1,w3,w2}, out.{nO,w});
+ * matrices are [out_features, in_features]; merge.wg is [d, 2d] over [e_t ; r].
+ * numel must match the configuration's shape for that name. */
+typedef struct {
+  const char* name;
+  const float* data;
+  int64_t numel;
+} rlt_tensor;
+
+typedef struct rlt_model rlt_model;
+typedef struct rlt_state rlt_state;
+
+/* Validate cfg, allocate library-owned packed weights on the current device and
+ * copy/convert the given tensors into them (the caller may free its tensors once
+ * this returns). Every manifest name for cfg must be present exactly once.
+ * Errors: INVALID_ARG (bad config / missing or mis-sized tensor), UNSUPPORTED
+ * (G not in {1, L_D}, d_head odd, share with L_E != L_D), OOM, HIP. */
+int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights,
+               hipStream_t stream, rlt_model** out);
+
+/* Replace the parameter values (same names and sizes as rlt_create). Every state
+ * created before becomes stale ([R] §6.4) until rlt_state_reset. */
+int rlt_update_weights(rlt_model* m, const rlt_tensor* weights, int n_weights, hipStream_t stream);
+
+/* Free the model. States of this model must be destroyed first. */
+int rlt_destroy(rlt_model* m);
+
+/* Allocate a batch state for `batch` sequences of up to `max_len` positions: the
+ * recurrent output s (and RLT-2 register), the per-layer SWA rings C^D, the
+ * encoder memory M^g_<=t, the encoder outputs, and (keep_encoder_cache != 0) the
+ * per-layer encoder cache C^E needed to encode further tokens after the first
+ * encode call (generation, multi-turn appends; [S] §2.4, appendix E). The state
+ * starts at H_0 = (s*, empty) ([R] §3.1). Errors: INVALID_ARG, OOM, HIP. */
+int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cache,
+                     hipStream_t stream, rlt_state** out);
+
+/* H_0 = (s*, empty caches), positions reset to 0; clears staleness. */
+int rlt_state_reset(rlt_model* m, rlt_state* s, hipStream_t stream);
+
+int rlt_state_destroy(rlt_state* s);
+
+/* Bytes of device memory held by the state, split as in [R] §4.2 eq 3.3:
+ * out[0] encoder cache C^E, out[1] memory M, out[2] decoder rings C^D,
+ * out[3] recurrent output and register, out[4] encoder outputs / gate inputs,
+ * out[5] workspaces. Any pointer may be null. */
+int rlt_state_bytes(const rlt_state* s, int64_t out[6]);
+
+/* Positions encoded so far and positions consumed by the decoder. */
+int rlt_state_positions(const rlt_state* s, int* n_encoded, int* n_decoded);
+
+/* Token-parallel causal encoding of positions n_enc+1 .. n_enc+T for every row
+ * ([S] §2.2, §2.4, appendix F.1): e_t, the memory entries of every group
+ * (k^g_t = RoPE_t(W^g_K RMSNorm_E(e_t)), v^g_t = W^g_V RMSNorm_E(e_t), [R] eq 2.1-2.2),
+ * and C^E when kept. Does not advance the decoder.
+ * tokens: device int32 [B, T] row-major. Errors: CAPACITY (n_enc + T > max_len),
+ * UNSUPPORTED (n_enc > 0 without an encoder cache), STALE_STATE, INVALID_ARG. */
+int rlt_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t stream);
+
+/* Consume the next T encoded positions in order, one transition each
+ * ([S] §2.3-§2.7; [R] §3.1 eq 2.7, §3.3 eq 2.9-2.16). RLT-2 runs each chunk's
+ * positions together inside every layer; RLT-0 runs positions in parallel.
+ * Outputs (device, each nullable):
+ *   logits       fp32 [B, T, V]   logits_t = W_out RMSNorm_out(s_t), predicting x_{t+1}
+ *   next_logprob fp32 [B, T]      log softmax(logits_t)[next_tokens[b, t]] ([R] eq 5.5)
+ *   next_tokens  int32 [B, T]     required when next_logprob is given; an entry < 0 writes 0
+ *   s_out        fp32 [B, T, d]   s_t
+ * Errors: ORDER (n_dec + T > n_enc), STALE_STATE, INVALID_ARG. */
+int rlt_decode_scan(rlt_model* m, rlt_state* s, int T, float* logits, float* next_logprob,
+                    const int32_t* next_tokens, float* s_out, hipStream_t stream);
+
+/* Generation step F.2 ([S] §2.4, appendix F.2; [R] §3.2): consume x_t for every row
+ * (encoder step with C^E, memory append, one transition) and write the fp32 logits
+ * [B, V] that predict x_{t+1}. tokens: device int32 [B]. Needs keep_encoder_cache
+ * unless the state is at position 0. Errors as rlt_encode. */
+int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, hipStream_t stream);
+
+/* Current-policy replay F.4 ([R] §6.2 eq 5.5, §6.5; [S] §2.8): from a fresh H_0 with
+ * the current weights, encode tokens [B, T] (x_1 = BOS), rebuild s_t, every SWA
+ * ring and the memory, and write logprob[b, t-1] = log p(x_{t+1} | x_<=t) for
+ * t = 1..T-1 (fp32 [B, T-1], device). s_out (nullable) receives s_t fp32 [B, T, d].
+ * `state` must have batch B and max_len >= T; it is reset first and holds H_T after. */
+int rlt_replay(rlt_model* m, rlt_state* state, const int32_t* tokens, int T, float* logprob,
+               float* s_out, hipStream_t stream);
+
+/* Scan driver for the decoder transitions: 0 = automatic, 1 = one launch sequence
+ * per position (stream-ordered), 2 = persistent cooperative kernel over all
+ * positions (configurations it supports). */
+int rlt_set_scan_mode(rlt_model* m, int mode);
+
+/* Number of dependent decoder block passes issued since the state was reset
+ * (T*L_D for RLT-1, ceil(T/K_c)*L_D for RLT-2 chunks, L_D per parallel RLT-0 pass;
+ * [S] §2.7, Table 1). */
+int rlt_state_block_steps(const rlt_state* s, int64_t* out);
+
+const char* rlt_status_string(int status);
+const char* rlt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLT_H */

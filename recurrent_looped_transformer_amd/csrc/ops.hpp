@@ -1,0 +1,104 @@
+// Host-side launch interface of the device operations. Each launcher enqueues
+// one kernel on `st`; shapes are validated by the caller (rlt_api.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlt {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// Row m of a logical [rows, width] matrix lives at  base + (m / tn) * sb + (m % tn) * st
+// (elements). Covers contiguous buffers (tn = rows) and [B][Tmax][d] position slices.
+struct RowMap {
+  int64_t sb = 0, st = 0;
+  int tn = 1;
+  __host__ __device__ int64_t off(int m) const { return (int64_t)(m / tn) * sb + (int64_t)(m % tn) * st; }
+};
+inline RowMap contiguous(int width) { RowMap r; r.tn = 1; r.sb = width; r.st = 0; return r; }
+
+// Destination of keys/values: [B][H][cap][dh] blocks starting at k / v.
+// Position p (1-based) of sequence b goes to slot (p - 1) % cap when ring != 0, else p - 1.
+struct KVDst {
+  void* k = nullptr;
+  void* v = nullptr;
+  int cap = 0;
+  int ring = 0;
+};
+
+enum class Ep : int {
+  StoreAct = 0,   // out[m*ldo + n] = act(acc)
+  StoreF32,       // outf[m*ldo + n] = acc
+  Residual,       // resid[rmap(m) + n] += acc
+  SwiGLU,         // rows (2j, 2j+1) = (W1 x, W3 x): out[m*ldo + j] = act(silu(a) * b)
+  QKV,            // n < hd: q = rope(acc) -> out; hd <= n < 2hd: k = rope -> kv.k; else v -> kv.v
+  RopeQ,          // out[m*ldo + n] = act(rope(acc))      (cross-attention query)
+  MemKV,          // n < hd: k = rope -> kv.k; else v -> kv.v
+  Merge,          // rows (2n, 2n+1) = (W_g,r r, W_s r): u = e + alpha*sigmoid(gpre + a)*b -> z
+  Bias,           // outf[rmap(m) + n] = acc + bias[n]    (gate pre-activation W_g,e e + b_g)
+};
+
+struct EpArgs {
+  void* out = nullptr;        // activation output (act type) or fp32 output for StoreF32
+  int64_t ldo = 0;
+  float* resid = nullptr;     // Residual: fp32 rows via rmap; Bias: fp32 out via rmap; Merge: z rows
+  RowMap rmap;
+  const float2* rope = nullptr;  // [pos][dh/2] (cos, sin), pos 0-based index = position
+  int H = 0, dh = 0, hd = 0;
+  int tn = 1;                 // rows per sequence in this GEMM: m -> b = m / tn, i = m % tn
+  int pos0 = 0;               // position of i = 0 is pos0 + 1
+  int b0 = 0;                 // sequence offset of row b = 0 inside the state
+  KVDst kv;
+  // Merge: e and gpre rows of (b, i) at rmap-like offsets eb * b + et * i; nrep outputs per row
+  const float* e = nullptr;
+  const float* gpre = nullptr;
+  int64_t eb = 0, et = 0;
+  int nrep = 1;
+  float alpha = 0.f;
+  const float* bias = nullptr;
+};
+
+// GEMM: Y[m, n] = sum_k X[m, k] * W[n, k]  (X act rows with leading dim ldx; W packed [N, K]),
+// Y consumed by the epilogue. bf16: MFMA; fp32: vector FMA.
+void gemm(Dt dt, Ep ep, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
+          hipStream_t st);
+
+// out[m, :] = act(rms(x[rmap(m), :]) * gain)  (gain may be null: plain cast)
+void rmsnorm(Dt dt, const float* x, RowMap xm, const float* gain, void* out, int64_t ldo, int rows, int d,
+             float eps, hipStream_t st);
+// h[rmap(m), :] = emb[tok[m], :]  (fp32 out)
+void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int rows, int d, hipStream_t st);
+// rope table [npos][dh/2] (cos, sin) of angle p * base^(-2i/dh), evaluated in double precision
+void rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
+// dst[rmap_d(m), :] = src[rmap_s(m), :] (fp32 rows)
+void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int d, hipStream_t st);
+// s[b, :] = s0 (fp32) for b < B; used for H_0 and the RLT-2 register
+void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st);
+// out[om(r)] = L[tok[tm(r)]] - logsumexp(L) with L = logits row lm(r); tok < 0 writes 0
+void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows,
+             int V, hipStream_t st);
+// pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind
+enum class Pack : int { Plain = 0, RopeRows, Interleave2 };
+void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* dst, int64_t dst_ld,
+                 int64_t dst_col0, int rows, int cols, Pack kind, int dh, int row_stride, int row_off,
+                 hipStream_t st);
+
+// Attention of nq query rows per (sequence, head) over a position range of a key/value store.
+struct AttnArgs {
+  const void* q = nullptr;      // act [B*nq][H*dh] (roped, pairs interleaved like the keys)
+  int64_t ldq = 0;
+  const void* k = nullptr;      // [B][H][cap][dh] starting at b = 0 of this call
+  const void* v = nullptr;
+  int64_t kv_bstride = 0;       // elements between sequences
+  int cap = 0;
+  int ring = 0;                 // slot(p) = (p-1) % cap if ring else p-1
+  void* out = nullptr;          // act [B*nq][H*dh]
+  int64_t ldo = 0;
+  int B = 0, nq = 1, H = 0, dh = 0;
+  int pos0 = 0;                 // query i sits at position pos0 + 1 + i
+  int window = 0;               // >0: keys max(1, p-window+1)..p ; 0: keys 1..p
+  float scale = 1.f;
+};
+void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
+
+}  // namespace rlt

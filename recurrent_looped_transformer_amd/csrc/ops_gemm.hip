@@ -1,0 +1,280 @@
+// GEMM kernels with fused epilogues.
+//
+// Y[m, n] = sum_k X[m, k] W[n, k] with W the packed weight [N, K] (K contiguous)
+// and X activations [M, K]. The weight is the MFMA "A" operand, so each lane of a
+// 16x16 output tile holds four consecutive output features n..n+3 of one row m:
+// row pairs packed next to each other (rotary pairs, SwiGLU W1/W3 rows, merge
+// gate/state rows) meet in one lane and the epilogue needs no shuffles.
+//
+//  - gemm_skinny_bf16: decode shapes (M = batch rows <= a few hundred). One
+//    workgroup streams 16 weight rows once for up to 64 activation rows; the four
+//    waves split K and reduce through LDS. Bandwidth-bound on the weights.
+//  - gemm_tiled_bf16: prefill shapes. 128x128 tiles, K step 32, LDS double
+//    buffer, 4 waves x (64x64) of 16x16x32 MFMAs.
+//  - gemm_f32: the fp32 configuration (vector FMA).
+#include "common.hpp"
+#include "ops.hpp"
+
+namespace rlt {
+
+template <typename T>
+__device__ __forceinline__ void rope_pair(const EpArgs& a, int pos, int c, float& x0, float& x1) {
+  const float2 cs = a.rope[(int64_t)pos * (a.dh >> 1) + (c >> 1)];
+  const float y0 = x0 * cs.x - x1 * cs.y;
+  const float y1 = x0 * cs.y + x1 * cs.x;
+  x0 = y0;
+  x1 = y1;
+}
+
+// kv slot address (elements) of (sequence b, head h, position pos, channel c)
+__device__ __forceinline__ int64_t kv_off(const EpArgs& a, int b, int h, int pos, int c) {
+  const int slot = a.kv.ring ? (pos - 1) % a.kv.cap : pos - 1;
+  return (((int64_t)(a.b0 + b) * a.H + h) * a.kv.cap + slot) * a.dh + c;
+}
+
+template <typename T, Ep E>
+__device__ __forceinline__ void epilogue(const EpArgs& a, int m, int n, float v[4]) {
+  T* out = reinterpret_cast<T*>(a.out);
+  if constexpr (E == Ep::StoreAct) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Elem<T>::st(out + (int64_t)m * a.ldo + n + i, v[i]);
+  } else if constexpr (E == Ep::StoreF32) {
+    float* o = reinterpret_cast<float*>(a.out) + (int64_t)m * a.ldo + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = v[i];
+  } else if constexpr (E == Ep::Residual) {
+    float* r = a.resid + a.rmap.off(m) + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] += v[i];
+  } else if constexpr (E == Ep::Bias) {
+    float* r = a.resid + a.rmap.off(m) + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i] + a.bias[n + i];
+  } else if constexpr (E == Ep::SwiGLU) {
+    T* o = out + (int64_t)m * a.ldo + (n >> 1);
+    Elem<T>::st(o, v[0] * sigmoidf_(v[0]) * v[1]);
+    Elem<T>::st(o + 1, v[2] * sigmoidf_(v[2]) * v[3]);
+  } else if constexpr (E == Ep::RopeQ) {
+    const int pos = a.pos0 + 1 + (m % a.tn);
+    const int c = n % a.dh;
+    rope_pair<T>(a, pos, c, v[0], v[1]);
+    rope_pair<T>(a, pos, c + 2, v[2], v[3]);
+    T* o = out + (int64_t)m * a.ldo + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Elem<T>::st(o + i, v[i]);
+  } else if constexpr (E == Ep::QKV || E == Ep::MemKV) {
+    const int b = m / a.tn, i = m % a.tn;
+    const int pos = a.pos0 + 1 + i;
+    int region = n / a.hd;
+    const int w = n - region * a.hd;
+    if constexpr (E == Ep::MemKV) region += 1;   // memory projection has no query part
+    const int h = w / a.dh, c = w % a.dh;
+    if (region < 2) {
+      rope_pair<T>(a, pos, c, v[0], v[1]);
+      rope_pair<T>(a, pos, c + 2, v[2], v[3]);
+    }
+    T* dst;
+    if (region == 0) dst = out + (int64_t)m * a.ldo + w;
+    else dst = reinterpret_cast<T*>(region == 1 ? a.kv.k : a.kv.v) + kv_off(a, b, h, pos, c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Elem<T>::st(dst + k, v[k]);
+  } else if constexpr (E == Ep::Merge) {
+    // rows (2j, 2j+1) of the packed [W_g,r ; W_s] weight: gate part and state projection of feature j
+    const int j = n >> 1;
+#pragma unroll
+    for (int rep = 0; rep < a.nrep; ++rep) {
+      const int64_t eo = (int64_t)m * a.eb + (int64_t)rep * a.et + j;
+      float* z = a.resid + a.rmap.off(m * a.nrep + rep) + j;
+      z[0] = a.e[eo] + a.alpha * sigmoidf_(a.gpre[eo] + v[0]) * v[1];
+      z[1] = a.e[eo + 1] + a.alpha * sigmoidf_(a.gpre[eo + 1] + v[2]) * v[3];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ skinny (decode)
+template <Ep E>
+__global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ X, int64_t ldx,
+                                                        const bf16_t* __restrict__ W, int M, int N, int K,
+                                                        EpArgs a) {
+  __shared__ f32x4 red[4][4][WAVE];
+  const int n0 = blockIdx.x * 16;
+  const int m0 = blockIdx.y * 64;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  const int nmb = min(4, (M - m0 + 15) / 16);
+  const int nrow = min(n0 + r, N - 1);
+  const bf16_t* wp = W + (int64_t)nrow * K + g * 16;
+  const bf16_t* xp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xp[j] = X + (int64_t)min(m0 + j * 16 + r, M - 1) * ldx + g * 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = K / 64;
+  for (int c = wave; c < nch; c += 4) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(wp + c * 64);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(wp + c * 64 + 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < nmb) {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(xp[j] + c * 64 + 8);
+        acc[j] = mfma16x16x32(a0, b0, acc[j]);
+        acc[j] = mfma16x16x32(a1, b1, acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  const int j = wave;
+  if (j < nmb) {
+    f32x4 s = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
+    const int m = m0 + j * 16 + r;
+    const int n = n0 + 4 * g;
+    if (m < M && n < N) {
+      float v[4] = {s[0], s[1], s[2], s[3]};
+      epilogue<bf16_t, E>(a, m, n, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tiled (prefill)
+constexpr int TB = 128;   // tile rows (both operands)
+constexpr int TK = 32;    // k per stage
+constexpr int TPAD = 5;   // uint4 per LDS row (4 used + 1 pad)
+
+template <Ep E>
+__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ X, int64_t ldx,
+                                                       const bf16_t* __restrict__ W, int M, int N, int K,
+                                                       EpArgs a) {
+  __shared__ uint4 sW[2][TB][TPAD];
+  __shared__ uint4 sX[2][TB][TPAD];
+  const int n0 = blockIdx.x * TB;
+  const int m0 = blockIdx.y * TB;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
+
+  // global load assignment: 2 x 16B of each tile per thread
+  const bf16_t* wsrc[2];
+  const bf16_t* xsrc[2];
+  int lrow[2], lq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + i * 256;
+    lrow[i] = idx >> 2;
+    lq[i] = idx & 3;
+    wsrc[i] = W + (int64_t)min(n0 + lrow[i], N - 1) * K + lq[i] * 8;
+    xsrc[i] = X + (int64_t)min(m0 + lrow[i], M - 1) * ldx + lq[i] * 8;
+  }
+  uint4 rw[2], rx[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0);
+      rx[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sW[buf][lrow[i]][lq[i]] = rw[i];
+      sX[buf][lrow[i]][lq[i]] = rx[i];
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / TK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * TK);
+    uint4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = sW[buf][wn + i * 16 + r][g];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = sX[buf][wm + j * 16 + r][g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wn + i * 16 + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm + j * 16 + r;
+      if (m < M) {
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        epilogue<bf16_t, E>(a, m, n, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+template <Ep E>
+__global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int64_t ldx,
+                                                const float* __restrict__ W, int M, int N, int K, EpArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nq = N / 4;
+  if (idx >= (int64_t)M * nq) return;
+  const int m = (int)(idx / nq);
+  const int n = (int)(idx % nq) * 4;
+  const float* x = X + (int64_t)m * ldx;
+  const float* w0 = W + (int64_t)n * K;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; ++k) {
+    const float xv = x[k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = fmaf(xv, w0[(int64_t)i * K + k], v[i]);
+  }
+  epilogue<float, E>(a, m, n, v);
+}
+
+template <Ep E>
+static void launch(Dt dt, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
+                   hipStream_t st) {
+  if (M <= 0 || N <= 0) return;
+  if (dt == Dt::F32) {
+    const int64_t total = (int64_t)M * (N / 4);
+    const int blocks = (int)((total + 255) / 256);
+    hipLaunchKernelGGL(gemm_f32<E>, dim3(blocks), dim3(256), 0, st, (const float*)X, ldx, (const float*)W, M, N, K,
+                       a);
+  } else if (M <= 512) {
+    hipLaunchKernelGGL(gemm_skinny_bf16<E>, dim3((N + 15) / 16, (M + 63) / 64), dim3(256), 0, st,
+                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
+  } else {
+    hipLaunchKernelGGL(gemm_tiled_bf16<E>, dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st,
+                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
+  }
+}
+
+void gemm(Dt dt, Ep ep, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
+          hipStream_t st) {
+  switch (ep) {
+    case Ep::StoreAct: launch<Ep::StoreAct>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::StoreF32: launch<Ep::StoreF32>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::Residual: launch<Ep::Residual>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::SwiGLU: launch<Ep::SwiGLU>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::QKV: launch<Ep::QKV>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::RopeQ: launch<Ep::RopeQ>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::MemKV: launch<Ep::MemKV>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::Merge: launch<Ep::Merge>(dt, a, X, ldx, W, M, N, K, st); break;
+    case Ep::Bias: launch<Ep::Bias>(dt, a, X, ldx, W, M, N, K, st); break;
+  }
+}
+
+}  // namespace rlt

@@ -1,0 +1,166 @@
+// Row-wise and elementwise kernels: RMSNorm (wavefront per row), embedding
+// gather, rotary table, row copies, state broadcast, readout log-probability,
+// and weight packing into the library layout.
+#include "common.hpp"
+#include "ops.hpp"
+
+namespace rlt {
+
+// out[m, :] = act(x[m, :] / sqrt(mean(x^2) + eps) * gain); one wavefront per row.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, RowMap xm,
+                                                 const float* __restrict__ gain, T* __restrict__ out,
+                                                 int64_t ldo, int rows, int d, float eps) {
+  const int row = blockIdx.x * 4 + threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (row >= rows) return;
+  const float* xr = x + xm.off(row);
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += WAVE * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float inv = gain ? rsqrtf(ss / (float)d + eps) : 1.f;
+  T* o = out + (int64_t)row * ldo;
+  for (int c = lane * 4; c < d; c += WAVE * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gv = gain ? gain[c + i] : 1.f;
+      Elem<T>::st(o + c + i, w[i] * inv * gv);
+    }
+  }
+}
+
+void rmsnorm(Dt dt, const float* x, RowMap xm, const float* gain, void* out, int64_t ldo, int rows, int d,
+             float eps, hipStream_t st) {
+  if (rows <= 0) return;
+  const dim3 grid((rows + 3) / 4);
+  if (dt == Dt::F32)
+    hipLaunchKernelGGL(rmsnorm_k<float>, grid, dim3(256), 0, st, x, xm, gain, (float*)out, ldo, rows, d, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_k<bf16_t>, grid, dim3(256), 0, st, x, xm, gain, (bf16_t*)out, ldo, rows, d, eps);
+}
+
+template <typename T>
+__global__ void embed_k(const int32_t* __restrict__ tok, const T* __restrict__ emb, float* __restrict__ h,
+                        RowMap hm, int rows, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = d / 4;
+  if (idx >= (int64_t)rows * per) return;
+  const int m = (int)(idx / per), c = (int)(idx % per) * 4;
+  const T* e = emb + (int64_t)tok[m] * d + c;
+  float* o = h + hm.off(m) + c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = Elem<T>::ld(e + i);
+}
+
+void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int rows, int d, hipStream_t st) {
+  if (rows <= 0) return;
+  const int64_t total = (int64_t)rows * (d / 4);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dt == Dt::F32) hipLaunchKernelGGL(embed_k<float>, grid, dim3(256), 0, st, tok, (const float*)emb, h, hm, rows, d);
+  else hipLaunchKernelGGL(embed_k<bf16_t>, grid, dim3(256), 0, st, tok, (const bf16_t*)emb, h, hm, rows, d);
+}
+
+// angle p * base^(-2i/dh), evaluated in double precision, stored as float (cos, sin)
+__global__ void rope_table_k(float2* tab, int npos, int dh, double base) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = dh / 2;
+  if (idx >= (int64_t)npos * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double theta = pow(base, -2.0 * (double)i / (double)dh);
+  const double ang = (double)p * theta;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+void rope_table(float2* tab, int npos, int dh, float base, hipStream_t st) {
+  const int64_t total = (int64_t)npos * (dh / 2);
+  hipLaunchKernelGGL(rope_table_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, tab, npos, dh,
+                     (double)base);
+}
+
+__global__ void copy_rows_k(const float* __restrict__ src, RowMap sm, float* __restrict__ dst, RowMap dm, int rows,
+                            int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = d / 4;
+  if (idx >= (int64_t)rows * per) return;
+  const int m = (int)(idx / per), c = (int)(idx % per) * 4;
+  *reinterpret_cast<float4*>(dst + dm.off(m) + c) = *reinterpret_cast<const float4*>(src + sm.off(m) + c);
+}
+
+void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int d, hipStream_t st) {
+  if (rows <= 0) return;
+  const int64_t total = (int64_t)rows * (d / 4);
+  hipLaunchKernelGGL(copy_rows_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, sm, dst, dm, rows, d);
+}
+
+__global__ void broadcast_row_k(const float* __restrict__ s0, float* __restrict__ s, int B, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)B * d) return;
+  s[idx] = s0[idx % d];
+}
+
+void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st) {
+  const int64_t total = (int64_t)B * d;
+  hipLaunchKernelGGL(broadcast_row_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, s0, s, B, d);
+}
+
+// log p(tok | logits row) = logits[tok] - (max + log(sum exp(logits - max)))
+__global__ __launch_bounds__(256) void logprob_k(const float* __restrict__ logits, RowMap lm,
+                                                 const int32_t* __restrict__ tok, RowMap tm, float* __restrict__ out,
+                                                 RowMap om, int V) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const float* L = logits + lm.off(r);
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < V; j += 256) mx = fmaxf(mx, L[j]);
+  mx = block_max(mx, red);
+  float s = 0.f;
+  for (int j = threadIdx.x; j < V; j += 256) s += __expf(L[j] - mx);
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    const int t = tok[tm.off(r)];
+    out[om.off(r)] = t >= 0 ? L[t] - (mx + __logf(s)) : 0.f;
+  }
+}
+
+void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows, int V,
+             hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(logprob_k, dim3(rows), dim3(256), 0, st, logits, lm, tok, tm, out, om, V);
+}
+
+// dst row (row_off + row_stride * perm(j)) <- src row j, columns [col0, col0 + cols) -> [dst_col0, ...)
+// RopeRows: within each head of dh rows, rotate-half pair (i, i + dh/2) lands on rows (2i, 2i + 1).
+template <typename T>
+__global__ void pack_k(const float* __restrict__ src, int64_t src_ld, int64_t col0, T* __restrict__ dst,
+                       int64_t dst_ld, int64_t dst_col0, int rows, int cols, int kind, int dh, int row_stride,
+                       int row_off) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * cols) return;
+  const int j = (int)(idx / cols), c = (int)(idx % cols);
+  int pj = j;
+  if (kind == (int)Pack::RopeRows) {
+    const int h = j / dh, w = j % dh, half = dh / 2;
+    pj = h * dh + (w < half ? 2 * w : 2 * (w - half) + 1);
+  }
+  const int64_t drow = (int64_t)row_off + (int64_t)row_stride * pj;
+  Elem<T>::st(dst + drow * dst_ld + dst_col0 + c, src[(int64_t)j * src_ld + col0 + c]);
+}
+
+void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* dst, int64_t dst_ld, int64_t dst_col0,
+                 int rows, int cols, Pack kind, int dh, int row_stride, int row_off, hipStream_t st) {
+  const int64_t total = (int64_t)rows * cols;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dt == Dt::F32)
+    hipLaunchKernelGGL(pack_k<float>, grid, dim3(256), 0, st, src, src_ld, col0, (float*)dst, dst_ld, dst_col0, rows,
+                       cols, (int)kind, dh, row_stride, row_off);
+  else
+    hipLaunchKernelGGL(pack_k<bf16_t>, grid, dim3(256), 0, st, src, src_ld, col0, (bf16_t*)dst, dst_ld, dst_col0,
+                       rows, cols, (int)kind, dh, row_stride, row_off);
+}
+
+}  // namespace rlt

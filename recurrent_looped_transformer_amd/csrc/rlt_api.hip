@@ -1,0 +1,783 @@
+// C ABI of the RLT transition library: validation, weight packing, state
+// ownership, and the launch schedules of encode / decode scan / step / replay.
+//
+// Sources: greeksharifa.github.io "Recurrent Looped Transformer 요약 설명"
+// (§2.1-§2.7, appendix A.1, E, F, I) and jiphyeonjeon.kr "Recurrent Looped
+// Transformer" (§2 eq 2.1-2.2, §3.1-§3.4 eq 2.7-2.16, §4.2 eq 3.3, §6.2 eq 5.5).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/rlt.h"
+#include "ops.hpp"
+
+using namespace rlt;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Fail {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const std::string& msg) { throw Fail{code, msg}; }
+
+#define HIPCHK(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t _e = (expr);                                                                 \
+    if (_e != hipSuccess) fail(RLT_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    f();
+    return RLT_OK;
+  } catch (const Fail& e) {
+    g_err = e.msg;
+    return e.code;
+  } catch (const std::exception& e) {
+    g_err = e.what();
+    return RLT_ERR_INVALID_ARG;
+  } catch (...) {
+    g_err = "unknown error";
+    return RLT_ERR_INVALID_ARG;
+  }
+}
+
+void check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) fail(RLT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+}
+
+constexpr int kReadoutPositions = 64;   // positions per batched readout
+constexpr int kParallelPositions = 64;  // RLT-0 positions per decoder pass
+constexpr int64_t kEncoderRows = 32768; // encoder workspace rows (sequences x tokens per group)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct LayerW {
+  float *n1 = nullptr, *n2 = nullptr, *n3 = nullptr;  // enc: n1, n2; dec: m1, m2, m3
+  void *wqkv = nullptr, *wo = nullptr, *w13 = nullptr, *w2 = nullptr;
+  void *xq = nullptr, *xo = nullptr;
+};
+
+}  // namespace
+
+struct rlt_model {
+  rlt_config cfg{};
+  int device = 0;
+  Dt dt = Dt::BF16;
+  size_t esz = 2;
+  int hd = 0;
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  void* emb = nullptr;
+  std::vector<LayerW> enc, dec;
+  float* nE = nullptr;
+  std::vector<void*> wkv;
+  float *ns = nullptr, *bg = nullptr, *s0 = nullptr;
+  void *wg_e = nullptr, *wsr = nullptr;
+  float* nO = nullptr;
+  void* wout = nullptr;
+  uint64_t version = 1;
+  int scan_mode = 0;
+  int n_states = 0;
+};
+
+struct rlt_state {
+  rlt_model* m = nullptr;
+  int B = 0, Tm = 0, keep_enc = 0;
+  int P = 1;          // max positions per decoder pass
+  int R = 1;          // ring capacity (slots per layer, sequence, head)
+  int n_enc = 0, n_dec = 0;
+  uint64_t version = 0;
+  int64_t block_steps = 0;
+  int64_t bytes[6] = {0, 0, 0, 0, 0, 0};
+  std::vector<void*> allocs;
+  float *s = nullptr, *rho = nullptr;
+  float *e = nullptr, *gpre = nullptr;   // [B][Tm][d]
+  void *mem_k = nullptr, *mem_v = nullptr;   // [G][B][H][Tm][dh]
+  void *enc_k = nullptr, *enc_v = nullptr;   // [L_E][B][H][Tm][dh]
+  void *ring_k = nullptr, *ring_v = nullptr; // [L_D][B][H][R][dh]
+  float2* rope = nullptr;                    // [Tm + 1][dh / 2]
+  // decoder workspace, rows = B * P
+  float* z = nullptr;
+  void *xa = nullptr, *q = nullptr, *ao = nullptr, *hid = nullptr;
+  // readout workspace, rows = B * kReadoutPositions
+  float* sbuf = nullptr;
+  void* xr = nullptr;
+  float* lbuf = nullptr;
+  // encoder workspace, rows = enc_rows
+  int64_t enc_rows = 0;
+  void *exa = nullptr, *eq = nullptr, *eao = nullptr, *ehid = nullptr;
+  void *ekv_k = nullptr, *ekv_v = nullptr;   // attention keys when no encoder cache is kept
+  int32_t* toks = nullptr;                   // [B][Tm] shifted next tokens (replay)
+  float* lp = nullptr;                       // [B][Tm] log-probabilities (replay)
+};
+
+namespace {
+
+void* dev_alloc(rlt_state* s, size_t bytes, int cls) {
+  void* p = nullptr;
+  if (bytes == 0) return nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) fail(RLT_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+  s->allocs.push_back(p);
+  s->bytes[cls] += (int64_t)bytes;
+  return p;
+}
+
+void validate_config(const rlt_config& c) {
+  auto bad = [](const std::string& m) { fail(RLT_ERR_INVALID_ARG, "config: " + m); };
+  if (c.vocab <= 0 || c.vocab % 4) bad("vocab must be a positive multiple of 4");
+  if (c.d <= 0 || c.d % 64) bad("d must be a positive multiple of 64");
+  if (c.n_heads <= 0 || c.d_head <= 0) bad("heads");
+  if (c.d_head % 2) fail(RLT_ERR_UNSUPPORTED, "d_head must be even (rotary pairs)");
+  if (c.d_head != 16 && c.d_head != 32 && c.d_head != 64 && c.d_head != 128 && c.d_head != 256)
+    fail(RLT_ERR_UNSUPPORTED, "d_head must be 16, 32, 64, 128 or 256");
+  if ((c.n_heads * c.d_head) % 64) bad("n_heads * d_head must be a multiple of 64");
+  if (c.L_E < 1 || c.L_D < 0) bad("depths");
+  if (c.ffn <= 0 || c.ffn % 64) bad("ffn must be a positive multiple of 64");
+  if (c.window < 1) bad("window must be >= 1");
+  if (c.L_D > 0 && !(c.groups == 1 || c.groups == c.L_D))
+    fail(RLT_ERR_UNSUPPORTED, "memory groups must be 1 or L_D");
+  if (c.variant != RLT_V0 && c.variant != RLT_V1 && c.variant != RLT_V2) bad("variant");
+  if (c.chunk < 1 || (c.variant != RLT_V2 && c.chunk != 1)) bad("chunk must be 1 unless RLT-2");
+  if (c.chunk > 64) fail(RLT_ERR_UNSUPPORTED, "chunk > 64");
+  if (c.share_enc_dec && c.L_E != c.L_D) fail(RLT_ERR_UNSUPPORTED, "sharing needs L_E == L_D");
+  if (c.dtype != RLT_FP32 && c.dtype != RLT_BF16) bad("dtype");
+  if (!(c.rms_eps >= 0.f) || !(c.rope_base > 0.f)) bad("eps / rope base");
+}
+
+struct Shape {
+  int64_t rows, cols;
+};
+
+std::map<std::string, Shape> manifest(const rlt_config& c) {
+  std::map<std::string, Shape> m;
+  const int64_t d = c.d, hd = (int64_t)c.n_heads * c.d_head, f = c.ffn, V = c.vocab;
+  m["emb"] = {V, d};
+  for (int l = 0; l < c.L_E; ++l) {
+    const std::string p = "enc." + std::to_string(l) + ".";
+    m[p + "n1"] = {1, d}; m[p + "n2"] = {1, d};
+    m[p + "wq"] = {hd, d}; m[p + "wk"] = {hd, d}; m[p + "wv"] = {hd, d}; m[p + "wo"] = {d, hd};
+    m[p + "w1"] = {f, d}; m[p + "w3"] = {f, d}; m[p + "w2"] = {d, f};
+  }
+  if (c.L_D > 0) {
+    m["mem.nE"] = {1, d};
+    for (int g = 0; g < c.groups; ++g) {
+      m["mem." + std::to_string(g) + ".wk"] = {hd, d};
+      m["mem." + std::to_string(g) + ".wv"] = {hd, d};
+    }
+  }
+  if (c.variant != RLT_V0) {
+    m["merge.ns"] = {1, d}; m["merge.wg"] = {d, 2 * d}; m["merge.bg"] = {1, d};
+    m["merge.ws"] = {d, d}; m["merge.s0"] = {1, d};
+  }
+  for (int l = 0; l < c.L_D; ++l) {
+    const std::string p = "dec." + std::to_string(l) + ".";
+    m[p + "m1"] = {1, d}; m[p + "m2"] = {1, d}; m[p + "m3"] = {1, d};
+    m[p + "xq"] = {hd, d}; m[p + "xo"] = {d, hd};
+    if (!c.share_enc_dec) {
+      m[p + "wq"] = {hd, d}; m[p + "wk"] = {hd, d}; m[p + "wv"] = {hd, d}; m[p + "wo"] = {d, hd};
+      m[p + "w1"] = {f, d}; m[p + "w3"] = {f, d}; m[p + "w2"] = {d, f};
+    }
+  }
+  m["out.nO"] = {1, d};
+  m["out.w"] = {V, d};
+  return m;
+}
+
+std::map<std::string, const float*> index_weights(const rlt_config& c, const rlt_tensor* w, int n) {
+  if (n < 0 || (n > 0 && !w)) fail(RLT_ERR_INVALID_ARG, "weights pointer");
+  auto man = manifest(c);
+  std::map<std::string, const float*> got;
+  for (int i = 0; i < n; ++i) {
+    if (!w[i].name || !w[i].data) fail(RLT_ERR_INVALID_ARG, "null weight name or data");
+    auto it = man.find(w[i].name);
+    if (it == man.end()) fail(RLT_ERR_INVALID_ARG, std::string("unknown weight ") + w[i].name);
+    if (w[i].numel != it->second.rows * it->second.cols)
+      fail(RLT_ERR_INVALID_ARG, std::string("wrong size for ") + w[i].name);
+    if (got.count(w[i].name)) fail(RLT_ERR_INVALID_ARG, std::string("duplicate weight ") + w[i].name);
+    got[w[i].name] = w[i].data;
+  }
+  for (auto& kv : man)
+    if (!got.count(kv.first)) fail(RLT_ERR_INVALID_ARG, "missing weight " + kv.first);
+  return got;
+}
+
+// Lay out the packed parameter arena (sizes only) and assign pointers.
+void layout_model(rlt_model* m, char* base, size_t* total) {
+  const rlt_config& c = m->cfg;
+  const size_t e = m->esz;
+  const int64_t d = c.d, hd = m->hd, f = c.ffn, V = c.vocab;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  auto takef = [&](int64_t n) { return (float*)take(n * 4); };
+  m->emb = take(V * d * e);
+  m->enc.assign(c.L_E, LayerW{});
+  for (auto& L : m->enc) {
+    L.n1 = takef(d); L.n2 = takef(d);
+    L.wqkv = take(3 * hd * d * e); L.wo = take(d * hd * e); L.w13 = take(2 * f * d * e); L.w2 = take(d * f * e);
+  }
+  m->wkv.assign(c.L_D > 0 ? c.groups : 0, nullptr);
+  if (c.L_D > 0) {
+    m->nE = takef(d);
+    for (auto& p : m->wkv) p = take(2 * hd * d * e);
+  }
+  if (c.variant != RLT_V0) {
+    m->ns = takef(d); m->bg = takef(d); m->s0 = takef(d);
+    m->wg_e = take(d * d * e); m->wsr = take(2 * d * d * e);
+  }
+  m->dec.assign(c.L_D, LayerW{});
+  for (int l = 0; l < c.L_D; ++l) {
+    LayerW& L = m->dec[l];
+    L.n1 = takef(d); L.n2 = takef(d); L.n3 = takef(d);
+    L.xq = take(hd * d * e); L.xo = take(d * hd * e);
+    if (c.share_enc_dec) {
+      L.wqkv = m->enc[l].wqkv; L.wo = m->enc[l].wo; L.w13 = m->enc[l].w13; L.w2 = m->enc[l].w2;
+    } else {
+      L.wqkv = take(3 * hd * d * e); L.wo = take(d * hd * e); L.w13 = take(2 * f * d * e); L.w2 = take(d * f * e);
+    }
+  }
+  m->nO = takef(d);
+  m->wout = take(V * d * e);
+  *total = off;
+}
+
+void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const int d = c.d, hd = m->hd, f = c.ffn, V = c.vocab, dh = c.d_head;
+  const Dt dt = m->dt;
+  auto vec = [&](float* dst, const std::string& name) {
+    HIPCHK(hipMemcpyAsync(dst, W.at(name), sizeof(float) * d, hipMemcpyDeviceToDevice, st));
+  };
+  auto plain = [&](void* dst, const std::string& name, int rows, int cols, int row_off = 0, int stride = 1) {
+    pack_matrix(dt, W.at(name), cols, 0, dst, cols, 0, rows, cols, Pack::Plain, dh, stride, row_off, st);
+  };
+  auto roped = [&](void* dst, const std::string& name, int row_off) {
+    pack_matrix(dt, W.at(name), d, 0, dst, d, 0, hd, d, Pack::RopeRows, dh, 1, row_off, st);
+  };
+  auto attn_ffn = [&](const LayerW& L, const std::string& p) {
+    roped(L.wqkv, p + "wq", 0);
+    roped(L.wqkv, p + "wk", hd);
+    plain(L.wqkv, p + "wv", hd, d, 2 * hd);
+    plain(L.wo, p + "wo", d, hd);
+    plain(L.w13, p + "w1", f, d, 0, 2);   // SwiGLU pair rows (2j, 2j + 1) = (W1 row j, W3 row j)
+    plain(L.w13, p + "w3", f, d, 1, 2);
+    plain(L.w2, p + "w2", d, f);
+  };
+  plain(m->emb, "emb", V, d);
+  for (int l = 0; l < c.L_E; ++l) {
+    const std::string p = "enc." + std::to_string(l) + ".";
+    vec(m->enc[l].n1, p + "n1");
+    vec(m->enc[l].n2, p + "n2");
+    attn_ffn(m->enc[l], p);
+  }
+  if (c.L_D > 0) {
+    vec(m->nE, "mem.nE");
+    for (int g = 0; g < c.groups; ++g) {
+      const std::string p = "mem." + std::to_string(g) + ".";
+      roped(m->wkv[g], p + "wk", 0);
+      plain(m->wkv[g], p + "wv", hd, d, hd);
+    }
+  }
+  if (c.variant != RLT_V0) {
+    vec(m->ns, "merge.ns");
+    vec(m->bg, "merge.bg");
+    vec(m->s0, "merge.s0");
+    // W_g = [W_g,e | W_g,r] over [e_t ; r]: the e half is applied once per position at encode time,
+    // the r half is interleaved with W_s (rows 2n, 2n + 1) for the per-step merge GEMM.
+    pack_matrix(dt, W.at("merge.wg"), 2 * d, 0, m->wg_e, d, 0, d, d, Pack::Plain, dh, 1, 0, st);
+    pack_matrix(dt, W.at("merge.wg"), 2 * d, d, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 0, st);
+    pack_matrix(dt, W.at("merge.ws"), d, 0, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 1, st);
+  }
+  for (int l = 0; l < c.L_D; ++l) {
+    const std::string p = "dec." + std::to_string(l) + ".";
+    vec(m->dec[l].n1, p + "m1");
+    vec(m->dec[l].n2, p + "m2");
+    vec(m->dec[l].n3, p + "m3");
+    pack_matrix(dt, W.at(p + "xq"), d, 0, m->dec[l].xq, d, 0, hd, d, Pack::RopeRows, dh, 1, 0, st);
+    plain(m->dec[l].xo, p + "xo", d, hd);
+    if (!c.share_enc_dec) attn_ffn(m->dec[l], p);
+  }
+  vec(m->nO, "out.nO");
+  plain(m->wout, "out.w", V, d);
+  check_launch();
+}
+
+void check_state(rlt_model* m, rlt_state* s) {
+  if (!m || !s) fail(RLT_ERR_INVALID_ARG, "null model or state");
+  if (s->m != m) fail(RLT_ERR_INVALID_ARG, "state belongs to another model");
+  if (s->version != m->version) fail(RLT_ERR_STALE_STATE, "state was built under older weights; reset it");
+}
+
+// ------------------------------------------------------------------ encode
+void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const Dt dt = m->dt;
+  const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, Tm = s->Tm;
+  const int t0 = s->n_enc;
+  const int Bc = (int)std::max<int64_t>(1, std::min<int64_t>(s->B, s->enc_rows / T));
+  for (int b0 = 0; b0 < s->B; b0 += Bc) {
+    const int nb = std::min(Bc, s->B - b0);
+    const int rows = nb * T;
+    RowMap hm;   // encoder residual stream lives in the state's e rows
+    hm.tn = T; hm.sb = (int64_t)Tm * d; hm.st = d;
+    float* h = s->e + ((int64_t)b0 * Tm + t0) * d;
+    embed(dt, tokens + (int64_t)b0 * T, m->emb, h, hm, rows, d, st);
+    for (int l = 0; l < c.L_E; ++l) {
+      const LayerW& L = m->enc[l];
+      rmsnorm(dt, h, hm, L.n1, s->exa, d, rows, d, c.rms_eps, st);
+      EpArgs a;
+      a.out = s->eq; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0;
+      AttnArgs at;
+      if (s->enc_k) {
+        const int64_t lo = (int64_t)l * s->B * H * Tm * dh;
+        a.kv.k = (char*)s->enc_k + lo * m->esz; a.kv.v = (char*)s->enc_v + lo * m->esz;
+        a.kv.cap = Tm; a.b0 = b0;
+        at.k = (char*)a.kv.k + (int64_t)b0 * H * Tm * dh * m->esz;
+        at.v = (char*)a.kv.v + (int64_t)b0 * H * Tm * dh * m->esz;
+        at.kv_bstride = (int64_t)H * Tm * dh; at.cap = Tm;
+      } else {
+        a.kv.k = s->ekv_k; a.kv.v = s->ekv_v; a.kv.cap = T; a.b0 = 0;
+        at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T;
+      }
+      a.kv.ring = 0;
+      gemm(dt, Ep::QKV, a, s->exa, d, L.wqkv, rows, 3 * hd, d, st);
+      at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = hd;
+      at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
+      at.scale = 1.f / std::sqrt((float)dh);
+      attn_decode(dt, at, st);
+      EpArgs r; r.resid = h; r.rmap = hm;
+      gemm(dt, Ep::Residual, r, s->eao, hd, L.wo, rows, d, hd, st);
+      rmsnorm(dt, h, hm, L.n2, s->exa, d, rows, d, c.rms_eps, st);
+      EpArgs sw; sw.out = s->ehid; sw.ldo = f;
+      gemm(dt, Ep::SwiGLU, sw, s->exa, d, L.w13, rows, 2 * f, d, st);
+      gemm(dt, Ep::Residual, r, s->ehid, f, L.w2, rows, d, f, st);
+    }
+    if (c.L_D > 0) {
+      // memory: k^g = RoPE(W^g_K RMSNorm_E(e)), v^g = W^g_V RMSNorm_E(e)  (eq 2.1-2.2)
+      rmsnorm(dt, h, hm, m->nE, s->exa, d, rows, d, c.rms_eps, st);
+      for (int g = 0; g < c.groups; ++g) {
+        EpArgs a;
+        a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0; a.b0 = b0;
+        const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
+        a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
+        gemm(dt, Ep::MemKV, a, s->exa, d, m->wkv[g], rows, 2 * hd, d, st);
+      }
+    }
+    if (c.variant != RLT_V0) {
+      // gate pre-activation W_g,e e_t + b_g: independent of the recurrence, computed token-parallel
+      rmsnorm(dt, h, hm, nullptr, s->exa, d, rows, d, 0.f, st);
+      EpArgs a; a.resid = s->gpre + ((int64_t)b0 * Tm + t0) * d; a.rmap = hm; a.bias = m->bg;
+      gemm(dt, Ep::Bias, a, s->exa, d, m->wg_e, rows, d, d, st);
+    }
+  }
+  check_launch();
+  s->n_enc += T;
+}
+
+// ------------------------------------------------------------------ decoder pass
+// Positions t0+1 .. t0+np for every sequence, rows m = b * np + i.
+void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const Dt dt = m->dt;
+  const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = s->B, Tm = s->Tm;
+  const int rows = B * np;
+  const RowMap zm = contiguous(d);
+  if (c.variant == RLT_V0) {
+    RowMap em; em.tn = np; em.sb = (int64_t)Tm * d; em.st = d;
+    copy_rows(s->e + (int64_t)t0 * d, em, s->z, zm, rows, d, st);
+  } else {
+    // merge (eq 2.9-2.11): r = RMSNorm_s(s_{t-1} or the RLT-2 register), gate and state projection
+    const float* src = c.variant == RLT_V1 ? s->s : s->rho;
+    rmsnorm(dt, src, contiguous(d), m->ns, s->xa, d, B, d, c.rms_eps, st);
+    EpArgs a;
+    a.resid = s->z; a.rmap = zm; a.e = s->e + (int64_t)t0 * d; a.gpre = s->gpre + (int64_t)t0 * d;
+    a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha;
+    gemm(dt, Ep::Merge, a, s->xa, d, m->wsr, B, 2 * d, d, st);
+  }
+  const float scale = 1.f / std::sqrt((float)dh);
+  for (int l = 0; l < c.L_D; ++l) {
+    const LayerW& L = m->dec[l];
+    // causal sliding-window self-attention over the ring (current key written first)
+    rmsnorm(dt, s->z, zm, L.n1, s->xa, d, rows, d, c.rms_eps, st);
+    EpArgs a;
+    a.out = s->q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
+    const int64_t ro = (int64_t)l * B * H * s->R * dh * m->esz;
+    a.kv.k = (char*)s->ring_k + ro; a.kv.v = (char*)s->ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
+    gemm(dt, Ep::QKV, a, s->xa, d, L.wqkv, rows, 3 * hd, d, st);
+    AttnArgs at;
+    at.q = s->q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
+    at.cap = s->R; at.ring = 1; at.out = s->ao; at.ldo = hd; at.B = B; at.nq = np; at.H = H; at.dh = dh;
+    at.pos0 = t0; at.window = c.window; at.scale = scale;
+    attn_decode(dt, at, st);
+    EpArgs r; r.resid = s->z; r.rmap = zm;
+    gemm(dt, Ep::Residual, r, s->ao, hd, L.wo, rows, d, hd, st);
+    // cross-attention to the prefix memory M_<=t of this layer's group
+    rmsnorm(dt, s->z, zm, L.n2, s->xa, d, rows, d, c.rms_eps, st);
+    EpArgs qx;
+    qx.out = s->q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0;
+    gemm(dt, Ep::RopeQ, qx, s->xa, d, L.xq, rows, hd, d, st);
+    const int g = c.groups == 1 ? 0 : l;
+    const int64_t go = (int64_t)g * B * H * Tm * dh * m->esz;
+    at.k = (char*)s->mem_k + go; at.v = (char*)s->mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
+    at.cap = Tm; at.ring = 0; at.window = 0;
+    attn_decode(dt, at, st);
+    gemm(dt, Ep::Residual, r, s->ao, hd, L.xo, rows, d, hd, st);
+    // SwiGLU FFN
+    rmsnorm(dt, s->z, zm, L.n3, s->xa, d, rows, d, c.rms_eps, st);
+    EpArgs sw; sw.out = s->hid; sw.ldo = f;
+    gemm(dt, Ep::SwiGLU, sw, s->xa, d, L.w13, rows, 2 * f, d, st);
+    gemm(dt, Ep::Residual, r, s->hid, f, L.w2, rows, d, f, st);
+  }
+  s->block_steps += c.L_D;
+  // s_t = the last position's output of every sequence
+  RowMap last; last.tn = 1; last.sb = (int64_t)np * d;
+  copy_rows(s->z + (int64_t)(np - 1) * d, last, s->s, zm, B, d, st);
+  if (c.variant == RLT_V2 && (t0 + np) % c.chunk == 0)
+    HIPCHK(hipMemcpyAsync(s->rho, s->s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
+}
+
+struct ScanOut {
+  float* logits = nullptr;          // rows (b, c) at logits + (b * ld_b + c) * V
+  int64_t ld_b = 0;
+  float* s_out = nullptr;           // rows (b, c) at s_out + (b * ld_b + c) * d
+  const int32_t* tok = nullptr;     // next token of (b, c) at tok[b * tok_ld + c]
+  int64_t tok_ld = 0;
+  float* lp = nullptr;              // log-prob of (b, c) at lp[b * lp_ld + c]
+  int64_t lp_ld = 0;
+  int lp_valid = 1 << 30;           // columns c >= lp_valid are not written
+};
+
+// Readout of buffered positions c0 .. c0+n-1 (scan-relative) held in sbuf [B][kReadoutPositions][d].
+void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const Dt dt = m->dt;
+  const int d = c.d, V = c.vocab, B = s->B;
+  const int rows = B * n;
+  RowMap sm; sm.tn = n; sm.sb = (int64_t)kReadoutPositions * d; sm.st = d;
+  if (o.s_out) {
+    RowMap dm; dm.tn = n; dm.sb = o.ld_b * d; dm.st = d;
+    copy_rows(s->sbuf, sm, o.s_out + (int64_t)c0 * d, dm, rows, d, st);
+  }
+  if (!o.logits && !o.lp) return;
+  rmsnorm(dt, s->sbuf, sm, m->nO, s->xr, d, rows, d, c.rms_eps, st);
+  EpArgs a; a.out = s->lbuf; a.ldo = V;
+  gemm(dt, Ep::StoreF32, a, s->xr, d, m->wout, rows, V, d, st);
+  if (o.logits) {
+    RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
+    copy_rows(s->lbuf, contiguous(V), o.logits + (int64_t)c0 * V, dm, rows, V, st);
+  }
+  if (o.lp) {
+    const int nv = std::min(n, o.lp_valid - c0);
+    if (nv > 0) {
+      RowMap lm; lm.tn = nv; lm.sb = (int64_t)n * V; lm.st = V;
+      RowMap tm; tm.tn = nv; tm.sb = o.tok_ld; tm.st = 1;
+      RowMap om; om.tn = nv; om.sb = o.lp_ld; om.st = 1;
+      logprob(s->lbuf, lm, o.tok + c0, tm, o.lp + c0, om, B * nv, V, st);
+    }
+  }
+}
+
+void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const int d = c.d;
+  const int start = s->n_dec;
+  const bool want_rows = o.logits || o.lp || o.s_out;
+  int c0 = 0;          // scan-relative column of the first buffered position
+  int buffered = 0;
+  int done = 0;
+  auto flush = [&] {
+    if (buffered > 0) readout(m, s, c0, buffered, o, st);
+    c0 += buffered;
+    buffered = 0;
+  };
+  while (done < T) {
+    const int t0 = start + done;
+    int np = 1;
+    if (c.variant == RLT_V2) np = std::min(T - done, (t0 / c.chunk + 1) * c.chunk - t0);
+    else if (c.variant == RLT_V0) np = std::min(T - done, s->P);
+    if (want_rows && buffered + np > kReadoutPositions) flush();
+    decoder_pass(m, s, t0, np, st);
+    if (want_rows) {
+      RowMap dm; dm.tn = np; dm.sb = (int64_t)kReadoutPositions * d; dm.st = d;
+      copy_rows(s->z, contiguous(d), s->sbuf + (int64_t)buffered * d, dm, s->B * np, d, st);
+      buffered += np;
+    }
+    done += np;
+    s->n_dec = t0 + np;
+  }
+  if (want_rows) flush();
+  check_launch();
+}
+
+}  // namespace
+
+// ======================================================================= C ABI
+extern "C" {
+
+const char* rlt_status_string(int status) {
+  switch (status) {
+    case RLT_OK: return "ok";
+    case RLT_ERR_INVALID_ARG: return "invalid argument";
+    case RLT_ERR_UNSUPPORTED: return "unsupported";
+    case RLT_ERR_OOM: return "out of device memory";
+    case RLT_ERR_CAPACITY: return "capacity exceeded";
+    case RLT_ERR_STALE_STATE: return "stale state";
+    case RLT_ERR_HIP: return "HIP error";
+    case RLT_ERR_ORDER: return "decoder ahead of encoder";
+    default: return "unknown status";
+  }
+}
+
+const char* rlt_last_error(void) { return g_err.c_str(); }
+
+int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, hipStream_t stream, rlt_model** out) {
+  return guarded([&] {
+    if (!cfg || !out) fail(RLT_ERR_INVALID_ARG, "null config or output");
+    *out = nullptr;
+    validate_config(*cfg);
+    auto W = index_weights(*cfg, weights, n_weights);
+    auto* m = new rlt_model();
+    try {
+      m->cfg = *cfg;
+      HIPCHK(hipGetDevice(&m->device));
+      m->dt = cfg->dtype == RLT_FP32 ? Dt::F32 : Dt::BF16;
+      m->esz = cfg->dtype == RLT_FP32 ? 4 : 2;
+      m->hd = cfg->n_heads * cfg->d_head;
+      size_t total = 0;
+      layout_model(m, nullptr, &total);
+      if (hipMalloc(&m->arena, total) != hipSuccess) fail(RLT_ERR_OOM, "weight arena allocation failed");
+      m->arena_bytes = total;
+      layout_model(m, (char*)m->arena, &total);
+      pack_all(m, W, stream);
+      HIPCHK(hipStreamSynchronize(stream));
+    } catch (...) {
+      if (m->arena) (void)hipFree(m->arena);
+      delete m;
+      throw;
+    }
+    *out = m;
+  });
+}
+
+int rlt_update_weights(rlt_model* m, const rlt_tensor* weights, int n_weights, hipStream_t stream) {
+  return guarded([&] {
+    if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
+    auto W = index_weights(m->cfg, weights, n_weights);
+    pack_all(m, W, stream);
+    HIPCHK(hipStreamSynchronize(stream));
+    m->version += 1;
+  });
+}
+
+int rlt_destroy(rlt_model* m) {
+  return guarded([&] {
+    if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
+    if (m->n_states > 0) fail(RLT_ERR_INVALID_ARG, "destroy the model's states first");
+    if (m->arena) HIPCHK(hipFree(m->arena));
+    delete m;
+  });
+}
+
+int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cache, hipStream_t stream,
+                     rlt_state** out) {
+  return guarded([&] {
+    if (!m || !out) fail(RLT_ERR_INVALID_ARG, "null model or output");
+    *out = nullptr;
+    if (batch < 1 || max_len < 1) fail(RLT_ERR_INVALID_ARG, "batch and max_len must be >= 1");
+    if (max_len > 16384) fail(RLT_ERR_UNSUPPORTED, "max_len > 16384");
+    const rlt_config& c = m->cfg;
+    auto* s = new rlt_state();
+    try {
+      s->m = m;
+      s->B = batch;
+      s->Tm = max_len;
+      s->keep_enc = keep_encoder_cache ? 1 : 0;
+      s->P = c.variant == RLT_V2 ? c.chunk : (c.variant == RLT_V0 ? std::min(kParallelPositions, max_len) : 1);
+      s->R = c.window + s->P - 1;
+      const int64_t B = batch, Tm = max_len, d = c.d, hd = m->hd, f = c.ffn, V = c.vocab, H = c.n_heads,
+                    dh = c.d_head;
+      const size_t e = m->esz;
+      if (s->keep_enc) {
+        s->enc_k = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0);
+        s->enc_v = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0);
+      }
+      if (c.L_D > 0) {
+        s->mem_k = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1);
+        s->mem_v = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1);
+        s->ring_k = dev_alloc(s, (size_t)c.L_D * B * H * s->R * dh * e, 2);
+        s->ring_v = dev_alloc(s, (size_t)c.L_D * B * H * s->R * dh * e, 2);
+      }
+      s->s = (float*)dev_alloc(s, sizeof(float) * B * d, 3);
+      s->rho = (float*)dev_alloc(s, sizeof(float) * B * d, 3);
+      s->e = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4);
+      if (c.variant != RLT_V0) s->gpre = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4);
+      s->rope = (float2*)dev_alloc(s, sizeof(float2) * (Tm + 1) * (dh / 2), 5);
+      const int64_t rows = B * s->P;
+      s->z = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
+      s->xa = dev_alloc(s, rows * d * e, 5);
+      s->q = dev_alloc(s, rows * hd * e, 5);
+      s->ao = dev_alloc(s, rows * hd * e, 5);
+      s->hid = dev_alloc(s, rows * f * e, 5);
+      const int64_t rr = B * kReadoutPositions;
+      s->sbuf = (float*)dev_alloc(s, sizeof(float) * rr * d, 5);
+      s->xr = dev_alloc(s, rr * d * e, 5);
+      s->lbuf = (float*)dev_alloc(s, sizeof(float) * rr * V, 5);
+      s->enc_rows = std::min<int64_t>(B * Tm, std::max<int64_t>(kEncoderRows, Tm));
+      const int64_t er = s->enc_rows;
+      s->exa = dev_alloc(s, er * d * e, 5);
+      s->eq = dev_alloc(s, er * hd * e, 5);
+      s->eao = dev_alloc(s, er * hd * e, 5);
+      s->ehid = dev_alloc(s, er * f * e, 5);
+      if (!s->keep_enc) {
+        s->ekv_k = dev_alloc(s, er * hd * e, 5);
+        s->ekv_v = dev_alloc(s, er * hd * e, 5);
+      }
+      s->toks = (int32_t*)dev_alloc(s, sizeof(int32_t) * B * Tm, 5);
+      s->lp = (float*)dev_alloc(s, sizeof(float) * B * Tm, 5);
+      rope_table(s->rope, max_len + 1, (int)dh, c.rope_base, stream);
+      check_launch();
+      m->n_states += 1;
+      *out = s;
+      if (rlt_state_reset(m, s, stream) != RLT_OK) fail(RLT_ERR_HIP, g_err);
+      HIPCHK(hipStreamSynchronize(stream));
+    } catch (...) {
+      if (*out) { m->n_states -= 1; *out = nullptr; }
+      for (void* p : s->allocs) (void)hipFree(p);
+      delete s;
+      throw;
+    }
+  });
+}
+
+int rlt_state_reset(rlt_model* m, rlt_state* s, hipStream_t stream) {
+  return guarded([&] {
+    if (!m || !s || s->m != m) fail(RLT_ERR_INVALID_ARG, "null or foreign state");
+    const rlt_config& c = m->cfg;
+    if (c.variant != RLT_V0) {
+      broadcast_row(m->s0, s->s, s->B, c.d, stream);
+      broadcast_row(m->s0, s->rho, s->B, c.d, stream);
+    } else {
+      HIPCHK(hipMemsetAsync(s->s, 0, sizeof(float) * s->B * c.d, stream));
+    }
+    check_launch();
+    s->n_enc = 0;
+    s->n_dec = 0;
+    s->block_steps = 0;
+    s->version = m->version;
+  });
+}
+
+int rlt_state_destroy(rlt_state* s) {
+  return guarded([&] {
+    if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
+    for (void* p : s->allocs) HIPCHK(hipFree(p));
+    s->m->n_states -= 1;
+    delete s;
+  });
+}
+
+int rlt_state_bytes(const rlt_state* s, int64_t out[6]) {
+  return guarded([&] {
+    if (!s || !out) fail(RLT_ERR_INVALID_ARG, "null state or output");
+    for (int i = 0; i < 6; ++i) out[i] = s->bytes[i];
+  });
+}
+
+int rlt_state_positions(const rlt_state* s, int* n_encoded, int* n_decoded) {
+  return guarded([&] {
+    if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
+    if (n_encoded) *n_encoded = s->n_enc;
+    if (n_decoded) *n_decoded = s->n_dec;
+  });
+}
+
+int rlt_state_block_steps(const rlt_state* s, int64_t* out) {
+  return guarded([&] {
+    if (!s || !out) fail(RLT_ERR_INVALID_ARG, "null state or output");
+    *out = s->block_steps;
+  });
+}
+
+int rlt_set_scan_mode(rlt_model* m, int mode) {
+  return guarded([&] {
+    if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
+    if (mode < 0 || mode > 2) fail(RLT_ERR_INVALID_ARG, "scan mode must be 0, 1 or 2");
+    m->scan_mode = mode;
+  });
+}
+
+int rlt_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!tokens || T < 1) fail(RLT_ERR_INVALID_ARG, "tokens and T >= 1 required");
+    if ((int64_t)s->n_enc + T > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "continuing an encode needs keep_encoder_cache");
+    do_encode(m, s, tokens, T, stream);
+  });
+}
+
+int rlt_decode_scan(rlt_model* m, rlt_state* s, int T, float* logits, float* next_logprob,
+                    const int32_t* next_tokens, float* s_out, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (T < 1) fail(RLT_ERR_INVALID_ARG, "T >= 1 required");
+    if (next_logprob && !next_tokens) fail(RLT_ERR_INVALID_ARG, "next_logprob needs next_tokens");
+    if ((int64_t)s->n_dec + T > s->n_enc) fail(RLT_ERR_ORDER, "decoder would pass the encoded positions");
+    ScanOut o;
+    o.logits = logits; o.ld_b = T; o.s_out = s_out;
+    o.tok = next_tokens; o.tok_ld = T; o.lp = next_logprob; o.lp_ld = T;
+    do_scan(m, s, T, o, stream);
+  });
+}
+
+int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!tokens || !logits) fail(RLT_ERR_INVALID_ARG, "tokens and logits required");
+    if (s->n_enc + 1 > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "generation needs keep_encoder_cache");
+    if (s->n_dec != s->n_enc) fail(RLT_ERR_ORDER, "consume the encoded positions before stepping");
+    do_encode(m, s, tokens, 1, stream);
+    ScanOut o;
+    o.logits = logits; o.ld_b = 1;
+    do_scan(m, s, 1, o, stream);
+  });
+}
+
+int rlt_replay(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, float* logprob, float* s_out,
+               hipStream_t stream) {
+  return guarded([&] {
+    if (!m || !s || s->m != m) fail(RLT_ERR_INVALID_ARG, "null or foreign state");
+    if (!tokens || T < 1) fail(RLT_ERR_INVALID_ARG, "tokens and T >= 1 required");
+    if (T > s->Tm) fail(RLT_ERR_CAPACITY, "T exceeds the state's max_len");
+    if (rlt_state_reset(m, s, stream) != RLT_OK) fail(RLT_ERR_HIP, g_err);
+    do_encode(m, s, tokens, T, stream);
+    ScanOut o;
+    o.ld_b = T;
+    o.s_out = s_out;
+    if (logprob && T > 1) {
+      o.tok = tokens + 1; o.tok_ld = T;          // next token of position c+1 is tokens[b, c+1]
+      o.lp = logprob; o.lp_ld = T - 1; o.lp_valid = T - 1;
+    }
+    do_scan(m, s, T, o, stream);
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+"""Python binding of librlt (ctypes). Argument marshalling only: every step of the
+forward pass runs in the library's HIP kernels. torch supplies device memory and
+the stream; no torch type crosses the C ABI.
+
+The functions mirror include/rlt.h one to one (same names); device arguments are
+torch tensors on the GPU, passed as raw pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import synth
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librlt.so")
+
+RLT_OK = 0
+STATUS = {0: "RLT_OK", -1: "RLT_ERR_INVALID_ARG", -2: "RLT_ERR_UNSUPPORTED", -3: "RLT_ERR_OOM",
+          -4: "RLT_ERR_CAPACITY", -5: "RLT_ERR_STALE_STATE", -6: "RLT_ERR_HIP", -7: "RLT_ERR_ORDER"}
+
+EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create", "rlt_state_reset",
+           "rlt_state_destroy", "rlt_state_bytes", "rlt_state_positions", "rlt_encode", "rlt_decode_scan",
+           "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
+           "rlt_last_error"]
+
+
+class RltError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class rlt_config(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int), ("d", ctypes.c_int), ("n_heads", ctypes.c_int),
+                ("d_head", ctypes.c_int), ("L_E", ctypes.c_int), ("L_D", ctypes.c_int),
+                ("ffn", ctypes.c_int), ("window", ctypes.c_int), ("groups", ctypes.c_int),
+                ("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("share_enc_dec", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("rope_base", ctypes.c_float)]
+
+
+class rlt_tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librlt.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m recurrent_looped_transformer_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "rlt_create": [ctypes.POINTER(rlt_config), ctypes.POINTER(rlt_tensor), i32, vp, ctypes.POINTER(vp)],
+        "rlt_update_weights": [vp, ctypes.POINTER(rlt_tensor), i32, vp],
+        "rlt_destroy": [vp],
+        "rlt_state_create": [vp, i32, i32, i32, vp, ctypes.POINTER(vp)],
+        "rlt_state_reset": [vp, vp, vp],
+        "rlt_state_destroy": [vp],
+        "rlt_state_bytes": [vp, i64p],
+        "rlt_state_positions": [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+        "rlt_encode": [vp, vp, vp, i32, vp],
+        "rlt_decode_scan": [vp, vp, i32, vp, vp, vp, vp, vp],
+        "rlt_step": [vp, vp, vp, vp, vp],
+        "rlt_replay": [vp, vp, vp, i32, vp, vp, vp],
+        "rlt_set_scan_mode": [vp, i32],
+        "rlt_state_block_steps": [vp, i64p],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.rlt_status_string.argtypes = [ctypes.c_int]
+    L.rlt_status_string.restype = ctypes.c_char_p
+    L.rlt_last_error.argtypes = []
+    L.rlt_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code: int) -> None:
+    if code != RLT_OK:
+        raise RltError(code, load().rlt_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous CUDA tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def config_struct(cfg: synth.Config) -> rlt_config:
+    return rlt_config(cfg.vocab, cfg.d, cfg.n_heads, cfg.d_head, cfg.L_E, cfg.L_D, cfg.ffn, cfg.window,
+                      cfg.groups, cfg.variant, cfg.chunk, 1 if cfg.share else 0,
+                      0 if cfg.dtype == "fp32" else 1, cfg.alpha, cfg.rms_eps, cfg.rope_base)
+
+
+def _tensors(params: Dict[str, np.ndarray], device) -> tuple:
+    keep, arr = [], (rlt_tensor * len(params))()
+    for i, (name, a) in enumerate(params.items()):
+        t = torch.as_tensor(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        keep.append(t)
+        arr[i] = rlt_tensor(name.encode(), t.data_ptr(), t.numel())
+    return arr, keep
+
+
+# ----------------------------------------------------------------- C ABI mirror
+def rlt_create(cfg: synth.Config, params: Dict[str, np.ndarray], device="cuda") -> ctypes.c_void_p:
+    L = load()
+    arr, keep = _tensors(params, device)
+    out = ctypes.c_void_p()
+    c = config_struct(cfg)
+    _check(L.rlt_create(ctypes.byref(c), arr, len(params), ctypes.c_void_p(_stream()), ctypes.byref(out)))
+    del keep
+    return out
+
+
+def rlt_update_weights(model, params: Dict[str, np.ndarray], device="cuda") -> None:
+    arr, keep = _tensors(params, device)
+    _check(load().rlt_update_weights(model, arr, len(params), ctypes.c_void_p(_stream())))
+    del keep
+
+
+def rlt_destroy(model) -> None:
+    _check(load().rlt_destroy(model))
+
+
+def rlt_state_create(model, batch: int, max_len: int, keep_encoder_cache: bool = True) -> ctypes.c_void_p:
+    out = ctypes.c_void_p()
+    _check(load().rlt_state_create(model, batch, max_len, 1 if keep_encoder_cache else 0,
+                                   ctypes.c_void_p(_stream()), ctypes.byref(out)))
+    return out
+
+
+def rlt_state_reset(model, state) -> None:
+    _check(load().rlt_state_reset(model, state, ctypes.c_void_p(_stream())))
+
+
+def rlt_state_destroy(state) -> None:
+    _check(load().rlt_state_destroy(state))
+
+
+def rlt_state_bytes(state) -> list:
+    out = (ctypes.c_int64 * 6)()
+    _check(load().rlt_state_bytes(state, out))
+    return list(out)
+
+
+def rlt_state_positions(state) -> tuple:
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check(load().rlt_state_positions(state, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def rlt_state_block_steps(state) -> int:
+    out = ctypes.c_int64()
+    _check(load().rlt_state_block_steps(state, ctypes.byref(out)))
+    return out.value
+
+
+def rlt_set_scan_mode(model, mode: int) -> None:
+    _check(load().rlt_set_scan_mode(model, mode))
+
+
+def rlt_encode(model, state, tokens: torch.Tensor) -> None:
+    assert tokens.dtype == torch.int32 and tokens.dim() == 2
+    _check(load().rlt_encode(model, state, _ptr(tokens), tokens.shape[1], ctypes.c_void_p(_stream())))
+
+
+def rlt_decode_scan(model, state, T: int, logits=None, next_logprob=None, next_tokens=None, s_out=None) -> None:
+    _check(load().rlt_decode_scan(model, state, T, _ptr(logits), _ptr(next_logprob), _ptr(next_tokens),
+                                  _ptr(s_out), ctypes.c_void_p(_stream())))
+
+
+def rlt_step(model, state, tokens: torch.Tensor, logits: torch.Tensor) -> None:
+    assert tokens.dtype == torch.int32 and tokens.dim() == 1
+    _check(load().rlt_step(model, state, _ptr(tokens), _ptr(logits), ctypes.c_void_p(_stream())))
+
+
+def rlt_replay(model, state, tokens: torch.Tensor, logprob: torch.Tensor, s_out=None) -> None:
+    assert tokens.dtype == torch.int32 and tokens.dim() == 2
+    _check(load().rlt_replay(model, state, _ptr(tokens), tokens.shape[1], _ptr(logprob), _ptr(s_out),
+                             ctypes.c_void_p(_stream())))
+
+
+# ----------------------------------------------------------------- convenience
+class Model:
+    """Owns one rlt_model and frees it on close()."""
+
+    def __init__(self, cfg: synth.Config, params: Dict[str, np.ndarray], device="cuda"):
+        self.cfg = cfg
+        self.device = device
+        self.h = rlt_create(cfg, params, device)
+        self.states = []
+
+    def state(self, batch: int, max_len: int, keep_encoder_cache: bool = True):
+        s = rlt_state_create(self.h, batch, max_len, keep_encoder_cache)
+        self.states.append(s)
+        return s
+
+    def replay(self, state, tokens: torch.Tensor, want_s: bool = False):
+        B, T = tokens.shape
+        lp = torch.empty((B, T - 1), dtype=torch.float32, device=self.device)
+        s = torch.empty((B, T, self.cfg.d), dtype=torch.float32, device=self.device) if want_s else None
+        rlt_replay(self.h, state, tokens, lp, s)
+        return lp, s
+
+    def prefill(self, state, tokens: torch.Tensor, want_logits=True, want_s=False):
+        B, T = tokens.shape
+        rlt_encode(self.h, state, tokens)
+        lg = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=self.device) if want_logits else None
+        s = torch.empty((B, T, self.cfg.d), dtype=torch.float32, device=self.device) if want_s else None
+        rlt_decode_scan(self.h, state, T, logits=lg, s_out=s)
+        return lg, s
+
+    def step(self, state, tok: torch.Tensor):
+        lg = torch.empty((tok.shape[0], self.cfg.vocab), dtype=torch.float32, device=self.device)
+        rlt_step(self.h, state, tok, lg)
+        return lg
+
+    def close(self):
+        for s in self.states:
+            rlt_state_destroy(s)
+        self.states = []
+        if self.h is not None:
+            rlt_destroy(self.h)
+            self.h = None

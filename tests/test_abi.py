@@ -1,0 +1,89 @@
+"""The C-ABI library loads, exports every function include/rlt.h declares, and
+rejects invalid arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from recurrent_looped_transformer_amd import rlt, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlt.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlt_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rlt.LIB_PATH):
+        pytest.fail("librlt.so is not built (run python -m recurrent_looped_transformer_amd.build)")
+    return rlt.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["rlt_create", "rlt_destroy", "rlt_state_create", "rlt_state_reset", "rlt_state_destroy",
+              "rlt_encode", "rlt_decode_scan", "rlt_step", "rlt_replay", "rlt_status_string"]:
+        assert n in names
+    assert sorted(rlt.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", rlt.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rlt_[a-z_]+)\b", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.rlt_status_string(0) == b"ok"
+    assert lib.rlt_status_string(-5) == b"stale state"
+    assert lib.rlt_status_string(-4) == b"capacity exceeded"
+
+
+def _create(lib, cfg, tensors=None, n=0):
+    c = rlt.config_struct(cfg)
+    out = ctypes.c_void_p()
+    return lib.rlt_create(ctypes.byref(c), tensors, n, None, ctypes.byref(out)), out
+
+
+def test_config_validation_on_host(lib):
+    base = synth.CONFIGS["tiny_fp32"]
+    assert _create(lib, base.replace(groups=3))[0] == -2          # G not in {1, L_D}
+    assert _create(lib, base.replace(d_head=15, n_heads=4))[0] in (-1, -2)
+    assert _create(lib, base.replace(window=0))[0] == -1
+    assert _create(lib, base.replace(chunk=2))[0] == -1           # chunk only for RLT-2
+    assert _create(lib, base.replace(share=True, L_E=3))[0] == -2
+    code, out = _create(lib, base)                                 # valid config, no weights
+    assert code == -1 and b"missing weight" in lib.rlt_last_error()
+    assert out.value is None
+
+
+def test_weight_validation_on_host(lib):
+    cfg = synth.CONFIGS["tiny_fp32"]
+    names = synth.manifest(cfg)
+    arr = (rlt.rlt_tensor * len(names))()
+    for i, (nm, shp) in enumerate(names):
+        arr[i] = rlt.rlt_tensor(nm.encode(), 16, 1)                  # wrong sizes (fake pointer, never read)
+    code, _ = _create(lib, cfg, arr, len(names))
+    assert code == -1 and b"wrong size" in lib.rlt_last_error()
+    arr[0] = rlt.rlt_tensor(b"no.such.weight", 16, 1)
+    code, _ = _create(lib, cfg, arr, len(names))
+    assert code == -1 and b"unknown weight" in lib.rlt_last_error()
+
+
+def test_null_arguments(lib):
+    assert lib.rlt_encode(None, None, None, 1, None) == -1
+    assert lib.rlt_decode_scan(None, None, 1, None, None, None, None, None) == -1
+    assert lib.rlt_step(None, None, None, None, None) == -1
+    assert lib.rlt_replay(None, None, None, 4, None, None, None) == -1
+    assert lib.rlt_state_destroy(None) == -1
+    assert lib.rlt_destroy(None) == -1
+    assert lib.rlt_set_scan_mode(None, 0) == -1
