@@ -1,0 +1,201 @@
+"""Throughput of the RLT hot path on one MI355X.
+
+A step is one current-policy replay of a batch of synthetic sequences: the
+token-parallel causal encode with its memory projection, then the sequential
+scan of decoder transitions over every position, then the batched readout of
+log p(x_{t+1} | x_<=t). The default workload is the algorithmic-task shape
+(vocab 8, d 512, 8x64 heads, 4+4 blocks, SwiGLU 2048, W 32, G 1, RLT-1) at
+batch 64 x 257 positions (BOS + 256 tokens from {0,1}).
+
+Prints one JSON line: value = decoder transitions per second of the whole step
+(B*T transitions / step time), plus encoder tokens/s and decode-scan
+transitions/s from HIP events, the roofline of the scan (algorithmic bytes of
+the recurrence / measured time vs 8 TB/s HBM), and the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decoder transitions/sec at batch B + encoder tok/s; % of HBM/MFMA roofline"
+
+
+def scan_bytes(cfg, B: int, T: int, t_start: int = 0) -> float:
+    """Algorithmic HBM bytes of decoder transitions t_start+1 .. t_start+T for B sequences.
+
+    Per transition at position t (batched): the decoder weights once per step
+    (e * P_dec with P_dec = L_D(6 d hd-sized blocks + 3 d f + 3 d) + 3 d^2 + 3 d + V d + d),
+    each layer's SWA window reads (min(t, W) - 1 past positions), each layer's
+    read of the memory prefix 1..t of its group, ring writes, e_t in, s in/out
+    and the fp32 logits out.
+    """
+    e = 2 if cfg.dtype == "bf16" else 4
+    d, f, V, L, W, hd = cfg.d, cfg.ffn, cfg.vocab, cfg.L_D, cfg.window, cfg.hd
+    P_dec = L * (4 * d * hd + 2 * d * hd + 3 * d * f + 3 * d) + 3 * d * d + 3 * d + V * d + d
+    total = 0.0
+    for t in range(t_start + 1, t_start + T + 1):
+        total += e * P_dec
+        total += B * L * (min(t, W) - 1) * 2 * hd * e
+        total += B * L * t * 2 * hd * e
+        total += B * (L * 2 * hd * e + d * 4 + 2 * d * 4 + V * 4)
+    return total
+
+
+def encoder_flops(cfg, B: int, T: int) -> float:
+    d, f, hd, L = cfg.d, cfg.ffn, cfg.hd, cfg.L_E
+    G = cfg.groups if cfg.L_D > 0 else 0
+    per_tok = 2 * (L * (4 * d * hd + 3 * d * f) + G * 2 * d * hd + (d * d if cfg.variant != 0 else 0))
+    attn = B * L * 4 * hd * T * (T + 1) / 2
+    return B * T * per_tok + attn
+
+
+def cpu_baseline(cfg, P, tokens, sample_B: int):
+    from threadpoolctl import threadpool_info
+    from oracle import Oracle
+    x = tokens[:sample_B]
+    o = Oracle(cfg, P)
+    t0 = time.perf_counter()
+    o.replay(x)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": x.shape[0] * x.shape[1] / dt, "unit": "transitions/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{x.shape[0]} of {tokens.shape[0]} sequences x {x.shape[1]} positions, full replay "
+                      f"(encode + scan + log-probs), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="algo_bf16")
+    ap.add_argument("--batch", type=int, default=0)
+    ap.add_argument("--seq-len", type=int, default=0)
+    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--scan-mode", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the RLT scan shards over independent sequences with no "
+              "exchange during the scan, and this build runs on a single MI355X (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens
+
+    cfg = CONFIGS[args.config]
+    if args.batch:
+        cfg = cfg.replace(batch=args.batch)
+    if args.seq_len:
+        cfg = cfg.replace(seq_len=args.seq_len)
+    if args.variant >= 0:
+        cfg = cfg.replace(variant=args.variant, chunk=cfg.chunk if args.variant == 2 else 1)
+    B, T = cfg.batch, cfg.seq_len
+    P = make_params(cfg)
+    tokens = make_tokens(cfg, length=T)
+    nxt = np.concatenate([tokens[:, 1:], np.full((B, 1), -1, np.int32)], axis=1)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    x = torch.as_tensor(tokens).to(dev)
+    nx = torch.as_tensor(np.ascontiguousarray(nxt)).to(dev)
+    lp = torch.empty((B, T), dtype=torch.float32, device=dev)
+    model = rlt.Model(cfg, P)
+    if args.scan_mode:
+        rlt.rlt_set_scan_mode(model.h, args.scan_mode)
+    st = model.state(B, T, keep_encoder_cache=False)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        rlt.rlt_state_reset(model.h, st)
+        if evs: evs[0].record(stream)
+        rlt.rlt_encode(model.h, st, x)
+        if evs: evs[1].record(stream)
+        rlt.rlt_decode_scan(model.h, st, T, next_logprob=lp, next_tokens=nx)
+        if evs: evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = B * T / (ms_per_step / 1e3)
+
+    sb = scan_bytes(cfg, B, T)
+    achieved = sb / (scan_ms / 1e3) / 1e9
+    ef = encoder_flops(cfg, B, T)
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_scan_{cfg.name}.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            if rec.get("scan_mode") == args.scan_mode and rec.get("B") == B and rec.get("T") == T and \
+                    rec.get("lib_sha") == rlt_lib_sha():
+                traffic = rec.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "transitions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} replay (encode + decoder scan + log-probs), "
+                               f"RLT-{cfg.variant} B={B} T={T}",
+                   "batch": B, "seq_len": T, "d": cfg.d, "L_E": cfg.L_E, "L_D": cfg.L_D,
+                   "window": cfg.window, "groups": cfg.groups, "vocab": cfg.vocab,
+                   "variant": f"RLT-{cfg.variant}", "chunk": cfg.chunk, "scan_mode": args.scan_mode},
+        "encoder_tok_s": B * T / (enc_ms / 1e3),
+        "encoder_ms": enc_ms,
+        "encoder_tflops": ef / (enc_ms / 1e3) / 1e12,
+        "decode_transitions_s": B * T / (scan_ms / 1e3),
+        "decode_scan_ms": scan_ms,
+        "roofline": {"bound": "hbm", "kernel": "decoder scan (all T transitions, one launch sequence)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": sb},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, P, tokens, min(args.cpu_sample, B))
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
+def rlt_lib_sha() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "recurrent_looped_transformer_amd", "librlt.so")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else ""
+
+
+if __name__ == "__main__":
+    main()

@@ -167,8 +167,13 @@ int rlt_replay(rlt_model* m, rlt_state* state, const int32_t* tokens, int T, flo
                float* s_out, hipStream_t stream);
 
 /* Scan driver for the decoder transitions: 0 = automatic, 1 = one launch sequence
- * per position (stream-ordered), 2 = persistent cooperative kernel over all
- * positions (configurations it supports). */
+ * per position (stream-ordered), 2 = persistent cooperative kernel with the
+ * automatic work split, 3 = persistent with every workgroup on all sequences,
+ * 4/5/6 = persistent with 1/2/4 workgroups per CU, the workgroups of each XCD
+ * and dispatch round forming an independent group that owns batch/8, batch/16 or
+ * batch/32 sequences (falling back to fewer groups when the batch does not
+ * divide). Configurations the persistent kernel does not cover (fp32, d_head
+ * other than 64 or 128) always use mode 1. */
 int rlt_set_scan_mode(rlt_model* m, int mode);
 
 /* Number of dependent decoder block passes issued since the state was reset

@@ -72,6 +72,8 @@ void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int 
 void rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
 // dst[rmap_d(m), :] = src[rmap_s(m), :] (fp32 rows)
 void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int d, hipStream_t st);
+// p[0 .. n) = 0 (32-bit words), a kernel rather than a memset so the call is capture-safe
+void fill_zero_u32(void* p, int64_t n, hipStream_t st);
 // s[b, :] = s0 (fp32) for b < B; used for H_0 and the RLT-2 register
 void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st);
 // out[om(r)] = L[tok[tm(r)]] - logsumexp(L) with L = logits row lm(r); tok < 0 writes 0

@@ -97,6 +97,16 @@ void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int
   hipLaunchKernelGGL(copy_rows_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, sm, dst, dm, rows, d);
 }
 
+__global__ void fill_zero_k(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+void fill_zero_u32(void* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(fill_zero_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (uint32_t*)p, n);
+}
+
 __global__ void broadcast_row_k(const float* __restrict__ s0, float* __restrict__ s, int B, int d) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)B * d) return;

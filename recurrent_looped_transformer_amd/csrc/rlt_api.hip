@@ -14,8 +14,9 @@
 #include <string>
 #include <vector>
 
-#include "../../include/rlt.h"
+#include "rlt.h"
 #include "ops.hpp"
+#include "scan.hpp"
 
 using namespace rlt;
 
@@ -122,6 +123,18 @@ struct rlt_state {
   void *ekv_k = nullptr, *ekv_v = nullptr;   // attention keys when no encoder cache is kept
   int32_t* toks = nullptr;                   // [B][Tm] shifted next tokens (replay)
   float* lp = nullptr;                       // [B][Tm] log-probabilities (replay)
+  // persistent scan (bf16 configurations it supports)
+  bool scan_ok = false;
+  float* pz[2] = {nullptr, nullptr};
+  void* pzb[2] = {nullptr, nullptr};
+  float* pssp[2] = {nullptr, nullptr};
+  void *pq = nullptr, *pao = nullptr, *phid = nullptr, *rhob = nullptr;
+  float* rhoss = nullptr;
+  float* sall = nullptr;                     // [B][Tm][d] s_t of every position
+  unsigned* bar = nullptr;
+  rlt::ScanLayer* layers_dev = nullptr;
+  int* abort_host = nullptr;                 // pinned copy of the scan's abort word
+  int scan_grid = 0;
 };
 
 namespace {
@@ -323,6 +336,8 @@ void check_state(rlt_model* m, rlt_state* s) {
   if (!m || !s) fail(RLT_ERR_INVALID_ARG, "null model or state");
   if (s->m != m) fail(RLT_ERR_INVALID_ARG, "state belongs to another model");
   if (s->version != m->version) fail(RLT_ERR_STALE_STATE, "state was built under older weights; reset it");
+  if (s->abort_host && *(volatile int*)s->abort_host)
+    fail(RLT_ERR_HIP, "a persistent scan on this state timed out in a grid barrier; its results are invalid");
 }
 
 // ------------------------------------------------------------------ encode
@@ -465,18 +480,20 @@ struct ScanOut {
 };
 
 // Readout of buffered positions c0 .. c0+n-1 (scan-relative) held in sbuf [B][kReadoutPositions][d].
-void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st) {
+void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st, const float* src = nullptr,
+             int64_t src_sb = 0) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, V = c.vocab, B = s->B;
   const int rows = B * n;
-  RowMap sm; sm.tn = n; sm.sb = (int64_t)kReadoutPositions * d; sm.st = d;
+  RowMap sm; sm.tn = n; sm.sb = src ? src_sb : (int64_t)kReadoutPositions * d; sm.st = d;
+  if (!src) src = s->sbuf;
   if (o.s_out) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * d; dm.st = d;
-    copy_rows(s->sbuf, sm, o.s_out + (int64_t)c0 * d, dm, rows, d, st);
+    copy_rows(src, sm, o.s_out + (int64_t)c0 * d, dm, rows, d, st);
   }
   if (!o.logits && !o.lp) return;
-  rmsnorm(dt, s->sbuf, sm, m->nO, s->xr, d, rows, d, c.rms_eps, st);
+  rmsnorm(dt, src, sm, m->nO, s->xr, d, rows, d, c.rms_eps, st);
   EpArgs a; a.out = s->lbuf; a.ldo = V;
   gemm(dt, Ep::StoreF32, a, s->xr, d, m->wout, rows, V, d, st);
   if (o.logits) {
@@ -494,7 +511,74 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
   }
 }
 
+// Work split of the persistent scan: 1 group of every block (grid-wide barriers), or
+// 8 * k groups (k blocks per CU, each group on one XCD owning batch / (8k) sequences).
+// Groups pay for streaming the step's decoder weights once per group (from the 256 MB
+// last-level cache), so they are chosen only when those weights are small.
+int scan_groups(rlt_model* m, rlt_state* s) {
+  const int B = s->B;
+  switch (m->scan_mode) {
+    case 3: return 1;
+    case 4: return B % 8 == 0 ? 8 : 1;
+    case 5: return B % 16 == 0 ? 16 : (B % 8 == 0 ? 8 : 1);
+    case 6: return B % 32 == 0 ? 32 : (B % 16 == 0 ? 16 : (B % 8 == 0 ? 8 : 1));
+    default: break;
+  }
+  const rlt_config& c = m->cfg;
+  const int64_t w = (int64_t)c.L_D * (4 * (int64_t)m->hd * c.d + 2 * (int64_t)c.d * m->hd + 3 * (int64_t)c.d * c.ffn) +
+                    2 * (int64_t)c.d * c.d;
+  if (w * (int64_t)m->esz > (int64_t)96 << 20) return 1;
+  if (B % 16 == 0) return 16;
+  return B % 8 == 0 ? 8 : 1;
+}
+
+// Automatic mode runs one launch sequence per position: on MI355X at the algorithmic-task
+// shape it measured faster than the persistent kernel, whose phases are bound by the
+// latency of reading activations just written by other CUs.
+bool use_persistent(rlt_model* m, rlt_state* s) {
+  return s->scan_ok && m->scan_mode >= 2;
+}
+
+void persistent_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const int d = c.d, start = s->n_dec;
+  ScanParams p{};
+  p.B = s->B; p.d = d; p.hd = m->hd; p.H = c.n_heads; p.dh = c.d_head; p.f = c.ffn; p.L = c.L_D;
+  p.W = c.window; p.R = s->R; p.Tm = s->Tm; p.variant = (int)c.variant; p.chunk = c.chunk; p.P = s->P;
+  p.ngroups = scan_groups(m, s);
+  p.cpx = scan_cus() / 8;
+  p.alpha = c.alpha; p.eps = c.rms_eps; p.scale = 1.f / std::sqrt((float)c.d_head);
+  p.wsr = (const bf16_t*)m->wsr; p.ns = m->ns;
+  p.g_first = c.L_D > 0 ? m->dec[0].n1 : m->ns;
+  p.e = s->e; p.gpre = s->gpre; p.s = s->s; p.rho = s->rho;
+  p.rhob = (bf16_t*)s->rhob; p.rhoss = s->rhoss; p.rope = s->rope;
+  for (int i = 0; i < 2; ++i) { p.z[i] = s->pz[i]; p.zb[i] = (bf16_t*)s->pzb[i]; p.ssp[i] = s->pssp[i]; }
+  p.q = (bf16_t*)s->pq; p.ao = (bf16_t*)s->pao; p.hid = (bf16_t*)s->phid;
+  p.sall = s->sall; p.start = start; p.T = T; p.bar = s->bar; p.layer = s->layers_dev;
+  fill_zero_u32(s->bar, kBarWords, st);
+  int grid = 0;
+  hipError_t e = launch_scan(p, &grid, st);
+  if (e != hipSuccess) fail(RLT_ERR_HIP, std::string("persistent scan launch: ") + hipGetErrorString(e));
+  s->scan_grid = grid;
+  HIPCHK(hipMemcpyAsync(s->abort_host, s->bar + 64 * 10, sizeof(int), hipMemcpyDeviceToHost, st));
+  s->block_steps += (int64_t)c.L_D * (c.variant == RLT_V1 ? T
+                                       : c.variant == RLT_V2 ? ((start + T - 1) / c.chunk - start / c.chunk + 1)
+                                                             : (T + s->P - 1) / s->P);
+  s->n_dec = start + T;
+  if (o.logits || o.lp || o.s_out) {
+    for (int c0 = 0; c0 < T; c0 += kReadoutPositions) {
+      const int n = std::min(kReadoutPositions, T - c0);
+      readout(m, s, c0, n, o, st, s->sall + (int64_t)(start + c0) * d, (int64_t)s->Tm * d);
+    }
+  }
+  check_launch();
+}
+
 void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
+  if (use_persistent(m, s)) {
+    persistent_scan(m, s, T, o, st);
+    return;
+  }
   const rlt_config& c = m->cfg;
   const int d = c.d;
   const int start = s->n_dec;
@@ -651,6 +735,41 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       }
       s->toks = (int32_t*)dev_alloc(s, sizeof(int32_t) * B * Tm, 5);
       s->lp = (float*)dev_alloc(s, sizeof(float) * B * Tm, 5);
+      if (m->dt == Dt::BF16 && scan_supported((int)dh, (int)rows, (int)d, (int)hd, (int)f, (int)Tm, c.L_D)) {
+        s->scan_ok = true;
+        for (int i = 0; i < 2; ++i) {
+          s->pz[i] = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
+          s->pzb[i] = dev_alloc(s, rows * d * e, 5);
+          s->pssp[i] = (float*)dev_alloc(s, sizeof(float) * rows * (d / 8), 5);
+        }
+        s->pq = dev_alloc(s, rows * hd * e, 5);
+        s->pao = dev_alloc(s, rows * hd * e, 5);
+        s->phid = dev_alloc(s, rows * f * e, 5);
+        s->rhob = dev_alloc(s, B * d * e, 3);
+        s->rhoss = (float*)dev_alloc(s, sizeof(float) * B * (d / 16), 3);
+        s->sall = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4);
+        s->bar = (unsigned*)dev_alloc(s, sizeof(unsigned) * kBarWords, 5);
+        std::vector<ScanLayer> Ls(c.L_D);
+        for (int l = 0; l < c.L_D; ++l) {
+          const LayerW& L = m->dec[l];
+          ScanLayer& y = Ls[l];
+          y.wqkv = (const bf16_t*)L.wqkv; y.wo = (const bf16_t*)L.wo; y.xq = (const bf16_t*)L.xq;
+          y.xo = (const bf16_t*)L.xo; y.w13 = (const bf16_t*)L.w13; y.w2 = (const bf16_t*)L.w2;
+          y.g1 = L.n1; y.g2 = L.n2; y.g3 = L.n3;
+          y.gnext = l + 1 < c.L_D ? m->dec[l + 1].n1 : (c.variant == RLT_V0 ? m->nO : m->ns);
+          const int g = c.groups == 1 ? 0 : l;
+          y.mk = (const bf16_t*)((char*)s->mem_k + (int64_t)g * B * H * Tm * dh * e);
+          y.mv = (const bf16_t*)((char*)s->mem_v + (int64_t)g * B * H * Tm * dh * e);
+          y.rk = (bf16_t*)((char*)s->ring_k + (int64_t)l * B * H * s->R * dh * e);
+          y.rv = (bf16_t*)((char*)s->ring_v + (int64_t)l * B * H * s->R * dh * e);
+        }
+        if (c.L_D > 0) {
+          s->layers_dev = (ScanLayer*)dev_alloc(s, sizeof(ScanLayer) * c.L_D, 5);
+          HIPCHK(hipMemcpy(s->layers_dev, Ls.data(), sizeof(ScanLayer) * c.L_D, hipMemcpyHostToDevice));
+        }
+        HIPCHK(hipHostMalloc((void**)&s->abort_host, sizeof(int), hipHostMallocDefault));
+        *s->abort_host = 0;
+      }
       rope_table(s->rope, max_len + 1, (int)dh, c.rope_base, stream);
       check_launch();
       m->n_states += 1;
@@ -660,6 +779,7 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
     } catch (...) {
       if (*out) { m->n_states -= 1; *out = nullptr; }
       for (void* p : s->allocs) (void)hipFree(p);
+      if (s->abort_host) (void)hipHostFree(s->abort_host);
       delete s;
       throw;
     }
@@ -688,6 +808,7 @@ int rlt_state_destroy(rlt_state* s) {
   return guarded([&] {
     if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
     for (void* p : s->allocs) HIPCHK(hipFree(p));
+    if (s->abort_host) HIPCHK(hipHostFree(s->abort_host));
     s->m->n_states -= 1;
     delete s;
   });
@@ -718,7 +839,7 @@ int rlt_state_block_steps(const rlt_state* s, int64_t* out) {
 int rlt_set_scan_mode(rlt_model* m, int mode) {
   return guarded([&] {
     if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
-    if (mode < 0 || mode > 2) fail(RLT_ERR_INVALID_ARG, "scan mode must be 0, 1 or 2");
+    if (mode < 0 || mode > 6) fail(RLT_ERR_INVALID_ARG, "scan mode must be 0..6");
     m->scan_mode = mode;
   });
 }

@@ -26,6 +26,16 @@ def gpu():
     yield
 
 
+_ORACLE_CACHE = {}
+
+
+def oracle_replay(cfg, P, x, dtype=np.float32):
+    key = (cfg, x.tobytes(), np.dtype(dtype).str)
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = Oracle(cfg, P, dtype).replay(x)
+    return _ORACLE_CACHE[key]
+
+
 def dev(a):
     return torch.as_tensor(np.ascontiguousarray(a)).cuda()
 
@@ -57,11 +67,12 @@ def check_logits(cfg, name, gpu, ref):
         assert agree >= 0.999
 
 
-def gpu_prefill(cfg, P, x, steps_from=None, keep_enc=True):
+def gpu_prefill(cfg, P, x, steps_from=None, keep_enc=True, scan_mode=0):
     """Prefill x[:, :p] then consume the rest one token at a time (p = steps_from or all)."""
     B, T = x.shape
     p = T if steps_from is None else steps_from
     m = rlt.Model(cfg, P)
+    rlt.rlt_set_scan_mode(m.h, scan_mode)
     try:
         st = m.state(B, T, keep_encoder_cache=keep_enc)
         xt = dev(x)
@@ -76,9 +87,10 @@ def gpu_prefill(cfg, P, x, steps_from=None, keep_enc=True):
         m.close()
 
 
-def gpu_replay(cfg, P, x):
+def gpu_replay(cfg, P, x, scan_mode=0):
     B, T = x.shape
     m = rlt.Model(cfg, P)
+    rlt.rlt_set_scan_mode(m.h, scan_mode)
     try:
         st = m.state(B, T, keep_encoder_cache=False)
         lp, s = m.replay(st, dev(x), want_s=True)
@@ -159,27 +171,50 @@ def test_block_step_counts():
         assert steps == expect, (kw, steps)
 
 
+# per-position launches; persistent grid-wide; persistent per-XCD groups with 1, 2, 4 blocks per CU
+SCAN_MODES = [1, 3, 4, 5, 6]
+
+
+@pytest.mark.parametrize("scan_mode", SCAN_MODES)
 @pytest.mark.parametrize("variant", [V1, V0])
-def test_algo_bf16_reduced(variant):
-    cfg = ALGO.replace(variant=variant, batch=4, seq_len=40)
+def test_algo_bf16_reduced(variant, scan_mode):
+    cfg = ALGO.replace(variant=variant, batch=32, seq_len=40)
     P = make_params(cfg)
     x = make_tokens(cfg)
-    print(f"[case] algo_bf16 variant={variant} B=4 T=40", flush=True)
-    ref_lp, ref_logits, ref_s = Oracle(cfg, P, np.float32).replay(x)
-    logits, s, _ = gpu_prefill(cfg, P, x, steps_from=30)
-    check_logits(cfg, f"algo v{variant} logits", logits, ref_logits)
-    lp, _ = gpu_replay(cfg, P, x)
-    assert report(f"algo v{variant} logprob", lp, ref_lp) <= 2e-2
+    print(f"[case] algo_bf16 variant={variant} B=32 T=40 scan_mode={scan_mode}", flush=True)
+    ref_lp, ref_logits, ref_s = oracle_replay(cfg, P, x)
+    logits, s, _ = gpu_prefill(cfg, P, x, steps_from=30, scan_mode=scan_mode)
+    check_logits(cfg, f"algo v{variant} m{scan_mode} logits", logits, ref_logits)
+    lp, _ = gpu_replay(cfg, P, x, scan_mode=scan_mode)
+    assert report(f"algo v{variant} m{scan_mode} logprob", lp, ref_lp) <= 2e-2
+
+
+@pytest.mark.parametrize("scan_mode", SCAN_MODES)
+@pytest.mark.parametrize("kw", [dict(variant=V2, chunk=4), dict(variant=V2, chunk=3), dict(L_D=0),
+                                dict(groups=4), dict(share=True, L_E=4), dict(window=1), dict(batch=3),
+                                dict(variant=V2, chunk=3, batch=32)],
+                         ids=["rlt2_k4", "rlt2_k3", "no_decoder", "groups_LD", "shared", "window1", "batch3",
+                              "rlt2_k3_b32"])
+def test_bf16_variants_small(kw, scan_mode):
+    cfg = ALGO.replace(**{"batch": 8, "seq_len": 21, **kw})
+    P = make_params(cfg)
+    x = make_tokens(cfg)
+    print(f"[case] algo_bf16 {kw} B={x.shape[0]} T=21 scan_mode={scan_mode}", flush=True)
+    _, ref_logits, ref_s = oracle_replay(cfg, P, x)
+    logits, s, steps = gpu_prefill(cfg, P, x, steps_from=13, scan_mode=scan_mode)
+    check_logits(cfg, f"bf16 {kw} m{scan_mode} logits", logits, ref_logits)
+    assert report(f"bf16 {kw} m{scan_mode} s", s, ref_s[:, :13]) <= 5e-2
 
 
 def test_rlt2_bf16_reduced():
-    cfg = CONFIGS["rlt2_bf16"].replace(batch=6, seq_len=24)
+    cfg = CONFIGS["rlt2_bf16"].replace(batch=16, seq_len=24)
     P = make_params(cfg)
     x = make_tokens(cfg)
-    print("[case] rlt2_bf16 B=6 T=24", flush=True)
-    _, ref_logits, _ = Oracle(cfg, P, np.float32).replay(x)
-    logits, _, _ = gpu_prefill(cfg, P, x)
-    check_logits(cfg, "rlt2 bf16 logits", logits, ref_logits)
+    print("[case] rlt2_bf16 B=16 T=24", flush=True)
+    _, ref_logits, _ = oracle_replay(cfg, P, x)
+    for mode in SCAN_MODES:
+        logits, _, _ = gpu_prefill(cfg, P, x, scan_mode=mode)
+        check_logits(cfg, f"rlt2 bf16 m{mode} logits", logits, ref_logits)
 
 
 # ------------------------------------------------------------------ error paths
