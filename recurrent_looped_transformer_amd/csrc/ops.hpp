@@ -102,5 +102,7 @@ struct AttnArgs {
   float scale = 1.f;
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
+// bf16 many-query attention with MFMA (dh 64 or 128); returns false when the shape is not covered
+bool attn_prefill(const AttnArgs& a, hipStream_t st);
 
 }  // namespace rlt

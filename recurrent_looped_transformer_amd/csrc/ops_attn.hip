@@ -116,3 +116,141 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 }
 
 }  // namespace rlt
+
+// ====================================================================== prefill
+// Causal (optionally windowed) attention of many queries per (sequence, head) with
+// bf16 MFMA, flash style: the encoder's token-parallel self-attention
+// (greeksharifa summary §2.2: each encoder layer processes the given positions
+// together under a causal mask).
+//
+// Block = 4 waves = 64 queries (16 per wave) of one (sequence, head); keys and
+// values stream through LDS in tiles of 64 positions (V stored transposed). Each
+// wave computes S^T = K Q^T with 16x16x32 MFMAs: lane l then holds the scores of
+// keys 4g..4g+3 (g = l / 16) of query l % 16, which is exactly the B operand layout
+// of the 16x16x16 MFMA used for O^T += V^T P^T, so probabilities never leave
+// registers. Softmax statistics are fp32 per query column, online over key tiles.
+namespace rlt {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x16(const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a), __builtin_bit_cast(bf16x4_t, b), c,
+                                                   0, 0, 0);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8;
+  __shared__ __align__(16) uint4 sK[BK][KP];
+  __shared__ __align__(16) bf16_t sVt[DH][VP];
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int g = lane >> 4, c = lane & 15;
+  const int myq = qb * 64 + wave * 16 + c;             // query index within this call
+  const bool qvalid = myq < a.nq;
+  const int qpos = a.pos0 + 1 + myq;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq + h * DH;
+  uint4 qf[DH / 32];
+#pragma unroll
+  for (int kc = 0; kc < DH / 32; ++kc) qf[kc] = *reinterpret_cast<const uint4*>(Q + kc * 32 + g * 8);
+  f32x4 o[DH / 16];
+#pragma unroll
+  for (int i = 0; i < DH / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qlast = min(a.nq, qb * 64 + 64);          // queries of this block: [qb*64, qlast)
+  const int kmax = a.pos0 + qlast;                     // last key position any query here needs
+  const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * 64 - a.window + 1) : 1;
+  const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+  const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+  for (int k0 = kmin; k0 <= kmax; k0 += BK) {
+    __syncthreads();
+    for (int idx = tid; idx < BK * (DH / 8); idx += 256) {
+      const int j = idx / (DH / 8), part = idx % (DH / 8);
+      const int p = k0 + j;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (p <= kmax) {
+        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
+        kv = *reinterpret_cast<const uint4*>(Kb + (int64_t)slot * DH + part * 8);
+        vv = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + part * 8);
+      }
+      sK[j][part] = kv;
+      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sVt[part * 8 + 2 * e][j] = (bf16_t)(w[e] & 0xffffu);
+        sVt[part * 8 + 2 * e + 1][j] = (bf16_t)(w[e] >> 16);
+      }
+    }
+    __syncthreads();
+    float s[4][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32(sK[st * 16 + c][kc * 4 + g], qf[kc], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kp = k0 + st * 16 + 4 * g + i;
+        const bool ok = qvalid && kp <= qpos && kp <= kmax && (a.window <= 0 || kp > qpos - a.window);
+        s[st][i] = ok ? acc[i] * a.scale : -INFINITY;
+        tmax = fmaxf(tmax, s[st][i]);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
+    const float m_new = fmaxf(m_run, tmax);
+    // branch-free: a column with nothing visible yet keeps l = 0 and o = 0 (exp(-inf) = 0)
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = __expf(m_run - m_use);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) o[i] *= corr;
+    float lsum = 0.f;
+    uint2 pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __expf(s[st][i] - m_use);
+        lsum += pv[i];
+      }
+      pb[st].x = (uint32_t)f2bf(pv[0]) | ((uint32_t)f2bf(pv[1]) << 16);
+      pb[st].y = (uint32_t)f2bf(pv[2]) | ((uint32_t)f2bf(pv[3]) << 16);
+    }
+    lsum += __shfl_xor(lsum, 16, WAVE);
+    lsum += __shfl_xor(lsum, 32, WAVE);
+    l_run += lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int db = 0; db < DH / 16; ++db) {
+        const uint2 av = *reinterpret_cast<const uint2*>(&sVt[db * 16 + c][st * 16 + 4 * g]);
+        o[db] = mfma16x16x16(av, pb[st], o[db]);
+      }
+    }
+  }
+  if (qvalid) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + ((int64_t)b * a.nq + myq) * a.ldo + h * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) {
+      uint2 w;
+      w.x = (uint32_t)f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
+      w.y = (uint32_t)f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(out + db * 16 + 4 * g) = w;
+    }
+  }
+}
+
+bool attn_prefill(const AttnArgs& a, hipStream_t st) {
+  if (a.dh != 64 && a.dh != 128) return false;
+  const dim3 grid((a.nq + 63) / 64, a.H, a.B);
+  if (a.dh == 64) hipLaunchKernelGGL(flash_prefill_k<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(flash_prefill_k<128>, grid, dim3(256), 0, st, a);
+  return true;
+}
+
+}  // namespace rlt

@@ -376,7 +376,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = hd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
-      attn_decode(dt, at, st);
+      if (!(dt == Dt::BF16 && T >= 16 && attn_prefill(at, st))) attn_decode(dt, at, st);
       EpArgs r; r.resid = h; r.rmap = hm;
       gemm(dt, Ep::Residual, r, s->eao, hd, L.wo, rows, d, hd, st);
       rmsnorm(dt, h, hm, L.n2, s->exa, d, rows, d, c.rms_eps, st);
