@@ -1,0 +1,65 @@
+"""Write expected outputs of the CPU oracle for the full-size workloads.
+
+Calls only the oracle and the seeded input generators (no HIP code). Each file
+holds the oracle's replay outputs for the named workload:
+  logprob [B, T-1]  log p(x_{t+1} | x_<=t)
+  logits  [B, T, V] readout logits at every position (omitted for large V)
+  s_last  [B, d]    s_T
+The medium-LM file covers the first `--rows` sequences and `--len` positions of
+that workload's token stream (causality makes them independent of the rest).
+
+Usage: python tests/golden/make_golden.py algo_bf16 [rlt2_bf16 algo_bf16_rlt0 medium_lm ...]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from oracle import Oracle, V0  # noqa: E402
+from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens  # noqa: E402
+
+
+def workload(name: str, rows: int, length: int):
+    if name == "algo_bf16_rlt0":
+        cfg = CONFIGS["algo_bf16"].replace(variant=V0)
+    else:
+        cfg = CONFIGS[name]
+    if name in ("medium_lm", "paper_shared"):
+        x = make_tokens(cfg, length=cfg.seq_len + cfg.gen_len)[:rows, :length]
+        return cfg, np.ascontiguousarray(x), np.float32
+    return cfg, make_tokens(cfg, length=cfg.seq_len), np.float64
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("names", nargs="+")
+    ap.add_argument("--rows", type=int, default=2)
+    ap.add_argument("--len", type=int, default=32)
+    args = ap.parse_args()
+    for name in args.names:
+        cfg, x, dt = workload(name, args.rows, args.len)
+        P = make_params(cfg)
+        t0 = time.time()
+        lp, logits, s = Oracle(cfg, P, dt).replay(x)
+        out = {"tokens": x, "logprob": lp.astype(np.float32), "s_last": s[:, -1].astype(np.float32)}
+        if cfg.vocab <= 64:
+            out["logits"] = logits.astype(np.float32)
+        else:
+            out["logits_head"] = logits[:, :, :64].astype(np.float32)
+            out["argmax"] = np.argmax(logits, axis=-1).astype(np.int32)
+            out["logit_max"] = logits.max(axis=-1).astype(np.float32)
+        path = os.path.join(HERE, f"{name}.npz")
+        np.savez_compressed(path, **out)
+        print(f"{name}: B={x.shape[0]} T={x.shape[1]} oracle {time.time() - t0:.1f} s -> {path}", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,70 @@
+"""Full-size GPU parity against stored oracle outputs (tests/golden/*.npz, written by
+tests/golden/make_golden.py, which calls only the oracle and the seeded generators).
+
+The algorithmic-task shape (B 64 x T 257, RLT-1 and RLT-0) and the RLT-2 shape
+(B 128 x T 64, K_c 4, G = L_D) run at their full sizes, in the same launch
+configuration as the benchmark (automatic scan driver) and in the persistent modes.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import V0
+from recurrent_looped_transformer_amd import rlt
+from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    path = os.path.join(GOLDEN, f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} missing: run tests/golden/make_golden.py {name}")
+    return dict(np.load(path))
+
+
+def cfg_of(name):
+    return CONFIGS["algo_bf16"].replace(variant=V0) if name == "algo_bf16_rlt0" else CONFIGS[name]
+
+
+def run(cfg, tokens, scan_mode):
+    B, T = tokens.shape
+    m = rlt.Model(cfg, make_params(cfg))
+    rlt.rlt_set_scan_mode(m.h, scan_mode)
+    try:
+        st = m.state(B, T, keep_encoder_cache=False)
+        x = torch.as_tensor(tokens).cuda()
+        rlt.rlt_encode(m.h, st, x)
+        lg = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device="cuda")
+        s = torch.empty((B, T, cfg.d), dtype=torch.float32, device="cuda")
+        rlt.rlt_decode_scan(m.h, st, T, logits=lg, s_out=s)
+        lp, _ = m.replay(st, x)
+        torch.cuda.synchronize()
+        return lg.cpu().numpy(), s.cpu().numpy(), lp.cpu().numpy()
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("scan_mode", [0, 3, 4])
+@pytest.mark.parametrize("name", ["algo_bf16", "algo_bf16_rlt0", "rlt2_bf16"])
+def test_full_size_matches_oracle(name, scan_mode):
+    g = load(name)
+    cfg = cfg_of(name)
+    tokens = make_tokens(cfg, length=cfg.seq_len)
+    assert np.array_equal(tokens, g["tokens"]), "seeded token stream changed"
+    print(f"[case] {name} B={tokens.shape[0]} T={tokens.shape[1]} scan_mode={scan_mode}", flush=True)
+    logits, s, lp = run(cfg, tokens, scan_mode)
+    err = float(np.max(np.abs(logits - g["logits"])))
+    gi, ri = np.argmax(logits, -1), np.argmax(g["logits"], -1)
+    ref_at = np.take_along_axis(g["logits"], gi[..., None], -1)[..., 0]
+    agree = float(np.mean((gi == ri) | (ref_at >= g["logits"].max(-1) - 2 * err)))
+    lp_err = float(np.max(np.abs(lp - g["logprob"])))
+    s_err = float(np.max(np.abs(s[:, -1] - g["s_last"])))
+    print(f"[parity] {name} m{scan_mode}: logits max err {err:.3e}, argmax agreement {agree:.5f} "
+          f"(raw {np.mean(gi == ri):.5f}), logprob err {lp_err:.3e}, s_T err {s_err:.3e}", flush=True)
+    assert err <= 2e-2
+    assert agree >= 0.999
+    assert lp_err <= 2e-2
