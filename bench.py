@@ -86,7 +86,9 @@ def main():
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--scan-mode", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8)
+    ap.add_argument("--cpu-sample", type=int, default=32)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the RLT scan shards over independent sequences with no "
@@ -95,6 +97,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        return
     from recurrent_looped_transformer_amd import rlt
     from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens
 
