@@ -52,6 +52,19 @@ __device__ __forceinline__ void load16(const bf16_t* p, float* o) {
     o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
+// the VEC elements of a 16-byte register value as float
+template <typename T> __device__ __forceinline__ void unpack16(const uint4& v, float* o);
+template <> __device__ __forceinline__ void unpack16<float>(const uint4& v, float* o) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4& v, float* o) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
 __device__ __forceinline__ void store16(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }

@@ -6,10 +6,10 @@
 // attention over its cache.
 //
 // One workgroup (256 threads) per (head, query row). A group of DH/VEC lanes
-// owns one key (16-byte loads), so a wave reads whole contiguous key rows.
-// Pass 1 writes the scaled scores to LDS, pass 2 takes max / exp / sum, pass 3
-// accumulates p_j v_j per lane group and reduces the groups through LDS. Keys
-// and values are each read once from HBM.
+// owns one key at a time (16-byte loads), so a wave reads whole contiguous key
+// rows. Each group runs a single-pass online softmax over its keys, UNR keys per
+// round with all K and V loads of the round issued before use; the groups are
+// combined through LDS at the end. Keys and values are each read once.
 #include "common.hpp"
 #include "ops.hpp"
 
@@ -17,11 +17,12 @@ namespace rlt {
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
-  extern __shared__ float smem[];          // [n] scores, then [256/G][DH] partials
-  __shared__ float red[16];
   constexpr int VEC = Elem<T>::VEC;
   constexpr int G = DH / VEC;              // lanes per key
-  constexpr int NG = 256 / G;              // keys in flight per block
+  constexpr int NG = 256 / G;              // keys in flight per block per round
+  constexpr int UNR = 8;
+  __shared__ float part[NG * DH];
+  __shared__ float ml[2 * NG];
   const int h = blockIdx.x;
   const int row = blockIdx.y;
   const int b = row / a.nq, qi = row % a.nq;
@@ -39,62 +40,79 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   const T* kb = reinterpret_cast<const T*>(a.k) + hb;
   const T* vb = reinterpret_cast<const T*>(a.v) + hb;
 
-  float* sc = smem;
-  for (int j = gi; j < n; j += NG) {
-    const int p = lo + j;
-    const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-    float kv[VEC];
-    load16(kb + (int64_t)slot * DH, kv);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) dot = fmaf(qv[e], kv[e], dot);
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, WAVE);
-    if (gl == 0) sc[j] = dot;
-  }
-  __syncthreads();
-  float mx = -INFINITY;
-  for (int j = tid; j < n; j += 256) mx = fmaxf(mx, sc[j]);
-  mx = block_max(mx, red);
-  float sum = 0.f;
-  for (int j = tid; j < n; j += 256) {
-    const float e = __expf(sc[j] - mx);
-    sc[j] = e;
-    sum += e;
-  }
-  sum = block_sum(sum, red);   // ends with a barrier: sc[] final for everyone
-  float acc[VEC];
+  float m_run = -INFINITY, l_run = 0.f, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  for (int j = gi; j < n; j += NG) {
-    const int p = lo + j;
-    const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-    float vv[VEC];
-    load16(vb + (int64_t)slot * DH, vv);
-    const float w = sc[j];
+  for (int j0 = gi; j0 < n; j0 += NG * UNR) {
+    uint4 kk[UNR], vv[UNR];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(w, vv[e], acc[e]);
+    for (int u = 0; u < UNR; ++u) {
+      const int j = j0 + u * NG;
+      if (j < n) {
+        const int p = lo + j;
+        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
+        kk[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);
+        vv[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);
+      }
+    }
+    float sc[UNR];
+    float mx = m_run;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float dot = -INFINITY;
+      if (j0 + u * NG < n) {
+        float kf[VEC];
+        unpack16<T>(kk[u], kf);
+        dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot = fmaf(qv[e], kf[e], dot);
+      }
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, WAVE);
+      sc[u] = dot;
+      mx = fmaxf(mx, dot);
+    }
+    const float corr = __expf(m_run - mx);
+    l_run *= corr;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (j0 + u * NG < n) {
+        const float pw = __expf(sc[u] - mx);
+        l_run += pw;
+        float vf[VEC];
+        unpack16<T>(vv[u], vf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pw, vf[e], acc[e]);
+      }
+    }
+    m_run = mx;
   }
-  __syncthreads();   // scores no longer needed: reuse LDS for partials
-  float* part = smem;   // [NG][DH]
 #pragma unroll
   for (int e = 0; e < VEC; ++e) part[gi * DH + gl * VEC + e] = acc[e];
+  if (gl == 0) {
+    ml[2 * gi] = m_run;
+    ml[2 * gi + 1] = l_run;
+  }
   __syncthreads();
   if (tid < DH) {
-    float s = 0.f;
-    for (int gg = 0; gg < NG; ++gg) s += part[gg * DH + tid];
+    float M = -INFINITY;
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, ml[2 * gg]);
+    float s = 0.f, den = 0.f;
+    for (int gg = 0; gg < NG; ++gg) {
+      const float w = __expf(ml[2 * gg] - M);
+      den += w * ml[2 * gg + 1];
+      s += w * part[gg * DH + tid];
+    }
     T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
-    Elem<T>::st(op, s / sum);
+    Elem<T>::st(op, s / den);
   }
 }
 
 template <typename T, int DH>
 static void launch_attn(const AttnArgs& a, hipStream_t st) {
-  const int maxn = a.window > 0 ? a.window : a.pos0 + a.nq;
-  constexpr int VEC = Elem<T>::VEC;
-  constexpr int NG = 256 / (DH / VEC);
-  const size_t lds = sizeof(float) * (size_t)max(maxn, NG * DH);
-  hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
 }
 
 template <typename T>

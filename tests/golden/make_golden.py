@@ -43,6 +43,7 @@ def main():
     ap.add_argument("names", nargs="+")
     ap.add_argument("--rows", type=int, default=2)
     ap.add_argument("--len", type=int, default=32)
+    ap.add_argument("--tag", default="")
     args = ap.parse_args()
     for name in args.names:
         cfg, x, dt = workload(name, args.rows, args.len)
@@ -50,13 +51,15 @@ def main():
         t0 = time.time()
         lp, logits, s = Oracle(cfg, P, dt).replay(x)
         out = {"tokens": x, "logprob": lp.astype(np.float32), "s_last": s[:, -1].astype(np.float32)}
+        if cfg.vocab > 64:
+            out["logits_tail"] = logits[:, -8:].astype(np.float32)   # last positions, full vocabulary
         if cfg.vocab <= 64:
             out["logits"] = logits.astype(np.float32)
         else:
             out["logits_head"] = logits[:, :, :64].astype(np.float32)
             out["argmax"] = np.argmax(logits, axis=-1).astype(np.int32)
             out["logit_max"] = logits.max(axis=-1).astype(np.float32)
-        path = os.path.join(HERE, f"{name}.npz")
+        path = os.path.join(HERE, f"{name}{args.tag}.npz")
         np.savez_compressed(path, **out)
         print(f"{name}: B={x.shape[0]} T={x.shape[1]} oracle {time.time() - t0:.1f} s -> {path}", flush=True)
 
