@@ -48,13 +48,18 @@ class Oracle:
     def __init__(self, cfg, params: Dict[str, np.ndarray], dtype=np.float64):
         self.cfg = cfg
         self.dt = np.dtype(dtype)
-        self._P = {k: np.asarray(v, dtype=self.dt) for k, v in params.items()}
+        # A mapping that decodes entries on read (16-bit storage of the largest
+        # shapes) stays lazy: each read yields that entry in the working dtype.
+        self._lazy = bool(getattr(params, "upcast_on_read", False))
+        self._P = params if self._lazy else {k: np.asarray(v, dtype=self.dt) for k, v in params.items()}
         self.used = set()          # names read so far (parameter-count pins)
         self.block_steps = 0       # dependent decoder block steps (schedule-depth pin)
 
     # ------------------------------------------------------------------ params
     def p(self, name: str) -> np.ndarray:
         self.used.add(name)
+        if self._lazy:
+            return np.asarray(self._P[name], dtype=self.dt)
         return self._P[name]
 
     def dec_w(self, l: int, short: str) -> np.ndarray:

@@ -36,6 +36,9 @@ Every matrix is [out_features, in_features].
 from __future__ import annotations
 
 import dataclasses
+import os
+from collections.abc import Mapping
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Tuple
 
 import numpy as np
@@ -157,26 +160,79 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out.reshape(a.shape)
 
 
-def make_params(cfg: Config, seed: int | None = None, std: float = 0.02) -> Dict[str, np.ndarray]:
-    """Draw a parameter set in manifest order from numpy PCG64.
+def _round_bf16_inplace(a: np.ndarray) -> None:
+    """Round finite float32 values to the nearest bfloat16 in place (ties to even)."""
+    u = a.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
 
-    Matrices, embedding and gate bias ~ N(0, std); norm gains 1 + N(0, std);
-    s* ~ N(0, 1). For bf16 workloads the matrices are rounded to bf16 values
-    (vectors stay float32); both sides consume these same values.
+
+class Bf16Params(Mapping):
+    """Parameter set holding bf16-valued matrices as their raw 16-bit patterns.
+
+    Reading an entry returns float32 (exact: every stored value is a bf16
+    value), so a consumer sees the same numbers as the float32 dict from
+    make_params while the set occupies half the host memory. Meant for the
+    11.7-billion-parameter shape, whose float32 set alone is 46.7 GB.
     """
-    rng = np.random.Generator(np.random.PCG64(cfg.weight_seed if seed is None else seed))
-    params: Dict[str, np.ndarray] = {}
-    for name, shape in manifest(cfg):
+    upcast_on_read = True
+
+    def __init__(self, raw: Dict[str, np.ndarray]):
+        self._raw = raw
+
+    def __getitem__(self, name: str) -> np.ndarray:
+        a = self._raw[name]
+        if a.dtype == np.uint16:
+            return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return a
+
+    def __iter__(self):
+        return iter(self._raw)
+
+    def __len__(self):
+        return len(self._raw)
+
+    def raw(self, name: str) -> np.ndarray:
+        return self._raw[name]
+
+
+def make_params(cfg: Config, seed: int | None = None, std: float = 0.02,
+                bf16_storage: bool = False, threads: int | None = None):
+    """Draw a parameter set in manifest order.
+
+    Tensor number i of the manifest is drawn from its own numpy PCG64 stream,
+    seeded with SeedSequence([weight_seed, i]), so tensors can be drawn in
+    parallel and each one's values do not depend on the others. Matrices,
+    embedding and gate bias ~ N(0, std); norm gains 1 + N(0, std); s* ~ N(0, 1).
+    For bf16 workloads the matrices are rounded to bf16 values (vectors stay
+    float32); both sides consume these same values. With bf16_storage the
+    matrices are kept as 16-bit patterns in a Bf16Params mapping.
+    """
+    base = cfg.weight_seed if seed is None else seed
+    items = manifest(cfg)
+    keep_bits = bf16_storage and cfg.dtype == "bf16"
+
+    def draw(i: int):
+        name, shape = items[i]
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, i])))
+        a = rng.standard_normal(shape, dtype=np.float32)
         if name == "merge.s0":
-            a = rng.standard_normal(shape, dtype=np.float32)
+            pass
         elif is_gain(name):
-            a = (1.0 + std * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+            a *= np.float32(std)
+            a += np.float32(1.0)
         else:
-            a = (std * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+            a *= np.float32(std)
         if cfg.dtype == "bf16" and is_matrix(name, shape):
-            a = round_bf16(a)
-        params[name] = a
-    return params
+            _round_bf16_inplace(a)
+            if keep_bits:
+                a = (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        return name, a
+
+    n = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        params = dict(ex.map(draw, range(len(items))))
+    return Bf16Params(params) if keep_bits else params
 
 
 def zipf_ids(rng: np.random.Generator, n_ranks: int, s: float, size) -> np.ndarray:

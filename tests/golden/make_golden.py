@@ -3,7 +3,9 @@
 Calls only the oracle and the seeded input generators (no HIP code). Each file
 holds the oracle's replay outputs for the named workload:
   logprob [B, T-1]  log p(x_{t+1} | x_<=t)
-  logits  [B, T, V] readout logits at every position (omitted for large V)
+  logits  [B, T, V] readout logits at every position; for large V instead
+          logits_head [B, T, 64] (first 64 ids), logits_tail [B, 8, V] (last 8
+          positions, every id) and top8_idx / top8_val [B, T, 8] (largest logits)
   s_last  [B, d]    s_T
 The medium-LM file covers the first `--rows` sequences and `--len` positions of
 that workload's token stream (causality makes them independent of the rest).
@@ -38,6 +40,12 @@ def workload(name: str, rows: int, length: int):
     return cfg, make_tokens(cfg, length=cfg.seq_len), np.float64
 
 
+def param_probe(P) -> np.ndarray:
+    """A few drawn parameter values, so a test can tell that the seeded draw is unchanged."""
+    keys = [k for k in ("emb", "out.w", "merge.s0") if k in P]
+    return np.concatenate([np.asarray(P[k]).ravel()[:8] for k in keys]).astype(np.float32)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("names", nargs="+")
@@ -47,18 +55,20 @@ def main():
     args = ap.parse_args()
     for name in args.names:
         cfg, x, dt = workload(name, args.rows, args.len)
-        P = make_params(cfg)
+        P = make_params(cfg, bf16_storage=cfg.d >= 4096)
         t0 = time.time()
         lp, logits, s = Oracle(cfg, P, dt).replay(x)
-        out = {"tokens": x, "logprob": lp.astype(np.float32), "s_last": s[:, -1].astype(np.float32)}
+        out = {"tokens": x, "logprob": lp.astype(np.float32), "s_last": s[:, -1].astype(np.float32),
+               "param_probe": param_probe(P)}
         if cfg.vocab > 64:
             out["logits_tail"] = logits[:, -8:].astype(np.float32)   # last positions, full vocabulary
         if cfg.vocab <= 64:
             out["logits"] = logits.astype(np.float32)
         else:
             out["logits_head"] = logits[:, :, :64].astype(np.float32)
-            out["argmax"] = np.argmax(logits, axis=-1).astype(np.int32)
-            out["logit_max"] = logits.max(axis=-1).astype(np.float32)
+            top = np.argsort(-logits, axis=-1, kind="stable")[..., :8]     # ties: lowest index first
+            out["top8_idx"] = top.astype(np.int32)
+            out["top8_val"] = np.take_along_axis(logits, top, -1).astype(np.float32)
         path = os.path.join(HERE, f"{name}{args.tag}.npz")
         np.savez_compressed(path, **out)
         print(f"{name}: B={x.shape[0]} T={x.shape[1]} oracle {time.time() - t0:.1f} s -> {path}", flush=True)

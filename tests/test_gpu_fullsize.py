@@ -3,7 +3,8 @@ tests/golden/make_golden.py, which calls only the oracle and the seeded generato
 
 The algorithmic-task shape (B 64 x T 257, RLT-1 and RLT-0) and the RLT-2 shape
 (B 128 x T 64, K_c 4, G = L_D) run at their full sizes, in the same launch
-configuration as the benchmark (automatic scan driver) and in the persistent modes.
+configuration as the benchmark (automatic scan driver), in the persistent modes and with
+four batch slices on their own streams.
 """
 import os
 
@@ -30,9 +31,9 @@ def cfg_of(name):
     return CONFIGS["algo_bf16"].replace(variant=V0) if name == "algo_bf16_rlt0" else CONFIGS[name]
 
 
-def run(cfg, tokens, scan_mode):
+def run(cfg, P, tokens, scan_mode):
     B, T = tokens.shape
-    m = rlt.Model(cfg, make_params(cfg))
+    m = rlt.Model(cfg, P)
     rlt.rlt_set_scan_mode(m.h, scan_mode)
     try:
         st = m.state(B, T, keep_encoder_cache=False)
@@ -48,15 +49,19 @@ def run(cfg, tokens, scan_mode):
         m.close()
 
 
-@pytest.mark.parametrize("scan_mode", [0, 3, 4])
+@pytest.mark.parametrize("scan_mode", [0, 3, 4, 8])
 @pytest.mark.parametrize("name", ["algo_bf16", "algo_bf16_rlt0", "rlt2_bf16"])
 def test_full_size_matches_oracle(name, scan_mode):
     g = load(name)
     cfg = cfg_of(name)
     tokens = make_tokens(cfg, length=cfg.seq_len)
     assert np.array_equal(tokens, g["tokens"]), "seeded token stream changed"
+    P = make_params(cfg)
+    keys = [k for k in ("emb", "out.w", "merge.s0") if k in P]
+    probe = np.concatenate([P[k].ravel()[:8] for k in keys]).astype(np.float32)
+    assert np.array_equal(probe, g["param_probe"]), "seeded parameter draw changed"
     print(f"[case] {name} B={tokens.shape[0]} T={tokens.shape[1]} scan_mode={scan_mode}", flush=True)
-    logits, s, lp = run(cfg, tokens, scan_mode)
+    logits, s, lp = run(cfg, P, tokens, scan_mode)
     err = float(np.max(np.abs(logits - g["logits"])))
     gi, ri = np.argmax(logits, -1), np.argmax(g["logits"], -1)
     ref_at = np.take_along_axis(g["logits"], gi[..., None], -1)[..., 0]
