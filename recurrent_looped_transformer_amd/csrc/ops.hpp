@@ -56,10 +56,28 @@ struct EpArgs {
   int nrep = 1;
   float alpha = 0.f;
   const float* bias = nullptr;
+  // Folded RMSNorm, producer side (Residual epilogue, decode GEMM): besides z += acc, write
+  // fold_zb[m * fold_ld + n] = act(z_new * fold_gain[n]) and fold_ssp[m * (N / 16) + n / 16] =
+  // sum of z_new^2 over the 16 features of the tile.
+  void* fold_zb = nullptr;
+  float* fold_ssp = nullptr;
+  const float* fold_gain = nullptr;
+  int64_t fold_ld = 0;
+  // Folded RMSNorm, consumer side (decode GEMM): acc of row m is scaled by
+  // 1 / sqrt(sum_k rs_ssp[m * rs_n + k] / rs_d + rs_eps) before the epilogue, so X may hold
+  // act(z * gain) instead of act(rms(z) * gain). rs_n <= 256.
+  const float* rs_ssp = nullptr;
+  int rs_n = 0;
+  int rs_d = 0;
+  float rs_eps = 0.f;
 };
 
-// GEMM: Y[m, n] = sum_k X[m, k] * W[n, k]  (X act rows with leading dim ldx; W packed [N, K]),
-// Y consumed by the epilogue. bf16: MFMA; fp32: vector FMA.
+// Largest row count the decode GEMM takes; folded RMSNorm is available up to it.
+constexpr int kSkinnyMaxRows = 512;
+
+// GEMM: Y[m, n] = sum_k X[m, k] * W[n, k]  (X act rows with leading dim ldx; W packed [N, K]:
+// tile-major for bf16, row-major for fp32), Y consumed by the epilogue. bf16: MFMA; fp32:
+// vector FMA.
 void gemm(Dt dt, Ep ep, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
           hipStream_t st);
 
@@ -79,11 +97,25 @@ void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st);
 // out[om(r)] = L[tok[tm(r)]] - logsumexp(L) with L = logits row lm(r); tok < 0 writes 0
 void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows,
              int V, hipStream_t st);
-// pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind
+// pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind.
+// tiles = false: row-major [N][K] (dst_ld = K). tiles = true (bf16 GEMM weights): the
+// tile-major layout below, with K = dst_ld a multiple of 64 and dst_col0 = 0.
+//
+// Tile-major bf16 weight layout. Rows are grouped in 16-row tiles (N padded to a multiple
+// of 16); tile t occupies 16 * K contiguous elements made of K / 64 blocks of 1024 elements,
+// one per 64-wide k chunk. Inside block c, element (row 16 t + r, k = 64 c + 16 g + 8 h + e)
+// sits at 512 h + 8 (16 g + r) + e. Lane l = 16 g + r of a wavefront then finds the MFMA
+// operand halves of its row r and k group g at l * 8 and 512 + l * 8: each load instruction
+// of a wavefront reads 1 KB of contiguous memory.
 enum class Pack : int { Plain = 0, RopeRows, Interleave2 };
 void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* dst, int64_t dst_ld,
                  int64_t dst_col0, int rows, int cols, Pack kind, int dh, int row_stride, int row_off,
-                 hipStream_t st);
+                 bool tiles, hipStream_t st);
+// element offset of (row n, column k) in the tile-major layout of a [*, K] weight
+__host__ __device__ inline int64_t tile_major_off(int64_t n, int64_t k, int64_t K) {
+  const int64_t kk = k & 63;
+  return (n >> 4) * 16 * K + (k >> 6) * 1024 + ((kk >> 3) & 1) * 512 + ((kk >> 4) * 16 + (n & 15)) * 8 + (kk & 7);
+}
 
 // Attention of nq query rows per (sequence, head) over a position range of a key/value store.
 struct AttnArgs {

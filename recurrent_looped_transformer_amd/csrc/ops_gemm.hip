@@ -7,8 +7,9 @@
 // gate/state rows) meet in one lane and the epilogue needs no shuffles.
 //
 //  - gemm_skinny_bf16: decode shapes (M = batch rows <= a few hundred). One
-//    workgroup streams 16 weight rows once for up to 64 activation rows; the four
-//    waves split K and reduce through LDS. Bandwidth-bound on the weights.
+//    workgroup streams 16 weight rows once for up to 64 activation rows; eight
+//    waves split K, keep the tile's loads in flight together and reduce through
+//    LDS. Bandwidth-bound on the weights. Carries the folded RMSNorm (see EpArgs).
 //  - gemm_tiled_bf16: prefill shapes. 128x128 tiles, K step 32, LDS double
 //    buffer, 4 waves x (64x64) of 16x16x32 MFMAs.
 //  - gemm_f32: the fp32 configuration (vector FMA).
@@ -32,8 +33,11 @@ __device__ __forceinline__ int64_t kv_off(const EpArgs& a, int b, int h, int pos
   return (((int64_t)(a.b0 + b) * a.H + h) * a.kv.cap + slot) * a.dh + c;
 }
 
+// Applies the epilogue to acc values v of row m, features n..n+3. Returns the sum of
+// squares of the new residual values when the Residual epilogue folds the next RMSNorm
+// (fold_zb set), else 0.
 template <typename T, Ep E>
-__device__ __forceinline__ void epilogue(const EpArgs& a, int m, int n, float v[4]) {
+__device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v[4]) {
   T* out = reinterpret_cast<T*>(a.out);
   if constexpr (E == Ep::StoreAct) {
 #pragma unroll
@@ -44,8 +48,18 @@ __device__ __forceinline__ void epilogue(const EpArgs& a, int m, int n, float v[
     for (int i = 0; i < 4; ++i) o[i] = v[i];
   } else if constexpr (E == Ep::Residual) {
     float* r = a.resid + a.rmap.off(m) + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] += v[i];
+    const float4 old = *reinterpret_cast<const float4*>(r);
+    const float z[4] = {old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]};
+    *reinterpret_cast<float4*>(r) = make_float4(z[0], z[1], z[2], z[3]);
+    if (a.fold_zb) {
+      T* zb = reinterpret_cast<T*>(a.fold_zb) + (int64_t)m * a.fold_ld + n;
+      const float4 gn = *reinterpret_cast<const float4*>(a.fold_gain + n);
+      Elem<T>::st(zb, z[0] * gn.x);
+      Elem<T>::st(zb + 1, z[1] * gn.y);
+      Elem<T>::st(zb + 2, z[2] * gn.z);
+      Elem<T>::st(zb + 3, z[3] * gn.w);
+      return z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3];
+    }
   } else if constexpr (E == Ep::Bias) {
     float* r = a.resid + a.rmap.off(m) + n;
 #pragma unroll
@@ -89,52 +103,107 @@ __device__ __forceinline__ void epilogue(const EpArgs& a, int m, int n, float v[
       z[1] = a.e[eo + 1] + a.alpha * sigmoidf_(a.gpre[eo + 1] + v[2]) * v[3];
     }
   }
+  return 0.f;
 }
 
 // ------------------------------------------------------------------ skinny (decode)
-template <Ep E>
-__global__ __launch_bounds__(256) void gemm_skinny_bf16(const bf16_t* __restrict__ X, int64_t ldx,
-                                                        const bf16_t* __restrict__ W, int M, int N, int K,
-                                                        EpArgs a) {
-  __shared__ f32x4 red[4][4][WAVE];
+// One workgroup of kSkW waves owns 16 output features and 16 * NMB rows (NMB <= 4). The
+// waves split K into 64-wide chunks (chunk c to wave c % kSkW) and each wave issues the
+// weight and activation loads of U chunks before their MFMAs, so that the whole 16 x K
+// weight tile is in flight at once for K up to kSkW * U * 64. Partial tiles meet in LDS.
+constexpr int kSkW = 8;
+
+template <Ep E, int NMB>
+__global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny_bf16(const bf16_t* __restrict__ X, int64_t ldx,
+                                                                const bf16_t* __restrict__ W, int M, int N,
+                                                                int K, EpArgs a) {
+  constexpr int U = NMB == 1 ? 8 : (NMB == 2 ? 4 : 2);
+  constexpr int RPW = NMB * 16 / kSkW;     // rows per wave in the row-scale prologue
+  __shared__ f32x4 red[kSkW][NMB][WAVE];
+  __shared__ float rsl[NMB * 16];
   const int n0 = blockIdx.x * 16;
-  const int m0 = blockIdx.y * 64;
+  const int m0 = blockIdx.y * (NMB * 16);
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r = lane & 15, g = lane >> 4;
-  const int nmb = min(4, (M - m0 + 15) / 16);
-  const int nrow = min(n0 + r, N - 1);
-  const bf16_t* wp = W + (int64_t)nrow * K + g * 16;
-  const bf16_t* xp[4];
+
+  // folded RMSNorm of the input rows: fetch the partial sums now, reduce after the main loop
+  float ssr[RPW][4];
+  if (a.rs_ssp) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xp[j] = X + (int64_t)min(m0 + j * 16 + r, M - 1) * ldx + g * 16;
-  f32x4 acc[4];
+    for (int i = 0; i < RPW; ++i) {
+      const int m = min(m0 + wave + kSkW * i, M - 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 4; ++q) {
+        const int k = lane + WAVE * q;
+        ssr[i][q] = k < a.rs_n ? a.rs_ssp[(int64_t)m * a.rs_n + k] : 0.f;
+      }
+    }
+  }
+
+  const bf16_t* wp = W + (int64_t)blockIdx.x * 16 * K + lane * 8;   // tile-major weight tile
+  const bf16_t* xp[NMB];
+#pragma unroll
+  for (int j = 0; j < NMB; ++j) xp[j] = X + (int64_t)min(m0 + j * 16 + r, M - 1) * ldx + g * 16;
+  f32x4 acc[NMB];
+#pragma unroll
+  for (int j = 0; j < NMB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nch = K / 64;
-  for (int c = wave; c < nch; c += 4) {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(wp + c * 64);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(wp + c * 64 + 8);
+  for (int c0 = wave; c0 < nch; c0 += kSkW * U) {
+    uint4 wa[U][2], xb[U][NMB][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < nmb) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(xp[j] + c * 64 + 8);
-        acc[j] = mfma16x16x32(a0, b0, acc[j]);
-        acc[j] = mfma16x16x32(a1, b1, acc[j]);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kSkW;
+      if (c < nch) {
+        wa[u][0] = *reinterpret_cast<const uint4*>(wp + c * 1024);
+        wa[u][1] = *reinterpret_cast<const uint4*>(wp + c * 1024 + 512);
+#pragma unroll
+        for (int j = 0; j < NMB; ++j) {
+          xb[u][j][0] = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
+          xb[u][j][1] = *reinterpret_cast<const uint4*>(xp[j] + c * 64 + 8);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * kSkW < nch) {
+#pragma unroll
+        for (int j = 0; j < NMB; ++j) {
+          acc[j] = mfma16x16x32(wa[u][0], xb[u][j][0], acc[j]);
+          acc[j] = mfma16x16x32(wa[u][1], xb[u][j][1], acc[j]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[wave][j][lane] = acc[j];
+  for (int j = 0; j < NMB; ++j) red[wave][j][lane] = acc[j];
+  if (a.rs_ssp) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const float t = wave_sum(ssr[i][0] + ssr[i][1] + ssr[i][2] + ssr[i][3]);
+      if (lane == 0) rsl[wave + kSkW * i] = rsqrtf(t / (float)a.rs_d + a.rs_eps);
+    }
+  }
   __syncthreads();
-  const int j = wave;
-  if (j < nmb) {
-    f32x4 s = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
+  if (wave < NMB) {
+    const int j = wave;
+    f32x4 sum = red[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kSkW; ++w) sum += red[w][j][lane];
     const int m = m0 + j * 16 + r;
     const int n = n0 + 4 * g;
+    const float sc = a.rs_ssp ? rsl[j * 16 + r] : 1.f;
+    float ss = 0.f;
     if (m < M && n < N) {
-      float v[4] = {s[0], s[1], s[2], s[3]};
-      epilogue<bf16_t, E>(a, m, n, v);
+      float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
+      ss = epilogue<bf16_t, E>(a, m, n, v);
+    }
+    if constexpr (E == Ep::Residual) {
+      if (a.fold_zb) {
+        // lanes r, r+16, r+32, r+48 hold the 16 features of row m
+        ss += __shfl_xor(ss, 16, WAVE);
+        ss += __shfl_xor(ss, 32, WAVE);
+        if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + blockIdx.x] = ss;
+      }
     }
   }
 }
@@ -157,30 +226,37 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
   const int r = lane & 15, g = lane >> 4;
   const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
 
-  // global load assignment: 2 x 16B of each tile per thread
+  // global load assignment: 2 x 16B of each tile per thread. Activations: row lrow, k group lq.
+  // Weights (tile-major): tile wt, row wr, k group 2 * (stage & 1) + wg, half wh, so that 32
+  // consecutive threads read 512 contiguous bytes; they land in LDS row 16 wt + wr, slot 2 wg + wh.
   const bf16_t* wsrc[2];
   const bf16_t* xsrc[2];
-  int lrow[2], lq[2];
+  int lrow[2], lq[2], wrow[2], wq[2];
+  const int ntiles = (N + 15) / 16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = tid + i * 256;
     lrow[i] = idx >> 2;
     lq[i] = idx & 3;
-    wsrc[i] = W + (int64_t)min(n0 + lrow[i], N - 1) * K + lq[i] * 8;
     xsrc[i] = X + (int64_t)min(m0 + lrow[i], M - 1) * ldx + lq[i] * 8;
+    const int wr = idx & 15, wg = (idx >> 4) & 1, wh = (idx >> 5) & 1, wt = idx >> 6;
+    wrow[i] = wt * 16 + wr;
+    wq[i] = wg * 2 + wh;
+    wsrc[i] = W + (int64_t)min(n0 / 16 + wt, ntiles - 1) * 16 * K + wh * 512 + (wg * 16 + wr) * 8;
   }
   uint4 rw[2], rx[2];
   auto gload = [&](int k0) {
+    const int64_t wk = (int64_t)(k0 >> 6) * 1024 + ((k0 >> 5) & 1) * 256;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0);
+      rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + wk);
       rx[i] = *reinterpret_cast<const uint4*>(xsrc[i] + k0);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      sW[buf][lrow[i]][lq[i]] = rw[i];
+      sW[buf][wrow[i]][wq[i]] = rw[i];
       sX[buf][lrow[i]][lq[i]] = rx[i];
     }
   };
@@ -253,9 +329,16 @@ static void launch(Dt dt, const EpArgs& a, const void* X, int64_t ldx, const voi
     const int blocks = (int)((total + 255) / 256);
     hipLaunchKernelGGL(gemm_f32<E>, dim3(blocks), dim3(256), 0, st, (const float*)X, ldx, (const float*)W, M, N, K,
                        a);
-  } else if (M <= 512) {
-    hipLaunchKernelGGL(gemm_skinny_bf16<E>, dim3((N + 15) / 16, (M + 63) / 64), dim3(256), 0, st,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
+  } else if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp) {
+    const dim3 blk(kSkW * WAVE);
+    const bf16_t *x = (const bf16_t*)X, *w = (const bf16_t*)W;
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 1>), dim3((N + 15) / 16, 1), blk, 0, st, x, ldx, w, M, N, K, a);
+    else if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 2>), dim3((N + 15) / 16, 1), blk, 0, st, x, ldx, w, M, N, K, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 4>), dim3((N + 15) / 16, (M + 63) / 64), blk, 0, st, x, ldx, w, M,
+                         N, K, a);
   } else {
     hipLaunchKernelGGL(gemm_tiled_bf16<E>, dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st,
                        (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);

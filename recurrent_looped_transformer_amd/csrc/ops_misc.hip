@@ -6,7 +6,10 @@
 
 namespace rlt {
 
-// out[m, :] = act(x[m, :] / sqrt(mean(x^2) + eps) * gain); one wavefront per row.
+// out[m, :] = act(x[m, :] / sqrt(mean(x^2) + eps) * gain); one wavefront per row. Rows up to
+// 64 * 4 * kRmsVec features are read once into registers with every load in flight together;
+// longer rows take a second, streaming pass.
+constexpr int kRmsVec = 16;
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, RowMap xm,
                                                  const float* __restrict__ gain, T* __restrict__ out,
@@ -15,23 +18,35 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, Ro
   const int lane = threadIdx.x & (WAVE - 1);
   if (row >= rows) return;
   const float* xr = x + xm.off(row);
+  float4 v[kRmsVec];
   float ss = 0.f;
-  for (int c = lane * 4; c < d; c += WAVE * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = (lane + WAVE * i) * 4;
+    v[i] = c < d ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < kRmsVec; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  for (int c = (lane + WAVE * kRmsVec) * 4; c < d; c += WAVE * 4) {
+    const float4 u = *reinterpret_cast<const float4*>(xr + c);
+    ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
   }
   ss = wave_sum(ss);
   const float inv = gain ? rsqrtf(ss / (float)d + eps) : 1.f;
   T* o = out + (int64_t)row * ldo;
-  for (int c = lane * 4; c < d; c += WAVE * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    float w[4] = {v.x, v.y, v.z, v.w};
+  auto put = [&](int c, float4 u) {
+    const float4 gv = gain ? *reinterpret_cast<const float4*>(gain + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+    Elem<T>::st(o + c, u.x * inv * gv.x);
+    Elem<T>::st(o + c + 1, u.y * inv * gv.y);
+    Elem<T>::st(o + c + 2, u.z * inv * gv.z);
+    Elem<T>::st(o + c + 3, u.w * inv * gv.w);
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float gv = gain ? gain[c + i] : 1.f;
-      Elem<T>::st(o + c + i, w[i] * inv * gv);
-    }
+  for (int i = 0; i < kRmsVec; ++i) {
+    const int c = (lane + WAVE * i) * 4;
+    if (c < d) put(c, v[i]);
   }
+  for (int c = (lane + WAVE * kRmsVec) * 4; c < d; c += WAVE * 4) put(c, *reinterpret_cast<const float4*>(xr + c));
 }
 
 void rmsnorm(Dt dt, const float* x, RowMap xm, const float* gain, void* out, int64_t ldo, int rows, int d,
@@ -148,7 +163,7 @@ void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, floa
 template <typename T>
 __global__ void pack_k(const float* __restrict__ src, int64_t src_ld, int64_t col0, T* __restrict__ dst,
                        int64_t dst_ld, int64_t dst_col0, int rows, int cols, int kind, int dh, int row_stride,
-                       int row_off) {
+                       int row_off, int tiles) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)rows * cols) return;
   const int j = (int)(idx / cols), c = (int)(idx % cols);
@@ -158,19 +173,20 @@ __global__ void pack_k(const float* __restrict__ src, int64_t src_ld, int64_t co
     pj = h * dh + (w < half ? 2 * w : 2 * (w - half) + 1);
   }
   const int64_t drow = (int64_t)row_off + (int64_t)row_stride * pj;
-  Elem<T>::st(dst + drow * dst_ld + dst_col0 + c, src[(int64_t)j * src_ld + col0 + c]);
+  const int64_t o = tiles ? tile_major_off(drow, dst_col0 + c, dst_ld) : drow * dst_ld + dst_col0 + c;
+  Elem<T>::st(dst + o, src[(int64_t)j * src_ld + col0 + c]);
 }
 
 void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* dst, int64_t dst_ld, int64_t dst_col0,
-                 int rows, int cols, Pack kind, int dh, int row_stride, int row_off, hipStream_t st) {
+                 int rows, int cols, Pack kind, int dh, int row_stride, int row_off, bool tiles, hipStream_t st) {
   const int64_t total = (int64_t)rows * cols;
   const dim3 grid((unsigned)((total + 255) / 256));
   if (dt == Dt::F32)
     hipLaunchKernelGGL(pack_k<float>, grid, dim3(256), 0, st, src, src_ld, col0, (float*)dst, dst_ld, dst_col0, rows,
-                       cols, (int)kind, dh, row_stride, row_off);
+                       cols, (int)kind, dh, row_stride, row_off, 0);
   else
     hipLaunchKernelGGL(pack_k<bf16_t>, grid, dim3(256), 0, st, src, src_ld, col0, (bf16_t*)dst, dst_ld, dst_col0,
-                       rows, cols, (int)kind, dh, row_stride, row_off);
+                       rows, cols, (int)kind, dh, row_stride, row_off, tiles ? 1 : 0);
 }
 
 }  // namespace rlt

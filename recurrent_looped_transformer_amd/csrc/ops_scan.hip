@@ -132,20 +132,19 @@ struct WPre {
 };
 __device__ __forceinline__ void w_prefetch(WPre& w, const bf16_t* __restrict__ W, int N, int K, int n0) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int r = lane & 15, g = lane >> 4;
-  const bf16_t* wp = W + (int64_t)min(n0 + r, N - 1) * K + g * 16;
+  const bf16_t* wp = W + (int64_t)(n0 >> 4) * 16 * K + lane * 8;   // tile-major weight tile
   const int nch = K / 64;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int cc = wave + 4 * u;
     if (cc < nch) {
-      w.a[u][0] = *reinterpret_cast<const uint4*>(wp + cc * 64);
-      w.a[u][1] = *reinterpret_cast<const uint4*>(wp + cc * 64 + 8);
+      w.a[u][0] = *reinterpret_cast<const uint4*>(wp + cc * 1024);
+      w.a[u][1] = *reinterpret_cast<const uint4*>(wp + cc * 1024 + 512);
     }
   }
 }
 
-// acc for weight rows n0..n0+15 (plain loads from W [N][K]) and activation rows
+// acc for weight rows n0..n0+15 (plain loads from the tile-major W) and activation rows
 // m0 + 16 j + r (device-scope loads from X with leading dimension ldx at buffer row
 // xrow(m) = (m / q) * xp + m % q + xo), j < nmb, rows limited to [.., M). Waves split
 // K in chunks of 64; each wave issues the loads of two chunks before their MFMAs; the
@@ -156,7 +155,7 @@ __device__ __forceinline__ void tile_mma(const bf16_t* __restrict__ W, int N, in
                                          const WPre* pre = nullptr) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r = lane & 15, g = lane >> 4;
-  const bf16_t* wp = W + (int64_t)min(n0 + r, N - 1) * K + g * 16;
+  const bf16_t* wp = W + (int64_t)(n0 >> 4) * 16 * K + lane * 8;   // tile-major weight tile
   u32 xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -178,8 +177,8 @@ __device__ __forceinline__ void tile_mma(const bf16_t* __restrict__ W, int N, in
           a[u][0] = pre->a[u][0];
           a[u][1] = pre->a[u][1];
         } else {
-          a[u][0] = *reinterpret_cast<const uint4*>(wp + cc * 64);
-          a[u][1] = *reinterpret_cast<const uint4*>(wp + cc * 64 + 8);
+          a[u][0] = *reinterpret_cast<const uint4*>(wp + cc * 1024);
+          a[u][1] = *reinterpret_cast<const uint4*>(wp + cc * 1024 + 512);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -60,6 +60,7 @@ void check_launch() {
 }
 
 constexpr int kReadoutPositions = 64;   // positions per batched readout
+constexpr int kMaxSlices = 4;           // concurrent batch slices of the launch-path scan
 constexpr int kParallelPositions = 64;  // RLT-0 positions per decoder pass
 constexpr int64_t kEncoderRows = 32768; // encoder workspace rows (sequences x tokens per group)
 
@@ -113,6 +114,7 @@ struct rlt_state {
   // decoder workspace, rows = B * P
   float* z = nullptr;
   void *xa = nullptr, *q = nullptr, *ao = nullptr, *hid = nullptr;
+  float* dssp = nullptr;   // [rows][d / 16] sums of squares of z (folded RMSNorm)
   // readout workspace, rows = B * kReadoutPositions
   float* sbuf = nullptr;
   void* xr = nullptr;
@@ -135,6 +137,10 @@ struct rlt_state {
   rlt::ScanLayer* layers_dev = nullptr;
   int* abort_host = nullptr;                 // pinned copy of the scan's abort word
   int scan_grid = 0;
+  // launch-path scan: batch slices run as independent chains on their own streams
+  hipStream_t sub[kMaxSlices] = {};
+  hipEvent_t ev_fork = nullptr;
+  hipEvent_t ev_join[kMaxSlices] = {};
 };
 
 namespace {
@@ -267,7 +273,7 @@ void layout_model(rlt_model* m, char* base, size_t* total) {
     }
   }
   m->nO = takef(d);
-  m->wout = take(V * d * e);
+  m->wout = take((V + 15) / 16 * 16 * d * e);   // whole 16-row tiles; the padding rows stay zero
   *total = off;
 }
 
@@ -278,11 +284,12 @@ void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStr
   auto vec = [&](float* dst, const std::string& name) {
     HIPCHK(hipMemcpyAsync(dst, W.at(name), sizeof(float) * d, hipMemcpyDeviceToDevice, st));
   };
+  const bool tiles = dt == Dt::BF16;   // GEMM weights: tile-major in bf16
   auto plain = [&](void* dst, const std::string& name, int rows, int cols, int row_off = 0, int stride = 1) {
-    pack_matrix(dt, W.at(name), cols, 0, dst, cols, 0, rows, cols, Pack::Plain, dh, stride, row_off, st);
+    pack_matrix(dt, W.at(name), cols, 0, dst, cols, 0, rows, cols, Pack::Plain, dh, stride, row_off, tiles, st);
   };
   auto roped = [&](void* dst, const std::string& name, int row_off) {
-    pack_matrix(dt, W.at(name), d, 0, dst, d, 0, hd, d, Pack::RopeRows, dh, 1, row_off, st);
+    pack_matrix(dt, W.at(name), d, 0, dst, d, 0, hd, d, Pack::RopeRows, dh, 1, row_off, tiles, st);
   };
   auto attn_ffn = [&](const LayerW& L, const std::string& p) {
     roped(L.wqkv, p + "wq", 0);
@@ -293,7 +300,8 @@ void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStr
     plain(L.w13, p + "w3", f, d, 1, 2);
     plain(L.w2, p + "w2", d, f);
   };
-  plain(m->emb, "emb", V, d);
+  // the embedding is gathered by rows, not a GEMM operand: row-major
+  pack_matrix(dt, W.at("emb"), d, 0, m->emb, d, 0, V, d, Pack::Plain, dh, 1, 0, false, st);
   for (int l = 0; l < c.L_E; ++l) {
     const std::string p = "enc." + std::to_string(l) + ".";
     vec(m->enc[l].n1, p + "n1");
@@ -314,16 +322,16 @@ void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStr
     vec(m->s0, "merge.s0");
     // W_g = [W_g,e | W_g,r] over [e_t ; r]: the e half is applied once per position at encode time,
     // the r half is interleaved with W_s (rows 2n, 2n + 1) for the per-step merge GEMM.
-    pack_matrix(dt, W.at("merge.wg"), 2 * d, 0, m->wg_e, d, 0, d, d, Pack::Plain, dh, 1, 0, st);
-    pack_matrix(dt, W.at("merge.wg"), 2 * d, d, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 0, st);
-    pack_matrix(dt, W.at("merge.ws"), d, 0, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 1, st);
+    pack_matrix(dt, W.at("merge.wg"), 2 * d, 0, m->wg_e, d, 0, d, d, Pack::Plain, dh, 1, 0, tiles, st);
+    pack_matrix(dt, W.at("merge.wg"), 2 * d, d, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 0, tiles, st);
+    pack_matrix(dt, W.at("merge.ws"), d, 0, m->wsr, d, 0, d, d, Pack::Plain, dh, 2, 1, tiles, st);
   }
   for (int l = 0; l < c.L_D; ++l) {
     const std::string p = "dec." + std::to_string(l) + ".";
     vec(m->dec[l].n1, p + "m1");
     vec(m->dec[l].n2, p + "m2");
     vec(m->dec[l].n3, p + "m3");
-    pack_matrix(dt, W.at(p + "xq"), d, 0, m->dec[l].xq, d, 0, hd, d, Pack::RopeRows, dh, 1, 0, st);
+    pack_matrix(dt, W.at(p + "xq"), d, 0, m->dec[l].xq, d, 0, hd, d, Pack::RopeRows, dh, 1, 0, tiles, st);
     plain(m->dec[l].xo, p + "xo", d, hd);
     if (!c.share_enc_dec) attn_ffn(m->dec[l], p);
   }
@@ -408,64 +416,112 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
 
 // ------------------------------------------------------------------ decoder pass
 // Positions t0+1 .. t0+np for every sequence, rows m = b * np + i.
-void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st) {
+// Sequences b0 .. b0+nb-1 of the state (a batch slice): the pointers of its rows.
+struct SliceBufs {
+  int b0 = 0, B = 0;
+  float *z, *s, *rho, *e, *gpre, *dssp;
+  void *xa, *q, *ao, *hid, *ring_k, *ring_v, *mem_k, *mem_v;
+};
+SliceBufs slice_bufs(rlt_model* m, rlt_state* s, int b0, int nb) {
+  const rlt_config& c = m->cfg;
+  const int64_t d = c.d, hd = m->hd, f = c.ffn, P = s->P, e = m->esz;
+  SliceBufs v;
+  v.b0 = b0; v.B = nb;
+  const int64_t r0 = (int64_t)b0 * P;   // first workspace row of the slice
+  v.z = s->z + r0 * d; v.dssp = s->dssp + r0 * (d / 16);
+  v.xa = (char*)s->xa + r0 * d * e; v.q = (char*)s->q + r0 * hd * e;
+  v.ao = (char*)s->ao + r0 * hd * e; v.hid = (char*)s->hid + r0 * f * e;
+  v.s = s->s + (int64_t)b0 * d; v.rho = s->rho + (int64_t)b0 * d;
+  v.e = s->e + (int64_t)b0 * s->Tm * d;
+  v.gpre = s->gpre ? s->gpre + (int64_t)b0 * s->Tm * d : nullptr;
+  const int64_t kvb = (int64_t)c.n_heads * c.d_head * e;   // bytes per position of one sequence
+  v.ring_k = s->ring_k ? (char*)s->ring_k + (int64_t)b0 * s->R * kvb : nullptr;
+  v.ring_v = s->ring_v ? (char*)s->ring_v + (int64_t)b0 * s->R * kvb : nullptr;
+  v.mem_k = s->mem_k ? (char*)s->mem_k + (int64_t)b0 * s->Tm * kvb : nullptr;
+  v.mem_v = s->mem_v ? (char*)s->mem_v + (int64_t)b0 * s->Tm * kvb : nullptr;
+  return v;
+}
+
+void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, const SliceBufs& sb) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
-  const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = s->B, Tm = s->Tm;
+  const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = sb.B, Tm = s->Tm;
   const int rows = B * np;
   const RowMap zm = contiguous(d);
   if (c.variant == RLT_V0) {
     RowMap em; em.tn = np; em.sb = (int64_t)Tm * d; em.st = d;
-    copy_rows(s->e + (int64_t)t0 * d, em, s->z, zm, rows, d, st);
+    copy_rows(sb.e + (int64_t)t0 * d, em, sb.z, zm, rows, d, st);
   } else {
     // merge (eq 2.9-2.11): r = RMSNorm_s(s_{t-1} or the RLT-2 register), gate and state projection
-    const float* src = c.variant == RLT_V1 ? s->s : s->rho;
-    rmsnorm(dt, src, contiguous(d), m->ns, s->xa, d, B, d, c.rms_eps, st);
+    const float* src = c.variant == RLT_V1 ? sb.s : sb.rho;
+    rmsnorm(dt, src, contiguous(d), m->ns, sb.xa, d, B, d, c.rms_eps, st);
     EpArgs a;
-    a.resid = s->z; a.rmap = zm; a.e = s->e + (int64_t)t0 * d; a.gpre = s->gpre + (int64_t)t0 * d;
+    a.resid = sb.z; a.rmap = zm; a.e = sb.e + (int64_t)t0 * d; a.gpre = sb.gpre + (int64_t)t0 * d;
     a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha;
-    gemm(dt, Ep::Merge, a, s->xa, d, m->wsr, B, 2 * d, d, st);
+    gemm(dt, Ep::Merge, a, sb.xa, d, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
+  // Folded RMSNorm on the bf16 decode GEMMs: each residual GEMM also writes bf16(z * gain of the
+  // next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the inverse
+  // RMS. The first norm of the pass comes from the norm kernel.
+  const bool fold = dt == Dt::BF16 && rows <= kSkinnyMaxRows && d / 16 <= 256;
+  auto norm_in = [&](EpArgs& a, const float* gain) {
+    if (fold) {
+      a.rs_ssp = sb.dssp; a.rs_n = d / 16; a.rs_d = d; a.rs_eps = c.rms_eps;
+    } else {
+      rmsnorm(dt, sb.z, zm, gain, sb.xa, d, rows, d, c.rms_eps, st);
+    }
+  };
+  auto fold_out = [&](EpArgs& r, const float* gain_next) {
+    if (fold && gain_next) {
+      r.fold_zb = sb.xa; r.fold_ld = d; r.fold_ssp = sb.dssp; r.fold_gain = gain_next;
+    }
+  };
+  if (fold && c.L_D > 0) rmsnorm(dt, sb.z, zm, m->dec[0].n1, sb.xa, d, rows, d, c.rms_eps, st);
   for (int l = 0; l < c.L_D; ++l) {
     const LayerW& L = m->dec[l];
     // causal sliding-window self-attention over the ring (current key written first)
-    rmsnorm(dt, s->z, zm, L.n1, s->xa, d, rows, d, c.rms_eps, st);
     EpArgs a;
-    a.out = s->q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
-    const int64_t ro = (int64_t)l * B * H * s->R * dh * m->esz;
-    a.kv.k = (char*)s->ring_k + ro; a.kv.v = (char*)s->ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
-    gemm(dt, Ep::QKV, a, s->xa, d, L.wqkv, rows, 3 * hd, d, st);
+    if (l > 0 || !fold) norm_in(a, L.n1);
+    a.out = sb.q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
+    const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
+    a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
+    gemm(dt, Ep::QKV, a, sb.xa, d, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
-    at.q = s->q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
-    at.cap = s->R; at.ring = 1; at.out = s->ao; at.ldo = hd; at.B = B; at.nq = np; at.H = H; at.dh = dh;
+    at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
+    at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = hd; at.B = B; at.nq = np; at.H = H; at.dh = dh;
     at.pos0 = t0; at.window = c.window; at.scale = scale;
     attn_decode(dt, at, st);
-    EpArgs r; r.resid = s->z; r.rmap = zm;
-    gemm(dt, Ep::Residual, r, s->ao, hd, L.wo, rows, d, hd, st);
+    EpArgs r; r.resid = sb.z; r.rmap = zm;
+    fold_out(r, L.n2);
+    gemm(dt, Ep::Residual, r, sb.ao, hd, L.wo, rows, d, hd, st);
     // cross-attention to the prefix memory M_<=t of this layer's group
-    rmsnorm(dt, s->z, zm, L.n2, s->xa, d, rows, d, c.rms_eps, st);
     EpArgs qx;
-    qx.out = s->q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0;
-    gemm(dt, Ep::RopeQ, qx, s->xa, d, L.xq, rows, hd, d, st);
+    norm_in(qx, L.n2);
+    qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0;
+    gemm(dt, Ep::RopeQ, qx, sb.xa, d, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
-    const int64_t go = (int64_t)g * B * H * Tm * dh * m->esz;
-    at.k = (char*)s->mem_k + go; at.v = (char*)s->mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
+    const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
+    at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
     at.cap = Tm; at.ring = 0; at.window = 0;
     attn_decode(dt, at, st);
-    gemm(dt, Ep::Residual, r, s->ao, hd, L.xo, rows, d, hd, st);
+    EpArgs r2; r2.resid = sb.z; r2.rmap = zm;
+    fold_out(r2, L.n3);
+    gemm(dt, Ep::Residual, r2, sb.ao, hd, L.xo, rows, d, hd, st);
     // SwiGLU FFN
-    rmsnorm(dt, s->z, zm, L.n3, s->xa, d, rows, d, c.rms_eps, st);
-    EpArgs sw; sw.out = s->hid; sw.ldo = f;
-    gemm(dt, Ep::SwiGLU, sw, s->xa, d, L.w13, rows, 2 * f, d, st);
-    gemm(dt, Ep::Residual, r, s->hid, f, L.w2, rows, d, f, st);
+    EpArgs sw;
+    norm_in(sw, L.n3);
+    sw.out = sb.hid; sw.ldo = f;
+    gemm(dt, Ep::SwiGLU, sw, sb.xa, d, L.w13, rows, 2 * f, d, st);
+    EpArgs r3; r3.resid = sb.z; r3.rmap = zm;
+    fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
+    gemm(dt, Ep::Residual, r3, sb.hid, f, L.w2, rows, d, f, st);
   }
-  s->block_steps += c.L_D;
   // s_t = the last position's output of every sequence
   RowMap last; last.tn = 1; last.sb = (int64_t)np * d;
-  copy_rows(s->z + (int64_t)(np - 1) * d, last, s->s, zm, B, d, st);
+  copy_rows(sb.z + (int64_t)(np - 1) * d, last, sb.s, zm, B, d, st);
   if (c.variant == RLT_V2 && (t0 + np) % c.chunk == 0)
-    HIPCHK(hipMemcpyAsync(s->rho, s->s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(sb.rho, sb.s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
 }
 
 struct ScanOut {
@@ -479,26 +535,29 @@ struct ScanOut {
   int lp_valid = 1 << 30;           // columns c >= lp_valid are not written
 };
 
-// Readout of buffered positions c0 .. c0+n-1 (scan-relative) held in sbuf [B][kReadoutPositions][d].
-void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st, const float* src = nullptr,
-             int64_t src_sb = 0) {
+// Readout of buffered positions c0 .. c0+n-1 (scan-relative) of sequences b0 .. b0+nb-1, held in
+// sbuf [B][kReadoutPositions][d] (or at src with sequence stride src_sb).
+void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st, int b0, int nb,
+             const float* src = nullptr, int64_t src_sb = 0) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
-  const int d = c.d, V = c.vocab, B = s->B;
-  const int rows = B * n;
+  const int d = c.d, V = c.vocab;
+  const int rows = nb * n;
   RowMap sm; sm.tn = n; sm.sb = src ? src_sb : (int64_t)kReadoutPositions * d; sm.st = d;
-  if (!src) src = s->sbuf;
+  if (!src) src = s->sbuf + (int64_t)b0 * kReadoutPositions * d;
+  void* xr = (char*)s->xr + (int64_t)b0 * kReadoutPositions * d * m->esz;
+  float* lbuf = s->lbuf + (int64_t)b0 * kReadoutPositions * V;
   if (o.s_out) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * d; dm.st = d;
-    copy_rows(src, sm, o.s_out + (int64_t)c0 * d, dm, rows, d, st);
+    copy_rows(src, sm, o.s_out + ((int64_t)b0 * o.ld_b + c0) * d, dm, rows, d, st);
   }
   if (!o.logits && !o.lp) return;
-  rmsnorm(dt, src, sm, m->nO, s->xr, d, rows, d, c.rms_eps, st);
-  EpArgs a; a.out = s->lbuf; a.ldo = V;
-  gemm(dt, Ep::StoreF32, a, s->xr, d, m->wout, rows, V, d, st);
+  rmsnorm(dt, src, sm, m->nO, xr, d, rows, d, c.rms_eps, st);
+  EpArgs a; a.out = lbuf; a.ldo = V;
+  gemm(dt, Ep::StoreF32, a, xr, d, m->wout, rows, V, d, st);
   if (o.logits) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
-    copy_rows(s->lbuf, contiguous(V), o.logits + (int64_t)c0 * V, dm, rows, V, st);
+    copy_rows(lbuf, contiguous(V), o.logits + ((int64_t)b0 * o.ld_b + c0) * V, dm, rows, V, st);
   }
   if (o.lp) {
     const int nv = std::min(n, o.lp_valid - c0);
@@ -506,7 +565,8 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
       RowMap lm; lm.tn = nv; lm.sb = (int64_t)n * V; lm.st = V;
       RowMap tm; tm.tn = nv; tm.sb = o.tok_ld; tm.st = 1;
       RowMap om; om.tn = nv; om.sb = o.lp_ld; om.st = 1;
-      logprob(s->lbuf, lm, o.tok + c0, tm, o.lp + c0, om, B * nv, V, st);
+      logprob(lbuf, lm, o.tok + (int64_t)b0 * o.tok_ld + c0, tm, o.lp + (int64_t)b0 * o.lp_ld + c0, om, nb * nv,
+              V, st);
     }
   }
 }
@@ -536,7 +596,15 @@ int scan_groups(rlt_model* m, rlt_state* s) {
 // shape it measured faster than the persistent kernel, whose phases are bound by the
 // latency of reading activations just written by other CUs.
 bool use_persistent(rlt_model* m, rlt_state* s) {
-  return s->scan_ok && m->scan_mode >= 2;
+  return s->scan_ok && m->scan_mode >= 2 && m->scan_mode <= 6;
+}
+
+// Batch slices of the launch-path scan (each an independent chain on its own stream).
+int scan_slices(rlt_model* m, rlt_state* s) {
+  int want = 1;
+  if (m->scan_mode == 7) want = 2;
+  else if (m->scan_mode == 8) want = 4;
+  return std::max(1, std::min(want, s->B));
 }
 
 void persistent_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
@@ -568,7 +636,7 @@ void persistent_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStr
   if (o.logits || o.lp || o.s_out) {
     for (int c0 = 0; c0 < T; c0 += kReadoutPositions) {
       const int n = std::min(kReadoutPositions, T - c0);
-      readout(m, s, c0, n, o, st, s->sall + (int64_t)(start + c0) * d, (int64_t)s->Tm * d);
+      readout(m, s, c0, n, o, st, 0, s->B, s->sall + (int64_t)(start + c0) * d, (int64_t)s->Tm * d);
     }
   }
   check_launch();
@@ -583,11 +651,25 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
   const int d = c.d;
   const int start = s->n_dec;
   const bool want_rows = o.logits || o.lp || o.s_out;
+  // batch slices: independent chains of sequences, each on its own stream
+  const int ns = scan_slices(m, s);
+  std::vector<SliceBufs> sl(ns);
+  std::vector<hipStream_t> ss(ns, st);
+  for (int k = 0; k < ns; ++k) {
+    const int b0 = (int)((int64_t)s->B * k / ns), b1 = (int)((int64_t)s->B * (k + 1) / ns);
+    sl[k] = slice_bufs(m, s, b0, b1 - b0);
+    if (ns > 1) ss[k] = s->sub[k];
+  }
+  if (ns > 1) {
+    HIPCHK(hipEventRecord(s->ev_fork, st));
+    for (int k = 0; k < ns; ++k) HIPCHK(hipStreamWaitEvent(ss[k], s->ev_fork, 0));
+  }
   int c0 = 0;          // scan-relative column of the first buffered position
   int buffered = 0;
   int done = 0;
   auto flush = [&] {
-    if (buffered > 0) readout(m, s, c0, buffered, o, st);
+    if (buffered > 0)
+      for (int k = 0; k < ns; ++k) readout(m, s, c0, buffered, o, ss[k], sl[k].b0, sl[k].B);
     c0 += buffered;
     buffered = 0;
   };
@@ -597,16 +679,26 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
     if (c.variant == RLT_V2) np = std::min(T - done, (t0 / c.chunk + 1) * c.chunk - t0);
     else if (c.variant == RLT_V0) np = std::min(T - done, s->P);
     if (want_rows && buffered + np > kReadoutPositions) flush();
-    decoder_pass(m, s, t0, np, st);
-    if (want_rows) {
-      RowMap dm; dm.tn = np; dm.sb = (int64_t)kReadoutPositions * d; dm.st = d;
-      copy_rows(s->z, contiguous(d), s->sbuf + (int64_t)buffered * d, dm, s->B * np, d, st);
-      buffered += np;
+    for (int k = 0; k < ns; ++k) {
+      decoder_pass(m, s, t0, np, ss[k], sl[k]);
+      if (want_rows) {
+        RowMap dm; dm.tn = np; dm.sb = (int64_t)kReadoutPositions * d; dm.st = d;
+        copy_rows(sl[k].z, contiguous(d), s->sbuf + ((int64_t)sl[k].b0 * kReadoutPositions + buffered) * d, dm,
+                  sl[k].B * np, d, ss[k]);
+      }
     }
+    s->block_steps += c.L_D;
+    if (want_rows) buffered += np;
     done += np;
     s->n_dec = t0 + np;
   }
   if (want_rows) flush();
+  if (ns > 1) {
+    for (int k = 0; k < ns; ++k) {
+      HIPCHK(hipEventRecord(s->ev_join[k], ss[k]));
+      HIPCHK(hipStreamWaitEvent(st, s->ev_join[k], 0));
+    }
+  }
   check_launch();
 }
 
@@ -649,6 +741,7 @@ int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, 
       if (hipMalloc(&m->arena, total) != hipSuccess) fail(RLT_ERR_OOM, "weight arena allocation failed");
       m->arena_bytes = total;
       layout_model(m, (char*)m->arena, &total);
+      fill_zero_u32(m->arena, (int64_t)(total / 4), stream);   // padding rows of tile-major weights
       pack_all(m, W, stream);
       HIPCHK(hipStreamSynchronize(stream));
     } catch (...) {
@@ -716,6 +809,7 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       const int64_t rows = B * s->P;
       s->z = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
       s->xa = dev_alloc(s, rows * d * e, 5);
+      s->dssp = (float*)dev_alloc(s, sizeof(float) * rows * (d / 16), 5);
       s->q = dev_alloc(s, rows * hd * e, 5);
       s->ao = dev_alloc(s, rows * hd * e, 5);
       s->hid = dev_alloc(s, rows * f * e, 5);
@@ -770,6 +864,11 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
         HIPCHK(hipHostMalloc((void**)&s->abort_host, sizeof(int), hipHostMallocDefault));
         *s->abort_host = 0;
       }
+      for (int k = 0; k < kMaxSlices; ++k) {
+        HIPCHK(hipStreamCreateWithFlags(&s->sub[k], hipStreamNonBlocking));
+        HIPCHK(hipEventCreateWithFlags(&s->ev_join[k], hipEventDisableTiming));
+      }
+      HIPCHK(hipEventCreateWithFlags(&s->ev_fork, hipEventDisableTiming));
       rope_table(s->rope, max_len + 1, (int)dh, c.rope_base, stream);
       check_launch();
       m->n_states += 1;
@@ -779,6 +878,11 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
     } catch (...) {
       if (*out) { m->n_states -= 1; *out = nullptr; }
       for (void* p : s->allocs) (void)hipFree(p);
+      for (int k = 0; k < kMaxSlices; ++k) {
+        if (s->sub[k]) (void)hipStreamDestroy(s->sub[k]);
+        if (s->ev_join[k]) (void)hipEventDestroy(s->ev_join[k]);
+      }
+      if (s->ev_fork) (void)hipEventDestroy(s->ev_fork);
       if (s->abort_host) (void)hipHostFree(s->abort_host);
       delete s;
       throw;
@@ -809,6 +913,11 @@ int rlt_state_destroy(rlt_state* s) {
     if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
     for (void* p : s->allocs) HIPCHK(hipFree(p));
     if (s->abort_host) HIPCHK(hipHostFree(s->abort_host));
+    for (int k = 0; k < kMaxSlices; ++k) {
+      if (s->sub[k]) HIPCHK(hipStreamDestroy(s->sub[k]));
+      if (s->ev_join[k]) HIPCHK(hipEventDestroy(s->ev_join[k]));
+    }
+    if (s->ev_fork) HIPCHK(hipEventDestroy(s->ev_fork));
     s->m->n_states -= 1;
     delete s;
   });
@@ -839,7 +948,7 @@ int rlt_state_block_steps(const rlt_state* s, int64_t* out) {
 int rlt_set_scan_mode(rlt_model* m, int mode) {
   return guarded([&] {
     if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
-    if (mode < 0 || mode > 6) fail(RLT_ERR_INVALID_ARG, "scan mode must be 0..6");
+    if (mode < 0 || mode > 8) fail(RLT_ERR_INVALID_ARG, "scan mode must be 0..8");
     m->scan_mode = mode;
   });
 }

@@ -171,8 +171,9 @@ def test_block_step_counts():
         assert steps == expect, (kw, steps)
 
 
-# per-position launches; persistent grid-wide; persistent per-XCD groups with 1, 2, 4 blocks per CU
-SCAN_MODES = [1, 3, 4, 5, 6]
+# per-position launches; persistent grid-wide; persistent per-XCD groups with 1, 2, 4 blocks per CU;
+# per-position launches on 2 and 4 batch slices with a stream each
+SCAN_MODES = [1, 3, 4, 5, 6, 7, 8]
 
 
 @pytest.mark.parametrize("scan_mode", SCAN_MODES)
