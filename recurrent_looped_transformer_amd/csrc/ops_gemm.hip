@@ -13,6 +13,8 @@
 //  - gemm_tiled_bf16: prefill shapes. 128x128 tiles, K step 32, LDS double
 //    buffer, 4 waves x (64x64) of 16x16x32 MFMAs.
 //  - gemm_f32: the fp32 configuration (vector FMA).
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "ops.hpp"
 
@@ -300,6 +302,115 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
   }
 }
 
+// ------------------------------------------------------------------ large (prefill)
+// 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave 128 x 128 (8 x 8 MFMA
+// tiles), K step 64, both operands staged in LDS in the MFMA lane order: a 16-row group of
+// a 64-wide k slice is one 2 KB block whose first (second) 1 KB holds k 16g..16g+7
+// (16g+8..16g+15) of row r for lane 16g + r. Weights arrive in that order already (tile-major
+// packing); activation rows are permuted on their way into LDS. Every fragment read is then
+// one contiguous 1 KB ds_read_b128 per wavefront. Per wave and stage: 32 fragment reads for
+// 128 MFMAs. Next stage's global loads are in registers while the current stage computes.
+constexpr int kBT = 256;                 // tile rows (both operands)
+constexpr int kBK = 64;                  // k per stage
+constexpr int kBStage = kBT * kBK;       // bf16 elements per operand per stage (32 KB)
+
+template <Ep E>
+__global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict__ X, int64_t ldx,
+                                                       const bf16_t* __restrict__ W, int M, int N, int K,
+                                                       EpArgs a) {
+  extern __shared__ uint4 smem[];   // [2 stages][W 2048 uint4 | X 2048 uint4]
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+
+  // tile order: consecutive workgroups share a weight tile column (N) and walk M; the
+  // hardware deals workgroups to the 8 XCDs round-robin, so remap ids to give each XCD a
+  // contiguous run of tiles (its L2 then sees neighbouring X and W tiles).
+  const int ntm = (M + kBT - 1) / kBT, ntn = (N + kBT - 1) / kBT;
+  const int nt = ntm * ntn;
+  int pid = blockIdx.x;
+  if (nt % 8 == 0) pid = (pid % 8) * (nt / 8) + pid / 8;
+  const int tm = pid % ntm, tn = pid / ntm;
+  const int m0 = tm * kBT, n0 = tn * kBT;
+
+  // global -> register assignment (8 x 16 B per operand per thread, index i = 0..7)
+  //  W: 16 tiles x 2 KB contiguous; thread t reads uint4 t + 256 i of the stage's 32 KB, i.e.
+  //     tile 2 i + t / 128 (weights are padded to whole 256-row tiles), uint4 t % 128
+  //  X: row (t >> 3) + 32 i of the tile, 16-byte chunk q = t & 7 of the 128-byte k slice; it
+  //     lands in LDS block row / 16, half q & 1, lane 16 (q >> 1) + row % 16
+  const bf16_t* wbase = W + ((int64_t)(n0 / 16 + (tid >> 7)) * 16 * K) + (tid & 127) * 8;
+  const int64_t wstep = (int64_t)2 * 16 * K;
+  const int xrow = m0 + (tid >> 3), xq = tid & 7;
+  const int xdst = ((tid >> 7) * 128) + (xq & 1) * 64 + (xq >> 1) * 16 + ((tid >> 3) & 15);
+  uint4 rw[8], rx[8];
+#define RLT_GLOAD(k0)                                                                \
+  {                                                                                  \
+    const bf16_t* wp_ = wbase + (int64_t)((k0) >> 6) * 1024;                         \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                  \
+      rw[i] = *reinterpret_cast<const uint4*>(wp_ + i * wstep);                      \
+      const int row_ = min(xrow + 32 * i, M - 1);                                    \
+      rx[i] = *reinterpret_cast<const uint4*>(X + (int64_t)row_ * ldx + xq * 8 + (k0)); \
+    }                                                                                \
+  }
+#define RLT_LSTORE(buf)                                      \
+  {                                                          \
+    uint4* sw_ = smem + (buf) * 4096;                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {          \
+      sw_[tid + 256 * i] = rw[i];                            \
+      sw_[2048 + xdst + 256 * i] = rx[i];                    \
+    }                                                        \
+  }
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / kBK;
+  RLT_GLOAD(0)
+  RLT_LSTORE(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // the last stage reloads itself: unconditional loads keep the staging registers out of memory
+    const int knext = min(kt + 1, nk - 1) * kBK;
+    RLT_GLOAD(knext)
+    const uint4* sw = smem + buf * 4096 + (wn / 16) * 128;
+    const uint4* sx = smem + buf * 4096 + 2048 + (wm / 16) * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 af[8], bfr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[i] = sw[i * 128 + h * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bfr[j] = sx[j * 128 + h * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    RLT_LSTORE(buf ^ 1)   // buffer buf ^ 1 was last read before the previous barrier
+    __syncthreads();
+  }
+#undef RLT_GLOAD
+#undef RLT_LSTORE
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = n0 + wn + i * 16 + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + wm + j * 16 + r;
+      if (m < M) {
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        epilogue<bf16_t, E>(a, m, n, v);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32
 template <Ep E>
 __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int64_t ldx,
@@ -320,6 +431,26 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int
   epilogue<float, E>(a, m, n, v);
 }
 
+// The large-tile kernel needs 128 KB of dynamic LDS; the attribute is set once per process.
+static bool large_gemm_enabled() {
+  static int state = -1;
+  if (state < 0) {
+    const char* env = getenv("RLT_GEMM_LARGE");
+    state = env && env[0] == '0' ? 0 : 1;
+    if (state) {
+      const int bytes = 2 * 2 * kBStage * (int)sizeof(bf16_t);
+#define RLT_SET_LDS(E_)                                                                                        \
+  if (hipFuncSetAttribute((const void*)gemm_large_bf16<E_>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != \
+      hipSuccess)                                                                                              \
+    state = 0;
+      RLT_SET_LDS(Ep::StoreAct) RLT_SET_LDS(Ep::StoreF32) RLT_SET_LDS(Ep::Residual) RLT_SET_LDS(Ep::SwiGLU)
+      RLT_SET_LDS(Ep::QKV) RLT_SET_LDS(Ep::RopeQ) RLT_SET_LDS(Ep::MemKV) RLT_SET_LDS(Ep::Merge) RLT_SET_LDS(Ep::Bias)
+#undef RLT_SET_LDS
+    }
+  }
+  return state == 1;
+}
+
 template <Ep E>
 static void launch(Dt dt, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
                    hipStream_t st) {
@@ -330,15 +461,25 @@ static void launch(Dt dt, const EpArgs& a, const void* X, int64_t ldx, const voi
     hipLaunchKernelGGL(gemm_f32<E>, dim3(blocks), dim3(256), 0, st, (const float*)X, ldx, (const float*)W, M, N, K,
                        a);
   } else if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp) {
+    // Row blocks per workgroup: one (more workgroups, less activation traffic per CU) while the
+    // grid stays near 400 workgroups, else two or four (measured on MI355X decode shapes).
     const dim3 blk(kSkW * WAVE);
     const bf16_t *x = (const bf16_t*)X, *w = (const bf16_t*)W;
-    if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 1>), dim3((N + 15) / 16, 1), blk, 0, st, x, ldx, w, M, N, K, a);
-    else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 2>), dim3((N + 15) / 16, 1), blk, 0, st, x, ldx, w, M, N, K, a);
+    const int ntile = (N + 15) / 16;
+    auto wgs = [&](int nmb) { return (int64_t)ntile * ((M + 16 * nmb - 1) / (16 * nmb)); };
+    int nmb = wgs(1) <= 400 ? 1 : (wgs(2) <= 400 ? 2 : 4);
+    if (nmb == 4 && M <= 32) nmb = 2;
+    const dim3 grid(ntile, (M + 16 * nmb - 1) / (16 * nmb));
+    if (nmb == 1)
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 1>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+    else if (nmb == 2)
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 2>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
     else
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 4>), dim3((N + 15) / 16, (M + 63) / 64), blk, 0, st, x, ldx, w, M,
-                         N, K, a);
+      hipLaunchKernelGGL((gemm_skinny_bf16<E, 4>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+  } else if (large_gemm_enabled() && K % kBK == 0) {
+    const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
+    hipLaunchKernelGGL(gemm_large_bf16<E>, dim3(nt), dim3(256), 2 * 2 * kBStage * sizeof(bf16_t), st,
+                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
   } else {
     hipLaunchKernelGGL(gemm_tiled_bf16<E>, dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st,
                        (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);

@@ -246,34 +246,40 @@ void layout_model(rlt_model* m, char* base, size_t* total) {
     return p;
   };
   auto takef = [&](int64_t n) { return (float*)take(n * 4); };
+  // GEMM weight [N, K]: bf16 weights hold whole 256-row groups of tiles (zero padding rows), the
+  // unit the large-tile GEMM reads
+  auto takew = [&](int64_t N, int64_t K) {
+    const int64_t rows = m->dt == Dt::BF16 ? (N + 255) / 256 * 256 : N;
+    return take(rows * K * e);
+  };
   m->emb = take(V * d * e);
   m->enc.assign(c.L_E, LayerW{});
   for (auto& L : m->enc) {
     L.n1 = takef(d); L.n2 = takef(d);
-    L.wqkv = take(3 * hd * d * e); L.wo = take(d * hd * e); L.w13 = take(2 * f * d * e); L.w2 = take(d * f * e);
+    L.wqkv = takew(3 * hd, d); L.wo = takew(d, hd); L.w13 = takew(2 * f, d); L.w2 = takew(d, f);
   }
   m->wkv.assign(c.L_D > 0 ? c.groups : 0, nullptr);
   if (c.L_D > 0) {
     m->nE = takef(d);
-    for (auto& p : m->wkv) p = take(2 * hd * d * e);
+    for (auto& p : m->wkv) p = takew(2 * hd, d);
   }
   if (c.variant != RLT_V0) {
     m->ns = takef(d); m->bg = takef(d); m->s0 = takef(d);
-    m->wg_e = take(d * d * e); m->wsr = take(2 * d * d * e);
+    m->wg_e = takew(d, d); m->wsr = takew(2 * d, d);
   }
   m->dec.assign(c.L_D, LayerW{});
   for (int l = 0; l < c.L_D; ++l) {
     LayerW& L = m->dec[l];
     L.n1 = takef(d); L.n2 = takef(d); L.n3 = takef(d);
-    L.xq = take(hd * d * e); L.xo = take(d * hd * e);
+    L.xq = takew(hd, d); L.xo = takew(d, hd);
     if (c.share_enc_dec) {
       L.wqkv = m->enc[l].wqkv; L.wo = m->enc[l].wo; L.w13 = m->enc[l].w13; L.w2 = m->enc[l].w2;
     } else {
-      L.wqkv = take(3 * hd * d * e); L.wo = take(d * hd * e); L.w13 = take(2 * f * d * e); L.w2 = take(d * f * e);
+      L.wqkv = takew(3 * hd, d); L.wo = takew(d, hd); L.w13 = takew(2 * f, d); L.w2 = takew(d, f);
     }
   }
   m->nO = takef(d);
-  m->wout = take((V + 15) / 16 * 16 * d * e);   // whole 16-row tiles; the padding rows stay zero
+  m->wout = takew(V, d);
   *total = off;
 }
 
