@@ -56,7 +56,13 @@ typedef enum {
   RLT_ERR_ORDER = -7          /* decoder asked to consume positions not yet encoded */
 } rlt_status;
 
-typedef enum { RLT_FP32 = 0, RLT_BF16 = 1 } rlt_dtype;
+/* Arithmetic type of the path. RLT_BF16 / RLT_FP16: the 16-bit storage and MFMA input type
+ * (weights are rounded to it on create; fp16 keeps 11 significant bits, so weights that are
+ * bf16 values stay exact unless their magnitude is below 2^-14, where fp16 spacing 2^-24 applies).
+ * RLT_FP16X2: fp16 weights, caches and memory, with every GEMM activation input carried as two
+ * fp16 terms (hi + lo, about 22 significant bits) and multiplied as two MFMA products; for the
+ * deepest shapes, where one 16-bit rounding per sublayer input adds up past the logit tolerance. */
+typedef enum { RLT_FP32 = 0, RLT_BF16 = 1, RLT_FP16 = 2, RLT_FP16X2 = 3 } rlt_dtype;
 typedef enum { RLT_V0 = 0, RLT_V1 = 1, RLT_V2 = 2 } rlt_variant;
 
 /* Model configuration ([S] §2.1-§2.7, §3.1; [R] §2-§3). Plain old data. */

@@ -1,6 +1,6 @@
-// Device-side building blocks shared by the kernels: storage types, bf16
-// conversion, 16-byte vector loads, the gfx950 bf16 MFMA tile, wave/block
-// reductions. CDNA4: 64-lane wavefronts, 160 KB LDS per CU.
+// Device-side building blocks shared by the kernels: storage types (fp32, bf16,
+// fp16), conversions, 16-byte vector loads, the gfx950 16-bit MFMA tiles,
+// wave/block reductions. CDNA4: 64-lane wavefronts, 160 KB LDS per CU.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,7 +8,11 @@
 namespace rlt {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
+typedef _Float16 f16_t;   // IEEE binary16 in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));   // bf16 operand of the 16x16x16 MFMA
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
@@ -35,8 +39,31 @@ template <> struct Elem<float> {
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ uint32_t bits(float v) { return f2bf(v); }
+  static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
   static constexpr int VEC = 8;
 };
+template <> struct Elem<f16_t> {
+  static __device__ __forceinline__ float ld(const f16_t* p) { return (float)*p; }
+  static __device__ __forceinline__ void st(f16_t* p, float v) { *p = (f16_t)v; }   // round to nearest even
+  static __device__ __forceinline__ uint32_t bits(float v) { return __builtin_bit_cast(uint16_t, (f16_t)v); }
+  static __device__ __forceinline__ float round(float v) { return (float)(f16_t)v; }
+  static constexpr int VEC = 8;
+};
+// Store v as one 16-bit term at p, or, when lo_off > 0, as two: hi = round(v) at p and
+// lo = round(v - hi) at p + lo_off (a two-term value carries about twice the significand).
+template <typename T>
+__device__ __forceinline__ void store_act(T* p, int64_t lo_off, float v) {
+  const float hi = Elem<T>::round(v);
+  Elem<T>::st(p, hi);
+  if (lo_off) Elem<T>::st(p + lo_off, v - hi);
+}
+template <>
+__device__ __forceinline__ void store_act<float>(float* p, int64_t, float v) { *p = v; }
+// two values rounded to the 16-bit type T, packed low | high << 16
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return Elem<T>::bits(lo) | (Elem<T>::bits(hi) << 16);
+}
 
 // 16-byte load of VEC elements converted to float.
 __device__ __forceinline__ void load16(const float* p, float* o) {
@@ -65,6 +92,22 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4& v, flo
     o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
+template <> __device__ __forceinline__ void unpack16<f16_t>(const uint4& v, float* o) {
+  const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)h[i];
+}
+__device__ __forceinline__ void load16(const f16_t* p, float* o) {
+  unpack16<f16_t>(*reinterpret_cast<const uint4*>(p), o);
+}
+__device__ __forceinline__ void store16(f16_t* p, const float* v) {
+  uint4 o;
+  o.x = pack2<f16_t>(v[0], v[1]);
+  o.y = pack2<f16_t>(v[2], v[3]);
+  o.z = pack2<f16_t>(v[4], v[5]);
+  o.w = pack2<f16_t>(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = o;
+}
 __device__ __forceinline__ void store16(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
@@ -78,13 +121,29 @@ __device__ __forceinline__ void store16(bf16_t* p, const float* v) {
 }
 
 // ---------------------------------------------------------------- MFMA
-// D(16x16, fp32) += A(16x32) * B(32x16), bf16 inputs (gfx950 v_mfma_f32_16x16x32_bf16).
-// Lane l supplies A row (l % 16), k = 8*(l / 16) .. +7 and B column (l % 16), same k;
-// it receives D rows 4*(l / 16) .. +3 of column (l % 16).
+// D(16x16, fp32) += A(16x32) * B(32x16), 16-bit inputs of type T (gfx950
+// v_mfma_f32_16x16x32_bf16 / _f16). Lane l supplies A row (l % 16), k = 8*(l / 16) .. +7
+// and B column (l % 16), same k; it receives D rows 4*(l / 16) .. +3 of column (l % 16).
+template <typename T = bf16_t>
 __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
-  bf16x8 av = __builtin_bit_cast(bf16x8, a);
-  bf16x8 bv = __builtin_bit_cast(bf16x8, b);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+  if constexpr (sizeof(T) == 2 && __is_same(T, f16_t)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+}
+// D(16x16) += A(16x16) * B(16x16): lane l supplies row/column (l % 16), k = 4*(l / 16) .. +3.
+template <typename T = bf16_t>
+__device__ __forceinline__ f32x4 mfma16x16x16(const uint2& a, const uint2& b, f32x4 c) {
+  if constexpr (__is_same(T, f16_t)) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                                 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------- reductions

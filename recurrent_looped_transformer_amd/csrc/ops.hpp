@@ -6,7 +6,7 @@
 
 namespace rlt {
 
-enum class Dt : int { F32 = 0, BF16 = 1 };
+enum class Dt : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 // Row m of a logical [rows, width] matrix lives at  base + (m / tn) * sb + (m % tn) * st
 // (elements). Covers contiguous buffers (tn = rows) and [B][Tmax][d] position slices.
@@ -70,6 +70,11 @@ struct EpArgs {
   int rs_n = 0;
   int rs_d = 0;
   float rs_eps = 0.f;
+  // Two-term activations (16-bit types). out_split > 0: the SwiGLU output and the folded zb are
+  // written as hi at their column and lo = v - hi at column + out_split. x_split != 0: each X row
+  // holds K hi terms followed by K lo terms (row stride >= 2K) and the GEMM adds both products.
+  int64_t out_split = 0;
+  int x_split = 0;
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.
@@ -81,9 +86,10 @@ constexpr int kSkinnyMaxRows = 512;
 void gemm(Dt dt, Ep ep, const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
           hipStream_t st);
 
-// out[m, :] = act(rms(x[rmap(m), :]) * gain)  (gain may be null: plain cast)
+// out[m, :] = act(rms(x[rmap(m), :]) * gain)  (gain may be null: plain cast); out_split > 0
+// also writes the lo terms at column + out_split (two-term activations)
 void rmsnorm(Dt dt, const float* x, RowMap xm, const float* gain, void* out, int64_t ldo, int rows, int d,
-             float eps, hipStream_t st);
+             float eps, hipStream_t st, int64_t out_split = 0);
 // h[rmap(m), :] = emb[tok[m], :]  (fp32 out)
 void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int rows, int d, hipStream_t st);
 // rope table [npos][dh/2] (cos, sin) of angle p * base^(-2i/dh), evaluated in double precision
@@ -132,9 +138,11 @@ struct AttnArgs {
   int pos0 = 0;                 // query i sits at position pos0 + 1 + i
   int window = 0;               // >0: keys max(1, p-window+1)..p ; 0: keys 1..p
   float scale = 1.f;
+  int64_t out_split = 0;        // > 0: output lo terms at column + out_split (two-term activations)
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
-// bf16 many-query attention with MFMA (dh 64 or 128); returns false when the shape is not covered
-bool attn_prefill(const AttnArgs& a, hipStream_t st);
+// 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is
+// not covered
+bool attn_prefill(Dt dt, const AttnArgs& a, hipStream_t st);
 
 }  // namespace rlt

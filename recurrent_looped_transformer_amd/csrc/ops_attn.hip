@@ -8,8 +8,9 @@
 // One workgroup (256 threads) per (head, query row). A group of DH/VEC lanes
 // owns one key at a time (16-byte loads), so a wave reads whole contiguous key
 // rows. Each group runs a single-pass online softmax over its keys, UNR keys per
-// round with all K and V loads of the round issued before use; the groups are
-// combined through LDS at the end. Keys and values are each read once.
+// round; the K and V loads of the next round are issued before the current round
+// computes (two register sets); the groups are combined through LDS at the end.
+// Keys and values are each read once.
 #include "common.hpp"
 #include "ops.hpp"
 
@@ -43,18 +44,22 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  for (int j0 = gi; j0 < n; j0 += NG * UNR) {
-    uint4 kk[UNR], vv[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int j = j0 + u * NG;
-      if (j < n) {
-        const int p = lo + j;
-        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-        kk[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);
-        vv[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);
-      }
-    }
+  constexpr int STEP = NG * UNR;
+  // software pipeline: the next round's keys and values are in flight while this round computes
+  uint4 kk[UNR], vv[UNR], kn[UNR], vn[UNR];
+#define RLT_ATTN_LOAD(K_, V_, J0_)                                              \
+  _Pragma("unroll") for (int u = 0; u < UNR; ++u) {                             \
+    const int j = (J0_) + u * NG;                                               \
+    if (j < n) {                                                                \
+      const int p = lo + j;                                                     \
+      const int slot = a.ring ? (p - 1) % a.cap : p - 1;                        \
+      K_[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);         \
+      V_[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);         \
+    }                                                                           \
+  }
+  RLT_ATTN_LOAD(kk, vv, gi)
+  for (int j0 = gi; j0 < n; j0 += STEP) {
+    if (j0 + STEP < n) RLT_ATTN_LOAD(kn, vn, j0 + STEP)
     float sc[UNR];
     float mx = m_run;
 #pragma unroll
@@ -88,7 +93,13 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
       }
     }
     m_run = mx;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      kk[u] = kn[u];
+      vv[u] = vn[u];
+    }
   }
+#undef RLT_ATTN_LOAD
 #pragma unroll
   for (int e = 0; e < VEC; ++e) part[gi * DH + gl * VEC + e] = acc[e];
   if (gl == 0) {
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
       s += w * part[gg * DH + tid];
     }
     T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
-    Elem<T>::st(op, s / den);
+    store_act<T>(op, a.out_split, s / den);
   }
 }
 
@@ -130,7 +141,8 @@ static void attn_dispatch(const AttnArgs& a, hipStream_t st) {
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.nq <= 0) return;
   if (dt == Dt::F32) attn_dispatch<float>(a, st);
-  else attn_dispatch<bf16_t>(a, st);
+  else if (dt == Dt::BF16) attn_dispatch<bf16_t>(a, st);
+  else attn_dispatch<f16_t>(a, st);
 }
 
 }  // namespace rlt
@@ -149,25 +161,18 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 // registers. Softmax statistics are fp32 per query column, online over key tiles.
 namespace rlt {
 
-typedef short bf16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16x16x16(const uint2& a, const uint2& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a), __builtin_bit_cast(bf16x4_t, b), c,
-                                                   0, 0, 0);
-}
-
-template <int DH>
+template <typename T, int DH>
 __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8;
   __shared__ __align__(16) uint4 sK[BK][KP];
-  __shared__ __align__(16) bf16_t sVt[DH][VP];
+  __shared__ __align__(16) uint16_t sVt[DH][VP];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int g = lane >> 4, c = lane & 15;
   const int myq = qb * 64 + wave * 16 + c;             // query index within this call
   const bool qvalid = myq < a.nq;
   const int qpos = a.pos0 + 1 + myq;
-  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq + h * DH;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq + h * DH;
   uint4 qf[DH / 32];
 #pragma unroll
   for (int kc = 0; kc < DH / 32; ++kc) qf[kc] = *reinterpret_cast<const uint4*>(Q + kc * 32 + g * 8);
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   const int qlast = min(a.nq, qb * 64 + 64);          // queries of this block: [qb*64, qlast)
   const int kmax = a.pos0 + qlast;                     // last key position any query here needs
   const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * 64 - a.window + 1) : 1;
-  const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
-  const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   for (int k0 = kmin; k0 <= kmax; k0 += BK) {
     __syncthreads();
     for (int idx = tid; idx < BK * (DH / 8); idx += 256) {
@@ -195,8 +200,8 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sVt[part * 8 + 2 * e][j] = (bf16_t)(w[e] & 0xffffu);
-        sVt[part * 8 + 2 * e + 1][j] = (bf16_t)(w[e] >> 16);
+        sVt[part * 8 + 2 * e][j] = (uint16_t)(w[e] & 0xffffu);
+        sVt[part * 8 + 2 * e + 1][j] = (uint16_t)(w[e] >> 16);
       }
     }
     __syncthreads();
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
     for (int st = 0; st < 4; ++st) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32(sK[st * 16 + c][kc * 4 + g], qf[kc], acc);
+      for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32<T>(sK[st * 16 + c][kc * 4 + g], qf[kc], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kp = k0 + st * 16 + 4 * g + i;
@@ -234,8 +239,8 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
         pv[i] = __expf(s[st][i] - m_use);
         lsum += pv[i];
       }
-      pb[st].x = (uint32_t)f2bf(pv[0]) | ((uint32_t)f2bf(pv[1]) << 16);
-      pb[st].y = (uint32_t)f2bf(pv[2]) | ((uint32_t)f2bf(pv[3]) << 16);
+      pb[st].x = pack2<T>(pv[0], pv[1]);
+      pb[st].y = pack2<T>(pv[2], pv[3]);
     }
     lsum += __shfl_xor(lsum, 16, WAVE);
     lsum += __shfl_xor(lsum, 32, WAVE);
@@ -246,28 +251,40 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) {
         const uint2 av = *reinterpret_cast<const uint2*>(&sVt[db * 16 + c][st * 16 + 4 * g]);
-        o[db] = mfma16x16x16(av, pb[st], o[db]);
+        o[db] = mfma16x16x16<T>(av, pb[st], o[db]);
       }
     }
   }
   if (qvalid) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + ((int64_t)b * a.nq + myq) * a.ldo + h * DH;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.nq + myq) * a.ldo + h * DH;
 #pragma unroll
     for (int db = 0; db < DH / 16; ++db) {
+      float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
       uint2 w;
-      w.x = (uint32_t)f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
-      w.y = (uint32_t)f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
+      w.x = pack2<T>(v[0], v[1]);
+      w.y = pack2<T>(v[2], v[3]);
       *reinterpret_cast<uint2*>(out + db * 16 + 4 * g) = w;
+      if (a.out_split) {   // lo terms
+        uint2 l;
+        l.x = pack2<T>(v[0] - Elem<T>::round(v[0]), v[1] - Elem<T>::round(v[1]));
+        l.y = pack2<T>(v[2] - Elem<T>::round(v[2]), v[3] - Elem<T>::round(v[3]));
+        *reinterpret_cast<uint2*>(out + a.out_split + db * 16 + 4 * g) = l;
+      }
     }
   }
 }
 
-bool attn_prefill(const AttnArgs& a, hipStream_t st) {
-  if (a.dh != 64 && a.dh != 128) return false;
+bool attn_prefill(Dt dt, const AttnArgs& a, hipStream_t st) {
+  if ((a.dh != 64 && a.dh != 128) || dt == Dt::F32) return false;
   const dim3 grid((a.nq + 63) / 64, a.H, a.B);
-  if (a.dh == 64) hipLaunchKernelGGL(flash_prefill_k<64>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(flash_prefill_k<128>, grid, dim3(256), 0, st, a);
+  if (dt == Dt::BF16) {
+    if (a.dh == 64) hipLaunchKernelGGL((flash_prefill_k<bf16_t, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((flash_prefill_k<bf16_t, 128>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.dh == 64) hipLaunchKernelGGL((flash_prefill_k<f16_t, 64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((flash_prefill_k<f16_t, 128>), grid, dim3(256), 0, st, a);
+  }
   return true;
 }
 

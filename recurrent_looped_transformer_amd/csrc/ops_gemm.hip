@@ -6,12 +6,14 @@
 // row pairs packed next to each other (rotary pairs, SwiGLU W1/W3 rows, merge
 // gate/state rows) meet in one lane and the epilogue needs no shuffles.
 //
-//  - gemm_skinny_bf16: decode shapes (M = batch rows <= a few hundred). One
+//  - gemm_skinny: decode shapes (M = batch rows <= a few hundred). One
 //    workgroup streams 16 weight rows once for up to 64 activation rows; eight
 //    waves split K, keep the tile's loads in flight together and reduce through
 //    LDS. Bandwidth-bound on the weights. Carries the folded RMSNorm (see EpArgs).
-//  - gemm_tiled_bf16: prefill shapes. 128x128 tiles, K step 32, LDS double
+//  - gemm_large: prefill shapes, 256x256 tiles (see below).
+//  - gemm_tiled: prefill fallback. 128x128 tiles, K step 32, LDS double
 //    buffer, 4 waves x (64x64) of 16x16x32 MFMAs.
+//  The 16-bit kernels take T = bf16_t or f16_t (storage and MFMA input type).
 //  - gemm_f32: the fp32 configuration (vector FMA).
 #include <stdlib.h>
 
@@ -38,7 +40,7 @@ __device__ __forceinline__ int64_t kv_off(const EpArgs& a, int b, int h, int pos
 // Applies the epilogue to acc values v of row m, features n..n+3. Returns the sum of
 // squares of the new residual values when the Residual epilogue folds the next RMSNorm
 // (fold_zb set), else 0.
-template <typename T, Ep E>
+template <typename T, Ep E, bool kFold = false>
 __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v[4]) {
   T* out = reinterpret_cast<T*>(a.out);
   if constexpr (E == Ep::StoreAct) {
@@ -53,13 +55,13 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     const float4 old = *reinterpret_cast<const float4*>(r);
     const float z[4] = {old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]};
     *reinterpret_cast<float4*>(r) = make_float4(z[0], z[1], z[2], z[3]);
-    if (a.fold_zb) {
+    if (kFold && a.fold_zb) {
       T* zb = reinterpret_cast<T*>(a.fold_zb) + (int64_t)m * a.fold_ld + n;
       const float4 gn = *reinterpret_cast<const float4*>(a.fold_gain + n);
-      Elem<T>::st(zb, z[0] * gn.x);
-      Elem<T>::st(zb + 1, z[1] * gn.y);
-      Elem<T>::st(zb + 2, z[2] * gn.z);
-      Elem<T>::st(zb + 3, z[3] * gn.w);
+      store_act<T>(zb, a.out_split, z[0] * gn.x);
+      store_act<T>(zb + 1, a.out_split, z[1] * gn.y);
+      store_act<T>(zb + 2, a.out_split, z[2] * gn.z);
+      store_act<T>(zb + 3, a.out_split, z[3] * gn.w);
       return z[0] * z[0] + z[1] * z[1] + z[2] * z[2] + z[3] * z[3];
     }
   } else if constexpr (E == Ep::Bias) {
@@ -68,8 +70,8 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     for (int i = 0; i < 4; ++i) r[i] = v[i] + a.bias[n + i];
   } else if constexpr (E == Ep::SwiGLU) {
     T* o = out + (int64_t)m * a.ldo + (n >> 1);
-    Elem<T>::st(o, v[0] * sigmoidf_(v[0]) * v[1]);
-    Elem<T>::st(o + 1, v[2] * sigmoidf_(v[2]) * v[3]);
+    store_act<T>(o, a.out_split, v[0] * sigmoidf_(v[0]) * v[1]);
+    store_act<T>(o + 1, a.out_split, v[2] * sigmoidf_(v[2]) * v[3]);
   } else if constexpr (E == Ep::RopeQ) {
     const int pos = a.pos0 + 1 + (m % a.tn);
     const int c = n % a.dh;
@@ -115,10 +117,10 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
 // weight tile is in flight at once for K up to kSkW * U * 64. Partial tiles meet in LDS.
 constexpr int kSkW = 8;
 
-template <Ep E, int NMB>
-__global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny_bf16(const bf16_t* __restrict__ X, int64_t ldx,
-                                                                const bf16_t* __restrict__ W, int M, int N,
-                                                                int K, EpArgs a) {
+template <typename T, Ep E, int NMB>
+__global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__ X, int64_t ldx,
+                                                           const T* __restrict__ W, int M, int N, int K,
+                                                           EpArgs a) {
   constexpr int U = NMB == 1 ? 8 : (NMB == 2 ? 4 : 2);
   constexpr int RPW = NMB * 16 / kSkW;     // rows per wave in the row-scale prologue
   __shared__ f32x4 red[kSkW][NMB][WAVE];
@@ -142,22 +144,24 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny_bf16(const bf16_t* __
     }
   }
 
-  const bf16_t* wp = W + (int64_t)blockIdx.x * 16 * K + lane * 8;   // tile-major weight tile
-  const bf16_t* xp[NMB];
+  const T* wp = W + (int64_t)blockIdx.x * 16 * K + lane * 8;   // tile-major weight tile
+  const T* xp[NMB];
 #pragma unroll
   for (int j = 0; j < NMB; ++j) xp[j] = X + (int64_t)min(m0 + j * 16 + r, M - 1) * ldx + g * 16;
   f32x4 acc[NMB];
 #pragma unroll
   for (int j = 0; j < NMB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nch = K / 64;
-  for (int c0 = wave; c0 < nch; c0 += kSkW * U) {
+  // two-term X: chunks nch .. 2 nch - 1 are the lo terms, against the same weight chunks
+  const int nch = K / 64, ncx = a.x_split ? 2 * nch : nch;
+  for (int c0 = wave; c0 < ncx; c0 += kSkW * U) {
     uint4 wa[U][2], xb[U][NMB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kSkW;
-      if (c < nch) {
-        wa[u][0] = *reinterpret_cast<const uint4*>(wp + c * 1024);
-        wa[u][1] = *reinterpret_cast<const uint4*>(wp + c * 1024 + 512);
+      if (c < ncx) {
+        const int cw = c < nch ? c : c - nch;
+        wa[u][0] = *reinterpret_cast<const uint4*>(wp + cw * 1024);
+        wa[u][1] = *reinterpret_cast<const uint4*>(wp + cw * 1024 + 512);
 #pragma unroll
         for (int j = 0; j < NMB; ++j) {
           xb[u][j][0] = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
@@ -167,11 +171,11 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny_bf16(const bf16_t* __
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + u * kSkW < nch) {
+      if (c0 + u * kSkW < ncx) {
 #pragma unroll
         for (int j = 0; j < NMB; ++j) {
-          acc[j] = mfma16x16x32(wa[u][0], xb[u][j][0], acc[j]);
-          acc[j] = mfma16x16x32(wa[u][1], xb[u][j][1], acc[j]);
+          acc[j] = mfma16x16x32<T>(wa[u][0], xb[u][j][0], acc[j]);
+          acc[j] = mfma16x16x32<T>(wa[u][1], xb[u][j][1], acc[j]);
         }
       }
     }
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny_bf16(const bf16_t* __
     float ss = 0.f;
     if (m < M && n < N) {
       float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
-      ss = epilogue<bf16_t, E>(a, m, n, v);
+      ss = epilogue<T, E, true>(a, m, n, v);
     }
     if constexpr (E == Ep::Residual) {
       if (a.fold_zb) {
@@ -215,10 +219,9 @@ constexpr int TB = 128;   // tile rows (both operands)
 constexpr int TK = 32;    // k per stage
 constexpr int TPAD = 5;   // uint4 per LDS row (4 used + 1 pad)
 
-template <Ep E>
-__global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict__ X, int64_t ldx,
-                                                       const bf16_t* __restrict__ W, int M, int N, int K,
-                                                       EpArgs a) {
+template <typename T, Ep E>
+__global__ __launch_bounds__(256) void gemm_tiled(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
+                                                  int M, int N, int K, EpArgs a) {
   __shared__ uint4 sW[2][TB][TPAD];
   __shared__ uint4 sX[2][TB][TPAD];
   const int n0 = blockIdx.x * TB;
@@ -231,8 +234,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
   // global load assignment: 2 x 16B of each tile per thread. Activations: row lrow, k group lq.
   // Weights (tile-major): tile wt, row wr, k group 2 * (stage & 1) + wg, half wh, so that 32
   // consecutive threads read 512 contiguous bytes; they land in LDS row 16 wt + wr, slot 2 wg + wh.
-  const bf16_t* wsrc[2];
-  const bf16_t* xsrc[2];
+  const T* wsrc[2];
+  const T* xsrc[2];
   int lrow[2], lq[2], wrow[2], wq[2];
   const int ntiles = (N + 15) / 16;
 #pragma unroll
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
   }
   uint4 rw[2], rx[2];
   auto gload = [&](int k0) {
-    const int64_t wk = (int64_t)(k0 >> 6) * 1024 + ((k0 >> 5) & 1) * 256;
+    const int kw = k0 < K ? k0 : k0 - K;   // two-term X: columns K .. 2K-1 meet the same weights
+    const int64_t wk = (int64_t)(kw >> 6) * 1024 + ((kw >> 5) & 1) * 256;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       rw[i] = *reinterpret_cast<const uint4*>(wsrc[i] + wk);
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / TK;
+  const int nk = (a.x_split ? 2 * K : K) / TK;
   gload(0);
   lstore(0);
   __syncthreads();
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
   }
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(const bf16_t* __restrict_
       const int m = m0 + wm + j * 16 + r;
       if (m < M) {
         float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        epilogue<bf16_t, E>(a, m, n, v);
+        epilogue<T, E>(a, m, n, v);
       }
     }
   }
@@ -314,10 +318,9 @@ constexpr int kBT = 256;                 // tile rows (both operands)
 constexpr int kBK = 64;                  // k per stage
 constexpr int kBStage = kBT * kBK;       // bf16 elements per operand per stage (32 KB)
 
-template <Ep E>
-__global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict__ X, int64_t ldx,
-                                                       const bf16_t* __restrict__ W, int M, int N, int K,
-                                                       EpArgs a) {
+template <typename T, Ep E>
+__global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
+                                                  int M, int N, int K, EpArgs a) {
   extern __shared__ uint4 smem[];   // [2 stages][W 2048 uint4 | X 2048 uint4]
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -339,14 +342,16 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict_
   //     tile 2 i + t / 128 (weights are padded to whole 256-row tiles), uint4 t % 128
   //  X: row (t >> 3) + 32 i of the tile, 16-byte chunk q = t & 7 of the 128-byte k slice; it
   //     lands in LDS block row / 16, half q & 1, lane 16 (q >> 1) + row % 16
-  const bf16_t* wbase = W + ((int64_t)(n0 / 16 + (tid >> 7)) * 16 * K) + (tid & 127) * 8;
+  const T* wbase = W + ((int64_t)(n0 / 16 + (tid >> 7)) * 16 * K) + (tid & 127) * 8;
   const int64_t wstep = (int64_t)2 * 16 * K;
   const int xrow = m0 + (tid >> 3), xq = tid & 7;
   const int xdst = ((tid >> 7) * 128) + (xq & 1) * 64 + (xq >> 1) * 16 + ((tid >> 3) & 15);
   uint4 rw[8], rx[8];
+  const int nkw = K / kBK;   // weight stages; two-term X adds as many lo stages after them
 #define RLT_GLOAD(k0)                                                                \
   {                                                                                  \
-    const bf16_t* wp_ = wbase + (int64_t)((k0) >> 6) * 1024;                         \
+    const int kw_ = ((k0) >> 6) < nkw ? ((k0) >> 6) : ((k0) >> 6) - nkw;             \
+    const T* wp_ = wbase + (int64_t)kw_ * 1024;                                      \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                  \
       rw[i] = *reinterpret_cast<const uint4*>(wp_ + i * wstep);                      \
       const int row_ = min(xrow + 32 * i, M - 1);                                    \
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / kBK;
+  const int nk = a.x_split ? 2 * nkw : nkw;
   RLT_GLOAD(0)
   RLT_LSTORE(0)
   __syncthreads();
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
     }
     RLT_LSTORE(buf ^ 1)   // buffer buf ^ 1 was last read before the previous barrier
     __syncthreads();
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(const bf16_t* __restrict_
       const int m = m0 + wm + j * 16 + r;
       if (m < M) {
         float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        epilogue<bf16_t, E>(a, m, n, v);
+        epilogue<T, E>(a, m, n, v);
       }
     }
   }
@@ -432,16 +437,17 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int
 }
 
 // The large-tile kernel needs 128 KB of dynamic LDS; the attribute is set once per process.
+template <typename T>
 static bool large_gemm_enabled() {
   static int state = -1;
   if (state < 0) {
     const char* env = getenv("RLT_GEMM_LARGE");
     state = env && env[0] == '0' ? 0 : 1;
     if (state) {
-      const int bytes = 2 * 2 * kBStage * (int)sizeof(bf16_t);
-#define RLT_SET_LDS(E_)                                                                                        \
-  if (hipFuncSetAttribute((const void*)gemm_large_bf16<E_>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != \
-      hipSuccess)                                                                                              \
+      const int bytes = 2 * 2 * kBStage * (int)sizeof(T);
+#define RLT_SET_LDS(E_)                                                                                       \
+  if (hipFuncSetAttribute((const void*)gemm_large<T, E_>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != \
+      hipSuccess)                                                                                             \
     state = 0;
       RLT_SET_LDS(Ep::StoreAct) RLT_SET_LDS(Ep::StoreF32) RLT_SET_LDS(Ep::Residual) RLT_SET_LDS(Ep::SwiGLU)
       RLT_SET_LDS(Ep::QKV) RLT_SET_LDS(Ep::RopeQ) RLT_SET_LDS(Ep::MemKV) RLT_SET_LDS(Ep::Merge) RLT_SET_LDS(Ep::Bias)
@@ -449,6 +455,35 @@ static bool large_gemm_enabled() {
     }
   }
   return state == 1;
+}
+
+template <typename T, Ep E>
+static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
+                     hipStream_t st) {
+  const T *x = (const T*)X, *w = (const T*)W;
+  if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp) {
+    // Row blocks per workgroup: one (more workgroups, less activation traffic per CU) while the
+    // grid stays near 400 workgroups, else two or four (measured on MI355X decode shapes).
+    const dim3 blk(kSkW * WAVE);
+    const int ntile = (N + 15) / 16;
+    auto wgs = [&](int nmb) { return (int64_t)ntile * ((M + 16 * nmb - 1) / (16 * nmb)); };
+    int nmb = wgs(1) <= 400 ? 1 : (wgs(2) <= 400 ? 2 : 4);
+    if (nmb == 4 && M <= 32) nmb = 2;
+    const dim3 grid(ntile, (M + 16 * nmb - 1) / (16 * nmb));
+    if (nmb == 1)
+      hipLaunchKernelGGL((gemm_skinny<T, E, 1>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+    else if (nmb == 2)
+      hipLaunchKernelGGL((gemm_skinny<T, E, 2>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny<T, E, 4>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+  } else if (large_gemm_enabled<T>() && K % kBK == 0) {
+    const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
+    hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(256), 2 * 2 * kBStage * sizeof(T), st, x, ldx, w, M, N,
+                       K, a);
+  } else {
+    hipLaunchKernelGGL((gemm_tiled<T, E>), dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st, x, ldx, w,
+                       M, N, K, a);
+  }
 }
 
 template <Ep E>
@@ -460,29 +495,10 @@ static void launch(Dt dt, const EpArgs& a, const void* X, int64_t ldx, const voi
     const int blocks = (int)((total + 255) / 256);
     hipLaunchKernelGGL(gemm_f32<E>, dim3(blocks), dim3(256), 0, st, (const float*)X, ldx, (const float*)W, M, N, K,
                        a);
-  } else if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp) {
-    // Row blocks per workgroup: one (more workgroups, less activation traffic per CU) while the
-    // grid stays near 400 workgroups, else two or four (measured on MI355X decode shapes).
-    const dim3 blk(kSkW * WAVE);
-    const bf16_t *x = (const bf16_t*)X, *w = (const bf16_t*)W;
-    const int ntile = (N + 15) / 16;
-    auto wgs = [&](int nmb) { return (int64_t)ntile * ((M + 16 * nmb - 1) / (16 * nmb)); };
-    int nmb = wgs(1) <= 400 ? 1 : (wgs(2) <= 400 ? 2 : 4);
-    if (nmb == 4 && M <= 32) nmb = 2;
-    const dim3 grid(ntile, (M + 16 * nmb - 1) / (16 * nmb));
-    if (nmb == 1)
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 1>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
-    else if (nmb == 2)
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 2>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
-    else
-      hipLaunchKernelGGL((gemm_skinny_bf16<E, 4>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
-  } else if (large_gemm_enabled() && K % kBK == 0) {
-    const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-    hipLaunchKernelGGL(gemm_large_bf16<E>, dim3(nt), dim3(256), 2 * 2 * kBStage * sizeof(bf16_t), st,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
+  } else if (dt == Dt::BF16) {
+    launch16<bf16_t, E>(a, X, ldx, W, M, N, K, st);
   } else {
-    hipLaunchKernelGGL(gemm_tiled_bf16<E>, dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, M, N, K, a);
+    launch16<f16_t, E>(a, X, ldx, W, M, N, K, st);
   }
 }
 

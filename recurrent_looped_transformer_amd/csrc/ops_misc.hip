@@ -13,7 +13,7 @@ constexpr int kRmsVec = 16;
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, RowMap xm,
                                                  const float* __restrict__ gain, T* __restrict__ out,
-                                                 int64_t ldo, int rows, int d, float eps) {
+                                                 int64_t ldo, int rows, int d, float eps, int64_t lo_off) {
   const int row = blockIdx.x * 4 + threadIdx.x / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   if (row >= rows) return;
@@ -36,10 +36,10 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, Ro
   T* o = out + (int64_t)row * ldo;
   auto put = [&](int c, float4 u) {
     const float4 gv = gain ? *reinterpret_cast<const float4*>(gain + c) : make_float4(1.f, 1.f, 1.f, 1.f);
-    Elem<T>::st(o + c, u.x * inv * gv.x);
-    Elem<T>::st(o + c + 1, u.y * inv * gv.y);
-    Elem<T>::st(o + c + 2, u.z * inv * gv.z);
-    Elem<T>::st(o + c + 3, u.w * inv * gv.w);
+    store_act<T>(o + c, lo_off, u.x * inv * gv.x);
+    store_act<T>(o + c + 1, lo_off, u.y * inv * gv.y);
+    store_act<T>(o + c + 2, lo_off, u.z * inv * gv.z);
+    store_act<T>(o + c + 3, lo_off, u.w * inv * gv.w);
   };
 #pragma unroll
   for (int i = 0; i < kRmsVec; ++i) {
@@ -50,13 +50,18 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, Ro
 }
 
 void rmsnorm(Dt dt, const float* x, RowMap xm, const float* gain, void* out, int64_t ldo, int rows, int d,
-             float eps, hipStream_t st) {
+             float eps, hipStream_t st, int64_t out_split) {
   if (rows <= 0) return;
   const dim3 grid((rows + 3) / 4);
   if (dt == Dt::F32)
-    hipLaunchKernelGGL(rmsnorm_k<float>, grid, dim3(256), 0, st, x, xm, gain, (float*)out, ldo, rows, d, eps);
+    hipLaunchKernelGGL(rmsnorm_k<float>, grid, dim3(256), 0, st, x, xm, gain, (float*)out, ldo, rows, d, eps,
+                       (int64_t)0);
+  else if (dt == Dt::BF16)
+    hipLaunchKernelGGL(rmsnorm_k<bf16_t>, grid, dim3(256), 0, st, x, xm, gain, (bf16_t*)out, ldo, rows, d, eps,
+                       out_split);
   else
-    hipLaunchKernelGGL(rmsnorm_k<bf16_t>, grid, dim3(256), 0, st, x, xm, gain, (bf16_t*)out, ldo, rows, d, eps);
+    hipLaunchKernelGGL(rmsnorm_k<f16_t>, grid, dim3(256), 0, st, x, xm, gain, (f16_t*)out, ldo, rows, d, eps,
+                       out_split);
 }
 
 template <typename T>
@@ -77,7 +82,9 @@ void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int 
   const int64_t total = (int64_t)rows * (d / 4);
   const dim3 grid((unsigned)((total + 255) / 256));
   if (dt == Dt::F32) hipLaunchKernelGGL(embed_k<float>, grid, dim3(256), 0, st, tok, (const float*)emb, h, hm, rows, d);
-  else hipLaunchKernelGGL(embed_k<bf16_t>, grid, dim3(256), 0, st, tok, (const bf16_t*)emb, h, hm, rows, d);
+  else if (dt == Dt::BF16)
+    hipLaunchKernelGGL(embed_k<bf16_t>, grid, dim3(256), 0, st, tok, (const bf16_t*)emb, h, hm, rows, d);
+  else hipLaunchKernelGGL(embed_k<f16_t>, grid, dim3(256), 0, st, tok, (const f16_t*)emb, h, hm, rows, d);
 }
 
 // angle p * base^(-2i/dh), evaluated in double precision, stored as float (cos, sin)
@@ -184,8 +191,11 @@ void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* ds
   if (dt == Dt::F32)
     hipLaunchKernelGGL(pack_k<float>, grid, dim3(256), 0, st, src, src_ld, col0, (float*)dst, dst_ld, dst_col0, rows,
                        cols, (int)kind, dh, row_stride, row_off, 0);
-  else
+  else if (dt == Dt::BF16)
     hipLaunchKernelGGL(pack_k<bf16_t>, grid, dim3(256), 0, st, src, src_ld, col0, (bf16_t*)dst, dst_ld, dst_col0,
+                       rows, cols, (int)kind, dh, row_stride, row_off, tiles ? 1 : 0);
+  else
+    hipLaunchKernelGGL(pack_k<f16_t>, grid, dim3(256), 0, st, src, src_ld, col0, (f16_t*)dst, dst_ld, dst_col0,
                        rows, cols, (int)kind, dh, row_stride, row_off, tiles ? 1 : 0);
 }
 

@@ -79,6 +79,7 @@ struct rlt_model {
   int device = 0;
   Dt dt = Dt::BF16;
   size_t esz = 2;
+  int act = 1;   // 2: GEMM activation inputs are two-term (hi | lo) 16-bit rows
   int hd = 0;
   void* arena = nullptr;
   size_t arena_bytes = 0;
@@ -173,7 +174,7 @@ void validate_config(const rlt_config& c) {
   if (c.chunk < 1 || (c.variant != RLT_V2 && c.chunk != 1)) bad("chunk must be 1 unless RLT-2");
   if (c.chunk > 64) fail(RLT_ERR_UNSUPPORTED, "chunk > 64");
   if (c.share_enc_dec && c.L_E != c.L_D) fail(RLT_ERR_UNSUPPORTED, "sharing needs L_E == L_D");
-  if (c.dtype != RLT_FP32 && c.dtype != RLT_BF16) bad("dtype");
+  if (c.dtype != RLT_FP32 && c.dtype != RLT_BF16 && c.dtype != RLT_FP16 && c.dtype != RLT_FP16X2) bad("dtype");
   if (!(c.rms_eps >= 0.f) || !(c.rope_base > 0.f)) bad("eps / rope base");
 }
 
@@ -249,7 +250,7 @@ void layout_model(rlt_model* m, char* base, size_t* total) {
   // GEMM weight [N, K]: bf16 weights hold whole 256-row groups of tiles (zero padding rows), the
   // unit the large-tile GEMM reads
   auto takew = [&](int64_t N, int64_t K) {
-    const int64_t rows = m->dt == Dt::BF16 ? (N + 255) / 256 * 256 : N;
+    const int64_t rows = m->dt != Dt::F32 ? (N + 255) / 256 * 256 : N;
     return take(rows * K * e);
   };
   m->emb = take(V * d * e);
@@ -290,7 +291,7 @@ void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStr
   auto vec = [&](float* dst, const std::string& name) {
     HIPCHK(hipMemcpyAsync(dst, W.at(name), sizeof(float) * d, hipMemcpyDeviceToDevice, st));
   };
-  const bool tiles = dt == Dt::BF16;   // GEMM weights: tile-major in bf16
+  const bool tiles = dt != Dt::F32;   // GEMM weights: tile-major in the 16-bit types
   auto plain = [&](void* dst, const std::string& name, int rows, int cols, int row_off = 0, int stride = 1) {
     pack_matrix(dt, W.at(name), cols, 0, dst, cols, 0, rows, cols, Pack::Plain, dh, stride, row_off, tiles, st);
   };
@@ -361,6 +362,9 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, Tm = s->Tm;
   const int t0 = s->n_enc;
   const int Bc = (int)std::max<int64_t>(1, std::min<int64_t>(s->B, s->enc_rows / T));
+  // GEMM activation rows: width w, or w hi terms then w lo terms (two-term activations)
+  const int A = m->act, ad = A * d, ahd = A * hd, af = A * f;
+  const int64_t sd = A > 1 ? d : 0, shd = A > 1 ? hd : 0, sf = A > 1 ? f : 0;
   for (int b0 = 0; b0 < s->B; b0 += Bc) {
     const int nb = std::min(Bc, s->B - b0);
     const int rows = nb * T;
@@ -370,9 +374,10 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
     embed(dt, tokens + (int64_t)b0 * T, m->emb, h, hm, rows, d, st);
     for (int l = 0; l < c.L_E; ++l) {
       const LayerW& L = m->enc[l];
-      rmsnorm(dt, h, hm, L.n1, s->exa, d, rows, d, c.rms_eps, st);
+      rmsnorm(dt, h, hm, L.n1, s->exa, ad, rows, d, c.rms_eps, st, sd);
       EpArgs a;
       a.out = s->eq; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0;
+      a.x_split = A > 1;
       AttnArgs at;
       if (s->enc_k) {
         const int64_t lo = (int64_t)l * s->B * H * Tm * dh;
@@ -386,34 +391,36 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T;
       }
       a.kv.ring = 0;
-      gemm(dt, Ep::QKV, a, s->exa, d, L.wqkv, rows, 3 * hd, d, st);
-      at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = hd;
+      gemm(dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
+      at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
-      if (!(dt == Dt::BF16 && T >= 16 && attn_prefill(at, st))) attn_decode(dt, at, st);
-      EpArgs r; r.resid = h; r.rmap = hm;
-      gemm(dt, Ep::Residual, r, s->eao, hd, L.wo, rows, d, hd, st);
-      rmsnorm(dt, h, hm, L.n2, s->exa, d, rows, d, c.rms_eps, st);
-      EpArgs sw; sw.out = s->ehid; sw.ldo = f;
-      gemm(dt, Ep::SwiGLU, sw, s->exa, d, L.w13, rows, 2 * f, d, st);
-      gemm(dt, Ep::Residual, r, s->ehid, f, L.w2, rows, d, f, st);
+      if (!(T >= 16 && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+      EpArgs r; r.resid = h; r.rmap = hm; r.x_split = A > 1;
+      gemm(dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
+      rmsnorm(dt, h, hm, L.n2, s->exa, ad, rows, d, c.rms_eps, st, sd);
+      EpArgs sw; sw.out = s->ehid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
+      gemm(dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
+      gemm(dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
     }
     if (c.L_D > 0) {
       // memory: k^g = RoPE(W^g_K RMSNorm_E(e)), v^g = W^g_V RMSNorm_E(e)  (eq 2.1-2.2)
-      rmsnorm(dt, h, hm, m->nE, s->exa, d, rows, d, c.rms_eps, st);
+      rmsnorm(dt, h, hm, m->nE, s->exa, ad, rows, d, c.rms_eps, st, sd);
       for (int g = 0; g < c.groups; ++g) {
         EpArgs a;
         a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0; a.b0 = b0;
         const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
         a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
-        gemm(dt, Ep::MemKV, a, s->exa, d, m->wkv[g], rows, 2 * hd, d, st);
+        a.x_split = A > 1;
+        gemm(dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
       }
     }
     if (c.variant != RLT_V0) {
       // gate pre-activation W_g,e e_t + b_g: independent of the recurrence, computed token-parallel
-      rmsnorm(dt, h, hm, nullptr, s->exa, d, rows, d, 0.f, st);
+      rmsnorm(dt, h, hm, nullptr, s->exa, ad, rows, d, 0.f, st, sd);
       EpArgs a; a.resid = s->gpre + ((int64_t)b0 * Tm + t0) * d; a.rmap = hm; a.bias = m->bg;
-      gemm(dt, Ep::Bias, a, s->exa, d, m->wg_e, rows, d, d, st);
+      a.x_split = A > 1;
+      gemm(dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
     }
   }
   check_launch();
@@ -435,8 +442,9 @@ SliceBufs slice_bufs(rlt_model* m, rlt_state* s, int b0, int nb) {
   v.b0 = b0; v.B = nb;
   const int64_t r0 = (int64_t)b0 * P;   // first workspace row of the slice
   v.z = s->z + r0 * d; v.dssp = s->dssp + r0 * (d / 16);
-  v.xa = (char*)s->xa + r0 * d * e; v.q = (char*)s->q + r0 * hd * e;
-  v.ao = (char*)s->ao + r0 * hd * e; v.hid = (char*)s->hid + r0 * f * e;
+  const int64_t A = m->act;
+  v.xa = (char*)s->xa + r0 * A * d * e; v.q = (char*)s->q + r0 * hd * e;
+  v.ao = (char*)s->ao + r0 * A * hd * e; v.hid = (char*)s->hid + r0 * A * f * e;
   v.s = s->s + (int64_t)b0 * d; v.rho = s->rho + (int64_t)b0 * d;
   v.e = s->e + (int64_t)b0 * s->Tm * d;
   v.gpre = s->gpre ? s->gpre + (int64_t)b0 * s->Tm * d : nullptr;
@@ -454,74 +462,78 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = sb.B, Tm = s->Tm;
   const int rows = B * np;
   const RowMap zm = contiguous(d);
+  const int A = m->act, ad = A * d, ahd = A * hd, af = A * f;
+  const int64_t sd = A > 1 ? d : 0, shd = A > 1 ? hd : 0, sf = A > 1 ? f : 0;
   if (c.variant == RLT_V0) {
     RowMap em; em.tn = np; em.sb = (int64_t)Tm * d; em.st = d;
     copy_rows(sb.e + (int64_t)t0 * d, em, sb.z, zm, rows, d, st);
   } else {
     // merge (eq 2.9-2.11): r = RMSNorm_s(s_{t-1} or the RLT-2 register), gate and state projection
     const float* src = c.variant == RLT_V1 ? sb.s : sb.rho;
-    rmsnorm(dt, src, contiguous(d), m->ns, sb.xa, d, B, d, c.rms_eps, st);
+    rmsnorm(dt, src, contiguous(d), m->ns, sb.xa, ad, B, d, c.rms_eps, st, sd);
     EpArgs a;
     a.resid = sb.z; a.rmap = zm; a.e = sb.e + (int64_t)t0 * d; a.gpre = sb.gpre + (int64_t)t0 * d;
-    a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha;
-    gemm(dt, Ep::Merge, a, sb.xa, d, m->wsr, B, 2 * d, d, st);
+    a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha; a.x_split = A > 1;
+    gemm(dt, Ep::Merge, a, sb.xa, ad, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
   // Folded RMSNorm on the bf16 decode GEMMs: each residual GEMM also writes bf16(z * gain of the
   // next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the inverse
   // RMS. The first norm of the pass comes from the norm kernel.
-  const bool fold = dt == Dt::BF16 && rows <= kSkinnyMaxRows && d / 16 <= 256;
+  const bool fold = dt != Dt::F32 && rows <= kSkinnyMaxRows && d / 16 <= 256;
   auto norm_in = [&](EpArgs& a, const float* gain) {
     if (fold) {
       a.rs_ssp = sb.dssp; a.rs_n = d / 16; a.rs_d = d; a.rs_eps = c.rms_eps;
     } else {
-      rmsnorm(dt, sb.z, zm, gain, sb.xa, d, rows, d, c.rms_eps, st);
+      rmsnorm(dt, sb.z, zm, gain, sb.xa, ad, rows, d, c.rms_eps, st, sd);
     }
   };
   auto fold_out = [&](EpArgs& r, const float* gain_next) {
     if (fold && gain_next) {
-      r.fold_zb = sb.xa; r.fold_ld = d; r.fold_ssp = sb.dssp; r.fold_gain = gain_next;
+      r.fold_zb = sb.xa; r.fold_ld = ad; r.out_split = sd; r.fold_ssp = sb.dssp; r.fold_gain = gain_next;
     }
   };
-  if (fold && c.L_D > 0) rmsnorm(dt, sb.z, zm, m->dec[0].n1, sb.xa, d, rows, d, c.rms_eps, st);
+  if (fold && c.L_D > 0) rmsnorm(dt, sb.z, zm, m->dec[0].n1, sb.xa, ad, rows, d, c.rms_eps, st, sd);
   for (int l = 0; l < c.L_D; ++l) {
     const LayerW& L = m->dec[l];
     // causal sliding-window self-attention over the ring (current key written first)
     EpArgs a;
     if (l > 0 || !fold) norm_in(a, L.n1);
     a.out = sb.q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
+    a.x_split = A > 1;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
-    gemm(dt, Ep::QKV, a, sb.xa, d, L.wqkv, rows, 3 * hd, d, st);
+    gemm(dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
-    at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = hd; at.B = B; at.nq = np; at.H = H; at.dh = dh;
+    at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
+    at.B = B; at.nq = np; at.H = H; at.dh = dh;
     at.pos0 = t0; at.window = c.window; at.scale = scale;
     attn_decode(dt, at, st);
-    EpArgs r; r.resid = sb.z; r.rmap = zm;
+    EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
-    gemm(dt, Ep::Residual, r, sb.ao, hd, L.wo, rows, d, hd, st);
+    gemm(dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
     // cross-attention to the prefix memory M_<=t of this layer's group
     EpArgs qx;
     norm_in(qx, L.n2);
-    qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0;
-    gemm(dt, Ep::RopeQ, qx, sb.xa, d, L.xq, rows, hd, d, st);
+    qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0; qx.x_split = A > 1;
+    gemm(dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
     at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
     at.cap = Tm; at.ring = 0; at.window = 0;
     attn_decode(dt, at, st);
-    EpArgs r2; r2.resid = sb.z; r2.rmap = zm;
+    EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
-    gemm(dt, Ep::Residual, r2, sb.ao, hd, L.xo, rows, d, hd, st);
+    gemm(dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
     // SwiGLU FFN
     EpArgs sw;
     norm_in(sw, L.n3);
-    sw.out = sb.hid; sw.ldo = f;
-    gemm(dt, Ep::SwiGLU, sw, sb.xa, d, L.w13, rows, 2 * f, d, st);
-    EpArgs r3; r3.resid = sb.z; r3.rmap = zm;
+    sw.out = sb.hid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
+    gemm(dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
+    EpArgs r3; r3.resid = sb.z; r3.rmap = zm; r3.x_split = A > 1;
     fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
-    gemm(dt, Ep::Residual, r3, sb.hid, f, L.w2, rows, d, f, st);
+    gemm(dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
   }
   // s_t = the last position's output of every sequence
   RowMap last; last.tn = 1; last.sb = (int64_t)np * d;
@@ -551,16 +563,17 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
   const int rows = nb * n;
   RowMap sm; sm.tn = n; sm.sb = src ? src_sb : (int64_t)kReadoutPositions * d; sm.st = d;
   if (!src) src = s->sbuf + (int64_t)b0 * kReadoutPositions * d;
-  void* xr = (char*)s->xr + (int64_t)b0 * kReadoutPositions * d * m->esz;
+  const int A = m->act;
+  void* xr = (char*)s->xr + (int64_t)b0 * kReadoutPositions * A * d * m->esz;
   float* lbuf = s->lbuf + (int64_t)b0 * kReadoutPositions * V;
   if (o.s_out) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * d; dm.st = d;
     copy_rows(src, sm, o.s_out + ((int64_t)b0 * o.ld_b + c0) * d, dm, rows, d, st);
   }
   if (!o.logits && !o.lp) return;
-  rmsnorm(dt, src, sm, m->nO, xr, d, rows, d, c.rms_eps, st);
-  EpArgs a; a.out = lbuf; a.ldo = V;
-  gemm(dt, Ep::StoreF32, a, xr, d, m->wout, rows, V, d, st);
+  rmsnorm(dt, src, sm, m->nO, xr, A * d, rows, d, c.rms_eps, st, A > 1 ? d : 0);
+  EpArgs a; a.out = lbuf; a.ldo = V; a.x_split = A > 1;
+  gemm(dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
   if (o.logits) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
     copy_rows(lbuf, contiguous(V), o.logits + ((int64_t)b0 * o.ld_b + c0) * V, dm, rows, V, st);
@@ -739,7 +752,8 @@ int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, 
     try {
       m->cfg = *cfg;
       HIPCHK(hipGetDevice(&m->device));
-      m->dt = cfg->dtype == RLT_FP32 ? Dt::F32 : Dt::BF16;
+      m->dt = cfg->dtype == RLT_FP32 ? Dt::F32 : (cfg->dtype == RLT_BF16 ? Dt::BF16 : Dt::F16);
+      m->act = cfg->dtype == RLT_FP16X2 ? 2 : 1;
       m->esz = cfg->dtype == RLT_FP32 ? 4 : 2;
       m->hd = cfg->n_heads * cfg->d_head;
       size_t total = 0;
@@ -814,21 +828,22 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->rope = (float2*)dev_alloc(s, sizeof(float2) * (Tm + 1) * (dh / 2), 5);
       const int64_t rows = B * s->P;
       s->z = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
-      s->xa = dev_alloc(s, rows * d * e, 5);
+      const int64_t A = m->act;   // two-term activation rows are twice as wide
+      s->xa = dev_alloc(s, rows * A * d * e, 5);
       s->dssp = (float*)dev_alloc(s, sizeof(float) * rows * (d / 16), 5);
       s->q = dev_alloc(s, rows * hd * e, 5);
-      s->ao = dev_alloc(s, rows * hd * e, 5);
-      s->hid = dev_alloc(s, rows * f * e, 5);
+      s->ao = dev_alloc(s, rows * A * hd * e, 5);
+      s->hid = dev_alloc(s, rows * A * f * e, 5);
       const int64_t rr = B * kReadoutPositions;
       s->sbuf = (float*)dev_alloc(s, sizeof(float) * rr * d, 5);
-      s->xr = dev_alloc(s, rr * d * e, 5);
+      s->xr = dev_alloc(s, rr * A * d * e, 5);
       s->lbuf = (float*)dev_alloc(s, sizeof(float) * rr * V, 5);
       s->enc_rows = std::min<int64_t>(B * Tm, std::max<int64_t>(kEncoderRows, Tm));
       const int64_t er = s->enc_rows;
-      s->exa = dev_alloc(s, er * d * e, 5);
+      s->exa = dev_alloc(s, er * A * d * e, 5);
       s->eq = dev_alloc(s, er * hd * e, 5);
-      s->eao = dev_alloc(s, er * hd * e, 5);
-      s->ehid = dev_alloc(s, er * f * e, 5);
+      s->eao = dev_alloc(s, er * A * hd * e, 5);
+      s->ehid = dev_alloc(s, er * A * f * e, 5);
       if (!s->keep_enc) {
         s->ekv_k = dev_alloc(s, er * hd * e, 5);
         s->ekv_v = dev_alloc(s, er * hd * e, 5);

@@ -108,7 +108,7 @@ def _ptr(t: Optional[torch.Tensor]):
 def config_struct(cfg: synth.Config) -> rlt_config:
     return rlt_config(cfg.vocab, cfg.d, cfg.n_heads, cfg.d_head, cfg.L_E, cfg.L_D, cfg.ffn, cfg.window,
                       cfg.groups, cfg.variant, cfg.chunk, 1 if cfg.share else 0,
-                      0 if cfg.dtype == "fp32" else 1, cfg.alpha, cfg.rms_eps, cfg.rope_base)
+                      {"fp32": 0, "bf16": 1, "fp16": 2, "fp16x2": 3}[cfg.path_dtype], cfg.alpha, cfg.rms_eps, cfg.rope_base)
 
 
 def _tensors(params: Dict[str, np.ndarray], device) -> tuple:
