@@ -60,6 +60,59 @@ def encoder_flops(cfg, B: int, T: int) -> float:
     return B * T * per_tok + attn
 
 
+def step_flops(cfg, B: int, t: int) -> float:
+    """Algorithmic flops of one batched decoder transition at position t (weights as GEMMs + attention)."""
+    d, f, V, L, W, hd = cfg.d, cfg.ffn, cfg.vocab, cfg.L_D, cfg.window, cfg.hd
+    P_dec = L * (4 * d * hd + 2 * d * hd + 3 * d * f + 3 * d) + 3 * d * d + 3 * d + V * d + d
+    return 2.0 * P_dec * B + B * L * 4 * hd * (min(t, W) + t)
+
+
+def decode_sweep(shapes, batches, positions, steps: int = 8):
+    """Decoder transitions at batch B and position t: one JSON line per point.
+
+    For each point: encode t + steps tokens, scan positions 1..t-1 untimed, then time the
+    scan of positions t..t+steps-1 with HIP events. Reports us per transition step (the
+    whole batch), the algorithmic bytes / flops of those steps, and their fractions of the
+    8 TB/s HBM and 2.5 PFLOP/s 16-bit MFMA peaks.
+    """
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens
+    for name in shapes:
+        cfg = CONFIGS[name]
+        P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+        model = rlt.Model(cfg, P)
+        del P
+        toks_all = make_tokens(cfg, batch=max(batches), length=max(positions[name]) + steps)
+        for B in batches:
+            for t in positions[name]:
+                st = model.state(B, t + steps, keep_encoder_cache=False)
+                x = torch.as_tensor(np.ascontiguousarray(toks_all[:B, :t + steps])).cuda()
+                rlt.rlt_encode(model.h, st, x)
+                if t > 1:
+                    rlt.rlt_decode_scan(model.h, st, t - 1)
+                stream = torch.cuda.current_stream()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                rlt.rlt_decode_scan(model.h, st, steps)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                rlt.rlt_state_destroy(st)
+                model.states.remove(st)
+                by = scan_bytes(cfg, B, steps, t_start=t - 1)
+                fl = sum(step_flops(cfg, B, tt) for tt in range(t, t + steps))
+                sec = ms / 1e3
+                print(json.dumps({"sweep": "decode", "config": name, "dtype": cfg.path_dtype, "batch": B,
+                                  "position": t, "steps": steps, "us_per_step": ms * 1e3 / steps,
+                                  "transitions_s": B * steps / sec,
+                                  "hbm_GBs": by / sec / 1e9, "hbm_frac": by / sec / 1e9 / HBM_PEAK_GBS,
+                                  "mfma_TFs": fl / sec / 1e12,
+                                  "mfma_frac": fl / sec / 1e12 / BF16_PEAK_TFLOPS}), flush=True)
+        model.close()
+
+
 def cpu_baseline(cfg, P, tokens, sample_B: int):
     from threadpoolctl import threadpool_info
     from oracle import Oracle
@@ -89,6 +142,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--sweep", default="",
+                    help="decode: decoder transitions at batch 1-8 (and the given --sweep-batches) at "
+                         "t = 32 and the prompt length of each shape; prints one JSON line per point")
+    ap.add_argument("--sweep-shapes", default="algo_bf16,medium_lm,paper_shared")
+    ap.add_argument("--sweep-batches", default="1,2,4,8")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the RLT scan shards over independent sequences with no "
@@ -97,6 +155,12 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.sweep == "decode":
+        from recurrent_looped_transformer_amd.synth import CONFIGS
+        shapes = [x for x in args.sweep_shapes.split(",") if x]
+        pos = {n: [32, CONFIGS[n].seq_len] for n in shapes}
+        decode_sweep(shapes, [int(b) for b in args.sweep_batches.split(",")], pos)
+        return
     if args.copy_probe:
         src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -179,7 +243,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16", "fp16x2": "f16x2"}[cfg.path_dtype],
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} replay (encode + decoder scan + log-probs), "
                                f"RLT-{cfg.variant} B={B} T={T}",

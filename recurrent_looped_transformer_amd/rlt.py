@@ -128,6 +128,7 @@ def rlt_create(cfg: synth.Config, params: Dict[str, np.ndarray], device="cuda") 
     c = config_struct(cfg)
     _check(L.rlt_create(ctypes.byref(c), arr, len(params), ctypes.c_void_p(_stream()), ctypes.byref(out)))
     del keep
+    torch.cuda.empty_cache()   # the fp32 staging copies (46.7 GB at the paper shape) go back to the device
     return out
 
 
