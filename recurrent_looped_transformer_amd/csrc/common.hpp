@@ -152,6 +152,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
 }
+// Wavefront sum through DPP lane moves (no LDS round trips): quad swaps, half-row and row
+// mirrors give every lane its 16-lane row sum, two row broadcasts carry the rows into lane 63,
+// which is read back as a wave-uniform value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                               true));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
+  v += dpp_<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]
+  v += dpp_<0x141, 0xf>(v);   // row_half_mirror
+  v += dpp_<0x140, 0xf>(v);   // row_mirror
+  v += dpp_<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Sum over aligned groups of G lanes (G a power of two <= 64), result in every lane of the
+// group: DPP moves within 16-lane rows, lane shuffles across rows.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  if constexpr (G >= 2) v += dpp_<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_<0x141, 0xf>(v);   // row_half_mirror: lane i + lane 7 - i (quad sums)
+  if constexpr (G >= 16) v += dpp_<0x140, 0xf>(v);  // row_mirror: lane i + lane 15 - i (half-row sums)
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, WAVE);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, WAVE);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));

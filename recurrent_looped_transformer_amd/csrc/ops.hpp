@@ -65,7 +65,7 @@ struct EpArgs {
   int64_t fold_ld = 0;
   // Folded RMSNorm, consumer side (decode GEMM): acc of row m is scaled by
   // 1 / sqrt(sum_k rs_ssp[m * rs_n + k] / rs_d + rs_eps) before the epilogue, so X may hold
-  // act(z * gain) instead of act(rms(z) * gain). rs_n <= 256.
+  // act(z * gain) instead of act(rms(z) * gain). rs_n a multiple of 4, <= 256.
   const float* rs_ssp = nullptr;
   int rs_n = 0;
   int rs_d = 0;

@@ -72,8 +72,7 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) dot = fmaf(qv[e], kf[e], dot);
       }
-#pragma unroll
-      for (int o = G / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, WAVE);
+      dot = group_sum_dpp<G>(dot);
       sc[u] = dot;
       mx = fmaxf(mx, dot);
     }

@@ -52,12 +52,14 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     for (int i = 0; i < 4; ++i) o[i] = v[i];
   } else if constexpr (E == Ep::Residual) {
     float* r = a.resid + a.rmap.off(m) + n;
+    // both loads before any store: the stores may alias the gain as far as the compiler knows
     const float4 old = *reinterpret_cast<const float4*>(r);
+    const float4 gn = kFold && a.fold_zb ? *reinterpret_cast<const float4*>(a.fold_gain + n)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
     const float z[4] = {old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]};
     *reinterpret_cast<float4*>(r) = make_float4(z[0], z[1], z[2], z[3]);
     if (kFold && a.fold_zb) {
       T* zb = reinterpret_cast<T*>(a.fold_zb) + (int64_t)m * a.fold_ld + n;
-      const float4 gn = *reinterpret_cast<const float4*>(a.fold_gain + n);
       store_act<T>(zb, a.out_split, z[0] * gn.x);
       store_act<T>(zb + 1, a.out_split, z[1] * gn.y);
       store_act<T>(zb + 2, a.out_split, z[2] * gn.z);
@@ -130,17 +132,16 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r = lane & 15, g = lane >> 4;
 
-  // folded RMSNorm of the input rows: fetch the partial sums now, reduce after the main loop
-  float ssr[RPW][4];
+  // folded RMSNorm of the input rows: fetch the partial sums now (one float4 per lane and
+  // row, no branches: rs_n is a multiple of 4), reduce after the main loop
+  // (the loaded values stay untouched until then, so no wait is placed before the weight loads)
+  float4 ssr[RPW];
   if (a.rs_ssp) {
+    const int k4 = min(lane * 4, a.rs_n - 4);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int m = min(m0 + wave + kSkW * i, M - 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = lane + WAVE * q;
-        ssr[i][q] = k < a.rs_n ? a.rs_ssp[(int64_t)m * a.rs_n + k] : 0.f;
-      }
+      ssr[i] = *reinterpret_cast<const float4*>(a.rs_ssp + (int64_t)m * a.rs_n + k4);
     }
   }
 
@@ -183,10 +184,13 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
 #pragma unroll
   for (int j = 0; j < NMB; ++j) red[wave][j][lane] = acc[j];
   if (a.rs_ssp) {
+    const float live = lane * 4 < a.rs_n ? 1.f : 0.f;
+    float t[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const float t = wave_sum(ssr[i][0] + ssr[i][1] + ssr[i][2] + ssr[i][3]);
-      if (lane == 0) rsl[wave + kSkW * i] = rsqrtf(t / (float)a.rs_d + a.rs_eps);
+    for (int i = 0; i < RPW; ++i) t[i] = wave_sum_dpp((ssr[i].x + ssr[i].y + ssr[i].z + ssr[i].w) * live);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) rsl[wave + kSkW * i] = rsqrtf(t[i] / (float)a.rs_d + a.rs_eps);
     }
   }
   __syncthreads();

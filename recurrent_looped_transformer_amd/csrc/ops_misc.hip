@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const float* __restrict__ x, Ro
     const float4 u = *reinterpret_cast<const float4*>(xr + c);
     ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_dpp(ss);
   const float inv = gain ? rsqrtf(ss / (float)d + eps) : 1.f;
   T* o = out + (int64_t)row * ldo;
   auto put = [&](int c, float4 u) {
