@@ -172,14 +172,16 @@ int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, h
 int rlt_replay(rlt_model* m, rlt_state* state, const int32_t* tokens, int T, float* logprob,
                float* s_out, hipStream_t stream);
 
-/* Scan driver for the decoder transitions: 0 = automatic, 1 = one launch sequence
- * per position (stream-ordered), 2 = persistent cooperative kernel with the
- * automatic work split, 3 = persistent with every workgroup on all sequences,
- * 4/5/6 = persistent with 1/2/4 workgroups per CU, the workgroups of each XCD
- * and dispatch round forming an independent group that owns batch/8, batch/16 or
- * batch/32 sequences (falling back to fewer groups when the batch does not
- * divide). Configurations the persistent kernel does not cover (fp32, d_head
- * other than 64 or 128) always use mode 1. */
+/* Scan driver for the decoder transitions: 0 = automatic (mode 1),
+ * 1 = one launch sequence per position (stream-ordered), 2 = persistent cooperative kernel
+ * with the automatic work split, 3 = persistent with every workgroup on all sequences,
+ * 4/5/6 = persistent with 1/2/4 workgroups per CU, the workgroups of each XCD and dispatch
+ * round forming an independent group that owns batch/8, batch/16 or batch/32 sequences
+ * (falling back to fewer groups when the batch does not divide), 7/8 = mode 1 on 2/4 batch
+ * slices each on its own stream, 9 = mode 1 with one position's launch sequence captured
+ * once per state as a HIP graph and replayed (RLT-1; positions read from device memory).
+ * The persistent kernel covers bf16 with d_head 64 or 128 only; other configurations use
+ * mode 1 there. */
 int rlt_set_scan_mode(rlt_model* m, int mode);
 
 /* Number of dependent decoder block passes issued since the state was reset

@@ -75,6 +75,11 @@ struct EpArgs {
   // holds K hi terms followed by K lo terms (row stride >= 2K) and the GEMM adds both products.
   int64_t out_split = 0;
   int x_split = 0;
+  // Position from device memory (graph replay of a scan pass): when set, the pass's first
+  // position index is pos_dev[0] instead of pos0, and the merge's e / gpre rows move by
+  // pos_dev[0] * pos_stride elements.
+  const int* pos_dev = nullptr;
+  int64_t pos_stride = 0;
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.
@@ -96,6 +101,12 @@ void embed(Dt dt, const int32_t* tok, const void* emb, float* h, RowMap hm, int 
 void rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
 // dst[rmap_d(m), :] = src[rmap_s(m), :] (fp32 rows)
 void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int d, hipStream_t st);
+// dst[rmap_d(m) + col * col_stride, :] = src[rmap_s(m), :] with col = col_dev[0] read on the device
+void copy_rows_at(const float* src, RowMap sm, float* dst, RowMap dm, const int* col_dev, int64_t col_stride,
+                  int rows, int d, hipStream_t st);
+// scan position words for graph replay: p[0] = position index, p[1] = readout buffer column
+void set_scan_pos(int* p, int pos, int col, hipStream_t st);
+void advance_scan_pos(int* p, int np, hipStream_t st);
 // p[0 .. n) = 0 (32-bit words), a kernel rather than a memset so the call is capture-safe
 void fill_zero_u32(void* p, int64_t n, hipStream_t st);
 // s[b, :] = s0 (fp32) for b < B; used for H_0 and the RLT-2 register
@@ -139,6 +150,7 @@ struct AttnArgs {
   int window = 0;               // >0: keys max(1, p-window+1)..p ; 0: keys 1..p
   float scale = 1.f;
   int64_t out_split = 0;        // > 0: output lo terms at column + out_split (two-term activations)
+  const int* pos_dev = nullptr; // when set, pos0 is read from pos_dev[0] (graph replay)
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
 // 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is

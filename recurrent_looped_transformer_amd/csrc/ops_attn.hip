@@ -27,16 +27,14 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   const int h = blockIdx.x;
   const int row = blockIdx.y;
   const int b = row / a.nq, qi = row % a.nq;
-  const int pos = a.pos0 + 1 + qi;
+  const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + qi;
   const int lo = a.window > 0 ? max(1, pos - a.window + 1) : 1;
   const int n = pos - lo + 1;
   const int tid = threadIdx.x, gi = tid / G, gl = tid % G;
 
+  // the query's raw bits now, unpacked after the first keys are requested (no wait in between)
   const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)row * a.ldq + h * DH + gl * VEC;
-  float qv[VEC];
-  load16(qp, qv);
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) qv[e] *= a.scale;
+  const uint4 qraw = *reinterpret_cast<const uint4*>(qp);
   const int64_t hb = (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH + gl * VEC;
   const T* kb = reinterpret_cast<const T*>(a.k) + hb;
   const T* vb = reinterpret_cast<const T*>(a.v) + hb;
@@ -58,6 +56,10 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     }                                                                           \
   }
   RLT_ATTN_LOAD(kk, vv, gi)
+  float qv[VEC];
+  unpack16<T>(qraw, qv);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qv[e] *= a.scale;
   for (int j0 = gi; j0 < n; j0 += STEP) {
     if (j0 + STEP < n) RLT_ATTN_LOAD(kn, vn, j0 + STEP)
     float sc[UNR];

@@ -22,13 +22,36 @@
 
 namespace rlt {
 
-template <typename T>
-__device__ __forceinline__ void rope_pair(const EpArgs& a, int pos, int c, float& x0, float& x1) {
-  const float2 cs = a.rope[(int64_t)pos * (a.dh >> 1) + (c >> 1)];
+__device__ __forceinline__ float2 rope_cs(const EpArgs& a, int pos, int c) {
+  return a.rope[(int64_t)pos * (a.dh >> 1) + (c >> 1)];
+}
+__device__ __forceinline__ void rope_apply(float2 cs, float& x0, float& x1) {
   const float y0 = x0 * cs.x - x1 * cs.y;
   const float y1 = x0 * cs.y + x1 * cs.x;
   x0 = y0;
   x1 = y1;
+}
+
+// Epilogue operands a decode GEMM loads before its main loop (they do not depend on it):
+// the residual row and the next norm's gain, or the rotary factors of the lane's features.
+struct EpPre {
+  float4 z, g;
+  float2 cs0, cs1;
+};
+template <Ep E, bool kFold>
+__device__ __forceinline__ EpPre ep_prefetch(const EpArgs& a, int m, int n) {
+  EpPre p{};
+  if constexpr (E == Ep::Residual) {
+    p.z = *reinterpret_cast<const float4*>(a.resid + a.rmap.off(m) + n);
+    if (kFold && a.fold_zb) p.g = *reinterpret_cast<const float4*>(a.fold_gain + n);
+  } else if constexpr (E == Ep::RopeQ || E == Ep::QKV || E == Ep::MemKV) {
+    // same position and channel as the epilogue below (rows m = b * tn + i, position pos0 + 1 + i)
+    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + (m % a.tn);
+    const int c = E == Ep::RopeQ ? n % a.dh : (n % a.hd) % a.dh;
+    p.cs0 = rope_cs(a, pos, c);
+    p.cs1 = rope_cs(a, pos, c + 2);
+  }
+  return p;
 }
 
 // kv slot address (elements) of (sequence b, head h, position pos, channel c)
@@ -41,7 +64,7 @@ __device__ __forceinline__ int64_t kv_off(const EpArgs& a, int b, int h, int pos
 // squares of the new residual values when the Residual epilogue folds the next RMSNorm
 // (fold_zb set), else 0.
 template <typename T, Ep E, bool kFold = false>
-__device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v[4]) {
+__device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v[4], const EpPre* pre = nullptr) {
   T* out = reinterpret_cast<T*>(a.out);
   if constexpr (E == Ep::StoreAct) {
 #pragma unroll
@@ -53,9 +76,9 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
   } else if constexpr (E == Ep::Residual) {
     float* r = a.resid + a.rmap.off(m) + n;
     // both loads before any store: the stores may alias the gain as far as the compiler knows
-    const float4 old = *reinterpret_cast<const float4*>(r);
-    const float4 gn = kFold && a.fold_zb ? *reinterpret_cast<const float4*>(a.fold_gain + n)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 old = pre ? pre->z : *reinterpret_cast<const float4*>(r);
+    const float4 gn = !(kFold && a.fold_zb) ? make_float4(0.f, 0.f, 0.f, 0.f)
+                      : pre ? pre->g : *reinterpret_cast<const float4*>(a.fold_gain + n);
     const float z[4] = {old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]};
     *reinterpret_cast<float4*>(r) = make_float4(z[0], z[1], z[2], z[3]);
     if (kFold && a.fold_zb) {
@@ -75,23 +98,23 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     store_act<T>(o, a.out_split, v[0] * sigmoidf_(v[0]) * v[1]);
     store_act<T>(o + 1, a.out_split, v[2] * sigmoidf_(v[2]) * v[3]);
   } else if constexpr (E == Ep::RopeQ) {
-    const int pos = a.pos0 + 1 + (m % a.tn);
+    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + (m % a.tn);
     const int c = n % a.dh;
-    rope_pair<T>(a, pos, c, v[0], v[1]);
-    rope_pair<T>(a, pos, c + 2, v[2], v[3]);
+    rope_apply(pre ? pre->cs0 : rope_cs(a, pos, c), v[0], v[1]);
+    rope_apply(pre ? pre->cs1 : rope_cs(a, pos, c + 2), v[2], v[3]);
     T* o = out + (int64_t)m * a.ldo + n;
 #pragma unroll
     for (int i = 0; i < 4; ++i) Elem<T>::st(o + i, v[i]);
   } else if constexpr (E == Ep::QKV || E == Ep::MemKV) {
     const int b = m / a.tn, i = m % a.tn;
-    const int pos = a.pos0 + 1 + i;
+    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + i;
     int region = n / a.hd;
     const int w = n - region * a.hd;
     if constexpr (E == Ep::MemKV) region += 1;   // memory projection has no query part
     const int h = w / a.dh, c = w % a.dh;
     if (region < 2) {
-      rope_pair<T>(a, pos, c, v[0], v[1]);
-      rope_pair<T>(a, pos, c + 2, v[2], v[3]);
+      rope_apply(pre ? pre->cs0 : rope_cs(a, pos, c), v[0], v[1]);
+      rope_apply(pre ? pre->cs1 : rope_cs(a, pos, c + 2), v[2], v[3]);
     }
     T* dst;
     if (region == 0) dst = out + (int64_t)m * a.ldo + w;
@@ -101,9 +124,10 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
   } else if constexpr (E == Ep::Merge) {
     // rows (2j, 2j+1) of the packed [W_g,r ; W_s] weight: gate part and state projection of feature j
     const int j = n >> 1;
+    const int64_t e0 = a.pos_dev ? (int64_t)a.pos_dev[0] * a.pos_stride : 0;
 #pragma unroll
     for (int rep = 0; rep < a.nrep; ++rep) {
-      const int64_t eo = (int64_t)m * a.eb + (int64_t)rep * a.et + j;
+      const int64_t eo = e0 + (int64_t)m * a.eb + (int64_t)rep * a.et + j;
       float* z = a.resid + a.rmap.off(m * a.nrep + rep) + j;
       z[0] = a.e[eo] + a.alpha * sigmoidf_(a.gpre[eo] + v[0]) * v[1];
       z[1] = a.e[eo + 1] + a.alpha * sigmoidf_(a.gpre[eo + 1] + v[2]) * v[3];
@@ -145,6 +169,12 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     }
   }
 
+  // the epilogue wave's operands (residual row, gain, rotary factors) are requested first
+  EpPre pre{};
+  if (wave < NMB) {
+    const int em = m0 + wave * 16 + r, en = n0 + 4 * g;
+    if (em < M && en < N) pre = ep_prefetch<E, true>(a, em, en);
+  }
   const T* wp = W + (int64_t)blockIdx.x * 16 * K + lane * 8;   // tile-major weight tile
   const T* xp[NMB];
 #pragma unroll
@@ -205,7 +235,7 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     float ss = 0.f;
     if (m < M && n < N) {
       float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
-      ss = epilogue<T, E, true>(a, m, n, v);
+      ss = epilogue<T, E, true>(a, m, n, v, &pre);
     }
     if constexpr (E == Ep::Residual) {
       if (a.fold_zb) {

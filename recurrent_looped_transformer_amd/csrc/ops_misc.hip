@@ -119,6 +119,39 @@ void copy_rows(const float* src, RowMap sm, float* dst, RowMap dm, int rows, int
   hipLaunchKernelGGL(copy_rows_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, sm, dst, dm, rows, d);
 }
 
+__global__ void copy_rows_at_k(const float* __restrict__ src, RowMap sm, float* __restrict__ dst, RowMap dm,
+                               const int* __restrict__ col_dev, int64_t col_stride, int rows, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = d / 4;
+  if (idx >= (int64_t)rows * per) return;
+  const int m = (int)(idx / per), c = (int)(idx % per) * 4;
+  const int64_t o = dm.off(m) + (int64_t)col_dev[0] * col_stride + c;
+  *reinterpret_cast<float4*>(dst + o) = *reinterpret_cast<const float4*>(src + sm.off(m) + c);
+}
+
+void copy_rows_at(const float* src, RowMap sm, float* dst, RowMap dm, const int* col_dev, int64_t col_stride,
+                  int rows, int d, hipStream_t st) {
+  if (rows <= 0) return;
+  const int64_t total = (int64_t)rows * (d / 4);
+  hipLaunchKernelGGL(copy_rows_at_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, sm, dst, dm,
+                     col_dev, col_stride, rows, d);
+}
+
+__global__ void set_scan_pos_k(int* p, int pos, int col) {
+  p[0] = pos;
+  p[1] = col;
+}
+__global__ void advance_scan_pos_k(int* p, int np) {
+  p[0] += np;
+  p[1] += np;
+}
+void set_scan_pos(int* p, int pos, int col, hipStream_t st) {
+  hipLaunchKernelGGL(set_scan_pos_k, dim3(1), dim3(1), 0, st, p, pos, col);
+}
+void advance_scan_pos(int* p, int np, hipStream_t st) {
+  hipLaunchKernelGGL(advance_scan_pos_k, dim3(1), dim3(1), 0, st, p, np);
+}
+
 __global__ void fill_zero_k(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;

@@ -172,8 +172,27 @@ def test_block_step_counts():
 
 
 # per-position launches; persistent grid-wide; persistent per-XCD groups with 1, 2, 4 blocks per CU;
-# per-position launches on 2 and 4 batch slices with a stream each
-SCAN_MODES = [1, 3, 4, 5, 6, 7, 8]
+# per-position launches on 2 and 4 batch slices with a stream each; graph replay per position
+SCAN_MODES = [1, 3, 4, 5, 6, 7, 8, 9]
+
+
+def test_graph_replay_matches_launches():
+    """Mode 9 (one position's launch sequence captured as a HIP graph and replayed per position)
+    equals mode 1 bit for bit: a 60-position prefill, then 10 rlt_step calls (each a replay and
+    an eager readout between replays), and a 70-position rlt_replay whose readout flushes after
+    64 replays."""
+    cfg = ALGO.replace(batch=8, seq_len=70)
+    P = make_params(cfg)
+    x = make_tokens(cfg)
+    outs = {}
+    for mode in (1, 9):
+        logits, s, _ = gpu_prefill(cfg, P, x, steps_from=60, scan_mode=mode)
+        lp, _ = gpu_replay(cfg, P, x, scan_mode=mode)
+        outs[mode] = (logits, s, lp)
+    for a, b in zip(outs[1], outs[9]):
+        assert np.array_equal(a, b)
+    ref_lp, ref_logits, _ = oracle_replay(cfg, P, x)
+    check_logits(cfg, "graph replay logits", outs[9][0], ref_logits)
 
 
 @pytest.mark.parametrize("scan_mode", SCAN_MODES)
@@ -193,9 +212,10 @@ def test_algo_bf16_reduced(variant, scan_mode):
 @pytest.mark.parametrize("scan_mode", SCAN_MODES)
 @pytest.mark.parametrize("kw", [dict(variant=V2, chunk=4), dict(variant=V2, chunk=3), dict(L_D=0),
                                 dict(groups=4), dict(share=True, L_E=4), dict(window=1), dict(batch=3),
-                                dict(variant=V2, chunk=3, batch=32)],
+                                dict(variant=V2, chunk=3, batch=32), dict(compute="fp16"),
+                                dict(compute="fp16x2"), dict(compute="fp16x2", variant=V2, chunk=3, batch=5)],
                          ids=["rlt2_k4", "rlt2_k3", "no_decoder", "groups_LD", "shared", "window1", "batch3",
-                              "rlt2_k3_b32"])
+                              "rlt2_k3_b32", "fp16", "fp16x2", "fp16x2_rlt2_b5"])
 def test_bf16_variants_small(kw, scan_mode):
     cfg = ALGO.replace(**{"batch": 8, "seq_len": 21, **kw})
     P = make_params(cfg)
