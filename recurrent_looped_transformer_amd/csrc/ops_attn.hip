@@ -154,114 +154,173 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 // (greeksharifa summary §2.2: each encoder layer processes the given positions
 // together under a causal mask).
 //
-// Block = 4 waves = 64 queries (16 per wave) of one (sequence, head); keys and
-// values stream through LDS in tiles of 64 positions (V stored transposed). Each
-// wave computes S^T = K Q^T with 16x16x32 MFMAs: lane l then holds the scores of
-// keys 4g..4g+3 (g = l / 16) of query l % 16, which is exactly the B operand layout
-// of the 16x16x16 MFMA used for O^T += V^T P^T, so probabilities never leave
-// registers. Softmax statistics are fp32 per query column, online over key tiles.
+// Block = 4 waves = 256 queries at dh 64 (64 per wave, as 4 MFMA column blocks of 16; 128
+// queries as 2 blocks of 16 per wave at dh 128) of one (sequence, head); keys and values stream through LDS in tiles of 64 positions, double
+// buffered (the next tile's loads are in registers while the current one computes; V is
+// stored transposed, 4 keys per 8-byte write). Each wave computes S^T = K Q^T with 16x16x32
+// MFMAs: lane l then holds the scores of keys 4g..4g+3 (g = l / 16) of query l % 16, which is
+// exactly the B operand layout of the 16x16x16 MFMA used for O^T += V^T P^T, so
+// probabilities never leave registers; each K or V^T fragment read from LDS feeds the four
+// query blocks of the wave. Softmax statistics are fp32 per query, online over key tiles.
 namespace rlt {
 
-template <typename T, int DH>
+// QB query blocks of 16 per wave: up to 4 at dh 64 and 2 at dh 128 (register budget); short
+// sequences take one so that the grid keeps enough workgroups.
+template <typename T, int DH, int QB>
 __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
-  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8;
-  __shared__ __align__(16) uint4 sK[BK][KP];
-  __shared__ __align__(16) uint16_t sVt[DH][VP];
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = 4 * QW;
+  constexpr int PARTS = DH / 8;                      // 16-byte chunks of a key row
+  constexpr int LOADERS = 16 * PARTS;                // threads that stage a tile: 4 keys x 8 values each
+  __shared__ __align__(16) uint4 sK[2][BK][KP];
+  __shared__ __align__(16) uint16_t sVt[2][DH][VP];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int g = lane >> 4, c = lane & 15;
-  const int myq = qb * 64 + wave * 16 + c;             // query index within this call
-  const bool qvalid = myq < a.nq;
-  const int qpos = a.pos0 + 1 + myq;
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq + h * DH;
-  uint4 qf[DH / 32];
+  const int q0 = qb * QBLK + wave * QW;              // first query (within this call) of the wave
+  uint4 qf[QB][DH / 32];
+  int qpos[QB];
+  bool qvalid[QB];
 #pragma unroll
-  for (int kc = 0; kc < DH / 32; ++kc) qf[kc] = *reinterpret_cast<const uint4*>(Q + kc * 32 + g * 8);
-  f32x4 o[DH / 16];
+  for (int j = 0; j < QB; ++j) {
+    const int myq = q0 + j * 16 + c;
+    qvalid[j] = myq < a.nq;
+    qpos[j] = a.pos0 + 1 + myq;
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq +
+                        h * DH;
 #pragma unroll
-  for (int i = 0; i < DH / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const int qlast = min(a.nq, qb * 64 + 64);          // queries of this block: [qb*64, qlast)
-  const int kmax = a.pos0 + qlast;                     // last key position any query here needs
-  const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * 64 - a.window + 1) : 1;
+    for (int kc = 0; kc < DH / 32; ++kc) qf[j][kc] = *reinterpret_cast<const uint4*>(Q + kc * 32 + g * 8);
+  }
+  f32x4 o[QB][DH / 16];
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) o[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
+  const int qlast = min(a.nq, (qb + 1) * QBLK);        // queries of this block: [qb*QBLK, qlast)
+  const int kmax = a.pos0 + qlast;                       // last key position any query here needs
+  const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * QBLK - a.window + 1) : 1;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
-  for (int k0 = kmin; k0 <= kmax; k0 += BK) {
-    __syncthreads();
-    for (int idx = tid; idx < BK * (DH / 8); idx += 256) {
-      const int j = idx / (DH / 8), part = idx % (DH / 8);
-      const int p = k0 + j;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (p <= kmax) {
+
+  // staging: thread t < LOADERS owns keys 4 jq .. 4 jq + 3 (jq = t / PARTS), 16-byte chunk part
+  const int jq = tid / PARTS, part = tid % PARTS;
+  uint4 rk[4], rv[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = k0 + 4 * jq + e;
+      rk[e] = make_uint4(0, 0, 0, 0);
+      rv[e] = make_uint4(0, 0, 0, 0);
+      if (tid < LOADERS && p <= kmax) {
         const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-        kv = *reinterpret_cast<const uint4*>(Kb + (int64_t)slot * DH + part * 8);
-        vv = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + part * 8);
-      }
-      sK[j][part] = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[part * 8 + 2 * e][j] = (uint16_t)(w[e] & 0xffffu);
-        sVt[part * 8 + 2 * e + 1][j] = (uint16_t)(w[e] >> 16);
+        rk[e] = *reinterpret_cast<const uint4*>(Kb + (int64_t)slot * DH + part * 8);
+        rv[e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + part * 8);
       }
     }
-    __syncthreads();
-    float s[4][4];
-    float tmax = -INFINITY;
+  };
+  auto lstore = [&](int buf) {
+    if (tid < LOADERS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sK[buf][4 * jq + e][part] = rk[e];
+      const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w}, {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
+                                {rv[2].x, rv[2].y, rv[2].z, rv[2].w}, {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {   // value e of the chunk for the 4 keys: one 8-byte write of V^T
+        const int sh = (e & 1) * 16;
+        uint2 t;
+        t.x = ((w[0][e >> 1] >> sh) & 0xffffu) | (((w[1][e >> 1] >> sh) & 0xffffu) << 16);
+        t.y = ((w[2][e >> 1] >> sh) & 0xffffu) | (((w[3][e >> 1] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint2*>(&sVt[buf][part * 8 + e][4 * jq]) = t;
+      }
+    }
+  };
+
+  gload(kmin);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kmin; k0 <= kmax; k0 += BK) {
+    const bool more = k0 + BK <= kmax;
+    if (more) gload(k0 + BK);
+    float s[QB][4][4];
+    float tmax[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      uint4 kf[DH / 32];
 #pragma unroll
-      for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32<T>(sK[st * 16 + c][kc * 4 + g], qf[kc], acc);
+      for (int kc = 0; kc < DH / 32; ++kc) kf[kc] = sK[buf][st * 16 + c][kc * 4 + g];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kp = k0 + st * 16 + 4 * g + i;
-        const bool ok = qvalid && kp <= qpos && kp <= kmax && (a.window <= 0 || kp > qpos - a.window);
-        s[st][i] = ok ? acc[i] * a.scale : -INFINITY;
-        tmax = fmaxf(tmax, s[st][i]);
+      for (int j = 0; j < QB; ++j) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32<T>(kf[kc], qf[j][kc], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kp = k0 + st * 16 + 4 * g + i;
+          const bool ok = qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
+          s[j][st][i] = ok ? acc[i] * a.scale : -INFINITY;
+          tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+        }
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
-    const float m_new = fmaxf(m_run, tmax);
-    // branch-free: a column with nothing visible yet keeps l = 0 and o = 0 (exp(-inf) = 0)
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = __expf(m_run - m_use);
-    l_run *= corr;
+    uint2 pb[QB][4];
 #pragma unroll
-    for (int i = 0; i < DH / 16; ++i) o[i] *= corr;
-    float lsum = 0.f;
-    uint2 pb[4];
+    for (int j = 0; j < QB; ++j) {
+      float tm = fmaxf(tmax[j], __shfl_xor(tmax[j], 16, WAVE));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, WAVE));
+      const float m_new = fmaxf(m_run[j], tm);
+      // branch-free: a column with nothing visible yet keeps l = 0 and o = 0 (exp(-inf) = 0)
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __expf(m_run[j] - m_use);
+      l_run[j] *= corr;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      float pv[4];
+      for (int i = 0; i < DH / 16; ++i) o[j][i] *= corr;
+      float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = __expf(s[st][i] - m_use);
-        lsum += pv[i];
+      for (int st = 0; st < 4; ++st) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __expf(s[j][st][i] - m_use);
+          lsum += pv[i];
+        }
+        pb[j][st].x = pack2<T>(pv[0], pv[1]);
+        pb[j][st].y = pack2<T>(pv[2], pv[3]);
       }
-      pb[st].x = pack2<T>(pv[0], pv[1]);
-      pb[st].y = pack2<T>(pv[2], pv[3]);
+      lsum += __shfl_xor(lsum, 16, WAVE);
+      lsum += __shfl_xor(lsum, 32, WAVE);
+      l_run[j] += lsum;
+      m_run[j] = m_new;
     }
-    lsum += __shfl_xor(lsum, 16, WAVE);
-    lsum += __shfl_xor(lsum, 32, WAVE);
-    l_run += lsum;
-    m_run = m_new;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) {
-        const uint2 av = *reinterpret_cast<const uint2*>(&sVt[db * 16 + c][st * 16 + 4 * g]);
-        o[db] = mfma16x16x16<T>(av, pb[st], o[db]);
+        const uint2 av = *reinterpret_cast<const uint2*>(&sVt[buf][db * 16 + c][st * 16 + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) o[j][db] = mfma16x16x16<T>(av, pb[j][st], o[j][db]);
       }
     }
+    if (more) lstore(buf ^ 1);   // buffer buf ^ 1 was last read before the previous barrier
+    __syncthreads();
+    buf ^= 1;
   }
-  if (qvalid) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    if (!qvalid[j]) continue;
+    const int myq = q0 + j * 16 + c;
+    const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.nq + myq) * a.ldo + h * DH;
 #pragma unroll
     for (int db = 0; db < DH / 16; ++db) {
-      float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+      float v[4] = {o[j][db][0] * inv, o[j][db][1] * inv, o[j][db][2] * inv, o[j][db][3] * inv};
       uint2 w;
       w.x = pack2<T>(v[0], v[1]);
       w.y = pack2<T>(v[2], v[3]);
@@ -276,15 +335,26 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   }
 }
 
+template <typename T, int DH>
+static void launch_flash(const AttnArgs& a, hipStream_t st) {
+  constexpr int QBMAX = DH >= 128 ? 2 : 4;
+  if (a.nq <= 512) {
+    hipLaunchKernelGGL((flash_prefill_k<T, DH, 1>), dim3((a.nq + 63) / 64, a.H, a.B), dim3(256), 0, st, a);
+  } else {
+    const int qblk = 64 * QBMAX;
+    hipLaunchKernelGGL((flash_prefill_k<T, DH, QBMAX>), dim3((a.nq + qblk - 1) / qblk, a.H, a.B), dim3(256), 0, st,
+                       a);
+  }
+}
+
 bool attn_prefill(Dt dt, const AttnArgs& a, hipStream_t st) {
   if ((a.dh != 64 && a.dh != 128) || dt == Dt::F32) return false;
-  const dim3 grid((a.nq + 63) / 64, a.H, a.B);
   if (dt == Dt::BF16) {
-    if (a.dh == 64) hipLaunchKernelGGL((flash_prefill_k<bf16_t, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((flash_prefill_k<bf16_t, 128>), grid, dim3(256), 0, st, a);
+    if (a.dh == 64) launch_flash<bf16_t, 64>(a, st);
+    else launch_flash<bf16_t, 128>(a, st);
   } else {
-    if (a.dh == 64) hipLaunchKernelGGL((flash_prefill_k<f16_t, 64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((flash_prefill_k<f16_t, 128>), grid, dim3(256), 0, st, a);
+    if (a.dh == 64) launch_flash<f16_t, 64>(a, st);
+    else launch_flash<f16_t, 128>(a, st);
   }
   return true;
 }
