@@ -59,6 +59,9 @@ struct EpArgs {
   // Folded RMSNorm, producer side (Residual epilogue, decode GEMM): besides z += acc, write
   // fold_zb[m * fold_ld + n] = act(z_new * fold_gain[n]) and fold_ssp[m * (N / 16) + n / 16] =
   // sum of z_new^2 over the 16 features of the tile.
+  // The Merge epilogue folds the same way (one row per sequence, nrep 1): fold_zb gets
+  // act(u * fold_gain) and fold_ssp[m * (N / 16) + tile] the sum of u^2 over the tile's 8
+  // features (N = 2d weight rows, so d / 8 partials per row).
   void* fold_zb = nullptr;
   float* fold_ssp = nullptr;
   const float* fold_gain = nullptr;
@@ -80,6 +83,12 @@ struct EpArgs {
   // pos_dev[0] * pos_stride elements.
   const int* pos_dev = nullptr;
   int64_t pos_stride = 0;
+  // Copies of the new residual rows (Residual epilogue): dup_rows[dup_map.off(m) + n], and for
+  // the last row of each sequence (m % tn == tn - 1) dup_last[(m / tn) * dup_last_ld + n].
+  float* dup_rows = nullptr;
+  RowMap dup_map;
+  float* dup_last = nullptr;
+  int64_t dup_last_ld = 0;
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.

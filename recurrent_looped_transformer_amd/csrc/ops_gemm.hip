@@ -80,7 +80,11 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     const float4 gn = !(kFold && a.fold_zb) ? make_float4(0.f, 0.f, 0.f, 0.f)
                       : pre ? pre->g : *reinterpret_cast<const float4*>(a.fold_gain + n);
     const float z[4] = {old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]};
-    *reinterpret_cast<float4*>(r) = make_float4(z[0], z[1], z[2], z[3]);
+    const float4 z4 = make_float4(z[0], z[1], z[2], z[3]);
+    *reinterpret_cast<float4*>(r) = z4;
+    if (a.dup_rows) *reinterpret_cast<float4*>(a.dup_rows + a.dup_map.off(m) + n) = z4;
+    if (a.dup_last && m % a.tn == a.tn - 1)
+      *reinterpret_cast<float4*>(a.dup_last + (int64_t)(m / a.tn) * a.dup_last_ld + n) = z4;
     if (kFold && a.fold_zb) {
       T* zb = reinterpret_cast<T*>(a.fold_zb) + (int64_t)m * a.fold_ld + n;
       store_act<T>(zb, a.out_split, z[0] * gn.x);
@@ -125,12 +129,21 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     // rows (2j, 2j+1) of the packed [W_g,r ; W_s] weight: gate part and state projection of feature j
     const int j = n >> 1;
     const int64_t e0 = a.pos_dev ? (int64_t)a.pos_dev[0] * a.pos_stride : 0;
+    float u0 = 0.f, u1 = 0.f;
 #pragma unroll
     for (int rep = 0; rep < a.nrep; ++rep) {
       const int64_t eo = e0 + (int64_t)m * a.eb + (int64_t)rep * a.et + j;
       float* z = a.resid + a.rmap.off(m * a.nrep + rep) + j;
-      z[0] = a.e[eo] + a.alpha * sigmoidf_(a.gpre[eo] + v[0]) * v[1];
-      z[1] = a.e[eo + 1] + a.alpha * sigmoidf_(a.gpre[eo + 1] + v[2]) * v[3];
+      u0 = a.e[eo] + a.alpha * sigmoidf_(a.gpre[eo] + v[0]) * v[1];
+      u1 = a.e[eo + 1] + a.alpha * sigmoidf_(a.gpre[eo + 1] + v[2]) * v[3];
+      z[0] = u0;
+      z[1] = u1;
+    }
+    if (kFold && a.fold_zb) {   // nrep == 1: u0, u1 are this row's features j, j + 1
+      T* zb = reinterpret_cast<T*>(a.fold_zb) + (int64_t)m * a.fold_ld + j;
+      store_act<T>(zb, a.out_split, u0 * a.fold_gain[j]);
+      store_act<T>(zb + 1, a.out_split, u1 * a.fold_gain[j + 1]);
+      return u0 * u0 + u1 * u1;
     }
   }
   return 0.f;
@@ -237,9 +250,9 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
       float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
       ss = epilogue<T, E, true>(a, m, n, v, &pre);
     }
-    if constexpr (E == Ep::Residual) {
+    if constexpr (E == Ep::Residual || E == Ep::Merge) {
       if (a.fold_zb) {
-        // lanes r, r+16, r+32, r+48 hold the 16 features of row m
+        // lanes r, r+16, r+32, r+48 hold the tile's features of row m (16, or 8 for Merge)
         ss += __shfl_xor(ss, 16, WAVE);
         ss += __shfl_xor(ss, 32, WAVE);
         if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + blockIdx.x] = ss;

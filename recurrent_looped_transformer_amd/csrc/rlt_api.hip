@@ -115,7 +115,9 @@ struct rlt_state {
   // decoder workspace, rows = B * P
   float* z = nullptr;
   void *xa = nullptr, *q = nullptr, *ao = nullptr, *hid = nullptr;
-  float* dssp = nullptr;   // [rows][d / 16] sums of squares of z (folded RMSNorm)
+  float* dssp = nullptr;   // [rows][d / 8] partial sums of squares of z (folded RMSNorm)
+  void* xs = nullptr;      // [B][act d] merge input: RMSNorm_s(s), or s * gain folded by the last block
+  float* sssp = nullptr;   // [B][d / 16] partial sums of squares of s (folded merge input)
   // readout workspace, rows = B * kReadoutPositions
   float* sbuf = nullptr;
   void* xr = nullptr;
@@ -144,7 +146,8 @@ struct rlt_state {
   hipEvent_t ev_join[kMaxSlices] = {};
   // graph replay of one RLT-1 position (launch path): [0] without, [1] with readout rows
   int* pos_dev = nullptr;                    // [0] position index of the pass, [1] readout column
-  hipGraphExec_t pass_graph[2] = {nullptr, nullptr};
+  // [with readout rows][merge input folded by the previous replay]
+  hipGraphExec_t pass_graph[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
 };
 
 namespace {
@@ -435,8 +438,8 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
 // Sequences b0 .. b0+nb-1 of the state (a batch slice): the pointers of its rows.
 struct SliceBufs {
   int b0 = 0, B = 0;
-  float *z, *s, *rho, *e, *gpre, *dssp;
-  void *xa, *q, *ao, *hid, *ring_k, *ring_v, *mem_k, *mem_v;
+  float *z, *s, *rho, *e, *gpre, *dssp, *sssp;
+  void *xa, *xs, *q, *ao, *hid, *ring_k, *ring_v, *mem_k, *mem_v;
 };
 SliceBufs slice_bufs(rlt_model* m, rlt_state* s, int b0, int nb) {
   const rlt_config& c = m->cfg;
@@ -444,8 +447,9 @@ SliceBufs slice_bufs(rlt_model* m, rlt_state* s, int b0, int nb) {
   SliceBufs v;
   v.b0 = b0; v.B = nb;
   const int64_t r0 = (int64_t)b0 * P;   // first workspace row of the slice
-  v.z = s->z + r0 * d; v.dssp = s->dssp + r0 * (d / 16);
+  v.z = s->z + r0 * d; v.dssp = s->dssp + r0 * (d / 8);
   const int64_t A = m->act;
+  v.xs = (char*)s->xs + (int64_t)b0 * A * d * e; v.sssp = s->sssp + (int64_t)b0 * (d / 16);
   v.xa = (char*)s->xa + r0 * A * d * e; v.q = (char*)s->q + r0 * hd * e;
   v.ao = (char*)s->ao + r0 * A * hd * e; v.hid = (char*)s->hid + r0 * A * f * e;
   v.s = s->s + (int64_t)b0 * d; v.rho = s->rho + (int64_t)b0 * d;
@@ -459,9 +463,18 @@ SliceBufs slice_bufs(rlt_model* m, rlt_state* s, int b0, int nb) {
   return v;
 }
 
+// Links between consecutive passes of one scan call.
+struct PassIO {
+  bool in_folded = false;   // xs / sssp hold s_{t-1} * gain_s and its partial sums of squares,
+                            // written by the previous pass's last block (RLT-1, folded norms)
+  bool out_fold = false;    // this pass's last block writes them for the next pass
+  float* rows = nullptr;    // this pass's output rows z also go to rows[rows_map.off(m)]
+  RowMap rows_map;
+};
+
 // pos_dev (graph replay, RLT-1): positions come from pos_dev[0] on the device instead of t0.
 void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, const SliceBufs& sb,
-                  const int* pos_dev = nullptr) {
+                  const int* pos_dev = nullptr, const PassIO& io = PassIO()) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = sb.B, Tm = s->Tm;
@@ -469,24 +482,34 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
   const RowMap zm = contiguous(d);
   const int A = m->act, ad = A * d, ahd = A * hd, af = A * f;
   const int64_t sd = A > 1 ? d : 0, shd = A > 1 ? hd : 0, sf = A > 1 ? f : 0;
+  // Folded RMSNorm on the 16-bit decode GEMMs: each residual GEMM also writes act(z * gain of
+  // the next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the
+  // inverse RMS. The merge folds the first block's norm the same way (8-feature partials) when
+  // the pass has one position; otherwise the first norm of the pass comes from the norm kernel.
+  const bool fold = dt != Dt::F32 && rows <= kSkinnyMaxRows && d / 16 <= 256;
+  const bool chain = fold && c.variant == RLT_V1 && c.L_D > 0;
+  const bool merge_fold = fold && c.variant != RLT_V0 && c.L_D > 0 && np == 1 && d / 8 <= 256;
   if (c.variant == RLT_V0) {
     RowMap em; em.tn = np; em.sb = (int64_t)Tm * d; em.st = d;
     copy_rows(sb.e + (int64_t)t0 * d, em, sb.z, zm, rows, d, st);
   } else {
     // merge (eq 2.9-2.11): r = RMSNorm_s(s_{t-1} or the RLT-2 register), gate and state projection
-    const float* src = c.variant == RLT_V1 ? sb.s : sb.rho;
-    rmsnorm(dt, src, contiguous(d), m->ns, sb.xa, ad, B, d, c.rms_eps, st, sd);
     EpArgs a;
+    if (chain && io.in_folded) {
+      a.rs_ssp = sb.sssp; a.rs_n = d / 16; a.rs_d = d; a.rs_eps = c.rms_eps;
+    } else {
+      const float* src = c.variant == RLT_V1 ? sb.s : sb.rho;
+      rmsnorm(dt, src, contiguous(d), m->ns, sb.xs, ad, B, d, c.rms_eps, st, sd);
+    }
     a.resid = sb.z; a.rmap = zm; a.e = sb.e + (int64_t)t0 * d; a.gpre = sb.gpre + (int64_t)t0 * d;
     a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha; a.x_split = A > 1;
     if (pos_dev) { a.e = sb.e; a.gpre = sb.gpre; a.pos_dev = pos_dev; a.pos_stride = d; }
-    gemm(dt, Ep::Merge, a, sb.xa, ad, m->wsr, B, 2 * d, d, st);
+    if (merge_fold) {
+      a.fold_zb = sb.xa; a.fold_ld = ad; a.out_split = sd; a.fold_ssp = sb.dssp; a.fold_gain = m->dec[0].n1;
+    }
+    gemm(dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
-  // Folded RMSNorm on the bf16 decode GEMMs: each residual GEMM also writes bf16(z * gain of the
-  // next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the inverse
-  // RMS. The first norm of the pass comes from the norm kernel.
-  const bool fold = dt != Dt::F32 && rows <= kSkinnyMaxRows && d / 16 <= 256;
   auto norm_in = [&](EpArgs& a, const float* gain) {
     if (fold) {
       a.rs_ssp = sb.dssp; a.rs_n = d / 16; a.rs_d = d; a.rs_eps = c.rms_eps;
@@ -499,12 +522,14 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
       r.fold_zb = sb.xa; r.fold_ld = ad; r.out_split = sd; r.fold_ssp = sb.dssp; r.fold_gain = gain_next;
     }
   };
-  if (fold && c.L_D > 0) rmsnorm(dt, sb.z, zm, m->dec[0].n1, sb.xa, ad, rows, d, c.rms_eps, st, sd);
+  if (fold && c.L_D > 0 && !merge_fold)
+    rmsnorm(dt, sb.z, zm, m->dec[0].n1, sb.xa, ad, rows, d, c.rms_eps, st, sd);
   for (int l = 0; l < c.L_D; ++l) {
     const LayerW& L = m->dec[l];
     // causal sliding-window self-attention over the ring (current key written first)
     EpArgs a;
     if (l > 0 || !fold) norm_in(a, L.n1);
+    else if (merge_fold) { a.rs_ssp = sb.dssp; a.rs_n = d / 8; a.rs_d = d; a.rs_eps = c.rms_eps; }
     a.out = sb.q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
     a.x_split = A > 1; a.pos_dev = pos_dev;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
@@ -540,11 +565,23 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     gemm(dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
     EpArgs r3; r3.resid = sb.z; r3.rmap = zm; r3.x_split = A > 1;
     fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
+    if (l + 1 == c.L_D) {
+      // the pass's outputs: s_t (last position of each sequence), the readout rows, and the
+      // next merge's folded input
+      r3.tn = np; r3.dup_last = sb.s; r3.dup_last_ld = d;
+      r3.dup_rows = io.rows; r3.dup_map = io.rows_map;
+      if (chain && io.out_fold) {
+        r3.fold_zb = sb.xs; r3.fold_ld = ad; r3.out_split = sd; r3.fold_ssp = sb.sssp; r3.fold_gain = m->ns;
+      }
+    }
     gemm(dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
   }
-  // s_t = the last position's output of every sequence
-  RowMap last; last.tn = 1; last.sb = (int64_t)np * d;
-  copy_rows(sb.z + (int64_t)(np - 1) * d, last, sb.s, zm, B, d, st);
+  if (c.L_D == 0) {
+    // s_t = the last position's output of every sequence
+    RowMap last; last.tn = 1; last.sb = (int64_t)np * d;
+    copy_rows(sb.z + (int64_t)(np - 1) * d, last, sb.s, zm, B, d, st);
+    if (io.rows) copy_rows(sb.z, zm, io.rows, io.rows_map, rows, d, st);
+  }
   if (c.variant == RLT_V2 && (t0 + np) % c.chunk == 0)
     HIPCHK(hipMemcpyAsync(sb.rho, sb.s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
 }
@@ -672,14 +709,17 @@ void persistent_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStr
 // for every position: the kernels read the position from s->pos_dev, advanced by the graph's
 // last kernel. Replaying saves the per-launch submission cost (measured: 2.6 -> 1.7 us per
 // dependent kernel). The readout stays eager every kReadoutPositions positions.
-hipGraphExec_t pass_graph(rlt_model* m, rlt_state* s, bool want_rows) {
-  hipGraphExec_t& ge = s->pass_graph[want_rows ? 1 : 0];
+hipGraphExec_t pass_graph(rlt_model* m, rlt_state* s, bool want_rows, bool in_folded) {
+  hipGraphExec_t& ge = s->pass_graph[want_rows ? 1 : 0][in_folded ? 1 : 0];
   if (ge) return ge;
   const int d = m->cfg.d;
   hipStream_t cs = s->sub[0];
   const SliceBufs sb = slice_bufs(m, s, 0, s->B);
   HIPCHK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-  decoder_pass(m, s, 0, 1, cs, sb, s->pos_dev);
+  PassIO io;
+  io.in_folded = in_folded;
+  io.out_fold = true;
+  decoder_pass(m, s, 0, 1, cs, sb, s->pos_dev, io);
   if (want_rows) {
     RowMap dm; dm.tn = 1; dm.sb = (int64_t)kReadoutPositions * d; dm.st = d;
     copy_rows_at(sb.z, contiguous(d), s->sbuf, dm, s->pos_dev + 1, d, s->B, d, cs);
@@ -710,7 +750,9 @@ bool use_graph(rlt_model* m, rlt_state* s) {
 void graph_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
   const int start = s->n_dec;
   const bool want_rows = o.logits || o.lp || o.s_out;
-  hipGraphExec_t ge = pass_graph(m, s, want_rows);
+  // the first replay of the call normalizes s_{t-1} itself; later replays take the folded
+  // merge input the previous replay wrote (the launch path's chaining)
+  hipGraphExec_t ge0 = pass_graph(m, s, want_rows, false), ge1 = pass_graph(m, s, want_rows, true);
   set_scan_pos(s->pos_dev, start, 0, st);
   int c0 = 0, buffered = 0;
   for (int done = 0; done < T; ++done) {
@@ -720,7 +762,7 @@ void graph_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t
       buffered = 0;
       set_scan_pos(s->pos_dev, start + done, 0, st);
     }
-    HIPCHK(hipGraphLaunch(ge, st));
+    HIPCHK(hipGraphLaunch(done == 0 ? ge0 : ge1, st));
     s->block_steps += m->cfg.L_D;
     if (want_rows) buffered += 1;
     s->n_dec = start + done + 1;
@@ -771,12 +813,14 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
     else if (c.variant == RLT_V0) np = std::min(T - done, s->P);
     if (want_rows && buffered + np > kReadoutPositions) flush();
     for (int k = 0; k < ns; ++k) {
-      decoder_pass(m, s, t0, np, ss[k], sl[k]);
+      PassIO io;
+      io.in_folded = done > 0;
+      io.out_fold = done + np < T;
       if (want_rows) {
-        RowMap dm; dm.tn = np; dm.sb = (int64_t)kReadoutPositions * d; dm.st = d;
-        copy_rows(sl[k].z, contiguous(d), s->sbuf + ((int64_t)sl[k].b0 * kReadoutPositions + buffered) * d, dm,
-                  sl[k].B * np, d, ss[k]);
+        io.rows = s->sbuf + ((int64_t)sl[k].b0 * kReadoutPositions + buffered) * d;
+        io.rows_map.tn = np; io.rows_map.sb = (int64_t)kReadoutPositions * d; io.rows_map.st = d;
       }
+      decoder_pass(m, s, t0, np, ss[k], sl[k], nullptr, io);
     }
     s->block_steps += c.L_D;
     if (want_rows) buffered += np;
@@ -902,7 +946,9 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->z = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
       const int64_t A = m->act;   // two-term activation rows are twice as wide
       s->xa = dev_alloc(s, rows * A * d * e, 5);
-      s->dssp = (float*)dev_alloc(s, sizeof(float) * rows * (d / 16), 5);
+      s->dssp = (float*)dev_alloc(s, sizeof(float) * rows * (d / 8), 5);
+      s->xs = dev_alloc(s, B * A * d * e, 5);
+      s->sssp = (float*)dev_alloc(s, sizeof(float) * B * (d / 16), 5);
       s->q = dev_alloc(s, rows * hd * e, 5);
       s->ao = dev_alloc(s, rows * A * hd * e, 5);
       s->hid = dev_alloc(s, rows * A * f * e, 5);
@@ -1005,8 +1051,9 @@ int rlt_state_reset(rlt_model* m, rlt_state* s, hipStream_t stream) {
 int rlt_state_destroy(rlt_state* s) {
   return guarded([&] {
     if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
-    for (auto& ge : s->pass_graph)
-      if (ge) HIPCHK(hipGraphExecDestroy(ge));
+    for (auto& gw : s->pass_graph)
+      for (auto& ge : gw)
+        if (ge) HIPCHK(hipGraphExecDestroy(ge));
     for (void* p : s->allocs) HIPCHK(hipFree(p));
     if (s->abort_host) HIPCHK(hipHostFree(s->abort_host));
     for (int k = 0; k < kMaxSlices; ++k) {
