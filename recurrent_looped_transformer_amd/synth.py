@@ -268,3 +268,9 @@ def make_tokens(cfg: Config, batch: int | None = None, length: int | None = None
         body = rng.integers(0, cfg.vocab, size=(B, T - 1), dtype=np.int32)
     bos = np.full((B, 1), cfg.bos, dtype=np.int32)
     return np.ascontiguousarray(np.concatenate([bos, body], axis=1).astype(np.int32))
+
+
+def make_logits(batch: int, vocab: int, seed: int, scale: float = 3.0) -> np.ndarray:
+    """fp32 [batch, vocab] synthetic logits, N(0, scale^2) (inputs of the sampling checks)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.ascontiguousarray((rng.standard_normal((batch, vocab)) * scale).astype(np.float32))
