@@ -172,6 +172,42 @@ int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, h
 int rlt_replay(rlt_model* m, rlt_state* state, const int32_t* tokens, int T, float* logprob,
                float* s_out, hipStream_t stream);
 
+/* Behaviour sampling with recorded log-probabilities ([R] §6.2, Figure 4): for each of
+ * `rows` rows of logits (device fp32, row stride ld >= vocab elements) draw
+ *   tokens[b] = argmax_j (logits[b, j] / temperature + G(b, j)),  G = -log(-log U),
+ * a draw from mu = softmax(logits[b] / temperature) over the whole vocabulary (Gumbel-max),
+ * and write logprob[b] = log mu(tokens[b]) (nullable), the denominator of the importance
+ * ratio. U(b, j) is a pure function of (seed, step, b, j): Philox4x64-10 (Salmon et al.,
+ * SC 2011) with key (seed, 0), counter (j / 4, b, step, 0), output word j % 4, and
+ * U = ((x >> 11) + 0.5) * 2^-53. Scores and the log-sum-exp are evaluated in float64.
+ * temperature 0 is greedy decoding (lowest index on ties; logprob 0, a point mass). No
+ * truncated sampling (top-k / top-p) is offered: [R] §6.2 notes that it breaks the support
+ * condition p_Theta << mu of exact importance sampling.
+ * tokens: device int32 [rows]. Errors: INVALID_ARG (null, rows < 0, vocab < 1, ld < vocab,
+ * temperature negative or not finite). Token ids are in [0, vocab). */
+int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
+               uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream);
+
+/* Generation F.2 with on-device behaviour sampling ([S] appendix F.2; [R] §6.2 Figure 4):
+ * consume `first` (device int32 [B], the last emitted token of every row: it is consumed
+ * once before continuing), then n times: draw x_i ~ mu from the new logits as rlt_sample
+ * does with draw index step0 + i, record tokens[b, i] = x_i and logprob[b, i] = log mu(x_i),
+ * and consume x_i before the next draw, except the last one: tokens[:, n-1] is returned
+ * unconsumed and is the next call's `first`. No host synchronisation between steps.
+ * tokens int32 [B, n], logprob fp32 [B, n], logits fp32 [B, n, V] (nullable) on the device.
+ * Needs keep_encoder_cache unless the state is at position 0. Errors: CAPACITY
+ * (n_enc + n > max_len), ORDER (encoded positions not yet consumed), UNSUPPORTED,
+ * STALE_STATE, INVALID_ARG. */
+int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float temperature, uint64_t seed,
+                 uint64_t step0, int32_t* tokens, float* logprob, float* logits, hipStream_t stream);
+
+/* Importance ratio of the replay contract ([R] §6.2 eq 5.5):
+ * ratio[i] = exp(logprob_current[i] - logprob_behaviour[i]) for i < n, with the current
+ * policy's log-probabilities from rlt_replay and the behaviour log-probabilities recorded
+ * at sampling time. Device fp32 arrays; float64 inside. Errors: INVALID_ARG. */
+int rlt_importance_ratio(const float* logprob_current, const float* logprob_behaviour, int64_t n, float* ratio,
+                         hipStream_t stream);
+
 /* Scan driver for the decoder transitions: 0 = automatic (mode 1),
  * 1 = one launch sequence per position (stream-ordered), 2 = persistent cooperative kernel
  * with the automatic work split, 3 = persistent with every workgroup on all sequences,

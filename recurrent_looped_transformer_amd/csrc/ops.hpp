@@ -123,6 +123,14 @@ void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st);
 // out[om(r)] = L[tok[tm(r)]] - logsumexp(L) with L = logits row lm(r); tok < 0 writes 0
 void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows,
              int V, hipStream_t st);
+// Behaviour sampling (one workgroup per row): tok[b * tok_ld] = a draw from
+// softmax(logits[b] / temperature) by Gumbel-max with Philox4x64-10 uniforms (key (seed, 0),
+// counter (j / 4, b, step, 0)); lp[b * lp_ld] (nullable) = log of its probability;
+// next[b] (nullable) = the token again. temperature 0: greedy, lp = 0.
+void sample_rows(const float* logits, int64_t ld, int rows, int V, float temperature, uint64_t seed, uint64_t step,
+                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st);
+// ratio[i] = exp(lp_cur[i] - lp_beh[i]) (float64 inside)
+void importance_ratio(const float* lp_cur, const float* lp_beh, int64_t n, float* ratio, hipStream_t st);
 // pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind.
 // tiles = false: row-major [N][K] (dst_ld = K). tiles = true (bf16 GEMM weights): the
 // tile-major layout below, with K = dst_ld a multiple of 64 and dst_col0 = 0.

@@ -1,0 +1,143 @@
+// Behaviour sampling with recorded log-probabilities, and the importance ratio.
+//
+// The sampler draws each token from mu = softmax(logits / tau) over the whole vocabulary
+// and records log mu of the drawn token, the denominator of the trainer's importance ratio
+// r = exp(log p_Theta - log mu) (jiphyeonjeon.kr review "Recurrent Looped Transformer",
+// §6.2, Figure 4 and eq 5.5). The draw is the Gumbel-max form: argmax_j (logits_j / tau
+// + G_j), G_j = -log(-log U_j), with U_j from the counter-based generator Philox4x64-10
+// (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011):
+// row b, entry j, draw index `step` use key (seed, 0), counter (j / 4, b, step, 0) and
+// output word j % 4, U = ((x >> 11) + 0.5) * 2^-53. Every draw is a pure function of
+// (seed, step, b, j), so a sequence of draws does not depend on how the calls are split.
+// tau = 0 is greedy decoding (lowest index on ties, log mu = 0).
+//
+// One workgroup per row; scores and the log-sum-exp in float64 (a row is tens of
+// thousands of entries: the kernel is a few microseconds whatever its precision).
+#include <climits>
+
+#include "common.hpp"
+#include "ops.hpp"
+
+namespace rlt {
+namespace {
+
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull, kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull, kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+// ten rounds of the two multiply-high/low S-boxes, key advanced by the Weyl constants
+// between rounds
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint64_t lo0 = kPhiloxM0 * c[0], hi0 = __umul64hi(kPhiloxM0, c[0]);
+    const uint64_t lo1 = kPhiloxM1 * c[2], hi1 = __umul64hi(kPhiloxM1, c[2]);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+constexpr int kSampleThreads = 256;
+
+// (score, index) with the larger score winning and the lower index breaking ties
+__device__ __forceinline__ void best_merge(double& y, int& j, double y2, int j2) {
+  if (y2 > y || (y2 == y && j2 < j)) {
+    y = y2;
+    j = j2;
+  }
+}
+// running log-sum-exp (m = max so far, s = sum of exp(z - m))
+__device__ __forceinline__ void lse_merge(double& m, double& s, double m2, double s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+  } else if (m2 > m) {
+    s = s * exp(m - m2) + s2;
+    m = m2;
+  } else {
+    s += s2 * exp(m2 - m);
+  }
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_k(const float* __restrict__ logits, int64_t ld, int V,
+                                                           float tau, uint64_t seed, uint64_t step, int32_t* tok,
+                                                           int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next) {
+  const int b = blockIdx.x;
+  const float* x = logits + (int64_t)b * ld;
+  const bool greedy = !(tau > 0.f);
+  const double dt = (double)tau;
+  double best = -INFINITY, m = -INFINITY, s = 0.0;
+  int bj = INT_MAX;
+  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads) {
+    uint64_t c[4] = {(uint64_t)jb, (uint64_t)b, step, 0ull};
+    if (!greedy) philox4x64_10(c, seed, 0ull);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = 4 * jb + w;
+      if (j < V) {
+        if (greedy) {
+          best_merge(best, bj, (double)x[j], j);
+        } else {
+          const double z = (double)x[j] / dt;
+          const double u = ((double)(c[w] >> 11) + 0.5) * 0x1p-53;
+          best_merge(best, bj, z - log(-log(u)), j);
+          lse_merge(m, s, z, 1.0);
+        }
+      }
+    }
+  }
+  __shared__ double sy[kSampleThreads], sm[kSampleThreads], ss[kSampleThreads];
+  __shared__ int sj[kSampleThreads];
+  sy[threadIdx.x] = best;
+  sj[threadIdx.x] = bj;
+  sm[threadIdx.x] = m;
+  ss[threadIdx.x] = s;
+  __syncthreads();
+  for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
+    if (threadIdx.x < h) {
+      double y = sy[threadIdx.x], mm = sm[threadIdx.x], s1 = ss[threadIdx.x];
+      int j = sj[threadIdx.x];
+      best_merge(y, j, sy[threadIdx.x + h], sj[threadIdx.x + h]);
+      lse_merge(mm, s1, sm[threadIdx.x + h], ss[threadIdx.x + h]);
+      sy[threadIdx.x] = y;
+      sj[threadIdx.x] = j;
+      sm[threadIdx.x] = mm;
+      ss[threadIdx.x] = s1;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int j = sj[0];
+    tok[(int64_t)b * tok_ld] = j;
+    if (next) next[b] = j;
+    if (lp) lp[(int64_t)b * lp_ld] = greedy ? 0.f : (float)((double)x[j] / dt - (sm[0] + log(ss[0])));
+  }
+}
+
+__global__ void ratio_k(const float* __restrict__ a, const float* __restrict__ b, int64_t n, float* __restrict__ r) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) r[i] = (float)exp((double)a[i] - (double)b[i]);
+}
+
+}  // namespace
+
+void sample_rows(const float* logits, int64_t ld, int rows, int V, float temperature, uint64_t seed, uint64_t step,
+                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(sample_k, dim3(rows), dim3(kSampleThreads), 0, st, logits, ld, V, temperature, seed, step, tok,
+                     tok_ld, lp, lp_ld, next);
+}
+
+void importance_ratio(const float* lp_cur, const float* lp_beh, int64_t n, float* ratio, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(ratio_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, lp_cur, lp_beh, n, ratio);
+}
+
+}  // namespace rlt

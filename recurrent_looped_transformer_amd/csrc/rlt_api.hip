@@ -127,6 +127,8 @@ struct rlt_state {
   void *exa = nullptr, *eq = nullptr, *eao = nullptr, *ehid = nullptr;
   void *ekv_k = nullptr, *ekv_v = nullptr;   // attention keys when no encoder cache is kept
   int32_t* toks = nullptr;                   // [B][Tm] shifted next tokens (replay)
+  float* glog = nullptr;                     // [B][V] logits of a generation step
+  int32_t* gtok = nullptr;                   // [B] token drawn last, consumed by the next step
   float* lp = nullptr;                       // [B][Tm] log-probabilities (replay)
   // persistent scan (bf16 configurations it supports)
   bool scan_ok = false;
@@ -967,6 +969,8 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
         s->ekv_v = dev_alloc(s, er * hd * e, 5);
       }
       s->toks = (int32_t*)dev_alloc(s, sizeof(int32_t) * B * Tm, 5);
+      s->glog = (float*)dev_alloc(s, sizeof(float) * B * V, 5);
+      s->gtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
       s->pos_dev = (int*)dev_alloc(s, 256, 5);
       s->lp = (float*)dev_alloc(s, sizeof(float) * B * Tm, 5);
       if (m->dt == Dt::BF16 && scan_supported((int)dh, (int)rows, (int)d, (int)hd, (int)f, (int)Tm, c.L_D)) {
@@ -1150,6 +1154,54 @@ int rlt_replay(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, float* 
       o.lp = logprob; o.lp_ld = T - 1; o.lp_valid = T - 1;
     }
     do_scan(m, s, T, o, stream);
+  });
+}
+
+int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
+               uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream) {
+  return guarded([&] {
+    if (!logits || !tokens) fail(RLT_ERR_INVALID_ARG, "logits and tokens required");
+    if (rows < 0 || vocab < 1 || ld < vocab) fail(RLT_ERR_INVALID_ARG, "rows >= 0, vocab >= 1, ld >= vocab required");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature))
+      fail(RLT_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+    sample_rows(logits, ld, rows, vocab, temperature, seed, step, tokens, 1, logprob, 1, nullptr, stream);
+    check_launch();
+  });
+}
+
+int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float temperature, uint64_t seed,
+                 uint64_t step0, int32_t* tokens, float* logprob, float* logits, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!first || !tokens || !logprob) fail(RLT_ERR_INVALID_ARG, "first, tokens and logprob required");
+    if (n < 1) fail(RLT_ERR_INVALID_ARG, "n >= 1 required");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature))
+      fail(RLT_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+    if (s->n_enc + n > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "generation needs keep_encoder_cache");
+    if (s->n_dec != s->n_enc) fail(RLT_ERR_ORDER, "consume the encoded positions before generating");
+    const int V = m->cfg.vocab;
+    for (int i = 0; i < n; ++i) {
+      // consume the last emitted token, then draw the next one from the new logits
+      do_encode(m, s, i == 0 ? first : s->gtok, 1, stream);
+      ScanOut o;
+      o.logits = logits ? logits + (int64_t)i * V : s->glog;
+      o.ld_b = logits ? n : 1;
+      do_scan(m, s, 1, o, stream);
+      sample_rows(o.logits, o.ld_b * V, s->B, V, temperature, seed, step0 + (uint64_t)i, tokens + i, n, logprob + i,
+                  n, s->gtok, stream);
+    }
+    check_launch();
+  });
+}
+
+int rlt_importance_ratio(const float* logprob_current, const float* logprob_behaviour, int64_t n, float* ratio,
+                         hipStream_t stream) {
+  return guarded([&] {
+    if (n < 0) fail(RLT_ERR_INVALID_ARG, "n >= 0 required");
+    if (n > 0 && (!logprob_current || !logprob_behaviour || !ratio)) fail(RLT_ERR_INVALID_ARG, "null pointer");
+    importance_ratio(logprob_current, logprob_behaviour, n, ratio, stream);
+    check_launch();
   });
 }
 

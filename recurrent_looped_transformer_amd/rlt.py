@@ -26,7 +26,7 @@ STATUS = {0: "RLT_OK", -1: "RLT_ERR_INVALID_ARG", -2: "RLT_ERR_UNSUPPORTED", -3:
 EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create", "rlt_state_reset",
            "rlt_state_destroy", "rlt_state_bytes", "rlt_state_positions", "rlt_encode", "rlt_decode_scan",
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
-           "rlt_last_error"]
+           "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio"]
 
 
 class RltError(RuntimeError):
@@ -75,6 +75,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_replay": [vp, vp, vp, i32, vp, vp, vp],
         "rlt_set_scan_mode": [vp, i32],
         "rlt_state_block_steps": [vp, i64p],
+        "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp],
+        "rlt_generate": [vp, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp],
+        "rlt_importance_ratio": [vp, vp, ctypes.c_int64, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -198,6 +201,28 @@ def rlt_replay(model, state, tokens: torch.Tensor, logprob: torch.Tensor, s_out=
     assert tokens.dtype == torch.int32 and tokens.dim() == 2
     _check(load().rlt_replay(model, state, _ptr(tokens), tokens.shape[1], _ptr(logprob), _ptr(s_out),
                              ctypes.c_void_p(_stream())))
+
+
+def rlt_sample(logits: torch.Tensor, temperature: float, seed: int, step: int, tokens: torch.Tensor,
+               logprob: Optional[torch.Tensor] = None) -> None:
+    assert logits.dtype == torch.float32 and logits.dim() == 2 and tokens.dtype == torch.int32
+    rows, V = logits.shape
+    _check(load().rlt_sample(_ptr(logits), rows, V, V, temperature, seed, step, _ptr(tokens), _ptr(logprob),
+                             ctypes.c_void_p(_stream())))
+
+
+def rlt_generate(model, state, first: torch.Tensor, n: int, temperature: float, seed: int, step0: int,
+                 tokens: torch.Tensor, logprob: torch.Tensor, logits: Optional[torch.Tensor] = None) -> None:
+    assert first.dtype == torch.int32 and first.dim() == 1 and tokens.dtype == torch.int32
+    _check(load().rlt_generate(model, state, _ptr(first), n, temperature, seed, step0, _ptr(tokens), _ptr(logprob),
+                               _ptr(logits), ctypes.c_void_p(_stream())))
+
+
+def rlt_importance_ratio(logprob_current: torch.Tensor, logprob_behaviour: torch.Tensor, ratio: torch.Tensor) -> None:
+    n = logprob_current.numel()
+    assert logprob_behaviour.numel() == n and ratio.numel() == n
+    _check(load().rlt_importance_ratio(_ptr(logprob_current), _ptr(logprob_behaviour), n, _ptr(ratio),
+                                       ctypes.c_void_p(_stream())))
 
 
 # ----------------------------------------------------------------- convenience
