@@ -172,6 +172,51 @@ int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, h
 int rlt_replay(rlt_model* m, rlt_state* state, const int32_t* tokens, int T, float* logprob,
                float* s_out, hipStream_t stream);
 
+/* Exact prefix snapshot ([R] §6.5 and [S] appendix E: an exact prefix checkpoint holds the
+ * encoder cache, the encoder-derived cross-attention memory, the complete decoder state,
+ * the token and position metadata, the SWA window convention and the model version).
+ * The payload (opaque bytes) holds s, the RLT-2 register, every decoder ring C^D, the memory
+ * prefix M_<=n_encoded of every group, the encoder cache prefix when the state keeps it, and
+ * the encoder outputs of encoded positions not yet consumed; the info block holds the
+ * positions, the dependent block-step count, the ring layout (window, ring slots) and two
+ * digests: of the configuration, and of the packed parameter values (the model version: a
+ * snapshot is valid for any model with the same configuration and parameter values, in this
+ * process or another). Restoring then continuing with the same calls gives bit-identical
+ * results to never having stopped (serving-split invariance, [R] Proposition 3.1). A prefix
+ * edit (deleting, rewriting or truncating earlier tokens) is served by restoring an earlier
+ * snapshot that precedes the edit and encoding the new tokens from there ([R] §6.5: a state
+ * that contains removed content must not be kept). */
+typedef struct {
+  uint64_t config_digest;   /* configuration fields */
+  uint64_t weights_digest;  /* packed parameter values */
+  int32_t batch;
+  int32_t n_encoded;        /* positions encoded (memory and encoder-cache prefix length) */
+  int32_t n_decoded;        /* positions consumed by the decoder */
+  int32_t window;           /* W */
+  int32_t ring_slots;       /* slots per ring (W + positions per pass - 1) */
+  int32_t has_encoder_cache;
+  int64_t block_steps;      /* dependent decoder block passes so far */
+  int64_t bytes;            /* payload bytes */
+} rlt_snapshot_info;
+
+/* Payload bytes rlt_snapshot needs for the state as it stands. Errors: STALE_STATE, INVALID_ARG. */
+int rlt_snapshot_size(rlt_model* m, rlt_state* s, int64_t* bytes);
+
+/* Copy the state's prefix into dst (device memory, or host memory: pinned host memory keeps the
+ * call asynchronous) and fill *info on the host. dst must hold rlt_snapshot_size bytes
+ * (`capacity`); it is written when the stream reaches the copies. Errors: CAPACITY (dst too
+ * small), STALE_STATE, INVALID_ARG. */
+int rlt_snapshot(rlt_model* m, rlt_state* s, void* dst, int64_t capacity, rlt_snapshot_info* info,
+                 hipStream_t stream);
+
+/* Make the state equal to the snapshot: its positions, rings, memory, encoder cache and
+ * pending encoder outputs are replaced (positions beyond the snapshot are dropped). The state
+ * must have the snapshot's batch and ring layout, the same encoder-cache choice and max_len >=
+ * n_encoded. Errors: INVALID_ARG (other configuration, batch, ring layout or cache choice),
+ * STALE_STATE (other parameter values: caches computed with other weights are not
+ * current-policy values, [R] §6.4), CAPACITY. Clears the state's staleness. */
+int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const void* src, hipStream_t stream);
+
 /* Behaviour sampling with recorded log-probabilities ([R] §6.2, Figure 4): for each of
  * `rows` rows of logits (device fp32, row stride ld >= vocab elements) draw
  *   tokens[b] = argmax_j (logits[b, j] / temperature + G(b, j)),  G = -log(-log U),

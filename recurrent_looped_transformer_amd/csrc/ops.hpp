@@ -116,6 +116,8 @@ void copy_rows_at(const float* src, RowMap sm, float* dst, RowMap dm, const int*
 // scan position words for graph replay: p[0] = position index, p[1] = readout buffer column
 void set_scan_pos(int* p, int pos, int col, hipStream_t st);
 void advance_scan_pos(int* p, int np, hipStream_t st);
+// *out_dev = order-independent 64-bit digest of n_words 64-bit words at p (device)
+void digest64(const void* p, int64_t n_words, uint64_t* out_dev, hipStream_t st);
 // p[0 .. n) = 0 (32-bit words), a kernel rather than a memset so the call is capture-safe
 void fill_zero_u32(void* p, int64_t n, hipStream_t st);
 // s[b, :] = s0 (fp32) for b < B; used for H_0 and the RLT-2 register

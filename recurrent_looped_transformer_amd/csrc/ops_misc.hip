@@ -1,6 +1,8 @@
 // Row-wise and elementwise kernels: RMSNorm (wavefront per row), embedding
 // gather, rotary table, row copies, state broadcast, readout log-probability,
 // and weight packing into the library layout.
+#include <algorithm>
+
 #include "common.hpp"
 #include "ops.hpp"
 
@@ -230,6 +232,38 @@ void pack_matrix(Dt dt, const float* src, int64_t src_ld, int64_t col0, void* ds
   else
     hipLaunchKernelGGL(pack_k<f16_t>, grid, dim3(256), 0, st, src, src_ld, col0, (f16_t*)dst, dst_ld, dst_col0,
                        rows, cols, (int)kind, dh, row_stride, row_off, tiles ? 1 : 0);
+}
+
+
+// ------------------------------------------------------------------ digest
+// Order-independent 64-bit digest of a buffer of 64-bit words: the sum (mod 2^64) of
+// splitmix64-finalised (word ^ index * golden-ratio constant) values (the finaliser of
+// Steele, Lea and Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__global__ __launch_bounds__(256) void digest_k(const uint64_t* __restrict__ w, int64_t n, unsigned long long* out) {
+  uint64_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    acc += mix64(w[i] ^ ((uint64_t)i * 0x9E3779B97F4A7C15ull));
+  __shared__ uint64_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicAdd(out, (unsigned long long)red[0]);
+}
+
+void digest64(const void* p, int64_t n_words, uint64_t* out_dev, hipStream_t st) {
+  fill_zero_u32(out_dev, 2, st);
+  if (n_words <= 0) return;
+  const int64_t blocks = std::min<int64_t>((n_words + 255) / 256, 4096);
+  hipLaunchKernelGGL(digest_k, dim3((unsigned)blocks), dim3(256), 0, st, (const uint64_t*)p, n_words,
+                     (unsigned long long*)out_dev);
 }
 
 }  // namespace rlt

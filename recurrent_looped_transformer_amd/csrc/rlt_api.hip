@@ -92,6 +92,7 @@ struct rlt_model {
   float* nO = nullptr;
   void* wout = nullptr;
   uint64_t version = 1;
+  uint64_t wdigest = 0;   // digest of the packed parameter values (identifies a snapshot's weights)
   int scan_mode = 0;
   int n_states = 0;
 };
@@ -353,6 +354,40 @@ void pack_all(rlt_model* m, const std::map<std::string, const float*>& W, hipStr
   vec(m->nO, "out.nO");
   plain(m->wout, "out.w", V, d);
   check_launch();
+}
+
+// Digest of the packed parameters, computed on the device when they are set.
+uint64_t weights_digest(rlt_model* m, hipStream_t st) {
+  uint64_t* d = nullptr;
+  if (hipMalloc((void**)&d, 16) != hipSuccess) fail(RLT_ERR_OOM, "digest scratch allocation failed");
+  uint64_t h = 0;
+  digest64(m->arena, (int64_t)(m->arena_bytes / 8), d, st);
+  const hipError_t e1 = hipMemcpyAsync(&h, d, 8, hipMemcpyDeviceToHost, st);
+  const hipError_t e2 = hipStreamSynchronize(st);
+  (void)hipFree(d);
+  if (e1 != hipSuccess || e2 != hipSuccess) fail(RLT_ERR_HIP, "weights digest failed");
+  return h;
+}
+
+// FNV-1a over the configuration fields that shape the state
+uint64_t config_digest(const rlt_config& c) {
+  uint64_t h = 0xCBF29CE484222325ull;
+  auto add = [&](uint64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (v >> (8 * i)) & 0xFF;
+      h *= 0x100000001B3ull;
+    }
+  };
+  uint32_t a, e, r;
+  std::memcpy(&a, &c.alpha, 4);
+  std::memcpy(&e, &c.rms_eps, 4);
+  std::memcpy(&r, &c.rope_base, 4);
+  for (uint64_t v : {(uint64_t)c.vocab, (uint64_t)c.d, (uint64_t)c.n_heads, (uint64_t)c.d_head, (uint64_t)c.L_E,
+                     (uint64_t)c.L_D, (uint64_t)c.ffn, (uint64_t)c.window, (uint64_t)c.groups, (uint64_t)c.variant,
+                     (uint64_t)c.chunk, (uint64_t)c.share_enc_dec, (uint64_t)c.dtype, (uint64_t)a, (uint64_t)e,
+                     (uint64_t)r})
+    add(v);
+  return h;
 }
 
 void check_state(rlt_model* m, rlt_state* s) {
@@ -839,6 +874,66 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
   check_launch();
 }
 
+// ------------------------------------------------------------------ snapshots
+// Payload of a prefix snapshot, in this order (B sequences, n_enc encoded and n_dec consumed
+// positions; every part contiguous):
+//   s, rho            fp32 [B][d] each
+//   rings C^D k, v    [L_D][B][H][R][dh] each (whole rings: slots are (position - 1) mod R)
+//   memory M k, v     [G][B][H][n_enc][dh] each (the encoded prefix of every group)
+//   encoder C^E k, v  [L_E][B][H][n_enc][dh] each, when the state keeps the encoder cache
+//   e, gpre           fp32 [B][n_enc - n_dec][d] (encoded, not yet consumed positions)
+// Element width esz for the caches, memory and rings.
+struct SnapPart {
+  char* state;        // first byte in the state (row 0)
+  int64_t rows;       // rows of the part
+  int64_t width;      // bytes copied per row
+  int64_t pitch;      // state row pitch in bytes
+};
+std::vector<SnapPart> snapshot_parts(rlt_model* m, rlt_state* s, int n_enc, int n_dec, bool with_enc) {
+  const rlt_config& c = m->cfg;
+  const int64_t B = s->B, d = c.d, H = c.n_heads, dh = c.d_head, e = m->esz, Tm = s->Tm;
+  std::vector<SnapPart> v;
+  v.push_back({(char*)s->s, 1, B * d * 4, B * d * 4});
+  v.push_back({(char*)s->rho, 1, B * d * 4, B * d * 4});
+  if (c.L_D > 0) {
+    const int64_t rb = (int64_t)c.L_D * B * H * s->R * dh * e;
+    v.push_back({(char*)s->ring_k, 1, rb, rb});
+    v.push_back({(char*)s->ring_v, 1, rb, rb});
+    const int64_t mr = (int64_t)c.groups * B * H;
+    v.push_back({(char*)s->mem_k, mr, (int64_t)n_enc * dh * e, Tm * dh * e});
+    v.push_back({(char*)s->mem_v, mr, (int64_t)n_enc * dh * e, Tm * dh * e});
+  }
+  if (with_enc) {
+    const int64_t er = (int64_t)c.L_E * B * H;
+    v.push_back({(char*)s->enc_k, er, (int64_t)n_enc * dh * e, Tm * dh * e});
+    v.push_back({(char*)s->enc_v, er, (int64_t)n_enc * dh * e, Tm * dh * e});
+  }
+  const int64_t pend = (int64_t)(n_enc - n_dec) * d * 4;
+  v.push_back({(char*)(s->e + (int64_t)n_dec * d), B, pend, Tm * d * 4});
+  if (s->gpre) v.push_back({(char*)(s->gpre + (int64_t)n_dec * d), B, pend, Tm * d * 4});
+  return v;
+}
+
+int64_t snapshot_payload(const std::vector<SnapPart>& parts) {
+  int64_t n = 0;
+  for (const SnapPart& p : parts) n += p.rows * p.width;
+  return n;
+}
+
+// to_state = false: state -> buf; true: buf -> state. buf may be device or host memory.
+void snapshot_copy(const std::vector<SnapPart>& parts, char* buf, bool to_state, hipStream_t st) {
+  int64_t off = 0;
+  for (const SnapPart& p : parts) {
+    if (p.rows > 0 && p.width > 0) {
+      if (to_state)
+        HIPCHK(hipMemcpy2DAsync(p.state, p.pitch, buf + off, p.width, p.width, p.rows, hipMemcpyDefault, st));
+      else
+        HIPCHK(hipMemcpy2DAsync(buf + off, p.width, p.state, p.pitch, p.width, p.rows, hipMemcpyDefault, st));
+    }
+    off += p.rows * p.width;
+  }
+}
+
 }  // namespace
 
 // ======================================================================= C ABI
@@ -882,6 +977,7 @@ int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, 
       fill_zero_u32(m->arena, (int64_t)(total / 4), stream);   // padding rows of tile-major weights
       pack_all(m, W, stream);
       HIPCHK(hipStreamSynchronize(stream));
+      m->wdigest = weights_digest(m, stream);
     } catch (...) {
       if (m->arena) (void)hipFree(m->arena);
       delete m;
@@ -897,6 +993,7 @@ int rlt_update_weights(rlt_model* m, const rlt_tensor* weights, int n_weights, h
     auto W = index_weights(m->cfg, weights, n_weights);
     pack_all(m, W, stream);
     HIPCHK(hipStreamSynchronize(stream));
+    m->wdigest = weights_digest(m, stream);
     m->version += 1;
   });
 }
@@ -1154,6 +1251,65 @@ int rlt_replay(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, float* 
       o.lp = logprob; o.lp_ld = T - 1; o.lp_valid = T - 1;
     }
     do_scan(m, s, T, o, stream);
+  });
+}
+
+int rlt_snapshot_size(rlt_model* m, rlt_state* s, int64_t* bytes) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!bytes) fail(RLT_ERR_INVALID_ARG, "null output");
+    *bytes = snapshot_payload(snapshot_parts(m, s, s->n_enc, s->n_dec, s->keep_enc != 0));
+  });
+}
+
+int rlt_snapshot(rlt_model* m, rlt_state* s, void* dst, int64_t capacity, rlt_snapshot_info* info,
+                 hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!dst || !info) fail(RLT_ERR_INVALID_ARG, "dst and info required");
+    const auto parts = snapshot_parts(m, s, s->n_enc, s->n_dec, s->keep_enc != 0);
+    const int64_t need = snapshot_payload(parts);
+    if (capacity < need) fail(RLT_ERR_CAPACITY, "snapshot buffer smaller than rlt_snapshot_size");
+    snapshot_copy(parts, (char*)dst, false, stream);
+    rlt_snapshot_info v{};
+    v.config_digest = config_digest(m->cfg);
+    v.weights_digest = m->wdigest;
+    v.batch = s->B;
+    v.n_encoded = s->n_enc;
+    v.n_decoded = s->n_dec;
+    v.window = m->cfg.window;
+    v.ring_slots = s->R;
+    v.has_encoder_cache = s->keep_enc;
+    v.block_steps = s->block_steps;
+    v.bytes = need;
+    *info = v;
+  });
+}
+
+int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const void* src, hipStream_t stream) {
+  return guarded([&] {
+    if (!m || !s || s->m != m) fail(RLT_ERR_INVALID_ARG, "null or foreign state");
+    if (!info || !src) fail(RLT_ERR_INVALID_ARG, "info and src required");
+    if (s->abort_host && *(volatile int*)s->abort_host)
+      fail(RLT_ERR_HIP, "a persistent scan on this state timed out in a grid barrier; its results are invalid");
+    if (info->config_digest != config_digest(m->cfg)) fail(RLT_ERR_INVALID_ARG, "snapshot of another configuration");
+    if (info->weights_digest != m->wdigest)
+      fail(RLT_ERR_STALE_STATE, "snapshot taken under other parameter values; recompute it from the tokens");
+    if (info->batch != s->B) fail(RLT_ERR_INVALID_ARG, "snapshot batch differs from the state's");
+    if (info->ring_slots != s->R || info->window != m->cfg.window)
+      fail(RLT_ERR_INVALID_ARG, "snapshot ring layout differs from the state's");
+    if (info->has_encoder_cache != s->keep_enc)
+      fail(RLT_ERR_INVALID_ARG, "snapshot and state differ in keeping the encoder cache");
+    if (info->n_encoded > s->Tm) fail(RLT_ERR_CAPACITY, "snapshot positions exceed the state's max_len");
+    if (info->n_decoded < 0 || info->n_decoded > info->n_encoded) fail(RLT_ERR_INVALID_ARG, "bad snapshot positions");
+    const auto parts = snapshot_parts(m, s, info->n_encoded, info->n_decoded, s->keep_enc != 0);
+    if (snapshot_payload(parts) != info->bytes) fail(RLT_ERR_INVALID_ARG, "snapshot size does not match its layout");
+    snapshot_copy(parts, (char*)src, true, stream);
+    check_launch();
+    s->n_enc = info->n_encoded;
+    s->n_dec = info->n_decoded;
+    s->block_steps = info->block_steps;
+    s->version = m->version;
   });
 }
 

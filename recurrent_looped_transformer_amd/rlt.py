@@ -26,7 +26,8 @@ STATUS = {0: "RLT_OK", -1: "RLT_ERR_INVALID_ARG", -2: "RLT_ERR_UNSUPPORTED", -3:
 EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create", "rlt_state_reset",
            "rlt_state_destroy", "rlt_state_bytes", "rlt_state_positions", "rlt_encode", "rlt_decode_scan",
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
-           "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio"]
+           "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
+           "rlt_snapshot", "rlt_restore"]
 
 
 class RltError(RuntimeError):
@@ -42,6 +43,13 @@ class rlt_config(ctypes.Structure):
                 ("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("share_enc_dec", ctypes.c_int),
                 ("dtype", ctypes.c_int), ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("rope_base", ctypes.c_float)]
+
+
+class rlt_snapshot_info(ctypes.Structure):
+    _fields_ = [("config_digest", ctypes.c_uint64), ("weights_digest", ctypes.c_uint64), ("batch", ctypes.c_int32),
+                ("n_encoded", ctypes.c_int32), ("n_decoded", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("ring_slots", ctypes.c_int32), ("has_encoder_cache", ctypes.c_int32),
+                ("block_steps", ctypes.c_int64), ("bytes", ctypes.c_int64)]
 
 
 class rlt_tensor(ctypes.Structure):
@@ -78,6 +86,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp],
         "rlt_generate": [vp, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp],
         "rlt_importance_ratio": [vp, vp, ctypes.c_int64, vp, vp],
+        "rlt_snapshot_size": [vp, vp, i64p],
+        "rlt_snapshot": [vp, vp, vp, ctypes.c_int64, ctypes.POINTER(rlt_snapshot_info), vp],
+        "rlt_restore": [vp, vp, ctypes.POINTER(rlt_snapshot_info), vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -223,6 +234,27 @@ def rlt_importance_ratio(logprob_current: torch.Tensor, logprob_behaviour: torch
     assert logprob_behaviour.numel() == n and ratio.numel() == n
     _check(load().rlt_importance_ratio(_ptr(logprob_current), _ptr(logprob_behaviour), n, _ptr(ratio),
                                        ctypes.c_void_p(_stream())))
+
+
+def rlt_snapshot_size(model, state) -> int:
+    n = ctypes.c_int64(0)
+    _check(load().rlt_snapshot_size(model, state, ctypes.byref(n)))
+    return n.value
+
+
+def rlt_snapshot(model, state, dst: torch.Tensor) -> rlt_snapshot_info:
+    """Snapshot into dst (a contiguous uint8 tensor on the GPU, or pinned on the host)."""
+    assert dst.dtype == torch.uint8 and dst.is_contiguous()
+    info = rlt_snapshot_info()
+    _check(load().rlt_snapshot(model, state, ctypes.c_void_p(dst.data_ptr()), dst.numel(), ctypes.byref(info),
+                               ctypes.c_void_p(_stream())))
+    return info
+
+
+def rlt_restore(model, state, info: rlt_snapshot_info, src: torch.Tensor) -> None:
+    assert src.dtype == torch.uint8 and src.is_contiguous() and src.numel() >= info.bytes
+    _check(load().rlt_restore(model, state, ctypes.byref(info), ctypes.c_void_p(src.data_ptr()),
+                              ctypes.c_void_p(_stream())))
 
 
 # ----------------------------------------------------------------- convenience
