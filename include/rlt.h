@@ -265,6 +265,17 @@ int rlt_importance_ratio(const float* logprob_current, const float* logprob_beha
  * mode 1 there. */
 int rlt_set_scan_mode(rlt_model* m, int mode);
 
+/* Batch-invariant arithmetic (on != 0): every kernel computes a row's result with the same
+ * operations in the same order whatever the batch, the number of positions per call and the
+ * serving split: the encoder runs its token-parallel positions through the decode GEMM and
+ * the per-query attention kernel, the decoder normalises with the norm kernel instead of
+ * the folded norms, and the scan uses the per-position launch path. Then a replay reproduces
+ * the prefill + step (or rlt_generate) chain bit for bit, and at temperature 1 the importance
+ * ratio of the replay against the recorded behaviour log-probabilities is exactly 1 ([R]
+ * §6.3 and the pages' discussion of batch-invariant kernels: equal forward probabilities
+ * need equal kernels, not only an equal schedule). Slower prefill; off by default. */
+int rlt_set_batch_invariant(rlt_model* m, int on);
+
 /* Number of dependent decoder block passes issued since the state was reset
  * (T*L_D for RLT-1, ceil(T/K_c)*L_D for RLT-2 chunks, L_D per parallel RLT-0 pass;
  * [S] §2.7, Table 1). */

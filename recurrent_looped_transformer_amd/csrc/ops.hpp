@@ -89,6 +89,9 @@ struct EpArgs {
   RowMap dup_map;
   float* dup_last = nullptr;
   int64_t dup_last_ld = 0;
+  // Row-invariant arithmetic: every row count takes the decode kernel, whose per-row sums
+  // run in the same order whatever M is (a row's result does not depend on the batch).
+  int row_invariant = 0;
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.

@@ -508,7 +508,7 @@ template <typename T, Ep E>
 static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
                      hipStream_t st) {
   const T *x = (const T*)X, *w = (const T*)W;
-  if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp) {
+  if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp || a.row_invariant) {
     // Row blocks per workgroup: one (more workgroups, less activation traffic per CU) while the
     // grid stays near 400 workgroups, else two or four (measured on MI355X decode shapes).
     const dim3 blk(kSkW * WAVE);

@@ -175,31 +175,6 @@ void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st) {
   hipLaunchKernelGGL(broadcast_row_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, s0, s, B, d);
 }
 
-// log p(tok | logits row) = logits[tok] - (max + log(sum exp(logits - max)))
-__global__ __launch_bounds__(256) void logprob_k(const float* __restrict__ logits, RowMap lm,
-                                                 const int32_t* __restrict__ tok, RowMap tm, float* __restrict__ out,
-                                                 RowMap om, int V) {
-  __shared__ float red[16];
-  const int r = blockIdx.x;
-  const float* L = logits + lm.off(r);
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < V; j += 256) mx = fmaxf(mx, L[j]);
-  mx = block_max(mx, red);
-  float s = 0.f;
-  for (int j = threadIdx.x; j < V; j += 256) s += __expf(L[j] - mx);
-  s = block_sum(s, red);
-  if (threadIdx.x == 0) {
-    const int t = tok[tm.off(r)];
-    out[om.off(r)] = t >= 0 ? L[t] - (mx + __logf(s)) : 0.f;
-  }
-}
-
-void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows, int V,
-             hipStream_t st) {
-  if (rows <= 0) return;
-  hipLaunchKernelGGL(logprob_k, dim3(rows), dim3(256), 0, st, logits, lm, tok, tm, out, om, V);
-}
-
 // dst row (row_off + row_stride * perm(j)) <- src row j, columns [col0, col0 + cols) -> [dst_col0, ...)
 // RopeRows: within each head of dh rows, rotate-half pair (i, i + dh/2) lands on rows (2i, 2i + 1).
 template <typename T>

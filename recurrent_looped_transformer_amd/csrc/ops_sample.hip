@@ -12,7 +12,8 @@
 // tau = 0 is greedy decoding (lowest index on ties, log mu = 0).
 //
 // One workgroup per row; scores and the log-sum-exp in float64 (a row is tens of
-// thousands of entries: the kernel is a few microseconds whatever its precision).
+// thousands of entries: the kernel is a few microseconds whatever its precision). The
+// replay's next-token log-probability (logprob_k) uses the same log-sum-exp routine.
 #include <climits>
 
 #include "common.hpp"
@@ -52,28 +53,54 @@ __device__ __forceinline__ void best_merge(double& y, int& j, double y2, int j2)
     j = j2;
   }
 }
-// running log-sum-exp (m = max so far, s = sum of exp(z - m))
-__device__ __forceinline__ void lse_merge(double& m, double& s, double m2, double s2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) {
-    m = m2;
-    s = s2;
-  } else if (m2 > m) {
-    s = s * exp(m - m2) + s2;
-    m = m2;
-  } else {
-    s += s2 * exp(m2 - m);
+
+// Row log-sum-exp of z_j = x_j / div in float64, shared by the sampler and the replay's
+// log-probability so that both evaluate log softmax with the same operations in the same
+// order: thread t visits j = 4 jb .. 4 jb + 3 for jb = t, t + 256, ...; max, then the sum of
+// exp(z - max), each reduced over the block in a fixed tree.
+__device__ __forceinline__ double block_max_d(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+    __syncthreads();
   }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ double row_sum_exp(const float* x, int V, double div, double mx, double* red) {
+  double s = 0.0;
+  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = 4 * jb + w;
+      if (j < V) s += exp((double)x[j] / div - mx);
+    }
+  return block_sum_d(s, red);
 }
 
 __global__ __launch_bounds__(kSampleThreads) void sample_k(const float* __restrict__ logits, int64_t ld, int V,
                                                            float tau, uint64_t seed, uint64_t step, int32_t* tok,
                                                            int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next) {
+  __shared__ double red[kSampleThreads];
+  __shared__ int redj[kSampleThreads];
   const int b = blockIdx.x;
   const float* x = logits + (int64_t)b * ld;
   const bool greedy = !(tau > 0.f);
-  const double dt = (double)tau;
-  double best = -INFINITY, m = -INFINITY, s = 0.0;
+  const double div = greedy ? 1.0 : (double)tau;
+  double best = -INFINITY, mx = -INFINITY;
   int bj = INT_MAX;
   for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads) {
     uint64_t c[4] = {(uint64_t)jb, (uint64_t)b, step, 0ull};
@@ -82,42 +109,71 @@ __global__ __launch_bounds__(kSampleThreads) void sample_k(const float* __restri
     for (int w = 0; w < 4; ++w) {
       const int j = 4 * jb + w;
       if (j < V) {
+        const double z = (double)x[j] / div;
+        mx = fmax(mx, z);
         if (greedy) {
-          best_merge(best, bj, (double)x[j], j);
+          best_merge(best, bj, z, j);
         } else {
-          const double z = (double)x[j] / dt;
           const double u = ((double)(c[w] >> 11) + 0.5) * 0x1p-53;
           best_merge(best, bj, z - log(-log(u)), j);
-          lse_merge(m, s, z, 1.0);
         }
       }
     }
   }
-  __shared__ double sy[kSampleThreads], sm[kSampleThreads], ss[kSampleThreads];
-  __shared__ int sj[kSampleThreads];
-  sy[threadIdx.x] = best;
-  sj[threadIdx.x] = bj;
-  sm[threadIdx.x] = m;
-  ss[threadIdx.x] = s;
+  // the draw: block argmax of the scores
+  red[threadIdx.x] = best;
+  redj[threadIdx.x] = bj;
   __syncthreads();
   for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
     if (threadIdx.x < h) {
-      double y = sy[threadIdx.x], mm = sm[threadIdx.x], s1 = ss[threadIdx.x];
-      int j = sj[threadIdx.x];
-      best_merge(y, j, sy[threadIdx.x + h], sj[threadIdx.x + h]);
-      lse_merge(mm, s1, sm[threadIdx.x + h], ss[threadIdx.x + h]);
-      sy[threadIdx.x] = y;
-      sj[threadIdx.x] = j;
-      sm[threadIdx.x] = mm;
-      ss[threadIdx.x] = s1;
+      double y = red[threadIdx.x];
+      int j = redj[threadIdx.x];
+      best_merge(y, j, red[threadIdx.x + h], redj[threadIdx.x + h]);
+      red[threadIdx.x] = y;
+      redj[threadIdx.x] = j;
     }
     __syncthreads();
   }
+  const int j = redj[0];
+  __syncthreads();
+  if (greedy) {
+    if (threadIdx.x == 0) {
+      tok[(int64_t)b * tok_ld] = j;
+      if (next) next[b] = j;
+      if (lp) lp[(int64_t)b * lp_ld] = 0.f;
+    }
+    return;
+  }
+  const double M = block_max_d(mx, red);
+  const double S = row_sum_exp(x, V, div, M, red);
   if (threadIdx.x == 0) {
-    const int j = sj[0];
     tok[(int64_t)b * tok_ld] = j;
     if (next) next[b] = j;
-    if (lp) lp[(int64_t)b * lp_ld] = greedy ? 0.f : (float)((double)x[j] / dt - (sm[0] + log(ss[0])));
+    if (lp) lp[(int64_t)b * lp_ld] = (float)((double)x[j] / div - (M + log(S)));
+  }
+}
+
+// log p(tok | logits row) = z_tok - log sum exp(z), z = logits (the sampler's arithmetic at
+// temperature 1, so a replay's log-probability of a token drawn at temperature 1 from the
+// same logits equals the recorded behaviour log-probability bit for bit)
+__global__ __launch_bounds__(kSampleThreads) void logprob_k(const float* __restrict__ logits, RowMap lm,
+                                                            const int32_t* __restrict__ tok, RowMap tm,
+                                                            float* __restrict__ out, RowMap om, int V) {
+  __shared__ double red[kSampleThreads];
+  const int r = blockIdx.x;
+  const float* x = logits + lm.off(r);
+  double mx = -INFINITY;
+  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = 4 * jb + w;
+      if (j < V) mx = fmax(mx, (double)x[j] / 1.0);
+    }
+  const double M = block_max_d(mx, red);
+  const double S = row_sum_exp(x, V, 1.0, M, red);
+  if (threadIdx.x == 0) {
+    const int t = tok[tm.off(r)];
+    out[om.off(r)] = t >= 0 ? (float)((double)x[t] / 1.0 - (M + log(S))) : 0.f;
   }
 }
 
@@ -133,6 +189,12 @@ void sample_rows(const float* logits, int64_t ld, int rows, int V, float tempera
   if (rows <= 0) return;
   hipLaunchKernelGGL(sample_k, dim3(rows), dim3(kSampleThreads), 0, st, logits, ld, V, temperature, seed, step, tok,
                      tok_ld, lp, lp_ld, next);
+}
+
+void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows, int V,
+             hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(logprob_k, dim3(rows), dim3(kSampleThreads), 0, st, logits, lm, tok, tm, out, om, V);
 }
 
 void importance_ratio(const float* lp_cur, const float* lp_beh, int64_t n, float* ratio, hipStream_t st) {

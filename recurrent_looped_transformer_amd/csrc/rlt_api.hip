@@ -94,6 +94,7 @@ struct rlt_model {
   uint64_t version = 1;
   uint64_t wdigest = 0;   // digest of the packed parameter values (identifies a snapshot's weights)
   int scan_mode = 0;
+  int batch_invariant = 0;   // every kernel's per-row arithmetic independent of batch and pass shape
   int n_states = 0;
 };
 
@@ -398,6 +399,14 @@ void check_state(rlt_model* m, rlt_state* s) {
     fail(RLT_ERR_HIP, "a persistent scan on this state timed out in a grid barrier; its results are invalid");
 }
 
+// GEMM of this model: the row-invariant dispatch when the model asks for batch-invariant
+// arithmetic.
+void mgemm(const rlt_model* m, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
+           int K, hipStream_t st) {
+  a.row_invariant = m->batch_invariant;
+  gemm(dt, ep, a, X, ldx, W, M, N, K, st);
+}
+
 // ------------------------------------------------------------------ encode
 void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t st) {
   const rlt_config& c = m->cfg;
@@ -434,17 +443,17 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T;
       }
       a.kv.ring = 0;
-      gemm(dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
+      mgemm(m, dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
       at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
-      if (!(T >= 16 && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+      if (!(T >= 16 && !m->batch_invariant && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
       EpArgs r; r.resid = h; r.rmap = hm; r.x_split = A > 1;
-      gemm(dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
+      mgemm(m, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
       rmsnorm(dt, h, hm, L.n2, s->exa, ad, rows, d, c.rms_eps, st, sd);
       EpArgs sw; sw.out = s->ehid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-      gemm(dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
-      gemm(dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
+      mgemm(m, dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
+      mgemm(m, dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
     }
     if (c.L_D > 0) {
       // memory: k^g = RoPE(W^g_K RMSNorm_E(e)), v^g = W^g_V RMSNorm_E(e)  (eq 2.1-2.2)
@@ -455,7 +464,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
         a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
         a.x_split = A > 1;
-        gemm(dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
+        mgemm(m, dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
       }
     }
     if (c.variant != RLT_V0) {
@@ -463,7 +472,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       rmsnorm(dt, h, hm, nullptr, s->exa, ad, rows, d, 0.f, st, sd);
       EpArgs a; a.resid = s->gpre + ((int64_t)b0 * Tm + t0) * d; a.rmap = hm; a.bias = m->bg;
       a.x_split = A > 1;
-      gemm(dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
+      mgemm(m, dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
     }
   }
   check_launch();
@@ -523,7 +532,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
   // the next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the
   // inverse RMS. The merge folds the first block's norm the same way (8-feature partials) when
   // the pass has one position; otherwise the first norm of the pass comes from the norm kernel.
-  const bool fold = dt != Dt::F32 && rows <= kSkinnyMaxRows && d / 16 <= 256;
+  const bool fold = !m->batch_invariant && dt != Dt::F32 && rows <= kSkinnyMaxRows && d / 16 <= 256;
   const bool chain = fold && c.variant == RLT_V1 && c.L_D > 0;
   const bool merge_fold = fold && c.variant != RLT_V0 && c.L_D > 0 && np == 1 && d / 8 <= 256;
   if (c.variant == RLT_V0) {
@@ -544,7 +553,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     if (merge_fold) {
       a.fold_zb = sb.xa; a.fold_ld = ad; a.out_split = sd; a.fold_ssp = sb.dssp; a.fold_gain = m->dec[0].n1;
     }
-    gemm(dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
+    mgemm(m, dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
   auto norm_in = [&](EpArgs& a, const float* gain) {
@@ -571,7 +580,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     a.x_split = A > 1; a.pos_dev = pos_dev;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
-    gemm(dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
+    mgemm(m, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
@@ -580,13 +589,13 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     attn_decode(dt, at, st);
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
-    gemm(dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
+    mgemm(m, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
     // cross-attention to the prefix memory M_<=t of this layer's group
     EpArgs qx;
     norm_in(qx, L.n2);
     qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0; qx.x_split = A > 1;
     qx.pos_dev = pos_dev;
-    gemm(dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
+    mgemm(m, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
     at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
@@ -594,12 +603,12 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     attn_decode(dt, at, st);
     EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
-    gemm(dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
+    mgemm(m, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
     // SwiGLU FFN
     EpArgs sw;
     norm_in(sw, L.n3);
     sw.out = sb.hid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-    gemm(dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
+    mgemm(m, dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
     EpArgs r3; r3.resid = sb.z; r3.rmap = zm; r3.x_split = A > 1;
     fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
     if (l + 1 == c.L_D) {
@@ -611,7 +620,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
         r3.fold_zb = sb.xs; r3.fold_ld = ad; r3.out_split = sd; r3.fold_ssp = sb.sssp; r3.fold_gain = m->ns;
       }
     }
-    gemm(dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
+    mgemm(m, dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
   }
   if (c.L_D == 0) {
     // s_t = the last position's output of every sequence
@@ -654,7 +663,7 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
   if (!o.logits && !o.lp) return;
   rmsnorm(dt, src, sm, m->nO, xr, A * d, rows, d, c.rms_eps, st, A > 1 ? d : 0);
   EpArgs a; a.out = lbuf; a.ldo = V; a.x_split = A > 1;
-  gemm(dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
+  mgemm(m, dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
   if (o.logits) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
     copy_rows(lbuf, contiguous(V), o.logits + ((int64_t)b0 * o.ld_b + c0) * V, dm, rows, V, st);
@@ -696,7 +705,7 @@ int scan_groups(rlt_model* m, rlt_state* s) {
 // shape it measured faster than the persistent kernel, whose phases are bound by the
 // latency of reading activations just written by other CUs.
 bool use_persistent(rlt_model* m, rlt_state* s) {
-  return s->scan_ok && m->scan_mode >= 2 && m->scan_mode <= 6;
+  return s->scan_ok && m->scan_mode >= 2 && m->scan_mode <= 6 && !m->batch_invariant;
 }
 
 // Batch slices of the launch-path scan (each an independent chain on its own stream).
@@ -781,7 +790,8 @@ hipGraphExec_t pass_graph(rlt_model* m, rlt_state* s, bool want_rows, bool in_fo
 // Explicit only: measured at the algorithmic shape the replayed graph (44.2 ms per 64x257 scan)
 // is not faster than the stream-ordered launches (43.2 ms), whose dispatch already overlaps.
 bool use_graph(rlt_model* m, rlt_state* s) {
-  return m->cfg.variant == RLT_V1 && m->cfg.L_D > 0 && scan_slices(m, s) == 1 && m->scan_mode == 9;
+  return m->cfg.variant == RLT_V1 && m->cfg.L_D > 0 && scan_slices(m, s) == 1 && m->scan_mode == 9 &&
+         !m->batch_invariant;
 }
 
 void graph_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st) {
@@ -1179,6 +1189,13 @@ int rlt_state_positions(const rlt_state* s, int* n_encoded, int* n_decoded) {
     if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
     if (n_encoded) *n_encoded = s->n_enc;
     if (n_decoded) *n_decoded = s->n_dec;
+  });
+}
+
+int rlt_set_batch_invariant(rlt_model* m, int on) {
+  return guarded([&] {
+    if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
+    m->batch_invariant = on ? 1 : 0;
   });
 }
 

@@ -27,7 +27,7 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_state_destroy", "rlt_state_bytes", "rlt_state_positions", "rlt_encode", "rlt_decode_scan",
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
-           "rlt_snapshot", "rlt_restore"]
+           "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant"]
 
 
 class RltError(RuntimeError):
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_step": [vp, vp, vp, vp, vp],
         "rlt_replay": [vp, vp, vp, i32, vp, vp, vp],
         "rlt_set_scan_mode": [vp, i32],
+        "rlt_set_batch_invariant": [vp, i32],
         "rlt_state_block_steps": [vp, i64p],
         "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp],
         "rlt_generate": [vp, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp],
@@ -191,6 +192,10 @@ def rlt_state_block_steps(state) -> int:
 
 def rlt_set_scan_mode(model, mode: int) -> None:
     _check(load().rlt_set_scan_mode(model, mode))
+
+
+def rlt_set_batch_invariant(model, on: bool) -> None:
+    _check(load().rlt_set_batch_invariant(model, 1 if on else 0))
 
 
 def rlt_encode(model, state, tokens: torch.Tensor) -> None:
