@@ -272,8 +272,10 @@ int rlt_set_scan_mode(rlt_model* m, int mode);
  * the folded norms, and the scan uses the per-position launch path. Then a replay reproduces
  * the prefill + step (or rlt_generate) chain bit for bit, and at temperature 1 the importance
  * ratio of the replay against the recorded behaviour log-probabilities is exactly 1 ([R]
- * §6.3 and the pages' discussion of batch-invariant kernels: equal forward probabilities
- * need equal kernels, not only an equal schedule). Slower prefill; off by default. */
+ * §6.3; the core.today essay on the method, §4-1, on sampler / trainer probabilities that
+ * differ under one checkpoint until the kernels are batch-invariant: equal forward
+ * probabilities need equal kernels, not only an equal schedule). Slower prefill; off by
+ * default. */
 int rlt_set_batch_invariant(rlt_model* m, int on);
 
 /* Number of dependent decoder block passes issued since the state was reset
