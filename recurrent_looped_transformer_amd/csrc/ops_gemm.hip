@@ -150,21 +150,30 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
 }
 
 // ------------------------------------------------------------------ skinny (decode)
-// One workgroup of kSkW waves owns 16 output features and 16 * NMB rows (NMB <= 4). The
+// One workgroup of kSkW waves owns TPW tiles of 16 output features and 16 * NMB rows. The
 // waves split K into 64-wide chunks (chunk c to wave c % kSkW) and each wave issues the
-// weight and activation loads of U chunks before their MFMAs, so that the whole 16 x K
-// weight tile is in flight at once for K up to kSkW * U * 64. Partial tiles meet in LDS.
+// weight and activation loads of U chunks before their MFMAs, so that the workgroup's whole
+// weight slice is in flight at once for K up to kSkW * U * 64; every activation fragment a
+// wave loads feeds the TPW weight tiles (fewer re-reads of X when N is large). Partial tiles
+// meet in LDS. A row's sums run in the same order for every TPW, NMB and M.
 constexpr int kSkW = 8;
 
-template <typename T, Ep E, int NMB>
+template <int TPW, int NMB>
+constexpr int skinny_unroll() {
+  return TPW + NMB <= 2 ? 8 : (TPW + NMB <= 3 ? 4 : (TPW + NMB <= 5 ? 2 : 1));
+}
+
+template <typename T, Ep E, int NMB, int TPW>
 __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__ X, int64_t ldx,
                                                            const T* __restrict__ W, int M, int N, int K,
                                                            EpArgs a) {
-  constexpr int U = NMB == 1 ? 8 : (NMB == 2 ? 4 : 2);
+  constexpr int U = skinny_unroll<TPW, NMB>();
+  constexpr int NO = TPW * NMB;            // output tiles of the workgroup
+  constexpr int NOB = NO < 4 ? NO : 4;     // output tiles reduced per pass (LDS: 32 KB)
   constexpr int RPW = NMB * 16 / kSkW;     // rows per wave in the row-scale prologue
-  __shared__ f32x4 red[kSkW][NMB][WAVE];
+  __shared__ f32x4 red[kSkW][NOB][WAVE];
   __shared__ float rsl[NMB * 16];
-  const int n0 = blockIdx.x * 16;
+  const int tile0 = blockIdx.x * TPW;
   const int m0 = blockIdx.y * (NMB * 16);
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r = lane & 15, g = lane >> 4;
@@ -182,30 +191,37 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     }
   }
 
-  // the epilogue wave's operands (residual row, gain, rotary factors) are requested first
+  // the epilogue waves' operands (residual row, gain, rotary factors) are requested first;
+  // in reduction pass p, wave w < NOB finishes output tile o = p NOB + w, (t, j) = (o / NMB,
+  // o % NMB); the first pass's operands are prefetched
   EpPre pre{};
-  if (wave < NMB) {
-    const int em = m0 + wave * 16 + r, en = n0 + 4 * g;
+  if (wave < NOB) {
+    const int em = m0 + (wave % NMB) * 16 + r, en = (tile0 + wave / NMB) * 16 + 4 * g;
     if (em < M && en < N) pre = ep_prefetch<E, true>(a, em, en);
   }
-  const T* wp = W + (int64_t)blockIdx.x * 16 * K + lane * 8;   // tile-major weight tile
+  const T* wp = W + (int64_t)tile0 * 16 * K + lane * 8;   // tile-major weight tiles
   const T* xp[NMB];
 #pragma unroll
   for (int j = 0; j < NMB; ++j) xp[j] = X + (int64_t)min(m0 + j * 16 + r, M - 1) * ldx + g * 16;
-  f32x4 acc[NMB];
+  f32x4 acc[TPW][NMB];
 #pragma unroll
-  for (int j = 0; j < NMB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int j = 0; j < NMB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // two-term X: chunks nch .. 2 nch - 1 are the lo terms, against the same weight chunks
   const int nch = K / 64, ncx = a.x_split ? 2 * nch : nch;
   for (int c0 = wave; c0 < ncx; c0 += kSkW * U) {
-    uint4 wa[U][2], xb[U][NMB][2];
+    uint4 wa[U][TPW][2], xb[U][NMB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kSkW;
       if (c < ncx) {
         const int cw = c < nch ? c : c - nch;
-        wa[u][0] = *reinterpret_cast<const uint4*>(wp + cw * 1024);
-        wa[u][1] = *reinterpret_cast<const uint4*>(wp + cw * 1024 + 512);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          wa[u][t][0] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + cw * 1024);
+          wa[u][t][1] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + cw * 1024 + 512);
+        }
 #pragma unroll
         for (int j = 0; j < NMB; ++j) {
           xb[u][j][0] = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
@@ -217,45 +233,55 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     for (int u = 0; u < U; ++u) {
       if (c0 + u * kSkW < ncx) {
 #pragma unroll
-        for (int j = 0; j < NMB; ++j) {
-          acc[j] = mfma16x16x32<T>(wa[u][0], xb[u][j][0], acc[j]);
-          acc[j] = mfma16x16x32<T>(wa[u][1], xb[u][j][1], acc[j]);
-        }
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int j = 0; j < NMB; ++j) {
+            acc[t][j] = mfma16x16x32<T>(wa[u][t][0], xb[u][j][0], acc[t][j]);
+            acc[t][j] = mfma16x16x32<T>(wa[u][t][1], xb[u][j][1], acc[t][j]);
+          }
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < NMB; ++j) red[wave][j][lane] = acc[j];
   if (a.rs_ssp) {
     const float live = lane * 4 < a.rs_n ? 1.f : 0.f;
-    float t[RPW];
+    float tt[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) t[i] = wave_sum_dpp((ssr[i].x + ssr[i].y + ssr[i].z + ssr[i].w) * live);
+    for (int i = 0; i < RPW; ++i) tt[i] = wave_sum_dpp((ssr[i].x + ssr[i].y + ssr[i].z + ssr[i].w) * live);
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) rsl[wave + kSkW * i] = rsqrtf(t[i] / (float)a.rs_d + a.rs_eps);
+      for (int i = 0; i < RPW; ++i) rsl[wave + kSkW * i] = rsqrtf(tt[i] / (float)a.rs_d + a.rs_eps);
     }
   }
-  __syncthreads();
-  if (wave < NMB) {
-    const int j = wave;
-    f32x4 sum = red[0][j][lane];
 #pragma unroll
-    for (int w = 1; w < kSkW; ++w) sum += red[w][j][lane];
-    const int m = m0 + j * 16 + r;
-    const int n = n0 + 4 * g;
-    const float sc = a.rs_ssp ? rsl[j * 16 + r] : 1.f;
-    float ss = 0.f;
-    if (m < M && n < N) {
-      float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
-      ss = epilogue<T, E, true>(a, m, n, v, &pre);
+  for (int p = 0; p < NO / NOB; ++p) {
+    if (p > 0) __syncthreads();   // the previous pass has read red
+#pragma unroll
+    for (int w = 0; w < NOB; ++w) {
+      const int o = p * NOB + w;
+      red[wave][w][lane] = acc[o / NMB][o % NMB];
     }
-    if constexpr (E == Ep::Residual || E == Ep::Merge) {
-      if (a.fold_zb) {
-        // lanes r, r+16, r+32, r+48 hold the tile's features of row m (16, or 8 for Merge)
-        ss += __shfl_xor(ss, 16, WAVE);
-        ss += __shfl_xor(ss, 32, WAVE);
-        if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + blockIdx.x] = ss;
+    __syncthreads();
+    if (wave < NOB) {
+      const int o = p * NOB + wave;
+      const int t = o / NMB, j = o % NMB;
+      f32x4 sum = red[0][wave][lane];
+#pragma unroll
+      for (int w = 1; w < kSkW; ++w) sum += red[w][wave][lane];
+      const int m = m0 + j * 16 + r;
+      const int n = (tile0 + t) * 16 + 4 * g;
+      const float sc = a.rs_ssp ? rsl[j * 16 + r] : 1.f;
+      float ss = 0.f;
+      if (m < M && n < N) {
+        float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
+        ss = epilogue<T, E, true>(a, m, n, v, p == 0 ? &pre : nullptr);
+      }
+      if constexpr (E == Ep::Residual || E == Ep::Merge) {
+        if (a.fold_zb) {
+          // lanes r, r+16, r+32, r+48 hold the tile's features of row m (16, or 8 for Merge)
+          ss += __shfl_xor(ss, 16, WAVE);
+          ss += __shfl_xor(ss, 32, WAVE);
+          if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + tile0 + t] = ss;
+        }
       }
     }
   }
@@ -509,20 +535,37 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
                      hipStream_t st) {
   const T *x = (const T*)X, *w = (const T*)W;
   if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp || a.row_invariant) {
-    // Row blocks per workgroup: one (more workgroups, less activation traffic per CU) while the
-    // grid stays near 400 workgroups, else two or four (measured on MI355X decode shapes).
+    // Tiles per workgroup (TPW) and row blocks (NMB) from a cost model fitted to MI355X
+    // measurements of this kernel: one workgroup per CU at a time, each round of up to 256
+    // workgroups costs a memory latency (~70 KB of per-CU transfer time) plus its
+    // workgroup's bytes (TPW weight tiles + the X rows it reads) at the per-CU rate.
     const dim3 blk(kSkW * WAVE);
-    const int ntile = (N + 15) / 16;
-    auto wgs = [&](int nmb) { return (int64_t)ntile * ((M + 16 * nmb - 1) / (16 * nmb)); };
-    int nmb = wgs(1) <= 400 ? 1 : (wgs(2) <= 400 ? 2 : 4);
-    if (nmb == 4 && M <= 32) nmb = 2;
-    const dim3 grid(ntile, (M + 16 * nmb - 1) / (16 * nmb));
-    if (nmb == 1)
-      hipLaunchKernelGGL((gemm_skinny<T, E, 1>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
-    else if (nmb == 2)
-      hipLaunchKernelGGL((gemm_skinny<T, E, 2>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
-    else
-      hipLaunchKernelGGL((gemm_skinny<T, E, 4>), grid, blk, 0, st, x, ldx, w, M, N, K, a);
+    const int64_t xs = a.x_split ? 2 : 1, e = sizeof(T);
+    static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
+    int best_t = 1, best_n = 1;
+    int64_t best_cost = -1;
+    for (const auto& c : cand) {
+      const int tpw = c[0], nmb = c[1];
+      if (tpw > 1 && N % (16 * tpw) != 0) continue;   // one tile per workgroup covers a ragged N
+      const int64_t wgs = (int64_t)((N + 16 * tpw - 1) / (16 * tpw)) * ((M + 16 * nmb - 1) / (16 * nmb));
+      const int64_t rows = std::min(16 * nmb, M);
+      const int64_t bytes = (int64_t)tpw * 16 * K * e + rows * K * e * xs;
+      const int64_t cost = ((wgs + 255) / 256) * (70 * 1024 + bytes);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_t = tpw;
+        best_n = nmb;
+      }
+    }
+    const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n));
+#define RLT_SKINNY(NMB_, TPW_)                                                                                   \
+  if (best_n == NMB_ && best_t == TPW_) {                                                                        \
+    hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_>), grid, blk, 0, st, x, ldx, w, M, N, K, a);                 \
+    return;                                                                                                      \
+  }
+    RLT_SKINNY(1, 1) RLT_SKINNY(2, 1) RLT_SKINNY(4, 1) RLT_SKINNY(1, 2) RLT_SKINNY(2, 2) RLT_SKINNY(4, 2)
+    RLT_SKINNY(1, 4) RLT_SKINNY(2, 4)
+#undef RLT_SKINNY
   } else if (large_gemm_enabled<T>() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
     hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(256), 2 * 2 * kBStage * sizeof(T), st, x, ldx, w, M, N,
