@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--scan-mode", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=32)
+    ap.add_argument("--progress-every", type=int, default=0,
+                    help="issue the scan as calls of this many positions, each followed by a sync and a "
+                         "progress line (slow profiler passes; adds one norm kernel per call)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--sweep", default="",
@@ -194,13 +197,23 @@ def main():
         rlt.rlt_set_scan_mode(model.h, args.scan_mode)
     st = model.state(B, T, keep_encoder_cache=False)
     stream = torch.cuda.current_stream()
+    pieces = []   # (first column, positions, log-prob buffer, next tokens) of each progress call
+    for c0 in range(0, T, args.progress_every if args.progress_every > 0 else T):
+        n = min(args.progress_every, T - c0) if args.progress_every > 0 else T
+        pieces.append((c0, n, torch.empty((B, n), dtype=torch.float32, device=dev), nx[:, c0:c0 + n].contiguous()))
 
     def step(evs=None):
         rlt.rlt_state_reset(model.h, st)
         if evs: evs[0].record(stream)
         rlt.rlt_encode(model.h, st, x)
         if evs: evs[1].record(stream)
-        rlt.rlt_decode_scan(model.h, st, T, next_logprob=lp, next_tokens=nx)
+        if args.progress_every > 0:
+            for c0, n, lpc, nxc in pieces:
+                rlt.rlt_decode_scan(model.h, st, n, next_logprob=lpc, next_tokens=nxc)
+                torch.cuda.synchronize()
+                print(f"[bench] scan positions {c0 + n}/{T} done", flush=True)
+        else:
+            rlt.rlt_decode_scan(model.h, st, T, next_logprob=lp, next_tokens=nx)
         if evs: evs[2].record(stream)
 
     for _ in range(args.warmup):

@@ -3,7 +3,10 @@
     python -m recurrent_looped_transformer_amd.profiling run OUT [bench args...]
         (on the GPU machine; starts rocprofv3 as child processes, never touches the GPU itself)
         1. --kernel-trace --stats over `bench.py --steps 3 --warmup 1 --no-cpu ...`
-        2. --pmc FETCH_SIZE, 3. --pmc WRITE_SIZE over `bench.py --steps 1 --warmup 0 --no-cpu ...`
+        2. --pmc FETCH_SIZE, 3. --pmc WRITE_SIZE over
+           `bench.py --steps 1 --warmup 0 --no-cpu --progress-every 64 ...` (the scan as calls of
+           64 positions with a progress line after each: counter collection serialises every
+           dispatch; each call adds one 64-row norm kernel)
         4./5. the same two counters over `bench.py --copy-probe 268435456` (a plain 256 MiB
            device copy: the counters' bytes per dispatch for known traffic)
     python -m recurrent_looped_transformer_amd.profiling summarize OUT NAME [bench args...]
@@ -46,13 +49,14 @@ def _rocprof(out_dir: str, tag: str, prof_args, bench_args, log):
 
 
 def run(out_dir: str, bench_args):
+    out_dir = os.path.abspath(out_dir)   # rocprofv3 runs from /tmp
     os.makedirs(out_dir, exist_ok=True)
     lg = lambda t: os.path.join(out_dir, f"{t}.log")
     _rocprof(out_dir, "trace", ["--kernel-trace", "--stats"],
              ["--steps", "3", "--warmup", "1", "--no-cpu"] + bench_args, lg("trace"))
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        _rocprof(out_dir, c.lower(), ["--pmc", c], ["--steps", "1", "--warmup", "0", "--no-cpu"] + bench_args,
-                 lg(c.lower()))
+        _rocprof(out_dir, c.lower(), ["--pmc", c],
+                 ["--steps", "1", "--warmup", "0", "--no-cpu", "--progress-every", "64"] + bench_args, lg(c.lower()))
         _rocprof(out_dir, "copy_" + c.lower(), ["--pmc", c], ["--copy-probe", str(COPY_BYTES)],
                  lg("copy_" + c.lower()))
     # keep only the small CSVs the summary reads (the per-dispatch trace can be hundreds of MB)
@@ -132,7 +136,8 @@ def summarize(out_dir: str, name: str, bench_args):
              "Commands (R = repository root on the MI355X box; every file run is committed):", "",
              f"    python -m recurrent_looped_transformer_amd.profiling run OUT {' '.join(bench_args)}",
              "    (rocprofv3 --kernel-trace --stats ... -- python3 R/bench.py --steps 3 --warmup 1 --no-cpu ARGS;",
-             "     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 R/bench.py --steps 1 --warmup 0 --no-cpu ARGS;",
+             "     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 R/bench.py --steps 1 --warmup 0 --no-cpu "
+             "--progress-every 64 ARGS;",
              f"     the same counters over python3 R/bench.py --copy-probe {COPY_BYTES})",
              f"    python -m recurrent_looped_transformer_amd.profiling summarize OUT {name} {' '.join(bench_args)}", "",
              f"Counter scale: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f} (a {COPY_BYTES >> 20} MiB copy reads "
