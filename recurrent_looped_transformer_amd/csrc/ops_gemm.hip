@@ -492,6 +492,117 @@ __global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64
   }
 }
 
+// ------------------------------------------------------------------ mid (decode, M >= 256)
+// Decode GEMMs with a few hundred rows and a wide output are MFMA work, not weight
+// streaming: 128 x 128 output tile per workgroup of 4 waves (2 x 2, each 64 x 64 = 4 x 4 MFMA
+// tiles), the LDS layout and copy scheme of gemm_large at half the tile (a stage is 16 KB:
+// one k half of 8 weight tiles and 8 row blocks; a ring of four stages requested three ahead;
+// 64 KB of LDS, two workgroups per CU), and the folded-norm row scale of the input rows.
+// (A ring of eight stages measured no faster: a stage's time is not the copies' latency.)
+constexpr int kMT = 128;
+
+template <typename T, Ep E>
+__global__ __launch_bounds__(256) void gemm_mid(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W, int M,
+                                                int N, int K, EpArgs a) {
+  // [W 512 uint4 | X 512 uint4] each; distinct objects so that every LDS read names its stage
+  __shared__ uint4 sb0[1024], sb1[1024], sb2[1024], sb3[1024];
+  __shared__ float rsl[kMT];
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int ntm = (M + kMT - 1) / kMT;
+  const int tm = blockIdx.x % ntm, tn = blockIdx.x / ntm;
+  const int m0 = tm * kMT, n0 = tn * kMT;
+  const int nkw = K / 64;
+  const int nk = 2 * (a.x_split ? 2 * nkw : nkw);   // half-slice stages
+
+  // wave w copies weight tiles 2 w, 2 w + 1 and row blocks 2 w, 2 w + 1 of each stage
+  const T* wbase = W + (int64_t)(n0 / 16 + wave * 2) * 16 * K + lane * 8;
+  const int xrow0 = m0 + wave * 32 + r;
+  const T* xbase = X + g * 16;
+  auto issue = [&](int st_, uint4* sb) {
+    const int kt = st_ >> 1, h = st_ & 1;
+    const int kw = kt < nkw ? kt : kt - nkw;
+    uint4* d = sb + wave * 2 * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const T* wsrc = wbase + (int64_t)i * 16 * K + h * 512 + (int64_t)kw * 1024;
+      const int row = min(xrow0 + i * 16, M - 1);
+      const T* xsrc = xbase + (int64_t)row * ldx + h * 8 + (int64_t)kt * 64;
+      __builtin_amdgcn_global_load_lds((const void*)wsrc, (__attribute__((address_space(3))) void*)(d + i * 64), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)xsrc, (__attribute__((address_space(3))) void*)(d + 512 + i * 64),
+                                       16, 0, 0);
+    }
+  };
+  issue(0, sb0);
+  if (1 < nk) issue(1, sb1);
+  if (2 < nk) issue(2, sb2);
+
+  // folded RMSNorm of the input rows (while the first stages are in flight): wave w owns rows
+  // m0 + 32 w .. + 31
+  if (a.rs_ssp) {
+    for (int i = 0; i < 32; ++i) {
+      const int m = min(m0 + wave * 32 + i, M - 1);
+      float t = 0.f;
+      for (int k = lane; k < a.rs_n; k += WAVE) t += a.rs_ssp[(int64_t)m * a.rs_n + k];
+      t = wave_sum_dpp(t);
+      if (lane == 0) rsl[wave * 32 + i] = rsqrtf(t / (float)a.rs_d + a.rs_eps);
+    }
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // stage s: this wave's copies of s have landed (the two later stages, 4 copies each, may be
+  // in flight), a bare barrier (the fence of __syncthreads would also wait for them), request
+  // stage s + 3 into the buffer stage s - 1 used, multiply stage s
+  auto stage = [&](int s, const uint4* cur, uint4* nxt) {
+    // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at max
+    if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
+    else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + 3 < nk) issue(s + 3, nxt);
+    const uint4* sw = cur + (wn / 16) * 64;
+    const uint4* sx = cur + 512 + (wm / 16) * 64;
+    uint4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = sw[i * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = sx[j * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
+  };
+  for (int s = 0; s < nk; s += 4) {
+    stage(s, sb0, sb3);
+    if (s + 1 < nk) stage(s + 1, sb1, sb0);
+    if (s + 2 < nk) stage(s + 2, sb2, sb1);
+    if (s + 3 < nk) stage(s + 3, sb3, sb2);
+  }
+  __syncthreads();   // rsl
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wn + i * 16 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm + j * 16 + r;
+      if (m < M && n < N) {
+        const float sc = a.rs_ssp ? rsl[wm + j * 16 + r] : 1.f;
+        float v[4] = {acc[i][j][0] * sc, acc[i][j][1] * sc, acc[i][j][2] * sc, acc[i][j][3] * sc};
+        epilogue<T, E>(a, m, n, v);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32
 template <Ep E>
 __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int64_t ldx,
@@ -525,7 +636,14 @@ template <typename T, Ep E>
 static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
                      hipStream_t st) {
   const T *x = (const T*)X, *w = (const T*)W;
-  if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp || a.row_invariant) {
+  const int mid_tiles = ((M + kMT - 1) / kMT) * ((N + kMT - 1) / kMT);
+  if (M >= 2 * kMT && M <= kSkinnyMaxRows && mid_tiles >= 128 && K % 64 == 0 && !a.row_invariant && !a.fold_zb) {
+    // a few hundred rows and a wide output: MFMA-bound tiles (measured on MI355X on the
+    // medium-LM shapes: M 512, N 6144, K 2048 in 34 us against 54 us for the streaming
+    // kernel below; with fewer than 128 tiles the streaming kernel stays faster)
+    const int nt = mid_tiles;
+    hipLaunchKernelGGL((gemm_mid<T, E>), dim3(nt), dim3(256), 0, st, x, ldx, w, M, N, K, a);
+  } else if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp || a.row_invariant) {
     // Tiles per workgroup (TPW) and row blocks (NMB) from a cost model fitted to MI355X
     // measurements of this kernel: one workgroup per CU at a time, each round of up to 256
     // workgroups costs a memory latency (~70 KB of per-CU transfer time) plus its
