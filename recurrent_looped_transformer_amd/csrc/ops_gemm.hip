@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(const T* __restrict__ X, int64
 }
 
 // ------------------------------------------------------------------ large (prefill)
-// 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave 128 x 128 (8 x 8 MFMA
+// 256 x 256 output tile per workgroup of 8 waves (2 x 4), each wave 128 x 64 (8 x 4 MFMA
 // tiles), both operands staged in LDS in the MFMA lane order: a 16-row group of a 64-wide k
 // slice is one 2 KB block whose first (second) 1 KB holds k 16g..16g+7 (16g+8..16g+15) of
 // row r for lane 16g + r; a stage is one of those 1 KB halves of every 16-row group of both
@@ -390,6 +390,9 @@ __global__ __launch_bounds__(256) void gemm_tiled(const T* __restrict__ X, int64
 constexpr int kBT = 256;                 // tile rows (both operands)
 constexpr int kBK = 64;                  // k per stage
 
+// Eight waves (2 x 4, each 128 rows x 64 features) rather than four (2 x 2, 128 x 128): two
+// waves per SIMD hide each other's LDS waits and barriers (measured +7-13%, e.g. 1014 against
+// 915 TFLOP/s at M 32768, N 2048, K 5632; the result is the same bit for bit).
 // The operands move straight from global memory into LDS (global_load_lds: 16 bytes per
 // lane, a wavefront fills 1 KB of LDS per instruction; no staging registers) over a ring of
 // four stage buffers, so that a stage is requested three stages before it is multiplied
@@ -398,17 +401,21 @@ constexpr int kBK = 64;                  // k per stage
 // i of a stage copies tile i's half (contiguous in the tile-major layout); activation
 // instruction i gathers 16-row block i: lane l reads 8 values of row l % 16 at k 16 (l / 16)
 // + 8 h.
-template <typename T, Ep E>
-__global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
-                                                      int M, int N, int K, EpArgs a) {
+template <typename T, Ep E, int NWV = 4>
+__global__ __launch_bounds__(NWV * 64) void gemm_large(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
+                                                       int M, int N, int K, EpArgs a) {
   // four stage buffers as distinct objects, each [W 1024 uint4 | X 1024 uint4]: with the stage
   // loop unrolled by four every LDS read names its buffer, so the compiler knows which
   // outstanding copies it depends on
   __shared__ uint4 sb0[2048], sb1[2048], sb2[2048], sb3[2048];
+  constexpr int WNT = NWV == 8 ? 64 : 128;   // wave tile: 128 rows x WNT features
+  constexpr int NI = WNT / 16;               // feature tiles per wave
+  constexpr int CPW = 16 / NWV;              // weight tiles (and row blocks) copied per wave and stage
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r = lane & 15, g = lane >> 4;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (NWV == 8 ? (wave >> 2) : (wave >> 1)) * 128;
+  const int wn = (NWV == 8 ? (wave & 3) : (wave & 1)) * WNT;
   const int ntm = (M + kBT - 1) / kBT, ntn = (N + kBT - 1) / kBT;
   const int nt = ntm * ntn;
   int pid = blockIdx.x;
@@ -418,16 +425,16 @@ __global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64
   const int nkw = K / kBK;
   const int nk = 2 * (a.x_split ? 2 * nkw : nkw);   // half-slice stages (a multiple of 2)
 
-  // wave w issues tiles / row blocks 4 w .. 4 w + 3 of each stage
-  const T* wbase = W + (int64_t)(n0 / 16 + wave * 4) * 16 * K + lane * 8;
-  const int xrow0 = m0 + wave * 64 + r;
+  // wave w issues tiles / row blocks CPW w .. CPW w + CPW - 1 of each stage
+  const T* wbase = W + (int64_t)(n0 / 16 + wave * CPW) * 16 * K + lane * 8;
+  const int xrow0 = m0 + wave * CPW * 16 + r;
   const T* xbase = X + g * 16;
   auto issue = [&](int st_, uint4* sb) {
     const int kt = st_ >> 1, h = st_ & 1;
     const int kw = kt < nkw ? kt : kt - nkw;
-    uint4* d = sb + wave * 4 * 64;
+    uint4* d = sb + wave * CPW * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPW; ++i) {
       const T* wsrc = wbase + (int64_t)i * 16 * K + h * 512 + (int64_t)kw * 1024;
       const int row = min(xrow0 + i * 16, M - 1);
       const T* xsrc = xbase + (int64_t)row * ldx + h * 8 + (int64_t)kt * kBK;
@@ -438,33 +445,39 @@ __global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[NI][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // stage s: wait for this wave's copies of s (the two later stages, 8 copies each, may still
-  // be in flight), a bare barrier (the fence of __syncthreads would also wait for them), then
-  // request stage s + 3 into the buffer stage s - 1 used, and multiply stage s
+  // stage s: wait for this wave's copies of s (the two later stages, 2 CPW copies each, may
+  // still be in flight), a bare barrier (the fence of __syncthreads would also wait for
+  // them), then request stage s + 3 into the buffer stage s - 1 used, and multiply stage s
   auto stage = [&](int s, const uint4* cur, uint4* nxt) {
     // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at max
-    if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-    else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    if constexpr (NWV == 8) {
+      if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
+      else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    } else {
+      if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+      else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (s + 3 < nk) issue(s + 3, nxt);
     const uint4* sw = cur + (wn / 16) * 64;
     const uint4* sx = cur + 1024 + (wm / 16) * 64;
-    uint4 af[8], bfr[8];
+    uint4 af[NI], bfr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = sw[i * 64 + lane];
+    for (int i = 0; i < NI; ++i) af[i] = sw[i * 64 + lane];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bfr[j] = sx[j * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
   };
@@ -478,7 +491,7 @@ __global__ __launch_bounds__(256) void gemm_large(const T* __restrict__ X, int64
     if (s + 3 < nk) stage(s + 3, sb3, sb2);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int n = n0 + wn + i * 16 + 4 * g;
     if (n >= N) continue;
 #pragma unroll
@@ -677,7 +690,7 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
 #undef RLT_SKINNY
   } else if (large_gemm_enabled() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-    hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(256), 0, st, x, ldx, w, M, N, K, a);
+    hipLaunchKernelGGL((gemm_large<T, E, 8>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
   } else {
     hipLaunchKernelGGL((gemm_tiled<T, E>), dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st, x, ldx, w,
                        M, N, K, a);
