@@ -164,7 +164,7 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 // query blocks of the wave. Softmax statistics are fp32 per query, online over key tiles.
 namespace rlt {
 
-// QB query blocks of 16 per wave: up to 4 at dh 64 and 2 at dh 128 (register budget); short
+// QB query blocks of 16 per wave: up to 4 (2 for bf16 at dh 128: register budget); short
 // sequences take one so that the grid keeps enough workgroups.
 template <typename T, int DH, int QB>
 __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
@@ -337,7 +337,10 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 
 template <typename T, int DH>
 static void launch_flash(const AttnArgs& a, hipStream_t st) {
-  constexpr int QBMAX = DH >= 128 ? 2 : 4;
+  // four query blocks per wave; at dh 128 fp16 that is 1.3x over two at the medium-LM encode
+  // (measured; 256 + 256 registers, no spills), while bf16 (whose unpacking takes more
+  // registers) would spill there and keeps two
+  constexpr int QBMAX = (DH >= 128 && !__is_same(T, f16_t)) ? 2 : 4;
   if (a.nq <= 512) {
     hipLaunchKernelGGL((flash_prefill_k<T, DH, 1>), dim3((a.nq + 63) / 64, a.H, a.B), dim3(256), 0, st, a);
   } else {
