@@ -72,7 +72,7 @@ def short(name: str) -> str:
             name = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip() or name
         except OSError:
             pass
-    name = re.sub(r"^void ", "", name)
+    name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
     if "<" in name.split("(")[0]:
         depth, end = 0, len(name)
         for i, ch in enumerate(name):
