@@ -401,21 +401,20 @@ constexpr int kBK = 64;                  // k per stage
 // i of a stage copies tile i's half (contiguous in the tile-major layout); activation
 // instruction i gathers 16-row block i: lane l reads 8 values of row l % 16 at k 16 (l / 16)
 // + 8 h.
-template <typename T, Ep E, int NWV = 4>
-__global__ __launch_bounds__(NWV * 64) void gemm_large(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
+template <typename T, Ep E>
+__global__ __launch_bounds__(512) void gemm_large(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
                                                        int M, int N, int K, EpArgs a) {
   // four stage buffers as distinct objects, each [W 1024 uint4 | X 1024 uint4]: with the stage
   // loop unrolled by four every LDS read names its buffer, so the compiler knows which
   // outstanding copies it depends on
   __shared__ uint4 sb0[2048], sb1[2048], sb2[2048], sb3[2048];
-  constexpr int WNT = NWV == 8 ? 64 : 128;   // wave tile: 128 rows x WNT features
-  constexpr int NI = WNT / 16;               // feature tiles per wave
-  constexpr int CPW = 16 / NWV;              // weight tiles (and row blocks) copied per wave and stage
+  constexpr int NI = 4;    // feature tiles per wave (wave tile: 128 rows x 64 features)
+  constexpr int CPW = 2;   // weight tiles (and row blocks) copied per wave and stage
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r = lane & 15, g = lane >> 4;
-  const int wm = (NWV == 8 ? (wave >> 2) : (wave >> 1)) * 128;
-  const int wn = (NWV == 8 ? (wave & 3) : (wave & 1)) * WNT;
+  const int wm = (wave >> 2) * 128;
+  const int wn = (wave & 3) * 64;
   const int ntm = (M + kBT - 1) / kBT, ntn = (N + kBT - 1) / kBT;
   const int nt = ntm * ntn;
   int pid = blockIdx.x;
@@ -456,15 +455,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_large(const T* __restrict__ X, 
   // them), then request stage s + 3 into the buffer stage s - 1 used, and multiply stage s
   auto stage = [&](int s, const uint4* cur, uint4* nxt) {
     // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at max
-    if constexpr (NWV == 8) {
-      if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
-      else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-    } else {
-      if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-      else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-    }
+    if (s + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
+    else if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -690,7 +683,7 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
 #undef RLT_SKINNY
   } else if (large_gemm_enabled() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-    hipLaunchKernelGGL((gemm_large<T, E, 8>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
+    hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
   } else {
     hipLaunchKernelGGL((gemm_tiled<T, E>), dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st, x, ldx, w,
                        M, N, K, a);
