@@ -253,6 +253,37 @@ int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float 
 int rlt_importance_ratio(const float* logprob_current, const float* logprob_behaviour, int64_t n, float* ratio,
                          hipStream_t stream);
 
+/* Full back-propagation through time of the replay ([R] §6.2 eq 5.5 for what is replayed;
+ * [R] appendix B eq B.4 and §6.4: the reference training computation differentiates the
+ * whole sequential unroll, through s_t, through every decoder key/value including entries
+ * the window later drops, and through the encoder memory). For the loss
+ *   L = sum_{b, t} dlogprob[b, t] * logprob[b, t]      (t = 1..T-1)
+ * writes logprob (fp32 [B, T-1], as rlt_replay computes it) and dL/dtheta for every
+ * manifest parameter. Any loss built from the replay's log-probabilities (an
+ * importance-weighted policy objective, a likelihood) enters through its derivative with
+ * respect to them, dlogprob (fp32 [B, T-1]).
+ * Arithmetic is fp32 throughout (the log-sum-exp of the readout in float64) whatever
+ * cfg->dtype: the weights are used as given. Every intermediate of the unroll is kept in
+ * `workspace` (device memory the caller owns, at least rlt_replay_grad_workspace bytes,
+ * 256-byte aligned); nothing is recomputed and nothing is allocated.
+ * weights: the manifest tensors (device fp32, as for rlt_create). grads: one writable
+ * device fp32 tensor per manifest name with the same size (zeroed, then filled).
+ * tokens: device int32 [B, T], x_1 = BOS. Asynchronous on `stream`.
+ * Errors: INVALID_ARG (configuration, missing/unknown/duplicate/mis-sized tensors, B < 1,
+ * T < 2, null pointers, workspace too small or misaligned), UNSUPPORTED (configuration
+ * outside the library's limits). */
+typedef struct {
+  const char* name;
+  float* data;
+  int64_t numel;
+} rlt_grad_tensor;
+
+int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int64_t* bytes);
+
+int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, rlt_grad_tensor* grads,
+                    int n_grads, const int32_t* tokens, int B, int T, const float* dlogprob, float* logprob,
+                    void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* Scan driver for the decoder transitions: 0 = automatic (mode 1),
  * 1 = one launch sequence per position (stream-ordered), 2 = persistent cooperative kernel
  * with the automatic work split, 3 = persistent with every workgroup on all sequences,

@@ -25,7 +25,7 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
-SOURCES = ["ops_gemm.hip", "ops_attn.hip", "ops_misc.hip", "ops_scan.hip", "ops_sample.hip", "rlt_api.hip"]
+SOURCES = ["ops_gemm.hip", "ops_attn.hip", "ops_misc.hip", "ops_scan.hip", "ops_sample.hip", "grad.hip", "rlt_api.hip"]
 
 
 def _compile(src: str) -> str:

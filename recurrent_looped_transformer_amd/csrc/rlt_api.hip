@@ -17,6 +17,7 @@
 #include "rlt.h"
 #include "ops.hpp"
 #include "scan.hpp"
+#include "grad.hpp"
 
 using namespace rlt;
 
@@ -1375,6 +1376,45 @@ int rlt_importance_ratio(const float* logprob_current, const float* logprob_beha
     if (n > 0 && (!logprob_current || !logprob_behaviour || !ratio)) fail(RLT_ERR_INVALID_ARG, "null pointer");
     importance_ratio(logprob_current, logprob_behaviour, n, ratio, stream);
     check_launch();
+  });
+}
+
+int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int64_t* bytes) {
+  return guarded([&] {
+    if (!cfg || !bytes) fail(RLT_ERR_INVALID_ARG, "null pointer");
+    validate_config(*cfg);
+    if (B < 1 || T < 2) fail(RLT_ERR_INVALID_ARG, "B >= 1 and T >= 2 required");
+    *bytes = (int64_t)grad_workspace_bytes(*cfg, B, T);
+  });
+}
+
+int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, rlt_grad_tensor* grads,
+                    int n_grads, const int32_t* tokens, int B, int T, const float* dlogprob, float* logprob,
+                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return guarded([&] {
+    if (!cfg) fail(RLT_ERR_INVALID_ARG, "null config");
+    validate_config(*cfg);
+    if (B < 1 || T < 2) fail(RLT_ERR_INVALID_ARG, "B >= 1 and T >= 2 required");
+    if (!tokens || !dlogprob || !logprob || !workspace) fail(RLT_ERR_INVALID_ARG, "null pointer");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) fail(RLT_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    if (workspace_bytes < (int64_t)grad_workspace_bytes(*cfg, B, T)) fail(RLT_ERR_INVALID_ARG, "workspace too small");
+    auto W = index_weights(*cfg, weights, n_weights);
+    if (n_grads < 0 || (n_grads > 0 && !grads)) fail(RLT_ERR_INVALID_ARG, "grads pointer");
+    auto man = manifest(*cfg);
+    std::map<std::string, std::pair<float*, int64_t>> G;
+    for (int i = 0; i < n_grads; ++i) {
+      if (!grads[i].name || !grads[i].data) fail(RLT_ERR_INVALID_ARG, "null gradient name or data");
+      auto it = man.find(grads[i].name);
+      if (it == man.end()) fail(RLT_ERR_INVALID_ARG, std::string("unknown gradient ") + grads[i].name);
+      if (grads[i].numel != it->second.rows * it->second.cols)
+        fail(RLT_ERR_INVALID_ARG, std::string("wrong size for gradient ") + grads[i].name);
+      if (G.count(grads[i].name)) fail(RLT_ERR_INVALID_ARG, std::string("duplicate gradient ") + grads[i].name);
+      G[grads[i].name] = {grads[i].data, grads[i].numel};
+    }
+    for (auto& kv : man)
+      if (!G.count(kv.first)) fail(RLT_ERR_INVALID_ARG, "missing gradient " + kv.first);
+    hipError_t e = replay_grad(*cfg, W, G, tokens, B, T, dlogprob, logprob, workspace, stream);
+    if (e != hipSuccess) fail(RLT_ERR_HIP, std::string("replay gradient: ") + hipGetErrorString(e));
   });
 }
 

@@ -27,7 +27,8 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_state_destroy", "rlt_state_bytes", "rlt_state_positions", "rlt_encode", "rlt_decode_scan",
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
-           "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant"]
+           "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant", "rlt_replay_grad_workspace",
+           "rlt_replay_grad"]
 
 
 class RltError(RuntimeError):
@@ -53,6 +54,10 @@ class rlt_snapshot_info(ctypes.Structure):
 
 
 class rlt_tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class rlt_grad_tensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("numel", ctypes.c_int64)]
 
 
@@ -90,6 +95,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_snapshot_size": [vp, vp, i64p],
         "rlt_snapshot": [vp, vp, vp, ctypes.c_int64, ctypes.POINTER(rlt_snapshot_info), vp],
         "rlt_restore": [vp, vp, ctypes.POINTER(rlt_snapshot_info), vp, vp],
+        "rlt_replay_grad_workspace": [ctypes.POINTER(rlt_config), i32, i32, i64p],
+        "rlt_replay_grad": [ctypes.POINTER(rlt_config), ctypes.POINTER(rlt_tensor), i32,
+                            ctypes.POINTER(rlt_grad_tensor), i32, vp, i32, i32, vp, vp, vp, ctypes.c_int64, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -260,6 +268,45 @@ def rlt_restore(model, state, info: rlt_snapshot_info, src: torch.Tensor) -> Non
     assert src.dtype == torch.uint8 and src.is_contiguous() and src.numel() >= info.bytes
     _check(load().rlt_restore(model, state, ctypes.byref(info), ctypes.c_void_p(src.data_ptr()),
                               ctypes.c_void_p(_stream())))
+
+
+def rlt_replay_grad_workspace(cfg: synth.Config, B: int, T: int) -> int:
+    n = ctypes.c_int64(0)
+    c = config_struct(cfg)
+    _check(load().rlt_replay_grad_workspace(ctypes.byref(c), B, T, ctypes.byref(n)))
+    return n.value
+
+
+def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens: torch.Tensor,
+                    dlogprob: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Full-BPTT gradient of sum(dlogprob * logprob) over the replay of tokens [B, T].
+
+    weights: manifest name -> contiguous fp32 device tensor. Returns (logprob [B, T-1],
+    {name: gradient tensor}). The workspace (uint8 device tensor) is allocated here unless
+    given."""
+    assert tokens.dtype == torch.int32 and tokens.dim() == 2 and dlogprob.dtype == torch.float32
+    B, T = tokens.shape
+    dev = tokens.device
+    need = rlt_replay_grad_workspace(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    assert workspace.dtype == torch.uint8 and workspace.numel() >= need
+    names = list(weights)
+    warr = (rlt_tensor * len(names))()
+    garr = (rlt_grad_tensor * len(names))()
+    grads = {}
+    for i, n in enumerate(names):
+        t = weights[n]
+        assert t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda
+        warr[i] = rlt_tensor(n.encode(), t.data_ptr(), t.numel())
+        grads[n] = torch.empty_like(t)
+        garr[i] = rlt_grad_tensor(n.encode(), grads[n].data_ptr(), t.numel())
+    logprob = torch.empty(B, T - 1, dtype=torch.float32, device=dev)
+    c = config_struct(cfg)
+    _check(load().rlt_replay_grad(ctypes.byref(c), warr, len(names), garr, len(names), _ptr(tokens), B, T,
+                                  _ptr(dlogprob.contiguous()), _ptr(logprob), ctypes.c_void_p(workspace.data_ptr()),
+                                  workspace.numel(), ctypes.c_void_p(_stream())))
+    return logprob, grads
 
 
 # ----------------------------------------------------------------- convenience

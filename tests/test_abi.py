@@ -87,3 +87,21 @@ def test_null_arguments(lib):
     assert lib.rlt_state_destroy(None) == -1
     assert lib.rlt_destroy(None) == -1
     assert lib.rlt_set_scan_mode(None, 0) == -1
+
+
+def test_replay_grad_workspace_and_host_checks(lib):
+    """Workspace bytes: positive, 256-byte multiple, growing with T and B; invalid
+    arguments are rejected on the host before any launch."""
+    cfg = synth.CONFIGS["tiny_fp32"]
+    a = rlt.rlt_replay_grad_workspace(cfg, 2, 16)
+    b = rlt.rlt_replay_grad_workspace(cfg, 2, 32)
+    c = rlt.rlt_replay_grad_workspace(cfg, 4, 16)
+    assert 0 < a < b and a < c and a % 256 == 0
+    n = ctypes.c_int64(0)
+    cs = rlt.config_struct(cfg)
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 2, 1, ctypes.byref(n)) == -1       # T < 2
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 0, 16, ctypes.byref(n)) == -1      # B < 1
+    bad = rlt.config_struct(cfg.replace(groups=3))
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(bad), 2, 16, ctypes.byref(n)) == -2     # G not in {1, L_D}
+    # null tokens / workspace: rejected before touching the device
+    assert lib.rlt_replay_grad(ctypes.byref(cs), None, 0, None, 0, None, 2, 16, None, None, None, 0, None) == -1
