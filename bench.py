@@ -113,6 +113,95 @@ def decode_sweep(shapes, batches, positions, steps: int = 8):
         model.close()
 
 
+FP32_PEAK_TFLOPS = 157.3
+GRAD_METRIC = "replay gradient (full BPTT) transitions/sec at batch B; % of fp32 vector roofline"
+
+
+def grad_flops(cfg, B: int, T: int) -> float:
+    """Algorithmic flops of one full-BPTT gradient pass (forward kept for the backward).
+
+    Every matrix product appears three times (forward, input gradient, weight gradient):
+    3 * 2 * (B*T rows) * (matrix parameters: encoder, memory, decoder, merge, readout). The
+    attention terms (scores and weighted sums: 4*hd per query-key pair; encoder causal,
+    decoder window min(t, W) and memory prefix t) also count three times (forward; and
+    the backward's four products over the same pairs, two of which repeat forward ones).
+    """
+    d, f, hd, V, LE, LD, W = cfg.d, cfg.ffn, cfg.hd, cfg.vocab, cfg.L_E, cfg.L_D, cfg.window
+    G = cfg.groups if LD > 0 else 0
+    mats = LE * (4 * d * hd + 3 * d * f) + G * 2 * d * hd + LD * (6 * d * hd + 3 * d * f) \
+        + (3 * d * d if cfg.variant != 0 else 0) + V * d
+    gemm = 2.0 * B * T * mats
+    attn = B * LE * 4 * hd * T * (T + 1) / 2 + B * LD * 4 * hd * sum(min(t, W) + t for t in range(1, T + 1))
+    return 3.0 * (gemm + attn)
+
+
+def grad_bench(args, cfg):
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import make_params, make_tokens
+    B, T = cfg.batch, cfg.seq_len
+    P = make_params(cfg)
+    tokens = make_tokens(cfg, length=T)
+    w = np.random.default_rng(3).standard_normal((B, T - 1)).astype(np.float32)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    W = {k: torch.as_tensor(np.ascontiguousarray(v, dtype=np.float32)).to(dev) for k, v in P.items()}
+    G = {k: torch.empty_like(v) for k, v in W.items()}
+    x = torch.as_tensor(tokens).to(dev)
+    wt = torch.as_tensor(w).to(dev)
+    lp = torch.empty((B, T - 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(rlt.rlt_replay_grad_workspace(cfg, B, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        rlt.rlt_replay_grad(cfg, W, x, wt, workspace=ws, grads=G, logprob=lp)
+        if ev: ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] gradient warm-up {i + 1}/{args.warmup} done", flush=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    ms_per_step = wall * 1e3 / args.steps
+    fl = grad_flops(cfg, B, T)
+    achieved = fl / (pass_ms / 1e3) / 1e12
+    out = {
+        "metric": GRAD_METRIC, "value": B * T / (ms_per_step / 1e3), "unit": "transitions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} shape, full-BPTT gradient of the replay loss "
+                               f"(fp32 arithmetic), RLT-{cfg.variant} B={B} T={T}",
+                   "batch": B, "seq_len": T, "d": cfg.d, "L_E": cfg.L_E, "L_D": cfg.L_D, "window": cfg.window,
+                   "groups": cfg.groups, "vocab": cfg.vocab, "variant": f"RLT-{cfg.variant}",
+                   "workspace_bytes": ws.numel()},
+        "gradient_pass_ms": pass_ms,
+        "roofline": {"bound": "alu", "kernel": "gradient pass (saved forward + reverse scan + weight gradients)",
+                     "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": fl},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+        from oracle.rlt_grad import GradOracle
+        sb = min(args.cpu_sample, B, 4)
+        t1 = time.perf_counter()
+        GradOracle(cfg, P).grad(tokens[:sb], w[:sb].astype(np.float64))
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": sb * T / dt, "unit": "transitions/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"{sb} of {B} sequences x {T} positions, full-BPTT gradient, "
+                                         f"float64 torch reverse mode, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, P, tokens, sample_B: int):
     from threadpoolctl import threadpool_info
     from oracle import Oracle
@@ -150,6 +239,8 @@ def main():
                          "t = 32 and the prompt length of each shape; prints one JSON line per point")
     ap.add_argument("--sweep-shapes", default="algo_bf16,medium_lm,paper_shared")
     ap.add_argument("--sweep-batches", default="1,2,4,8")
+    ap.add_argument("--grad", action="store_true",
+                    help="time the full-BPTT gradient of the replay (fp32 arithmetic) instead of the replay")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the RLT scan shards over independent sequences with no "
@@ -182,6 +273,9 @@ def main():
         cfg = cfg.replace(seq_len=args.seq_len)
     if args.variant >= 0:
         cfg = cfg.replace(variant=args.variant, chunk=cfg.chunk if args.variant == 2 else 1)
+    if args.grad:
+        grad_bench(args, cfg)
+        return
     B, T = cfg.batch, cfg.seq_len
     P = make_params(cfg)
     tokens = make_tokens(cfg, length=T)

@@ -53,11 +53,12 @@ constexpr int NOWIN = INT_MAX / 4;
 // C[m, n] = (R ? R[m, n] : 0) + sum_k A(m, k) B(k, n), or, when atomic, C[m, n] += sum.
 // A(m, k) = AK ? A[m*lda + k] : A[k*lda + m];  B(k, n) = BK ? B[n*ldb + k] : B[k*ldb + n].
 // R, when given, has C's layout (it may be C itself). blockIdx.z takes k in
-// [z*kchunk, (z+1)*kchunk).
+// [z*kchunk, (z+1)*kchunk). With `part`, the k-slice z writes its partial sums to
+// part[z][M][N] instead (summed by g_splitk_reduce in a fixed order).
 template <bool AK, bool BK>
 __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                                               const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
-                                              const float* R, int atomic, int kchunk) {
+                                              const float* R, int atomic, int kchunk, float* __restrict__ part) {
   __shared__ float As[GK][GT + 4];
   __shared__ float Bs[GK][GT + 4];
   const int tid = threadIdx.x;
@@ -119,11 +120,26 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
     for (int j = 0; j < 4; ++j) {
       const int gn = n0 + tx + 16 * j;
       if (gn >= N) continue;
+      if (part) {
+        part[((int64_t)blockIdx.z * M + gm) * N + gn] = acc[i][j];
+        continue;
+      }
       float* c = C + (int64_t)gm * ldc + gn;
       if (atomic) atomicAdd(c, acc[i][j]);
       else *c = (R ? R[(int64_t)gm * ldc + gn] : 0.f) + acc[i][j];
     }
   }
+}
+
+// C[m, n] = (R ? R[m, n] : 0) + sum_{z < splits} part[z][m][n], z ascending
+__global__ void g_splitk_reduce(int M, int N, int splits, const float* __restrict__ part, const float* R, float* C,
+                                int64_t ldc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int64_t m = i / N, n = i % N;
+  float v = 0.f;
+  for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + i];
+  C[m * ldc + n] = (R ? R[m * ldc + n] : 0.f) + v;
 }
 
 // ------------------------------------------------------------------------ RMSNorm
@@ -505,6 +521,8 @@ __global__ __launch_bounds__(64) void g_attn_bwd_kv(int B, int T, int win, int H
 // ----------------------------------------------------------------- host helpers
 struct Ctx {
   hipStream_t st;
+  float* part = nullptr;   // split-K partial sums of the small-M products
+  int64_t part_cap = 0;    // floats
   hipError_t err = hipSuccess;
   void check() {
     if (err == hipSuccess) err = hipGetLastError();
@@ -513,27 +531,40 @@ struct Ctx {
 
 inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-// C = R + A.B (see g_gemm), or C += A.B split over k with atomics
+// C = R + A.B (see g_gemm), or C += A.B split over k with atomics. Products with few
+// output tiles (the per-position products have B rows) split k over up to 16 slices whose
+// partial sums a second kernel adds in a fixed order (deterministic).
+constexpr int kMaxSplits = 16;
 void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, const float* Bm, int64_t ldb, bool bk,
           float* C, int64_t ldc, const float* R, bool atomic) {
   if (M <= 0 || N <= 0) return;
   const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT;
   int splits = 1;
+  float* part = nullptr;
   if (atomic) {
     const int want = std::max(1, 1024 / (tm * tn));
     splits = std::max(1, std::min(want, (K + 255) / 256));
+  } else if (tm * tn < 128 && K >= 128 && c.part) {
+    splits = std::min({kMaxSplits, (256 + tm * tn - 1) / (tm * tn), K / 64});
+    while (splits > 1 && (int64_t)splits * M * N > c.part_cap) --splits;
+    if (splits > 1) part = c.part;
   }
   int kchunk = (K + splits - 1) / splits;
   kchunk = (kchunk + GK - 1) / GK * GK;
   if (kchunk <= 0) kchunk = GK;
   splits = std::max(1, (K + kchunk - 1) / kchunk);
+  if (splits == 1) part = nullptr;
   dim3 grid(tn, tm, splits);
   const int at = atomic ? 1 : 0;
-  if (ak && bk) g_gemm<true, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk);
-  else if (ak) g_gemm<true, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk);
-  else if (bk) g_gemm<false, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk);
-  else g_gemm<false, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk);
+  if (ak && bk) g_gemm<true, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
+  else if (ak) g_gemm<true, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
+  else if (bk) g_gemm<false, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
+  else g_gemm<false, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
   c.check();
+  if (part) {
+    g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc);
+    c.check();
+  }
 }
 // Y[M, out] = R + X[M, in] . W^T, W row-major [out, ldw] (ldw = in unless a column slice)
 void lin(Ctx& c, int M, const float* X, int in, const float* W, int64_t ldw, int out, float* Y, const float* R) {
@@ -658,6 +689,8 @@ struct Bufs {
   float *tBd, *tBf, *tBhd, *gu, *carry, *greg;
   // encoder backward
   float *gh, *gmid, *gec, *gf1, *gf3, *geo, *geq, *gek, *gev, *Dq;
+  float* part;     // split-K partials of the per-position products
+  int64_t part_n;  // its floats
 };
 
 void plan(const rlt_config& c, int B, int T, Arena& A, Bufs& u) {
@@ -696,6 +729,8 @@ void plan(const rlt_config& c, int B, int T, Arena& A, Bufs& u) {
   u.gu = A.f((int64_t)B * d); u.carry = A.f((int64_t)B * d); u.greg = A.f((int64_t)B * d);
   u.gh = A.f(M * d); u.gmid = A.f(M * d); u.gec = A.f(M * d); u.gf1 = A.f(M * f); u.gf3 = A.f(M * f);
   u.geo = A.f(M * hd); u.geq = A.f(M * hd); u.gek = A.f(M * hd); u.gev = A.f(M * hd); u.Dq = A.f(M * H);
+  u.part_n = (int64_t)kMaxSplits * B * std::max({d, hd, f, 2 * d, (int64_t)c.vocab});
+  u.part = A.f(u.part_n);
 }
 
 }  // namespace
@@ -715,6 +750,8 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   A.base = static_cast<char*>(workspace);
   Bufs u;
   plan(cf, B, T, A, u);
+  c.part = u.part;
+  c.part_cap = u.part_n;
   const int M = B * T, d = cf.d, H = cf.n_heads, dh = cf.d_head, hd = H * dh, f = cf.ffn, V = cf.vocab;
   const double base = cf.rope_base;
   const float eps = cf.rms_eps, alpha = cf.alpha;

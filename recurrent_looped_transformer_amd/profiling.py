@@ -11,6 +11,10 @@
            device copy: the counters' bytes per dispatch for known traffic)
     python -m recurrent_looped_transformer_amd.profiling summarize OUT NAME [bench args...]
         writes profiles/kernels_NAME.md and profiles/traffic_scan_NAME.json
+    python -m recurrent_looped_transformer_amd.profiling trace OUT [bench args...]
+        (on the GPU machine) only pass 1, over `bench.py --steps 2 --warmup 1 --no-cpu ...`
+    python -m recurrent_looped_transformer_amd.profiling summarize-trace OUT NAME [bench args...]
+        writes profiles/kernels_NAME.md (kernel table only, no counters)
 
 Traffic of the scan = the sum of the counters over the scan's dispatches of the single
 profiled step: every dispatch from the RMSNorm that precedes the step's first merge GEMM
@@ -171,10 +175,53 @@ def summarize(out_dir: str, name: str, bench_args):
     print("\n".join(lines))
 
 
+def trace(out_dir: str, bench_args):
+    out_dir = os.path.abspath(out_dir)
+    os.makedirs(out_dir, exist_ok=True)
+    _rocprof(out_dir, "trace", ["--kernel-trace", "--stats"], ["--steps", "2", "--warmup", "1", "--no-cpu"] + bench_args,
+             os.path.join(out_dir, "trace.log"))
+    for big in glob.glob(os.path.join(out_dir, "trace", "**", "*kernel_trace.csv"), recursive=True):
+        os.remove(big)
+
+
+def summarize_trace(out_dir: str, name: str, bench_args):
+    stats = list(csv.DictReader(open(_one(os.path.join(out_dir, "trace", "**", "*kernel_stats.csv")))))
+    bench_line = ""
+    log = os.path.join(out_dir, "trace.log")
+    if os.path.exists(log):
+        for ln in open(log):
+            if ln.startswith("{") and '"metric"' in ln:
+                bench_line = ln.strip()
+    lines = [f"# Kernel summary: {name}", "",
+             "Commands (R = repository root on the MI355X box; every file run is committed):", "",
+             f"    python -m recurrent_looped_transformer_amd.profiling trace OUT {' '.join(bench_args)}",
+             "    (rocprofv3 --kernel-trace --stats ... -- python3 R/bench.py --steps 2 --warmup 1 --no-cpu ARGS)",
+             f"    python -m recurrent_looped_transformer_amd.profiling summarize-trace OUT {name} "
+             f"{' '.join(bench_args)}", "",
+             f"Library sha256 prefix: {lib_sha()}", "",
+             "rocprofv3 --stats (2 timed + 1 warm-up steps):", "",
+             "| kernel | calls | total ms | mean us | share |", "|---|---|---|---|---|"]
+    for r in stats[:20]:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    if bench_line:
+        lines += ["", "bench line of the profiled run (times include the profiler's overhead):", "",
+                  "    " + bench_line]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"kernels_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
-    if len(sys.argv) < 3 or sys.argv[1] not in ("run", "summarize"):
+    cmds = ("run", "summarize", "trace", "summarize-trace")
+    if len(sys.argv) < 3 or sys.argv[1] not in cmds:
         raise SystemExit(__doc__)
     if sys.argv[1] == "run":
         run(sys.argv[2], sys.argv[3:])
-    else:
+    elif sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3:])
+    elif sys.argv[1] == "summarize":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4:])
+    else:
+        summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4:])

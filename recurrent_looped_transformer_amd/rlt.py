@@ -278,12 +278,13 @@ def rlt_replay_grad_workspace(cfg: synth.Config, B: int, T: int) -> int:
 
 
 def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens: torch.Tensor,
-                    dlogprob: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+                    dlogprob: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                    grads: Optional[Dict[str, torch.Tensor]] = None, logprob: Optional[torch.Tensor] = None):
     """Full-BPTT gradient of sum(dlogprob * logprob) over the replay of tokens [B, T].
 
     weights: manifest name -> contiguous fp32 device tensor. Returns (logprob [B, T-1],
-    {name: gradient tensor}). The workspace (uint8 device tensor) is allocated here unless
-    given."""
+    {name: gradient tensor}). The workspace (uint8 device tensor), the gradient tensors and
+    the log-probability buffer are allocated here unless given."""
     assert tokens.dtype == torch.int32 and tokens.dim() == 2 and dlogprob.dtype == torch.float32
     B, T = tokens.shape
     dev = tokens.device
@@ -294,17 +295,20 @@ def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens:
     names = list(weights)
     warr = (rlt_tensor * len(names))()
     garr = (rlt_grad_tensor * len(names))()
-    grads = {}
+    if grads is None:
+        grads = {n: torch.empty_like(weights[n]) for n in names}
     for i, n in enumerate(names):
-        t = weights[n]
+        t, gt = weights[n], grads[n]
         assert t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda
+        assert gt.dtype == torch.float32 and gt.is_contiguous() and gt.numel() == t.numel()
         warr[i] = rlt_tensor(n.encode(), t.data_ptr(), t.numel())
-        grads[n] = torch.empty_like(t)
-        garr[i] = rlt_grad_tensor(n.encode(), grads[n].data_ptr(), t.numel())
-    logprob = torch.empty(B, T - 1, dtype=torch.float32, device=dev)
+        garr[i] = rlt_grad_tensor(n.encode(), gt.data_ptr(), t.numel())
+    if logprob is None:
+        logprob = torch.empty(B, T - 1, dtype=torch.float32, device=dev)
+    dlp = dlogprob.contiguous()
     c = config_struct(cfg)
     _check(load().rlt_replay_grad(ctypes.byref(c), warr, len(names), garr, len(names), _ptr(tokens), B, T,
-                                  _ptr(dlogprob.contiguous()), _ptr(logprob), ctypes.c_void_p(workspace.data_ptr()),
+                                  _ptr(dlp), _ptr(logprob), ctypes.c_void_p(workspace.data_ptr()),
                                   workspace.numel(), ctypes.c_void_p(_stream())))
     return logprob, grads
 
