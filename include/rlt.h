@@ -253,6 +253,27 @@ int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float 
 int rlt_importance_ratio(const float* logprob_current, const float* logprob_behaviour, int64_t n, float* ratio,
                          hipStream_t stream);
 
+/* Rows at their own positions (continuous batching; [S] appendix F.2 generation and [S]
+ * appendix I.3 on RLT-2 generation with partial chunks, batched over rows that are at
+ * unequal positions). rlt_step_rows consumes tokens[b] (device int32 [B]) for every row with
+ * active[b] != 0 (HOST int32 [B]): encoder step, memory append and one transition at that
+ * row's own position n_b + 1, logits of the moving rows in logits[b] (device fp32 [B, V];
+ * rows that do not move get unspecified values there). Rows that do not move keep their
+ * state exactly (their token is not read). RLT-2 rows update their register when their own
+ * position closes a chunk. rlt_state_reset_rows returns the rows with rows[b] != 0 (host) to
+ * H_0 (position 0, s = rho = s*), the others untouched: a finished sequence's row takes a new
+ * sequence while the rest continue. Results per row equal an unbatched run of that row.
+ * The first per-row call needs the state's encoded positions consumed (ORDER otherwise);
+ * afterwards the batch-wide calls (encode, decode scan, step, generate, snapshot) accept the
+ * state only while every row is at the same position (ORDER otherwise); reset and restore
+ * return it to the batch-wide form. Per-row steps need keep_encoder_cache (UNSUPPORTED).
+ * Errors: CAPACITY (a moving row at max_len), STALE_STATE, INVALID_ARG. */
+int rlt_step_rows(rlt_model* m, rlt_state* s, const int32_t* tokens, const int32_t* active, float* logits,
+                  hipStream_t stream);
+int rlt_state_reset_rows(rlt_model* m, rlt_state* s, const int32_t* rows, hipStream_t stream);
+/* Positions consumed by each row (host int32 [B]). */
+int rlt_state_row_positions(const rlt_state* s, int32_t* n);
+
 /* Full back-propagation through time of the replay ([R] §6.2 eq 5.5 for what is replayed;
  * [R] appendix B eq B.4 and §6.4: the reference training computation differentiates the
  * whole sequential unroll, through s_t, through every decoder key/value including entries

@@ -13,7 +13,11 @@ enum class Dt : int { F32 = 0, BF16 = 1, F16 = 2 };
 struct RowMap {
   int64_t sb = 0, st = 0;
   int tn = 1;
-  __host__ __device__ int64_t off(int m) const { return (int64_t)(m / tn) * sb + (int64_t)(m % tn) * st; }
+  const int* pos = nullptr;   // per-sequence position offsets (device): + pos[m / tn] * pst
+  int64_t pst = 0;
+  __device__ int64_t off(int m) const {
+    return (int64_t)(m / tn) * sb + (int64_t)(m % tn) * st + (pos ? (int64_t)pos[m / tn] * pst : 0);
+  }
 };
 inline RowMap contiguous(int width) { RowMap r; r.tn = 1; r.sb = width; r.st = 0; return r; }
 
@@ -83,6 +87,10 @@ struct EpArgs {
   // pos_dev[0] * pos_stride elements.
   const int* pos_dev = nullptr;
   int64_t pos_stride = 0;
+  // Per-sequence positions (rows at different positions, device memory): sequence b = m / tn of
+  // this call has its first position index at row_pos[b] (overrides pos0 / pos_dev); the
+  // merge's e / gpre rows of sequence b move by row_pos[b] * pos_stride elements.
+  const int* row_pos = nullptr;
   // Copies of the new residual rows (Residual epilogue): dup_rows[dup_map.off(m) + n], and for
   // the last row of each sequence (m % tn == tn - 1) dup_last[(m / tn) * dup_last_ld + n].
   float* dup_rows = nullptr;
@@ -125,6 +133,10 @@ void digest64(const void* p, int64_t n_words, uint64_t* out_dev, hipStream_t st)
 void fill_zero_u32(void* p, int64_t n, hipStream_t st);
 // s[b, :] = s0 (fp32) for b < B; used for H_0 and the RLT-2 register
 void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st);
+// dst[b] <- src[b * src_ld ...] (src_ld 0: one vector for every row) where mask[b] != 0
+void masked_rows(const float* src, int64_t src_ld, float* dst, const int* mask, int B, int d, hipStream_t st);
+// out[b] = keep[b] ? 0 : tok[b]
+void active_tokens(const int32_t* tok, const int* keep, int32_t* out, int B, hipStream_t st);
 // out[om(r)] = L[tok[tm(r)]] - logsumexp(L) with L = logits row lm(r); tok < 0 writes 0
 void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows,
              int V, hipStream_t st);
@@ -173,6 +185,7 @@ struct AttnArgs {
   float scale = 1.f;
   int64_t out_split = 0;        // > 0: output lo terms at column + out_split (two-term activations)
   const int* pos_dev = nullptr; // when set, pos0 is read from pos_dev[0] (graph replay)
+  const int* row_pos = nullptr; // when set, sequence b's pos0 is row_pos[b] (rows at different positions)
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
 // 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is

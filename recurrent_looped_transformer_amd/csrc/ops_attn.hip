@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   const int h = blockIdx.x;
   const int row = blockIdx.y;
   const int b = row / a.nq, qi = row % a.nq;
-  const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + qi;
+  const int pos = (a.row_pos ? a.row_pos[b] : a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + qi;
   const int lo = a.window > 0 ? max(1, pos - a.window + 1) : 1;
   const int n = pos - lo + 1;
   const int tid = threadIdx.x, gi = tid / G, gl = tid % G;

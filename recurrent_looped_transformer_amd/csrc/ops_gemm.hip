@@ -32,6 +32,11 @@ __device__ __forceinline__ void rope_apply(float2 cs, float& x0, float& x1) {
   x1 = y1;
 }
 
+// Position index (0-based) before the first position of row m's sequence in this call.
+__device__ __forceinline__ int ep_pos0(const EpArgs& a, int m) {
+  return a.row_pos ? a.row_pos[m / a.tn] : (a.pos_dev ? a.pos_dev[0] : a.pos0);
+}
+
 // Epilogue operands a decode GEMM loads before its main loop (they do not depend on it):
 // the residual row and the next norm's gain, or the rotary factors of the lane's features.
 struct EpPre {
@@ -46,7 +51,7 @@ __device__ __forceinline__ EpPre ep_prefetch(const EpArgs& a, int m, int n) {
     if (kFold && a.fold_zb) p.g = *reinterpret_cast<const float4*>(a.fold_gain + n);
   } else if constexpr (E == Ep::RopeQ || E == Ep::QKV || E == Ep::MemKV) {
     // same position and channel as the epilogue below (rows m = b * tn + i, position pos0 + 1 + i)
-    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + (m % a.tn);
+    const int pos = ep_pos0(a, m) + 1 + (m % a.tn);
     const int c = E == Ep::RopeQ ? n % a.dh : (n % a.hd) % a.dh;
     p.cs0 = rope_cs(a, pos, c);
     p.cs1 = rope_cs(a, pos, c + 2);
@@ -102,7 +107,7 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     store_act<T>(o, a.out_split, v[0] * sigmoidf_(v[0]) * v[1]);
     store_act<T>(o + 1, a.out_split, v[2] * sigmoidf_(v[2]) * v[3]);
   } else if constexpr (E == Ep::RopeQ) {
-    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + (m % a.tn);
+    const int pos = ep_pos0(a, m) + 1 + (m % a.tn);
     const int c = n % a.dh;
     rope_apply(pre ? pre->cs0 : rope_cs(a, pos, c), v[0], v[1]);
     rope_apply(pre ? pre->cs1 : rope_cs(a, pos, c + 2), v[2], v[3]);
@@ -111,7 +116,7 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
     for (int i = 0; i < 4; ++i) Elem<T>::st(o + i, v[i]);
   } else if constexpr (E == Ep::QKV || E == Ep::MemKV) {
     const int b = m / a.tn, i = m % a.tn;
-    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + 1 + i;
+    const int pos = ep_pos0(a, m) + 1 + i;
     int region = n / a.hd;
     const int w = n - region * a.hd;
     if constexpr (E == Ep::MemKV) region += 1;   // memory projection has no query part
@@ -128,7 +133,8 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
   } else if constexpr (E == Ep::Merge) {
     // rows (2j, 2j+1) of the packed [W_g,r ; W_s] weight: gate part and state projection of feature j
     const int j = n >> 1;
-    const int64_t e0 = a.pos_dev ? (int64_t)a.pos_dev[0] * a.pos_stride : 0;
+    const int64_t e0 = a.row_pos ? (int64_t)a.row_pos[m] * a.pos_stride
+                     : a.pos_dev ? (int64_t)a.pos_dev[0] * a.pos_stride : 0;
     float u0 = 0.f, u1 = 0.f;
 #pragma unroll
     for (int rep = 0; rep < a.nrep; ++rep) {

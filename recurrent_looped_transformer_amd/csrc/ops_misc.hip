@@ -175,6 +175,33 @@ void broadcast_row(const float* s0, float* s, int B, int d, hipStream_t st) {
   hipLaunchKernelGGL(broadcast_row_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, s0, s, B, d);
 }
 
+// Rows at different positions: dst[b] <- src[b] (or the one vector src when src_ld == 0) for
+// the rows with mask[b] != 0; other rows untouched.
+__global__ void masked_rows_k(const float* __restrict__ src, int64_t src_ld, float* __restrict__ dst,
+                              const int* __restrict__ mask, int B, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)B * d) return;
+  const int b = (int)(idx / d), c = (int)(idx % d);
+  if (mask[b]) dst[idx] = src[(int64_t)b * src_ld + c];
+}
+
+void masked_rows(const float* src, int64_t src_ld, float* dst, const int* mask, int B, int d, hipStream_t st) {
+  const int64_t total = (int64_t)B * d;
+  hipLaunchKernelGGL(masked_rows_k, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, src, src_ld, dst,
+                     mask, B, d);
+}
+
+// out[b] = keep[b] ? 0 : tok[b]: the token of a row that does not move is never read as an id
+__global__ void active_tokens_k(const int32_t* __restrict__ tok, const int* __restrict__ keep,
+                                int32_t* __restrict__ out, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) out[b] = keep[b] ? 0 : tok[b];
+}
+
+void active_tokens(const int32_t* tok, const int* keep, int32_t* out, int B, hipStream_t st) {
+  hipLaunchKernelGGL(active_tokens_k, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, tok, keep, out, B);
+}
+
 // dst row (row_off + row_stride * perm(j)) <- src row j, columns [col0, col0 + cols) -> [dst_col0, ...)
 // RopeRows: within each head of dh rows, rotate-half pair (i, i + dh/2) lands on rows (2i, 2i + 1).
 template <typename T>

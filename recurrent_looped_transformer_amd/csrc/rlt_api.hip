@@ -64,6 +64,7 @@ constexpr int kReadoutPositions = 64;   // positions per batched readout
 constexpr int kMaxSlices = 4;           // concurrent batch slices of the launch-path scan
 constexpr int kParallelPositions = 64;  // RLT-0 positions per decoder pass
 constexpr int64_t kEncoderRows = 32768; // encoder workspace rows (sequences x tokens per group)
+constexpr int kStage = 8;               // pinned staging slots of the per-row position arrays
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -101,7 +102,8 @@ struct rlt_model {
 
 struct rlt_state {
   rlt_model* m = nullptr;
-  int B = 0, Tm = 0, keep_enc = 0;
+  int B = 0, Tm = 0, keep_enc = 0;   // Tm: position pitch of every per-position store (max_len + 1)
+  int cap = 0;                        // max_len: positions a sequence may hold
   int P = 1;          // max positions per decoder pass
   int R = 1;          // ring capacity (slots per layer, sequence, head)
   int n_enc = 0, n_dec = 0;
@@ -153,17 +155,30 @@ struct rlt_state {
   int* pos_dev = nullptr;                    // [0] position index of the pass, [1] readout column
   // [with readout rows][merge input folded by the previous replay]
   hipGraphExec_t pass_graph[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+  // rows at different positions (rlt_step_rows / rlt_state_reset_rows)
+  bool ragged = false;
+  std::vector<int> row_n;             // positions consumed by each row (while ragged)
+  int* rp_dev = nullptr;              // [3][B]: position index, row stays, register update
+  int32_t* rtok = nullptr;            // [B] tokens of the rows that move
+  float* s_bak = nullptr;             // [B][d] s before a per-row step
+  int* rp_host = nullptr;             // pinned [kStage][3][B] staging of rp_dev
+  hipEvent_t rp_ev[kStage] = {};
+  bool rp_used[kStage] = {};
+  int rp_next = 0;
 };
 
 namespace {
 
-void* dev_alloc(rlt_state* s, size_t bytes, int cls) {
+// `logical` (when >= 0) is the part reported under cls; the rest counts as workspace (class 5).
+void* dev_alloc(rlt_state* s, size_t bytes, int cls, int64_t logical = -1) {
   void* p = nullptr;
   if (bytes == 0) return nullptr;
   hipError_t e = hipMalloc(&p, bytes);
   if (e != hipSuccess) fail(RLT_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
   s->allocs.push_back(p);
-  s->bytes[cls] += (int64_t)bytes;
+  const int64_t rep = logical >= 0 ? logical : (int64_t)bytes;
+  s->bytes[cls] += rep;
+  s->bytes[5] += (int64_t)bytes - rep;
   return p;
 }
 
@@ -409,11 +424,14 @@ void mgemm(const rlt_model* m, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ld
 }
 
 // ------------------------------------------------------------------ encode
-void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t st) {
+// row_pos (device [B], rows at different positions): sequence b encodes position row_pos[b] + 1
+// (T = 1) instead of n_enc + 1 .. n_enc + T; the state's n_enc is then left to the caller.
+void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t st,
+               const int* row_pos = nullptr) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, Tm = s->Tm;
-  const int t0 = s->n_enc;
+  const int t0 = row_pos ? 0 : s->n_enc;
   const int Bc = (int)std::max<int64_t>(1, std::min<int64_t>(s->B, s->enc_rows / T));
   // GEMM activation rows: width w, or w hi terms then w lo terms (two-term activations)
   const int A = m->act, ad = A * d, ahd = A * hd, af = A * f;
@@ -423,6 +441,8 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
     const int rows = nb * T;
     RowMap hm;   // encoder residual stream lives in the state's e rows
     hm.tn = T; hm.sb = (int64_t)Tm * d; hm.st = d;
+    const int* rp = row_pos ? row_pos + b0 : nullptr;
+    if (rp) { hm.pos = rp; hm.pst = d; }
     float* h = s->e + ((int64_t)b0 * Tm + t0) * d;
     embed(dt, tokens + (int64_t)b0 * T, m->emb, h, hm, rows, d, st);
     for (int l = 0; l < c.L_E; ++l) {
@@ -430,8 +450,9 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       rmsnorm(dt, h, hm, L.n1, s->exa, ad, rows, d, c.rms_eps, st, sd);
       EpArgs a;
       a.out = s->eq; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0;
-      a.x_split = A > 1;
+      a.x_split = A > 1; a.row_pos = rp;
       AttnArgs at;
+      at.row_pos = rp;
       if (s->enc_k) {
         const int64_t lo = (int64_t)l * s->B * H * Tm * dh;
         a.kv.k = (char*)s->enc_k + lo * m->esz; a.kv.v = (char*)s->enc_v + lo * m->esz;
@@ -461,7 +482,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       rmsnorm(dt, h, hm, m->nE, s->exa, ad, rows, d, c.rms_eps, st, sd);
       for (int g = 0; g < c.groups; ++g) {
         EpArgs a;
-        a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0; a.b0 = b0;
+        a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0; a.b0 = b0; a.row_pos = rp;
         const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
         a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
         a.x_split = A > 1;
@@ -477,7 +498,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
     }
   }
   check_launch();
-  s->n_enc += T;
+  if (!row_pos) s->n_enc += T;
 }
 
 // ------------------------------------------------------------------ decoder pass
@@ -520,8 +541,10 @@ struct PassIO {
 };
 
 // pos_dev (graph replay, RLT-1): positions come from pos_dev[0] on the device instead of t0.
+// row_pos (device [state B], np = 1, t0 = 0): sequence b transitions at position row_pos[b] + 1;
+// the RLT-2 register is then left to the caller.
 void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, const SliceBufs& sb,
-                  const int* pos_dev = nullptr, const PassIO& io = PassIO()) {
+                  const int* pos_dev = nullptr, const PassIO& io = PassIO(), const int* row_pos = nullptr) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = sb.B, Tm = s->Tm;
@@ -529,6 +552,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
   const RowMap zm = contiguous(d);
   const int A = m->act, ad = A * d, ahd = A * hd, af = A * f;
   const int64_t sd = A > 1 ? d : 0, shd = A > 1 ? hd : 0, sf = A > 1 ? f : 0;
+  const int* rp = row_pos ? row_pos + sb.b0 : nullptr;
   // Folded RMSNorm on the 16-bit decode GEMMs: each residual GEMM also writes act(z * gain of
   // the next norm) and per-16-feature sums of squares; the next GEMM scales its rows by the
   // inverse RMS. The merge folds the first block's norm the same way (8-feature partials) when
@@ -538,6 +562,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
   const bool merge_fold = fold && c.variant != RLT_V0 && c.L_D > 0 && np == 1 && d / 8 <= 256;
   if (c.variant == RLT_V0) {
     RowMap em; em.tn = np; em.sb = (int64_t)Tm * d; em.st = d;
+    if (rp) { em.pos = rp; em.pst = d; }
     copy_rows(sb.e + (int64_t)t0 * d, em, sb.z, zm, rows, d, st);
   } else {
     // merge (eq 2.9-2.11): r = RMSNorm_s(s_{t-1} or the RLT-2 register), gate and state projection
@@ -551,6 +576,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     a.resid = sb.z; a.rmap = zm; a.e = sb.e + (int64_t)t0 * d; a.gpre = sb.gpre + (int64_t)t0 * d;
     a.eb = (int64_t)Tm * d; a.et = d; a.nrep = np; a.alpha = c.alpha; a.x_split = A > 1;
     if (pos_dev) { a.e = sb.e; a.gpre = sb.gpre; a.pos_dev = pos_dev; a.pos_stride = d; }
+    if (rp) { a.e = sb.e; a.gpre = sb.gpre; a.row_pos = rp; a.pos_stride = d; }
     if (merge_fold) {
       a.fold_zb = sb.xa; a.fold_ld = ad; a.out_split = sd; a.fold_ssp = sb.dssp; a.fold_gain = m->dec[0].n1;
     }
@@ -578,7 +604,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     if (l > 0 || !fold) norm_in(a, L.n1);
     else if (merge_fold) { a.rs_ssp = sb.dssp; a.rs_n = d / 8; a.rs_d = d; a.rs_eps = c.rms_eps; }
     a.out = sb.q; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = np; a.pos0 = t0;
-    a.x_split = A > 1; a.pos_dev = pos_dev;
+    a.x_split = A > 1; a.pos_dev = pos_dev; a.row_pos = rp;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
     mgemm(m, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
@@ -586,7 +612,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
     at.B = B; at.nq = np; at.H = H; at.dh = dh;
-    at.pos0 = t0; at.window = c.window; at.scale = scale; at.pos_dev = pos_dev;
+    at.pos0 = t0; at.window = c.window; at.scale = scale; at.pos_dev = pos_dev; at.row_pos = rp;
     attn_decode(dt, at, st);
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
@@ -595,7 +621,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     EpArgs qx;
     norm_in(qx, L.n2);
     qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0; qx.x_split = A > 1;
-    qx.pos_dev = pos_dev;
+    qx.pos_dev = pos_dev; qx.row_pos = rp;
     mgemm(m, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
@@ -629,7 +655,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     copy_rows(sb.z + (int64_t)(np - 1) * d, last, sb.s, zm, B, d, st);
     if (io.rows) copy_rows(sb.z, zm, io.rows, io.rows_map, rows, d, st);
   }
-  if (c.variant == RLT_V2 && (t0 + np) % c.chunk == 0)
+  if (c.variant == RLT_V2 && !rp && (t0 + np) % c.chunk == 0)
     HIPCHK(hipMemcpyAsync(sb.rho, sb.s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
 }
 
@@ -885,6 +911,81 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
   check_launch();
 }
 
+// ------------------------------------------------------------------ rows at their own positions
+// Batch-wide calls need every row at one position (and the state leaves the per-row mode then).
+void leave_ragged(rlt_state* s) {
+  if (!s->ragged) return;
+  for (int b = 1; b < s->B; ++b)
+    if (s->row_n[b] != s->row_n[0])
+      fail(RLT_ERR_ORDER, "rows are at different positions: use rlt_step_rows / rlt_state_reset_rows, or "
+                          "reset the state");
+  s->n_enc = s->n_dec = s->row_n[0];
+  s->ragged = false;
+}
+
+void enter_ragged(rlt_state* s) {
+  if (s->ragged) return;
+  if (s->n_dec != s->n_enc) fail(RLT_ERR_ORDER, "consume the encoded positions before per-row calls");
+  s->row_n.assign(s->B, s->n_dec);
+  s->ragged = true;
+}
+
+// Copies v (3 arrays of B ints) to rp_dev on the stream through a pinned slot; a slot is
+// rewritten only after the copy that last read it has run.
+void stage_rows(rlt_state* s, const std::vector<int>& v, hipStream_t st) {
+  const int k = s->rp_next;
+  s->rp_next = (k + 1) % kStage;
+  if (s->rp_used[k]) HIPCHK(hipEventSynchronize(s->rp_ev[k]));
+  int* h = s->rp_host + (size_t)k * 3 * s->B;
+  std::memcpy(h, v.data(), sizeof(int) * 3 * s->B);
+  HIPCHK(hipMemcpyAsync(s->rp_dev, h, sizeof(int) * 3 * s->B, hipMemcpyHostToDevice, st));
+  HIPCHK(hipEventRecord(s->rp_ev[k], st));
+  s->rp_used[k] = true;
+}
+
+// One position for every row with active[b] != 0, each at its own position row_n[b] + 1: the
+// encoder step, memory append and transition of generation F.2 (summary appendix F.2), batched
+// over rows at unequal positions. Rows that do not move run the same kernels at position
+// row_n[b] + 1 (keys, memory and encoder rows land beyond their prefix, in the slack position
+// when the row is full, or in the ring slot of a position the window has already left) and
+// get their s back afterwards, so their state is unchanged.
+void step_rows(rlt_model* m, rlt_state* s, const int32_t* tokens, const int32_t* active, float* logits,
+               hipStream_t st) {
+  const rlt_config& c = m->cfg;
+  const int B = s->B, d = c.d;
+  std::vector<int> v(3 * B, 0);
+  int moving = 0;
+  for (int b = 0; b < B; ++b) {
+    const bool a = active[b] != 0;
+    v[b] = s->row_n[b];
+    v[B + b] = a ? 0 : 1;
+    v[2 * B + b] = (a && c.variant == RLT_V2 && (s->row_n[b] + 1) % c.chunk == 0) ? 1 : 0;
+    moving += a ? 1 : 0;
+  }
+  if (!moving) return;
+  stage_rows(s, v, st);
+  const int* pos = s->rp_dev;
+  const int* keep = s->rp_dev + B;
+  const int* reg = s->rp_dev + 2 * B;
+  active_tokens(tokens, keep, s->rtok, B, st);
+  HIPCHK(hipMemcpyAsync(s->s_bak, s->s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
+  do_encode(m, s, s->rtok, 1, st, pos);
+  const SliceBufs sb = slice_bufs(m, s, 0, B);
+  PassIO io;
+  io.rows = s->sbuf;
+  io.rows_map.tn = 1; io.rows_map.sb = (int64_t)kReadoutPositions * d; io.rows_map.st = d;
+  decoder_pass(m, s, 0, 1, st, sb, nullptr, io, pos);
+  ScanOut o;
+  o.logits = logits; o.ld_b = 1;
+  readout(m, s, 0, 1, o, st, 0, B);
+  if (c.variant == RLT_V2) masked_rows(s->s, d, s->rho, reg, B, d, st);
+  masked_rows(s->s_bak, d, s->s, keep, B, d, st);
+  check_launch();
+  s->block_steps += c.L_D;
+  for (int b = 0; b < B; ++b)
+    if (active[b]) s->row_n[b] += 1;
+}
+
 // ------------------------------------------------------------------ snapshots
 // Payload of a prefix snapshot, in this order (B sequences, n_enc encoded and n_dec consumed
 // positions; every part contiguous):
@@ -1030,27 +1131,31 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
     try {
       s->m = m;
       s->B = batch;
-      s->Tm = max_len;
+      s->Tm = max_len + 1;   // one slack position per sequence: a per-row step of a row that does not
+                             // move writes its discarded keys, memory and encoder rows there when the
+                             // row is full
+      s->cap = max_len;
       s->keep_enc = keep_encoder_cache ? 1 : 0;
       s->P = c.variant == RLT_V2 ? c.chunk : (c.variant == RLT_V0 ? std::min(kParallelPositions, max_len) : 1);
       s->R = c.window + s->P - 1;
-      const int64_t B = batch, Tm = max_len, d = c.d, hd = m->hd, f = c.ffn, V = c.vocab, H = c.n_heads,
+      const int64_t B = batch, Tm = s->Tm, d = c.d, hd = m->hd, f = c.ffn, V = c.vocab, H = c.n_heads,
                     dh = c.d_head;
       const size_t e = m->esz;
       if (s->keep_enc) {
-        s->enc_k = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0);
-        s->enc_v = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0);
+        s->enc_k = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0, (int64_t)c.L_E * B * H * max_len * dh * e);
+        s->enc_v = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0, (int64_t)c.L_E * B * H * max_len * dh * e);
       }
       if (c.L_D > 0) {
-        s->mem_k = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1);
-        s->mem_v = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1);
+        s->mem_k = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1, (int64_t)c.groups * B * H * max_len * dh * e);
+        s->mem_v = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1, (int64_t)c.groups * B * H * max_len * dh * e);
         s->ring_k = dev_alloc(s, (size_t)c.L_D * B * H * s->R * dh * e, 2);
         s->ring_v = dev_alloc(s, (size_t)c.L_D * B * H * s->R * dh * e, 2);
       }
       s->s = (float*)dev_alloc(s, sizeof(float) * B * d, 3);
       s->rho = (float*)dev_alloc(s, sizeof(float) * B * d, 3);
-      s->e = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4);
-      if (c.variant != RLT_V0) s->gpre = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4);
+      s->e = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4, (int64_t)sizeof(float) * B * max_len * d);
+      if (c.variant != RLT_V0)
+        s->gpre = (float*)dev_alloc(s, sizeof(float) * B * Tm * d, 4, (int64_t)sizeof(float) * B * max_len * d);
       s->rope = (float2*)dev_alloc(s, sizeof(float2) * (Tm + 1) * (dh / 2), 5);
       const int64_t rows = B * s->P;
       s->z = (float*)dev_alloc(s, sizeof(float) * rows * d, 5);
@@ -1081,6 +1186,11 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->gtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
       s->pos_dev = (int*)dev_alloc(s, 256, 5);
       s->lp = (float*)dev_alloc(s, sizeof(float) * B * Tm, 5);
+      s->rp_dev = (int*)dev_alloc(s, sizeof(int) * 3 * B, 5);
+      s->rtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
+      s->s_bak = (float*)dev_alloc(s, sizeof(float) * B * d, 5);
+      HIPCHK(hipHostMalloc((void**)&s->rp_host, sizeof(int) * kStage * 3 * B, hipHostMallocDefault));
+      for (int k = 0; k < kStage; ++k) HIPCHK(hipEventCreateWithFlags(&s->rp_ev[k], hipEventDisableTiming));
       if (m->dt == Dt::BF16 && scan_supported((int)dh, (int)rows, (int)d, (int)hd, (int)f, (int)Tm, c.L_D)) {
         s->scan_ok = true;
         for (int i = 0; i < 2; ++i) {
@@ -1121,7 +1231,7 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
         HIPCHK(hipEventCreateWithFlags(&s->ev_join[k], hipEventDisableTiming));
       }
       HIPCHK(hipEventCreateWithFlags(&s->ev_fork, hipEventDisableTiming));
-      rope_table(s->rope, max_len + 1, (int)dh, c.rope_base, stream);
+      rope_table(s->rope, (int)Tm + 1, (int)dh, c.rope_base, stream);
       check_launch();
       m->n_states += 1;
       *out = s;
@@ -1136,6 +1246,9 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       }
       if (s->ev_fork) (void)hipEventDestroy(s->ev_fork);
       if (s->abort_host) (void)hipHostFree(s->abort_host);
+      if (s->rp_host) (void)hipHostFree(s->rp_host);
+      for (int k = 0; k < kStage; ++k)
+        if (s->rp_ev[k]) (void)hipEventDestroy(s->rp_ev[k]);
       delete s;
       throw;
     }
@@ -1157,6 +1270,7 @@ int rlt_state_reset(rlt_model* m, rlt_state* s, hipStream_t stream) {
     s->n_dec = 0;
     s->block_steps = 0;
     s->version = m->version;
+    s->ragged = false;
   });
 }
 
@@ -1173,6 +1287,9 @@ int rlt_state_destroy(rlt_state* s) {
       if (s->ev_join[k]) HIPCHK(hipEventDestroy(s->ev_join[k]));
     }
     if (s->ev_fork) HIPCHK(hipEventDestroy(s->ev_fork));
+    if (s->rp_host) HIPCHK(hipHostFree(s->rp_host));
+    for (int k = 0; k < kStage; ++k)
+      if (s->rp_ev[k]) HIPCHK(hipEventDestroy(s->rp_ev[k]));
     s->m->n_states -= 1;
     delete s;
   });
@@ -1188,8 +1305,58 @@ int rlt_state_bytes(const rlt_state* s, int64_t out[6]) {
 int rlt_state_positions(const rlt_state* s, int* n_encoded, int* n_decoded) {
   return guarded([&] {
     if (!s) fail(RLT_ERR_INVALID_ARG, "null state");
-    if (n_encoded) *n_encoded = s->n_enc;
-    if (n_decoded) *n_decoded = s->n_dec;
+    int ne = s->n_enc, nd = s->n_dec;
+    if (s->ragged) {
+      for (int b = 1; b < s->B; ++b)
+        if (s->row_n[b] != s->row_n[0]) fail(RLT_ERR_ORDER, "rows are at different positions (rlt_state_row_positions)");
+      ne = nd = s->row_n[0];
+    }
+    if (n_encoded) *n_encoded = ne;
+    if (n_decoded) *n_decoded = nd;
+  });
+}
+
+int rlt_state_row_positions(const rlt_state* s, int32_t* n) {
+  return guarded([&] {
+    if (!s || !n) fail(RLT_ERR_INVALID_ARG, "null pointer");
+    for (int b = 0; b < s->B; ++b) n[b] = s->ragged ? s->row_n[b] : s->n_dec;
+  });
+}
+
+int rlt_step_rows(rlt_model* m, rlt_state* s, const int32_t* tokens, const int32_t* active, float* logits,
+                  hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!tokens || !active || !logits) fail(RLT_ERR_INVALID_ARG, "tokens, active and logits required");
+    if (!s->enc_k) fail(RLT_ERR_UNSUPPORTED, "per-row steps need keep_encoder_cache");
+    enter_ragged(s);
+    for (int b = 0; b < s->B; ++b)
+      if (active[b] && s->row_n[b] + 1 > s->cap) fail(RLT_ERR_CAPACITY, "a moving row would exceed max_len");
+    step_rows(m, s, tokens, active, logits, stream);
+  });
+}
+
+int rlt_state_reset_rows(rlt_model* m, rlt_state* s, const int32_t* rows, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    if (!rows) fail(RLT_ERR_INVALID_ARG, "rows required");
+    enter_ragged(s);
+    const int B = s->B, d = m->cfg.d;
+    std::vector<int> v(3 * B, 0);
+    int any = 0;
+    for (int b = 0; b < B; ++b) {
+      v[B + b] = rows[b] ? 1 : 0;
+      any += v[B + b];
+    }
+    if (!any) return;
+    stage_rows(s, v, stream);
+    if (m->cfg.variant != RLT_V0) {
+      masked_rows(m->s0, 0, s->s, s->rp_dev + B, B, d, stream);
+      masked_rows(m->s0, 0, s->rho, s->rp_dev + B, B, d, stream);
+    }
+    check_launch();
+    for (int b = 0; b < B; ++b)
+      if (rows[b]) s->row_n[b] = 0;
   });
 }
 
@@ -1218,8 +1385,9 @@ int rlt_set_scan_mode(rlt_model* m, int mode) {
 int rlt_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t stream) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (!tokens || T < 1) fail(RLT_ERR_INVALID_ARG, "tokens and T >= 1 required");
-    if ((int64_t)s->n_enc + T > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if ((int64_t)s->n_enc + T > s->cap) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
     if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "continuing an encode needs keep_encoder_cache");
     do_encode(m, s, tokens, T, stream);
   });
@@ -1229,6 +1397,7 @@ int rlt_decode_scan(rlt_model* m, rlt_state* s, int T, float* logits, float* nex
                     const int32_t* next_tokens, float* s_out, hipStream_t stream) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (T < 1) fail(RLT_ERR_INVALID_ARG, "T >= 1 required");
     if (next_logprob && !next_tokens) fail(RLT_ERR_INVALID_ARG, "next_logprob needs next_tokens");
     if ((int64_t)s->n_dec + T > s->n_enc) fail(RLT_ERR_ORDER, "decoder would pass the encoded positions");
@@ -1242,8 +1411,9 @@ int rlt_decode_scan(rlt_model* m, rlt_state* s, int T, float* logits, float* nex
 int rlt_step(rlt_model* m, rlt_state* s, const int32_t* tokens, float* logits, hipStream_t stream) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (!tokens || !logits) fail(RLT_ERR_INVALID_ARG, "tokens and logits required");
-    if (s->n_enc + 1 > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if (s->n_enc + 1 > s->cap) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
     if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "generation needs keep_encoder_cache");
     if (s->n_dec != s->n_enc) fail(RLT_ERR_ORDER, "consume the encoded positions before stepping");
     do_encode(m, s, tokens, 1, stream);
@@ -1258,7 +1428,7 @@ int rlt_replay(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, float* 
   return guarded([&] {
     if (!m || !s || s->m != m) fail(RLT_ERR_INVALID_ARG, "null or foreign state");
     if (!tokens || T < 1) fail(RLT_ERR_INVALID_ARG, "tokens and T >= 1 required");
-    if (T > s->Tm) fail(RLT_ERR_CAPACITY, "T exceeds the state's max_len");
+    if (T > s->cap) fail(RLT_ERR_CAPACITY, "T exceeds the state's max_len");
     if (rlt_state_reset(m, s, stream) != RLT_OK) fail(RLT_ERR_HIP, g_err);
     do_encode(m, s, tokens, T, stream);
     ScanOut o;
@@ -1275,6 +1445,7 @@ int rlt_replay(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, float* 
 int rlt_snapshot_size(rlt_model* m, rlt_state* s, int64_t* bytes) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (!bytes) fail(RLT_ERR_INVALID_ARG, "null output");
     *bytes = snapshot_payload(snapshot_parts(m, s, s->n_enc, s->n_dec, s->keep_enc != 0));
   });
@@ -1284,6 +1455,7 @@ int rlt_snapshot(rlt_model* m, rlt_state* s, void* dst, int64_t capacity, rlt_sn
                  hipStream_t stream) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (!dst || !info) fail(RLT_ERR_INVALID_ARG, "dst and info required");
     const auto parts = snapshot_parts(m, s, s->n_enc, s->n_dec, s->keep_enc != 0);
     const int64_t need = snapshot_payload(parts);
@@ -1318,7 +1490,7 @@ int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const
       fail(RLT_ERR_INVALID_ARG, "snapshot ring layout differs from the state's");
     if (info->has_encoder_cache != s->keep_enc)
       fail(RLT_ERR_INVALID_ARG, "snapshot and state differ in keeping the encoder cache");
-    if (info->n_encoded > s->Tm) fail(RLT_ERR_CAPACITY, "snapshot positions exceed the state's max_len");
+    if (info->n_encoded > s->cap) fail(RLT_ERR_CAPACITY, "snapshot positions exceed the state's max_len");
     if (info->n_decoded < 0 || info->n_decoded > info->n_encoded) fail(RLT_ERR_INVALID_ARG, "bad snapshot positions");
     const auto parts = snapshot_parts(m, s, info->n_encoded, info->n_decoded, s->keep_enc != 0);
     if (snapshot_payload(parts) != info->bytes) fail(RLT_ERR_INVALID_ARG, "snapshot size does not match its layout");
@@ -1326,6 +1498,7 @@ int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const
     check_launch();
     s->n_enc = info->n_encoded;
     s->n_dec = info->n_decoded;
+    s->ragged = false;
     s->block_steps = info->block_steps;
     s->version = m->version;
   });
@@ -1347,11 +1520,12 @@ int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float 
                  uint64_t step0, int32_t* tokens, float* logprob, float* logits, hipStream_t stream) {
   return guarded([&] {
     check_state(m, s);
+    leave_ragged(s);
     if (!first || !tokens || !logprob) fail(RLT_ERR_INVALID_ARG, "first, tokens and logprob required");
     if (n < 1) fail(RLT_ERR_INVALID_ARG, "n >= 1 required");
     if (!(temperature >= 0.f) || !std::isfinite(temperature))
       fail(RLT_ERR_INVALID_ARG, "temperature must be finite and >= 0");
-    if (s->n_enc + n > s->Tm) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
+    if (s->n_enc + n > s->cap) fail(RLT_ERR_CAPACITY, "positions would exceed max_len");
     if (s->n_enc > 0 && !s->enc_k) fail(RLT_ERR_UNSUPPORTED, "generation needs keep_encoder_cache");
     if (s->n_dec != s->n_enc) fail(RLT_ERR_ORDER, "consume the encoded positions before generating");
     const int V = m->cfg.vocab;

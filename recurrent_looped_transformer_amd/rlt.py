@@ -28,7 +28,7 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
            "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant", "rlt_replay_grad_workspace",
-           "rlt_replay_grad"]
+           "rlt_replay_grad", "rlt_step_rows", "rlt_state_reset_rows", "rlt_state_row_positions"]
 
 
 class RltError(RuntimeError):
@@ -96,6 +96,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_snapshot": [vp, vp, vp, ctypes.c_int64, ctypes.POINTER(rlt_snapshot_info), vp],
         "rlt_restore": [vp, vp, ctypes.POINTER(rlt_snapshot_info), vp, vp],
         "rlt_replay_grad_workspace": [ctypes.POINTER(rlt_config), i32, i32, i64p],
+        "rlt_step_rows": [vp, vp, vp, ctypes.POINTER(ctypes.c_int32), vp, vp],
+        "rlt_state_reset_rows": [vp, vp, ctypes.POINTER(ctypes.c_int32), vp],
+        "rlt_state_row_positions": [vp, ctypes.POINTER(ctypes.c_int32)],
         "rlt_replay_grad": [ctypes.POINTER(rlt_config), ctypes.POINTER(rlt_tensor), i32,
                             ctypes.POINTER(rlt_grad_tensor), i32, vp, i32, i32, vp, vp, vp, ctypes.c_int64, vp],
     }
@@ -268,6 +271,28 @@ def rlt_restore(model, state, info: rlt_snapshot_info, src: torch.Tensor) -> Non
     assert src.dtype == torch.uint8 and src.is_contiguous() and src.numel() >= info.bytes
     _check(load().rlt_restore(model, state, ctypes.byref(info), ctypes.c_void_p(src.data_ptr()),
                               ctypes.c_void_p(_stream())))
+
+
+def _host_i32(vals) -> ctypes.Array:
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def rlt_step_rows(model, state, tokens: torch.Tensor, active, logits: torch.Tensor) -> None:
+    """One position for the rows with active[b] (host sequence of B flags), each at its own position."""
+    assert tokens.dtype == torch.int32 and tokens.dim() == 1 and logits.dtype == torch.float32
+    _check(load().rlt_step_rows(model, state, _ptr(tokens), _host_i32(active), _ptr(logits),
+                                ctypes.c_void_p(_stream())))
+
+
+def rlt_state_reset_rows(model, state, rows) -> None:
+    _check(load().rlt_state_reset_rows(model, state, _host_i32(rows), ctypes.c_void_p(_stream())))
+
+
+def rlt_state_row_positions(state, batch: int) -> list:
+    out = (ctypes.c_int32 * batch)()
+    _check(load().rlt_state_row_positions(state, out))
+    return list(out)
 
 
 def rlt_replay_grad_workspace(cfg: synth.Config, B: int, T: int) -> int:
