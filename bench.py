@@ -202,6 +202,139 @@ def grad_bench(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+RAGGED_METRIC = "continuous-batching generation tokens/sec (every row at its own position); % of HBM roofline"
+
+
+def gen_step_bytes(cfg, positions) -> float:
+    """Algorithmic HBM bytes of one generation step of rows at the given positions (1-based
+    position of the token each row consumes): encoder, memory, merge and decoder weights once
+    per step (e * P_dec as in scan_bytes, plus the encoder's e * P_enc), and per row the
+    encoder-cache reads (L_E * t keys and values), the window and memory-prefix reads of
+    every decoder layer, the cache / memory / ring writes and the state and logits I/O."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    d, f, V, LE, LD, W, hd = cfg.d, cfg.ffn, cfg.vocab, cfg.L_E, cfg.L_D, cfg.window, cfg.hd
+    G = cfg.groups if LD > 0 else 0
+    P_enc = LE * (4 * d * hd + 3 * d * f + 2 * d) + G * 2 * d * hd + (d if LD > 0 else 0) \
+        + (d * d if cfg.variant != 0 else 0)
+    P_dec = LD * (4 * d * hd + 2 * d * hd + 3 * d * f + 3 * d) + 3 * d * d + 3 * d + V * d + d
+    total = float(e * (P_enc + P_dec))
+    for t in positions:
+        total += LE * t * 2 * hd * e + LD * (min(t, W) - 1) * 2 * hd * e + LD * t * 2 * hd * e
+        total += (LE + LD + G) * 2 * hd * e + 3 * d * 4 + V * 4
+    return total
+
+
+def ragged_bench(args, cfg):
+    """Rows at unequal positions: prefill every row to `base`, move row b alone for
+    b * spread / (B - 1) more positions (rows spread linearly over base..base+spread), then
+    time steps in which every row consumes one token at its own position. The same batch
+    stepping at one common position (the mean) is timed beside it."""
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import make_params, make_tokens
+    B = cfg.batch
+    base = args.ragged_base or cfg.seq_len // 2
+    spread = args.ragged_spread
+    K, Wm = args.steps, args.warmup
+    max_len = base + spread + Wm + K + 1
+    P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+    torch.cuda.set_device(0)
+    model = rlt.Model(cfg, P)
+    del P
+    toks = make_tokens(cfg, batch=B, length=max_len)
+    x = torch.as_tensor(np.ascontiguousarray(toks)).cuda()
+    rows = torch.arange(B, device="cuda")
+    stream = torch.cuda.current_stream()
+    lg = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+
+    st = model.state(B, max_len, keep_encoder_cache=True)
+    rlt.rlt_encode(model.h, st, x[:, :base].contiguous())
+    rlt.rlt_decode_scan(model.h, st, base)
+    pos = np.full(B, base, np.int64)
+    target = base + (np.arange(B) * spread) // max(1, B - 1)
+    for c in range(spread):
+        act = (pos < target).astype(np.int32)
+        tk = x[rows, torch.as_tensor(np.minimum(pos, max_len - 1)).cuda()].contiguous()
+        rlt.rlt_step_rows(model.h, st, tk, act, lg)
+        pos += act
+        if (c + 1) % 128 == 0 or c + 1 == spread:
+            torch.cuda.synchronize()
+            print(f"[bench] rows spread: {c + 1}/{spread} calls", flush=True)
+    ones = np.ones(B, np.int32)
+
+    def timed(fn):
+        for _ in range(Wm):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(K):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / K
+
+    pos_start = pos.copy()
+
+    def ragged_step():
+        tk = x[rows, torch.as_tensor(pos).cuda()].contiguous()
+        rlt.rlt_step_rows(model.h, st, tk, ones, lg)
+        pos[:] += 1
+
+    ms_r = timed(ragged_step)
+    by = np.mean([gen_step_bytes(cfg, pos_start + Wm + k + 1) for k in range(K)])
+    print("[bench] ragged steps timed", flush=True)
+    rlt.rlt_state_destroy(st)
+    model.states.remove(st)
+
+    mean_p = int(round(float(np.mean(pos_start))))
+    su = model.state(B, max_len, keep_encoder_cache=True)
+    rlt.rlt_encode(model.h, su, x[:, :mean_p].contiguous())
+    rlt.rlt_decode_scan(model.h, su, mean_p)
+    col = [mean_p]
+
+    def uniform_step():
+        rlt.rlt_step(model.h, su, x[:, col[0]].contiguous(), lg)
+        col[0] += 1
+
+    ms_u = timed(uniform_step)
+    by_u = np.mean([gen_step_bytes(cfg, [mean_p + Wm + k + 1] * B) for k in range(K)])
+    model.close()
+    ach = by / (ms_r / 1e3) / 1e9
+    out = {
+        "metric": RAGGED_METRIC, "value": B / (ms_r / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": ms_r, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16", "fp16x2": "f16x2"}[cfg.path_dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} generation, B={B} rows at positions {int(pos_start.min())}.."
+                               f"{int(pos_start.max())} (linear spread), every row consuming one token per step",
+                   "batch": B, "positions_min": int(pos_start.min()), "positions_max": int(pos_start.max()),
+                   "d": cfg.d, "L_E": cfg.L_E, "L_D": cfg.L_D, "window": cfg.window, "vocab": cfg.vocab},
+        "uniform_same_mean": {"position": mean_p, "ms_per_step": ms_u, "tokens_s": B / (ms_u / 1e3),
+                              "hbm_GBs": by_u / (ms_u / 1e3) / 1e9},
+        "roofline": {"bound": "hbm", "kernel": "generation step (encoder step + transition + logits)",
+                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": by},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+        from oracle import Oracle
+        from recurrent_looped_transformer_amd.synth import make_params as mp
+        n = min(256, max_len)
+        o = Oracle(cfg, mp(cfg, bf16_storage=cfg.d >= 4096), np.float32)
+        ost = o.new_state(1)
+        t1 = time.perf_counter()
+        for i in range(n):
+            o.consume(ost, toks[:1, i])
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"1 row x {n} generation steps from BOS (positions 1-{n}; the "
+                                         f"oracle's per-position cost is dominated by streaming the weights), "
+                                         f"float32 numpy, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, P, tokens, sample_B: int):
     from threadpoolctl import threadpool_info
     from oracle import Oracle
@@ -239,6 +372,10 @@ def main():
                          "t = 32 and the prompt length of each shape; prints one JSON line per point")
     ap.add_argument("--sweep-shapes", default="algo_bf16,medium_lm,paper_shared")
     ap.add_argument("--sweep-batches", default="1,2,4,8")
+    ap.add_argument("--ragged", action="store_true",
+                    help="time generation steps of rows at unequal positions (continuous batching)")
+    ap.add_argument("--ragged-base", type=int, default=0)
+    ap.add_argument("--ragged-spread", type=int, default=512)
     ap.add_argument("--grad", action="store_true",
                     help="time the full-BPTT gradient of the replay (fp32 arithmetic) instead of the replay")
     args = ap.parse_args()
@@ -275,6 +412,9 @@ def main():
         cfg = cfg.replace(variant=args.variant, chunk=cfg.chunk if args.variant == 2 else 1)
     if args.grad:
         grad_bench(args, cfg)
+        return
+    if args.ragged:
+        ragged_bench(args, cfg)
         return
     B, T = cfg.batch, cfg.seq_len
     P = make_params(cfg)
