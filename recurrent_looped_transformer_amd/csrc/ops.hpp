@@ -168,6 +168,10 @@ __host__ __device__ inline int64_t tile_major_off(int64_t n, int64_t k, int64_t 
   return (n >> 4) * 16 * K + (k >> 6) * 1024 + ((kk >> 3) & 1) * 512 + ((kk >> 4) * 16 + (n & 15)) * 8 + (kk & 7);
 }
 
+// Blocks of a key-split decode attention launch at most; a split workspace holds
+// kAttnSplitBlocks * (dh + 2) floats.
+constexpr int kAttnSplitBlocks = 2048;
+
 // Attention of nq query rows per (sequence, head) over a position range of a key/value store.
 struct AttnArgs {
   const void* q = nullptr;      // act [B*nq][H*dh] (roped, pairs interleaved like the keys)
@@ -186,6 +190,13 @@ struct AttnArgs {
   int64_t out_split = 0;        // > 0: output lo terms at column + out_split (two-term activations)
   const int* pos_dev = nullptr; // when set, pos0 is read from pos_dev[0] (graph replay)
   const int* row_pos = nullptr; // when set, sequence b's pos0 is row_pos[b] (rows at different positions)
+  // Key splits (load balance of few long key ranges; attn_decode only): split_ws holds
+  // kAttnSplitBlocks * (dh + 2) floats, n_max bounds every query's key count (0: unknown, no
+  // split), split_max caps the pieces per range. split_keys is set by the launcher.
+  float* split_ws = nullptr;
+  int split_max = 0;
+  int n_max = 0;
+  int split_keys = 0;
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
 // 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is

@@ -12,6 +12,8 @@
 // computes (two register sets); the groups are combined through LDS at the end.
 // Keys and values are each read once.
 #include "common.hpp"
+#include <algorithm>
+
 #include "ops.hpp"
 
 namespace rlt {
@@ -31,6 +33,9 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   const int lo = a.window > 0 ? max(1, pos - a.window + 1) : 1;
   const int n = pos - lo + 1;
   const int tid = threadIdx.x, gi = tid / G, gl = tid % G;
+  // split over keys (gridDim.z > 1): this block takes keys [jb, je) of the n
+  const int jb = gridDim.z > 1 ? (int)blockIdx.z * a.split_keys : 0;
+  const int je = gridDim.z > 1 ? min(n, jb + a.split_keys) : n;
 
   // the query's raw bits now, unpacked after the first keys are requested (no wait in between)
   const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)row * a.ldq + h * DH + gl * VEC;
@@ -48,26 +53,26 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
 #define RLT_ATTN_LOAD(K_, V_, J0_)                                              \
   _Pragma("unroll") for (int u = 0; u < UNR; ++u) {                             \
     const int j = (J0_) + u * NG;                                               \
-    if (j < n) {                                                                \
+    if (j < je) {                                                               \
       const int p = lo + j;                                                     \
       const int slot = a.ring ? (p - 1) % a.cap : p - 1;                        \
       K_[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);         \
       V_[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);         \
     }                                                                           \
   }
-  RLT_ATTN_LOAD(kk, vv, gi)
+  RLT_ATTN_LOAD(kk, vv, jb + gi)
   float qv[VEC];
   unpack16<T>(qraw, qv);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) qv[e] *= a.scale;
-  for (int j0 = gi; j0 < n; j0 += STEP) {
-    if (j0 + STEP < n) RLT_ATTN_LOAD(kn, vn, j0 + STEP)
+  for (int j0 = jb + gi; j0 < je; j0 += STEP) {
+    if (j0 + STEP < je) RLT_ATTN_LOAD(kn, vn, j0 + STEP)
     float sc[UNR];
     float mx = m_run;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       float dot = -INFINITY;
-      if (j0 + u * NG < n) {
+      if (j0 + u * NG < je) {
         float kf[VEC];
         unpack16<T>(kk[u], kf);
         dot = 0.f;
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     for (int e = 0; e < VEC; ++e) acc[e] *= corr;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      if (j0 + u * NG < n) {
+      if (j0 + u * NG < je) {
         const float pw = __expf(sc[u] - mx);
         l_run += pw;
         float vf[VEC];
@@ -112,19 +117,73 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     float M = -INFINITY;
     for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, ml[2 * gg]);
     float s = 0.f, den = 0.f;
-    for (int gg = 0; gg < NG; ++gg) {
-      const float w = __expf(ml[2 * gg] - M);
-      den += w * ml[2 * gg + 1];
-      s += w * part[gg * DH + tid];
+    if (M != -INFINITY) {   // a split block past its row's last key has no keys
+      for (int gg = 0; gg < NG; ++gg) {
+        const float w = __expf(ml[2 * gg] - M);
+        den += w * ml[2 * gg + 1];
+        s += w * part[gg * DH + tid];
+      }
+    }
+    if (gridDim.z > 1) {
+      float* w = a.split_ws + (((int64_t)row * a.H + h) * gridDim.z + blockIdx.z) * (DH + 2);
+      w[tid] = s;
+      if (tid == 0) {
+        w[DH] = M;
+        w[DH + 1] = den;
+      }
+      return;
     }
     T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
     store_act<T>(op, a.out_split, s / den);
   }
 }
 
+// Combines the key splits of attn_decode_k in ascending split order: out = sum_z e^(M_z - M)
+// s_z / sum_z e^(M_z - M) den_z (empty splits carry M_z = -inf and weigh nothing).
 template <typename T, int DH>
-static void launch_attn(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
+__global__ __launch_bounds__(DH) void attn_combine_k(AttnArgs a, int S) {
+  const int h = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const float* w = a.split_ws + ((int64_t)row * a.H + h) * S * (DH + 2);
+  float M = -INFINITY;
+  for (int z = 0; z < S; ++z) M = fmaxf(M, w[z * (DH + 2) + DH]);
+  float num = 0.f, den = 0.f;
+  for (int z = 0; z < S; ++z) {
+    const float mz = w[z * (DH + 2) + DH];
+    if (mz == -INFINITY) continue;
+    const float e = __expf(mz - M);
+    num += e * w[z * (DH + 2) + tid];
+    den += e * w[z * (DH + 2) + DH + 1];
+  }
+  T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
+  store_act<T>(op, a.out_split, num / den);
+}
+
+// Key splits: when the launch has at most kSplitMaxBlocks (head, query) blocks and its longest
+// key range is long, every range is cut into pieces of split_keys keys (the same for every row,
+// so a long prefix gets more blocks than a short one), one round of at most 256 blocks in
+// all; the pieces are combined by attn_combine_k. Measured on the medium-LM decode (16
+// heads, dh 128, t 2048): 8 rows split 16 ways ran 6.7 us slower per launch than unsplit (the
+// extra launch and per-block overheads outweigh the occupancy), so only launches of one or
+// two rows split.
+constexpr int kSplitMinKeys = 1024, kSplitMaxBlocks = 32, kSplitPiece = 256, kSplitRound = 256;
+static_assert(kSplitRound <= kAttnSplitBlocks, "split workspace");
+template <typename T, int DH>
+static void launch_attn(const AttnArgs& a0, hipStream_t st) {
+  AttnArgs a = a0;
+  const int blocks = a.H * a.B * a.nq;
+  int S = 1;
+  if (a.split_ws && a.n_max >= kSplitMinKeys && blocks <= kSplitMaxBlocks) {
+    S = std::min({(a.n_max + kSplitPiece - 1) / kSplitPiece, kSplitRound / blocks, a.split_max});
+    S = std::max(S, 1);
+    a.split_keys = (a.n_max + S - 1) / S;
+    S = (a.n_max + a.split_keys - 1) / a.split_keys;
+  }
+  if (S > 1) {
+    hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq, S), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
+  } else {
+    hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
+  }
 }
 
 template <typename T>

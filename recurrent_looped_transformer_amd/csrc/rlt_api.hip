@@ -161,6 +161,7 @@ struct rlt_state {
   int* rp_dev = nullptr;              // [3][B]: position index, row stays, register update
   int32_t* rtok = nullptr;            // [B] tokens of the rows that move
   float* s_bak = nullptr;             // [B][d] s before a per-row step
+  float* attn_ws = nullptr;           // [kMaxSlices][kAttnSplitBlocks][dh + 2] key-split partials
   int* rp_host = nullptr;             // pinned [kStage][3][B] staging of rp_dev
   hipEvent_t rp_ev[kStage] = {};
   bool rp_used[kStage] = {};
@@ -417,6 +418,15 @@ void check_state(rlt_model* m, rlt_state* s) {
 
 // GEMM of this model: the row-invariant dispatch when the model asks for batch-invariant
 // arithmetic.
+// Key-split workspace of a slice for attention launches whose key counts are at most n_max
+// (none in batch-invariant mode: the split depends on the batch).
+void attn_split(const rlt_model* m, const rlt_state* s, AttnArgs& at, int slice, int n_max) {
+  if (m->batch_invariant || n_max <= 0) return;
+  at.split_ws = s->attn_ws + (int64_t)slice * kAttnSplitBlocks * (m->cfg.d_head + 2);
+  at.split_max = 64;
+  at.n_max = n_max;
+}
+
 void mgemm(const rlt_model* m, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
            int K, hipStream_t st) {
   a.row_invariant = m->batch_invariant;
@@ -427,7 +437,7 @@ void mgemm(const rlt_model* m, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ld
 // row_pos (device [B], rows at different positions): sequence b encodes position row_pos[b] + 1
 // (T = 1) instead of n_enc + 1 .. n_enc + T; the state's n_enc is then left to the caller.
 void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStream_t st,
-               const int* row_pos = nullptr) {
+               const int* row_pos = nullptr, int pos_max = 0) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, Tm = s->Tm;
@@ -469,6 +479,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
+      attn_split(m, s, at, 0, row_pos ? pos_max : t0 + T);
       if (!(T >= 16 && !m->batch_invariant && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
       EpArgs r; r.resid = h; r.rmap = hm; r.x_split = A > 1;
       mgemm(m, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
@@ -506,6 +517,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
 // Sequences b0 .. b0+nb-1 of the state (a batch slice): the pointers of its rows.
 struct SliceBufs {
   int b0 = 0, B = 0;
+  int slice = 0;   // index of the concurrent slice (its own key-split workspace)
   float *z, *s, *rho, *e, *gpre, *dssp, *sssp;
   void *xa, *xs, *q, *ao, *hid, *ring_k, *ring_v, *mem_k, *mem_v;
 };
@@ -543,8 +555,10 @@ struct PassIO {
 // pos_dev (graph replay, RLT-1): positions come from pos_dev[0] on the device instead of t0.
 // row_pos (device [state B], np = 1, t0 = 0): sequence b transitions at position row_pos[b] + 1;
 // the RLT-2 register is then left to the caller.
+// pos_max (row_pos only): the largest position any row of the pass reaches.
 void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, const SliceBufs& sb,
-                  const int* pos_dev = nullptr, const PassIO& io = PassIO(), const int* row_pos = nullptr) {
+                  const int* pos_dev = nullptr, const PassIO& io = PassIO(), const int* row_pos = nullptr,
+                  int pos_max = 0) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, hd = m->hd, f = c.ffn, H = c.n_heads, dh = c.d_head, B = sb.B, Tm = s->Tm;
@@ -613,6 +627,8 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
     at.B = B; at.nq = np; at.H = H; at.dh = dh;
     at.pos0 = t0; at.window = c.window; at.scale = scale; at.pos_dev = pos_dev; at.row_pos = rp;
+    const int pmax = pos_dev ? 0 : (rp ? pos_max : t0 + np);
+    attn_split(m, s, at, sb.slice, std::min(pmax, c.window));
     attn_decode(dt, at, st);
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
@@ -627,6 +643,8 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
     at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
     at.cap = Tm; at.ring = 0; at.window = 0;
+    at.split_ws = nullptr;
+    attn_split(m, s, at, sb.slice, pmax);
     attn_decode(dt, at, st);
     EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
@@ -865,6 +883,7 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
   for (int k = 0; k < ns; ++k) {
     const int b0 = (int)((int64_t)s->B * k / ns), b1 = (int)((int64_t)s->B * (k + 1) / ns);
     sl[k] = slice_bufs(m, s, b0, b1 - b0);
+    sl[k].slice = k;
     if (ns > 1) ss[k] = s->sub[k];
   }
   if (ns > 1) {
@@ -969,12 +988,13 @@ void step_rows(rlt_model* m, rlt_state* s, const int32_t* tokens, const int32_t*
   const int* reg = s->rp_dev + 2 * B;
   active_tokens(tokens, keep, s->rtok, B, st);
   HIPCHK(hipMemcpyAsync(s->s_bak, s->s, sizeof(float) * B * d, hipMemcpyDeviceToDevice, st));
-  do_encode(m, s, s->rtok, 1, st, pos);
+  const int pmax = *std::max_element(s->row_n.begin(), s->row_n.end()) + 1;
+  do_encode(m, s, s->rtok, 1, st, pos, pmax);
   const SliceBufs sb = slice_bufs(m, s, 0, B);
   PassIO io;
   io.rows = s->sbuf;
   io.rows_map.tn = 1; io.rows_map.sb = (int64_t)kReadoutPositions * d; io.rows_map.st = d;
-  decoder_pass(m, s, 0, 1, st, sb, nullptr, io, pos);
+  decoder_pass(m, s, 0, 1, st, sb, nullptr, io, pos, pmax);
   ScanOut o;
   o.logits = logits; o.ld_b = 1;
   readout(m, s, 0, 1, o, st, 0, B);
@@ -1189,6 +1209,7 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->rp_dev = (int*)dev_alloc(s, sizeof(int) * 3 * B, 5);
       s->rtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
       s->s_bak = (float*)dev_alloc(s, sizeof(float) * B * d, 5);
+      s->attn_ws = (float*)dev_alloc(s, sizeof(float) * kMaxSlices * kAttnSplitBlocks * (dh + 2), 5);
       HIPCHK(hipHostMalloc((void**)&s->rp_host, sizeof(int) * kStage * 3 * B, hipHostMallocDefault));
       for (int k = 0; k < kStage; ++k) HIPCHK(hipEventCreateWithFlags(&s->rp_ev[k], hipEventDisableTiming));
       if (m->dt == Dt::BF16 && scan_supported((int)dh, (int)rows, (int)d, (int)hd, (int)f, (int)Tm, c.L_D)) {

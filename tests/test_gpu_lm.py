@@ -170,3 +170,36 @@ def test_lm_generation_steps_full_size(lm, replay):
     assert d <= TOL_GPU_GPU
     assert agree >= 0.999
     assert lp_d <= TOL_GPU_GPU
+
+
+def test_lm_single_row_long_context(lm):
+    """Row 0 alone (B = 1: 16 attention blocks per launch, so every memory or window range of
+    512 keys or more is cut into 128-key pieces whose partial softmax sums are combined
+    afterwards): replay of positions 1-2052 against the oracle, and prefill 2048 + 4 rlt_step
+    (the encoder-cache attention of the steps is split too) against the oracle at 2045-2052."""
+    m, tokens, _, ggen = lm
+    T = 2052
+    print("[case] medium_lm B=1 T=2052 (key-split attention)", flush=True)
+    x = torch.as_tensor(np.ascontiguousarray(tokens[:1, :T])).cuda()
+    st = m.state(1, T, keep_encoder_cache=True)
+    nxt = torch.full((1, T), -1, dtype=torch.int32, device="cuda")
+    nxt[:, :-1] = x[:, 1:]
+    lg = torch.empty((1, T, CFG.vocab), dtype=torch.float32, device="cuda")
+    lp = torch.empty((1, T), dtype=torch.float32, device="cuda")
+    s = torch.empty((1, T, CFG.d), dtype=torch.float32, device="cuda")
+    rlt.rlt_encode(m.h, st, x)
+    rlt.rlt_decode_scan(m.h, st, T, logits=lg, next_logprob=lp, next_tokens=nxt, s_out=s)
+    torch.cuda.synchronize()
+    compare_rows("medium_lm B=1 replay positions 1-2052", lg, lp[:, :T - 1], s[:, T - 1], ggen)
+    del lg, s
+    p = 2048
+    st2 = m.state(1, T, keep_encoder_cache=True)
+    pre = torch.empty((1, p, CFG.vocab), dtype=torch.float32, device="cuda")
+    rlt.rlt_encode(m.h, st2, x[:, :p].contiguous())
+    rlt.rlt_decode_scan(m.h, st2, p, logits=pre)
+    steps = [m.step(st2, x[:, i].contiguous()) for i in range(p, T)]
+    tail = torch.cat([pre[:, p - 4:], torch.stack(steps, dim=1)], dim=1).cpu().numpy()
+    err = float(np.max(np.abs(tail - ggen["logits_tail"])))
+    print(f"[parity] medium_lm B=1 positions 2045-2052 (prefill + rlt_step) vs oracle, every id: {err:.3e}",
+          flush=True)
+    assert err <= TOL

@@ -201,3 +201,51 @@ def test_order_capacity_and_reset():
         m.step(st, tok)
     finally:
         m.close()
+
+
+def test_long_rows_split_attention():
+    """Tiny fp32, 2 rows prefilled to 1030 positions, then 150 per-row calls (rows end up ~90
+    positions apart): 8 attention blocks per launch, so memory ranges of 1024 keys or more are
+    cut into pieces; every row's logits against the oracle (prefill of the same prefix, then
+    one consume per token). Also a single-row replay of 1200 positions against the oracle."""
+    cfg = TINY
+    P = make_params(cfg)
+    B, L, p0 = 2, 1200, 1030
+    rng = np.random.default_rng(23)
+    prefix = rng.integers(0, cfg.vocab - 1, size=(B, p0)).astype(np.int32)
+    prefix[:, 0] = cfg.bos
+    m = rlt.Model(cfg, P)
+    hist = [[] for _ in range(B)]
+    try:
+        st = m.state(B, L, keep_encoder_cache=True)
+        rlt.rlt_encode(m.h, st, dev(prefix))
+        rlt.rlt_decode_scan(m.h, st, p0)
+        lg = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+        for _ in range(150):
+            act = (rng.random(B) < np.array([0.9, 0.3])).astype(np.int32)
+            toks = rng.integers(0, cfg.vocab - 1, size=B).astype(np.int32)
+            rlt.rlt_step_rows(m.h, st, dev(toks), act, lg)
+            g = lg.cpu().numpy()
+            for b in np.nonzero(act)[0]:
+                hist[b].append((int(toks[b]), g[b].copy()))
+        x1 = rng.integers(0, cfg.vocab - 1, size=(1, L)).astype(np.int32)
+        x1[:, 0] = cfg.bos
+        st1 = m.state(1, L, keep_encoder_cache=False)
+        lp1, _ = m.replay(st1, dev(x1))
+        lp1 = lp1.cpu().numpy()
+    finally:
+        m.close()
+    o = Oracle(cfg, P)
+    worst = 0.0
+    for b in range(B):
+        ost = o.new_state(1)
+        o.prefill(ost, prefix[b:b + 1].astype(np.int64))
+        for tok, g in hist[b]:
+            ref, _ = o.consume(ost, np.array([tok], dtype=np.int64))
+            worst = max(worst, float(np.max(np.abs(g - ref[0]))))
+    ref_lp, _, _ = o.replay(x1.astype(np.int64))
+    lp_err = float(np.max(np.abs(lp1 - ref_lp)))
+    print(f"[ragged] long rows (positions {p0}..{p0 + max(len(h) for h in hist)}): max abs logit err "
+          f"{worst:.2e}; replay of {L} positions log-prob err {lp_err:.2e}", flush=True)
+    assert worst <= 1e-4
+    assert lp_err <= 1e-4
