@@ -150,12 +150,13 @@ def grad_bench(args, cfg):
     x = torch.as_tensor(tokens).to(dev)
     wt = torch.as_tensor(w).to(dev)
     lp = torch.empty((B, T - 1), dtype=torch.float32, device=dev)
-    ws = torch.empty(rlt.rlt_replay_grad_workspace(cfg, B, T), dtype=torch.uint8, device=dev)
+    ck = bool(args.checkpoint)
+    ws = torch.empty(rlt.rlt_replay_grad_workspace(cfg, B, T, ck), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        rlt.rlt_replay_grad(cfg, W, x, wt, workspace=ws, grads=G, logprob=lp)
+        rlt.rlt_replay_grad(cfg, W, x, wt, workspace=ws, grads=G, logprob=lp, checkpoint=ck)
         if ev: ev[1].record(stream)
 
     for i in range(args.warmup):
@@ -178,10 +179,11 @@ def grad_bench(args, cfg):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name} shape, full-BPTT gradient of the replay loss "
-                               f"(fp32 arithmetic), RLT-{cfg.variant} B={B} T={T}",
+                               f"(fp32 arithmetic{', activation checkpointing' if ck else ''}), "
+                               f"RLT-{cfg.variant} B={B} T={T}",
                    "batch": B, "seq_len": T, "d": cfg.d, "L_E": cfg.L_E, "L_D": cfg.L_D, "window": cfg.window,
                    "groups": cfg.groups, "vocab": cfg.vocab, "variant": f"RLT-{cfg.variant}",
-                   "workspace_bytes": ws.numel()},
+                   "workspace_bytes": ws.numel(), "checkpoint": ck},
         "gradient_pass_ms": pass_ms,
         "roofline": {"bound": "alu", "kernel": "gradient pass (saved forward + reverse scan + weight gradients)",
                      "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -376,6 +378,8 @@ def main():
                     help="time generation steps of rows at unequal positions (continuous batching)")
     ap.add_argument("--ragged-base", type=int, default=0)
     ap.add_argument("--ragged-spread", type=int, default=512)
+    ap.add_argument("--checkpoint", action="store_true",
+                    help="with --grad: activation checkpointing (recompute block intermediates per position)")
     ap.add_argument("--grad", action="store_true",
                     help="time the full-BPTT gradient of the replay (fp32 arithmetic) instead of the replay")
     args = ap.parse_args()

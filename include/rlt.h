@@ -284,9 +284,13 @@ int rlt_state_row_positions(const rlt_state* s, int32_t* n);
  * importance-weighted policy objective, a likelihood) enters through its derivative with
  * respect to them, dlogprob (fp32 [B, T-1]).
  * Arithmetic is fp32 throughout (the log-sum-exp of the readout in float64) whatever
- * cfg->dtype: the weights are used as given. Every intermediate of the unroll is kept in
- * `workspace` (device memory the caller owns, at least rlt_replay_grad_workspace bytes,
- * 256-byte aligned); nothing is recomputed and nothing is allocated.
+ * cfg->dtype: the weights are used as given. The unroll's intermediates live in `workspace`
+ * (device memory the caller owns, at least rlt_replay_grad_workspace bytes for the same
+ * checkpoint flag, 256-byte aligned); nothing is allocated. checkpoint = 0 keeps every
+ * intermediate; checkpoint != 0 (activation checkpointing) keeps each block's input, the
+ * decoder keys/values and the memory, and recomputes a position's block intermediates (an
+ * encoder layer's, token-parallel) just before its backward: about a quarter of the
+ * workspace for one more forward pass; weight gradients then accumulate position by position.
  * weights: the manifest tensors (device fp32, as for rlt_create). grads: one writable
  * device fp32 tensor per manifest name with the same size (zeroed, then filled).
  * tokens: device int32 [B, T], x_1 = BOS. Asynchronous on `stream`.
@@ -299,11 +303,11 @@ typedef struct {
   int64_t numel;
 } rlt_grad_tensor;
 
-int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int64_t* bytes);
+int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int checkpoint, int64_t* bytes);
 
 int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, rlt_grad_tensor* grads,
                     int n_grads, const int32_t* tokens, int B, int T, const float* dlogprob, float* logprob,
-                    void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                    int checkpoint, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Scan driver for the decoder transitions: 0 = automatic (mode 1),
  * 1 = one launch sequence per position (stream-ordered), 2 = persistent cooperative kernel

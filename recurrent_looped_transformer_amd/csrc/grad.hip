@@ -537,6 +537,7 @@ inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 constexpr int kMaxSplits = 16;
 void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, const float* Bm, int64_t ldb, bool bk,
           float* C, int64_t ldc, const float* R, bool atomic) {
+  // atomic: C += A.B; otherwise C = R + A.B
   if (M <= 0 || N <= 0) return;
   const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT;
   int splits = 1;
@@ -544,6 +545,10 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   if (atomic) {
     const int want = std::max(1, 1024 / (tm * tn));
     splits = std::max(1, std::min(want, (K + 255) / 256));
+    if (splits == 1) {   // one slice: a plain read-add-write is exact and deterministic
+      atomic = false;
+      R = C;
+    }
   } else if (tm * tn < 128 && K >= 128 && c.part) {
     splits = std::min({kMaxSplits, (256 + tm * tn - 1) / (tm * tn), K / 64});
     while (splits > 1 && (int64_t)splits * M * N > c.part_cap) --splits;
@@ -674,17 +679,22 @@ struct Arena {
 struct EncBuf {  // one encoder layer, M = T*B rows
   float *a, *rs1, *q, *k, *v, *o, *lse, *mid, *c, *rs2, *f1, *f3, *g;
 };
-struct DecBuf {  // one decoder layer, M rows; forward then backward
+// One decoder layer. zin, k, v and the key / value gradients hold every position (M rows);
+// the others hold every position too, or, with checkpointing, the B rows of the position
+// being differentiated (recomputed from zin just before its backward).
+struct DecBuf {
   float *zin, *a, *rs1, *q, *k, *v, *o, *lse1, *z1, *b, *rs2, *qx, *ox, *lse2, *z2, *c, *rs3, *f1, *f3, *g;
   float *gq, *gk, *gv, *gz1, *gqx, *gz2, *gz3, *gda, *gdb, *gdc, *gf1, *gf3;
 };
 struct Bufs {
-  std::vector<float*> eh;  // L_E + 1 residual streams
-  std::vector<EncBuf> enc;
+  bool ck = false;
+  std::vector<float*> eh;   // L_E + 1 residual streams
+  std::vector<EncBuf> enc;  // every layer, or one (checkpointing: each layer recomputed from eh)
   float *en, *ens;
   std::vector<float*> mk, mv, gmk, gmv;
   std::vector<DecBuf> dec;
-  float *msrc, *mr, *mrs, *gate, *sr, *ggp, *gsr, *gmr;
+  float* msrc;                                   // merge source rows (every position)
+  float *mr, *mrs, *gate, *sr, *ggp, *gsr, *gmr;  // every position, or one (checkpointing)
   float *S, *nS, *nrs, *logits, *glog, *gS, *ge, *tMd;
   float *tBd, *tBf, *tBhd, *gu, *carry, *greg;
   // encoder backward
@@ -693,11 +703,13 @@ struct Bufs {
   int64_t part_n;  // its floats
 };
 
-void plan(const rlt_config& c, int B, int T, Arena& A, Bufs& u) {
+void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
   const int64_t M = (int64_t)B * T, d = c.d, hd = (int64_t)c.n_heads * c.d_head, f = c.ffn, H = c.n_heads;
+  const int64_t Ms = ck ? B : M;   // rows of a per-position buffer
+  u.ck = ck;
   u.eh.resize(c.L_E + 1);
   for (auto& p : u.eh) p = A.f(M * d);
-  u.enc.resize(c.L_E);
+  u.enc.resize(ck ? 1 : c.L_E);
   for (auto& e : u.enc) {
     e.a = A.f(M * d); e.rs1 = A.f(M); e.q = A.f(M * hd); e.k = A.f(M * hd); e.v = A.f(M * hd);
     e.o = A.f(M * hd); e.lse = A.f(M * H); e.mid = A.f(M * d); e.c = A.f(M * d); e.rs2 = A.f(M);
@@ -711,18 +723,20 @@ void plan(const rlt_config& c, int B, int T, Arena& A, Bufs& u) {
   }
   u.dec.resize(c.L_D);
   for (auto& D : u.dec) {
-    D.zin = A.f(M * d); D.a = A.f(M * d); D.rs1 = A.f(M); D.q = A.f(M * hd); D.k = A.f(M * hd); D.v = A.f(M * hd);
-    D.o = A.f(M * hd); D.lse1 = A.f(M * H); D.z1 = A.f(M * d); D.b = A.f(M * d); D.rs2 = A.f(M);
-    D.qx = A.f(M * hd); D.ox = A.f(M * hd); D.lse2 = A.f(M * H); D.z2 = A.f(M * d); D.c = A.f(M * d);
-    D.rs3 = A.f(M); D.f1 = A.f(M * f); D.f3 = A.f(M * f); D.g = A.f(M * f);
-    D.gq = A.f(M * hd); D.gk = A.f(M * hd); D.gv = A.f(M * hd); D.gz1 = A.f(M * d); D.gqx = A.f(M * hd);
-    D.gz2 = A.f(M * d); D.gz3 = A.f(M * d); D.gda = A.f(M * d); D.gdb = A.f(M * d); D.gdc = A.f(M * d);
-    D.gf1 = A.f(M * f); D.gf3 = A.f(M * f);
+    D.zin = A.f(M * d); D.k = A.f(M * hd); D.v = A.f(M * hd); D.gk = A.f(M * hd); D.gv = A.f(M * hd);
+    D.a = A.f(Ms * d); D.rs1 = A.f(Ms); D.q = A.f(Ms * hd);
+    D.o = A.f(Ms * hd); D.lse1 = A.f(Ms * H); D.z1 = A.f(Ms * d); D.b = A.f(Ms * d); D.rs2 = A.f(Ms);
+    D.qx = A.f(Ms * hd); D.ox = A.f(Ms * hd); D.lse2 = A.f(Ms * H); D.z2 = A.f(Ms * d); D.c = A.f(Ms * d);
+    D.rs3 = A.f(Ms); D.f1 = A.f(Ms * f); D.f3 = A.f(Ms * f); D.g = A.f(Ms * f);
+    D.gq = A.f(Ms * hd); D.gz1 = A.f(Ms * d); D.gqx = A.f(Ms * hd);
+    D.gz2 = A.f(Ms * d); D.gz3 = A.f(Ms * d); D.gda = A.f(Ms * d); D.gdb = A.f(Ms * d); D.gdc = A.f(Ms * d);
+    D.gf1 = A.f(Ms * f); D.gf3 = A.f(Ms * f);
   }
   const bool mg = c.variant != RLT_V0;
-  const int64_t Mm = mg ? M : 0;
-  u.msrc = A.f(Mm * d); u.mr = A.f(Mm * d); u.mrs = A.f(Mm); u.gate = A.f(Mm * d); u.sr = A.f(Mm * d);
-  u.ggp = A.f(Mm * d); u.gsr = A.f(Mm * d); u.gmr = A.f(Mm * d);
+  const int64_t Mm = mg ? M : 0, Mms = mg ? Ms : 0;
+  u.msrc = A.f(Mm * d);
+  u.mr = A.f(Mms * d); u.mrs = A.f(Mms); u.gate = A.f(Mms * d); u.sr = A.f(Mms * d);
+  u.ggp = A.f(Mms * d); u.gsr = A.f(Mms * d); u.gmr = A.f(Mms * d);
   u.S = A.f(M * d); u.nS = A.f(M * d); u.nrs = A.f(M); u.logits = A.f(M * c.vocab); u.glog = A.f(M * c.vocab);
   u.gS = A.f(M * d); u.ge = A.f(M * d); u.tMd = A.f(M * d);
   u.tBd = A.f((int64_t)B * d); u.tBf = A.f((int64_t)B * f); u.tBhd = A.f((int64_t)B * hd);
@@ -733,25 +747,32 @@ void plan(const rlt_config& c, int B, int T, Arena& A, Bufs& u) {
   u.part = A.f(u.part_n);
 }
 
+// Pointers of position t (B rows) of decoder layer l.
+struct Step {
+  float *zin, *a, *rs1, *q, *k, *v, *o, *lse1, *z1, *b, *rs2, *qx, *ox, *lse2, *z2, *c, *rs3, *f1, *f3, *g;
+  float *gq, *gk, *gv, *gz1, *gqx, *gz2, *gz3, *gda, *gdb, *gdc, *gf1, *gf3;
+};
+
 }  // namespace
 
-size_t grad_workspace_bytes(const rlt_config& c, int B, int T) {
+size_t grad_workspace_bytes(const rlt_config& c, int B, int T, bool checkpoint) {
   Arena A;
   Bufs u;
-  plan(c, B, T, A, u);
+  plan(c, B, T, checkpoint, A, u);
   return A.off;
 }
 
 hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const float*>& Wm,
                        const std::map<std::string, std::pair<float*, int64_t>>& Gm, const int32_t* tokens, int B, int T,
-                       const float* dlogprob, float* logprob, void* workspace, hipStream_t stream) {
+                       const float* dlogprob, float* logprob, void* workspace, bool checkpoint, hipStream_t stream) {
   Ctx c{stream};
   Arena A;
   A.base = static_cast<char*>(workspace);
   Bufs u;
-  plan(cf, B, T, A, u);
+  plan(cf, B, T, checkpoint, A, u);
   c.part = u.part;
   c.part_cap = u.part_n;
+  const bool ck = checkpoint;
   const int M = B * T, d = cf.d, H = cf.n_heads, dh = cf.d_head, hd = H * dh, f = cf.ffn, V = cf.vocab;
   const double base = cf.rope_base;
   const float eps = cf.rms_eps, alpha = cf.alpha;
@@ -770,14 +791,26 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   for (auto& kv : Gm) fill(c, kv.second.first, kv.second.second, 0.f);
   if (T <= 0 || B <= 0) return c.err;
 
+  // position t's rows: R0 in every-position buffers, Rs in per-position ones
+  auto step = [&](int l, int t) {
+    const DecBuf& D = u.dec[l];
+    const int64_t R0 = (int64_t)t * B, Rs = ck ? 0 : R0;
+    Step s;
+    s.zin = D.zin + R0 * d; s.k = D.k + R0 * hd; s.v = D.v + R0 * hd; s.gk = D.gk + R0 * hd; s.gv = D.gv + R0 * hd;
+    s.a = D.a + Rs * d; s.rs1 = D.rs1 + Rs; s.q = D.q + Rs * hd; s.o = D.o + Rs * hd; s.lse1 = D.lse1 + Rs * H;
+    s.z1 = D.z1 + Rs * d; s.b = D.b + Rs * d; s.rs2 = D.rs2 + Rs; s.qx = D.qx + Rs * hd; s.ox = D.ox + Rs * hd;
+    s.lse2 = D.lse2 + Rs * H; s.z2 = D.z2 + Rs * d; s.c = D.c + Rs * d; s.rs3 = D.rs3 + Rs;
+    s.f1 = D.f1 + Rs * f; s.f3 = D.f3 + Rs * f; s.g = D.g + Rs * f;
+    s.gq = D.gq + Rs * hd; s.gz1 = D.gz1 + Rs * d; s.gqx = D.gqx + Rs * hd; s.gz2 = D.gz2 + Rs * d;
+    s.gz3 = D.gz3 + Rs * d; s.gda = D.gda + Rs * d; s.gdb = D.gdb + Rs * d; s.gdc = D.gdc + Rs * d;
+    s.gf1 = D.gf1 + Rs * f; s.gf3 = D.gf3 + Rs * f;
+    return s;
+  };
+  auto mrow = [&](float* p, int t, int64_t width) { return p + (ck ? 0 : (int64_t)t * B * width); };
+
   // ------------------------------------------------------------ forward: encoder
-  {
-    const int64_t n = (int64_t)M * d;
-    g_embed<<<blocks(n), 256, 0, c.st>>>(B, T, d, tokens, w("emb"), u.eh[0]);
-    c.check();
-  }
-  for (int l = 0; l < cf.L_E; ++l) {
-    EncBuf& e = u.enc[l];
+  auto enc_fwd = [&](int l) {
+    EncBuf& e = u.enc[ck ? 0 : l];
     rms_fwd(c, M, d, u.eh[l], w(E(l, "n1")), eps, e.a, e.rs1);
     lin(c, M, e.a, d, w(E(l, "wq")), d, hd, e.q, nullptr);
     lin(c, M, e.a, d, w(E(l, "wk")), d, hd, e.k, nullptr);
@@ -792,7 +825,13 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     g_swiglu_fwd<<<blocks((int64_t)M * f), 256, 0, c.st>>>((int64_t)M * f, e.f1, e.f3, e.g);
     c.check();
     lin(c, M, e.g, f, w(E(l, "w2")), f, d, u.eh[l + 1], e.mid);
+  };
+  {
+    const int64_t n = (int64_t)M * d;
+    g_embed<<<blocks(n), 256, 0, c.st>>>(B, T, d, tokens, w("emb"), u.eh[0]);
+    c.check();
   }
+  for (int l = 0; l < cf.L_E; ++l) enc_fwd(l);
   const float* e_all = u.eh[cf.L_E];
   // ------------------------------------------------------------- forward: memory
   if (cf.L_D > 0) {
@@ -805,11 +844,51 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   }
   // --------------------------------------------------------- forward: transitions
   const int64_t Bd = (int64_t)B * d;
-  int rho_t = -1;  // RLT-2: position whose state the register holds (-1: s*)
-  for (int t = 0; t < T; ++t) {
+  // merge at position t from the source rows already in msrc; writes u (the first block's
+  // input, or s_t when there are no blocks)
+  auto merge_fwd = [&](int t) {
     const int64_t R0 = (int64_t)t * B;
     const float* et = e_all + R0 * d;
     float* uu = cf.L_D > 0 ? u.dec[0].zin + R0 * d : u.S + R0 * d;
+    float* r = mrow(u.mr, t, d);
+    rms_fwd(c, B, d, u.msrc + R0 * d, w("merge.ns"), eps, r, mrow(u.mrs, t, 1));
+    lin(c, B, et, d, w("merge.wg"), 2 * d, d, u.tBd, nullptr);
+    lin(c, B, r, d, w("merge.wg") + d, 2 * d, d, u.tBd, u.tBd);
+    lin(c, B, r, d, w("merge.ws"), d, d, mrow(u.sr, t, d), nullptr);
+    g_merge_fwd<<<blocks(Bd), 256, 0, c.st>>>(B, d, et, u.tBd, w("merge.bg"), mrow(u.sr, t, d), alpha,
+                                               mrow(u.gate, t, d), uu);
+    c.check();
+  };
+  // block l at position t up to its FFN hidden state (the block output is the caller's);
+  // with_kv: also this position's key and value rows
+  auto layer_fwd = [&](int l, int t, bool with_kv) {
+    const DecBuf& D = u.dec[l];
+    const Step s = step(l, t);
+    rms_fwd(c, B, d, s.zin, w(Dn(l, "m1")), eps, s.a, s.rs1);
+    lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr);
+    rope(c, B, H, dh, s.q, t + 1, B, base, 1.f);
+    if (with_kv) {
+      lin(c, B, s.a, d, w(Ds(l, "wk")), d, hd, s.k, nullptr);
+      lin(c, B, s.a, d, w(Ds(l, "wv")), d, hd, s.v, nullptr);
+      rope(c, B, H, dh, s.k, t + 1, B, base, 1.f);
+    }
+    attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1);
+    lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin);
+    rms_fwd(c, B, d, s.z1, w(Dn(l, "m2")), eps, s.b, s.rs2);
+    lin(c, B, s.b, d, w(Dn(l, "xq")), d, hd, s.qx, nullptr);
+    rope(c, B, H, dh, s.qx, t + 1, B, base, 1.f);
+    attn_fwd(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[grp(l)], u.mv[grp(l)], s.ox, s.lse2);
+    lin(c, B, s.ox, hd, w(Dn(l, "xo")), hd, d, s.z2, s.z1);
+    rms_fwd(c, B, d, s.z2, w(Dn(l, "m3")), eps, s.c, s.rs3);
+    lin(c, B, s.c, d, w(Ds(l, "w1")), d, f, s.f1, nullptr);
+    lin(c, B, s.c, d, w(Ds(l, "w3")), d, f, s.f3, nullptr);
+    g_swiglu_fwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, s.f1, s.f3, s.g);
+    c.check();
+    return s;
+  };
+  int rho_t = -1;  // RLT-2: position whose state the register holds (-1: s*)
+  for (int t = 0; t < T; ++t) {
+    const int64_t R0 = (int64_t)t * B;
     if (mg) {
       float* src = u.msrc + R0 * d;
       const int st = cf.variant == RLT_V1 ? t - 1 : rho_t;
@@ -819,41 +898,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       } else {
         add(c, Bd, u.S + (int64_t)st * B * d, nullptr, src);
       }
-      float* r = u.mr + R0 * d;
-      rms_fwd(c, B, d, src, w("merge.ns"), eps, r, u.mrs + R0);
-      lin(c, B, et, d, w("merge.wg"), 2 * d, d, u.tBd, nullptr);
-      lin(c, B, r, d, w("merge.wg") + d, 2 * d, d, u.tBd, u.tBd);
-      lin(c, B, r, d, w("merge.ws"), d, d, u.sr + R0 * d, nullptr);
-      g_merge_fwd<<<blocks(Bd), 256, 0, c.st>>>(B, d, et, u.tBd, w("merge.bg"), u.sr + R0 * d, alpha,
-                                                 u.gate + R0 * d, uu);
-      c.check();
+      merge_fwd(t);
     } else {
-      add(c, Bd, et, nullptr, uu);
+      add(c, Bd, e_all + R0 * d, nullptr, cf.L_D > 0 ? u.dec[0].zin + R0 * d : u.S + R0 * d);
     }
     for (int l = 0; l < cf.L_D; ++l) {
-      DecBuf& D = u.dec[l];
-      const int64_t o = R0 * d, oh = R0 * hd;
-      rms_fwd(c, B, d, D.zin + o, w(Dn(l, "m1")), eps, D.a + o, D.rs1 + R0);
-      lin(c, B, D.a + o, d, w(Ds(l, "wq")), d, hd, D.q + oh, nullptr);
-      lin(c, B, D.a + o, d, w(Ds(l, "wk")), d, hd, D.k + oh, nullptr);
-      lin(c, B, D.a + o, d, w(Ds(l, "wv")), d, hd, D.v + oh, nullptr);
-      rope(c, B, H, dh, D.q + oh, t + 1, B, base, 1.f);
-      rope(c, B, H, dh, D.k + oh, t + 1, B, base, 1.f);
-      attn_fwd(c, B, B, t, cf.window, H, dh, D.q + oh, D.k, D.v, D.o + oh, D.lse1 + R0 * H);
-      lin(c, B, D.o + oh, hd, w(Ds(l, "wo")), hd, d, D.z1 + o, D.zin + o);
-      rms_fwd(c, B, d, D.z1 + o, w(Dn(l, "m2")), eps, D.b + o, D.rs2 + R0);
-      lin(c, B, D.b + o, d, w(Dn(l, "xq")), d, hd, D.qx + oh, nullptr);
-      rope(c, B, H, dh, D.qx + oh, t + 1, B, base, 1.f);
-      attn_fwd(c, B, B, t, NOWIN, H, dh, D.qx + oh, u.mk[grp(l)], u.mv[grp(l)], D.ox + oh, D.lse2 + R0 * H);
-      lin(c, B, D.ox + oh, hd, w(Dn(l, "xo")), hd, d, D.z2 + o, D.z1 + o);
-      rms_fwd(c, B, d, D.z2 + o, w(Dn(l, "m3")), eps, D.c + o, D.rs3 + R0);
-      const int64_t of = R0 * f;
-      lin(c, B, D.c + o, d, w(Ds(l, "w1")), d, f, D.f1 + of, nullptr);
-      lin(c, B, D.c + o, d, w(Ds(l, "w3")), d, f, D.f3 + of, nullptr);
-      g_swiglu_fwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, D.f1 + of, D.f3 + of, D.g + of);
-      c.check();
-      float* out = (l + 1 < cf.L_D ? u.dec[l + 1].zin : u.S) + o;
-      lin(c, B, D.g + of, f, w(Ds(l, "w2")), f, d, out, D.z2 + o);
+      const Step s = layer_fwd(l, t, true);
+      float* out = (l + 1 < cf.L_D ? u.dec[l + 1].zin : u.S) + R0 * d;
+      lin(c, B, s.g, f, w(Ds(l, "w2")), f, d, out, s.z2);
     }
     if (v2 && (t + 1) % cf.chunk == 0) rho_t = t;
   }
@@ -868,6 +920,32 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   colsum(c, M, d, u.tMd, u.S, u.nrs, g("out.nO"));
   rms_bwd(c, M, d, u.tMd, u.S, u.nrs, w("out.nO"), nullptr, u.gS);
   // ------------------------------------------------ backward: transitions, reversed
+  // weight and gain gradients of block l over `rows` rows starting at s (every position at
+  // once, or one position with checkpointing)
+  auto layer_wgrad = [&](int l, const Step& s, int rows) {
+    wgrad(c, rows, s.gq, hd, s.a, d, g(Ds(l, "wq")), d);
+    wgrad(c, rows, s.gk, hd, s.a, d, g(Ds(l, "wk")), d);
+    wgrad(c, rows, s.gv, hd, s.a, d, g(Ds(l, "wv")), d);
+    wgrad(c, rows, s.gz1, d, s.o, hd, g(Ds(l, "wo")), hd);
+    wgrad(c, rows, s.gqx, hd, s.b, d, g(Dn(l, "xq")), d);
+    wgrad(c, rows, s.gz2, d, s.ox, hd, g(Dn(l, "xo")), hd);
+    wgrad(c, rows, s.gf1, f, s.c, d, g(Ds(l, "w1")), d);
+    wgrad(c, rows, s.gf3, f, s.c, d, g(Ds(l, "w3")), d);
+    wgrad(c, rows, s.gz3, d, s.g, f, g(Ds(l, "w2")), f);
+    colsum(c, rows, d, s.gda, s.zin, s.rs1, g(Dn(l, "m1")));
+    colsum(c, rows, d, s.gdb, s.z1, s.rs2, g(Dn(l, "m2")));
+    colsum(c, rows, d, s.gdc, s.z2, s.rs3, g(Dn(l, "m3")));
+  };
+  auto merge_wgrad = [&](int t, int rows) {   // t: first position of the rows
+    const int64_t R0 = (int64_t)t * B;
+    float* ggp = mrow(u.ggp, t, d);
+    float* mr = mrow(u.mr, t, d);
+    wgrad(c, rows, ggp, d, e_all + R0 * d, d, g("merge.wg"), 2 * d);
+    wgrad(c, rows, ggp, d, mr, d, g("merge.wg") + d, 2 * d);
+    colsum(c, rows, d, ggp, nullptr, nullptr, g("merge.bg"));
+    wgrad(c, rows, mrow(u.gsr, t, d), d, mr, d, g("merge.ws"), d);
+    colsum(c, rows, d, mrow(u.gmr, t, d), u.msrc + R0 * d, mrow(u.mrs, t, 1), g("merge.ns"));
+  };
   fill(c, u.carry, Bd, 0.f);
   fill(c, u.greg, Bd, 0.f);
   for (auto& D : u.dec) {
@@ -879,8 +957,12 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     fill(c, u.gmv[gi], (int64_t)M * hd, 0.f);
   }
   for (int t = T - 1; t >= 0; --t) {
-    const int64_t R0 = (int64_t)t * B, o = R0 * d, oh = R0 * hd, of = R0 * f;
-    float* gzo = cf.L_D > 0 ? u.dec[cf.L_D - 1].gz3 + o : u.gu;
+    const int64_t R0 = (int64_t)t * B, o = R0 * d;
+    if (ck) {   // recompute this position's intermediates from the kept block inputs
+      if (mg) merge_fwd(t);
+      for (int l = 0; l < cf.L_D; ++l) layer_fwd(l, t, false);
+    }
+    float* gzo = cf.L_D > 0 ? step(cf.L_D - 1, t).gz3 : u.gu;
     add(c, Bd, u.gS + o, cf.variant == RLT_V1 ? u.carry : nullptr, gzo);
     if (v2 && (t + 1) % cf.chunk == 0) {
       add(c, Bd, gzo, u.greg, gzo);
@@ -888,75 +970,58 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     }
     for (int l = cf.L_D - 1; l >= 0; --l) {
       DecBuf& D = u.dec[l];
-      const float* gz3 = D.gz3 + o;
+      const Step s = step(l, t);
       // FFN
-      lin_t(c, B, gz3, d, w(Ds(l, "w2")), f, f, u.tBf, nullptr);
-      g_swiglu_bwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, u.tBf, D.f1 + of, D.f3 + of,
-                                                             D.gf1 + of, D.gf3 + of);
+      lin_t(c, B, s.gz3, d, w(Ds(l, "w2")), f, f, u.tBf, nullptr);
+      g_swiglu_bwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, u.tBf, s.f1, s.f3, s.gf1, s.gf3);
       c.check();
-      lin_t(c, B, D.gf1 + of, f, w(Ds(l, "w1")), d, d, D.gdc + o, nullptr);
-      lin_t(c, B, D.gf3 + of, f, w(Ds(l, "w3")), d, d, D.gdc + o, D.gdc + o);
-      rms_bwd(c, B, d, D.gdc + o, D.z2 + o, D.rs3 + R0, w(Dn(l, "m3")), gz3, D.gz2 + o);
+      lin_t(c, B, s.gf1, f, w(Ds(l, "w1")), d, d, s.gdc, nullptr);
+      lin_t(c, B, s.gf3, f, w(Ds(l, "w3")), d, d, s.gdc, s.gdc);
+      rms_bwd(c, B, d, s.gdc, s.z2, s.rs3, w(Dn(l, "m3")), s.gz3, s.gz2);
       // cross-attention over memory rows 1..t
       const int gi = grp(l);
-      lin_t(c, B, D.gz2 + o, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr);
-      attn_bwd_q(c, B, B, t, NOWIN, H, dh, D.qx + oh, u.mk[gi], u.mv[gi], D.ox + oh, D.lse2 + R0 * H, u.tBhd,
-                 D.gqx + oh, nullptr, u.gmk[gi], u.gmv[gi]);
-      rope(c, B, H, dh, D.gqx + oh, t + 1, B, base, -1.f);
-      lin_t(c, B, D.gqx + oh, hd, w(Dn(l, "xq")), d, d, D.gdb + o, nullptr);
-      rms_bwd(c, B, d, D.gdb + o, D.z1 + o, D.rs2 + R0, w(Dn(l, "m2")), D.gz2 + o, D.gz1 + o);
+      lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr);
+      attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
+                 u.gmk[gi], u.gmv[gi]);
+      rope(c, B, H, dh, s.gqx, t + 1, B, base, -1.f);
+      lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr);
+      rms_bwd(c, B, d, s.gdb, s.z1, s.rs2, w(Dn(l, "m2")), s.gz2, s.gz1);
       // window attention; the key/value gradient rows of t are complete afterwards
-      lin_t(c, B, D.gz1 + o, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr);
-      attn_bwd_q(c, B, B, t, cf.window, H, dh, D.q + oh, D.k, D.v, D.o + oh, D.lse1 + R0 * H, u.tBhd,
-                 D.gq + oh, nullptr, D.gk, D.gv);
-      rope(c, B, H, dh, D.gq + oh, t + 1, B, base, -1.f);
-      rope(c, B, H, dh, D.gk + oh, t + 1, B, base, -1.f);
-      lin_t(c, B, D.gq + oh, hd, w(Ds(l, "wq")), d, d, D.gda + o, nullptr);
-      lin_t(c, B, D.gk + oh, hd, w(Ds(l, "wk")), d, d, D.gda + o, D.gda + o);
-      lin_t(c, B, D.gv + oh, hd, w(Ds(l, "wv")), d, d, D.gda + o, D.gda + o);
-      float* gin = l > 0 ? u.dec[l - 1].gz3 + o : u.gu;
-      rms_bwd(c, B, d, D.gda + o, D.zin + o, D.rs1 + R0, w(Dn(l, "m1")), D.gz1 + o, gin);
+      lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr);
+      attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv);
+      rope(c, B, H, dh, s.gq, t + 1, B, base, -1.f);
+      rope(c, B, H, dh, s.gk, t + 1, B, base, -1.f);
+      lin_t(c, B, s.gq, hd, w(Ds(l, "wq")), d, d, s.gda, nullptr);
+      lin_t(c, B, s.gk, hd, w(Ds(l, "wk")), d, d, s.gda, s.gda);
+      lin_t(c, B, s.gv, hd, w(Ds(l, "wv")), d, d, s.gda, s.gda);
+      float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
+      rms_bwd(c, B, d, s.gda, s.zin, s.rs1, w(Dn(l, "m1")), s.gz1, gin);
+      if (ck) layer_wgrad(l, s, B);
     }
     float* get = u.ge + o;
     if (mg) {
-      float* ggp = u.ggp + o;
-      float* gsr = u.gsr + o;
-      g_merge_bwd<<<blocks(Bd), 256, 0, c.st>>>(Bd, u.gu, u.gate + o, u.sr + o, alpha, ggp, gsr);
+      float* ggp = mrow(u.ggp, t, d);
+      float* gsr = mrow(u.gsr, t, d);
+      float* gmr = mrow(u.gmr, t, d);
+      g_merge_bwd<<<blocks(Bd), 256, 0, c.st>>>(Bd, u.gu, mrow(u.gate, t, d), mrow(u.sr, t, d), alpha, ggp, gsr);
       c.check();
       lin_t(c, B, ggp, d, w("merge.wg"), 2 * d, d, get, u.gu);
-      lin_t(c, B, ggp, d, w("merge.wg") + d, 2 * d, d, u.gmr + o, nullptr);
-      lin_t(c, B, gsr, d, w("merge.ws"), d, d, u.gmr + o, u.gmr + o);
+      lin_t(c, B, ggp, d, w("merge.wg") + d, 2 * d, d, gmr, nullptr);
+      lin_t(c, B, gsr, d, w("merge.ws"), d, d, gmr, gmr);
       if (cf.variant == RLT_V1)
-        rms_bwd(c, B, d, u.gmr + o, u.msrc + o, u.mrs + R0, w("merge.ns"), nullptr, u.carry);
+        rms_bwd(c, B, d, gmr, u.msrc + o, mrow(u.mrs, t, 1), w("merge.ns"), nullptr, u.carry);
       else
-        rms_bwd(c, B, d, u.gmr + o, u.msrc + o, u.mrs + R0, w("merge.ns"), u.greg, u.greg);
+        rms_bwd(c, B, d, gmr, u.msrc + o, mrow(u.mrs, t, 1), w("merge.ns"), u.greg, u.greg);
+      if (ck) merge_wgrad(t, B);
     } else {
       add(c, Bd, u.gu, nullptr, get);
     }
   }
   if (mg) colsum(c, B, d, cf.variant == RLT_V1 ? u.carry : u.greg, nullptr, nullptr, g("merge.s0"));
   // --------------------------------------------- decoder and merge weight gradients
-  for (int l = 0; l < cf.L_D; ++l) {
-    DecBuf& D = u.dec[l];
-    wgrad(c, M, D.gq, hd, D.a, d, g(Ds(l, "wq")), d);
-    wgrad(c, M, D.gk, hd, D.a, d, g(Ds(l, "wk")), d);
-    wgrad(c, M, D.gv, hd, D.a, d, g(Ds(l, "wv")), d);
-    wgrad(c, M, D.gz1, d, D.o, hd, g(Ds(l, "wo")), hd);
-    wgrad(c, M, D.gqx, hd, D.b, d, g(Dn(l, "xq")), d);
-    wgrad(c, M, D.gz2, d, D.ox, hd, g(Dn(l, "xo")), hd);
-    wgrad(c, M, D.gf1, f, D.c, d, g(Ds(l, "w1")), d);
-    wgrad(c, M, D.gf3, f, D.c, d, g(Ds(l, "w3")), d);
-    wgrad(c, M, D.gz3, d, D.g, f, g(Ds(l, "w2")), f);
-    colsum(c, M, d, D.gda, D.zin, D.rs1, g(Dn(l, "m1")));
-    colsum(c, M, d, D.gdb, D.z1, D.rs2, g(Dn(l, "m2")));
-    colsum(c, M, d, D.gdc, D.z2, D.rs3, g(Dn(l, "m3")));
-  }
-  if (mg) {
-    wgrad(c, M, u.ggp, d, e_all, d, g("merge.wg"), 2 * d);
-    wgrad(c, M, u.ggp, d, u.mr, d, g("merge.wg") + d, 2 * d);
-    colsum(c, M, d, u.ggp, nullptr, nullptr, g("merge.bg"));
-    wgrad(c, M, u.gsr, d, u.mr, d, g("merge.ws"), d);
-    colsum(c, M, d, u.gmr, u.msrc, u.mrs, g("merge.ns"));
+  if (!ck) {
+    for (int l = 0; l < cf.L_D; ++l) layer_wgrad(l, step(l, 0), M);
+    if (mg) merge_wgrad(0, M);
   }
   // ------------------------------------------------------------ backward: memory
   if (cf.L_D > 0) {
@@ -973,7 +1038,8 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   // ----------------------------------------------------------- backward: encoder
   float* gh = u.ge;
   for (int l = cf.L_E - 1; l >= 0; --l) {
-    EncBuf& e = u.enc[l];
+    if (ck) enc_fwd(l);   // recompute the layer's intermediates (its output row is rewritten unchanged)
+    EncBuf& e = u.enc[ck ? 0 : l];
     lin_t(c, M, gh, d, w(E(l, "w2")), f, f, u.gf1, nullptr);
     g_swiglu_bwd<<<blocks((int64_t)M * f), 256, 0, c.st>>>((int64_t)M * f, u.gf1, e.f1, e.f3, u.gf1, u.gf3);
     c.check();

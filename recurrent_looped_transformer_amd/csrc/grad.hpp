@@ -11,8 +11,9 @@
 
 namespace rlt {
 
-// Bytes of device workspace the gradient needs for B sequences of T positions.
-size_t grad_workspace_bytes(const rlt_config& c, int B, int T);
+// Bytes of device workspace the gradient needs for B sequences of T positions (checkpoint:
+// keep block inputs, keys and values only, and recompute the rest before each backward).
+size_t grad_workspace_bytes(const rlt_config& c, int B, int T, bool checkpoint);
 
 // Runs the saved-activation forward, the loss gradient, the reverse-time decoder
 // scan and the encoder backward on `stream`. W: every manifest weight (fp32, device);
@@ -21,6 +22,6 @@ size_t grad_workspace_bytes(const rlt_config& c, int B, int T);
 // Shapes and names are validated by the caller. Returns the first HIP error.
 hipError_t replay_grad(const rlt_config& c, const std::map<std::string, const float*>& W,
                        const std::map<std::string, std::pair<float*, int64_t>>& G, const int32_t* tokens, int B, int T,
-                       const float* dlogprob, float* logprob, void* workspace, hipStream_t stream);
+                       const float* dlogprob, float* logprob, void* workspace, bool checkpoint, hipStream_t stream);
 
 }  // namespace rlt

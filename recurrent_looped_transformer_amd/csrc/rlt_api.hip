@@ -1574,25 +1574,26 @@ int rlt_importance_ratio(const float* logprob_current, const float* logprob_beha
   });
 }
 
-int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int64_t* bytes) {
+int rlt_replay_grad_workspace(const rlt_config* cfg, int B, int T, int checkpoint, int64_t* bytes) {
   return guarded([&] {
     if (!cfg || !bytes) fail(RLT_ERR_INVALID_ARG, "null pointer");
     validate_config(*cfg);
     if (B < 1 || T < 2) fail(RLT_ERR_INVALID_ARG, "B >= 1 and T >= 2 required");
-    *bytes = (int64_t)grad_workspace_bytes(*cfg, B, T);
+    *bytes = (int64_t)grad_workspace_bytes(*cfg, B, T, checkpoint != 0);
   });
 }
 
 int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, rlt_grad_tensor* grads,
                     int n_grads, const int32_t* tokens, int B, int T, const float* dlogprob, float* logprob,
-                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                    int checkpoint, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   return guarded([&] {
     if (!cfg) fail(RLT_ERR_INVALID_ARG, "null config");
     validate_config(*cfg);
     if (B < 1 || T < 2) fail(RLT_ERR_INVALID_ARG, "B >= 1 and T >= 2 required");
     if (!tokens || !dlogprob || !logprob || !workspace) fail(RLT_ERR_INVALID_ARG, "null pointer");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) fail(RLT_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-    if (workspace_bytes < (int64_t)grad_workspace_bytes(*cfg, B, T)) fail(RLT_ERR_INVALID_ARG, "workspace too small");
+    if (workspace_bytes < (int64_t)grad_workspace_bytes(*cfg, B, T, checkpoint != 0))
+      fail(RLT_ERR_INVALID_ARG, "workspace too small");
     auto W = index_weights(*cfg, weights, n_weights);
     if (n_grads < 0 || (n_grads > 0 && !grads)) fail(RLT_ERR_INVALID_ARG, "grads pointer");
     auto man = manifest(*cfg);
@@ -1608,7 +1609,7 @@ int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weig
     }
     for (auto& kv : man)
       if (!G.count(kv.first)) fail(RLT_ERR_INVALID_ARG, "missing gradient " + kv.first);
-    hipError_t e = replay_grad(*cfg, W, G, tokens, B, T, dlogprob, logprob, workspace, stream);
+    hipError_t e = replay_grad(*cfg, W, G, tokens, B, T, dlogprob, logprob, workspace, checkpoint != 0, stream);
     if (e != hipSuccess) fail(RLT_ERR_HIP, std::string("replay gradient: ") + hipGetErrorString(e));
   });
 }

@@ -95,12 +95,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_snapshot_size": [vp, vp, i64p],
         "rlt_snapshot": [vp, vp, vp, ctypes.c_int64, ctypes.POINTER(rlt_snapshot_info), vp],
         "rlt_restore": [vp, vp, ctypes.POINTER(rlt_snapshot_info), vp, vp],
-        "rlt_replay_grad_workspace": [ctypes.POINTER(rlt_config), i32, i32, i64p],
+        "rlt_replay_grad_workspace": [ctypes.POINTER(rlt_config), i32, i32, i32, i64p],
         "rlt_step_rows": [vp, vp, vp, ctypes.POINTER(ctypes.c_int32), vp, vp],
         "rlt_state_reset_rows": [vp, vp, ctypes.POINTER(ctypes.c_int32), vp],
         "rlt_state_row_positions": [vp, ctypes.POINTER(ctypes.c_int32)],
         "rlt_replay_grad": [ctypes.POINTER(rlt_config), ctypes.POINTER(rlt_tensor), i32,
-                            ctypes.POINTER(rlt_grad_tensor), i32, vp, i32, i32, vp, vp, vp, ctypes.c_int64, vp],
+                            ctypes.POINTER(rlt_grad_tensor), i32, vp, i32, i32, vp, vp, i32, vp, ctypes.c_int64,
+                            vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -295,16 +296,17 @@ def rlt_state_row_positions(state, batch: int) -> list:
     return list(out)
 
 
-def rlt_replay_grad_workspace(cfg: synth.Config, B: int, T: int) -> int:
+def rlt_replay_grad_workspace(cfg: synth.Config, B: int, T: int, checkpoint: bool = False) -> int:
     n = ctypes.c_int64(0)
     c = config_struct(cfg)
-    _check(load().rlt_replay_grad_workspace(ctypes.byref(c), B, T, ctypes.byref(n)))
+    _check(load().rlt_replay_grad_workspace(ctypes.byref(c), B, T, 1 if checkpoint else 0, ctypes.byref(n)))
     return n.value
 
 
 def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens: torch.Tensor,
                     dlogprob: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                    grads: Optional[Dict[str, torch.Tensor]] = None, logprob: Optional[torch.Tensor] = None):
+                    grads: Optional[Dict[str, torch.Tensor]] = None, logprob: Optional[torch.Tensor] = None,
+                    checkpoint: bool = False):
     """Full-BPTT gradient of sum(dlogprob * logprob) over the replay of tokens [B, T].
 
     weights: manifest name -> contiguous fp32 device tensor. Returns (logprob [B, T-1],
@@ -313,7 +315,7 @@ def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens:
     assert tokens.dtype == torch.int32 and tokens.dim() == 2 and dlogprob.dtype == torch.float32
     B, T = tokens.shape
     dev = tokens.device
-    need = rlt_replay_grad_workspace(cfg, B, T)
+    need = rlt_replay_grad_workspace(cfg, B, T, checkpoint)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     assert workspace.dtype == torch.uint8 and workspace.numel() >= need
@@ -333,7 +335,7 @@ def rlt_replay_grad(cfg: synth.Config, weights: Dict[str, torch.Tensor], tokens:
     dlp = dlogprob.contiguous()
     c = config_struct(cfg)
     _check(load().rlt_replay_grad(ctypes.byref(c), warr, len(names), garr, len(names), _ptr(tokens), B, T,
-                                  _ptr(dlp), _ptr(logprob), ctypes.c_void_p(workspace.data_ptr()),
+                                  _ptr(dlp), _ptr(logprob), 1 if checkpoint else 0, ctypes.c_void_p(workspace.data_ptr()),
                                   workspace.numel(), ctypes.c_void_p(_stream())))
     return logprob, grads
 

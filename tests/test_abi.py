@@ -99,9 +99,14 @@ def test_replay_grad_workspace_and_host_checks(lib):
     assert 0 < a < b and a < c and a % 256 == 0
     n = ctypes.c_int64(0)
     cs = rlt.config_struct(cfg)
-    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 2, 1, ctypes.byref(n)) == -1       # T < 2
-    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 0, 16, ctypes.byref(n)) == -1      # B < 1
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 2, 1, 0, ctypes.byref(n)) == -1    # T < 2
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(cs), 0, 16, 0, ctypes.byref(n)) == -1   # B < 1
     bad = rlt.config_struct(cfg.replace(groups=3))
-    assert lib.rlt_replay_grad_workspace(ctypes.byref(bad), 2, 16, ctypes.byref(n)) == -2     # G not in {1, L_D}
+    assert lib.rlt_replay_grad_workspace(ctypes.byref(bad), 2, 16, 0, ctypes.byref(n)) == -2  # G not in {1, L_D}
+    # checkpointing keeps a fraction of the intermediates
+    big = synth.CONFIGS["algo_bf16"]
+    full = rlt.rlt_replay_grad_workspace(big, 64, 257)
+    ck = rlt.rlt_replay_grad_workspace(big, 64, 257, checkpoint=True)
+    assert ck < 0.5 * full
     # null tokens / workspace: rejected before touching the device
-    assert lib.rlt_replay_grad(ctypes.byref(cs), None, 0, None, 0, None, 2, 16, None, None, None, 0, None) == -1
+    assert lib.rlt_replay_grad(ctypes.byref(cs), None, 0, None, 0, None, 2, 16, None, None, 0, None, 0, None) == -1

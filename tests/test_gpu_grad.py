@@ -58,9 +58,9 @@ def weights_for(cfg, B, T, seed=5):
     return np.random.default_rng(seed).standard_normal((B, T - 1)).astype(np.float32)
 
 
-def run_gpu(cfg, P, x, w):
+def run_gpu(cfg, P, x, w, ck=False):
     lp, G = rlt.rlt_replay_grad(cfg, to_dev(P), torch.as_tensor(x, dtype=torch.int32).cuda(),
-                                torch.as_tensor(w).cuda())
+                                torch.as_tensor(w).cuda(), checkpoint=ck)
     torch.cuda.synchronize()
     return lp.cpu().numpy().astype(np.float64), {k: v.cpu().numpy().astype(np.float64) for k, v in G.items()}
 
@@ -81,16 +81,17 @@ def compare(cfg, lp, G, lp_ref, G_ref, tag):
     assert err_lp <= LP_TOL, (tag, err_lp)
 
 
+@pytest.mark.parametrize("ck", [False, True], ids=["kept", "checkpointed"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_gradient_matches_oracle(case):
+def test_gradient_matches_oracle(case, ck):
     cfg = TINY.replace(**CASES[case])
     P = make_params(cfg, std=0.1)
     x = make_tokens(cfg)
     w = weights_for(cfg, cfg.batch, cfg.seq_len)
-    print(f"[grad] case {case} B={cfg.batch} T={cfg.seq_len}", flush=True)
-    lp, G = run_gpu(cfg, P, x, w)
+    print(f"[grad] case {case} B={cfg.batch} T={cfg.seq_len} checkpoint={ck}", flush=True)
+    lp, G = run_gpu(cfg, P, x, w, ck)
     lp_ref, G_ref = GradOracle(cfg, P).grad(x, w.astype(np.float64))
-    compare(cfg, lp, G, lp_ref, G_ref, case)
+    compare(cfg, lp, G, lp_ref, G_ref, case + (" checkpointed" if ck else ""))
 
 
 def test_gradient_is_deterministic_up_to_atomics():
@@ -120,15 +121,32 @@ def algo_fp32():
 
 def test_algo_shape_two_sequences_match_oracle():
     """The 512-wide 4 + 4 shape at its full length T = 257 (window 32 slides 225 times),
-    2 sequences, against the float64 oracle."""
+    2 sequences, against the float64 oracle, with and without checkpointing."""
     cfg = algo_fp32().replace(batch=2)
     P = make_params(cfg)
     x = make_tokens(cfg)
     w = weights_for(cfg, 2, cfg.seq_len)
     print("[grad] algo shape B=2 T=257", flush=True)
-    lp, G = run_gpu(cfg, P, x, w)
     lp_ref, G_ref = GradOracle(cfg, P).grad(x, w.astype(np.float64))
-    compare(cfg, lp, G, lp_ref, G_ref, "algo B=2")
+    for ck in (False, True):
+        lp, G = run_gpu(cfg, P, x, w, ck)
+        compare(cfg, lp, G, lp_ref, G_ref, "algo B=2" + (" checkpointed" if ck else ""))
+
+
+def test_checkpointed_equals_kept_at_full_batch():
+    """B = 64 at T = 257: the checkpointed gradient equals the kept-intermediates one within
+    fp32 reassociation (weight gradients summed position by position instead of at once);
+    the log-probabilities are identical (the same forward kernels)."""
+    cfg = algo_fp32()
+    P = make_params(cfg)
+    x = make_tokens(cfg)
+    w = weights_for(cfg, cfg.batch, cfg.seq_len)
+    lp0, G0 = run_gpu(cfg, P, x, w, False)
+    lp1, G1 = run_gpu(cfg, P, x, w, True)
+    assert np.array_equal(lp0, lp1)
+    for name, _ in manifest(cfg):
+        a, b = G1[name].reshape(-1), G0[name].reshape(-1)
+        assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(b) + 1e-7 * np.sqrt(a.size), name
 
 
 def test_algo_shape_full_batch_is_sum_of_slices():
