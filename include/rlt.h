@@ -291,7 +291,7 @@ int rlt_state_row_positions(const rlt_state* s, int32_t* n);
  * decoder keys/values and the memory, and recomputes a position's block intermediates (an
  * encoder layer's, token-parallel) just before its backward: about a quarter of the
  * workspace for one more forward pass; weight gradients then accumulate position by position.
- * weights: the manifest tensors (device fp32, as for rlt_create). grads: one writable
+ * weights: the manifest tensors (device fp32, as for rlt_create, 16-byte aligned). grads: one writable
  * device fp32 tensor per manifest name with the same size (zeroed, then filled).
  * tokens: device int32 [B, T], x_1 = BOS. Asynchronous on `stream`.
  * Errors: INVALID_ARG (configuration, missing/unknown/duplicate/mis-sized tensors, B < 1,

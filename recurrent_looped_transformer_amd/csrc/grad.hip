@@ -27,11 +27,12 @@
 // Kernels: a 64x64-tiled fp32 GEMM with both operand orientations (and split-K with
 // atomic accumulation for the weight gradients, whose reduction runs over T*B rows);
 // wave-per-row RMSNorm forward/backward; column reductions for gains and biases; rotary
-// rotation by +/- angle (float64 angles, as in the forward path); one-wave-per-(query,
-// head) attention forward (online softmax, log-sum-exp kept) and backward (probabilities
-// recomputed from the log-sum-exp; query-side kernel that can also update the key/value
-// gradient rows when each launch holds one query per (sequence, head), key-side kernel
-// for the causal encoder); SwiGLU, merge and readout elementwise kernels.
+// rotation by +/- angle (float64 angles, as in the forward path); attention with a block
+// per (query, head) and dh/4 lanes per key (forward with per-group online softmax and the
+// log-sum-exp kept; backward with probabilities recomputed from the log-sum-exp: a
+// query-side kernel that can also update the key/value gradient rows when each launch
+// holds one query per (sequence, head), and a key-side kernel for the causal encoder);
+// SwiGLU, merge and readout elementwise kernels.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -46,10 +47,22 @@ namespace rlt {
 namespace {
 
 constexpr int GT = 64;  // GEMM tile rows / columns
-constexpr int GK = 16;  // GEMM k step
+constexpr int GK = 16;  // GEMM k step: a 64x16 operand tile is one float4 per thread
 constexpr int NOWIN = INT_MAX / 4;
 
 // ----------------------------------------------------------------------------- GEMM
+// Optional segments of one product. A along k (A(m, k) with k-contiguous rows only): for
+// kseg > 0, k in [p*kseg, (p+1)*kseg) reads a[p][m*lda + k - p*kseg] (a sum of up to three
+// products with equal m and n). C and R along n: for nseg > 0, column n in
+// [p*nseg, (p+1)*nseg) is c[p][m*ldc + n - p*nseg] (up to three outputs of one input).
+struct Seg {
+  const float* a[3] = {nullptr, nullptr, nullptr};
+  int kseg = 0;
+  float* c[3] = {nullptr, nullptr, nullptr};
+  const float* r[3] = {nullptr, nullptr, nullptr};
+  int nseg = 0;
+};
+__device__ __forceinline__ int seg_of(int x, int len) { return (x >= len) + (x >= 2 * len); }
 // C[m, n] = (R ? R[m, n] : 0) + sum_k A(m, k) B(k, n), or, when atomic, C[m, n] += sum.
 // A(m, k) = AK ? A[m*lda + k] : A[k*lda + m];  B(k, n) = BK ? B[n*ldb + k] : B[k*ldb + n].
 // R, when given, has C's layout (it may be C itself). blockIdx.z takes k in
@@ -58,28 +71,42 @@ constexpr int NOWIN = INT_MAX / 4;
 template <bool AK, bool BK>
 __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                                               const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
-                                              const float* R, int atomic, int kchunk, float* __restrict__ part) {
+                                              const float* R, int atomic, int kchunk, float* __restrict__ part,
+                                              Seg sg) {
   __shared__ float As[GK][GT + 4];
   __shared__ float Bs[GK][GT + 4];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
   const int kb = blockIdx.z * kchunk;
   const int ke = min(K, kb + kchunk);
-  float ra[4], rb[4];
+  // Each thread loads one float4 of each operand tile: along k when k is the contiguous index
+  // (row = tid / 4, k = 4 * (tid % 4)), else along m / n (k = tid / 16, 4 * (tid % 16)). Every
+  // contiguous extent (k for k-contiguous operands, m / n otherwise) is a multiple of 4.
+  float4 ra, rb;
   auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;
-      {
-        const int m = AK ? (e >> 4) : (e & 63), k = AK ? (e & 15) : (e >> 6);
-        const int gm = m0 + m, gk = k0 + k;
-        ra[i] = (gm < M && gk < ke) ? (AK ? A[(int64_t)gm * lda + gk] : A[(int64_t)gk * lda + gm]) : 0.f;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (AK) {
+      const int gm = m0 + (tid >> 2), gk = k0 + 4 * (tid & 3);
+      if (gm < M && gk < ke) {
+        if (sg.kseg) {
+          const int sp = seg_of(gk, sg.kseg);
+          ra = *reinterpret_cast<const float4*>(sg.a[sp] + (int64_t)gm * lda + gk - sp * sg.kseg);
+        } else {
+          ra = *reinterpret_cast<const float4*>(A + (int64_t)gm * lda + gk);
+        }
+      } else {
+        ra = z;
       }
-      {
-        const int n = BK ? (e >> 4) : (e & 63), k = BK ? (e & 15) : (e >> 6);
-        const int gn = n0 + n, gk = k0 + k;
-        rb[i] = (gn < N && gk < ke) ? (BK ? Bm[(int64_t)gn * ldb + gk] : Bm[(int64_t)gk * ldb + gn]) : 0.f;
-      }
+    } else {
+      const int gk = k0 + (tid >> 4), gm = m0 + 4 * (tid & 15);
+      ra = (gk < ke && gm < M) ? *reinterpret_cast<const float4*>(A + (int64_t)gk * lda + gm) : z;
+    }
+    if (BK) {
+      const int gn = n0 + (tid >> 2), gk = k0 + 4 * (tid & 3);
+      rb = (gn < N && gk < ke) ? *reinterpret_cast<const float4*>(Bm + (int64_t)gn * ldb + gk) : z;
+    } else {
+      const int gk = k0 + (tid >> 4), gn = n0 + 4 * (tid & 15);
+      rb = (gk < ke && gn < N) ? *reinterpret_cast<const float4*>(Bm + (int64_t)gk * ldb + gn) : z;
     }
   };
   float acc[4][4];
@@ -91,11 +118,19 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
   if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += GK) {
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;
-      if (AK) As[e & 15][e >> 4] = ra[i]; else As[e >> 6][e & 63] = ra[i];
-      if (BK) Bs[e & 15][e >> 4] = rb[i]; else Bs[e >> 6][e & 63] = rb[i];
+    if (AK) {
+      const int r = tid >> 2, k = 4 * (tid & 3);
+      As[k][r] = ra.x; As[k + 1][r] = ra.y; As[k + 2][r] = ra.z; As[k + 3][r] = ra.w;
+    } else {
+      const int k = tid >> 4, r = 4 * (tid & 15);
+      *reinterpret_cast<float4*>(&As[k][r]) = ra;
+    }
+    if (BK) {
+      const int r = tid >> 2, k = 4 * (tid & 3);
+      Bs[k][r] = rb.x; Bs[k + 1][r] = rb.y; Bs[k + 2][r] = rb.z; Bs[k + 3][r] = rb.w;
+    } else {
+      const int k = tid >> 4, r = 4 * (tid & 15);
+      *reinterpret_cast<float4*>(&Bs[k][r]) = rb;
     }
     __syncthreads();
     if (k0 + GK < ke) load(k0 + GK);
@@ -124,21 +159,33 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
         part[((int64_t)blockIdx.z * M + gm) * N + gn] = acc[i][j];
         continue;
       }
-      float* c = C + (int64_t)gm * ldc + gn;
-      if (atomic) atomicAdd(c, acc[i][j]);
-      else *c = (R ? R[(int64_t)gm * ldc + gn] : 0.f) + acc[i][j];
+      float* Cp = C;
+      const float* Rp = R;
+      int nn = gn;
+      if (sg.nseg) {
+        const int sp = seg_of(gn, sg.nseg);
+        Cp = sg.c[sp]; Rp = sg.r[sp]; nn = gn - sp * sg.nseg;
+      }
+      float* cc = Cp + (int64_t)gm * ldc + nn;
+      if (atomic) atomicAdd(cc, acc[i][j]);
+      else *cc = (Rp ? Rp[(int64_t)gm * ldc + nn] : 0.f) + acc[i][j];
     }
   }
 }
 
 // C[m, n] = (R ? R[m, n] : 0) + sum_{z < splits} part[z][m][n], z ascending
 __global__ void g_splitk_reduce(int M, int N, int splits, const float* __restrict__ part, const float* R, float* C,
-                                int64_t ldc) {
+                                int64_t ldc, Seg sg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)M * N) return;
-  const int64_t m = i / N, n = i % N;
+  const int64_t m = i / N;
+  int n = (int)(i % N);
   float v = 0.f;
   for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + i];
+  if (sg.nseg) {
+    const int sp = seg_of(n, sg.nseg);
+    C = sg.c[sp]; R = sg.r[sp]; n -= sp * sg.nseg;
+  }
   C[m * ldc + n] = (R ? R[m * ldc + n] : 0.f) + v;
 }
 
@@ -336,185 +383,158 @@ __global__ __launch_bounds__(256) void g_readout(int B, int T, int V, const floa
 }
 
 // ---------------------------------------------------------------------- attention
-// One wave per (query row r, head h). Query r belongs to sequence b = r % B at time
-// tq = tq0 + r / B (0-based); it reads keys j in [max(0, tq - win + 1), tq] at rows j*B + b
-// of K and V. Q, O rows are local (r); lse is [nq, H].
-template <int NV>
-__global__ __launch_bounds__(64) void g_attn_fwd(int nq, int B, int tq0, int win, int H, int dh, float scale,
-                                                 const float* __restrict__ Q, const float* __restrict__ K,
-                                                 const float* __restrict__ Vv, float* __restrict__ O,
-                                                 float* __restrict__ lse) {
-  __shared__ float qs[64 * NV];
-  const int r = blockIdx.x / H, h = blockIdx.x % H, lane = threadIdx.x;
-  const int hd = H * dh, b = r % B, tq = tq0 + r / B;
+// A block of 256 threads per (row, head); a key (or, key side, a query) is handled by a group
+// of G = DH/4 lanes, each with four of its dimensions in a float4, so NG = 256/G of them are in
+// flight per round; dot products are group sums over shuffles. Query r of a query-side kernel
+// belongs to sequence b = r % B at time tq = tq0 + r / B (0-based) and reads keys j in
+// [max(0, tq - win + 1), tq] at rows j*B + b of K and V; Q, O rows are local (r), lse [nq, H].
+template <int G>
+__device__ __forceinline__ float gsum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 c) {
+  return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z), fmaf(s, a.w, c.w));
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+
+// Online softmax per group, the groups merged at the end: O and lse.
+template <int DH>
+__global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int win, int H, float scale,
+                                                  const float* __restrict__ Q, const float* __restrict__ K,
+                                                  const float* __restrict__ Vv, float* __restrict__ O,
+                                                  float* __restrict__ lse) {
+  constexpr int G = DH / 4, NG = 256 / G;
+  __shared__ float4 pacc[256];
+  __shared__ float pm[NG], pl[NG];
+  const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
+  const int hd = H * DH, b = r % B, tq = tq0 + r / B;
   const int lo = max(0, tq - win + 1);
-  for (int i = lane; i < dh; i += 64) qs[i] = Q[(int64_t)r * hd + h * dh + i] * scale;
-  __syncthreads();
-  float m = -INFINITY, l = 0.f, o[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) o[v] = 0.f;
-  for (int j0 = lo; j0 <= tq; j0 += 64) {
-    const int j = j0 + lane;
-    const bool ok = j <= tq;
-    float s = -INFINITY;
-    if (ok) {
-      const float* kp = K + ((int64_t)j * B + b) * hd + h * dh;
-      float a = 0.f;
-      for (int i = 0; i < dh; ++i) a = fmaf(qs[i], kp[i], a);
-      s = a;
-    }
-    const float mn = fmaxf(m, wave_max(s));
-    const float sc = expf(m - mn);
-    const float p = ok ? expf(s - mn) : 0.f;
-    l = l * sc + wave_sum(p);
-#pragma unroll
-    for (int v = 0; v < NV; ++v) o[v] *= sc;
-    const int cnt = min(64, tq - j0 + 1);
-    for (int k = 0; k < cnt; ++k) {
-      const float pk = __shfl(p, k, 64);
-      const float* vp = Vv + ((int64_t)(j0 + k) * B + b) * hd + h * dh;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int dd = lane + 64 * v;
-        if (dd < dh) o[v] = fmaf(pk, vp[dd], o[v]);
-      }
-    }
+  float4 q = ld4(Q + (int64_t)r * hd + h * DH + gl * 4);
+  q.x *= scale; q.y *= scale; q.z *= scale; q.w *= scale;
+  float m = -INFINITY, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = lo + gi; j <= tq; j += NG) {
+    const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
+    const float4 k = ld4(K + ro), v = ld4(Vv + ro);
+    const float sc = gsum<G>(dot4(q, k));
+    const float mn = fmaxf(m, sc);
+    const float c = __expf(m - mn), p = __expf(sc - mn);
+    l = l * c + p;
+    acc = fma4(p, v, make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c));
     m = mn;
   }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int dd = lane + 64 * v;
-    if (dd < dh) O[(int64_t)r * hd + h * dh + dd] = o[v] / l;
-  }
-  if (lane == 0) lse[(int64_t)r * H + h] = m + logf(l);
-}
-
-// Query side of the attention backward, same indexing as g_attn_fwd. With probabilities
-// p_j = exp(s_j - lse) recomputed, D = dO.O, dS_j = p_j (dO.v_j - D):
-//   dQ = scale * sum_j dS_j k_j; Dout (optional) = D;
-//   KV: dK[row_j] += scale * dS_j q, dV[row_j] += p_j dO (plain read-modify-write: the
-//   launch must hold at most one query per (sequence, head)).
-template <int NV, bool KV>
-__global__ __launch_bounds__(64) void g_attn_bwd_q(int nq, int B, int tq0, int win, int H, int dh, float scale,
-                                                   const float* __restrict__ Q, const float* __restrict__ K,
-                                                   const float* __restrict__ Vv, const float* __restrict__ O,
-                                                   const float* __restrict__ lse, const float* __restrict__ dO,
-                                                   float* __restrict__ dQ, float* __restrict__ Dout, float* dK,
-                                                   float* dV) {
-  __shared__ float qs[64 * NV], gs[64 * NV];
-  const int r = blockIdx.x / H, h = blockIdx.x % H, lane = threadIdx.x;
-  const int hd = H * dh, b = r % B, tq = tq0 + r / B;
-  const int lo = max(0, tq - win + 1);
-  const int64_t qo = (int64_t)r * hd + h * dh;
-  float dpart = 0.f;
-  for (int i = lane; i < dh; i += 64) {
-    qs[i] = Q[qo + i] * scale;
-    gs[i] = dO[qo + i];
-    dpart = fmaf(dO[qo + i], O[qo + i], dpart);
-  }
-  const float D = wave_sum(dpart);
+  pacc[tid] = acc;
+  if (gl == 0) { pm[gi] = m; pl[gi] = l; }
   __syncthreads();
-  const float L = lse[(int64_t)r * H + h];
-  float dq[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) dq[v] = 0.f;
-  for (int j0 = lo; j0 <= tq; j0 += 64) {
-    const int j = j0 + lane;
-    float p = 0.f, ds = 0.f;
-    if (j <= tq) {
-      const int64_t ro = ((int64_t)j * B + b) * hd + h * dh;
-      float s = 0.f, dp = 0.f;
-      for (int i = 0; i < dh; ++i) {
-        s = fmaf(qs[i], K[ro + i], s);
-        dp = fmaf(gs[i], Vv[ro + i], dp);
-      }
-      p = expf(s - L);
-      ds = p * (dp - D);
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int k = 0; k < NG; ++k) M = fmaxf(M, pm[k]);
+    float den = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < NG; ++k) {
+      if (pm[k] == -INFINITY) continue;
+      const float e = __expf(pm[k] - M);
+      den += e * pl[k];
+      o = fma4(e, pacc[k * G + tid], o);
     }
-    const int cnt = min(64, tq - j0 + 1);
-    for (int k = 0; k < cnt; ++k) {
-      const float dsk = __shfl(ds, k, 64);
-      const float pk = __shfl(p, k, 64);
-      const int64_t ro = ((int64_t)(j0 + k) * B + b) * hd + h * dh;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int dd = lane + 64 * v;
-        if (dd < dh) {
-          dq[v] = fmaf(dsk, K[ro + dd], dq[v]);
-          if (KV) {
-            dK[ro + dd] += dsk * qs[dd];
-            dV[ro + dd] += pk * gs[dd];
-          }
-        }
-      }
-    }
+    const float inv = 1.f / den;
+    st4(O + (int64_t)r * hd + h * DH + tid * 4, make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+    if (tid == 0) lse[(int64_t)r * H + h] = M + logf(den);
   }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int dd = lane + 64 * v;
-    if (dd < dh) dQ[qo + dd] = dq[v] * scale;
-  }
-  if (Dout && lane == 0) Dout[(int64_t)r * H + h] = D;
 }
 
-// Key side of the attention backward for token-parallel causal attention over T
-// positions: one wave per (key row kr = tk*B + b, head); queries i in [tk, min(T-1,
-// tk + win - 1)] at rows i*B + b. dK = scale * sum_i dS_i q_i, dV = sum_i p_i dO_i (written).
-template <int NV>
-__global__ __launch_bounds__(64) void g_attn_bwd_kv(int B, int T, int win, int H, int dh, float scale,
+// Query side of the attention backward. With p_j = exp(s_j - lse) recomputed, D = dO.O,
+// dS_j = p_j (dO.v_j - D): dQ = scale * sum_j dS_j k_j; Dout (optional) = D;
+// KV: dK[row_j] += scale * dS_j q, dV[row_j] += p_j dO (plain read-modify-write: the launch
+// must hold at most one query per (sequence, head)).
+template <int DH, bool KV>
+__global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int win, int H, float scale,
                                                     const float* __restrict__ Q, const float* __restrict__ K,
-                                                    const float* __restrict__ Vv, const float* __restrict__ lse,
-                                                    const float* __restrict__ Dq, const float* __restrict__ dO,
-                                                    float* __restrict__ dK, float* __restrict__ dV) {
-  __shared__ float ks[64 * NV], vs[64 * NV];
-  const int kr = blockIdx.x / H, h = blockIdx.x % H, lane = threadIdx.x;
-  const int hd = H * dh, b = kr % B, tk = kr / B;
-  const int hi = (int)std::min<int64_t>(T - 1, (int64_t)tk + win - 1);
-  const int64_t ko = (int64_t)kr * hd + h * dh;
-  for (int i = lane; i < dh; i += 64) {
-    ks[i] = K[ko + i] * scale;
-    vs[i] = Vv[ko + i];
+                                                    const float* __restrict__ Vv, const float* __restrict__ O,
+                                                    const float* __restrict__ lse, const float* __restrict__ dO,
+                                                    float* __restrict__ dQ, float* __restrict__ Dout, float* dK,
+                                                    float* dV) {
+  constexpr int G = DH / 4, NG = 256 / G;
+  __shared__ float4 pdq[256];
+  const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
+  const int hd = H * DH, b = r % B, tq = tq0 + r / B;
+  const int lo = max(0, tq - win + 1);
+  const int64_t qo = (int64_t)r * hd + h * DH + gl * 4;
+  float4 q = ld4(Q + qo);
+  q.x *= scale; q.y *= scale; q.z *= scale; q.w *= scale;
+  const float4 go = ld4(dO + qo);
+  const float D = gsum<G>(dot4(go, ld4(O + qo)));
+  const float L = lse[(int64_t)r * H + h];
+  float4 dq = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = lo + gi; j <= tq; j += NG) {
+    const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
+    const float4 k = ld4(K + ro), v = ld4(Vv + ro);
+    const float p = __expf(gsum<G>(dot4(q, k)) - L);
+    const float ds = p * (gsum<G>(dot4(go, v)) - D);
+    dq = fma4(ds, k, dq);
+    if (KV) {
+      st4(dK + ro, fma4(ds, q, ld4(dK + ro)));
+      st4(dV + ro, fma4(p, go, ld4(dV + ro)));
+    }
   }
+  pdq[tid] = dq;
   __syncthreads();
-  float dk[NV], dv[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) dk[v] = dv[v] = 0.f;
-  for (int i0 = tk; i0 <= hi; i0 += 64) {
-    const int i = i0 + lane;
-    float p = 0.f, ds = 0.f;
-    if (i <= hi) {
-      const int64_t qr = (int64_t)i * B + b;
-      const int64_t ro = qr * hd + h * dh;
-      float s = 0.f, dp = 0.f;
-      for (int c = 0; c < dh; ++c) {
-        s = fmaf(Q[ro + c], ks[c], s);
-        dp = fmaf(dO[ro + c], vs[c], dp);
-      }
-      p = expf(s - lse[qr * H + h]);
-      ds = p * (dp - Dq[qr * H + h]);
+  if (tid < G) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < NG; ++k) {
+      const float4 x = pdq[k * G + tid];
+      t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
     }
-    const int cnt = min(64, hi - i0 + 1);
-    for (int k = 0; k < cnt; ++k) {
-      const float dsk = __shfl(ds, k, 64);
-      const float pk = __shfl(p, k, 64);
-      const int64_t ro = ((int64_t)(i0 + k) * B + b) * hd + h * dh;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int dd = lane + 64 * v;
-        if (dd < dh) {
-          dk[v] = fmaf(dsk, Q[ro + dd], dk[v]);
-          dv[v] = fmaf(pk, dO[ro + dd], dv[v]);
-        }
-      }
-    }
+    st4(dQ + (int64_t)r * hd + h * DH + tid * 4, make_float4(t.x * scale, t.y * scale, t.z * scale, t.w * scale));
+    if (Dout && tid == 0) Dout[(int64_t)r * H + h] = D;
   }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int dd = lane + 64 * v;
-    if (dd < dh) {
-      dK[ko + dd] = dk[v] * scale;
-      dV[ko + dd] = dv[v];
+}
+
+// Key side of the attention backward for token-parallel causal attention over T positions:
+// a block per (key row kr = tk*B + b, head); queries i in [tk, min(T-1, tk + win - 1)] at
+// rows i*B + b. dK = scale * sum_i dS_i q_i, dV = sum_i p_i dO_i (written).
+template <int DH>
+__global__ __launch_bounds__(256) void g_attn_bwd_kv(int B, int T, int win, int H, float scale,
+                                                     const float* __restrict__ Q, const float* __restrict__ K,
+                                                     const float* __restrict__ Vv, const float* __restrict__ lse,
+                                                     const float* __restrict__ Dq, const float* __restrict__ dO,
+                                                     float* __restrict__ dK, float* __restrict__ dV) {
+  constexpr int G = DH / 4, NG = 256 / G;
+  __shared__ float4 pk[256], pv[256];
+  const int kr = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
+  const int hd = H * DH, b = kr % B, tk = kr / B;
+  const int hi = (int)std::min<int64_t>(T - 1, (int64_t)tk + win - 1);
+  const int64_t ko = (int64_t)kr * hd + h * DH + gl * 4;
+  float4 k = ld4(K + ko);
+  k.x *= scale; k.y *= scale; k.z *= scale; k.w *= scale;
+  const float4 v = ld4(Vv + ko);
+  float4 dk = make_float4(0.f, 0.f, 0.f, 0.f), dv = dk;
+  for (int i = tk + gi; i <= hi; i += NG) {
+    const int64_t qr = (int64_t)i * B + b;
+    const int64_t ro = qr * hd + h * DH + gl * 4;
+    const float4 q = ld4(Q + ro), go = ld4(dO + ro);
+    const float p = __expf(gsum<G>(dot4(q, k)) - lse[qr * H + h]);
+    const float ds = p * (gsum<G>(dot4(go, v)) - Dq[qr * H + h]);
+    dk = fma4(ds, q, dk);
+    dv = fma4(p, go, dv);
+  }
+  pk[tid] = dk;
+  pv[tid] = dv;
+  __syncthreads();
+  if (tid < G) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+    for (int j = 0; j < NG; ++j) {
+      const float4 x = pk[j * G + tid], y = pv[j * G + tid];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      c.x += y.x; c.y += y.y; c.z += y.z; c.w += y.w;
     }
+    const int64_t o = (int64_t)kr * hd + h * DH + tid * 4;
+    st4(dK + o, make_float4(a.x * scale, a.y * scale, a.z * scale, a.w * scale));
+    st4(dV + o, c);
   }
 }
 
@@ -536,7 +556,7 @@ inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 // partial sums a second kernel adds in a fixed order (deterministic).
 constexpr int kMaxSplits = 16;
 void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, const float* Bm, int64_t ldb, bool bk,
-          float* C, int64_t ldc, const float* R, bool atomic) {
+          float* C, int64_t ldc, const float* R, bool atomic, const Seg& sg = Seg()) {
   // atomic: C += A.B; otherwise C = R + A.B
   if (M <= 0 || N <= 0) return;
   const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT;
@@ -561,15 +581,30 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   if (splits == 1) part = nullptr;
   dim3 grid(tn, tm, splits);
   const int at = atomic ? 1 : 0;
-  if (ak && bk) g_gemm<true, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
-  else if (ak) g_gemm<true, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
-  else if (bk) g_gemm<false, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
-  else g_gemm<false, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
+  if (ak && bk) g_gemm<true, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  else if (ak) g_gemm<true, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  else if (bk) g_gemm<false, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  else g_gemm<false, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
   c.check();
   if (part) {
-    g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc);
+    g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc, sg);
     c.check();
   }
+}
+// Y_p[M, out] = X[M, in] . W_p^T for the np row blocks W_p of Wcat [np*out, in] (one launch)
+void lin_n(Ctx& c, int M, const float* X, int in, const float* Wcat, int out, int np, float* const* Y) {
+  Seg sg;
+  for (int p = 0; p < np; ++p) sg.c[p] = Y[p];
+  sg.nseg = out;
+  gemm(c, M, np * out, in, X, in, true, Wcat, in, true, Y[0], out, nullptr, false, sg);
+}
+// dX[M, in] = R + sum_p dY_p[M, out] . W_p for the np row blocks W_p of Wcat [np*out, in]
+void lin_tk(Ctx& c, int M, const float* const* dY, int out, int np, const float* Wcat, int in, float* dX,
+            const float* R) {
+  Seg sg;
+  for (int p = 0; p < np; ++p) sg.a[p] = dY[p];
+  sg.kseg = out;
+  gemm(c, M, in, np * out, dY[0], out, true, Wcat, in, false, dX, in, R, false, sg);
 }
 // Y[M, out] = R + X[M, in] . W^T, W row-major [out, ldw] (ldw = in unless a column slice)
 void lin(Ctx& c, int M, const float* X, int in, const float* W, int64_t ldw, int out, float* Y, const float* R) {
@@ -617,51 +652,60 @@ void add(Ctx& c, int64_t n, const float* a, const float* b, float* out) {
   c.check();
 }
 
-template <int NV>
-void attn_fwd_n(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
-                const float* V, float* O, float* lse) {
-  g_attn_fwd<NV><<<nq * H, 64, 0, c.st>>>(nq, B, tq0, win, H, dh, 1.f / sqrtf((float)dh), Q, K, V, O, lse);
+template <int DH>
+void attn_fwd_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
+                float* O, float* lse) {
+  g_attn_fwd<DH><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, 1.f / sqrtf((float)DH), Q, K, V, O, lse);
 }
 void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
               const float* V, float* O, float* lse) {
   if (nq <= 0) return;
-  if (dh <= 64) attn_fwd_n<1>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse);
-  else if (dh <= 128) attn_fwd_n<2>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse);
-  else attn_fwd_n<4>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse);
+  switch (dh) {
+    case 16: attn_fwd_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+    case 32: attn_fwd_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+    case 64: attn_fwd_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+    case 128: attn_fwd_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+    default: attn_fwd_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+  }
   c.check();
 }
-template <int NV, bool KV>
-void attn_bwd_q_n(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
-                  const float* V, const float* O, const float* lse, const float* dO, float* dQ, float* Dout,
-                  float* dK, float* dV) {
-  g_attn_bwd_q<NV, KV><<<nq * H, 64, 0, c.st>>>(nq, B, tq0, win, H, dh, 1.f / sqrtf((float)dh), Q, K, V, O, lse,
-                                                dO, dQ, Dout, dK, dV);
+template <int DH>
+void attn_bwd_q_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
+                  const float* O, const float* lse, const float* dO, float* dQ, float* Dout, float* dK, float* dV) {
+  const float sc = 1.f / sqrtf((float)DH);
+  if (dK)
+    g_attn_bwd_q<DH, true><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
+  else
+    g_attn_bwd_q<DH, false><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
 }
 void attn_bwd_q(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
                 const float* V, const float* O, const float* lse, const float* dO, float* dQ, float* Dout,
                 float* dK, float* dV) {
   if (nq <= 0) return;
-  const bool kv = dK != nullptr;
-  if (dh <= 64) {
-    if (kv) attn_bwd_q_n<1, true>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
-    else attn_bwd_q_n<1, false>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
-  } else if (dh <= 128) {
-    if (kv) attn_bwd_q_n<2, true>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
-    else attn_bwd_q_n<2, false>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
-  } else {
-    if (kv) attn_bwd_q_n<4, true>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
-    else attn_bwd_q_n<4, false>(c, nq, B, tq0, win, H, dh, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
+  switch (dh) {
+    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
+    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
+    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
+    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
+    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
   }
   c.check();
 }
+template <int DH>
+void attn_bwd_kv_n(Ctx& c, int B, int T, int win, int H, const float* Q, const float* K, const float* V,
+                   const float* lse, const float* Dq, const float* dO, float* dK, float* dV) {
+  g_attn_bwd_kv<DH><<<B * T * H, 256, 0, c.st>>>(B, T, win, H, 1.f / sqrtf((float)DH), Q, K, V, lse, Dq, dO, dK, dV);
+}
 void attn_bwd_kv(Ctx& c, int B, int T, int win, int H, int dh, const float* Q, const float* K, const float* V,
                  const float* lse, const float* Dq, const float* dO, float* dK, float* dV) {
-  const int nk = B * T;
-  if (nk <= 0) return;
-  const float sc = 1.f / sqrtf((float)dh);
-  if (dh <= 64) g_attn_bwd_kv<1><<<nk * H, 64, 0, c.st>>>(B, T, win, H, dh, sc, Q, K, V, lse, Dq, dO, dK, dV);
-  else if (dh <= 128) g_attn_bwd_kv<2><<<nk * H, 64, 0, c.st>>>(B, T, win, H, dh, sc, Q, K, V, lse, Dq, dO, dK, dV);
-  else g_attn_bwd_kv<4><<<nk * H, 64, 0, c.st>>>(B, T, win, H, dh, sc, Q, K, V, lse, Dq, dO, dK, dV);
+  if (B * T <= 0) return;
+  switch (dh) {
+    case 16: attn_bwd_kv_n<16>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+    case 32: attn_bwd_kv_n<32>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+    case 64: attn_bwd_kv_n<64>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+    case 128: attn_bwd_kv_n<128>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+    default: attn_bwd_kv_n<256>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+  }
   c.check();
 }
 
@@ -701,6 +745,8 @@ struct Bufs {
   float *gh, *gmid, *gec, *gf1, *gf3, *geo, *geq, *gek, *gev, *Dq;
   float* part;     // split-K partials of the per-position products
   int64_t part_n;  // its floats
+  // row-concatenated copies of each layer's [Wq; Wk; Wv] and [W1; W3] (one launch per group)
+  std::vector<float*> qkv_e, w13_e, qkv_d, w13_d;
 };
 
 void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
@@ -743,8 +789,16 @@ void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
   u.gu = A.f((int64_t)B * d); u.carry = A.f((int64_t)B * d); u.greg = A.f((int64_t)B * d);
   u.gh = A.f(M * d); u.gmid = A.f(M * d); u.gec = A.f(M * d); u.gf1 = A.f(M * f); u.gf3 = A.f(M * f);
   u.geo = A.f(M * hd); u.geq = A.f(M * hd); u.gek = A.f(M * hd); u.gev = A.f(M * hd); u.Dq = A.f(M * H);
-  u.part_n = (int64_t)kMaxSplits * B * std::max({d, hd, f, 2 * d, (int64_t)c.vocab});
+  u.part_n = (int64_t)kMaxSplits * B * std::max({d, hd, f, 2 * d, 3 * hd, 2 * f, (int64_t)c.vocab});
   u.part = A.f(u.part_n);
+  for (int l = 0; l < c.L_E; ++l) {
+    u.qkv_e.push_back(A.f(3 * hd * d));
+    u.w13_e.push_back(A.f(2 * f * d));
+  }
+  for (int l = 0; l < c.L_D; ++l) {
+    u.qkv_d.push_back(c.share_enc_dec ? u.qkv_e[l] : A.f(3 * hd * d));
+    u.w13_d.push_back(c.share_enc_dec ? u.w13_e[l] : A.f(2 * f * d));
+  }
 }
 
 // Pointers of position t (B rows) of decoder layer l.
@@ -790,6 +844,19 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
 
   for (auto& kv : Gm) fill(c, kv.second.first, kv.second.second, 0.f);
   if (T <= 0 || B <= 0) return c.err;
+  {
+    const int64_t qn = (int64_t)hd * d, fn = (int64_t)f * d;
+    auto cat = [&](const std::string& pre, float* qkv, float* w13) {
+      add(c, qn, w(pre + "wq"), nullptr, qkv);
+      add(c, qn, w(pre + "wk"), nullptr, qkv + qn);
+      add(c, qn, w(pre + "wv"), nullptr, qkv + 2 * qn);
+      add(c, fn, w(pre + "w1"), nullptr, w13);
+      add(c, fn, w(pre + "w3"), nullptr, w13 + fn);
+    };
+    for (int l = 0; l < cf.L_E; ++l) cat("enc." + std::to_string(l) + ".", u.qkv_e[l], u.w13_e[l]);
+    if (!cf.share_enc_dec)
+      for (int l = 0; l < cf.L_D; ++l) cat("dec." + std::to_string(l) + ".", u.qkv_d[l], u.w13_d[l]);
+  }
 
   // position t's rows: R0 in every-position buffers, Rs in per-position ones
   auto step = [&](int l, int t) {
@@ -812,16 +879,19 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   auto enc_fwd = [&](int l) {
     EncBuf& e = u.enc[ck ? 0 : l];
     rms_fwd(c, M, d, u.eh[l], w(E(l, "n1")), eps, e.a, e.rs1);
-    lin(c, M, e.a, d, w(E(l, "wq")), d, hd, e.q, nullptr);
-    lin(c, M, e.a, d, w(E(l, "wk")), d, hd, e.k, nullptr);
-    lin(c, M, e.a, d, w(E(l, "wv")), d, hd, e.v, nullptr);
+    {
+      float* y[3] = {e.q, e.k, e.v};
+      lin_n(c, M, e.a, d, u.qkv_e[l], hd, 3, y);
+    }
     rope(c, M, H, dh, e.q, 1, B, base, 1.f);
     rope(c, M, H, dh, e.k, 1, B, base, 1.f);
     attn_fwd(c, M, B, 0, NOWIN, H, dh, e.q, e.k, e.v, e.o, e.lse);
     lin(c, M, e.o, hd, w(E(l, "wo")), hd, d, e.mid, u.eh[l]);
     rms_fwd(c, M, d, e.mid, w(E(l, "n2")), eps, e.c, e.rs2);
-    lin(c, M, e.c, d, w(E(l, "w1")), d, f, e.f1, nullptr);
-    lin(c, M, e.c, d, w(E(l, "w3")), d, f, e.f3, nullptr);
+    {
+      float* y[2] = {e.f1, e.f3};
+      lin_n(c, M, e.c, d, u.w13_e[l], f, 2, y);
+    }
     g_swiglu_fwd<<<blocks((int64_t)M * f), 256, 0, c.st>>>((int64_t)M * f, e.f1, e.f3, e.g);
     c.check();
     lin(c, M, e.g, f, w(E(l, "w2")), f, d, u.eh[l + 1], e.mid);
@@ -852,8 +922,11 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     float* uu = cf.L_D > 0 ? u.dec[0].zin + R0 * d : u.S + R0 * d;
     float* r = mrow(u.mr, t, d);
     rms_fwd(c, B, d, u.msrc + R0 * d, w("merge.ns"), eps, r, mrow(u.mrs, t, 1));
-    lin(c, B, et, d, w("merge.wg"), 2 * d, d, u.tBd, nullptr);
-    lin(c, B, r, d, w("merge.wg") + d, 2 * d, d, u.tBd, u.tBd);
+    {
+      Seg sg;   // W_g [e_t ; r] in one product (k over the two inputs)
+      sg.a[0] = et; sg.a[1] = r; sg.kseg = d;
+      gemm(c, B, d, 2 * d, et, d, true, w("merge.wg"), 2 * d, true, u.tBd, d, nullptr, false, sg);
+    }
     lin(c, B, r, d, w("merge.ws"), d, d, mrow(u.sr, t, d), nullptr);
     g_merge_fwd<<<blocks(Bd), 256, 0, c.st>>>(B, d, et, u.tBd, w("merge.bg"), mrow(u.sr, t, d), alpha,
                                                mrow(u.gate, t, d), uu);
@@ -865,13 +938,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     const DecBuf& D = u.dec[l];
     const Step s = step(l, t);
     rms_fwd(c, B, d, s.zin, w(Dn(l, "m1")), eps, s.a, s.rs1);
-    lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr);
-    rope(c, B, H, dh, s.q, t + 1, B, base, 1.f);
     if (with_kv) {
-      lin(c, B, s.a, d, w(Ds(l, "wk")), d, hd, s.k, nullptr);
-      lin(c, B, s.a, d, w(Ds(l, "wv")), d, hd, s.v, nullptr);
+      float* y[3] = {s.q, s.k, s.v};
+      lin_n(c, B, s.a, d, u.qkv_d[l], hd, 3, y);
       rope(c, B, H, dh, s.k, t + 1, B, base, 1.f);
+    } else {
+      lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr);
     }
+    rope(c, B, H, dh, s.q, t + 1, B, base, 1.f);
     attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1);
     lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin);
     rms_fwd(c, B, d, s.z1, w(Dn(l, "m2")), eps, s.b, s.rs2);
@@ -880,8 +954,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     attn_fwd(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[grp(l)], u.mv[grp(l)], s.ox, s.lse2);
     lin(c, B, s.ox, hd, w(Dn(l, "xo")), hd, d, s.z2, s.z1);
     rms_fwd(c, B, d, s.z2, w(Dn(l, "m3")), eps, s.c, s.rs3);
-    lin(c, B, s.c, d, w(Ds(l, "w1")), d, f, s.f1, nullptr);
-    lin(c, B, s.c, d, w(Ds(l, "w3")), d, f, s.f3, nullptr);
+    {
+      float* y[2] = {s.f1, s.f3};
+      lin_n(c, B, s.c, d, u.w13_d[l], f, 2, y);
+    }
     g_swiglu_fwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, s.f1, s.f3, s.g);
     c.check();
     return s;
@@ -975,8 +1051,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       lin_t(c, B, s.gz3, d, w(Ds(l, "w2")), f, f, u.tBf, nullptr);
       g_swiglu_bwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, u.tBf, s.f1, s.f3, s.gf1, s.gf3);
       c.check();
-      lin_t(c, B, s.gf1, f, w(Ds(l, "w1")), d, d, s.gdc, nullptr);
-      lin_t(c, B, s.gf3, f, w(Ds(l, "w3")), d, d, s.gdc, s.gdc);
+      {
+        const float* gy[2] = {s.gf1, s.gf3};
+        lin_tk(c, B, gy, f, 2, u.w13_d[l], d, s.gdc, nullptr);
+      }
       rms_bwd(c, B, d, s.gdc, s.z2, s.rs3, w(Dn(l, "m3")), s.gz3, s.gz2);
       // cross-attention over memory rows 1..t
       const int gi = grp(l);
@@ -991,9 +1069,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv);
       rope(c, B, H, dh, s.gq, t + 1, B, base, -1.f);
       rope(c, B, H, dh, s.gk, t + 1, B, base, -1.f);
-      lin_t(c, B, s.gq, hd, w(Ds(l, "wq")), d, d, s.gda, nullptr);
-      lin_t(c, B, s.gk, hd, w(Ds(l, "wk")), d, d, s.gda, s.gda);
-      lin_t(c, B, s.gv, hd, w(Ds(l, "wv")), d, d, s.gda, s.gda);
+      {
+        const float* gy[3] = {s.gq, s.gk, s.gv};
+        lin_tk(c, B, gy, hd, 3, u.qkv_d[l], d, s.gda, nullptr);
+      }
       float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
       rms_bwd(c, B, d, s.gda, s.zin, s.rs1, w(Dn(l, "m1")), s.gz1, gin);
       if (ck) layer_wgrad(l, s, B);
@@ -1005,8 +1084,11 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       float* gmr = mrow(u.gmr, t, d);
       g_merge_bwd<<<blocks(Bd), 256, 0, c.st>>>(Bd, u.gu, mrow(u.gate, t, d), mrow(u.sr, t, d), alpha, ggp, gsr);
       c.check();
-      lin_t(c, B, ggp, d, w("merge.wg"), 2 * d, d, get, u.gu);
-      lin_t(c, B, ggp, d, w("merge.wg") + d, 2 * d, d, gmr, nullptr);
+      {
+        Seg sg;   // [de_t | dr] = ggp . W_g in one product (n over the two outputs); de_t adds du
+        sg.c[0] = get; sg.c[1] = gmr; sg.r[0] = u.gu; sg.nseg = d;
+        gemm(c, B, 2 * d, d, ggp, d, true, w("merge.wg"), 2 * d, false, get, d, nullptr, false, sg);
+      }
       lin_t(c, B, gsr, d, w("merge.ws"), d, d, gmr, gmr);
       if (cf.variant == RLT_V1)
         rms_bwd(c, B, d, gmr, u.msrc + o, mrow(u.mrs, t, 1), w("merge.ns"), nullptr, u.carry);
@@ -1044,8 +1126,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     g_swiglu_bwd<<<blocks((int64_t)M * f), 256, 0, c.st>>>((int64_t)M * f, u.gf1, e.f1, e.f3, u.gf1, u.gf3);
     c.check();
     wgrad(c, M, gh, d, e.g, f, g(E(l, "w2")), f);
-    lin_t(c, M, u.gf1, f, w(E(l, "w1")), d, d, u.gec, nullptr);
-    lin_t(c, M, u.gf3, f, w(E(l, "w3")), d, d, u.gec, u.gec);
+    {
+      const float* gy[2] = {u.gf1, u.gf3};
+      lin_tk(c, M, gy, f, 2, u.w13_e[l], d, u.gec, nullptr);
+    }
     wgrad(c, M, u.gf1, f, e.c, d, g(E(l, "w1")), d);
     wgrad(c, M, u.gf3, f, e.c, d, g(E(l, "w3")), d);
     colsum(c, M, d, u.gec, e.mid, e.rs2, g(E(l, "n2")));
@@ -1056,9 +1140,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     attn_bwd_kv(c, B, T, NOWIN, H, dh, e.q, e.k, e.v, e.lse, u.Dq, u.geo, u.gek, u.gev);
     rope(c, M, H, dh, u.geq, 1, B, base, -1.f);
     rope(c, M, H, dh, u.gek, 1, B, base, -1.f);
-    lin_t(c, M, u.geq, hd, w(E(l, "wq")), d, d, u.gec, nullptr);
-    lin_t(c, M, u.gek, hd, w(E(l, "wk")), d, d, u.gec, u.gec);
-    lin_t(c, M, u.gev, hd, w(E(l, "wv")), d, d, u.gec, u.gec);
+    {
+      const float* gy[3] = {u.geq, u.gek, u.gev};
+      lin_tk(c, M, gy, hd, 3, u.qkv_e[l], d, u.gec, nullptr);
+    }
     wgrad(c, M, u.geq, hd, e.a, d, g(E(l, "wq")), d);
     wgrad(c, M, u.gek, hd, e.a, d, g(E(l, "wk")), d);
     wgrad(c, M, u.gev, hd, e.a, d, g(E(l, "wv")), d);

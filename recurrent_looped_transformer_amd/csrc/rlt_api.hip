@@ -1609,6 +1609,8 @@ int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weig
     }
     for (auto& kv : man)
       if (!G.count(kv.first)) fail(RLT_ERR_INVALID_ARG, "missing gradient " + kv.first);
+    for (auto& kv : W)   // the products read weights as 16-byte vectors
+      if (reinterpret_cast<uintptr_t>(kv.second) & 15) fail(RLT_ERR_INVALID_ARG, "weight " + kv.first + " not 16-byte aligned");
     hipError_t e = replay_grad(*cfg, W, G, tokens, B, T, dlogprob, logprob, workspace, checkpoint != 0, stream);
     if (e != hipSuccess) fail(RLT_ERR_HIP, std::string("replay gradient: ") + hipGetErrorString(e));
   });
