@@ -18,7 +18,9 @@
 
 namespace rlt {
 
-template <typename T, int DH>
+// SPLIT: this block takes the keys [z * split_keys, (z + 1) * split_keys) of its range
+// (z = blockIdx.z) and writes its partial softmax sums to split_ws for attn_combine_k.
+template <typename T, int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int G = DH / VEC;              // lanes per key
@@ -33,9 +35,8 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   const int lo = a.window > 0 ? max(1, pos - a.window + 1) : 1;
   const int n = pos - lo + 1;
   const int tid = threadIdx.x, gi = tid / G, gl = tid % G;
-  // split over keys (gridDim.z > 1): this block takes keys [jb, je) of the n
-  const int jb = gridDim.z > 1 ? (int)blockIdx.z * a.split_keys : 0;
-  const int je = gridDim.z > 1 ? min(n, jb + a.split_keys) : n;
+  const int jb = SPLIT ? (int)blockIdx.z * a.split_keys : 0;
+  const int je = SPLIT ? min(n, jb + a.split_keys) : n;
 
   // the query's raw bits now, unpacked after the first keys are requested (no wait in between)
   const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)row * a.ldq + h * DH + gl * VEC;
@@ -117,24 +118,24 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     float M = -INFINITY;
     for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, ml[2 * gg]);
     float s = 0.f, den = 0.f;
-    if (M != -INFINITY) {   // a split block past its row's last key has no keys
+    if (!SPLIT || M != -INFINITY) {   // a split block past its row's last key has no keys
       for (int gg = 0; gg < NG; ++gg) {
         const float w = __expf(ml[2 * gg] - M);
         den += w * ml[2 * gg + 1];
         s += w * part[gg * DH + tid];
       }
     }
-    if (gridDim.z > 1) {
+    if constexpr (SPLIT) {
       float* w = a.split_ws + (((int64_t)row * a.H + h) * gridDim.z + blockIdx.z) * (DH + 2);
       w[tid] = s;
       if (tid == 0) {
         w[DH] = M;
         w[DH + 1] = den;
       }
-      return;
+    } else {
+      T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
+      store_act<T>(op, a.out_split, s / den);
     }
-    T* op = reinterpret_cast<T*>(a.out) + (int64_t)row * a.ldo + h * DH + tid;
-    store_act<T>(op, a.out_split, s / den);
   }
 }
 
@@ -179,10 +180,10 @@ static void launch_attn(const AttnArgs& a0, hipStream_t st) {
     S = (a.n_max + a.split_keys - 1) / a.split_keys;
   }
   if (S > 1) {
-    hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq, S), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_decode_k<T, DH, true>), dim3(a.H, a.B * a.nq, S), dim3(256), 0, st, a);
     hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
   } else {
-    hipLaunchKernelGGL((attn_decode_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_decode_k<T, DH, false>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
   }
 }
 
