@@ -337,6 +337,189 @@ def ragged_bench(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+GEN_METRIC = "generation tokens/sec with on-device behaviour sampling and recorded log-probabilities; % of HBM roofline"
+SNAP_METRIC = "prefix snapshot + restore bandwidth (device and pinned-host copies); % of HBM roofline"
+
+
+def _events(torch, stream, fn, reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def generate_bench(args, cfg):
+    """rlt_generate after a prefill of `base` positions: n draws per call (temperature 1), each
+    consumed before the next; plus the sampler kernel alone on the same logits shape."""
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import make_logits, make_params, make_tokens
+    B = cfg.batch
+    base = args.ragged_base or cfg.seq_len
+    n = 32
+    K, Wm = args.steps, args.warmup
+    max_len = base + (K + Wm) * n + 1
+    P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+    torch.cuda.set_device(0)
+    model = rlt.Model(cfg, P)
+    del P
+    toks = make_tokens(cfg, batch=B, length=base)
+    x = torch.as_tensor(np.ascontiguousarray(toks)).cuda()
+    st = model.state(B, max_len, keep_encoder_cache=True)
+    rlt.rlt_encode(model.h, st, x[:, :base - 1].contiguous())
+    rlt.rlt_decode_scan(model.h, st, base - 1)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill of {base - 1} positions done", flush=True)
+    stream = torch.cuda.current_stream()
+    first = x[:, base - 1].contiguous()
+    out_t = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    out_lp = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    calls = [0]
+    start_pos = base
+
+    def gen():
+        rlt.rlt_generate(model.h, st, first, n, 1.0, 1234, calls[0] * n, out_t, out_lp)
+        first.copy_(out_t[:, n - 1])
+        calls[0] += 1
+
+    for _ in range(Wm):
+        gen()
+    p0 = start_pos + Wm * n
+    ms = _events(torch, stream, gen, K) / n          # per generated token of the batch
+    positions = [p0 + i for i in range(K * n)]
+    by = float(np.mean([gen_step_bytes(cfg, [p] * B) for p in positions])) + B * cfg.vocab * 4 * 2
+    model.close()
+    # the sampler alone: B rows of V logits
+    lg = torch.as_tensor(make_logits(B, cfg.vocab, seed=7)).cuda()
+    tk = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    step = [0]
+
+    def samp():
+        rlt.rlt_sample(lg, 1.0, 99, step[0], tk, lp)
+        step[0] += 1
+
+    for _ in range(3):
+        samp()
+    us_s = _events(torch, stream, samp, 200) * 1e3
+    sb = B * cfg.vocab * 4
+    ach = by / (ms / 1e3) / 1e9
+    out = {
+        "metric": GEN_METRIC, "value": B / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16", "fp16x2": "f16x2"}[cfg.path_dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} generation (rlt_generate, {n} draws per call, temperature 1) after a "
+                               f"{base - 1}-position prefill, B={B}", "batch": B, "prefill": base - 1,
+                   "draws_per_call": n, "vocab": cfg.vocab},
+        "sampler": {"us_per_call": us_s, "rows": B, "vocab": cfg.vocab, "logit_bytes": sb,
+                    "GBs": sb / (us_s / 1e6) / 1e9},
+        "roofline": {"bound": "hbm", "kernel": "generation step (encoder step + transition + logits + draw)",
+                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": by},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+        from oracle.rlt_sampler import sample as oracle_sample
+        lgh = make_logits(B, cfg.vocab, seed=7)
+        reps = 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < 10.0:
+            oracle_sample(lgh, 1.0, 99, reps)
+            reps += 1
+        dt = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": reps * B / dt, "unit": "draws/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"{reps} sampler calls of {B} rows x {cfg.vocab} logits (Philox4x64-10 "
+                                         f"uniforms, Gumbel-max, float64 log mu), {dt:.1f} s; the GPU's sampler "
+                                         f"alone: {B / (us_s / 1e6):.0f} draws/s"}
+    print(json.dumps(out), flush=True)
+
+
+def snapshot_bench(args, cfg):
+    """Snapshot and restore of a state after a prefill of `base` positions (encoder cache kept):
+    to / from a device buffer and a pinned host buffer. Algorithmic bytes: the payload read
+    and written once per copy."""
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import make_params, make_tokens
+    B = cfg.batch
+    base = args.ragged_base or 512
+    P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+    torch.cuda.set_device(0)
+    model = rlt.Model(cfg, P)
+    del P
+    x = torch.as_tensor(np.ascontiguousarray(make_tokens(cfg, batch=B, length=base))).cuda()
+    st = model.state(B, base, keep_encoder_cache=True)
+    rlt.rlt_encode(model.h, st, x)
+    rlt.rlt_decode_scan(model.h, st, base)
+    nbytes = rlt.rlt_snapshot_size(model.h, st)
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hbuf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    info = [None]
+
+    def snap_d():
+        info[0] = rlt.rlt_snapshot(model.h, st, dbuf)
+
+    def rest_d():
+        rlt.rlt_restore(model.h, st, info[0], dbuf)
+
+    def snap_h():
+        info[0] = rlt.rlt_snapshot(model.h, st, hbuf)
+
+    def rest_h():
+        rlt.rlt_restore(model.h, st, info[0], hbuf)
+
+    res = {}
+    for name, fn in (("snapshot_device", snap_d), ("restore_device", rest_d), ("snapshot_host", snap_h),
+                     ("restore_host", rest_h)):
+        fn()
+        ms = _events(torch, stream, fn, args.steps)
+        res[name] = {"ms": ms, "GBs": nbytes / (ms / 1e3) / 1e9}
+        print(f"[bench] {name}: {ms:.3f} ms", flush=True)
+    model.close()
+    ms = res["snapshot_device"]["ms"]
+    ach = 2 * nbytes / (ms / 1e3) / 1e9
+    out = {
+        "metric": SNAP_METRIC, "value": nbytes / (ms / 1e3) / 1e9, "unit": "GB/s (payload, device snapshot)",
+        "n_gpus": 1, "steps": args.steps, "warmup": 1, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16", "fp16x2": "f16x2"}[cfg.path_dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} state after a {base}-position prefill, B={B}, encoder cache kept",
+                   "batch": B, "positions": base, "payload_bytes": nbytes},
+        "copies": res,
+        "roofline": {"bound": "hbm", "kernel": "device snapshot (payload read + written once)",
+                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": 2 * nbytes},
+    }
+    if not args.no_cpu:
+        import copy
+        from oracle import Oracle
+        cs = cfg.replace(batch=1)
+        o = Oracle(cs, make_params(cs, bf16_storage=cs.d >= 4096), np.float32)
+        ost = o.new_state(1)
+        o.encoder_chunk(ost, make_tokens(cs, batch=1, length=min(base, 64)))
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < 5.0:
+            copy.deepcopy(ost)
+            reps += 1
+        dt = time.perf_counter() - t1
+        cache = sum(a.nbytes for l in ost.enc_k + ost.enc_v for a in l) + \
+            sum(a.nbytes for g in ost.mem_k + ost.mem_v for a in g)
+        out["cpu_baseline"] = {"value": cache * reps / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"deep copies of the oracle's state of 1 row after {min(base, 64)} "
+                                         f"encoded positions ({cache / 1e6:.1f} MB of caches and memory), "
+                                         f"{reps} copies in {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, P, tokens, sample_B: int):
     from threadpoolctl import threadpool_info
     from oracle import Oracle
@@ -374,6 +557,10 @@ def main():
                          "t = 32 and the prompt length of each shape; prints one JSON line per point")
     ap.add_argument("--sweep-shapes", default="algo_bf16,medium_lm,paper_shared")
     ap.add_argument("--sweep-batches", default="1,2,4,8")
+    ap.add_argument("--generate", action="store_true",
+                    help="time rlt_generate (on-device sampling with recorded log-probabilities) and the sampler")
+    ap.add_argument("--snapshot", action="store_true",
+                    help="time prefix snapshot / restore to device and pinned-host buffers")
     ap.add_argument("--ragged", action="store_true",
                     help="time generation steps of rows at unequal positions (continuous batching)")
     ap.add_argument("--ragged-base", type=int, default=0)
@@ -419,6 +606,12 @@ def main():
         return
     if args.ragged:
         ragged_bench(args, cfg)
+        return
+    if args.generate:
+        generate_bench(args, cfg)
+        return
+    if args.snapshot:
+        snapshot_bench(args, cfg)
         return
     B, T = cfg.batch, cfg.seq_len
     P = make_params(cfg)

@@ -11,9 +11,10 @@
 // (seed, step, b, j), so a sequence of draws does not depend on how the calls are split.
 // tau = 0 is greedy decoding (lowest index on ties, log mu = 0).
 //
-// One workgroup per row; scores and the log-sum-exp in float64 (a row is tens of
-// thousands of entries: the kernel is a few microseconds whatever its precision). The
-// replay's next-token log-probability (logprob_k) uses the same log-sum-exp routine.
+// One workgroup of 1024 threads per row; scores and the log-sum-exp in float64. The cost is
+// the float64 Gumbel noise (two logarithms per id) and exponentials: a row of 32000 ids is
+// about 60 of each per thread. The replay's next-token log-probability (logprob_k) uses the
+// same log-sum-exp routine, so both evaluate log softmax identically.
 #include <climits>
 
 #include "common.hpp"
@@ -44,7 +45,7 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
   }
 }
 
-constexpr int kSampleThreads = 256;
+constexpr int kSampleThreads = 1024;
 
 // (score, index) with the larger score winning and the lower index breaking ties
 __device__ __forceinline__ void best_merge(double& y, int& j, double y2, int j2) {
@@ -56,7 +57,7 @@ __device__ __forceinline__ void best_merge(double& y, int& j, double y2, int j2)
 
 // Row log-sum-exp of z_j = x_j / div in float64, shared by the sampler and the replay's
 // log-probability so that both evaluate log softmax with the same operations in the same
-// order: thread t visits j = 4 jb .. 4 jb + 3 for jb = t, t + 256, ...; max, then the sum of
+// order: thread t visits j = 4 jb .. 4 jb + 3 for jb = t, t + 1024, ...; max, then the sum of
 // exp(z - max), each reduced over the block in a fixed tree.
 __device__ __forceinline__ double block_max_d(double v, double* red) {
   red[threadIdx.x] = v;
