@@ -228,10 +228,16 @@ int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const
  * temperature 0 is greedy decoding (lowest index on ties; logprob 0, a point mass). No
  * truncated sampling (top-k / top-p) is offered: [R] §6.2 notes that it breaks the support
  * condition p_Theta << mu of exact importance sampling.
- * tokens: device int32 [rows]. Errors: INVALID_ARG (null, rows < 0, vocab < 1, ld < vocab,
- * temperature negative or not finite). Token ids are in [0, vocab). */
+ * tokens: device int32 [rows]. workspace (nullable): device memory of at least
+ * rlt_sample_workspace bytes, 16-byte aligned; with it the 4096-id chunks of every row are
+ * evaluated by separate workgroups side by side (the results are the same bit for bit).
+ * Errors: INVALID_ARG (null, rows < 0, vocab < 1, ld < vocab, temperature negative or not
+ * finite, workspace too small or misaligned), UNSUPPORTED (vocab > 2^20). Token ids are in
+ * [0, vocab). */
+int rlt_sample_workspace(int rows, int vocab, int64_t* bytes);
 int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
-               uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream);
+               uint64_t step, int32_t* tokens, float* logprob, void* workspace, int64_t workspace_bytes,
+               hipStream_t stream);
 
 /* Generation F.2 with on-device behaviour sampling ([S] appendix F.2; [R] §6.2 Figure 4):
  * consume `first` (device int32 [B], the last emitted token of every row: it is consumed

@@ -145,7 +145,10 @@ void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, floa
 // counter (j / 4, b, step, 0)); lp[b * lp_ld] (nullable) = log of its probability;
 // next[b] (nullable) = the token again. temperature 0: greedy, lp = 0.
 void sample_rows(const float* logits, int64_t ld, int rows, int V, float temperature, uint64_t seed, uint64_t step,
-                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st);
+                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st,
+                 void* ws = nullptr);
+// bytes of the optional sample_rows workspace (chunk statistics of every row) for rows x V
+int64_t sample_workspace_bytes(int rows, int V);
 // ratio[i] = exp(lp_cur[i] - lp_beh[i]) (float64 inside)
 void importance_ratio(const float* lp_cur, const float* lp_beh, int64_t n, float* ratio, hipStream_t st);
 // pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind.

@@ -11,10 +11,12 @@
 // (seed, step, b, j), so a sequence of draws does not depend on how the calls are split.
 // tau = 0 is greedy decoding (lowest index on ties, log mu = 0).
 //
-// One workgroup of 1024 threads per row; scores and the log-sum-exp in float64. The cost is
-// the float64 Gumbel noise (two logarithms per id) and exponentials: a row of 32000 ids is
-// about 60 of each per thread. The replay's next-token log-probability (logprob_k) uses the
-// same log-sum-exp routine, so both evaluate log softmax identically.
+// Scores and the log-sum-exp in float64, in chunks of 4096 ids (one 1024-thread pass each)
+// combined in a fixed order: a workgroup per row walks its chunks (rlt_sample), or a
+// workgroup per (row, chunk) and a combining pass run them side by side (rlt_generate,
+// which has a workspace), with the same values bit for bit. The cost is the float64 Gumbel
+// noise (two logarithms per id). The replay's next-token log-probability (logprob_k) uses
+// the same chunked log-sum-exp, so both evaluate log softmax identically.
 #include <climits>
 
 #include "common.hpp"
@@ -55,10 +57,7 @@ __device__ __forceinline__ void best_merge(double& y, int& j, double y2, int j2)
   }
 }
 
-// Row log-sum-exp of z_j = x_j / div in float64, shared by the sampler and the replay's
-// log-probability so that both evaluate log softmax with the same operations in the same
-// order: thread t visits j = 4 jb .. 4 jb + 3 for jb = t, t + 1024, ...; max, then the sum of
-// exp(z - max), each reduced over the block in a fixed tree.
+// Block-wide float64 max and sum over a fixed tree.
 __device__ __forceinline__ double block_max_d(double v, double* red) {
   red[threadIdx.x] = v;
   __syncthreads();
@@ -81,77 +80,144 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
   __syncthreads();
   return r;
 }
-__device__ __forceinline__ double row_sum_exp(const float* x, int V, double div, double mx, double* red) {
-  double s = 0.0;
-  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads)
+// Log-softmax and the draw are defined over chunks of kChunk = 4 * kSampleThreads ids:
+// chunk c holds ids [c * kChunk, (c + 1) * kChunk), thread t its group 4 (c * kSampleThreads
+// + t) .. + 3. Per chunk (block trees, fixed order): m_c = max z, s_c = sum exp(z - m_c), and
+// the best (score, id). Over chunks in ascending order: M = max m_c, S = sum e^(m_c - M) s_c,
+// the best (score, id) with ties to the lower id; log softmax(z)_j = z_j - (M + log S).
+// Whether one workgroup walks the chunks or a workgroup per chunk computes them, the values
+// are the same bit for bit.
+constexpr int kChunk = 4 * kSampleThreads;
+constexpr int kMaxChunks = 256;   // vocabularies up to 2^20 ids
+
+struct ChunkStat {
+  double m, s, best;
+  int bj;
+};
+
+// Chunk c of the row x (all threads of the block; the result is valid in every thread).
+// scores: also the draw's best (score, id): z itself when greedy, else z + Gumbel noise.
+__device__ ChunkStat chunk_stat(const float* __restrict__ x, int V, int c, double div, bool scores, bool greedy,
+                                uint64_t seed, uint64_t step, int b, double* red, int* redj) {
+  const int jb = c * kSampleThreads + threadIdx.x;
+  double z[4];
+  double mx = -INFINITY, best = -INFINITY;
+  int bj = INT_MAX;
+  uint64_t cw[4] = {(uint64_t)jb, (uint64_t)b, step, 0ull};
+  if (scores && !greedy) philox4x64_10(cw, seed, 0ull);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = 4 * jb + w;
-      if (j < V) s += exp((double)x[j] / div - mx);
+  for (int w = 0; w < 4; ++w) {
+    const int j = 4 * jb + w;
+    z[w] = -INFINITY;
+    if (j < V) {
+      z[w] = (double)x[j] / div;
+      mx = fmax(mx, z[w]);
+      if (scores) {
+        if (greedy) {
+          best_merge(best, bj, z[w], j);
+        } else {
+          const double u = ((double)(cw[w] >> 11) + 0.5) * 0x1p-53;
+          best_merge(best, bj, z[w] - log(-log(u)), j);
+        }
+      }
     }
-  return block_sum_d(s, red);
+  }
+  ChunkStat r;
+  r.m = block_max_d(mx, red);
+  double sl = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (4 * jb + w < V) sl += exp(z[w] - r.m);
+  r.s = block_sum_d(sl, red);
+  r.best = -INFINITY;
+  r.bj = INT_MAX;
+  if (scores) {
+    red[threadIdx.x] = best;
+    redj[threadIdx.x] = bj;
+    __syncthreads();
+    for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
+      if (threadIdx.x < h) {
+        double y = red[threadIdx.x];
+        int jj = redj[threadIdx.x];
+        best_merge(y, jj, red[threadIdx.x + h], redj[threadIdx.x + h]);
+        red[threadIdx.x] = y;
+        redj[threadIdx.x] = jj;
+      }
+      __syncthreads();
+    }
+    r.best = red[0];
+    r.bj = redj[0];
+    __syncthreads();
+  }
+  return r;
 }
 
+// M + log S and the best id over nc chunk statistics (one thread)
+__device__ void combine_chunks(const ChunkStat* st, int nc, double& lse, int& bj) {
+  double M = -INFINITY, best = -INFINITY;
+  bj = INT_MAX;
+  for (int c = 0; c < nc; ++c) {
+    M = fmax(M, st[c].m);
+    best_merge(best, bj, st[c].best, st[c].bj);
+  }
+  double S = 0.0;
+  for (int c = 0; c < nc; ++c) S += exp(st[c].m - M) * st[c].s;
+  lse = M + log(S);
+}
+
+// One workgroup per row, walking the chunks.
 __global__ __launch_bounds__(kSampleThreads) void sample_k(const float* __restrict__ logits, int64_t ld, int V,
                                                            float tau, uint64_t seed, uint64_t step, int32_t* tok,
                                                            int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next) {
   __shared__ double red[kSampleThreads];
   __shared__ int redj[kSampleThreads];
+  __shared__ ChunkStat st[kMaxChunks];
   const int b = blockIdx.x;
   const float* x = logits + (int64_t)b * ld;
   const bool greedy = !(tau > 0.f);
   const double div = greedy ? 1.0 : (double)tau;
-  double best = -INFINITY, mx = -INFINITY;
-  int bj = INT_MAX;
-  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads) {
-    uint64_t c[4] = {(uint64_t)jb, (uint64_t)b, step, 0ull};
-    if (!greedy) philox4x64_10(c, seed, 0ull);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = 4 * jb + w;
-      if (j < V) {
-        const double z = (double)x[j] / div;
-        mx = fmax(mx, z);
-        if (greedy) {
-          best_merge(best, bj, z, j);
-        } else {
-          const double u = ((double)(c[w] >> 11) + 0.5) * 0x1p-53;
-          best_merge(best, bj, z - log(-log(u)), j);
-        }
-      }
-    }
+  const int nc = (V + kChunk - 1) / kChunk;
+  for (int c = 0; c < nc; ++c) {
+    const ChunkStat r = chunk_stat(x, V, c, div, true, greedy, seed, step, b, red, redj);
+    if (threadIdx.x == 0) st[c] = r;
   }
-  // the draw: block argmax of the scores
-  red[threadIdx.x] = best;
-  redj[threadIdx.x] = bj;
   __syncthreads();
-  for (int h = kSampleThreads / 2; h > 0; h >>= 1) {
-    if (threadIdx.x < h) {
-      double y = red[threadIdx.x];
-      int j = redj[threadIdx.x];
-      best_merge(y, j, red[threadIdx.x + h], redj[threadIdx.x + h]);
-      red[threadIdx.x] = y;
-      redj[threadIdx.x] = j;
-    }
-    __syncthreads();
-  }
-  const int j = redj[0];
-  __syncthreads();
-  if (greedy) {
-    if (threadIdx.x == 0) {
-      tok[(int64_t)b * tok_ld] = j;
-      if (next) next[b] = j;
-      if (lp) lp[(int64_t)b * lp_ld] = 0.f;
-    }
-    return;
-  }
-  const double M = block_max_d(mx, red);
-  const double S = row_sum_exp(x, V, div, M, red);
   if (threadIdx.x == 0) {
+    double lse;
+    int j;
+    combine_chunks(st, nc, lse, j);
     tok[(int64_t)b * tok_ld] = j;
     if (next) next[b] = j;
-    if (lp) lp[(int64_t)b * lp_ld] = (float)((double)x[j] / div - (M + log(S)));
+    if (lp) lp[(int64_t)b * lp_ld] = greedy ? 0.f : (float)((double)x[j] / div - lse);
   }
+}
+
+// A workgroup per (row, chunk) writing its statistics to ws[b][c]; sample_combine_k finishes.
+__global__ __launch_bounds__(kSampleThreads) void sample_chunks_k(const float* __restrict__ logits, int64_t ld,
+                                                                  int V, float tau, uint64_t seed, uint64_t step,
+                                                                  ChunkStat* __restrict__ ws) {
+  __shared__ double red[kSampleThreads];
+  __shared__ int redj[kSampleThreads];
+  const int b = blockIdx.x, c = blockIdx.y;
+  const bool greedy = !(tau > 0.f);
+  const ChunkStat r = chunk_stat(logits + (int64_t)b * ld, V, c, greedy ? 1.0 : (double)tau, true, greedy, seed,
+                                 step, b, red, redj);
+  if (threadIdx.x == 0) ws[(int64_t)b * gridDim.y + c] = r;
+}
+
+__global__ void sample_combine_k(const float* __restrict__ logits, int64_t ld, int V, int nc, float tau,
+                                 const ChunkStat* __restrict__ ws, int rows, int32_t* tok, int64_t tok_ld, float* lp,
+                                 int64_t lp_ld, int32_t* next) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= rows) return;
+  const bool greedy = !(tau > 0.f);
+  const double div = greedy ? 1.0 : (double)tau;
+  double lse;
+  int j;
+  combine_chunks(ws + (int64_t)b * nc, nc, lse, j);
+  tok[(int64_t)b * tok_ld] = j;
+  if (next) next[b] = j;
+  if (lp) lp[(int64_t)b * lp_ld] = greedy ? 0.f : (float)((double)logits[(int64_t)b * ld + j] / div - lse);
 }
 
 // log p(tok | logits row) = z_tok - log sum exp(z), z = logits (the sampler's arithmetic at
@@ -161,20 +227,22 @@ __global__ __launch_bounds__(kSampleThreads) void logprob_k(const float* __restr
                                                             const int32_t* __restrict__ tok, RowMap tm,
                                                             float* __restrict__ out, RowMap om, int V) {
   __shared__ double red[kSampleThreads];
+  __shared__ int redj[kSampleThreads];
+  __shared__ ChunkStat st[kMaxChunks];
   const int r = blockIdx.x;
   const float* x = logits + lm.off(r);
-  double mx = -INFINITY;
-  for (int jb = threadIdx.x; jb < (V + 3) / 4; jb += kSampleThreads)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = 4 * jb + w;
-      if (j < V) mx = fmax(mx, (double)x[j] / 1.0);
-    }
-  const double M = block_max_d(mx, red);
-  const double S = row_sum_exp(x, V, 1.0, M, red);
+  const int nc = (V + kChunk - 1) / kChunk;
+  for (int c = 0; c < nc; ++c) {
+    const ChunkStat q = chunk_stat(x, V, c, 1.0, false, false, 0ull, 0ull, 0, red, redj);
+    if (threadIdx.x == 0) st[c] = q;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    double lse;
+    int j;
+    combine_chunks(st, nc, lse, j);
     const int t = tok[tm.off(r)];
-    out[om.off(r)] = t >= 0 ? (float)((double)x[t] / 1.0 - (M + log(S))) : 0.f;
+    out[om.off(r)] = t >= 0 ? (float)((double)x[t] / 1.0 - lse) : 0.f;
   }
 }
 
@@ -185,11 +253,24 @@ __global__ void ratio_k(const float* __restrict__ a, const float* __restrict__ b
 
 }  // namespace
 
+int64_t sample_workspace_bytes(int rows, int V) {
+  return (int64_t)rows * ((V + kChunk - 1) / kChunk) * (int64_t)sizeof(ChunkStat);
+}
+
 void sample_rows(const float* logits, int64_t ld, int rows, int V, float temperature, uint64_t seed, uint64_t step,
-                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st) {
+                 int32_t* tok, int64_t tok_ld, float* lp, int64_t lp_ld, int32_t* next, hipStream_t st, void* ws) {
   if (rows <= 0) return;
-  hipLaunchKernelGGL(sample_k, dim3(rows), dim3(kSampleThreads), 0, st, logits, ld, V, temperature, seed, step, tok,
-                     tok_ld, lp, lp_ld, next);
+  const int nc = (V + kChunk - 1) / kChunk;
+  if (ws && nc > 1) {
+    ChunkStat* w = static_cast<ChunkStat*>(ws);
+    hipLaunchKernelGGL(sample_chunks_k, dim3(rows, nc), dim3(kSampleThreads), 0, st, logits, ld, V, temperature, seed,
+                       step, w);
+    hipLaunchKernelGGL(sample_combine_k, dim3((rows + 63) / 64), dim3(64), 0, st, logits, ld, V, nc, temperature, w,
+                       rows, tok, tok_ld, lp, lp_ld, next);
+  } else {
+    hipLaunchKernelGGL(sample_k, dim3(rows), dim3(kSampleThreads), 0, st, logits, ld, V, temperature, seed, step, tok,
+                       tok_ld, lp, lp_ld, next);
+  }
 }
 
 void logprob(const float* logits, RowMap lm, const int32_t* tok, RowMap tm, float* out, RowMap om, int rows, int V,

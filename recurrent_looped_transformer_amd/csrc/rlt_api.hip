@@ -162,6 +162,7 @@ struct rlt_state {
   int32_t* rtok = nullptr;            // [B] tokens of the rows that move
   float* s_bak = nullptr;             // [B][d] s before a per-row step
   float* attn_ws = nullptr;           // [kMaxSlices][kAttnSplitBlocks][dh + 2] key-split partials
+  void* samp_ws = nullptr;            // chunk statistics of the generation sampler
   int* rp_host = nullptr;             // pinned [kStage][3][B] staging of rp_dev
   hipEvent_t rp_ev[kStage] = {};
   bool rp_used[kStage] = {};
@@ -186,6 +187,7 @@ void* dev_alloc(rlt_state* s, size_t bytes, int cls, int64_t logical = -1) {
 void validate_config(const rlt_config& c) {
   auto bad = [](const std::string& m) { fail(RLT_ERR_INVALID_ARG, "config: " + m); };
   if (c.vocab <= 0 || c.vocab % 4) bad("vocab must be a positive multiple of 4");
+  if (c.vocab > (1 << 20)) fail(RLT_ERR_UNSUPPORTED, "vocab > 2^20");
   if (c.d <= 0 || c.d % 64) bad("d must be a positive multiple of 64");
   if (c.n_heads <= 0 || c.d_head <= 0) bad("heads");
   if (c.d_head % 2) fail(RLT_ERR_UNSUPPORTED, "d_head must be even (rotary pairs)");
@@ -1210,6 +1212,7 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->rtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
       s->s_bak = (float*)dev_alloc(s, sizeof(float) * B * d, 5);
       s->attn_ws = (float*)dev_alloc(s, sizeof(float) * kMaxSlices * kAttnSplitBlocks * (dh + 2), 5);
+      s->samp_ws = dev_alloc(s, (size_t)sample_workspace_bytes((int)B, (int)V), 5);
       HIPCHK(hipHostMalloc((void**)&s->rp_host, sizeof(int) * kStage * 3 * B, hipHostMallocDefault));
       for (int k = 0; k < kStage; ++k) HIPCHK(hipEventCreateWithFlags(&s->rp_ev[k], hipEventDisableTiming));
       if (m->dt == Dt::BF16 && scan_supported((int)dh, (int)rows, (int)d, (int)hd, (int)f, (int)Tm, c.L_D)) {
@@ -1525,14 +1528,27 @@ int rlt_restore(rlt_model* m, rlt_state* s, const rlt_snapshot_info* info, const
   });
 }
 
+int rlt_sample_workspace(int rows, int vocab, int64_t* bytes) {
+  return guarded([&] {
+    if (!bytes || rows < 0 || vocab < 1) fail(RLT_ERR_INVALID_ARG, "rows >= 0, vocab >= 1 and bytes required");
+    if (vocab > (1 << 20)) fail(RLT_ERR_UNSUPPORTED, "vocab > 2^20");
+    *bytes = sample_workspace_bytes(rows, vocab);
+  });
+}
+
 int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
-               uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream) {
+               uint64_t step, int32_t* tokens, float* logprob, void* workspace, int64_t workspace_bytes,
+               hipStream_t stream) {
   return guarded([&] {
     if (!logits || !tokens) fail(RLT_ERR_INVALID_ARG, "logits and tokens required");
     if (rows < 0 || vocab < 1 || ld < vocab) fail(RLT_ERR_INVALID_ARG, "rows >= 0, vocab >= 1, ld >= vocab required");
+    if (vocab > (1 << 20)) fail(RLT_ERR_UNSUPPORTED, "vocab > 2^20");
     if (!(temperature >= 0.f) || !std::isfinite(temperature))
       fail(RLT_ERR_INVALID_ARG, "temperature must be finite and >= 0");
-    sample_rows(logits, ld, rows, vocab, temperature, seed, step, tokens, 1, logprob, 1, nullptr, stream);
+    if (workspace && workspace_bytes < sample_workspace_bytes(rows, vocab))
+      fail(RLT_ERR_INVALID_ARG, "workspace smaller than rlt_sample_workspace");
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15)) fail(RLT_ERR_INVALID_ARG, "workspace alignment");
+    sample_rows(logits, ld, rows, vocab, temperature, seed, step, tokens, 1, logprob, 1, nullptr, stream, workspace);
     check_launch();
   });
 }
@@ -1558,7 +1574,7 @@ int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float 
       o.ld_b = logits ? n : 1;
       do_scan(m, s, 1, o, stream);
       sample_rows(o.logits, o.ld_b * V, s->B, V, temperature, seed, step0 + (uint64_t)i, tokens + i, n, logprob + i,
-                  n, s->gtok, stream);
+                  n, s->gtok, stream, s->samp_ws);
     }
     check_launch();
   });

@@ -28,7 +28,8 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_step", "rlt_replay", "rlt_set_scan_mode", "rlt_state_block_steps", "rlt_status_string",
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
            "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant", "rlt_replay_grad_workspace",
-           "rlt_replay_grad", "rlt_step_rows", "rlt_state_reset_rows", "rlt_state_row_positions"]
+           "rlt_replay_grad", "rlt_step_rows", "rlt_state_reset_rows", "rlt_state_row_positions",
+           "rlt_sample_workspace"]
 
 
 class RltError(RuntimeError):
@@ -89,7 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_set_scan_mode": [vp, i32],
         "rlt_set_batch_invariant": [vp, i32],
         "rlt_state_block_steps": [vp, i64p],
-        "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp],
+        "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp,
+                       ctypes.c_int64, vp],
+        "rlt_sample_workspace": [i32, i32, i64p],
         "rlt_generate": [vp, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp],
         "rlt_importance_ratio": [vp, vp, ctypes.c_int64, vp, vp],
         "rlt_snapshot_size": [vp, vp, i64p],
@@ -231,12 +234,20 @@ def rlt_replay(model, state, tokens: torch.Tensor, logprob: torch.Tensor, s_out=
                              ctypes.c_void_p(_stream())))
 
 
+def rlt_sample_workspace(rows: int, vocab: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(load().rlt_sample_workspace(rows, vocab, ctypes.byref(n)))
+    return n.value
+
+
 def rlt_sample(logits: torch.Tensor, temperature: float, seed: int, step: int, tokens: torch.Tensor,
-               logprob: Optional[torch.Tensor] = None) -> None:
+               logprob: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> None:
     assert logits.dtype == torch.float32 and logits.dim() == 2 and tokens.dtype == torch.int32
     rows, V = logits.shape
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
     _check(load().rlt_sample(_ptr(logits), rows, V, V, temperature, seed, step, _ptr(tokens), _ptr(logprob),
-                             ctypes.c_void_p(_stream())))
+                             ws, wn, ctypes.c_void_p(_stream())))
 
 
 def rlt_generate(model, state, first: torch.Tensor, n: int, temperature: float, seed: int, step0: int,

@@ -86,19 +86,41 @@ def test_sample_row_stride_and_rows_zero():
     lp = torch.empty(4, dtype=torch.float32, device="cuda")
     lib = rlt.load()
     w = dev(wide)
-    rc = lib.rlt_sample(rlt._ptr(w), 4, 40, 64, 1.0, 77, 5, rlt._ptr(tok), rlt._ptr(lp),
+    rc = lib.rlt_sample(rlt._ptr(w), 4, 40, 64, 1.0, 77, 5, rlt._ptr(tok), rlt._ptr(lp), None, 0,
                         rlt.ctypes.c_void_p(rlt._stream()))
     assert rc == 0
     torch.cuda.synchronize()
     ref_tok, ref_lp, _ = oracle_sample(logits, 1.0, 77, 5)
     assert np.array_equal(tok.cpu().numpy(), ref_tok)
     assert np.max(np.abs(lp.cpu().numpy() - ref_lp)) <= 1e-6
-    assert lib.rlt_sample(rlt._ptr(w), 0, 40, 64, 1.0, 77, 5, rlt._ptr(tok), None,
+    assert lib.rlt_sample(rlt._ptr(w), 0, 40, 64, 1.0, 77, 5, rlt._ptr(tok), None, None, 0,
                           rlt.ctypes.c_void_p(rlt._stream())) == 0
-    assert lib.rlt_sample(rlt._ptr(w), 4, 40, 39, 1.0, 77, 5, rlt._ptr(tok), None,
+    assert lib.rlt_sample(rlt._ptr(w), 4, 40, 39, 1.0, 77, 5, rlt._ptr(tok), None, None, 0,
                           rlt.ctypes.c_void_p(rlt._stream())) == -1
-    assert lib.rlt_sample(rlt._ptr(w), 4, 40, 64, -1.0, 77, 5, rlt._ptr(tok), None,
+    assert lib.rlt_sample(rlt._ptr(w), 4, 40, 64, -1.0, 77, 5, rlt._ptr(tok), None, None, 0,
                           rlt.ctypes.c_void_p(rlt._stream())) == -1
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7, 0.0])
+def test_sample_chunks_side_by_side_equal_one_workgroup(tau):
+    """With a workspace the 4096-id chunks of each row run in separate workgroups: tokens and
+    log mu equal the one-workgroup-per-row path bit for bit (vocabulary 32000: 8 chunks; 37
+    rows), and both equal the oracle's draws."""
+    logits = make_logits(37, 32000, seed=21)
+    lg = dev(logits)
+    t1 = torch.empty(37, dtype=torch.int32, device="cuda")
+    l1 = torch.empty(37, dtype=torch.float32, device="cuda")
+    t2, l2 = torch.empty_like(t1), torch.empty_like(l1)
+    ws = torch.empty(rlt.rlt_sample_workspace(37, 32000), dtype=torch.uint8, device="cuda")
+    rlt.rlt_sample(lg, tau, 5, 11, t1, l1)
+    rlt.rlt_sample(lg, tau, 5, 11, t2, l2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(t1, t2) and torch.equal(l1, l2)
+    ref_tok, ref_lp, _ = oracle_sample(logits, tau, 5, 11)
+    assert np.array_equal(t1.cpu().numpy(), ref_tok)
+    assert np.max(np.abs(l1.cpu().numpy() - ref_lp)) <= 1e-6
+    with pytest.raises(rlt.RltError):
+        rlt.rlt_sample(lg, tau, 5, 11, t2, l2, workspace=ws[:8])
 
 
 def gpu_generate(cfg, P, x, p, n, tau, seed, step0, splits=None):
