@@ -166,7 +166,7 @@ constexpr int kSkW = 8;
 
 template <int TPW, int NMB>
 constexpr int skinny_unroll() {
-  return TPW + NMB <= 2 ? 8 : (TPW + NMB <= 3 ? 4 : (TPW + NMB <= 5 ? 2 : 1));
+  return TPW + NMB <= 2 ? 8 : (TPW + NMB <= 4 ? 4 : (TPW + NMB <= 6 ? 2 : 1));
 }
 
 template <typename T, Ep E, int NMB, int TPW>

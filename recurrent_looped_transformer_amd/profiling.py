@@ -73,7 +73,9 @@ def short(name: str) -> str:
     """Kernel name without return type, namespace and argument list (demangled if needed)."""
     if name.startswith("_Z"):
         try:
-            name = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip() or name
+            # _Float16 mangles as DF16_, which older c++filt builds do not know; half (Dh) reads the same
+            name = subprocess.run(["c++filt", name.replace("DF16_", "Dh")], capture_output=True,
+                                  text=True).stdout.strip() or name
         except OSError:
             pass
     name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
@@ -90,7 +92,7 @@ def short(name: str) -> str:
         name = name[:end]
     else:
         name = name.split("(")[0]
-    return name.replace("rlt::", "").replace("unsigned short", "bf16").replace("_Float16", "f16")
+    return name.replace("rlt::", "").replace("unsigned short", "bf16").replace("_Float16", "f16").replace("half", "f16")
 
 
 def _one(path_glob: str) -> str:
