@@ -1,7 +1,7 @@
 """rocprofv3 passes over bench.py and their summary (kernel table + HBM traffic of the scan).
 
     python -m recurrent_looped_transformer_amd.profiling run OUT [bench args...]
-        (on the GPU machine; starts rocprofv3 as child processes, never touches the GPU itself)
+        (on the MI355X host; starts rocprofv3 as child processes, never touches the GPU itself)
         1. --kernel-trace --stats over `bench.py --steps 3 --warmup 1 --no-cpu ...`
         2. --pmc FETCH_SIZE, 3. --pmc WRITE_SIZE over
            `bench.py --steps 1 --warmup 0 --no-cpu --progress-every 64 ...` (the scan as calls of
@@ -12,7 +12,7 @@
     python -m recurrent_looped_transformer_amd.profiling summarize OUT NAME [bench args...]
         writes profiles/kernels_NAME.md and profiles/traffic_scan_NAME.json
     python -m recurrent_looped_transformer_amd.profiling trace OUT [bench args...]
-        (on the GPU machine) only pass 1, over `bench.py --steps 2 --warmup 1 --no-cpu ...`
+        (on the MI355X host) only pass 1, over `bench.py --steps 2 --warmup 1 --no-cpu ...`
     python -m recurrent_looped_transformer_amd.profiling summarize-trace OUT NAME [bench args...]
         writes profiles/kernels_NAME.md (kernel table only, no counters)
 
@@ -139,7 +139,7 @@ def summarize(out_dir: str, name: str, bench_args):
     write_b = sum(sum(v) for v in per_k_w.values())
 
     lines = [f"# Kernel summary: {name}", "",
-             "Commands (R = repository root on the MI355X box; every file run is committed):", "",
+             "Commands (R = repository root on the MI355X host; every file run is committed):", "",
              f"    python -m recurrent_looped_transformer_amd.profiling run OUT {' '.join(bench_args)}",
              "    (rocprofv3 --kernel-trace --stats ... -- python3 R/bench.py --steps 3 --warmup 1 --no-cpu ARGS;",
              "     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 R/bench.py --steps 1 --warmup 0 --no-cpu "
@@ -195,7 +195,7 @@ def summarize_trace(out_dir: str, name: str, bench_args):
             if ln.startswith("{") and '"metric"' in ln:
                 bench_line = ln.strip()
     lines = [f"# Kernel summary: {name}", "",
-             "Commands (R = repository root on the MI355X box; every file run is committed):", "",
+             "Commands (R = repository root on the MI355X host; every file run is committed):", "",
              f"    python -m recurrent_looped_transformer_amd.profiling trace OUT {' '.join(bench_args)}",
              "    (rocprofv3 --kernel-trace --stats ... -- python3 R/bench.py --steps 2 --warmup 1 --no-cpu ARGS)",
              f"    python -m recurrent_looped_transformer_amd.profiling summarize-trace OUT {name} "
