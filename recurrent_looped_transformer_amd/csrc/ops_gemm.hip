@@ -33,8 +33,14 @@ __device__ __forceinline__ void rope_apply(float2 cs, float& x0, float& x1) {
 }
 
 // Position index (0-based) before the first position of row m's sequence in this call.
+// (a.pos0 passes through readfirstlane, an identity on this uniform value: otherwise the
+// compiler merges the three loads into one load from a chosen address, and the argument's
+// address space forces a copy of it to per-lane scratch memory and a flat load)
 __device__ __forceinline__ int ep_pos0(const EpArgs& a, int m) {
-  return a.row_pos ? a.row_pos[m / a.tn] : (a.pos_dev ? a.pos_dev[0] : a.pos0);
+  int p = __builtin_amdgcn_readfirstlane(a.pos0);
+  if (a.row_pos) p = a.row_pos[m / a.tn];
+  else if (a.pos_dev) p = a.pos_dev[0];
+  return p;
 }
 
 // Epilogue operands a decode GEMM loads before its main loop (they do not depend on it):
