@@ -63,12 +63,21 @@ struct Seg {
   int nseg = 0;
 };
 __device__ __forceinline__ int seg_of(int x, int len) { return (x >= len) + (x >= 2 * len); }
+// p[i] for i in 0..2 by selects (a runtime index into the kernel-argument array would place
+// it in per-lane scratch memory)
+template <typename P>
+__device__ __forceinline__ P seg_pick(const P (&p)[3], int i) {
+  return i == 0 ? p[0] : (i == 1 ? p[1] : p[2]);
+}
 // C[m, n] = (R ? R[m, n] : 0) + sum_k A(m, k) B(k, n), or, when atomic, C[m, n] += sum.
 // A(m, k) = AK ? A[m*lda + k] : A[k*lda + m];  B(k, n) = BK ? B[n*ldb + k] : B[k*ldb + n].
 // R, when given, has C's layout (it may be C itself). blockIdx.z takes k in
 // [z*kchunk, (z+1)*kchunk). With `part`, the k-slice z writes its partial sums to
-// part[z][M][N] instead (summed by g_splitk_reduce in a fixed order).
-template <bool AK, bool BK>
+// part[z][M][N] instead (summed by g_splitk_reduce in a fixed order). PF k-steps of operand
+// loads are in flight at once (a register ring): the split products have short k ranges
+// and few workgroups, where the load round trip of every k-step would otherwise be paid
+// one after the other.
+template <bool AK, bool BK, int PF>
 __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                                               const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
                                               const float* R, int atomic, int kchunk, float* __restrict__ part,
@@ -82,15 +91,15 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
   // Each thread loads one float4 of each operand tile: along k when k is the contiguous index
   // (row = tid / 4, k = 4 * (tid % 4)), else along m / n (k = tid / 16, 4 * (tid % 16)). Every
   // contiguous extent (k for k-contiguous operands, m / n otherwise) is a multiple of 4.
-  float4 ra, rb;
-  auto load = [&](int k0) {
+  float4 ra_[PF], rb_[PF];
+  auto load = [&](int k0, float4& ra, float4& rb) {
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
     if (AK) {
       const int gm = m0 + (tid >> 2), gk = k0 + 4 * (tid & 3);
       if (gm < M && gk < ke) {
         if (sg.kseg) {
           const int sp = seg_of(gk, sg.kseg);
-          ra = *reinterpret_cast<const float4*>(sg.a[sp] + (int64_t)gm * lda + gk - sp * sg.kseg);
+          ra = *reinterpret_cast<const float4*>(seg_pick(sg.a, sp) + (int64_t)gm * lda + gk - sp * sg.kseg);
         } else {
           ra = *reinterpret_cast<const float4*>(A + (int64_t)gm * lda + gk);
         }
@@ -99,14 +108,17 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
       }
     } else {
       const int gk = k0 + (tid >> 4), gm = m0 + 4 * (tid & 15);
-      ra = (gk < ke && gm < M) ? *reinterpret_cast<const float4*>(A + (int64_t)gk * lda + gm) : z;
+      ra = z;
+      if (gk < ke && gm < M) ra = *reinterpret_cast<const float4*>(A + (int64_t)gk * lda + gm);
     }
     if (BK) {
       const int gn = n0 + (tid >> 2), gk = k0 + 4 * (tid & 3);
-      rb = (gn < N && gk < ke) ? *reinterpret_cast<const float4*>(Bm + (int64_t)gn * ldb + gk) : z;
+      rb = z;
+      if (gn < N && gk < ke) rb = *reinterpret_cast<const float4*>(Bm + (int64_t)gn * ldb + gk);
     } else {
       const int gk = k0 + (tid >> 4), gn = n0 + 4 * (tid & 15);
-      rb = (gk < ke && gn < N) ? *reinterpret_cast<const float4*>(Bm + (int64_t)gk * ldb + gn) : z;
+      rb = z;
+      if (gk < ke && gn < N) rb = *reinterpret_cast<const float4*>(Bm + (int64_t)gk * ldb + gn);
     }
   };
   float acc[4][4];
@@ -115,36 +127,46 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
   const int ty = tid >> 4, tx = tid & 15;
-  if (kb < ke) load(kb);
-  for (int k0 = kb; k0 < ke; k0 += GK) {
-    __syncthreads();
-    if (AK) {
-      const int r = tid >> 2, k = 4 * (tid & 3);
-      As[k][r] = ra.x; As[k + 1][r] = ra.y; As[k + 2][r] = ra.z; As[k + 3][r] = ra.w;
-    } else {
-      const int k = tid >> 4, r = 4 * (tid & 15);
-      *reinterpret_cast<float4*>(&As[k][r]) = ra;
-    }
-    if (BK) {
-      const int r = tid >> 2, k = 4 * (tid & 3);
-      Bs[k][r] = rb.x; Bs[k + 1][r] = rb.y; Bs[k + 2][r] = rb.z; Bs[k + 3][r] = rb.w;
-    } else {
-      const int k = tid >> 4, r = 4 * (tid & 15);
-      *reinterpret_cast<float4*>(&Bs[k][r]) = rb;
-    }
-    __syncthreads();
-    if (k0 + GK < ke) load(k0 + GK);
+  const int nst = kb < ke ? (ke - kb + GK - 1) / GK : 0;   // k-steps of this slice
 #pragma unroll
-    for (int kk = 0; kk < GK; ++kk) {
-      float a[4], b[4];
+  for (int j = 0; j < PF; ++j)
+    if (j < nst) load(kb + j * GK, ra_[j], rb_[j]);
+  for (int s0 = 0; s0 < nst; s0 += PF) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+    for (int j = 0; j < PF; ++j) {
+      const int st = s0 + j;   // uniform across the block
+      if (st < nst) {
+        __syncthreads();
+        const float4 ra = ra_[j], rb = rb_[j];
+        if (AK) {
+          const int r = tid >> 2, k = 4 * (tid & 3);
+          As[k][r] = ra.x; As[k + 1][r] = ra.y; As[k + 2][r] = ra.z; As[k + 3][r] = ra.w;
+        } else {
+          const int k = tid >> 4, r = 4 * (tid & 15);
+          *reinterpret_cast<float4*>(&As[k][r]) = ra;
+        }
+        if (BK) {
+          const int r = tid >> 2, k = 4 * (tid & 3);
+          Bs[k][r] = rb.x; Bs[k + 1][r] = rb.y; Bs[k + 2][r] = rb.z; Bs[k + 3][r] = rb.w;
+        } else {
+          const int k = tid >> 4, r = 4 * (tid & 15);
+          *reinterpret_cast<float4*>(&Bs[k][r]) = rb;
+        }
+        __syncthreads();
+        if (st + PF < nst) load(kb + (st + PF) * GK, ra_[j], rb_[j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+        for (int kk = 0; kk < GK; ++kk) {
+          float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+          for (int jj = 0; jj < 4; ++jj) b[jj] = Bs[kk][tx + 16 * jj];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(a[i], b[jj], acc[i][jj]);
+        }
+      }
     }
   }
 #pragma unroll
@@ -164,7 +186,7 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
       int nn = gn;
       if (sg.nseg) {
         const int sp = seg_of(gn, sg.nseg);
-        Cp = sg.c[sp]; Rp = sg.r[sp]; nn = gn - sp * sg.nseg;
+        Cp = seg_pick(sg.c, sp); Rp = seg_pick(sg.r, sp); nn = gn - sp * sg.nseg;
       }
       float* cc = Cp + (int64_t)gm * ldc + nn;
       if (atomic) atomicAdd(cc, acc[i][j]);
@@ -184,7 +206,7 @@ __global__ void g_splitk_reduce(int M, int N, int splits, const float* __restric
   for (int z = 0; z < splits; ++z) v += part[(int64_t)z * M * N + i];
   if (sg.nseg) {
     const int sp = seg_of(n, sg.nseg);
-    C = sg.c[sp]; R = sg.r[sp]; n -= sp * sg.nseg;
+    C = seg_pick(sg.c, sp); R = seg_pick(sg.r, sp); n -= sp * sg.nseg;
   }
   C[m * ldc + n] = (R ? R[m * ldc + n] : 0.f) + v;
 }
@@ -581,10 +603,24 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   if (splits == 1) part = nullptr;
   dim3 grid(tn, tm, splits);
   const int at = atomic ? 1 : 0;
-  if (ak && bk) g_gemm<true, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
-  else if (ak) g_gemm<true, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
-  else if (bk) g_gemm<false, true><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
-  else g_gemm<false, false><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  // deep prefetch for the split products (row-block products of B rows, short k slices)
+  const int pf = part == nullptr ? 1 : (kchunk / GK >= 8 ? 8 : 4);
+#define G_GEMM(AKV, BKV, PFV) \
+  g_gemm<AKV, BKV, PFV><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg)
+  if (ak && bk) {
+    if (pf == 8) G_GEMM(true, true, 8);
+    else if (pf == 4) G_GEMM(true, true, 4);
+    else G_GEMM(true, true, 1);
+  } else if (ak) {
+    if (pf == 8) G_GEMM(true, false, 8);
+    else if (pf == 4) G_GEMM(true, false, 4);
+    else G_GEMM(true, false, 1);
+  } else if (bk) {
+    G_GEMM(false, true, 1);
+  } else {
+    G_GEMM(false, false, 1);
+  }
+#undef G_GEMM
   c.check();
   if (part) {
     g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc, sg);
