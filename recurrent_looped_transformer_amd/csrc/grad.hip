@@ -341,6 +341,161 @@ __global__ void g_swiglu_bwd(int64_t n, const float* gg, const float* __restrict
   g1[i] = gv * f3[i] * s * (1.f + a * (1.f - s));
 }
 
+// ------------------------------------------- split-K reduction fused with its consumer
+// Each kernel below adds the k-slices of a split product (z ascending, then R, as
+// g_splitk_reduce) and applies the operation that consumes the product's rows: the same
+// arithmetic as the separate kernel named with it. The rotary and SwiGLU forms give the
+// separate forms' bits; the RMSNorm forms run a row on a workgroup (columns spread over 256
+// threads), so their row sums are added in another order.
+__device__ __forceinline__ float part_sum(const float* __restrict__ part, int64_t MN, int splits, int64_t i) {
+  float v = 0.f;
+#pragma unroll 8
+  for (int z = 0; z < splits; ++z) v += part[(int64_t)z * MN + i];
+  return v;
+}
+
+constexpr int kRowCols = 4;   // columns per thread of the row kernels: rows of up to 1024
+
+// sum over the 256 threads of a workgroup: wave sums, then the 4 waves in order
+__device__ __forceinline__ float block_sum256(float v, float* lds4) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+}
+
+// C = R + sum part (N <= 1024 columns, row stride N), then y = RMSNorm(C) * g and rstd
+// (g_rms_fwd). One workgroup per row.
+__global__ __launch_bounds__(256) void g_reduce_rms_fwd(int M, int N, int splits, const float* __restrict__ part,
+                                                        const float* R, float* C, const float* __restrict__ g,
+                                                        float eps, float* __restrict__ y, float* __restrict__ rstd) {
+  __shared__ float lds4[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int64_t o = (int64_t)row * N, MN = (int64_t)M * N;
+  float xv[kRowCols];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRowCols; ++q) {
+    const int j = tid + 256 * q;
+    xv[q] = 0.f;
+    if (j < N) {
+      const float v = part_sum(part, MN, splits, o + j);
+      xv[q] = (R ? R[o + j] : 0.f) + v;
+      C[o + j] = xv[q];
+      ss = fmaf(xv[q], xv[q], ss);
+    }
+  }
+  ss = block_sum256(ss, lds4);
+  const float r = 1.f / sqrtf(ss / (float)N + eps);
+#pragma unroll
+  for (int q = 0; q < kRowCols; ++q) {
+    const int j = tid + 256 * q;
+    if (j < N) y[o + j] = xv[q] * r * g[j];
+  }
+  if (tid == 0) rstd[row] = r;
+}
+
+// C = R + sum part (the output gradient dy of an RMSNorm, N <= 1024, row stride N), then
+// out = res + dx as g_rms_bwd (res may alias out). One workgroup per row.
+__global__ __launch_bounds__(256) void g_reduce_rms_bwd(int M, int N, int splits, const float* __restrict__ part,
+                                                        const float* R, float* C, const float* __restrict__ x,
+                                                        const float* __restrict__ rstd, const float* __restrict__ g,
+                                                        const float* res, float* out) {
+  __shared__ float lds4[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int64_t o = (int64_t)row * N, MN = (int64_t)M * N;
+  float dv[kRowCols], xv[kRowCols], gv[kRowCols];
+  float dot = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRowCols; ++q) {
+    const int j = tid + 256 * q;
+    dv[q] = xv[q] = gv[q] = 0.f;
+    if (j < N) {
+      const float v = part_sum(part, MN, splits, o + j);
+      dv[q] = (R ? R[o + j] : 0.f) + v;
+      xv[q] = x[o + j];
+      gv[q] = g[j];
+      C[o + j] = dv[q];
+      dot = fmaf(gv[q] * dv[q], xv[q], dot);
+    }
+  }
+  dot = block_sum256(dot, lds4);
+  const float r = rstd[row];
+  const float c = r * r * r * dot / (float)N;
+#pragma unroll
+  for (int q = 0; q < kRowCols; ++q) {
+    const int j = tid + 256 * q;
+    if (j < N) {
+      const float v = r * gv[q] * dv[q] - c * xv[q];
+      out[o + j] = (res ? res[o + j] : 0.f) + v;
+    }
+  }
+}
+
+// C = sum part over heads of dh columns (outputs by Seg when nseg > 0, else row stride N);
+// the pairs (i, i + dh/2) of the first nrot columns rotated by +angle as g_rope with
+// pos = pos0 + row / rpp. One thread per pair.
+__global__ void g_reduce_rope(int M, int N, int splits, const float* __restrict__ part, float* C, Seg sg, int dh,
+                              int nrot, int pos0, int rpp, double base) {
+  const int half = dh / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * (N / 2)) return;
+  const int npr = N / 2;
+  const int64_t row = idx / npr;
+  const int pi = (int)(idx % npr);
+  const int n1 = (pi / half) * dh + pi % half, n2 = n1 + half;
+  const int64_t MN = (int64_t)M * N;
+  const float x1 = 0.f + part_sum(part, MN, splits, row * N + n1);   // 0 + v: the reduction's R-less sum
+  const float x2 = 0.f + part_sum(part, MN, splits, row * N + n2);
+  float y1 = x1, y2 = x2;
+  if (n1 < nrot) {
+    const int i = pi % half;
+    const double pos = (double)(pos0 + row / rpp);
+    const double a = pos * pow(base, -2.0 * i / dh);
+    const float c = (float)cos(a), s = 1.f * (float)sin(a);
+    y1 = x1 * c - x2 * s;
+    y2 = x1 * s + x2 * c;
+  }
+  float* dst = C + row * N;
+  int c1 = n1;
+  if (sg.nseg) {
+    const int sp = seg_of(n1, sg.nseg);
+    dst = seg_pick(sg.c, sp) + row * sg.nseg;
+    c1 = n1 - sp * sg.nseg;
+  }
+  dst[c1] = y1;
+  dst[c1 + half] = y2;
+}
+
+// f1, f3 = the two f-column outputs of a split product (Seg, nseg = f); g = silu(f1) f3
+// (g_swiglu_fwd)
+__global__ void g_reduce_swiglu(int M, int f, int splits, const float* __restrict__ part, Seg sg,
+                                float* __restrict__ g) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * f) return;
+  const int64_t row = i / f;
+  const int j = (int)(i % f);
+  const int64_t MN = (int64_t)M * 2 * f;
+  const float a = 0.f + part_sum(part, MN, splits, row * 2 * f + j);
+  const float b = 0.f + part_sum(part, MN, splits, row * 2 * f + f + j);
+  sg.c[0][i] = a;
+  sg.c[1][i] = b;
+  g[i] = a * sigm(a) * b;
+}
+
+// gg = R + sum part (C, row stride N = f); g1, g3 as g_swiglu_bwd
+__global__ void g_reduce_swiglu_bwd(int M, int N, int splits, const float* __restrict__ part, const float* R,
+                                    float* C, const float* __restrict__ f1, const float* __restrict__ f3,
+                                    float* g1, float* __restrict__ g3) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const float gv = (R ? R[i] : 0.f) + part_sum(part, (int64_t)M * N, splits, i);
+  C[i] = gv;
+  const float a = f1[i], s = sigm(a);
+  g3[i] = gv * a * s;
+  g1[i] = gv * f3[i] * s * (1.f + a * (1.f - s));
+}
+
 // u = e + alpha * gate * sr, gate = sigmoid(gp + bg)
 __global__ void g_merge_fwd(int M, int d, const float* __restrict__ e, const float* __restrict__ gp,
                             const float* __restrict__ bg, const float* __restrict__ sr, float alpha,
@@ -573,14 +728,45 @@ struct Ctx {
 
 inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// The operation that consumes a product's rows, run by the split-K reduction when the product
+// splits, else by its own kernel after the product.
+struct Post {
+  enum Kind { None, RmsFwd, RmsBwd, Rope, SwiGlu, SwiGluBwd } kind = None;
+  const float* g = nullptr;       // RmsFwd / RmsBwd: gain
+  float eps = 0.f;                // RmsFwd
+  float* y = nullptr;             // RmsFwd: normalised rows; SwiGlu: silu(f1) f3
+  float* rstd = nullptr;          // RmsFwd: 1 / rms per row
+  const float* x = nullptr;       // RmsBwd: the norm's input rows
+  const float* rs = nullptr;      // RmsBwd: their 1 / rms
+  const float* res = nullptr;     // RmsBwd: added to the input gradient (may alias out)
+  float* out = nullptr;           // RmsBwd: input gradient
+  int H = 0, dh = 0, nrot = 0, pos0 = 0, rpp = 1;   // Rope: columns [0, nrot) rotated, heads of dh
+  double base = 0.0;
+  const float* f1 = nullptr;      // SwiGluBwd: FFN pre-activations
+  const float* f3 = nullptr;
+  float* g1 = nullptr;            // SwiGluBwd: their gradients
+  float* g3 = nullptr;
+};
+void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p);
+
 // C = R + A.B (see g_gemm), or C += A.B split over k with atomics. Products with few
 // output tiles (the per-position products have B rows) split k over up to 16 slices whose
 // partial sums a second kernel adds in a fixed order (deterministic).
 constexpr int kMaxSplits = 16;
 void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, const float* Bm, int64_t ldb, bool bk,
-          float* C, int64_t ldc, const float* R, bool atomic, const Seg& sg = Seg()) {
+          float* C, int64_t ldc, const float* R, bool atomic, const Seg& sg = Seg(), const Post& post = Post()) {
   // atomic: C += A.B; otherwise C = R + A.B
   if (M <= 0 || N <= 0) return;
+  {   // the consumers read rows of N contiguous columns; rotary and SwiGLU products have no R
+    const bool rows = post.kind == Post::RmsFwd || post.kind == Post::RmsBwd || post.kind == Post::SwiGluBwd;
+    const bool nor = post.kind == Post::Rope || post.kind == Post::SwiGlu;
+    if ((rows && (sg.nseg || ldc != N)) || (nor && R) || (post.kind == Post::SwiGlu && sg.nseg * 2 != N) ||
+        (post.kind == Post::Rope && (sg.nseg ? sg.nseg : N) % (post.H * post.dh) != 0) ||
+        (post.kind != Post::None && atomic)) {
+      if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
+      return;
+    }
+  }
   const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT;
   int splits = 1;
   float* part = nullptr;
@@ -622,33 +808,65 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   }
 #undef G_GEMM
   c.check();
-  if (part) {
+  const bool row_kernel = post.kind == Post::RmsFwd || post.kind == Post::RmsBwd;
+  if (part && row_kernel && N > 256 * kRowCols) {   // rows too long for the fused form
     g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc, sg);
     c.check();
+    part = nullptr;
   }
+  if (!part) {
+    post_separate(c, M, N, C, sg, post);
+    return;
+  }
+  switch (post.kind) {
+    case Post::None:
+      g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc, sg);
+      break;
+    case Post::RmsFwd:
+      g_reduce_rms_fwd<<<M, 256, 0, c.st>>>(M, N, splits, part, R, C, post.g, post.eps, post.y, post.rstd);
+      break;
+    case Post::RmsBwd:
+      g_reduce_rms_bwd<<<M, 256, 0, c.st>>>(M, N, splits, part, R, C, post.x, post.rs, post.g, post.res, post.out);
+      break;
+    case Post::Rope:
+      g_reduce_rope<<<blocks((int64_t)M * (N / 2)), 256, 0, c.st>>>(M, N, splits, part, C, sg, post.dh, post.nrot,
+                                                                   post.pos0, post.rpp, post.base);
+      break;
+    case Post::SwiGlu:
+      g_reduce_swiglu<<<blocks((int64_t)M * (N / 2)), 256, 0, c.st>>>(M, N / 2, splits, part, sg, post.y);
+      break;
+    case Post::SwiGluBwd:
+      g_reduce_swiglu_bwd<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, post.f1, post.f3,
+                                                                     post.g1, post.g3);
+      break;
+  }
+  c.check();
 }
 // Y_p[M, out] = X[M, in] . W_p^T for the np row blocks W_p of Wcat [np*out, in] (one launch)
-void lin_n(Ctx& c, int M, const float* X, int in, const float* Wcat, int out, int np, float* const* Y) {
+void lin_n(Ctx& c, int M, const float* X, int in, const float* Wcat, int out, int np, float* const* Y,
+           const Post& post = Post()) {
   Seg sg;
   for (int p = 0; p < np; ++p) sg.c[p] = Y[p];
   sg.nseg = out;
-  gemm(c, M, np * out, in, X, in, true, Wcat, in, true, Y[0], out, nullptr, false, sg);
+  gemm(c, M, np * out, in, X, in, true, Wcat, in, true, Y[0], out, nullptr, false, sg, post);
 }
 // dX[M, in] = R + sum_p dY_p[M, out] . W_p for the np row blocks W_p of Wcat [np*out, in]
 void lin_tk(Ctx& c, int M, const float* const* dY, int out, int np, const float* Wcat, int in, float* dX,
-            const float* R) {
+            const float* R, const Post& post = Post()) {
   Seg sg;
   for (int p = 0; p < np; ++p) sg.a[p] = dY[p];
   sg.kseg = out;
-  gemm(c, M, in, np * out, dY[0], out, true, Wcat, in, false, dX, in, R, false, sg);
+  gemm(c, M, in, np * out, dY[0], out, true, Wcat, in, false, dX, in, R, false, sg, post);
 }
 // Y[M, out] = R + X[M, in] . W^T, W row-major [out, ldw] (ldw = in unless a column slice)
-void lin(Ctx& c, int M, const float* X, int in, const float* W, int64_t ldw, int out, float* Y, const float* R) {
-  gemm(c, M, out, in, X, in, true, W, ldw, true, Y, out, R, false);
+void lin(Ctx& c, int M, const float* X, int in, const float* W, int64_t ldw, int out, float* Y, const float* R,
+         const Post& post = Post()) {
+  gemm(c, M, out, in, X, in, true, W, ldw, true, Y, out, R, false, Seg(), post);
 }
 // dX[M, in] = R + dY[M, out] . W, W row-major [out, ldw]
-void lin_t(Ctx& c, int M, const float* dY, int out, const float* W, int64_t ldw, int in, float* dX, const float* R) {
-  gemm(c, M, in, out, dY, out, true, W, ldw, false, dX, in, R, false);
+void lin_t(Ctx& c, int M, const float* dY, int out, const float* W, int64_t ldw, int in, float* dX, const float* R,
+           const Post& post = Post()) {
+  gemm(c, M, in, out, dY, out, true, W, ldw, false, dX, in, R, false, Seg(), post);
 }
 // dW[out, in] (row stride ldc) += dY[M, out]^T . X[M, in]
 void wgrad(Ctx& c, int M, const float* dY, int out, const float* X, int in, float* dW, int64_t ldc) {
@@ -686,6 +904,30 @@ void add(Ctx& c, int64_t n, const float* a, const float* b, float* out) {
   if (n <= 0) return;
   g_add<<<blocks(n), 256, 0, c.st>>>(n, a, b, out);
   c.check();
+}
+
+// The consumer of a product that did not split: its own kernel after the product.
+void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p) {
+  switch (p.kind) {
+    case Post::None: break;
+    case Post::RmsFwd: rms_fwd(c, M, N, C, p.g, p.eps, p.y, p.rstd); break;
+    case Post::RmsBwd: rms_bwd(c, M, N, C, p.x, p.rs, p.g, p.res, p.out); break;
+    case Post::Rope:
+      if (sg.nseg) {
+        for (int q = 0; q < 3 && q * sg.nseg < p.nrot; ++q) rope(c, M, p.H, p.dh, sg.c[q], p.pos0, p.rpp, p.base, 1.f);
+      } else {
+        rope(c, M, p.H, p.dh, C, p.pos0, p.rpp, p.base, 1.f);
+      }
+      break;
+    case Post::SwiGlu:
+      g_swiglu_fwd<<<blocks((int64_t)M * (N / 2)), 256, 0, c.st>>>((int64_t)M * (N / 2), sg.c[0], sg.c[1], p.y);
+      c.check();
+      break;
+    case Post::SwiGluBwd:
+      g_swiglu_bwd<<<blocks((int64_t)M * N), 256, 0, c.st>>>((int64_t)M * N, C, p.f1, p.f3, p.g1, p.g3);
+      c.check();
+      break;
+  }
 }
 
 template <int DH>
@@ -970,32 +1212,38 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   };
   // block l at position t up to its FFN hidden state (the block output is the caller's);
   // with_kv: also this position's key and value rows
-  auto layer_fwd = [&](int l, int t, bool with_kv) {
+  // normalised: the block input's RMSNorm (s.a, s.rs1) was written by the producer of s.zin
+  auto rope_post = [&](int nrot, int t) {
+    Post p;
+    p.kind = Post::Rope; p.H = H; p.dh = dh; p.nrot = nrot; p.pos0 = t + 1; p.rpp = B; p.base = base;
+    return p;
+  };
+  auto rms_post = [&](const std::string& gain, float* y, float* rstd) {
+    Post p;
+    p.kind = Post::RmsFwd; p.g = w(gain); p.eps = eps; p.y = y; p.rstd = rstd;
+    return p;
+  };
+  auto layer_fwd = [&](int l, int t, bool with_kv, bool normalised) {
     const DecBuf& D = u.dec[l];
     const Step s = step(l, t);
-    rms_fwd(c, B, d, s.zin, w(Dn(l, "m1")), eps, s.a, s.rs1);
+    if (!normalised) rms_fwd(c, B, d, s.zin, w(Dn(l, "m1")), eps, s.a, s.rs1);
     if (with_kv) {
       float* y[3] = {s.q, s.k, s.v};
-      lin_n(c, B, s.a, d, u.qkv_d[l], hd, 3, y);
-      rope(c, B, H, dh, s.k, t + 1, B, base, 1.f);
+      lin_n(c, B, s.a, d, u.qkv_d[l], hd, 3, y, rope_post(2 * hd, t));   // q and k rotated
     } else {
-      lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr);
+      lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr, rope_post(hd, t));
     }
-    rope(c, B, H, dh, s.q, t + 1, B, base, 1.f);
     attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1);
-    lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin);
-    rms_fwd(c, B, d, s.z1, w(Dn(l, "m2")), eps, s.b, s.rs2);
-    lin(c, B, s.b, d, w(Dn(l, "xq")), d, hd, s.qx, nullptr);
-    rope(c, B, H, dh, s.qx, t + 1, B, base, 1.f);
+    lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin, rms_post(Dn(l, "m2"), s.b, s.rs2));
+    lin(c, B, s.b, d, w(Dn(l, "xq")), d, hd, s.qx, nullptr, rope_post(hd, t));
     attn_fwd(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[grp(l)], u.mv[grp(l)], s.ox, s.lse2);
-    lin(c, B, s.ox, hd, w(Dn(l, "xo")), hd, d, s.z2, s.z1);
-    rms_fwd(c, B, d, s.z2, w(Dn(l, "m3")), eps, s.c, s.rs3);
+    lin(c, B, s.ox, hd, w(Dn(l, "xo")), hd, d, s.z2, s.z1, rms_post(Dn(l, "m3"), s.c, s.rs3));
     {
       float* y[2] = {s.f1, s.f3};
-      lin_n(c, B, s.c, d, u.w13_d[l], f, 2, y);
+      Post p;
+      p.kind = Post::SwiGlu; p.y = s.g;
+      lin_n(c, B, s.c, d, u.w13_d[l], f, 2, y, p);
     }
-    g_swiglu_fwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, s.f1, s.f3, s.g);
-    c.check();
     return s;
   };
   int rho_t = -1;  // RLT-2: position whose state the register holds (-1: s*)
@@ -1015,9 +1263,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       add(c, Bd, e_all + R0 * d, nullptr, cf.L_D > 0 ? u.dec[0].zin + R0 * d : u.S + R0 * d);
     }
     for (int l = 0; l < cf.L_D; ++l) {
-      const Step s = layer_fwd(l, t, true);
+      const Step s = layer_fwd(l, t, true, l > 0);
       float* out = (l + 1 < cf.L_D ? u.dec[l + 1].zin : u.S) + R0 * d;
-      lin(c, B, s.g, f, w(Ds(l, "w2")), f, d, out, s.z2);
+      Post p;   // the next block's input norm
+      if (l + 1 < cf.L_D) {
+        const Step n = step(l + 1, t);
+        p = rms_post(Dn(l + 1, "m1"), n.a, n.rs1);
+      }
+      lin(c, B, s.g, f, w(Ds(l, "w2")), f, d, out, s.z2, p);
     }
     if (v2 && (t + 1) % cf.chunk == 0) rho_t = t;
   }
@@ -1034,6 +1287,11 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   // ------------------------------------------------ backward: transitions, reversed
   // weight and gain gradients of block l over `rows` rows starting at s (every position at
   // once, or one position with checkpointing)
+  auto rms_bwd_post = [&](const std::string& gain, const float* x, const float* rs, const float* res, float* out) {
+    Post p;
+    p.kind = Post::RmsBwd; p.g = w(gain); p.x = x; p.rs = rs; p.res = res; p.out = out;
+    return p;
+  };
   auto layer_wgrad = [&](int l, const Step& s, int rows) {
     wgrad(c, rows, s.gq, hd, s.a, d, g(Ds(l, "wq")), d);
     wgrad(c, rows, s.gk, hd, s.a, d, g(Ds(l, "wk")), d);
@@ -1072,7 +1330,7 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     const int64_t R0 = (int64_t)t * B, o = R0 * d;
     if (ck) {   // recompute this position's intermediates from the kept block inputs
       if (mg) merge_fwd(t);
-      for (int l = 0; l < cf.L_D; ++l) layer_fwd(l, t, false);
+      for (int l = 0; l < cf.L_D; ++l) layer_fwd(l, t, false, false);
     }
     float* gzo = cf.L_D > 0 ? step(cf.L_D - 1, t).gz3 : u.gu;
     add(c, Bd, u.gS + o, cf.variant == RLT_V1 ? u.carry : nullptr, gzo);
@@ -1084,22 +1342,22 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       DecBuf& D = u.dec[l];
       const Step s = step(l, t);
       // FFN
-      lin_t(c, B, s.gz3, d, w(Ds(l, "w2")), f, f, u.tBf, nullptr);
-      g_swiglu_bwd<<<blocks((int64_t)B * f), 256, 0, c.st>>>((int64_t)B * f, u.tBf, s.f1, s.f3, s.gf1, s.gf3);
-      c.check();
+      {
+        Post p;
+        p.kind = Post::SwiGluBwd; p.f1 = s.f1; p.f3 = s.f3; p.g1 = s.gf1; p.g3 = s.gf3;
+        lin_t(c, B, s.gz3, d, w(Ds(l, "w2")), f, f, u.tBf, nullptr, p);
+      }
       {
         const float* gy[2] = {s.gf1, s.gf3};
-        lin_tk(c, B, gy, f, 2, u.w13_d[l], d, s.gdc, nullptr);
+        lin_tk(c, B, gy, f, 2, u.w13_d[l], d, s.gdc, nullptr, rms_bwd_post(Dn(l, "m3"), s.z2, s.rs3, s.gz3, s.gz2));
       }
-      rms_bwd(c, B, d, s.gdc, s.z2, s.rs3, w(Dn(l, "m3")), s.gz3, s.gz2);
       // cross-attention over memory rows 1..t
       const int gi = grp(l);
       lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr);
       attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
                  u.gmk[gi], u.gmv[gi]);
       rope(c, B, H, dh, s.gqx, t + 1, B, base, -1.f);
-      lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr);
-      rms_bwd(c, B, d, s.gdb, s.z1, s.rs2, w(Dn(l, "m2")), s.gz2, s.gz1);
+      lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr, rms_bwd_post(Dn(l, "m2"), s.z1, s.rs2, s.gz2, s.gz1));
       // window attention; the key/value gradient rows of t are complete afterwards
       lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr);
       attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv);
@@ -1107,10 +1365,9 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       rope(c, B, H, dh, s.gk, t + 1, B, base, -1.f);
       {
         const float* gy[3] = {s.gq, s.gk, s.gv};
-        lin_tk(c, B, gy, hd, 3, u.qkv_d[l], d, s.gda, nullptr);
+        float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
+        lin_tk(c, B, gy, hd, 3, u.qkv_d[l], d, s.gda, nullptr, rms_bwd_post(Dn(l, "m1"), s.zin, s.rs1, s.gz1, gin));
       }
-      float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
-      rms_bwd(c, B, d, s.gda, s.zin, s.rs1, w(Dn(l, "m1")), s.gz1, gin);
       if (ck) layer_wgrad(l, s, B);
     }
     float* get = u.ge + o;
@@ -1125,11 +1382,12 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
         sg.c[0] = get; sg.c[1] = gmr; sg.r[0] = u.gu; sg.nseg = d;
         gemm(c, B, 2 * d, d, ggp, d, true, w("merge.wg"), 2 * d, false, get, d, nullptr, false, sg);
       }
-      lin_t(c, B, gsr, d, w("merge.ws"), d, d, gmr, gmr);
       if (cf.variant == RLT_V1)
-        rms_bwd(c, B, d, gmr, u.msrc + o, mrow(u.mrs, t, 1), w("merge.ns"), nullptr, u.carry);
+        lin_t(c, B, gsr, d, w("merge.ws"), d, d, gmr, gmr,
+              rms_bwd_post("merge.ns", u.msrc + o, mrow(u.mrs, t, 1), nullptr, u.carry));
       else
-        rms_bwd(c, B, d, gmr, u.msrc + o, mrow(u.mrs, t, 1), w("merge.ns"), u.greg, u.greg);
+        lin_t(c, B, gsr, d, w("merge.ws"), d, d, gmr, gmr,
+              rms_bwd_post("merge.ns", u.msrc + o, mrow(u.mrs, t, 1), u.greg, u.greg));
       if (ck) merge_wgrad(t, B);
     } else {
       add(c, Bd, u.gu, nullptr, get);
