@@ -264,18 +264,29 @@ __global__ __launch_bounds__(256) void g_colsum(int M, int d, const float* __res
 }
 
 // ------------------------------------------------------------------ small kernels
-// Rotary rotation of the pairs (i, i + dh/2) of every head by sgn * pos * base^(-2i/dh),
-// pos = pos0 + row / rpp; angles and their cosine/sine in float64, rounded to fp32.
-__global__ void g_rope(int M, int H, int dh, float* x, int pos0, int rpp, double base, float sgn) {
+// cos and sin of pos * base^(-2i/dh) for positions 0..P-1 and i < dh/2: angles and their
+// cosine / sine in float64, rounded to fp32 (the rotary factors every kernel below reads).
+__global__ void g_rope_table(int P, int dh, double base, float2* __restrict__ tab) {
+  const int half = dh / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)P * half) return;
+  const int i = (int)(idx % half);
+  const double a = (double)(idx / half) * pow(base, -2.0 * i / dh);
+  tab[idx] = make_float2((float)cos(a), (float)sin(a));
+}
+
+// Rotary rotation of the pairs (i, i + dh/2) of every head by sgn * angle(pos, i),
+// pos = pos0 + row / rpp, with the table's factors.
+__global__ void g_rope(int M, int H, int dh, float* x, int pos0, int rpp, const float2* __restrict__ tab,
+                       float sgn) {
   const int half = dh / 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)M * H * half) return;
   const int i = (int)(idx % half);
   const int h = (int)((idx / half) % H);
   const int64_t row = idx / ((int64_t)half * H);
-  const double pos = (double)(pos0 + row / rpp);
-  const double a = pos * pow(base, -2.0 * i / dh);
-  const float c = (float)cos(a), s = sgn * (float)sin(a);
+  const float2 cs = tab[(pos0 + row / rpp) * half + i];
+  const float c = cs.x, s = sgn * cs.y;
   float* p = x + row * (int64_t)H * dh + (int64_t)h * dh;
   const float x1 = p[i], x2 = p[i + half];
   p[i] = x1 * c - x2 * s;
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(256) void g_reduce_rms_bwd(int M, int N, int splits
 // the pairs (i, i + dh/2) of the first nrot columns rotated by +angle as g_rope with
 // pos = pos0 + row / rpp. One thread per pair.
 __global__ void g_reduce_rope(int M, int N, int splits, const float* __restrict__ part, float* C, Seg sg, int dh,
-                              int nrot, int pos0, int rpp, double base) {
+                              int nrot, int pos0, int rpp, const float2* __restrict__ tab) {
   const int half = dh / 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)M * (N / 2)) return;
@@ -449,10 +460,8 @@ __global__ void g_reduce_rope(int M, int N, int splits, const float* __restrict_
   const float x2 = 0.f + part_sum(part, MN, splits, row * N + n2);
   float y1 = x1, y2 = x2;
   if (n1 < nrot) {
-    const int i = pi % half;
-    const double pos = (double)(pos0 + row / rpp);
-    const double a = pos * pow(base, -2.0 * i / dh);
-    const float c = (float)cos(a), s = 1.f * (float)sin(a);
+    const float2 cs = tab[(pos0 + row / rpp) * half + pi % half];
+    const float c = cs.x, s = 1.f * cs.y;
     y1 = x1 * c - x2 * s;
     y2 = x1 * s + x2 * c;
   }
@@ -624,17 +633,41 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
   }
 }
 
+// The float4 x holds elements 4 gl .. 4 gl + 3 of a head row of DH values spread over the
+// DH/4 lanes gl of a lane group; returns them rotated by -angle of position pos, as g_rope
+// with sgn -1 (the pair partner of an element sits in lane gl ^ DH/8 of the same group).
+// Every lane of the group must take part.
+template <int DH>
+__device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const float2* __restrict__ tab) {
+  constexpr int HG = DH / 8;
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+  const float ps[4] = {__shfl_xor(x.x, HG, WAVE), __shfl_xor(x.y, HG, WAVE), __shfl_xor(x.z, HG, WAVE),
+                       __shfl_xor(x.w, HG, WAVE)};
+  const bool first = gl < HG;
+  const int i0 = 4 * (gl & (HG - 1));
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 cs = tab[pos * (DH / 2) + i0 + e];
+    const float c = cs.x, sn = -1.f * cs.y;
+    y[e] = first ? xs[e] * c - ps[e] * sn : ps[e] * sn + xs[e] * c;
+  }
+  return make_float4(y[0], y[1], y[2], y[3]);
+}
+
 // Query side of the attention backward. With p_j = exp(s_j - lse) recomputed, D = dO.O,
 // dS_j = p_j (dO.v_j - D): dQ = scale * sum_j dS_j k_j; Dout (optional) = D;
 // KV: dK[row_j] += scale * dS_j q, dV[row_j] += p_j dO (plain read-modify-write: the launch
-// must hold at most one query per (sequence, head)).
+// must hold at most one query per (sequence, head)). rot 1: dQ leaves rotated back by the
+// query's position (the gradient before the rotary map); rot 2: also the key row of the
+// query's own position, whose last contribution this is.
 template <int DH, bool KV>
 __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int win, int H, float scale,
                                                     const float* __restrict__ Q, const float* __restrict__ K,
                                                     const float* __restrict__ Vv, const float* __restrict__ O,
                                                     const float* __restrict__ lse, const float* __restrict__ dO,
                                                     float* __restrict__ dQ, float* __restrict__ Dout, float* dK,
-                                                    float* dV) {
+                                                    float* dV, int rot, const float2* __restrict__ tab) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pdq[256];
   const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
@@ -654,7 +687,9 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
     const float ds = p * (gsum<G>(dot4(go, v)) - D);
     dq = fma4(ds, k, dq);
     if (KV) {
-      st4(dK + ro, fma4(ds, q, ld4(dK + ro)));
+      float4 nk = fma4(ds, q, ld4(dK + ro));
+      if (rot == 2 && j == tq) nk = rope_inv4<DH>(nk, gl, tq + 1, tab);   // the whole group takes j == tq
+      st4(dK + ro, nk);
       st4(dV + ro, fma4(p, go, ld4(dV + ro)));
     }
   }
@@ -666,7 +701,9 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
       const float4 x = pdq[k * G + tid];
       t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
     }
-    st4(dQ + (int64_t)r * hd + h * DH + tid * 4, make_float4(t.x * scale, t.y * scale, t.z * scale, t.w * scale));
+    float4 dqs = make_float4(t.x * scale, t.y * scale, t.z * scale, t.w * scale);
+    if (rot) dqs = rope_inv4<DH>(dqs, tid, tq + 1, tab);
+    st4(dQ + (int64_t)r * hd + h * DH + tid * 4, dqs);
     if (Dout && tid == 0) Dout[(int64_t)r * H + h] = D;
   }
 }
@@ -720,6 +757,7 @@ struct Ctx {
   hipStream_t st;
   float* part = nullptr;   // split-K partial sums of the small-M products
   int64_t part_cap = 0;    // floats
+  const float2* rope_tab = nullptr;   // rotary factors [position][d_head / 2]
   hipError_t err = hipSuccess;
   void check() {
     if (err == hipSuccess) err = hipGetLastError();
@@ -741,7 +779,6 @@ struct Post {
   const float* res = nullptr;     // RmsBwd: added to the input gradient (may alias out)
   float* out = nullptr;           // RmsBwd: input gradient
   int H = 0, dh = 0, nrot = 0, pos0 = 0, rpp = 1;   // Rope: columns [0, nrot) rotated, heads of dh
-  double base = 0.0;
   const float* f1 = nullptr;      // SwiGluBwd: FFN pre-activations
   const float* f3 = nullptr;
   float* g1 = nullptr;            // SwiGluBwd: their gradients
@@ -750,9 +787,9 @@ struct Post {
 void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p);
 
 // C = R + A.B (see g_gemm), or C += A.B split over k with atomics. Products with few
-// output tiles (the per-position products have B rows) split k over up to 16 slices whose
+// output tiles (the per-position products have B rows) split k over up to 32 slices whose
 // partial sums a second kernel adds in a fixed order (deterministic).
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, const float* Bm, int64_t ldb, bool bk,
           float* C, int64_t ldc, const float* R, bool atomic, const Seg& sg = Seg(), const Post& post = Post()) {
   // atomic: C += A.B; otherwise C = R + A.B
@@ -830,7 +867,7 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
       break;
     case Post::Rope:
       g_reduce_rope<<<blocks((int64_t)M * (N / 2)), 256, 0, c.st>>>(M, N, splits, part, C, sg, post.dh, post.nrot,
-                                                                   post.pos0, post.rpp, post.base);
+                                                                   post.pos0, post.rpp, c.rope_tab);
       break;
     case Post::SwiGlu:
       g_reduce_swiglu<<<blocks((int64_t)M * (N / 2)), 256, 0, c.st>>>(M, N / 2, splits, part, sg, post.y);
@@ -889,10 +926,10 @@ void colsum(Ctx& c, int M, int d, const float* dy, const float* x, const float* 
   g_colsum<<<grid, 256, 0, c.st>>>(M, d, dy, x, rstd, dg);
   c.check();
 }
-void rope(Ctx& c, int M, int H, int dh, float* x, int pos0, int rpp, double base, float sgn) {
+void rope(Ctx& c, int M, int H, int dh, float* x, int pos0, int rpp, float sgn) {
   const int64_t n = (int64_t)M * H * (dh / 2);
   if (n <= 0) return;
-  g_rope<<<blocks(n), 256, 0, c.st>>>(M, H, dh, x, pos0, rpp, base, sgn);
+  g_rope<<<blocks(n), 256, 0, c.st>>>(M, H, dh, x, pos0, rpp, c.rope_tab, sgn);
   c.check();
 }
 void fill(Ctx& c, float* p, int64_t n, float v) {
@@ -914,9 +951,9 @@ void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p)
     case Post::RmsBwd: rms_bwd(c, M, N, C, p.x, p.rs, p.g, p.res, p.out); break;
     case Post::Rope:
       if (sg.nseg) {
-        for (int q = 0; q < 3 && q * sg.nseg < p.nrot; ++q) rope(c, M, p.H, p.dh, sg.c[q], p.pos0, p.rpp, p.base, 1.f);
+        for (int q = 0; q < 3 && q * sg.nseg < p.nrot; ++q) rope(c, M, p.H, p.dh, sg.c[q], p.pos0, p.rpp, 1.f);
       } else {
-        rope(c, M, p.H, p.dh, C, p.pos0, p.rpp, p.base, 1.f);
+        rope(c, M, p.H, p.dh, C, p.pos0, p.rpp, 1.f);
       }
       break;
     case Post::SwiGlu:
@@ -949,23 +986,32 @@ void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const floa
 }
 template <int DH>
 void attn_bwd_q_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
-                  const float* O, const float* lse, const float* dO, float* dQ, float* Dout, float* dK, float* dV) {
+                  const float* O, const float* lse, const float* dO, float* dQ, float* Dout, float* dK, float* dV,
+                  int rot) {
   const float sc = 1.f / sqrtf((float)DH);
   if (dK)
-    g_attn_bwd_q<DH, true><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
+    g_attn_bwd_q<DH, true><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV,
+                                                     rot, c.rope_tab);
   else
-    g_attn_bwd_q<DH, false><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV);
+    g_attn_bwd_q<DH, false><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK,
+                                                      dV, rot, c.rope_tab);
 }
+// rot (see g_attn_bwd_q): 0 none, 1 dQ rotated back, 2 dQ and the key row of the query's
+// position (needs dK and one query position per launch)
 void attn_bwd_q(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
                 const float* V, const float* O, const float* lse, const float* dO, float* dQ, float* Dout,
-                float* dK, float* dV) {
+                float* dK, float* dV, int rot = 0) {
   if (nq <= 0) return;
+  if (rot == 2 && (!dK || nq != B)) {
+    if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
+    return;
+  }
   switch (dh) {
-    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
-    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
-    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
-    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
-    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV); break;
+    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
+    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
+    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
+    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
+    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
   }
   c.check();
 }
@@ -1010,6 +1056,7 @@ struct DecBuf {
 };
 struct Bufs {
   bool ck = false;
+  float2* rope_tab = nullptr;   // rotary factors of positions 0..T
   std::vector<float*> eh;   // L_E + 1 residual streams
   std::vector<EncBuf> enc;  // every layer, or one (checkpointing: each layer recomputed from eh)
   float *en, *ens;
@@ -1069,6 +1116,7 @@ void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
   u.geo = A.f(M * hd); u.geq = A.f(M * hd); u.gek = A.f(M * hd); u.gev = A.f(M * hd); u.Dq = A.f(M * H);
   u.part_n = (int64_t)kMaxSplits * B * std::max({d, hd, f, 2 * d, 3 * hd, 2 * f, (int64_t)c.vocab});
   u.part = A.f(u.part_n);
+  u.rope_tab = reinterpret_cast<float2*>(A.f((int64_t)2 * (T + 1) * (c.d_head / 2)));
   for (int l = 0; l < c.L_E; ++l) {
     u.qkv_e.push_back(A.f(3 * hd * d));
     u.w13_e.push_back(A.f(2 * f * d));
@@ -1104,6 +1152,7 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   plan(cf, B, T, checkpoint, A, u);
   c.part = u.part;
   c.part_cap = u.part_n;
+  c.rope_tab = u.rope_tab;
   const bool ck = checkpoint;
   const int M = B * T, d = cf.d, H = cf.n_heads, dh = cf.d_head, hd = H * dh, f = cf.ffn, V = cf.vocab;
   const double base = cf.rope_base;
@@ -1122,6 +1171,11 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
 
   for (auto& kv : Gm) fill(c, kv.second.first, kv.second.second, 0.f);
   if (T <= 0 || B <= 0) return c.err;
+  {
+    const int64_t n = (int64_t)(T + 1) * (dh / 2);
+    g_rope_table<<<blocks(n), 256, 0, c.st>>>(T + 1, dh, base, u.rope_tab);
+    c.check();
+  }
   {
     const int64_t qn = (int64_t)hd * d, fn = (int64_t)f * d;
     auto cat = [&](const std::string& pre, float* qkv, float* w13) {
@@ -1161,8 +1215,8 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       float* y[3] = {e.q, e.k, e.v};
       lin_n(c, M, e.a, d, u.qkv_e[l], hd, 3, y);
     }
-    rope(c, M, H, dh, e.q, 1, B, base, 1.f);
-    rope(c, M, H, dh, e.k, 1, B, base, 1.f);
+    rope(c, M, H, dh, e.q, 1, B, 1.f);
+    rope(c, M, H, dh, e.k, 1, B, 1.f);
     attn_fwd(c, M, B, 0, NOWIN, H, dh, e.q, e.k, e.v, e.o, e.lse);
     lin(c, M, e.o, hd, w(E(l, "wo")), hd, d, e.mid, u.eh[l]);
     rms_fwd(c, M, d, e.mid, w(E(l, "n2")), eps, e.c, e.rs2);
@@ -1186,7 +1240,7 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     rms_fwd(c, M, d, e_all, w("mem.nE"), eps, u.en, u.ens);
     for (int gi = 0; gi < cf.groups; ++gi) {
       lin(c, M, u.en, d, w(Mg(gi, "wk")), d, hd, u.mk[gi], nullptr);
-      rope(c, M, H, dh, u.mk[gi], 1, B, base, 1.f);
+      rope(c, M, H, dh, u.mk[gi], 1, B, 1.f);
       lin(c, M, u.en, d, w(Mg(gi, "wv")), d, hd, u.mv[gi], nullptr);
     }
   }
@@ -1215,7 +1269,7 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   // normalised: the block input's RMSNorm (s.a, s.rs1) was written by the producer of s.zin
   auto rope_post = [&](int nrot, int t) {
     Post p;
-    p.kind = Post::Rope; p.H = H; p.dh = dh; p.nrot = nrot; p.pos0 = t + 1; p.rpp = B; p.base = base;
+    p.kind = Post::Rope; p.H = H; p.dh = dh; p.nrot = nrot; p.pos0 = t + 1; p.rpp = B;
     return p;
   };
   auto rms_post = [&](const std::string& gain, float* y, float* rstd) {
@@ -1355,14 +1409,12 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       const int gi = grp(l);
       lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr);
       attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
-                 u.gmk[gi], u.gmv[gi]);
-      rope(c, B, H, dh, s.gqx, t + 1, B, base, -1.f);
+                 u.gmk[gi], u.gmv[gi], 1);   // the query gradient leaves rotated back
       lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr, rms_bwd_post(Dn(l, "m2"), s.z1, s.rs2, s.gz2, s.gz1));
       // window attention; the key/value gradient rows of t are complete afterwards
       lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr);
-      attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv);
-      rope(c, B, H, dh, s.gq, t + 1, B, base, -1.f);
-      rope(c, B, H, dh, s.gk, t + 1, B, base, -1.f);
+      // the query gradient and the (now complete) key gradient row of t leave rotated back
+      attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv, 2);
       {
         const float* gy[3] = {s.gq, s.gk, s.gv};
         float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
@@ -1402,7 +1454,7 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   // ------------------------------------------------------------ backward: memory
   if (cf.L_D > 0) {
     for (int gi = 0; gi < cf.groups; ++gi) {
-      rope(c, M, H, dh, u.gmk[gi], 1, B, base, -1.f);
+      rope(c, M, H, dh, u.gmk[gi], 1, B, -1.f);
       lin_t(c, M, u.gmk[gi], hd, w(Mg(gi, "wk")), d, d, u.tMd, gi == 0 ? nullptr : u.tMd);
       lin_t(c, M, u.gmv[gi], hd, w(Mg(gi, "wv")), d, d, u.tMd, u.tMd);
       wgrad(c, M, u.gmk[gi], hd, u.en, d, g(Mg(gi, "wk")), d);
@@ -1432,8 +1484,8 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     wgrad(c, M, u.gmid, d, e.o, hd, g(E(l, "wo")), hd);
     attn_bwd_q(c, M, B, 0, NOWIN, H, dh, e.q, e.k, e.v, e.o, e.lse, u.geo, u.geq, u.Dq, nullptr, nullptr);
     attn_bwd_kv(c, B, T, NOWIN, H, dh, e.q, e.k, e.v, e.lse, u.Dq, u.geo, u.gek, u.gev);
-    rope(c, M, H, dh, u.geq, 1, B, base, -1.f);
-    rope(c, M, H, dh, u.gek, 1, B, base, -1.f);
+    rope(c, M, H, dh, u.geq, 1, B, -1.f);
+    rope(c, M, H, dh, u.gek, 1, B, -1.f);
     {
       const float* gy[3] = {u.geq, u.gek, u.gev};
       lin_tk(c, M, gy, hd, 3, u.qkv_e[l], d, u.gec, nullptr);
