@@ -74,9 +74,8 @@ __device__ __forceinline__ P seg_pick(const P (&p)[3], int i) {
 // R, when given, has C's layout (it may be C itself). blockIdx.z takes k in
 // [z*kchunk, (z+1)*kchunk). With `part`, the k-slice z writes its partial sums to
 // part[z][M][N] instead (summed by g_splitk_reduce in a fixed order). PF k-steps of operand
-// loads are in flight at once (a register ring): the split products have short k ranges
-// and few workgroups, where the load round trip of every k-step would otherwise be paid
-// one after the other.
+// loads are in flight at once (a register ring; the launcher takes PF 1: the products with
+// short k slices, where deeper rings paid, now run on g_gemm_mfma).
 template <bool AK, bool BK, int PF>
 __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                                               const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
@@ -191,6 +190,109 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
       float* cc = Cp + (int64_t)gm * ldc + nn;
       if (atomic) atomicAdd(cc, acc[i][j]);
       else *cc = (Rp ? Rp[(int64_t)gm * ldc + nn] : 0.f) + acc[i][j];
+    }
+  }
+}
+
+// MFMA form of g_gemm (non-atomic) for k-contiguous A (A(m, k) = A[m*lda + k], segments
+// along k as g_gemm) and either orientation of B: a workgroup of 4 waves per 64x64 output
+// tile and k slice, wave w owning rows 16w..16w+15 and the tile's 4 column blocks of 16.
+// Operands go from memory straight into v_mfma_f32_16x16x4f32 fragments, no LDS: in each
+// 16-wide k block, lane l holds row (or column) l % 16 at the k quad 4 (l / 16) .. + 3 (one
+// float4 for k-contiguous operands, four loads for B(k, n) = B[k*ldb + n]), and the quad's
+// four elements feed four MFMAs; KB k blocks of loads are in flight. The MFMA result of
+// lane l, element t, is row 4 (l / 16) + t, column l % 16 of the 16x16 block. Every k
+// extent is a multiple of 4 (as for g_gemm).
+template <bool BK, int KB>
+__global__ __launch_bounds__(256) void g_gemm_mfma(int M, int N, int K, const float* __restrict__ A, int64_t lda,
+                                                   const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
+                                                   const float* R, int kchunk, float* __restrict__ part, Seg sg) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int kb = blockIdx.z * kchunk;
+  const int ke = min(K, kb + kchunk);
+  const int nbl = kb < ke ? (ke - kb + 15) / 16 : 0;   // k blocks of this slice
+  const int am = m0 + 16 * w + r;
+  float4 fa[KB], fb[KB][4];
+  auto load = [&](int blk, float4& a, float4 (&b)[4]) {
+    const int k = kb + blk * 16 + 4 * q;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    a = z;
+    if (am < M && k < ke) {
+      if (sg.kseg) {
+        const int sp = seg_of(k, sg.kseg);
+        a = *reinterpret_cast<const float4*>(seg_pick(sg.a, sp) + (int64_t)am * lda + k - sp * sg.kseg);
+      } else {
+        a = *reinterpret_cast<const float4*>(A + (int64_t)am * lda + k);
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int n = n0 + 16 * sb + r;
+      b[sb] = z;
+      if (n < N && k < ke) {
+        if (BK) {
+          b[sb] = *reinterpret_cast<const float4*>(Bm + (int64_t)n * ldb + k);
+        } else {
+          const float* bp = Bm + (int64_t)k * ldb + n;
+          b[sb].x = bp[0];
+          b[sb].y = bp[ldb];
+          b[sb].z = bp[2 * ldb];
+          b[sb].w = bp[3 * ldb];
+        }
+      }
+    }
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KB; ++j)
+    if (j < nbl) load(j, fa[j], fb[j]);
+  for (int b0 = 0; b0 < nbl; b0 += KB) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int blk = b0 + j;
+      if (blk < nbl) {
+        const float4 a = fa[j];
+        float4 bb[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) bb[sb] = fb[j][sb];
+        if (blk + KB < nbl) load(blk + KB, fa[j], fb[j]);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          acc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, bb[sb].x, acc[sb], 0, 0, 0);
+          acc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, bb[sb].y, acc[sb], 0, 0, 0);
+          acc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, bb[sb].z, acc[sb], 0, 0, 0);
+          acc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, bb[sb].w, acc[sb], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int gn = n0 + 16 * sb + r;
+    if (gn >= N) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int gm = m0 + 16 * w + 4 * q + t;
+      if (gm >= M) continue;
+      const float v = acc[sb][t];
+      if (part) {
+        part[((int64_t)blockIdx.z * M + gm) * N + gn] = v;
+        continue;
+      }
+      float* Cp = C;
+      const float* Rp = R;
+      int nn = gn;
+      if (sg.nseg) {
+        const int sp = seg_of(gn, sg.nseg);
+        Cp = seg_pick(sg.c, sp); Rp = seg_pick(sg.r, sp); nn = gn - sp * sg.nseg;
+      }
+      float r0 = 0.f;
+      if (Rp) r0 = Rp[(int64_t)gm * ldc + nn];
+      Cp[(int64_t)gm * ldc + nn] = r0 + v;
     }
   }
 }
@@ -815,7 +917,7 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
       R = C;
     }
   } else if (tm * tn < 128 && K >= 128 && c.part) {
-    splits = std::min({kMaxSplits, (256 + tm * tn - 1) / (tm * tn), K / 64});
+    splits = std::min({kMaxSplits, (512 + tm * tn - 1) / (tm * tn), K / 32});
     while (splits > 1 && (int64_t)splits * M * N > c.part_cap) --splits;
     if (splits > 1) part = c.part;
   }
@@ -826,24 +928,18 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   if (splits == 1) part = nullptr;
   dim3 grid(tn, tm, splits);
   const int at = atomic ? 1 : 0;
-  // deep prefetch for the split products (row-block products of B rows, short k slices)
-  const int pf = part == nullptr ? 1 : (kchunk / GK >= 8 ? 8 : 4);
-#define G_GEMM(AKV, BKV, PFV) \
-  g_gemm<AKV, BKV, PFV><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg)
-  if (ak && bk) {
-    if (pf == 8) G_GEMM(true, true, 8);
-    else if (pf == 4) G_GEMM(true, true, 4);
-    else G_GEMM(true, true, 1);
+  if (ak && !atomic) {   // k-contiguous A (every product but the weight gradients): the MFMA form
+    if (bk)
+      g_gemm_mfma<true, 4><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
+    else
+      g_gemm_mfma<false, 4><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
   } else if (ak) {
-    if (pf == 8) G_GEMM(true, false, 8);
-    else if (pf == 4) G_GEMM(true, false, 4);
-    else G_GEMM(true, false, 1);
-  } else if (bk) {
-    G_GEMM(false, true, 1);
+    if (bk) g_gemm<true, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+    else g_gemm<true, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
   } else {
-    G_GEMM(false, false, 1);
+    if (bk) g_gemm<false, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+    else g_gemm<false, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
   }
-#undef G_GEMM
   c.check();
   const bool row_kernel = post.kind == Post::RmsFwd || post.kind == Post::RmsBwd;
   if (part && row_kernel && N > 256 * kRowCols) {   // rows too long for the fused form
