@@ -762,14 +762,16 @@ __device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const flo
 // KV: dK[row_j] += scale * dS_j q, dV[row_j] += p_j dO (plain read-modify-write: the launch
 // must hold at most one query per (sequence, head)). rot 1: dQ leaves rotated back by the
 // query's position (the gradient before the rotary map); rot 2: also the key row of the
-// query's own position, whose last contribution this is.
+// query's own position, whose last contribution this is. With dO_part, dO is read as the
+// sum of dO_splits partial products [z][nq rows][H*DH] (the reduction its product skipped).
 template <int DH, bool KV>
 __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int win, int H, float scale,
                                                     const float* __restrict__ Q, const float* __restrict__ K,
                                                     const float* __restrict__ Vv, const float* __restrict__ O,
                                                     const float* __restrict__ lse, const float* __restrict__ dO,
                                                     float* __restrict__ dQ, float* __restrict__ Dout, float* dK,
-                                                    float* dV, int rot, const float2* __restrict__ tab) {
+                                                    float* dV, int rot, const float2* __restrict__ tab,
+                                                    const float* __restrict__ dO_part, int dO_splits) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pdq[256];
   const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
@@ -778,7 +780,18 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
   const int64_t qo = (int64_t)r * hd + h * DH + gl * 4;
   float4 q = ld4(Q + qo);
   q.x *= scale; q.y *= scale; q.z *= scale; q.w *= scale;
-  const float4 go = ld4(dO + qo);
+  float4 go;
+  if (dO_part) {   // dO still as the k-slice partial sums of its product: added here, z ascending
+    const int64_t MN = (int64_t)nq * hd;
+    go = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < dO_splits; ++z) {
+      const float4 v = ld4(dO_part + (int64_t)z * MN + qo);
+      go.x += v.x; go.y += v.y; go.z += v.z; go.w += v.w;
+    }
+    go.x = 0.f + go.x; go.y = 0.f + go.y; go.z = 0.f + go.z; go.w = 0.f + go.w;
+  } else {
+    go = ld4(dO + qo);
+  }
   const float D = gsum<G>(dot4(go, ld4(O + qo)));
   const float L = lse[(int64_t)r * H + h];
   float4 dq = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -870,8 +883,14 @@ inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 // The operation that consumes a product's rows, run by the split-K reduction when the product
 // splits, else by its own kernel after the product.
+// Partial sums of a split product whose reduction its consumer performs (Post::Defer).
+struct Deferred {
+  const float* part = nullptr;
+  int splits = 0;
+};
 struct Post {
-  enum Kind { None, RmsFwd, RmsBwd, Rope, SwiGlu, SwiGluBwd } kind = None;
+  enum Kind { None, RmsFwd, RmsBwd, Rope, SwiGlu, SwiGluBwd, Defer } kind = None;
+  Deferred* defer = nullptr;      // Defer: receives the partials (part null: C was written)
   const float* g = nullptr;       // RmsFwd / RmsBwd: gain
   float eps = 0.f;                // RmsFwd
   float* y = nullptr;             // RmsFwd: normalised rows; SwiGlu: silu(f1) f3
@@ -901,6 +920,7 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
     const bool nor = post.kind == Post::Rope || post.kind == Post::SwiGlu;
     if ((rows && (sg.nseg || ldc != N)) || (nor && R) || (post.kind == Post::SwiGlu && sg.nseg * 2 != N) ||
         (post.kind == Post::Rope && (sg.nseg ? sg.nseg : N) % (post.H * post.dh) != 0) ||
+        (post.kind == Post::Defer && (R || sg.nseg || ldc != N || !post.defer)) ||
         (post.kind != Post::None && atomic)) {
       if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
       return;
@@ -954,6 +974,10 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   switch (post.kind) {
     case Post::None:
       g_splitk_reduce<<<blocks((int64_t)M * N), 256, 0, c.st>>>(M, N, splits, part, R, C, ldc, sg);
+      break;
+    case Post::Defer:   // the consumer adds the slices; nothing is written to C
+      post.defer->part = part;
+      post.defer->splits = splits;
       break;
     case Post::RmsFwd:
       g_reduce_rms_fwd<<<M, 256, 0, c.st>>>(M, N, splits, part, R, C, post.g, post.eps, post.y, post.rstd);
@@ -1043,6 +1067,7 @@ void add(Ctx& c, int64_t n, const float* a, const float* b, float* out) {
 void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p) {
   switch (p.kind) {
     case Post::None: break;
+    case Post::Defer: *p.defer = Deferred(); break;
     case Post::RmsFwd: rms_fwd(c, M, N, C, p.g, p.eps, p.y, p.rstd); break;
     case Post::RmsBwd: rms_bwd(c, M, N, C, p.x, p.rs, p.g, p.res, p.out); break;
     case Post::Rope:
@@ -1083,31 +1108,31 @@ void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const floa
 template <int DH>
 void attn_bwd_q_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
                   const float* O, const float* lse, const float* dO, float* dQ, float* Dout, float* dK, float* dV,
-                  int rot) {
+                  int rot, const float* dO_part, int dO_splits) {
   const float sc = 1.f / sqrtf((float)DH);
   if (dK)
     g_attn_bwd_q<DH, true><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV,
-                                                     rot, c.rope_tab);
+                                                     rot, c.rope_tab, dO_part, dO_splits);
   else
     g_attn_bwd_q<DH, false><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK,
-                                                      dV, rot, c.rope_tab);
+                                                      dV, rot, c.rope_tab, dO_part, dO_splits);
 }
 // rot (see g_attn_bwd_q): 0 none, 1 dQ rotated back, 2 dQ and the key row of the query's
 // position (needs dK and one query position per launch)
 void attn_bwd_q(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
                 const float* V, const float* O, const float* lse, const float* dO, float* dQ, float* Dout,
-                float* dK, float* dV, int rot = 0) {
+                float* dK, float* dV, int rot = 0, const Deferred& dd = Deferred()) {
   if (nq <= 0) return;
   if (rot == 2 && (!dK || nq != B)) {
     if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
     return;
   }
   switch (dh) {
-    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
-    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
-    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
-    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
-    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot); break;
+    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
+    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
+    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
+    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
+    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
   }
   c.check();
 }
@@ -1437,6 +1462,11 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   // ------------------------------------------------ backward: transitions, reversed
   // weight and gain gradients of block l over `rows` rows starting at s (every position at
   // once, or one position with checkpointing)
+  auto defer_post = [](Deferred* dd) {
+    Post p;
+    p.kind = Post::Defer; p.defer = dd;
+    return p;
+  };
   auto rms_bwd_post = [&](const std::string& gain, const float* x, const float* rs, const float* res, float* out) {
     Post p;
     p.kind = Post::RmsBwd; p.g = w(gain); p.x = x; p.rs = rs; p.res = res; p.out = out;
@@ -1503,14 +1533,16 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       }
       // cross-attention over memory rows 1..t
       const int gi = grp(l);
-      lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr);
+      Deferred dd;   // dO of the attention: the product's slices, added by the attention backward
+      lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr, defer_post(&dd));
       attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
-                 u.gmk[gi], u.gmv[gi], 1);   // the query gradient leaves rotated back
+                 u.gmk[gi], u.gmv[gi], 1, dd);   // the query gradient leaves rotated back
       lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr, rms_bwd_post(Dn(l, "m2"), s.z1, s.rs2, s.gz2, s.gz1));
       // window attention; the key/value gradient rows of t are complete afterwards
-      lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr);
+      lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr, defer_post(&dd));
       // the query gradient and the (now complete) key gradient row of t leave rotated back
-      attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv, 2);
+      attn_bwd_q(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, u.tBhd, s.gq, nullptr, D.gk, D.gv, 2,
+                 dd);
       {
         const float* gy[3] = {s.gq, s.gk, s.gv};
         float* gin = l > 0 ? step(l - 1, t).gz3 : u.gu;
