@@ -114,7 +114,7 @@ def decode_sweep(shapes, batches, positions, steps: int = 8):
 
 
 FP32_PEAK_TFLOPS = 157.3
-GRAD_METRIC = "replay gradient (full BPTT) transitions/sec at batch B; % of fp32 vector roofline"
+GRAD_METRIC = "replay gradient (full BPTT) transitions/sec at batch B; % of fp32 MFMA roofline"
 
 
 def grad_flops(cfg, B: int, T: int) -> float:
@@ -185,7 +185,7 @@ def grad_bench(args, cfg):
                    "groups": cfg.groups, "vocab": cfg.vocab, "variant": f"RLT-{cfg.variant}",
                    "workspace_bytes": ws.numel(), "checkpoint": ck},
         "gradient_pass_ms": pass_ms,
-        "roofline": {"bound": "alu", "kernel": "gradient pass (saved forward + reverse scan + weight gradients)",
+        "roofline": {"bound": "mfma", "kernel": "gradient pass (saved forward + reverse scan + weight gradients)",
                      "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": fl},
     }
