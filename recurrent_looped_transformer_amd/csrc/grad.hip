@@ -297,6 +297,72 @@ __global__ __launch_bounds__(256) void g_gemm_mfma(int M, int N, int K, const fl
   }
 }
 
+// MFMA form of g_gemm<false, false> (the weight-gradient products dY^T X: A(m, k) =
+// A[k*lda + m], B(k, n) = B[k*ldb + n], both contiguous along m / n): 64x64 tiles, k steps
+// of 16 staged through LDS (one float4 per thread and operand, the next step's in
+// registers), wave w owning rows 16w..16w+15 and the tile's 4 column blocks of 16; lane l
+// reads its fragments at row / column l % 16 and k 4 (l / 16) + j for the j-th of four
+// v_mfma_f32_16x16x4f32 per k quad. C = R + A.B, C += A.B (atomic) or the k-slice partials.
+__global__ __launch_bounds__(256) void g_gemm_mfma_mn(int M, int N, int K, const float* __restrict__ A, int64_t lda,
+                                                      const float* __restrict__ Bm, int64_t ldb, float* C, int64_t ldc,
+                                                      const float* R, int atomic, int kchunk,
+                                                      float* __restrict__ part) {
+  __shared__ float As[GK][GT + 4];
+  __shared__ float Bs[GK][GT + 4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int kb = blockIdx.z * kchunk;
+  const int ke = min(K, kb + kchunk);
+  const int lk = tid >> 4, lc = 4 * (tid & 15);   // the thread's float4 of each operand tile
+  float4 ra, rb;
+  auto load = [&](int k0) {
+    const int gk = k0 + lk;
+    ra = make_float4(0.f, 0.f, 0.f, 0.f);
+    rb = ra;
+    if (gk < ke && m0 + lc < M) ra = *reinterpret_cast<const float4*>(A + (int64_t)gk * lda + m0 + lc);
+    if (gk < ke && n0 + lc < N) rb = *reinterpret_cast<const float4*>(Bm + (int64_t)gk * ldb + n0 + lc);
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += GK) {
+    __syncthreads();
+    *reinterpret_cast<float4*>(&As[lk][lc]) = ra;
+    *reinterpret_cast<float4*>(&Bs[lk][lc]) = rb;
+    __syncthreads();
+    if (k0 + GK < ke) load(k0 + GK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = As[4 * q + j][16 * w + r];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        acc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[4 * q + j][16 * sb + r], acc[sb], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int gn = n0 + 16 * sb + r;
+    if (gn >= N) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int gm = m0 + 16 * w + 4 * q + t;
+      if (gm >= M) continue;
+      const float v = acc[sb][t];
+      if (part) {
+        part[((int64_t)blockIdx.z * M + gm) * N + gn] = v;
+      } else if (atomic) {
+        atomicAdd(C + (int64_t)gm * ldc + gn, v);
+      } else {
+        float r0 = 0.f;
+        if (R) r0 = R[(int64_t)gm * ldc + gn];
+        C[(int64_t)gm * ldc + gn] = r0 + v;
+      }
+    }
+  }
+}
+
 // C[m, n] = (R ? R[m, n] : 0) + sum_{z < splits} part[z][m][n], z ascending
 __global__ void g_splitk_reduce(int M, int N, int splits, const float* __restrict__ part, const float* R, float* C,
                                 int64_t ldc, Seg sg) {
@@ -956,9 +1022,12 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   } else if (ak) {
     if (bk) g_gemm<true, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
     else g_gemm<true, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  } else if (bk) {
+    g_gemm<false, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+  } else if (sg.kseg == 0 && sg.nseg == 0) {   // the weight gradients: MFMA with LDS-staged operands
+    g_gemm_mfma_mn<<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part);
   } else {
-    if (bk) g_gemm<false, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
-    else g_gemm<false, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
+    g_gemm<false, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
   }
   c.check();
   const bool row_kernel = post.kind == Post::RmsFwd || post.kind == Post::RmsBwd;
