@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void g_gemm(int M, int N, int K, const float* 
 // Operands go from memory straight into v_mfma_f32_16x16x4f32 fragments, no LDS: in each
 // 16-wide k block, lane l holds row (or column) l % 16 at the k quad 4 (l / 16) .. + 3 (one
 // float4 for k-contiguous operands, four loads for B(k, n) = B[k*ldb + n]), and the quad's
-// four elements feed four MFMAs; KB k blocks of loads are in flight. The MFMA result of
+// four elements feed four MFMAs; KB k blocks of loads are in flight (2 measured best). The MFMA result of
 // lane l, element t, is row 4 (l / 16) + t, column l % 16 of the 16x16 block. Every k
 // extent is a multiple of 4 (as for g_gemm).
 template <bool BK, int KB>
@@ -850,6 +850,7 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
   if (dO_part) {   // dO still as the k-slice partial sums of its product: added here, z ascending
     const int64_t MN = (int64_t)nq * hd;
     go = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int z = 0; z < dO_splits; ++z) {
       const float4 v = ld4(dO_part + (int64_t)z * MN + qo);
       go.x += v.x; go.y += v.y; go.z += v.z; go.w += v.w;
@@ -1016,9 +1017,9 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   const int at = atomic ? 1 : 0;
   if (ak && !atomic) {   // k-contiguous A (every product but the weight gradients): the MFMA form
     if (bk)
-      g_gemm_mfma<true, 4><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
+      g_gemm_mfma<true, 2><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
     else
-      g_gemm_mfma<false, 4><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
+      g_gemm_mfma<false, 2><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, kchunk, part, sg);
   } else if (ak) {
     if (bk) g_gemm<true, true, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
     else g_gemm<true, false, 1><<<grid, 256, 0, c.st>>>(M, N, K, A, lda, Bm, ldb, C, ldc, R, at, kchunk, part, sg);
