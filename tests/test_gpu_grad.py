@@ -5,10 +5,11 @@ pinned to the numpy oracle's forward and to finite differences). The GPU path ru
 throughout. Bars (derivation: every gradient entry is a sum of fp32 products over up to
 T*B rows and through L_E + L_D blocks of T dependent steps; fp32 rounding u = 6e-8 grows
 like sqrt(terms) per sum and roughly linearly along the chain, which stays below 1e-5
-relative at these sizes; the bar leaves a margin of about 10 above the measured worst):
+relative at these sizes; the bars leave a margin of about 5 and 10 above the measured worst):
   - logprob: max |gpu - oracle| <= 2e-5;
   - every parameter gradient: ||gpu - oracle||_2 <= 5e-5 ||oracle||_2 + 1e-7 sqrt(n)
-    (measured worst: 3.3e-6 on logprob, 6e-6 relative on a gradient, at the 512-wide shape).
+    (measured worst with the MFMA products: 4.2e-6 on logprob (the ragged shape), 4.6e-6
+    relative on a gradient (the 512-wide shape)).
 Cases: the tiny fp32 configuration and its variants (RLT-0, RLT-2 with K_c = 3, one memory
 group per layer, shared encoder/decoder weights, window 1, no decoder), and a ragged shape
 (d 128, f 320, B 3, T 37: GEMM tiles with a tail in every dimension, windows that slide).
