@@ -830,6 +830,7 @@ __device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const flo
 // query's position (the gradient before the rotary map); rot 2: also the key row of the
 // query's own position, whose last contribution this is. With dO_part, dO is read as the
 // sum of dO_splits partial products [z][nq rows][H*DH] (the reduction its product skipped).
+// dO_save (optional) receives dO, Dout (optional) D, for a later key-side pass.
 template <int DH, bool KV>
 __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int win, int H, float scale,
                                                     const float* __restrict__ Q, const float* __restrict__ K,
@@ -837,7 +838,8 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
                                                     const float* __restrict__ lse, const float* __restrict__ dO,
                                                     float* __restrict__ dQ, float* __restrict__ Dout, float* dK,
                                                     float* dV, int rot, const float2* __restrict__ tab,
-                                                    const float* __restrict__ dO_part, int dO_splits) {
+                                                    const float* __restrict__ dO_part, int dO_splits,
+                                                    float* __restrict__ dO_save) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pdq[256];
   const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
@@ -859,6 +861,7 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
   } else {
     go = ld4(dO + qo);
   }
+  if (dO_save && gi == 0) st4(dO_save + qo, go);
   const float D = gsum<G>(dot4(go, ld4(O + qo)));
   const float L = lse[(int64_t)r * H + h];
   float4 dq = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -892,13 +895,13 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
 
 // Key side of the attention backward for token-parallel causal attention over T positions:
 // a block per (key row kr = tk*B + b, head); queries i in [tk, min(T-1, tk + win - 1)] at
-// rows i*B + b. dK = scale * sum_i dS_i q_i, dV = sum_i p_i dO_i (written).
+// rows i*B + b. dK = scale * sum_i dS_i q_i, dV = sum_i p_i dO_i (written, or added when acc).
 template <int DH>
 __global__ __launch_bounds__(256) void g_attn_bwd_kv(int B, int T, int win, int H, float scale,
                                                      const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ Vv, const float* __restrict__ lse,
                                                      const float* __restrict__ Dq, const float* __restrict__ dO,
-                                                     float* __restrict__ dK, float* __restrict__ dV) {
+                                                     float* __restrict__ dK, float* __restrict__ dV, int acc) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pk[256], pv[256];
   const int kr = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
@@ -929,8 +932,14 @@ __global__ __launch_bounds__(256) void g_attn_bwd_kv(int B, int T, int win, int 
       c.x += y.x; c.y += y.y; c.z += y.z; c.w += y.w;
     }
     const int64_t o = (int64_t)kr * hd + h * DH + tid * 4;
-    st4(dK + o, make_float4(a.x * scale, a.y * scale, a.z * scale, a.w * scale));
-    st4(dV + o, c);
+    float4 nk = make_float4(a.x * scale, a.y * scale, a.z * scale, a.w * scale), nv = c;
+    if (acc) {
+      const float4 pk = ld4(dK + o), pv = ld4(dV + o);
+      nk = make_float4(pk.x + nk.x, pk.y + nk.y, pk.z + nk.z, pk.w + nk.w);
+      nv = make_float4(pv.x + nv.x, pv.y + nv.y, pv.z + nv.z, pv.w + nv.w);
+    }
+    st4(dK + o, nk);
+    st4(dV + o, nv);
   }
 }
 
@@ -1178,48 +1187,50 @@ void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const floa
 template <int DH>
 void attn_bwd_q_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
                   const float* O, const float* lse, const float* dO, float* dQ, float* Dout, float* dK, float* dV,
-                  int rot, const float* dO_part, int dO_splits) {
+                  int rot, const float* dO_part, int dO_splits, float* dO_save) {
   const float sc = 1.f / sqrtf((float)DH);
   if (dK)
     g_attn_bwd_q<DH, true><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK, dV,
-                                                     rot, c.rope_tab, dO_part, dO_splits);
+                                                     rot, c.rope_tab, dO_part, dO_splits, dO_save);
   else
     g_attn_bwd_q<DH, false><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, sc, Q, K, V, O, lse, dO, dQ, Dout, dK,
-                                                      dV, rot, c.rope_tab, dO_part, dO_splits);
+                                                      dV, rot, c.rope_tab, dO_part, dO_splits, dO_save);
 }
 // rot (see g_attn_bwd_q): 0 none, 1 dQ rotated back, 2 dQ and the key row of the query's
 // position (needs dK and one query position per launch)
 void attn_bwd_q(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
                 const float* V, const float* O, const float* lse, const float* dO, float* dQ, float* Dout,
-                float* dK, float* dV, int rot = 0, const Deferred& dd = Deferred()) {
+                float* dK, float* dV, int rot = 0, const Deferred& dd = Deferred(), float* dO_save = nullptr) {
   if (nq <= 0) return;
   if (rot == 2 && (!dK || nq != B)) {
     if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
     return;
   }
   switch (dh) {
-    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
-    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
-    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
-    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
-    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits); break;
+    case 16: attn_bwd_q_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits, dO_save); break;
+    case 32: attn_bwd_q_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits, dO_save); break;
+    case 64: attn_bwd_q_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits, dO_save); break;
+    case 128: attn_bwd_q_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits, dO_save); break;
+    default: attn_bwd_q_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dO, dQ, Dout, dK, dV, rot, dd.part, dd.splits, dO_save); break;
   }
   c.check();
 }
 template <int DH>
-void attn_bwd_kv_n(Ctx& c, int B, int T, int win, int H, const float* Q, const float* K, const float* V,
+void attn_bwd_kv_n(Ctx& c, int B, int T, int win, int H, const float* Q, const float* K, const float* V, int acc,
                    const float* lse, const float* Dq, const float* dO, float* dK, float* dV) {
-  g_attn_bwd_kv<DH><<<B * T * H, 256, 0, c.st>>>(B, T, win, H, 1.f / sqrtf((float)DH), Q, K, V, lse, Dq, dO, dK, dV);
+  g_attn_bwd_kv<DH><<<B * T * H, 256, 0, c.st>>>(B, T, win, H, 1.f / sqrtf((float)DH), Q, K, V, lse, Dq, dO, dK, dV,
+                                                  acc);
 }
+// acc: add to dK / dV instead of writing them
 void attn_bwd_kv(Ctx& c, int B, int T, int win, int H, int dh, const float* Q, const float* K, const float* V,
-                 const float* lse, const float* Dq, const float* dO, float* dK, float* dV) {
+                 const float* lse, const float* Dq, const float* dO, float* dK, float* dV, int acc = 0) {
   if (B * T <= 0) return;
   switch (dh) {
-    case 16: attn_bwd_kv_n<16>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
-    case 32: attn_bwd_kv_n<32>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
-    case 64: attn_bwd_kv_n<64>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
-    case 128: attn_bwd_kv_n<128>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
-    default: attn_bwd_kv_n<256>(c, B, T, win, H, Q, K, V, lse, Dq, dO, dK, dV); break;
+    case 16: attn_bwd_kv_n<16>(c, B, T, win, H, Q, K, V, acc, lse, Dq, dO, dK, dV); break;
+    case 32: attn_bwd_kv_n<32>(c, B, T, win, H, Q, K, V, acc, lse, Dq, dO, dK, dV); break;
+    case 64: attn_bwd_kv_n<64>(c, B, T, win, H, Q, K, V, acc, lse, Dq, dO, dK, dV); break;
+    case 128: attn_bwd_kv_n<128>(c, B, T, win, H, Q, K, V, acc, lse, Dq, dO, dK, dV); break;
+    default: attn_bwd_kv_n<256>(c, B, T, win, H, Q, K, V, acc, lse, Dq, dO, dK, dV); break;
   }
   c.check();
 }
@@ -1244,6 +1255,7 @@ struct EncBuf {  // one encoder layer, M = T*B rows
 struct DecBuf {
   float *zin, *a, *rs1, *q, *k, *v, *o, *lse1, *z1, *b, *rs2, *qx, *ox, *lse2, *z2, *c, *rs3, *f1, *f3, *g;
   float *gq, *gk, *gv, *gz1, *gqx, *gz2, *gz3, *gda, *gdb, *gdc, *gf1, *gf3;
+  float *dO2 = nullptr, *D2 = nullptr;   // intermediates kept: cross-attention dO and D of every row
 };
 struct Bufs {
   bool ck = false;
@@ -1293,6 +1305,10 @@ void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
     D.gq = A.f(Ms * hd); D.gz1 = A.f(Ms * d); D.gqx = A.f(Ms * hd);
     D.gz2 = A.f(Ms * d); D.gz3 = A.f(Ms * d); D.gda = A.f(Ms * d); D.gdb = A.f(Ms * d); D.gdc = A.f(Ms * d);
     D.gf1 = A.f(Ms * f); D.gf3 = A.f(Ms * f);
+    if (!ck) {
+      D.dO2 = A.f(M * hd);
+      D.D2 = A.f(M * H);
+    }
   }
   const bool mg = c.variant != RLT_V0;
   const int64_t Mm = mg ? M : 0, Mms = mg ? Ms : 0;
@@ -1322,6 +1338,7 @@ void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
 struct Step {
   float *zin, *a, *rs1, *q, *k, *v, *o, *lse1, *z1, *b, *rs2, *qx, *ox, *lse2, *z2, *c, *rs3, *f1, *f3, *g;
   float *gq, *gk, *gv, *gz1, *gqx, *gz2, *gz3, *gda, *gdb, *gdc, *gf1, *gf3;
+  float *dO2 = nullptr, *D2 = nullptr;
 };
 
 }  // namespace
@@ -1394,6 +1411,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     s.gq = D.gq + Rs * hd; s.gz1 = D.gz1 + Rs * d; s.gqx = D.gqx + Rs * hd; s.gz2 = D.gz2 + Rs * d;
     s.gz3 = D.gz3 + Rs * d; s.gda = D.gda + Rs * d; s.gdb = D.gdb + Rs * d; s.gdc = D.gdc + Rs * d;
     s.gf1 = D.gf1 + Rs * f; s.gf3 = D.gf3 + Rs * f;
+    if (D.dO2) {
+      s.dO2 = D.dO2 + R0 * hd;
+      s.D2 = D.D2 + R0 * H;
+    }
     return s;
   };
   auto mrow = [&](float* p, int t, int64_t width) { return p + (ck ? 0 : (int64_t)t * B * width); };
@@ -1605,8 +1626,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
       const int gi = grp(l);
       Deferred dd;   // dO of the attention: the product's slices, added by the attention backward
       lin_t(c, B, s.gz2, d, w(Dn(l, "xo")), hd, hd, u.tBhd, nullptr, defer_post(&dd));
-      attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
-                 u.gmk[gi], u.gmv[gi], 1, dd);   // the query gradient leaves rotated back
+      // the query gradient leaves rotated back; the memory's key / value gradients come from
+      // the key-side pass after the scan when every row's dO and D are kept, else here
+      if (s.dO2)
+        attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, s.D2, nullptr,
+                   nullptr, 1, dd, s.dO2);
+      else
+        attn_bwd_q(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[gi], u.mv[gi], s.ox, s.lse2, u.tBhd, s.gqx, nullptr,
+                   u.gmk[gi], u.gmv[gi], 1, dd);
       lin_t(c, B, s.gqx, hd, w(Dn(l, "xq")), d, d, s.gdb, nullptr, rms_bwd_post(Dn(l, "m2"), s.z1, s.rs2, s.gz2, s.gz1));
       // window attention; the key/value gradient rows of t are complete afterwards
       lin_t(c, B, s.gz1, d, w(Ds(l, "wo")), hd, hd, u.tBhd, nullptr, defer_post(&dd));
@@ -1648,6 +1675,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   if (!ck) {
     for (int l = 0; l < cf.L_D; ++l) layer_wgrad(l, step(l, 0), M);
     if (mg) merge_wgrad(0, M);
+  }
+  // the memory's key / value gradients, one key-side pass per decoder layer over every
+  // (query, key) pair of its cross-attention (keys 1..t for the query at t)
+  for (int l = 0; l < cf.L_D; ++l) {
+    const DecBuf& D = u.dec[l];
+    if (!D.dO2) break;
+    attn_bwd_kv(c, B, T, NOWIN, H, dh, D.qx, u.mk[grp(l)], u.mv[grp(l)], D.lse2, D.D2, D.dO2, u.gmk[grp(l)],
+                u.gmv[grp(l)], 1);
   }
   // ------------------------------------------------------------ backward: memory
   if (cf.L_D > 0) {
