@@ -16,23 +16,29 @@
 //              (rows are position-major: row = t*B + b), then the readout of all rows;
 //   loss     : float64 log-sum-exp per row, logprob and dL/dlogits;
 //   backward : readout; the decoder in reverse time -- at position t each layer's FFN,
-//              cross-attention (its key/value gradient goes straight into the memory
-//              gradient rows 1..t) and window attention (into the key/value gradient rows
-//              of the window; the row of t is complete once t itself is done, because only
-//              queries t..t+W-1 read it), then the merge, whose state-input gradient is
-//              carried to position t-1 (RLT-1) or collected for the chunk register's source
-//              position (RLT-2); the weight gradients of every decoder matrix are then one
-//              GEMM over all T*B rows each; memory projection; encoder blocks in reverse.
+//              cross-attention (its key/value gradient goes into the memory gradient rows
+//              1..t at once, or, with every intermediate kept, from a key-side pass per
+//              layer after the scan, from the stored dO and D of every row) and window
+//              attention (into the key/value gradient rows of the window; the row of t is
+//              complete once t itself is done, because only queries t..t+W-1 read it), then
+//              the merge, whose state-input gradient is carried to position t-1 (RLT-1) or
+//              collected for the chunk register's source position (RLT-2); the weight
+//              gradients of every decoder matrix are then one product over all T*B rows
+//              each; memory projection; encoder blocks in reverse.
 //
-// Kernels: a 64x64-tiled fp32 GEMM with both operand orientations (and split-K with
-// atomic accumulation for the weight gradients, whose reduction runs over T*B rows);
-// wave-per-row RMSNorm forward/backward; column reductions for gains and biases; rotary
-// rotation by +/- angle (float64 angles, as in the forward path); attention with a block
-// per (query, head) and dh/4 lanes per key (forward with per-group online softmax and the
-// log-sum-exp kept; backward with probabilities recomputed from the log-sum-exp: a
-// query-side kernel that can also update the key/value gradient rows when each launch
-// holds one query per (sequence, head), and a key-side kernel for the causal encoder);
-// SwiGLU, merge and readout elementwise kernels.
+// Kernels: fp32 products on v_mfma_f32_16x16x4f32 -- operands straight from memory into
+// fragments for k-contiguous A, LDS-staged for the weight gradients (m-contiguous A, with
+// atomic split-K accumulation over the T*B rows) -- and a 64x64 FMA tile for the other
+// orientations; products of B rows split k into slices whose partial sums are added in a
+// fixed order by a reduction fused with the consumer of the rows (RMSNorm forward or
+// backward, rotary, SwiGLU, or the attention backward reading its dO); wave-per-row
+// RMSNorm forward/backward; column reductions for gains and biases; rotary rotation by +/-
+// angle from a per-call table (float64 angles rounded to fp32, as in the forward path);
+// attention with a block per (query, head) and dh/4 lanes per key (forward with per-group
+// online softmax and the log-sum-exp kept; backward with probabilities recomputed from the
+// log-sum-exp: a query-side kernel that can also update the key/value gradient rows when
+// each launch holds one query per (sequence, head), and a key-side kernel for the causal
+// encoder and the memory); SwiGLU, merge and readout elementwise kernels.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
