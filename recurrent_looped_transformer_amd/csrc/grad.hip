@@ -761,19 +761,63 @@ __device__ __forceinline__ float4 fma4(float s, float4 a, float4 c) {
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
-// Online softmax per group, the groups merged at the end: O and lse.
+// The float4 x holds elements 4 gl .. 4 gl + 3 of a head row of DH values spread over the
+// DH/4 lanes gl of a lane group; returns them rotated by sgn * angle of position pos, as
+// g_rope (the pair partner of an element sits in lane gl ^ DH/8 of the same group).
+// Every lane of the group must take part.
+template <int DH>
+__device__ __forceinline__ float4 rope4(float4 x, int gl, int pos, const float2* __restrict__ tab, float sgn) {
+  constexpr int HG = DH / 8;
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+  const float ps[4] = {__shfl_xor(x.x, HG, WAVE), __shfl_xor(x.y, HG, WAVE), __shfl_xor(x.z, HG, WAVE),
+                       __shfl_xor(x.w, HG, WAVE)};
+  const bool first = gl < HG;
+  const int i0 = 4 * (gl & (HG - 1));
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 cs = tab[pos * (DH / 2) + i0 + e];
+    const float c = cs.x, sn = sgn * cs.y;
+    y[e] = first ? xs[e] * c - ps[e] * sn : ps[e] * sn + xs[e] * c;
+  }
+  return make_float4(y[0], y[1], y[2], y[3]);
+}
+template <int DH>
+__device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const float2* __restrict__ tab) {
+  return rope4<DH>(x, gl, pos, tab, -1.f);
+}
+
+// Online softmax per group, the groups merged at the end: O and lse. With q_part, q is the
+// sum of q_splits partial products [z][nq rows][H*DH]; with tab, q is first rotated by
+// +angle of its position (the projection's rotary map) and, with q_save, stored rotated.
 template <int DH>
 __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int win, int H, float scale,
                                                   const float* __restrict__ Q, const float* __restrict__ K,
                                                   const float* __restrict__ Vv, float* __restrict__ O,
-                                                  float* __restrict__ lse) {
+                                                  float* __restrict__ lse, const float* __restrict__ q_part,
+                                                  int q_splits, const float2* __restrict__ tab, float* q_save) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pacc[256];
   __shared__ float pm[NG], pl[NG];
   const int r = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x, gi = tid / G, gl = tid % G;
   const int hd = H * DH, b = r % B, tq = tq0 + r / B;
   const int lo = max(0, tq - win + 1);
-  float4 q = ld4(Q + (int64_t)r * hd + h * DH + gl * 4);
+  const int64_t qo = (int64_t)r * hd + h * DH + gl * 4;
+  float4 q;
+  if (q_part) {   // q still as the k-slice partial sums of its product: added here, z ascending
+    const int64_t MN = (int64_t)nq * hd;
+    q = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int z = 0; z < q_splits; ++z) {
+      const float4 v = ld4(q_part + (int64_t)z * MN + qo);
+      q.x += v.x; q.y += v.y; q.z += v.z; q.w += v.w;
+    }
+    q.x = 0.f + q.x; q.y = 0.f + q.y; q.z = 0.f + q.z; q.w = 0.f + q.w;
+  } else {
+    q = ld4(Q + qo);
+  }
+  if (tab) q = rope4<DH>(q, gl, tq + 1, tab, 1.f);   // the projection's rotary map, applied here
+  const float4 q_rot = q;
   q.x *= scale; q.y *= scale; q.z *= scale; q.w *= scale;
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -804,30 +848,10 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
     const float inv = 1.f / den;
     st4(O + (int64_t)r * hd + h * DH + tid * 4, make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
     if (tid == 0) lse[(int64_t)r * H + h] = M + logf(den);
+    if (q_save) st4(q_save + qo, q_rot);   // after every group has read Q (q_save may be Q)
   }
 }
 
-// The float4 x holds elements 4 gl .. 4 gl + 3 of a head row of DH values spread over the
-// DH/4 lanes gl of a lane group; returns them rotated by -angle of position pos, as g_rope
-// with sgn -1 (the pair partner of an element sits in lane gl ^ DH/8 of the same group).
-// Every lane of the group must take part.
-template <int DH>
-__device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const float2* __restrict__ tab) {
-  constexpr int HG = DH / 8;
-  const float xs[4] = {x.x, x.y, x.z, x.w};
-  const float ps[4] = {__shfl_xor(x.x, HG, WAVE), __shfl_xor(x.y, HG, WAVE), __shfl_xor(x.z, HG, WAVE),
-                       __shfl_xor(x.w, HG, WAVE)};
-  const bool first = gl < HG;
-  const int i0 = 4 * (gl & (HG - 1));
-  float y[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float2 cs = tab[pos * (DH / 2) + i0 + e];
-    const float c = cs.x, sn = -1.f * cs.y;
-    y[e] = first ? xs[e] * c - ps[e] * sn : ps[e] * sn + xs[e] * c;
-  }
-  return make_float4(y[0], y[1], y[2], y[3]);
-}
 
 // Query side of the attention backward. With p_j = exp(s_j - lse) recomputed, D = dO.O,
 // dS_j = p_j (dO.v_j - D): dQ = scale * sum_j dS_j k_j; Dout (optional) = D;
@@ -1175,18 +1199,23 @@ void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p)
 
 template <int DH>
 void attn_fwd_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
-                float* O, float* lse) {
-  g_attn_fwd<DH><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, 1.f / sqrtf((float)DH), Q, K, V, O, lse);
+                float* O, float* lse, const Deferred& dq, const float2* tab, float* q_save) {
+  g_attn_fwd<DH><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, 1.f / sqrtf((float)DH), Q, K, V, O, lse, dq.part,
+                                           dq.splits, tab, q_save);
 }
+// rot: Q (or the slices dq of its product) is the unrotated query; it is rotated by the
+// query's position here and stored rotated to Q
 void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
-              const float* V, float* O, float* lse) {
+              const float* V, float* O, float* lse, const Deferred& dq = Deferred(), bool rot = false) {
   if (nq <= 0) return;
+  const float2* tab = rot ? c.rope_tab : nullptr;
+  float* qs = rot ? const_cast<float*>(Q) : nullptr;
   switch (dh) {
-    case 16: attn_fwd_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
-    case 32: attn_fwd_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
-    case 64: attn_fwd_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
-    case 128: attn_fwd_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
-    default: attn_fwd_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse); break;
+    case 16: attn_fwd_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
+    case 32: attn_fwd_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
+    case 64: attn_fwd_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
+    case 128: attn_fwd_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
+    default: attn_fwd_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
   }
   c.check();
 }
@@ -1507,8 +1536,14 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     }
     attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1);
     lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin, rms_post(Dn(l, "m2"), s.b, s.rs2));
-    lin(c, B, s.b, d, w(Dn(l, "xq")), d, hd, s.qx, nullptr, rope_post(hd, t));
-    attn_fwd(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[grp(l)], u.mv[grp(l)], s.ox, s.lse2);
+    {   // the cross-attention query: its product's slices (or the product) summed, rotated and
+        // stored by the attention kernel
+      Deferred dq;
+      Post p;
+      p.kind = Post::Defer; p.defer = &dq;
+      lin(c, B, s.b, d, w(Dn(l, "xq")), d, hd, s.qx, nullptr, p);
+      attn_fwd(c, B, B, t, NOWIN, H, dh, s.qx, u.mk[grp(l)], u.mv[grp(l)], s.ox, s.lse2, dq, true);
+    }
     lin(c, B, s.ox, hd, w(Dn(l, "xo")), hd, d, s.z2, s.z1, rms_post(Dn(l, "m3"), s.c, s.rs3));
     {
       float* y[2] = {s.f1, s.f3};
