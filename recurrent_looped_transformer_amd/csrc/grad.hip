@@ -788,14 +788,18 @@ __device__ __forceinline__ float4 rope_inv4(float4 x, int gl, int pos, const flo
 }
 
 // Online softmax per group, the groups merged at the end: O and lse. With q_part, q is the
-// sum of q_splits partial products [z][nq rows][H*DH]; with tab, q is first rotated by
+// sum of q_splits partial products [z][nq rows][part_ld]; with tab, q is first rotated by
 // +angle of its position (the projection's rotary map) and, with q_save, stored rotated.
+// With kv_k / kv_v (= K / V), this launch also produces the key / value row of each query's
+// own position (from the slices at columns hd / 2 hd, or from K / V unrotated), rotates the
+// key, attends to it from registers and stores both.
 template <int DH>
 __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int win, int H, float scale,
                                                   const float* __restrict__ Q, const float* __restrict__ K,
                                                   const float* __restrict__ Vv, float* __restrict__ O,
                                                   float* __restrict__ lse, const float* __restrict__ q_part,
-                                                  int q_splits, const float2* __restrict__ tab, float* q_save) {
+                                                  int q_splits, int part_ld, const float2* __restrict__ tab,
+                                                  float* q_save, float* kv_k, float* kv_v) {
   constexpr int G = DH / 4, NG = 256 / G;
   __shared__ float4 pacc[256];
   __shared__ float pm[NG], pl[NG];
@@ -803,18 +807,26 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
   const int hd = H * DH, b = r % B, tq = tq0 + r / B;
   const int lo = max(0, tq - win + 1);
   const int64_t qo = (int64_t)r * hd + h * DH + gl * 4;
-  float4 q;
-  if (q_part) {   // q still as the k-slice partial sums of its product: added here, z ascending
-    const int64_t MN = (int64_t)nq * hd;
-    q = make_float4(0.f, 0.f, 0.f, 0.f);
+  // q (and, with kv_k, the key / value row of position tq) still as the k-slice partial sums of
+  // their product (rows of part_ld columns: q, then k and v at hd and 2 hd): added here, z
+  // ascending
+  auto psum = [&](int col) {
+    const int64_t MN = (int64_t)nq * part_ld;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
     for (int z = 0; z < q_splits; ++z) {
-      const float4 v = ld4(q_part + (int64_t)z * MN + qo);
-      q.x += v.x; q.y += v.y; q.z += v.z; q.w += v.w;
+      const float4 v = ld4(q_part + (int64_t)z * MN + (int64_t)r * part_ld + col);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
     }
-    q.x = 0.f + q.x; q.y = 0.f + q.y; q.z = 0.f + q.z; q.w = 0.f + q.w;
-  } else {
-    q = ld4(Q + qo);
+    return make_float4(0.f + a.x, 0.f + a.y, 0.f + a.z, 0.f + a.w);
+  };
+  float4 q = q_part ? psum(h * DH + gl * 4) : ld4(Q + qo);
+  const int64_t kto = ((int64_t)tq * B + b) * hd + h * DH + gl * 4;   // key / value row of tq
+  float4 kt = make_float4(0.f, 0.f, 0.f, 0.f), vt = kt;
+  if (kv_k) {
+    kt = q_part ? psum(hd + h * DH + gl * 4) : ld4(K + kto);
+    vt = q_part ? psum(2 * hd + h * DH + gl * 4) : ld4(Vv + kto);
+    kt = rope4<DH>(kt, gl, tq + 1, tab, 1.f);
   }
   if (tab) q = rope4<DH>(q, gl, tq + 1, tab, 1.f);   // the projection's rotary map, applied here
   const float4 q_rot = q;
@@ -823,7 +835,14 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = lo + gi; j <= tq; j += NG) {
     const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
-    const float4 k = ld4(K + ro), v = ld4(Vv + ro);
+    float4 k, v;
+    if (kv_k && j == tq) {   // the row this launch produces (group-uniform branch)
+      k = kt;
+      v = vt;
+    } else {
+      k = ld4(K + ro);
+      v = ld4(Vv + ro);
+    }
     const float sc = gsum<G>(dot4(q, k));
     const float mn = fmaxf(m, sc);
     const float c = __expf(m - mn), p = __expf(sc - mn);
@@ -849,6 +868,10 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
     st4(O + (int64_t)r * hd + h * DH + tid * 4, make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
     if (tid == 0) lse[(int64_t)r * H + h] = M + logf(den);
     if (q_save) st4(q_save + qo, q_rot);   // after every group has read Q (q_save may be Q)
+    if (kv_k) {                            // after every group has read the row (or its slices)
+      st4(kv_k + kto, kt);
+      st4(kv_v + kto, vt);
+    }
   }
 }
 
@@ -1026,7 +1049,7 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
     const bool nor = post.kind == Post::Rope || post.kind == Post::SwiGlu;
     if ((rows && (sg.nseg || ldc != N)) || (nor && R) || (post.kind == Post::SwiGlu && sg.nseg * 2 != N) ||
         (post.kind == Post::Rope && (sg.nseg ? sg.nseg : N) % (post.H * post.dh) != 0) ||
-        (post.kind == Post::Defer && (R || sg.nseg || ldc != N || !post.defer)) ||
+        (post.kind == Post::Defer && (R || ldc != (sg.nseg ? sg.nseg : N) || !post.defer)) ||
         (post.kind != Post::None && atomic)) {
       if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
       return;
@@ -1199,23 +1222,34 @@ void post_separate(Ctx& c, int M, int N, float* C, const Seg& sg, const Post& p)
 
 template <int DH>
 void attn_fwd_n(Ctx& c, int nq, int B, int tq0, int win, int H, const float* Q, const float* K, const float* V,
-                float* O, float* lse, const Deferred& dq, const float2* tab, float* q_save) {
+                float* O, float* lse, const Deferred& dq, int part_ld, const float2* tab, float* q_save,
+                float* kv_k, float* kv_v) {
   g_attn_fwd<DH><<<nq * H, 256, 0, c.st>>>(nq, B, tq0, win, H, 1.f / sqrtf((float)DH), Q, K, V, O, lse, dq.part,
-                                           dq.splits, tab, q_save);
+                                           dq.splits, part_ld, tab, q_save, kv_k, kv_v);
 }
 // rot: Q (or the slices dq of its product) is the unrotated query; it is rotated by the
-// query's position here and stored rotated to Q
+// query's position here and stored rotated to Q. kv_row (with rot, one query position per
+// launch): the key / value rows of that position are the product's too (slices at columns
+// hd, 2 hd of rows of 3 hd, or unrotated in K / V), produced and stored here.
 void attn_fwd(Ctx& c, int nq, int B, int tq0, int win, int H, int dh, const float* Q, const float* K,
-              const float* V, float* O, float* lse, const Deferred& dq = Deferred(), bool rot = false) {
+              const float* V, float* O, float* lse, const Deferred& dq = Deferred(), bool rot = false,
+              bool kv_row = false) {
   if (nq <= 0) return;
+  if (kv_row && (!rot || nq != B)) {
+    if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
+    return;
+  }
   const float2* tab = rot ? c.rope_tab : nullptr;
   float* qs = rot ? const_cast<float*>(Q) : nullptr;
+  float* kk = kv_row ? const_cast<float*>(K) : nullptr;
+  float* vv = kv_row ? const_cast<float*>(V) : nullptr;
+  const int part_ld = (kv_row ? 3 : 1) * H * dh;
   switch (dh) {
-    case 16: attn_fwd_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
-    case 32: attn_fwd_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
-    case 64: attn_fwd_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
-    case 128: attn_fwd_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
-    default: attn_fwd_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, tab, qs); break;
+    case 16: attn_fwd_n<16>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, part_ld, tab, qs, kk, vv); break;
+    case 32: attn_fwd_n<32>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, part_ld, tab, qs, kk, vv); break;
+    case 64: attn_fwd_n<64>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, part_ld, tab, qs, kk, vv); break;
+    case 128: attn_fwd_n<128>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, part_ld, tab, qs, kk, vv); break;
+    default: attn_fwd_n<256>(c, nq, B, tq0, win, H, Q, K, V, O, lse, dq, part_ld, tab, qs, kk, vv); break;
   }
   c.check();
 }
@@ -1528,13 +1562,19 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     const DecBuf& D = u.dec[l];
     const Step s = step(l, t);
     if (!normalised) rms_fwd(c, B, d, s.zin, w(Dn(l, "m1")), eps, s.a, s.rs1);
-    if (with_kv) {
-      float* y[3] = {s.q, s.k, s.v};
-      lin_n(c, B, s.a, d, u.qkv_d[l], hd, 3, y, rope_post(2 * hd, t));   // q and k rotated
-    } else {
-      lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr, rope_post(hd, t));
+    {   // q (and the key / value rows of t) from the product's slices (or the product), summed,
+        // rotated and stored by the attention kernel
+      Deferred dq;
+      Post p;
+      p.kind = Post::Defer; p.defer = &dq;
+      if (with_kv) {
+        float* y[3] = {s.q, s.k, s.v};
+        lin_n(c, B, s.a, d, u.qkv_d[l], hd, 3, y, p);
+      } else {
+        lin(c, B, s.a, d, w(Ds(l, "wq")), d, hd, s.q, nullptr, p);
+      }
+      attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1, dq, true, with_kv);
     }
-    attn_fwd(c, B, B, t, cf.window, H, dh, s.q, D.k, D.v, s.o, s.lse1);
     lin(c, B, s.o, hd, w(Ds(l, "wo")), hd, d, s.z1, s.zin, rms_post(Dn(l, "m2"), s.b, s.rs2));
     {   // the cross-attention query: its product's slices (or the product) summed, rotated and
         // stored by the attention kernel
