@@ -100,9 +100,11 @@ typedef struct {
 typedef struct rlt_model rlt_model;
 typedef struct rlt_state rlt_state;
 
-/* Validate cfg, allocate library-owned packed weights on the current device and
- * copy/convert the given tensors into them (the caller may free its tensors once
- * this returns). Every manifest name for cfg must be present exactly once.
+/* Load the parameters theta that every procedure of [S] appendix F runs with (F.1
+ * prefill, F.2 generation, F.4 replay all take the current weights as given; [R] §6.4:
+ * replay uses the current parameters). Validate cfg, allocate library-owned packed
+ * weights on the current device and copy/convert the given tensors into them (the
+ * caller may free its tensors once this returns). Every manifest name for cfg must be present exactly once.
  * Errors: INVALID_ARG (bad config / missing or mis-sized tensor), UNSUPPORTED
  * (G not in {1, L_D}, d_head odd, share with L_E != L_D), OOM, HIP. */
 int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights,
@@ -112,7 +114,9 @@ int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights,
  * created before becomes stale ([R] §6.4) until rlt_state_reset. */
 int rlt_update_weights(rlt_model* m, const rlt_tensor* weights, int n_weights, hipStream_t stream);
 
-/* Free the model. States of this model must be destroyed first. */
+/* Free the model. States of this model must be destroyed first: every cache a state holds
+ * was computed with these parameters and means nothing under others ([R] §6.4: caches
+ * built with old parameters are stale). Errors: INVALID_ARG (null, or states remain). */
 int rlt_destroy(rlt_model* m);
 
 /* Allocate a batch state for `batch` sequences of up to `max_len` positions: the
@@ -127,6 +131,9 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
 /* H_0 = (s*, empty caches), positions reset to 0; clears staleness. */
 int rlt_state_reset(rlt_model* m, rlt_state* s, hipStream_t stream);
 
+/* Free a state: its encoder cache, memory, rings and s. The pages' procedures end a
+ * sequence's use of its state here ([S] appendix F.2 generation ends; [R] §6.4: after a
+ * parameter update cached states are invalidated, not reused). Errors: INVALID_ARG. */
 int rlt_state_destroy(rlt_state* s);
 
 /* Bytes of device memory held by the state, split as in [R] §4.2 eq 3.3:
@@ -345,7 +352,14 @@ int rlt_set_batch_invariant(rlt_model* m, int on);
  * [S] §2.7, Table 1). */
 int rlt_state_block_steps(const rlt_state* s, int64_t* out);
 
+/* Text of a status code. The codes name the conditions the pages' procedures rule out:
+ * consuming positions the encoder has not produced ([S] appendix F.2: the last emitted token
+ * is consumed before generation continues; RLT_ERR_ORDER), caches under other parameters
+ * ([R] §6.4; RLT_ERR_STALE_STATE), and forms the pages do not define ([S] §2.2: G is 1 or L_D;
+ * RLT_ERR_UNSUPPORTED). Returns a static string; never null. */
 const char* rlt_status_string(int status);
+/* Message of the calling thread's last failure (empty after none). Static storage per thread;
+ * valid until that thread's next failing call. */
 const char* rlt_last_error(void);
 
 #ifdef __cplusplus
