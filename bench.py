@@ -1,17 +1,19 @@
 """Throughput of the RLT hot path on one MI355X.
 
-A step is one current-policy replay of a batch of synthetic sequences: the
-token-parallel causal encode with its memory projection, then the sequential
-scan of decoder transitions over every position, then the batched readout of
-log p(x_{t+1} | x_<=t). The default workload is the algorithmic-task shape
-(vocab 8, d 512, 8x64 heads, 4+4 blocks, SwiGLU 2048, W 32, G 1, RLT-1) at
-batch 64 x 257 positions (BOS + 256 tokens from {0,1}).
+Default: the paper's reference shape (48 + 48 blocks with attention / FFN weights shared
+between encoder and decoder, d 4096, 32 x 128 heads, SwiGLU 11008, vocab 32000, W 1024,
+G 1, RLT-1) at batch 64. The token-parallel causal encode of the 8192-token Zipf prompt
+(plus the positions the decoder then consumes) is timed once (encoder tok/s); the decoder
+is sought to position 8192 (memory of every encoded position real, window entries zero)
+and --steps batched transitions at positions 8193.. are timed with HIP events (decoder
+transitions/s = batch x steps / time). The roofline object is that of the step's dominant
+kernel, the cross-attention over the memory prefix, timed live per launch with HIP events
+on its stream; step_roofline is the whole transition against the same HBM peak. The CPU
+oracle is timed on a bounded sample (cpu_baseline).
 
-Prints one JSON line: value = decoder transitions per second of the whole step
-(B*T transitions / step time), plus encoder tokens/s and decode-scan
-transitions/s from HIP events, the roofline of the scan (algorithmic bytes of
-the recurrence / measured time vs 8 TB/s HBM), and the CPU oracle on a bounded
-sample of the same workload.
+--config NAME picks another workload (same measurement at its prompt length); --replay
+times whole replays (encode + scan of every position + log-probabilities) as before;
+--grad, --generate, --ragged, --snapshot and --sweep decode time the other paths.
 """
 from __future__ import annotations
 
@@ -70,8 +72,9 @@ def step_flops(cfg, B: int, t: int) -> float:
 def decode_sweep(shapes, batches, positions, steps: int = 8):
     """Decoder transitions at batch B and position t: one JSON line per point.
 
-    For each point: encode t + steps tokens, scan positions 1..t-1 untimed, then time the
-    scan of positions t..t+steps-1 with HIP events. Reports us per transition step (the
+    For each point: encode t + steps tokens, seek the decoder to position t-1 (rlt_state_seek:
+    window entries zero, memory real), then time the scan of positions t..t+steps-1 with HIP
+    events. Reports us per transition step (the
     whole batch), the algorithmic bytes / flops of those steps, and their fractions of the
     8 TB/s HBM and 2.5 PFLOP/s 16-bit MFMA peaks.
     """
@@ -89,8 +92,7 @@ def decode_sweep(shapes, batches, positions, steps: int = 8):
                 st = model.state(B, t + steps, keep_encoder_cache=False)
                 x = torch.as_tensor(np.ascontiguousarray(toks_all[:B, :t + steps])).cuda()
                 rlt.rlt_encode(model.h, st, x)
-                if t > 1:
-                    rlt.rlt_decode_scan(model.h, st, t - 1)
+                rlt.rlt_state_seek(model.h, st, t - 1)
                 stream = torch.cuda.current_stream()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
@@ -529,6 +531,147 @@ def snapshot_bench(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def mem_attn_bytes(cfg, B: int, t: int) -> float:
+    """Algorithmic bytes of one decoder cross-attention launch at position t: every row reads the
+    keys and values of memory positions 1..t of its group once (16-bit), reads its query and
+    writes its output (two-term output rows when GEMM inputs are two-term)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    act = 2 if cfg.path_dtype == "fp16x2" else 1
+    return B * (t * 2 * cfg.hd * e + cfg.hd * e + act * cfg.hd * e)
+
+
+def decode_bench(args, cfg, prompt: int):
+    """Decoder transitions at position ~prompt for the whole batch, plus the encoder prefill.
+
+    Encodes prompt + warmup + steps tokens per row (timed: encoder tok/s), seeks the decoder
+    to position `prompt` (the window rings cleared, the memory of every encoded position
+    real: rlt_state_seek), runs `warmup` transitions, then times `steps` transitions with HIP
+    events, the cross-attention launches among them on their own event timers. A step is one
+    batched transition (merge, L_D blocks, readout with fp32 logits) of every row."""
+    import torch
+    from recurrent_looped_transformer_amd import rlt
+    from recurrent_looped_transformer_amd.synth import make_params, make_tokens
+    B, K, Wm = cfg.batch, args.steps, args.warmup
+    T = prompt + Wm + K
+    t0 = time.perf_counter()
+    P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+    torch.cuda.set_device(0)
+    model = rlt.Model(cfg, P)
+    print(f"[bench] {cfg.name}: parameters drawn and packed in {time.perf_counter() - t0:.0f} s", flush=True)
+    tokens = make_tokens(cfg, length=T)
+    x = torch.as_tensor(tokens).cuda()
+    st = model.state(B, T, keep_encoder_cache=False)
+    stream = torch.cuda.current_stream()
+    lg = torch.empty((B, K, cfg.vocab), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    rlt.rlt_kernel_timing(model.h, True)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    rlt.rlt_encode(model.h, st, x)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    enc_ms = ev[0].elapsed_time(ev[1])
+    print(f"[bench] encode of {B} x {T} tokens: {enc_ms:.0f} ms", flush=True)
+    for k in range(5):
+        rlt.rlt_kernel_time(model.h, k)          # clear the encoder's timers
+    rlt.rlt_state_seek(model.h, st, prompt)
+    if Wm:
+        rlt.rlt_decode_scan(model.h, st, Wm)
+    for k in range(5):
+        rlt.rlt_kernel_time(model.h, k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev[2].record(stream)
+    rlt.rlt_decode_scan(model.h, st, K, logits=lg)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    scan_ms = ev[2].elapsed_time(ev[3])
+    att_ms, att_n = rlt.rlt_kernel_time(model.h, rlt.TIME_MEMORY_ATTN)
+    win_ms, win_n = rlt.rlt_kernel_time(model.h, rlt.TIME_WINDOW_ATTN)
+    gem_ms, gem_n = rlt.rlt_kernel_time(model.h, rlt.TIME_DECODER_GEMM)
+    rlt.rlt_kernel_timing(model.h, False)
+    assert att_n == K * cfg.L_D, (att_n, K * cfg.L_D)
+    pos = list(range(prompt + Wm + 1, prompt + Wm + K + 1))
+    ms_step = scan_ms / K
+    sb = scan_bytes(cfg, B, K, t_start=prompt + Wm)
+    att_bytes = float(np.mean([mem_attn_bytes(cfg, B, t) for t in pos]))
+    att_avg = att_ms / att_n
+    ach = att_bytes / (att_avg / 1e3) / 1e9
+    ef = encoder_flops(cfg, B, T)
+    act = 2 if cfg.path_dtype == "fp16x2" else 1
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_memattn_{cfg.name}.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            if rec.get("lib_sha") == rlt_lib_sha() and rec.get("B") == B and rec.get("position") == prompt:
+                traffic = rec.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    kern = f"attn_decode_k<{'f16' if cfg.path_dtype != 'bf16' else 'bf16'},{cfg.d_head},false,1> " \
+           f"(decoder cross-attention over the memory prefix)"
+    out = {
+        "metric": METRIC, "value": B * K / (scan_ms / 1e3), "unit": "transitions/s", "n_gpus": 1,
+        "steps": K, "warmup": Wm, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16", "fp16x2": "f16x2"}[cfg.path_dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: decoder transitions of B={B} rows at positions {pos[0]}-{pos[-1]} "
+                               f"(RLT-{cfg.variant}, L_E+L_D={cfg.L_E}+{cfg.L_D}{' shared' if cfg.share else ''}, "
+                               f"d {cfg.d}, {cfg.n_heads}x{cfg.d_head} heads, SwiGLU {cfg.ffn}, W {cfg.window}, "
+                               f"vocab {cfg.vocab}) after the {T}-token encode of the Zipf prompt; the decoder is "
+                               f"sought to position {prompt} (memory real, window entries zero), a step is one "
+                               f"batched transition with fp32 logits",
+                   "batch": B, "prompt": prompt, "positions": [pos[0], pos[-1]], "d": cfg.d, "L_E": cfg.L_E,
+                   "L_D": cfg.L_D, "window": cfg.window, "groups": cfg.groups, "vocab": cfg.vocab,
+                   "shared": bool(cfg.share), "variant": f"RLT-{cfg.variant}", "gemm_inputs": "two-term" if act == 2
+                   else "one-term"},
+        "decode_transitions_s": B * K / (scan_ms / 1e3),
+        "decode_step_ms": ms_step,
+        "step_roofline": {"bound": "hbm", "achieved": sb / (scan_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": sb / (scan_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes_per_step": sb / K},
+        "step_breakdown_ms": {"memory_attention": att_ms / K, "window_attention": win_ms / K,
+                              "gemms": gem_ms / K, "launches_per_step": (att_n + win_n + gem_n) / K},
+        "encoder_tok_s": B * T / (enc_ms / 1e3), "encoder_ms": enc_ms, "encoder_tokens": B * T,
+        "encoder_tflops": ef / (enc_ms / 1e3) / 1e12,
+        "encoder_mfma_frac": ef / (enc_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": att_bytes,
+                     "avg_launch_ms": att_avg, "launches": att_n},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_steps(cfg, P, tokens, args.cpu_seconds)
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_steps(cfg, P, tokens, budget_s: float):
+    """The oracle (float32 numpy, as it stands) on one row: encode 2 tokens, then decoder
+    transitions until the time budget is spent (at least one). Its per-transition cost is the
+    decoder's weights streamed once per position and row, nearly independent of the position."""
+    from threadpoolctl import threadpool_info
+    from oracle import Oracle
+    o = Oracle(cfg, P, np.float32)
+    st = o.new_state(1)
+    n_enc = 8
+    t0 = time.perf_counter()
+    o.encoder_chunk(st, tokens[:1, :n_enc])
+    enc_s = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    n = 0
+    while n < n_enc and (n == 0 or time.perf_counter() - t1 < budget_s):
+        o.decode(st, 1)
+        n += 1
+    dt = time.perf_counter() - t1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "transitions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 row: encode of {n_enc} tokens ({enc_s:.1f} s, {n_enc / enc_s:.2f} tok/s), then {n} "
+                      f"decoder transitions at positions 1-{n} ({dt:.1f} s), float32 numpy"}
+
+
 def cpu_baseline(cfg, P, tokens, sample_B: int):
     from threadpoolctl import threadpool_info
     from oracle import Oracle
@@ -549,7 +692,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="algo_bf16")
+    ap.add_argument("--config", default="paper_shared")
+    ap.add_argument("--replay", action="store_true",
+                    help="time whole replays (encode + scan over every position + log-probs) instead of "
+                         "decoder transitions at the prompt's end")
+    ap.add_argument("--prompt", type=int, default=0, help="decoder position of the timed transitions "
+                                                           "(default: the configuration's prompt length)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--batch", type=int, default=0)
     ap.add_argument("--seq-len", type=int, default=0)
     ap.add_argument("--variant", type=int, default=-1)
@@ -621,6 +770,9 @@ def main():
         return
     if args.snapshot:
         snapshot_bench(args, cfg)
+        return
+    if not args.replay:
+        decode_bench(args, cfg, args.prompt or cfg.seq_len)
         return
     B, T = cfg.batch, cfg.seq_len
     P = make_params(cfg)

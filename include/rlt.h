@@ -322,6 +322,35 @@ int rlt_replay_grad(const rlt_config* cfg, const rlt_tensor* weights, int n_weig
                     int n_grads, const int32_t* tokens, int B, int T, const float* dlogprob, float* logprob,
                     int checkpoint, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/* Measurement aid: set the decoder of a state to have consumed its first n encoded
+ * positions without running their transitions. s and the RLT-2 register keep their values
+ * and every window ring slot is cleared to zero keys and values, so the next transition at
+ * position n + 1 attends to zero-valued window entries at positions max(1, n-W+2)..n and
+ * to the real memory prefix 1..n+1. The cost of a transition grows with its position
+ * through the memory reads ([R] §4.2 eq 3.1 and 3.3: the per-step cost of the decoder
+ * depends on t); this call lets a transition at a late position be timed, and checked, without
+ * first running every earlier one. The resulting state is not the H_n of the method for
+ * the encoded tokens. Requires n_decoded <= n <= n_encoded (RLT_ERR_ORDER otherwise). */
+int rlt_state_seek(rlt_model* m, rlt_state* s, int n, hipStream_t stream);
+
+/* Kernel timers (measurement). Kinds of launches that can be timed. */
+typedef enum {
+  RLT_TIME_MEMORY_ATTN = 0,    /* decoder cross-attention over the memory prefix ([S] §2.2) */
+  RLT_TIME_WINDOW_ATTN = 1,    /* decoder sliding-window attention over the ring ([R] §3.3) */
+  RLT_TIME_ENCODER_ATTN = 2,   /* encoder self-attention (prefill or over the encoder cache) */
+  RLT_TIME_ENCODER_GEMM = 3,   /* encoder and memory-projection GEMMs (prefill, [S] §2.2) */
+  RLT_TIME_DECODER_GEMM = 4,   /* merge, decoder block and readout GEMMs of the transitions */
+  RLT_TIME_KINDS = 5
+} rlt_time_kind;
+/* With on != 0, every later launch of those kinds from the scan's launch path and the encoder
+ * is bracketed by a pair of HIP events recorded on its stream (no device memory is allocated;
+ * launches under stream capture are not timed). The timed launches of a per-row call cover
+ * the launches of that call. Errors: INVALID_ARG. */
+int rlt_kernel_timing(rlt_model* m, int on);
+/* Sum of the event-timed durations (ms) and number of launches of one kind since the last
+ * read; waits for the last recorded event, then clears the record. Errors: INVALID_ARG, HIP. */
+int rlt_kernel_time(rlt_model* m, int kind, double* total_ms, int64_t* launches);
+
 /* Scan driver for the decoder transitions: 0 = automatic (mode 1),
  * 1 = one launch sequence per position (stream-ordered), 2 = persistent cooperative kernel
  * with the automatic work split, 3 = persistent with every workgroup on all sequences,

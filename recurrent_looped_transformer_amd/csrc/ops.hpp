@@ -28,6 +28,7 @@ struct KVDst {
   void* v = nullptr;
   int cap = 0;
   int ring = 0;
+  int64_t lo = 0;   // > 0: two-term keys/values, the lo term of an element `lo` elements after its hi term
 };
 
 enum class Ep : int {
@@ -36,6 +37,7 @@ enum class Ep : int {
   Residual,       // resid[rmap(m) + n] += acc
   SwiGLU,         // rows (2j, 2j+1) = (W1 x, W3 x): out[m*ldo + j] = act(silu(a) * b)
   QKV,            // n < hd: q = rope(acc) -> out; hd <= n < 2hd: k = rope -> kv.k; else v -> kv.v
+                  // (two-term q when out_split > 0, two-term k / v when kv.lo > 0)
   RopeQ,          // out[m*ldo + n] = act(rope(acc))      (cross-attention query)
   MemKV,          // n < hd: k = rope -> kv.k; else v -> kv.v
   Merge,          // rows (2n, 2n+1) = (W_g,r r, W_s r): u = e + alpha*sigmoid(gpre + a)*b -> z
@@ -200,6 +202,14 @@ struct AttnArgs {
   int split_max = 0;
   int n_max = 0;
   int split_keys = 0;
+  // Two-term operands (16-bit types): q_lo > 0: each query row holds its lo terms q_lo elements
+  // after the hi terms; kv_lo > 0: the lo term of a key / value element lies kv_lo elements after
+  // its hi term. Scores and weighted sums then use (hi + lo) in fp32 (decode) or three MFMA
+  // products hi*hi + hi*lo + lo*hi (prefill, whose probabilities are split the same way).
+  int64_t q_lo = 0;
+  int64_t kv_lo = 0;
+  int memory = 0;               // 1: the decoder's cross-attention over the memory (its own kernel
+                                // instance, so profiles report it apart from the window attention)
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
 // 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is

@@ -20,12 +20,13 @@ namespace rlt {
 
 // SPLIT: this block takes the keys [z * split_keys, (z + 1) * split_keys) of its range
 // (z = blockIdx.z) and writes its partial softmax sums to split_ws for attn_combine_k.
-template <typename T, int DH, bool SPLIT>
+// X2: two-term query, keys and values (q_lo, kv_lo): each operand is hi + lo in fp32.
+template <typename T, int DH, bool SPLIT, int MEM, bool X2 = false>
 __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int G = DH / VEC;              // lanes per key
   constexpr int NG = 256 / G;              // keys in flight per block per round
-  constexpr int UNR = 8;
+  constexpr int UNR = X2 ? 4 : 8;
   __shared__ float part[NG * DH];
   __shared__ float ml[2 * NG];
   const int h = blockIdx.x;
@@ -41,6 +42,8 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   // the query's raw bits now, unpacked after the first keys are requested (no wait in between)
   const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)row * a.ldq + h * DH + gl * VEC;
   const uint4 qraw = *reinterpret_cast<const uint4*>(qp);
+  uint4 qraw_lo = make_uint4(0, 0, 0, 0);
+  if constexpr (X2) qraw_lo = *reinterpret_cast<const uint4*>(qp + a.q_lo);
   const int64_t hb = (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH + gl * VEC;
   const T* kb = reinterpret_cast<const T*>(a.k) + hb;
   const T* vb = reinterpret_cast<const T*>(a.v) + hb;
@@ -51,7 +54,8 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   constexpr int STEP = NG * UNR;
   // software pipeline: the next round's keys and values are in flight while this round computes
   uint4 kk[UNR], vv[UNR], kn[UNR], vn[UNR];
-#define RLT_ATTN_LOAD(K_, V_, J0_)                                              \
+  uint4 kkl[X2 ? UNR : 1], vvl[X2 ? UNR : 1], knl[X2 ? UNR : 1], vnl[X2 ? UNR : 1];
+#define RLT_ATTN_LOAD(K_, V_, KL_, VL_, J0_)                                    \
   _Pragma("unroll") for (int u = 0; u < UNR; ++u) {                             \
     const int j = (J0_) + u * NG;                                               \
     if (j < je) {                                                               \
@@ -59,15 +63,25 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
       const int slot = a.ring ? (p - 1) % a.cap : p - 1;                        \
       K_[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);         \
       V_[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);         \
+      if constexpr (X2) {                                                       \
+        KL_[u] = *reinterpret_cast<const uint4*>(kb + a.kv_lo + (int64_t)slot * DH); \
+        VL_[u] = *reinterpret_cast<const uint4*>(vb + a.kv_lo + (int64_t)slot * DH); \
+      }                                                                         \
     }                                                                           \
   }
-  RLT_ATTN_LOAD(kk, vv, jb + gi)
+  RLT_ATTN_LOAD(kk, vv, kkl, vvl, jb + gi)
   float qv[VEC];
   unpack16<T>(qraw, qv);
+  if constexpr (X2) {
+    float ql[VEC];
+    unpack16<T>(qraw_lo, ql);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[e] += ql[e];
+  }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) qv[e] *= a.scale;
   for (int j0 = jb + gi; j0 < je; j0 += STEP) {
-    if (j0 + STEP < je) RLT_ATTN_LOAD(kn, vn, j0 + STEP)
+    if (j0 + STEP < je) RLT_ATTN_LOAD(kn, vn, knl, vnl, j0 + STEP)
     float sc[UNR];
     float mx = m_run;
 #pragma unroll
@@ -76,6 +90,12 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
       if (j0 + u * NG < je) {
         float kf[VEC];
         unpack16<T>(kk[u], kf);
+        if constexpr (X2) {
+          float kl[VEC];
+          unpack16<T>(kkl[u], kl);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) kf[e] += kl[e];
+        }
         dot = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) dot = fmaf(qv[e], kf[e], dot);
@@ -95,6 +115,12 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
         l_run += pw;
         float vf[VEC];
         unpack16<T>(vv[u], vf);
+        if constexpr (X2) {
+          float vl[VEC];
+          unpack16<T>(vvl[u], vl);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) vf[e] += vl[e];
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pw, vf[e], acc[e]);
       }
@@ -104,6 +130,10 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     for (int u = 0; u < UNR; ++u) {
       kk[u] = kn[u];
       vv[u] = vn[u];
+      if constexpr (X2) {
+        kkl[u] = knl[u];
+        vvl[u] = vnl[u];
+      }
     }
   }
 #undef RLT_ATTN_LOAD
@@ -179,11 +209,19 @@ static void launch_attn(const AttnArgs& a0, hipStream_t st) {
     a.split_keys = (a.n_max + S - 1) / S;
     S = (a.n_max + a.split_keys - 1) / a.split_keys;
   }
+  // the memory attention runs its own instance of the same code (MEM = 1): a separate symbol;
+  // two-term operands (the encoder's, 16-bit types) take the X2 instances
+  const dim3 grid(a.H, a.B * a.nq, S);
+  const bool x2 = !__is_same(T, float) && (a.q_lo > 0 || a.kv_lo > 0);
   if (S > 1) {
-    hipLaunchKernelGGL((attn_decode_k<T, DH, true>), dim3(a.H, a.B * a.nq, S), dim3(256), 0, st, a);
+    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, true>), grid, dim3(256), 0, st, a);
+    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
   } else {
-    hipLaunchKernelGGL((attn_decode_k<T, DH, false>), dim3(a.H, a.B * a.nq), dim3(256), 0, st, a);
+    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, true>), grid, dim3(256), 0, st, a);
+    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0>), grid, dim3(256), 0, st, a);
   }
 }
 
@@ -395,8 +433,219 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   }
 }
 
+// Two-term operands (q_lo, kv_lo > 0): every query, key and value is hi + lo in the 16-bit
+// type. Scores take three MFMA products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
+// below the fp32 rounding of the sum), the probabilities are split into hi + lo in registers
+// and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Same tiling as above with both
+// terms of a key / value tile in LDS (4 stages: buffer x term); at most two query blocks per
+// wave (register budget).
+template <typename T, int DH, int QB>
+__global__ __launch_bounds__(256) void flash_prefill_x2_k(AttnArgs a) {
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = 4 * QW;
+  constexpr int PARTS = DH / 8;
+  constexpr int LOADERS = 16 * PARTS;
+  __shared__ __align__(16) uint4 sK[2][2][BK][KP];           // [buffer][term]
+  __shared__ __align__(16) uint16_t sVt[2][2][DH][VP];
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int g = lane >> 4, c = lane & 15;
+  const int q0 = qb * QBLK + wave * QW;
+  uint4 qh[QB][DH / 32], ql[QB][DH / 32];
+  int qpos[QB];
+  bool qvalid[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int myq = q0 + j * 16 + c;
+    qvalid[j] = myq < a.nq;
+    qpos[j] = a.pos0 + 1 + myq;
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.nq + min(myq, a.nq - 1)) * a.ldq +
+                        h * DH;
+#pragma unroll
+    for (int kc = 0; kc < DH / 32; ++kc) {
+      qh[j][kc] = *reinterpret_cast<const uint4*>(Q + kc * 32 + g * 8);
+      ql[j][kc] = *reinterpret_cast<const uint4*>(Q + a.q_lo + kc * 32 + g * 8);
+    }
+  }
+  f32x4 o[QB][DH / 16];
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) o[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
+  const int qlast = min(a.nq, (qb + 1) * QBLK);
+  const int kmax = a.pos0 + qlast;
+  const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * QBLK - a.window + 1) : 1;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
+
+  const int jq = tid / PARTS, part = tid % PARTS;
+  uint4 rk[2][4], rv[2][4];                                   // [term][key]
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = k0 + 4 * jq + e;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        rk[t][e] = make_uint4(0, 0, 0, 0);
+        rv[t][e] = make_uint4(0, 0, 0, 0);
+      }
+      if (tid < LOADERS && p <= kmax) {
+        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
+        const int64_t off = (int64_t)slot * DH + part * 8;
+        rk[0][e] = *reinterpret_cast<const uint4*>(Kb + off);
+        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + off);
+        rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + off);
+        rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + off);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    if (tid < LOADERS) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sK[buf][t][4 * jq + e][part] = rk[t][e];
+        const uint32_t w[4][4] = {{rv[t][0].x, rv[t][0].y, rv[t][0].z, rv[t][0].w},
+                                  {rv[t][1].x, rv[t][1].y, rv[t][1].z, rv[t][1].w},
+                                  {rv[t][2].x, rv[t][2].y, rv[t][2].z, rv[t][2].w},
+                                  {rv[t][3].x, rv[t][3].y, rv[t][3].z, rv[t][3].w}};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = (e & 1) * 16;
+          uint2 u;
+          u.x = ((w[0][e >> 1] >> sh) & 0xffffu) | (((w[1][e >> 1] >> sh) & 0xffffu) << 16);
+          u.y = ((w[2][e >> 1] >> sh) & 0xffffu) | (((w[3][e >> 1] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<uint2*>(&sVt[buf][t][part * 8 + e][4 * jq]) = u;
+        }
+      }
+    }
+  };
+
+  gload(kmin);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kmin; k0 <= kmax; k0 += BK) {
+    const bool more = k0 + BK <= kmax;
+    if (more) gload(k0 + BK);
+    float s[QB][4][4];
+    float tmax[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint4 kh[DH / 32], kl[DH / 32];
+#pragma unroll
+      for (int kc = 0; kc < DH / 32; ++kc) {
+        kh[kc] = sK[buf][0][st * 16 + c][kc * 4 + g];
+        kl[kc] = sK[buf][1][st * 16 + c][kc * 4 + g];
+      }
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < DH / 32; ++kc) {
+          acc = mfma16x16x32<T>(kl[kc], qh[j][kc], acc);
+          acc = mfma16x16x32<T>(kh[kc], ql[j][kc], acc);
+          acc = mfma16x16x32<T>(kh[kc], qh[j][kc], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kp = k0 + st * 16 + 4 * g + i;
+          const bool ok = qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
+          s[j][st][i] = ok ? acc[i] * a.scale : -INFINITY;
+          tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+        }
+      }
+    }
+    uint2 pbh[QB][4], pbl[QB][4];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float tm = fmaxf(tmax[j], __shfl_xor(tmax[j], 16, WAVE));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, WAVE));
+      const float m_new = fmaxf(m_run[j], tm);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __expf(m_run[j] - m_use);
+      l_run[j] *= corr;
+#pragma unroll
+      for (int i = 0; i < DH / 16; ++i) o[j][i] *= corr;
+      float lsum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __expf(s[j][st][i] - m_use);
+          lsum += pv;
+          ph[i] = Elem<T>::round(pv);
+          pl[i] = pv - ph[i];
+        }
+        pbh[j][st].x = pack2<T>(ph[0], ph[1]);
+        pbh[j][st].y = pack2<T>(ph[2], ph[3]);
+        pbl[j][st].x = pack2<T>(pl[0], pl[1]);
+        pbl[j][st].y = pack2<T>(pl[2], pl[3]);
+      }
+      lsum += __shfl_xor(lsum, 16, WAVE);
+      lsum += __shfl_xor(lsum, 32, WAVE);
+      l_run[j] += lsum;
+      m_run[j] = m_new;
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int db = 0; db < DH / 16; ++db) {
+        const uint2 vh = *reinterpret_cast<const uint2*>(&sVt[buf][0][db * 16 + c][st * 16 + 4 * g]);
+        const uint2 vl = *reinterpret_cast<const uint2*>(&sVt[buf][1][db * 16 + c][st * 16 + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          o[j][db] = mfma16x16x16<T>(vl, pbh[j][st], o[j][db]);
+          o[j][db] = mfma16x16x16<T>(vh, pbl[j][st], o[j][db]);
+          o[j][db] = mfma16x16x16<T>(vh, pbh[j][st], o[j][db]);
+        }
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    if (!qvalid[j]) continue;
+    const int myq = q0 + j * 16 + c;
+    const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.nq + myq) * a.ldo + h * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) {
+      float v[4] = {o[j][db][0] * inv, o[j][db][1] * inv, o[j][db][2] * inv, o[j][db][3] * inv};
+      uint2 w;
+      w.x = pack2<T>(v[0], v[1]);
+      w.y = pack2<T>(v[2], v[3]);
+      *reinterpret_cast<uint2*>(out + db * 16 + 4 * g) = w;
+      if (a.out_split) {
+        uint2 l;
+        l.x = pack2<T>(v[0] - Elem<T>::round(v[0]), v[1] - Elem<T>::round(v[1]));
+        l.y = pack2<T>(v[2] - Elem<T>::round(v[2]), v[3] - Elem<T>::round(v[3]));
+        *reinterpret_cast<uint2*>(out + a.out_split + db * 16 + 4 * g) = l;
+      }
+    }
+  }
+}
+
 template <typename T, int DH>
 static void launch_flash(const AttnArgs& a, hipStream_t st) {
+  if (a.q_lo > 0 || a.kv_lo > 0) {
+    if (a.nq <= 512) {
+      hipLaunchKernelGGL((flash_prefill_x2_k<T, DH, 1>), dim3((a.nq + 63) / 64, a.H, a.B), dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((flash_prefill_x2_k<T, DH, 2>), dim3((a.nq + 127) / 128, a.H, a.B), dim3(256), 0, st, a);
+    }
+    return;
+  }
   // four query blocks per wave; at dh 128 fp16 that is 1.3x over two at the medium-LM encode
   // (measured; 256 + 256 registers, no spills), while bf16 (whose unpacking takes more
   // registers) would spill there and keeps two

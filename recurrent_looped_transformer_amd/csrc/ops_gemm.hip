@@ -132,10 +132,16 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
       rope_apply(pre ? pre->cs1 : rope_cs(a, pos, c + 2), v[2], v[3]);
     }
     T* dst;
-    if (region == 0) dst = out + (int64_t)m * a.ldo + w;
-    else dst = reinterpret_cast<T*>(region == 1 ? a.kv.k : a.kv.v) + kv_off(a, b, h, pos, c);
+    int64_t lo;
+    if (region == 0) {
+      dst = out + (int64_t)m * a.ldo + w;
+      lo = a.out_split;
+    } else {
+      dst = reinterpret_cast<T*>(region == 1 ? a.kv.k : a.kv.v) + kv_off(a, b, h, pos, c);
+      lo = a.kv.lo;
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) Elem<T>::st(dst + k, v[k]);
+    for (int k = 0; k < 4; ++k) store_act<T>(dst + k, lo, v[k]);
   } else if constexpr (E == Ep::Merge) {
     // rows (2j, 2j+1) of the packed [W_g,r ; W_s] weight: gate part and state projection of feature j
     const int j = n >> 1;
@@ -175,11 +181,14 @@ constexpr int skinny_unroll() {
   return TPW + NMB <= 2 ? 8 : (TPW + NMB <= 4 ? 4 : (TPW + NMB <= 6 ? 2 : 1));
 }
 
-template <typename T, Ep E, int NMB, int TPW>
+// XS: two-term X (each row K hi terms, then K lo terms): every weight chunk loaded once feeds
+// the MFMAs of both terms.
+template <typename T, Ep E, int NMB, int TPW, bool XS>
 __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__ X, int64_t ldx,
                                                            const T* __restrict__ W, int M, int N, int K,
                                                            EpArgs a) {
-  constexpr int U = skinny_unroll<TPW, NMB>();
+  constexpr int U = XS ? (skinny_unroll<TPW, NMB>() > 1 ? skinny_unroll<TPW, NMB>() / 2 : 1)
+                       : skinny_unroll<TPW, NMB>();
   constexpr int NO = TPW * NMB;            // output tiles of the workgroup
   constexpr int NOB = NO < 4 ? NO : 4;     // output tiles reduced per pass (LDS: 32 KB)
   constexpr int RPW = NMB * 16 / kSkW;     // rows per wave in the row-scale prologue
@@ -220,34 +229,41 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int j = 0; j < NMB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // two-term X: chunks nch .. 2 nch - 1 are the lo terms, against the same weight chunks
-  const int nch = K / 64, ncx = a.x_split ? 2 * nch : nch;
-  for (int c0 = wave; c0 < ncx; c0 += kSkW * U) {
-    uint4 wa[U][TPW][2], xb[U][NMB][2];
+  // two-term X: the lo terms of chunk c lie at chunk c + nch of the row
+  const int nch = K / 64;
+  for (int c0 = wave; c0 < nch; c0 += kSkW * U) {
+    uint4 wa[U][TPW][2], xb[U][NMB][2], xl[XS ? U : 1][NMB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kSkW;
-      if (c < ncx) {
-        const int cw = c < nch ? c : c - nch;
+      if (c < nch) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          wa[u][t][0] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + cw * 1024);
-          wa[u][t][1] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + cw * 1024 + 512);
+          wa[u][t][0] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + c * 1024);
+          wa[u][t][1] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + c * 1024 + 512);
         }
 #pragma unroll
         for (int j = 0; j < NMB; ++j) {
           xb[u][j][0] = *reinterpret_cast<const uint4*>(xp[j] + c * 64);
           xb[u][j][1] = *reinterpret_cast<const uint4*>(xp[j] + c * 64 + 8);
+          if constexpr (XS) {
+            xl[u][j][0] = *reinterpret_cast<const uint4*>(xp[j] + (c + nch) * 64);
+            xl[u][j][1] = *reinterpret_cast<const uint4*>(xp[j] + (c + nch) * 64 + 8);
+          }
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + u * kSkW < ncx) {
+      if (c0 + u * kSkW < nch) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
           for (int j = 0; j < NMB; ++j) {
+            if constexpr (XS) {
+              acc[t][j] = mfma16x16x32<T>(wa[u][t][0], xl[u][j][0], acc[t][j]);
+              acc[t][j] = mfma16x16x32<T>(wa[u][t][1], xl[u][j][1], acc[t][j]);
+            }
             acc[t][j] = mfma16x16x32<T>(wa[u][t][0], xb[u][j][0], acc[t][j]);
             acc[t][j] = mfma16x16x32<T>(wa[u][t][1], xb[u][j][1], acc[t][j]);
           }
@@ -687,7 +703,8 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n));
 #define RLT_SKINNY(NMB_, TPW_)                                                                                   \
   if (best_n == NMB_ && best_t == TPW_) {                                                                        \
-    hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_>), grid, blk, 0, st, x, ldx, w, M, N, K, a);                 \
+    if (a.x_split) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+    else hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, false>), grid, blk, 0, st, x, ldx, w, M, N, K, a);   \
     return;                                                                                                      \
   }
     RLT_SKINNY(1, 1) RLT_SKINNY(2, 1) RLT_SKINNY(4, 1) RLT_SKINNY(1, 2) RLT_SKINNY(2, 2) RLT_SKINNY(4, 2)

@@ -98,6 +98,10 @@ struct rlt_model {
   int scan_mode = 0;
   int batch_invariant = 0;   // every kernel's per-row arithmetic independent of batch and pass shape
   int n_states = 0;
+  // kernel timers (measurement): launches of each kind bracketed by events on their stream
+  bool timing = false;
+  std::vector<hipEvent_t> ev_free;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> timed[RLT_TIME_KINDS];
 };
 
 struct rlt_state {
@@ -114,7 +118,9 @@ struct rlt_state {
   float *s = nullptr, *rho = nullptr;
   float *e = nullptr, *gpre = nullptr;   // [B][Tm][d]
   void *mem_k = nullptr, *mem_v = nullptr;   // [G][B][H][Tm][dh]
-  void *enc_k = nullptr, *enc_v = nullptr;   // [L_E][B][H][Tm][dh]
+  void *enc_k = nullptr, *enc_v = nullptr;   // [term][L_E][B][H][Tm][dh] (one term, or hi and lo planes)
+  int64_t enc_lo = 0;                        // elements from a C^E hi term to its lo term (0: one term)
+  int64_t ekv_lo = 0;                        // the same for ekv_k / ekv_v
   void *ring_k = nullptr, *ring_v = nullptr; // [L_D][B][H][R][dh]
   float2* rope = nullptr;                    // [Tm + 1][dh / 2]
   // decoder workspace, rows = B * P
@@ -429,10 +435,35 @@ void attn_split(const rlt_model* m, const rlt_state* s, AttnArgs& at, int slice,
   at.n_max = n_max;
 }
 
-void mgemm(const rlt_model* m, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
+
+// Runs launch() and, while the model's timers are on and the stream is not being captured,
+// brackets it with a pair of events recorded on that stream.
+template <typename F>
+void timed(rlt_model* m, int kind, hipStream_t st, F&& launch) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (!m->timing || hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    launch();
+    return;
+  }
+  hipEvent_t ev[2];
+  for (auto& e : ev) {
+    if (m->ev_free.empty()) {
+      HIPCHK(hipEventCreate(&e));
+    } else {
+      e = m->ev_free.back();
+      m->ev_free.pop_back();
+    }
+  }
+  HIPCHK(hipEventRecord(ev[0], st));
+  launch();
+  HIPCHK(hipEventRecord(ev[1], st));
+  m->timed[kind].push_back({ev[0], ev[1]});
+}
+
+void mgemm(rlt_model* m, int kind, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
            int K, hipStream_t st) {
   a.row_invariant = m->batch_invariant;
-  gemm(dt, ep, a, X, ldx, W, M, N, K, st);
+  timed(m, kind, st, [&] { gemm(dt, ep, a, X, ldx, W, M, N, K, st); });
 }
 
 // ------------------------------------------------------------------ encode
@@ -460,35 +491,39 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
     for (int l = 0; l < c.L_E; ++l) {
       const LayerW& L = m->enc[l];
       rmsnorm(dt, h, hm, L.n1, s->exa, ad, rows, d, c.rms_eps, st, sd);
+      // q, k, v: two-term (hi, lo) with two-term GEMM inputs: q rows [hi | lo], keys and values
+      // in a lo plane after the hi plane
       EpArgs a;
-      a.out = s->eq; a.ldo = hd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd; a.tn = T; a.pos0 = t0;
-      a.x_split = A > 1; a.row_pos = rp;
+      a.out = s->eq; a.ldo = ahd; a.out_split = shd; a.rope = s->rope; a.H = H; a.dh = dh; a.hd = hd;
+      a.tn = T; a.pos0 = t0; a.x_split = A > 1; a.row_pos = rp;
       AttnArgs at;
       at.row_pos = rp;
       if (s->enc_k) {
         const int64_t lo = (int64_t)l * s->B * H * Tm * dh;
         a.kv.k = (char*)s->enc_k + lo * m->esz; a.kv.v = (char*)s->enc_v + lo * m->esz;
-        a.kv.cap = Tm; a.b0 = b0;
+        a.kv.cap = Tm; a.b0 = b0; a.kv.lo = s->enc_lo;
         at.k = (char*)a.kv.k + (int64_t)b0 * H * Tm * dh * m->esz;
         at.v = (char*)a.kv.v + (int64_t)b0 * H * Tm * dh * m->esz;
-        at.kv_bstride = (int64_t)H * Tm * dh; at.cap = Tm;
+        at.kv_bstride = (int64_t)H * Tm * dh; at.cap = Tm; at.kv_lo = s->enc_lo;
       } else {
-        a.kv.k = s->ekv_k; a.kv.v = s->ekv_v; a.kv.cap = T; a.b0 = 0;
-        at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T;
+        a.kv.k = s->ekv_k; a.kv.v = s->ekv_v; a.kv.cap = T; a.b0 = 0; a.kv.lo = s->ekv_lo;
+        at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T; at.kv_lo = s->ekv_lo;
       }
       a.kv.ring = 0;
-      mgemm(m, dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
-      at.q = s->eq; at.ldq = hd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
+      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
+      at.q = s->eq; at.ldq = ahd; at.q_lo = shd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
       attn_split(m, s, at, 0, row_pos ? pos_max : t0 + T);
-      if (!(T >= 16 && !m->batch_invariant && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+      timed(m, RLT_TIME_ENCODER_ATTN, st, [&] {
+        if (!(T >= 16 && !m->batch_invariant && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+      });
       EpArgs r; r.resid = h; r.rmap = hm; r.x_split = A > 1;
-      mgemm(m, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
+      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
       rmsnorm(dt, h, hm, L.n2, s->exa, ad, rows, d, c.rms_eps, st, sd);
       EpArgs sw; sw.out = s->ehid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-      mgemm(m, dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
-      mgemm(m, dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
+      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
+      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
     }
     if (c.L_D > 0) {
       // memory: k^g = RoPE(W^g_K RMSNorm_E(e)), v^g = W^g_V RMSNorm_E(e)  (eq 2.1-2.2)
@@ -499,7 +534,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
         a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
         a.x_split = A > 1;
-        mgemm(m, dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
+        mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
       }
     }
     if (c.variant != RLT_V0) {
@@ -507,7 +542,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       rmsnorm(dt, h, hm, nullptr, s->exa, ad, rows, d, 0.f, st, sd);
       EpArgs a; a.resid = s->gpre + ((int64_t)b0 * Tm + t0) * d; a.rmap = hm; a.bias = m->bg;
       a.x_split = A > 1;
-      mgemm(m, dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
+      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
     }
   }
   check_launch();
@@ -596,7 +631,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     if (merge_fold) {
       a.fold_zb = sb.xa; a.fold_ld = ad; a.out_split = sd; a.fold_ssp = sb.dssp; a.fold_gain = m->dec[0].n1;
     }
-    mgemm(m, dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
   auto norm_in = [&](EpArgs& a, const float* gain) {
@@ -623,7 +658,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     a.x_split = A > 1; a.pos_dev = pos_dev; a.row_pos = rp;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
-    mgemm(m, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
@@ -631,31 +666,32 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     at.pos0 = t0; at.window = c.window; at.scale = scale; at.pos_dev = pos_dev; at.row_pos = rp;
     const int pmax = pos_dev ? 0 : (rp ? pos_max : t0 + np);
     attn_split(m, s, at, sb.slice, std::min(pmax, c.window));
-    attn_decode(dt, at, st);
+    timed(m, RLT_TIME_WINDOW_ATTN, st, [&] { attn_decode(dt, at, st); });
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
-    mgemm(m, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
     // cross-attention to the prefix memory M_<=t of this layer's group
     EpArgs qx;
     norm_in(qx, L.n2);
     qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0; qx.x_split = A > 1;
     qx.pos_dev = pos_dev; qx.row_pos = rp;
-    mgemm(m, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
     at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
     at.cap = Tm; at.ring = 0; at.window = 0;
     at.split_ws = nullptr;
     attn_split(m, s, at, sb.slice, pmax);
-    attn_decode(dt, at, st);
+    at.memory = 1;
+    timed(m, RLT_TIME_MEMORY_ATTN, st, [&] { attn_decode(dt, at, st); });
     EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
-    mgemm(m, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
     // SwiGLU FFN
     EpArgs sw;
     norm_in(sw, L.n3);
     sw.out = sb.hid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-    mgemm(m, dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
     EpArgs r3; r3.resid = sb.z; r3.rmap = zm; r3.x_split = A > 1;
     fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
     if (l + 1 == c.L_D) {
@@ -667,7 +703,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
         r3.fold_zb = sb.xs; r3.fold_ld = ad; r3.out_split = sd; r3.fold_ssp = sb.sssp; r3.fold_gain = m->ns;
       }
     }
-    mgemm(m, dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
+    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
   }
   if (c.L_D == 0) {
     // s_t = the last position's output of every sequence
@@ -710,7 +746,7 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
   if (!o.logits && !o.lp) return;
   rmsnorm(dt, src, sm, m->nO, xr, A * d, rows, d, c.rms_eps, st, A > 1 ? d : 0);
   EpArgs a; a.out = lbuf; a.ldo = V; a.x_split = A > 1;
-  mgemm(m, dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
+  mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
   if (o.logits) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
     copy_rows(lbuf, contiguous(V), o.logits + ((int64_t)b0 * o.ld_b + c0) * V, dm, rows, V, st);
@@ -1041,6 +1077,10 @@ std::vector<SnapPart> snapshot_parts(rlt_model* m, rlt_state* s, int n_enc, int 
     const int64_t er = (int64_t)c.L_E * B * H;
     v.push_back({(char*)s->enc_k, er, (int64_t)n_enc * dh * e, Tm * dh * e});
     v.push_back({(char*)s->enc_v, er, (int64_t)n_enc * dh * e, Tm * dh * e});
+    if (s->enc_lo > 0) {   // lo planes of two-term keys and values
+      v.push_back({(char*)s->enc_k + s->enc_lo * e, er, (int64_t)n_enc * dh * e, Tm * dh * e});
+      v.push_back({(char*)s->enc_v + s->enc_lo * e, er, (int64_t)n_enc * dh * e, Tm * dh * e});
+    }
   }
   const int64_t pend = (int64_t)(n_enc - n_dec) * d * 4;
   v.push_back({(char*)(s->e + (int64_t)n_dec * d), B, pend, Tm * d * 4});
@@ -1137,7 +1177,40 @@ int rlt_destroy(rlt_model* m) {
     if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
     if (m->n_states > 0) fail(RLT_ERR_INVALID_ARG, "destroy the model's states first");
     if (m->arena) HIPCHK(hipFree(m->arena));
+    for (auto& list : m->timed)
+      for (auto& pr : list) {
+        HIPCHK(hipEventDestroy(pr.first));
+        HIPCHK(hipEventDestroy(pr.second));
+      }
+    for (hipEvent_t e : m->ev_free) HIPCHK(hipEventDestroy(e));
     delete m;
+  });
+}
+
+int rlt_kernel_timing(rlt_model* m, int on) {
+  return guarded([&] {
+    if (!m) fail(RLT_ERR_INVALID_ARG, "null model");
+    m->timing = on != 0;
+  });
+}
+
+int rlt_kernel_time(rlt_model* m, int kind, double* total_ms, int64_t* launches) {
+  return guarded([&] {
+    if (!m || !total_ms || !launches) fail(RLT_ERR_INVALID_ARG, "null model or output");
+    if (kind < 0 || kind >= RLT_TIME_KINDS) fail(RLT_ERR_INVALID_ARG, "unknown kernel kind");
+    double tot = 0.0;
+    auto& list = m->timed[kind];
+    for (auto& pr : list) {
+      HIPCHK(hipEventSynchronize(pr.second));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, pr.first, pr.second));
+      tot += ms;
+      m->ev_free.push_back(pr.first);
+      m->ev_free.push_back(pr.second);
+    }
+    *total_ms = tot;
+    *launches = (int64_t)list.size();
+    list.clear();
   });
 }
 
@@ -1163,9 +1236,13 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       const int64_t B = batch, Tm = s->Tm, d = c.d, hd = m->hd, f = c.ffn, V = c.vocab, H = c.n_heads,
                     dh = c.d_head;
       const size_t e = m->esz;
+      // two-term encoder attention operands (with two-term GEMM inputs): C^E holds a lo plane
+      const int64_t EA = m->act;
       if (s->keep_enc) {
-        s->enc_k = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0, (int64_t)c.L_E * B * H * max_len * dh * e);
-        s->enc_v = dev_alloc(s, (size_t)c.L_E * B * H * Tm * dh * e, 0, (int64_t)c.L_E * B * H * max_len * dh * e);
+        const int64_t plane = (int64_t)c.L_E * B * H * Tm * dh;
+        s->enc_k = dev_alloc(s, (size_t)(EA * plane) * e, 0, EA * c.L_E * B * H * max_len * dh * (int64_t)e);
+        s->enc_v = dev_alloc(s, (size_t)(EA * plane) * e, 0, EA * c.L_E * B * H * max_len * dh * (int64_t)e);
+        s->enc_lo = EA > 1 ? plane : 0;
       }
       if (c.L_D > 0) {
         s->mem_k = dev_alloc(s, (size_t)c.groups * B * H * Tm * dh * e, 1, (int64_t)c.groups * B * H * max_len * dh * e);
@@ -1196,12 +1273,13 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->enc_rows = std::min<int64_t>(B * Tm, std::max<int64_t>(kEncoderRows, Tm));
       const int64_t er = s->enc_rows;
       s->exa = dev_alloc(s, er * A * d * e, 5);
-      s->eq = dev_alloc(s, er * hd * e, 5);
+      s->eq = dev_alloc(s, er * A * hd * e, 5);
       s->eao = dev_alloc(s, er * A * hd * e, 5);
       s->ehid = dev_alloc(s, er * A * f * e, 5);
       if (!s->keep_enc) {
-        s->ekv_k = dev_alloc(s, er * hd * e, 5);
-        s->ekv_v = dev_alloc(s, er * hd * e, 5);
+        s->ekv_k = dev_alloc(s, er * A * hd * e, 5);
+        s->ekv_v = dev_alloc(s, er * A * hd * e, 5);
+        s->ekv_lo = A > 1 ? er * hd : 0;
       }
       s->toks = (int32_t*)dev_alloc(s, sizeof(int32_t) * B * Tm, 5);
       s->glog = (float*)dev_alloc(s, sizeof(float) * B * V, 5);
@@ -1395,6 +1473,22 @@ int rlt_state_block_steps(const rlt_state* s, int64_t* out) {
   return guarded([&] {
     if (!s || !out) fail(RLT_ERR_INVALID_ARG, "null state or output");
     *out = s->block_steps;
+  });
+}
+
+int rlt_state_seek(rlt_model* m, rlt_state* s, int n, hipStream_t stream) {
+  return guarded([&] {
+    check_state(m, s);
+    leave_ragged(s);
+    if (n < s->n_dec || n > s->n_enc) fail(RLT_ERR_ORDER, "seek target must lie between the decoded and encoded positions");
+    const rlt_config& c = m->cfg;
+    const int64_t ring = (int64_t)c.L_D * s->B * c.n_heads * s->R * c.d_head * (int64_t)m->esz;
+    if (ring > 0) {
+      fill_zero_u32(s->ring_k, ring / 4, stream);
+      fill_zero_u32(s->ring_v, ring / 4, stream);
+    }
+    check_launch();
+    s->n_dec = n;
   });
 }
 

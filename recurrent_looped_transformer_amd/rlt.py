@@ -29,7 +29,10 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
            "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant", "rlt_replay_grad_workspace",
            "rlt_replay_grad", "rlt_step_rows", "rlt_state_reset_rows", "rlt_state_row_positions",
-           "rlt_sample_workspace"]
+           "rlt_sample_workspace", "rlt_state_seek", "rlt_kernel_timing", "rlt_kernel_time"]
+
+# kernel kinds of rlt_kernel_time (rlt_time_kind)
+TIME_MEMORY_ATTN, TIME_WINDOW_ATTN, TIME_ENCODER_ATTN, TIME_ENCODER_GEMM, TIME_DECODER_GEMM = range(5)
 
 
 class RltError(RuntimeError):
@@ -88,6 +91,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_step": [vp, vp, vp, vp, vp],
         "rlt_replay": [vp, vp, vp, i32, vp, vp, vp],
         "rlt_set_scan_mode": [vp, i32],
+        "rlt_state_seek": [vp, vp, i32, vp],
+        "rlt_kernel_timing": [vp, i32],
+        "rlt_kernel_time": [vp, i32, ctypes.POINTER(ctypes.c_double), i64p],
         "rlt_set_batch_invariant": [vp, i32],
         "rlt_state_block_steps": [vp, i64p],
         "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp,
@@ -207,6 +213,21 @@ def rlt_state_block_steps(state) -> int:
 
 def rlt_set_scan_mode(model, mode: int) -> None:
     _check(load().rlt_set_scan_mode(model, mode))
+
+
+def rlt_state_seek(model, state, n: int) -> None:
+    _check(load().rlt_state_seek(model, state, n, ctypes.c_void_p(_stream())))
+
+
+def rlt_kernel_timing(model, on: bool) -> None:
+    _check(load().rlt_kernel_timing(model, 1 if on else 0))
+
+
+def rlt_kernel_time(model, kind: int) -> tuple:
+    """(total ms, launches) of one kernel kind since the last read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load().rlt_kernel_time(model, kind, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def rlt_set_batch_invariant(model, on: bool) -> None:

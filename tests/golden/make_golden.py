@@ -10,6 +10,11 @@ holds the oracle's replay outputs for the named workload:
 The medium-LM file covers the first `--rows` sequences and `--len` positions of
 that workload's token stream (causality makes them independent of the rest).
 
+With --full-at P1,P2,... the file also holds full_at_pos [n] (1-based positions) and
+logits_full_at [B, n, V] (every id at those positions); with --param-cache DIR the
+parameters are read from float32 files written once under DIR (same values, memory-mapped:
+the paper shape's decoder then reads its weights from the page cache at every position).
+
 Usage: python tests/golden/make_golden.py algo_bf16 [rlt2_bf16 algo_bf16_rlt0 medium_lm ...]
 """
 from __future__ import annotations
@@ -26,7 +31,7 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 from oracle import Oracle, V0  # noqa: E402
-from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens  # noqa: E402
+from recurrent_looped_transformer_amd.synth import CONFIGS, file_params, make_params, make_tokens  # noqa: E402
 
 
 def workload(name: str, rows: int, length: int):
@@ -52,10 +57,13 @@ def main():
     ap.add_argument("--rows", type=int, default=2)
     ap.add_argument("--len", type=int, default=32)
     ap.add_argument("--tag", default="")
+    ap.add_argument("--full-at", default="", help="comma-separated 1-based positions stored with every id")
+    ap.add_argument("--param-cache", default="", help="directory of float32 parameter files")
     args = ap.parse_args()
     for name in args.names:
         cfg, x, dt = workload(name, args.rows, args.len)
-        P = make_params(cfg, bf16_storage=cfg.d >= 4096)
+        P = file_params(cfg, args.param_cache) if args.param_cache else \
+            make_params(cfg, bf16_storage=cfg.d >= 4096)
         t0 = time.time()
         lp, logits, s = Oracle(cfg, P, dt).replay(x)
         out = {"tokens": x, "logprob": lp.astype(np.float32), "s_last": s[:, -1].astype(np.float32),
@@ -69,6 +77,10 @@ def main():
             top = np.argsort(-logits, axis=-1, kind="stable")[..., :8]     # ties: lowest index first
             out["top8_idx"] = top.astype(np.int32)
             out["top8_val"] = np.take_along_axis(logits, top, -1).astype(np.float32)
+        if args.full_at:
+            pos = np.array([int(p) for p in args.full_at.split(",")], dtype=np.int32)
+            out["full_at_pos"] = pos
+            out["logits_full_at"] = logits[:, pos - 1].astype(np.float32)
         path = os.path.join(HERE, f"{name}{args.tag}.npz")
         np.savez_compressed(path, **out)
         print(f"{name}: B={x.shape[0]} T={x.shape[1]} oracle {time.time() - t0:.1f} s -> {path}", flush=True)

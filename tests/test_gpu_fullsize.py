@@ -2,9 +2,10 @@
 tests/golden/make_golden.py, which calls only the oracle and the seeded generators).
 
 The algorithmic-task shape (B 64 x T 257, RLT-1 and RLT-0) and the RLT-2 shape
-(B 128 x T 64, K_c 4, G = L_D) run at their full sizes, in the same launch
-configuration as the benchmark (automatic scan driver), in the persistent modes and with
-four batch slices on their own streams.
+(B 128 x T 64, K_c 4, G = L_D) run at their full sizes in fp16 arithmetic, in the same
+launch configuration as the benchmark (automatic scan driver), with four batch slices on
+their own streams, and as a graph replay per position. Bar: max abs logit error <= 2e-2
+and identical argmax (raw, no tie rule) on >= 99.9% of the 16,448 / 8,192 positions.
 """
 import os
 
@@ -49,7 +50,7 @@ def run(cfg, P, tokens, scan_mode):
         m.close()
 
 
-@pytest.mark.parametrize("scan_mode", [0, 3, 4, 8])
+@pytest.mark.parametrize("scan_mode", [0, 8, 9])
 @pytest.mark.parametrize("name", ["algo_bf16", "algo_bf16_rlt0", "rlt2_bf16"])
 def test_full_size_matches_oracle(name, scan_mode):
     g = load(name)
@@ -64,12 +65,11 @@ def test_full_size_matches_oracle(name, scan_mode):
     logits, s, lp = run(cfg, P, tokens, scan_mode)
     err = float(np.max(np.abs(logits - g["logits"])))
     gi, ri = np.argmax(logits, -1), np.argmax(g["logits"], -1)
-    ref_at = np.take_along_axis(g["logits"], gi[..., None], -1)[..., 0]
-    agree = float(np.mean((gi == ri) | (ref_at >= g["logits"].max(-1) - 2 * err)))
+    raw = float(np.mean(gi == ri))
     lp_err = float(np.max(np.abs(lp - g["logprob"])))
     s_err = float(np.max(np.abs(s[:, -1] - g["s_last"])))
-    print(f"[parity] {name} m{scan_mode}: logits max err {err:.3e}, argmax agreement {agree:.5f} "
-          f"(raw {np.mean(gi == ri):.5f}), logprob err {lp_err:.3e}, s_T err {s_err:.3e}", flush=True)
+    print(f"[parity] {name} m{scan_mode}: logits max err {err:.3e}, raw argmax agreement {raw:.5f} over "
+          f"{gi.size} positions, logprob err {lp_err:.3e}, s_T err {s_err:.3e}", flush=True)
     assert err <= 2e-2
-    assert agree >= 0.999
+    assert raw >= 0.999
     assert lp_err <= 2e-2

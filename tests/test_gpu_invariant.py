@@ -47,9 +47,9 @@ def run(m, cfg, x, p):
 
 CASES = {
     "tiny_fp32_rlt1": (TINY, {}),
-    "algo_bf16_rlt1": (ALGO, dict(batch=16, seq_len=40)),
-    "algo_bf16_rlt0": (ALGO, dict(batch=16, seq_len=40, variant=V0)),
-    "rlt2_bf16_k4_GLD": (CONFIGS["rlt2_bf16"], dict(batch=16, seq_len=40)),
+    "algo_bf16_rlt1": (ALGO, dict(batch=16, seq_len=40, compute="bf16")),
+    "algo_bf16_rlt0": (ALGO, dict(batch=16, seq_len=40, variant=V0, compute="bf16")),
+    "rlt2_bf16_k4_GLD": (CONFIGS["rlt2_bf16"], dict(batch=16, seq_len=40, compute="bf16")),
     "algo_fp16_rlt1": (ALGO, dict(batch=16, seq_len=40, compute="fp16")),
     "algo_fp16x2_rlt1": (ALGO, dict(batch=16, seq_len=40, compute="fp16x2")),
 }

@@ -3,7 +3,7 @@
 Workload: vocab 32000, d 2048, 16 x 128 heads, 24 + 24 blocks, SwiGLU 5632, W 512,
 G 1, RLT-1, batch 32, a 2048-token Zipf prompt followed by 256 more positions
 (2304 in all), every input from the seeded generators; bf16-valued weights, fp16
-arithmetic on the GPU path.
+arithmetic on the GPU path with two-term (hi + lo) fp16 GEMM activation inputs.
 
 - Replay of all 2304 positions at B = 32 in the benchmark's launch configuration,
   checked on sampled outputs against the oracle: rows 0-1 at positions 1-64 and
@@ -16,8 +16,9 @@ arithmetic on the GPU path.
   step log-probs and argmax with the full-size replay (serving-split invariance).
 
 The stored oracle logits are the first 64 ids at every position, every id at the
-last 8 positions, and the 8 largest per position; the near-tie argmax rule
-(oracle_j >= oracle_max - 2 * err) is applied through the stored top 8.
+last 8 positions, and the 8 largest per position (the oracle's argmax is the first of
+them). Bar: max abs logit error <= 2e-2 and the GPU's argmax identical to the oracle's
+(no tie rule) on >= 99.9% of the compared positions.
 """
 import os
 
@@ -31,8 +32,8 @@ from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_to
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 CFG = CONFIGS["medium_lm"]
-TOL = 2e-2            # bf16 path vs oracle, max abs logit / log-prob error
-TOL_GPU_GPU = 4e-2    # two bf16 GPU paths, each within TOL of the oracle
+TOL = 2e-2            # 16-bit path vs oracle, max abs logit / log-prob error
+TOL_GPU_GPU = 4e-2    # two 16-bit GPU paths, each within TOL of the oracle
 
 
 def load(name):
@@ -47,12 +48,9 @@ def param_probe(P):
     return np.concatenate([np.asarray(P[k]).ravel()[:8] for k in keys]).astype(np.float32)
 
 
-def argmax_check(gpu_argmax, top_idx, top_val, err):
-    """Share of positions whose GPU argmax is the oracle's, or within 2*err of the oracle max."""
-    raw = gpu_argmax == top_idx[..., 0]
-    hit = top_idx == gpu_argmax[..., None]
-    near = np.any(hit & (top_val >= top_val[..., :1] - 2 * err), axis=-1)
-    return float(np.mean(raw | near)), float(np.mean(raw))
+def raw_argmax(gpu_argmax, top_idx):
+    """Share of positions whose GPU argmax is the oracle's (no tie rule)."""
+    return float(np.mean(gpu_argmax == top_idx[..., 0]))
 
 
 def compare_rows(tag, lg_rows, lp_rows, s_rows, g):
@@ -62,14 +60,14 @@ def compare_rows(tag, lg_rows, lp_rows, s_rows, g):
     err_h = float(np.max(np.abs(head - g["logits_head"])))
     err_t = float(np.max(np.abs(tail - g["logits_tail"])))
     err = max(err_h, err_t)
-    agree, raw = argmax_check(lg_rows.argmax(-1).cpu().numpy(), g["top8_idx"], g["top8_val"], err)
+    raw = raw_argmax(lg_rows.argmax(-1).cpu().numpy(), g["top8_idx"])
     lp_err = float(np.max(np.abs(lp_rows.cpu().numpy() - g["logprob"])))
     s_err = float(np.max(np.abs(s_rows.cpu().numpy() - g["s_last"])))
     print(f"[parity] {tag}: logits err first-64 ids {err_h:.3e}, last-8 positions all ids {err_t:.3e}; "
-          f"argmax agreement {agree:.5f} (raw {raw:.5f}); log-prob err {lp_err:.3e}; s_T err {s_err:.3e}",
-          flush=True)
+          f"raw argmax agreement {raw:.5f} over {g['top8_idx'][..., 0].size} positions; log-prob err "
+          f"{lp_err:.3e}; s_T err {s_err:.3e}", flush=True)
     assert err <= TOL
-    assert agree >= 0.999
+    assert raw >= 0.999
     assert lp_err <= TOL
 
 
@@ -160,13 +158,11 @@ def test_lm_generation_steps_full_size(lm, replay):
     # serving-split invariance at full size: step chain vs replay, every row and step
     rep = replay["lg"][:, p:]
     d = float((lg_step - rep).abs().max())
-    ga, ra = lg_step.argmax(-1), rep.argmax(-1)
-    near = torch.gather(rep, -1, ga[..., None])[..., 0] >= rep.max(-1).values - 2 * d
-    agree = float(((ga == ra) | near).float().mean())
+    agree = float((lg_step.argmax(-1) == rep.argmax(-1)).float().mean())
     lps = torch.log_softmax(lg_step[:, :-1].double(), -1).gather(-1, x[:, p + 1:, None].long())[..., 0]
     lp_d = float((lps.float() - replay["lp"][:, p:T - 1]).abs().max())
     print(f"[parity] medium_lm rlt_step chain vs replay, positions {p + 1}-{T}, all rows: logits max diff "
-          f"{d:.3e}, argmax agreement {agree:.5f}, log-prob max diff {lp_d:.3e}", flush=True)
+          f"{d:.3e}, raw argmax agreement {agree:.5f}, log-prob max diff {lp_d:.3e}", flush=True)
     assert d <= TOL_GPU_GPU
     assert agree >= 0.999
     assert lp_d <= TOL_GPU_GPU

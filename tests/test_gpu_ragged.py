@@ -4,7 +4,7 @@ rlt_state_reset_rows, rlt_state_row_positions).
 Every row is an independent sequence (the state H_t is per sequence, greeksharifa summary
 §2.1), so the oracle runs each row alone, one consume per token, and the GPU's batched rows
 at unequal positions must match it: fp32 logits within 1e-4; the 16-bit algorithmic shape
-within the 2e-2 logit bar with argmax agreement. Schedules are seeded: each row moves with
+within the 2e-2 logit bar (raw argmax agreement printed). Schedules are seeded: each row moves with
 probability 0.6 per call, rows start late, rows fill max_len and stay idle while the others
 move (their discarded step lands in the slack position), rows are reset mid-stream and take
 a new sequence, RLT-2 rows close chunks at different calls (partial chunks inside a mixed
@@ -90,12 +90,10 @@ def compare(cfg, hist, ref, bar, tag):
             e = float(np.max(np.abs(g - rr)))
             worst = max(worst, e)
             n += 1
-            top = int(np.argmax(g))
-            agree += int(rr[top] >= rr.max() - 2 * e)
-    print(f"[ragged] {tag}: {n} row-steps, max abs logit err {worst:.2e}, argmax agreement {agree / n:.4f}",
+            agree += int(np.argmax(g) == np.argmax(rr))
+    print(f"[ragged] {tag}: {n} row-steps, max abs logit err {worst:.2e}, raw argmax agreement {agree / n:.4f}",
           flush=True)
     assert worst <= bar, (tag, worst)
-    assert agree / n >= 0.999
 
 
 CASES = {
