@@ -246,6 +246,18 @@ int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float tempe
                uint64_t step, int32_t* tokens, float* logprob, void* workspace, int64_t workspace_bytes,
                hipStream_t stream);
 
+/* rlt_sample for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same draws and log mu, bit for bit, as
+ * rlt_sample with a workspace, with the chunk statistics in a static device array of 1 MiB
+ * that the library holds on every GPU it runs on until the process ends (its address is
+ * looked up once per device, on the first call there). Calls no allocation routine. Every
+ * call on a GPU uses that GPU's one array: calls that overlap on one GPU (different streams,
+ * or different threads) race and give undefined results; calls ordered on one stream do not.
+ * Capacity: rows * ceil(vocab / 4096) * 32 bytes <= 1 MiB (e.g. 4096 rows of a 32000-id
+ * vocabulary); larger calls fail with CAPACITY before any launch. Other errors as rlt_sample. */
+int rlt_sample_noalloc(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
+                       uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream);
+
 /* Generation F.2 with on-device behaviour sampling ([S] appendix F.2; [R] §6.2 Figure 4):
  * consume `first` (device int32 [B], the last emitted token of every row: it is consumed
  * once before continuing), then n times: draw x_i ~ mu from the new logits as rlt_sample

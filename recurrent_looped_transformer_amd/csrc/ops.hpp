@@ -151,6 +151,10 @@ void sample_rows(const float* logits, int64_t ld, int rows, int V, float tempera
                  void* ws = nullptr);
 // bytes of the optional sample_rows workspace (chunk statistics of every row) for rows x V
 int64_t sample_workspace_bytes(int rows, int V);
+// Size of the sampler's static scratch array (one per GPU, held until the process ends) and the
+// current device's address of it (looked up once per device; no allocation).
+constexpr int64_t kSampleScratchBytes = 1 << 20;
+hipError_t sample_scratch(void** out);
 // ratio[i] = exp(lp_cur[i] - lp_beh[i]) (float64 inside)
 void importance_ratio(const float* lp_cur, const float* lp_beh, int64_t n, float* ratio, hipStream_t st);
 // pack fp32 [N, K] into the library layout: dst row r <- src row perm(r); perm per kind.

@@ -18,6 +18,7 @@
 // noise (two logarithms per id). The replay's next-token log-probability (logprob_k) uses
 // the same chunked log-sum-exp, so both evaluate log softmax identically.
 #include <climits>
+#include <mutex>
 
 #include "common.hpp"
 #include "ops.hpp"
@@ -255,6 +256,36 @@ __global__ void ratio_k(const float* __restrict__ a, const float* __restrict__ b
 
 int64_t sample_workspace_bytes(int rows, int V) {
   return (int64_t)rows * ((V + kChunk - 1) / kChunk) * (int64_t)sizeof(ChunkStat);
+}
+
+// Scratch of the allocation-free sampler entry point: the chunk statistics of one call, in a
+// device array of fixed size that the library holds on every GPU it runs on until the process
+// ends. Host code never passes the array's name to a kernel (in host code it is a stand-in,
+// not a device address): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kSampleScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_ok[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t sample_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ok[dev]) {   // first call on this device (the device is current)
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+    g_scratch_ok[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 void sample_rows(const float* logits, int64_t ld, int rows, int V, float temperature, uint64_t seed, uint64_t step,

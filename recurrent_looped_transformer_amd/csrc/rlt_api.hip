@@ -1647,6 +1647,24 @@ int rlt_sample(const float* logits, int rows, int vocab, int64_t ld, float tempe
   });
 }
 
+int rlt_sample_noalloc(const float* logits, int rows, int vocab, int64_t ld, float temperature, uint64_t seed,
+                       uint64_t step, int32_t* tokens, float* logprob, hipStream_t stream) {
+  return guarded([&] {
+    if (!logits || !tokens) fail(RLT_ERR_INVALID_ARG, "logits and tokens required");
+    if (rows < 0 || vocab < 1 || ld < vocab) fail(RLT_ERR_INVALID_ARG, "rows >= 0, vocab >= 1, ld >= vocab required");
+    if (vocab > (1 << 20)) fail(RLT_ERR_UNSUPPORTED, "vocab > 2^20");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature))
+      fail(RLT_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+    if (sample_workspace_bytes(rows, vocab) > kSampleScratchBytes)
+      fail(RLT_ERR_CAPACITY, "rows x vocabulary chunks exceed the static scratch (" +
+                                 std::to_string(kSampleScratchBytes) + " bytes: rows * ceil(vocab / 4096) * 32)");
+    void* ws = nullptr;
+    HIPCHK(sample_scratch(&ws));
+    sample_rows(logits, ld, rows, vocab, temperature, seed, step, tokens, 1, logprob, 1, nullptr, stream, ws);
+    check_launch();
+  });
+}
+
 int rlt_generate(rlt_model* m, rlt_state* s, const int32_t* first, int n, float temperature, uint64_t seed,
                  uint64_t step0, int32_t* tokens, float* logprob, float* logits, hipStream_t stream) {
   return guarded([&] {

@@ -29,7 +29,7 @@ EXPORTS = ["rlt_create", "rlt_update_weights", "rlt_destroy", "rlt_state_create"
            "rlt_last_error", "rlt_sample", "rlt_generate", "rlt_importance_ratio", "rlt_snapshot_size",
            "rlt_snapshot", "rlt_restore", "rlt_set_batch_invariant", "rlt_replay_grad_workspace",
            "rlt_replay_grad", "rlt_step_rows", "rlt_state_reset_rows", "rlt_state_row_positions",
-           "rlt_sample_workspace", "rlt_state_seek", "rlt_kernel_timing", "rlt_kernel_time"]
+           "rlt_sample_workspace", "rlt_state_seek", "rlt_kernel_timing", "rlt_kernel_time", "rlt_sample_noalloc"]
 
 # kernel kinds of rlt_kernel_time (rlt_time_kind)
 TIME_MEMORY_ATTN, TIME_WINDOW_ATTN, TIME_ENCODER_ATTN, TIME_ENCODER_GEMM, TIME_DECODER_GEMM = range(5)
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rlt_sample": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp,
                        ctypes.c_int64, vp],
         "rlt_sample_workspace": [i32, i32, i64p],
+        "rlt_sample_noalloc": [vp, i32, i32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp,
+                               vp, vp],
         "rlt_generate": [vp, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp],
         "rlt_importance_ratio": [vp, vp, ctypes.c_int64, vp, vp],
         "rlt_snapshot_size": [vp, vp, i64p],
@@ -269,6 +271,15 @@ def rlt_sample(logits: torch.Tensor, temperature: float, seed: int, step: int, t
     wn = workspace.numel() if workspace is not None else 0
     _check(load().rlt_sample(_ptr(logits), rows, V, V, temperature, seed, step, _ptr(tokens), _ptr(logprob),
                              ws, wn, ctypes.c_void_p(_stream())))
+
+
+def rlt_sample_noalloc(logits: torch.Tensor, temperature: float, seed: int, step: int, tokens: torch.Tensor,
+                       logprob: Optional[torch.Tensor] = None) -> None:
+    """rlt_sample with the library's static scratch (no allocation here or in the library)."""
+    assert logits.dtype == torch.float32 and logits.dim() == 2 and tokens.dtype == torch.int32
+    rows, V = logits.shape
+    _check(load().rlt_sample_noalloc(_ptr(logits), rows, V, V, temperature, seed, step, _ptr(tokens), _ptr(logprob),
+                                     ctypes.c_void_p(_stream())))
 
 
 def rlt_generate(model, state, first: torch.Tensor, n: int, temperature: float, seed: int, step0: int,
