@@ -120,6 +120,20 @@ __device__ __forceinline__ void store16(bf16_t* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = o;
 }
 
+// 16-byte load with the nontemporal hint: for streams read once per launch and larger than the
+// last-level cache (measured on MI355X: a 4 GB read streams at 7.1 TB/s this way against 6.25
+// TB/s with plain loads)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (NT) return ld16_nt(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+
 // ---------------------------------------------------------------- MFMA
 // D(16x16, fp32) += A(16x32) * B(32x16), 16-bit inputs of type T (gfx950
 // v_mfma_f32_16x16x32_bf16 / _f16). Lane l supplies A row (l % 16), k = 8*(l / 16) .. +7

@@ -212,6 +212,8 @@ struct AttnArgs {
   // products hi*hi + hi*lo + lo*hi (prefill, whose probabilities are split the same way).
   int64_t q_lo = 0;
   int64_t kv_lo = 0;
+  int stream = 0;               // 1: nontemporal key / value loads (the launch streams more than the
+                                // last-level cache holds)
   int memory = 0;               // 1: the decoder's cross-attention over the memory (its own kernel
                                 // instance, so profiles report it apart from the window attention)
 };

@@ -21,7 +21,9 @@ namespace rlt {
 // SPLIT: this block takes the keys [z * split_keys, (z + 1) * split_keys) of its range
 // (z = blockIdx.z) and writes its partial softmax sums to split_ws for attn_combine_k.
 // X2: two-term query, keys and values (q_lo, kv_lo): each operand is hi + lo in fp32.
-template <typename T, int DH, bool SPLIT, int MEM, bool X2 = false>
+// NT: keys and values read with the nontemporal hint (launches that stream more than the
+// last-level cache holds).
+template <typename T, int DH, bool SPLIT, int MEM, bool X2 = false, bool NT = false>
 __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int G = DH / VEC;              // lanes per key
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
     if (j < je) {                                                               \
       const int p = lo + j;                                                     \
       const int slot = a.ring ? (p - 1) % a.cap : p - 1;                        \
-      K_[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)slot * DH);         \
-      V_[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)slot * DH);         \
+      K_[u] = ld16<NT>(kb + (int64_t)slot * DH);                                \
+      V_[u] = ld16<NT>(vb + (int64_t)slot * DH);                                \
       if constexpr (X2) {                                                       \
         KL_[u] = *reinterpret_cast<const uint4*>(kb + a.kv_lo + (int64_t)slot * DH); \
         VL_[u] = *reinterpret_cast<const uint4*>(vb + a.kv_lo + (int64_t)slot * DH); \
@@ -213,14 +215,19 @@ static void launch_attn(const AttnArgs& a0, hipStream_t st) {
   // two-term operands (the encoder's, 16-bit types) take the X2 instances
   const dim3 grid(a.H, a.B * a.nq, S);
   const bool x2 = !__is_same(T, float) && (a.q_lo > 0 || a.kv_lo > 0);
+  const bool nt = a.stream != 0 && !x2;
   if (S > 1) {
     if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, true>), grid, dim3(256), 0, st, a);
+    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1, false, true>), grid, dim3(256), 0, st, a);
     else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1>), grid, dim3(256), 0, st, a);
+    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, false, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
   } else {
     if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, true>), grid, dim3(256), 0, st, a);
+    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1, false, true>), grid, dim3(256), 0, st, a);
     else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1>), grid, dim3(256), 0, st, a);
+    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, false, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0>), grid, dim3(256), 0, st, a);
   }
 }

@@ -15,6 +15,7 @@
 //    buffer, 4 waves x (64x64) of 16x16x32 MFMAs.
 //  The 16-bit kernels take T = bf16_t or f16_t (storage and MFMA input type).
 //  - gemm_f32: the fp32 configuration (vector FMA).
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -666,6 +667,19 @@ static bool large_gemm_enabled() {
   return state == 1;
 }
 
+// RLT_SKINNY_TILE=<TPW>x<NMB> (one of the candidates below) makes every decode GEMM whose N
+// admits it take that tile shape instead of the cost model's choice (tile measurements).
+static void skinny_override(int& tpw, int& nmb) {
+  static const int v = [] {
+    const char* env = getenv("RLT_SKINNY_TILE");
+    int t = 0, n = 0;
+    if (env && sscanf(env, "%dx%d", &t, &n) == 2) return t * 16 + n;
+    return 0;
+  }();
+  tpw = v / 16;
+  nmb = v % 16;
+}
+
 template <typename T, Ep E>
 static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
                      hipStream_t st) {
@@ -684,12 +698,15 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     // workgroup's bytes (TPW weight tiles + the X rows it reads) at the per-CU rate.
     const dim3 blk(kSkW * WAVE);
     const int64_t xs = a.x_split ? 2 : 1, e = sizeof(T);
-    static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
+    static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}, {4, 4}};
     int best_t = 1, best_n = 1;
     int64_t best_cost = -1;
+    int ov_t = 0, ov_n = 0;
+    skinny_override(ov_t, ov_n);
     for (const auto& c : cand) {
       const int tpw = c[0], nmb = c[1];
       if (tpw > 1 && N % (16 * tpw) != 0) continue;   // one tile per workgroup covers a ragged N
+      if (tpw * nmb > 8) continue;                     // 4 x 4 only on request
       const int64_t wgs = (int64_t)((N + 16 * tpw - 1) / (16 * tpw)) * ((M + 16 * nmb - 1) / (16 * nmb));
       const int64_t rows = std::min(16 * nmb, M);
       const int64_t bytes = (int64_t)tpw * 16 * K * e + rows * K * e * xs;
@@ -700,6 +717,10 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
         best_n = nmb;
       }
     }
+    if (ov_t && (ov_t == 1 || N % (16 * ov_t) == 0)) {
+      best_t = ov_t;
+      best_n = ov_n;
+    }
     const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n));
 #define RLT_SKINNY(NMB_, TPW_)                                                                                   \
   if (best_n == NMB_ && best_t == TPW_) {                                                                        \
@@ -708,7 +729,7 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     return;                                                                                                      \
   }
     RLT_SKINNY(1, 1) RLT_SKINNY(2, 1) RLT_SKINNY(4, 1) RLT_SKINNY(1, 2) RLT_SKINNY(2, 2) RLT_SKINNY(4, 2)
-    RLT_SKINNY(1, 4) RLT_SKINNY(2, 4)
+    RLT_SKINNY(1, 4) RLT_SKINNY(2, 4) RLT_SKINNY(4, 4)
 #undef RLT_SKINNY
   } else if (large_gemm_enabled() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);

@@ -64,6 +64,7 @@ constexpr int kReadoutPositions = 64;   // positions per batched readout
 constexpr int kMaxSlices = 4;           // concurrent batch slices of the launch-path scan
 constexpr int kParallelPositions = 64;  // RLT-0 positions per decoder pass
 constexpr int64_t kEncoderRows = 32768; // encoder workspace rows (sequences x tokens per group)
+constexpr int64_t kStreamBytes = 256ll << 20;   // last-level cache: larger streams load nontemporally
 constexpr int kStage = 8;               // pinned staging slots of the per-row position arrays
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -666,7 +667,16 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     at.pos0 = t0; at.window = c.window; at.scale = scale; at.pos_dev = pos_dev; at.row_pos = rp;
     const int pmax = pos_dev ? 0 : (rp ? pos_max : t0 + np);
     attn_split(m, s, at, sb.slice, std::min(pmax, c.window));
-    timed(m, RLT_TIME_WINDOW_ATTN, st, [&] { attn_decode(dt, at, st); });
+    // passes of many positions (RLT-0) attend on MFMA tiles that the pass's queries of a
+    // (sequence, head) share: the window and prefix masks of the flash kernel
+    const bool tiles = np >= 16 && !m->batch_invariant && !pos_dev && !rp;
+    // launches that read more keys and values than the last-level cache holds stream them with
+    // the nontemporal hint (bytes of the longest range, every row)
+    const int64_t kv_row = 2 * (int64_t)hd * m->esz;
+    at.stream = (int64_t)B * std::min(pmax > 0 ? pmax : s->cap, c.window) * kv_row > kStreamBytes;
+    timed(m, RLT_TIME_WINDOW_ATTN, st, [&] {
+      if (!(tiles && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+    });
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
     mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
@@ -683,7 +693,10 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     at.split_ws = nullptr;
     attn_split(m, s, at, sb.slice, pmax);
     at.memory = 1;
-    timed(m, RLT_TIME_MEMORY_ATTN, st, [&] { attn_decode(dt, at, st); });
+    at.stream = (int64_t)B * (pmax > 0 ? pmax : s->cap) * kv_row > kStreamBytes;
+    timed(m, RLT_TIME_MEMORY_ATTN, st, [&] {
+      if (!(tiles && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
+    });
     EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
     mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);

@@ -13,6 +13,10 @@ Rounding points (each "fp16", "bf16", "fp16x2" = two fp16 terms hi + lo, or abse
   swa_qkv  decoder window query, keys and values
   cross_q  decoder cross-attention query
   act      inputs of the projections: every RMSNorm output
+  enc_act  the encoder's projection inputs: its RMSNorm outputs (blocks and memory norm), its
+           attention outputs and SwiGLU hidden rows
+  dec_act  the decoder's projection inputs: its RMSNorm outputs (merge, blocks, readout), its
+           attention outputs and SwiGLU hidden rows
 
 The encoder runs token by token here (the oracle's incremental encoder, pinned equal to
 its parallel form), so every attention goes through Oracle.attend.
@@ -22,6 +26,7 @@ its parallel form), so every attention goes through Oracle.attend.
 from __future__ import annotations
 
 import argparse
+import json
 import time
 
 import numpy as np
@@ -29,7 +34,7 @@ import numpy as np
 from oracle import Oracle
 from recurrent_looped_transformer_amd.synth import CONFIGS, file_params, make_params, make_tokens, round_bf16
 
-POINTS = ("enc_qk", "enc_v", "enc_p", "mem_kv", "swa_qkv", "cross_q", "act")
+POINTS = ("enc_qk", "enc_v", "enc_p", "mem_kv", "swa_qkv", "cross_q", "act", "enc_act", "dec_act")
 
 
 def rounder(kind):
@@ -64,7 +69,18 @@ class RoundingOracle(Oracle):
 
     def rms(self, x, gain):
         y = super().rms(x, gain)
-        return self._rd("act", y) if gain is not None else y
+        if gain is None:
+            return y
+        y = self._rd("act", y)
+        return self._rd("enc_act" if self._ctx == "enc" else "dec_act", y)
+
+    def swiglu(self, x, w1, w3, w2):
+        point = "enc_act" if self._ctx == "enc" else "dec_act"
+        if self.r[point] is None:
+            return super().swiglu(x, w1, w3, w2)
+        a = x @ w1.T
+        b = x @ w3.T
+        return self._rd(point, a * self.sigmoid(a) * b) @ w2.T
 
     def attend(self, q, keys, vals):
         if self._ctx == "enc":
@@ -80,13 +96,14 @@ class RoundingOracle(Oracle):
                 q, keys, vals = (self._rd("swa_qkv", a) for a in (q, keys, vals))
             pr = None
         if pr is None:
-            return super().attend(q, keys, vals)
+            out = super().attend(q, keys, vals)
+            return self._rd("enc_act" if self._ctx == "enc" else "dec_act", out)
         H, dh = self.cfg.n_heads, self.cfg.d_head
         B, n = keys.shape[0], keys.shape[1]
         s = np.einsum("bhd,bnhd->bhn", q.reshape(B, H, dh), keys.reshape(B, n, H, dh)) / np.sqrt(self.dt.type(dh))
         e = np.exp(s - s.max(axis=-1, keepdims=True))
         out = np.einsum("bhn,bnhd->bhd", pr(e).astype(self.dt), vals.reshape(B, n, H, dh))
-        return (out / e.sum(axis=-1)[..., None]).reshape(B, H * dh)
+        return self._rd("enc_act", (out / e.sum(axis=-1)[..., None]).reshape(B, H * dh))
 
     def encoder_step(self, st, x):
         self._ctx = "enc"
@@ -141,12 +158,14 @@ def main():
     ap.add_argument("--rows", type=int, default=1)
     ap.add_argument("--param-cache", default="")
     ap.add_argument("--only-gpu-spec", action="store_true")
+    ap.add_argument("--specs", default="", help="JSON list of specs to run instead of the study")
     args = ap.parse_args()
     cfg = CONFIGS[args.shape]
     P = file_params(cfg, args.param_cache) if args.param_cache else make_params(cfg, bf16_storage=cfg.d >= 4096)
     tokens = make_tokens(cfg, length=cfg.seq_len + cfg.gen_len)[:args.rows, :args.positions]
     ref = RoundingOracle(cfg, P, {}).logits(tokens)
-    for spec in ([GPU_FP16X2] if args.only_gpu_spec else STUDY):
+    specs = json.loads(args.specs) if args.specs else ([GPU_FP16X2] if args.only_gpu_spec else STUDY)
+    for spec in specs:
         t0 = time.time()
         got = RoundingOracle(cfg, P, spec).logits(tokens)
         print(f"{args.shape} rows {args.rows} x {args.positions} positions {spec}: max logit shift "
