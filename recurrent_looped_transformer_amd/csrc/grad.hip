@@ -421,11 +421,13 @@ __global__ __launch_bounds__(256) void g_rms_bwd(int M, int d, const float* __re
   }
 }
 
-// dg[j] += sum_rows dy[row, j] * (x ? x[row, j] * rstd[row] : 1)  (gain or bias gradient)
+// dg[j] += sum_rows dy[row, j] * (x ? x[row, j] * rstd[row] : 1)  (gain or bias gradient):
+// each chunk of kColRows rows writes its column sums to part[chunk], then g_colsum_reduce adds
+// the chunks in ascending order (a fixed summation order: two calls give the same bits)
 constexpr int kColRows = 64;
 __global__ __launch_bounds__(256) void g_colsum(int M, int d, const float* __restrict__ dy,
                                                 const float* __restrict__ x, const float* __restrict__ rstd,
-                                                float* __restrict__ dg) {
+                                                float* __restrict__ part) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= d) return;
   const int r0 = blockIdx.y * kColRows, r1 = min(M, r0 + kColRows);
@@ -434,7 +436,14 @@ __global__ __launch_bounds__(256) void g_colsum(int M, int d, const float* __res
     const float v = dy[(int64_t)r * d + j];
     acc += x ? v * x[(int64_t)r * d + j] * rstd[r] : v;
   }
-  atomicAdd(dg + j, acc);
+  part[(int64_t)blockIdx.y * d + j] = acc;
+}
+__global__ void g_colsum_reduce(int d, int chunks, const float* __restrict__ part, float* __restrict__ dg) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  float acc = 0.f;
+  for (int y = 0; y < chunks; ++y) acc += part[(int64_t)y * d + j];
+  dg[j] += acc;
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -478,14 +487,84 @@ __global__ void g_embed(int B, int T, int d, const int32_t* __restrict__ tok, co
   h[idx] = emb[(int64_t)tok[(int64_t)b * T + t] * d + j];
 }
 
-__global__ void g_embed_bwd(int B, int T, int d, const int32_t* __restrict__ tok, const float* __restrict__ gh,
-                            float* __restrict__ gemb) {
+// Embedding gradient gemb[v] += sum of gh[row] over the rows (row = t * B + b) whose token is v,
+// in ascending row order: rows counted per token (integer counts), token starts by a scan,
+// rows placed stably into per-token runs, then each (token, column) sums its run in order.
+__device__ __forceinline__ int tok_of(const int32_t* tok, int B, int T, int r) {
+  return tok[(int64_t)(r % B) * T + r / B];
+}
+__global__ void g_tok_hist(int M, int B, int T, const int32_t* __restrict__ tok, int* __restrict__ cnt) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < M) atomicAdd(cnt + tok_of(tok, B, T, r), 1);
+}
+// start[v] = sum_{u < v} cnt[u] (one workgroup of 1024 threads, each owning a run of ids)
+__global__ __launch_bounds__(1024) void g_tok_scan(int V, const int* __restrict__ cnt, int* __restrict__ start) {
+  __shared__ int sums[1024];
+  const int per = (V + 1023) / 1024, i0 = threadIdx.x * per, i1 = min(V, i0 + per);
+  int s = 0;
+  for (int i = i0; i < i1; ++i) s += cnt[i];
+  sums[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int k = 0; k < 1024; ++k) {
+      const int v = sums[k];
+      sums[k] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int run = sums[threadIdx.x];
+  for (int i = i0; i < i1; ++i) {
+    start[i] = run;
+    run += cnt[i];
+  }
+}
+// Stable placement (one workgroup): rows in chunks of 1024, in order; a row's place in its
+// token's run is the run's fill so far plus the rows of the same token earlier in the chunk.
+__global__ __launch_bounds__(1024) void g_tok_place(int M, int B, int T, const int32_t* __restrict__ tok,
+                                                     int* __restrict__ fill, int* __restrict__ order) {
+  __shared__ int ct[1024];
+  for (int r0 = 0; r0 < M; r0 += 1024) {
+    const int r = r0 + threadIdx.x;
+    const int v = r < M ? tok_of(tok, B, T, r) : -1;
+    ct[threadIdx.x] = v;
+    __syncthreads();
+    int before = 0, after = 0;
+    for (int k = 0; k < 1024; ++k) {
+      const int u = ct[k];
+      before += (k < (int)threadIdx.x && u == v) ? 1 : 0;
+      after += (k > (int)threadIdx.x && u == v) ? 1 : 0;
+    }
+    int base = 0;
+    if (v >= 0) base = fill[v];
+    __syncthreads();            // every thread has read fill for this chunk
+    if (v >= 0) {
+      order[base + before] = r;
+      if (after == 0) fill[v] = base + before + 1;   // the chunk's last row of token v
+    }
+    __syncthreads();
+  }
+}
+__global__ void g_embed_sum(int V, int d, const int* __restrict__ start, const int* __restrict__ cnt,
+                            const int* __restrict__ order, const float* __restrict__ gh, float* __restrict__ gemb) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)B * T * d) return;
-  const int j = (int)(idx % d);
-  const int64_t row = idx / d;
-  const int b = (int)(row % B), t = (int)(row / B);
-  atomicAdd(gemb + (int64_t)tok[(int64_t)b * T + t] * d + j, gh[idx]);
+  if (idx >= (int64_t)V * d) return;
+  const int v = (int)(idx / d), j = (int)(idx % d);
+  const int s0 = start[v], n = cnt[v];
+  // eight interleaved partial sums (row i of the run into sum i % 8), added in index order:
+  // a fixed order, with eight independent loads in flight
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += gh[(int64_t)order[s0 + i + u] * d + j];
+  }
+  for (int u = 0; i + u < n; ++u) acc[u] += gh[(int64_t)order[s0 + i + u] * d + j];
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) sum += acc[u];
+  gemb[idx] += sum;
 }
 
 __global__ void g_fill(int64_t n, float* p, float v) {
@@ -1001,6 +1080,10 @@ struct Ctx {
   hipStream_t st;
   float* part = nullptr;   // split-K partial sums of the small-M products
   int64_t part_cap = 0;    // floats
+  float* wpart = nullptr;  // split-K partial sums of the weight gradients (k = every row)
+  int64_t wpart_cap = 0;   // floats
+  float* cpart = nullptr;  // column-sum partials (one row per chunk of rows)
+  int64_t cpart_cap = 0;   // floats
   const float2* rope_tab = nullptr;   // rotary factors [position][d_head / 2]
   hipError_t err = hipSuccess;
   void check() {
@@ -1058,13 +1141,17 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT;
   int splits = 1;
   float* part = nullptr;
+  bool accumulate = false;
   if (atomic) {
+    // C += A.B: k slices write partial sums that a second kernel adds to C in slice order
+    // (deterministic); one slice adds in place
     const int want = std::max(1, 1024 / (tm * tn));
     splits = std::max(1, std::min(want, (K + 255) / 256));
-    if (splits == 1) {   // one slice: a plain read-add-write is exact and deterministic
-      atomic = false;
-      R = C;
-    }
+    while (splits > 1 && (int64_t)splits * M * N > c.wpart_cap) --splits;
+    atomic = false;
+    R = C;
+    accumulate = true;
+    if (splits > 1) part = c.wpart;
   } else if (tm * tn < 128 && K >= 128 && c.part) {
     splits = std::min({kMaxSplits, (512 + tm * tn - 1) / (tm * tn), K / 32});
     while (splits > 1 && (int64_t)splits * M * N > c.part_cap) --splits;
@@ -1075,6 +1162,7 @@ void gemm(Ctx& c, int M, int N, int K, const float* A, int64_t lda, bool ak, con
   if (kchunk <= 0) kchunk = GK;
   splits = std::max(1, (K + kchunk - 1) / kchunk);
   if (splits == 1) part = nullptr;
+  (void)accumulate;
   dim3 grid(tn, tm, splits);
   const int at = atomic ? 1 : 0;
   if (ak && !atomic) {   // k-contiguous A (every product but the weight gradients): the MFMA form
@@ -1174,8 +1262,14 @@ void rms_bwd(Ctx& c, int M, int d, const float* dy, const float* x, const float*
 }
 void colsum(Ctx& c, int M, int d, const float* dy, const float* x, const float* rstd, float* dg) {
   if (M <= 0) return;
-  dim3 grid((d + 255) / 256, (M + kColRows - 1) / kColRows);
-  g_colsum<<<grid, 256, 0, c.st>>>(M, d, dy, x, rstd, dg);
+  const int chunks = (M + kColRows - 1) / kColRows;
+  if ((int64_t)chunks * d > c.cpart_cap) {
+    if (c.err == hipSuccess) c.err = hipErrorInvalidValue;
+    return;
+  }
+  dim3 grid((d + 255) / 256, chunks);
+  g_colsum<<<grid, 256, 0, c.st>>>(M, d, dy, x, rstd, c.cpart);
+  g_colsum_reduce<<<(d + 255) / 256, 256, 0, c.st>>>(d, chunks, c.cpart, dg);
   c.check();
 }
 void rope(Ctx& c, int M, int H, int dh, float* x, int pos0, int rpp, float sgn) {
@@ -1328,6 +1422,9 @@ struct DecBuf {
 };
 struct Bufs {
   bool ck = false;
+  float *wpart = nullptr, *cpart = nullptr;
+  int64_t wpart_n = 0, cpart_n = 0;
+  int *tcnt = nullptr, *tstart = nullptr, *tfill = nullptr, *torder = nullptr;   // embedding gradient order
   float2* rope_tab = nullptr;   // rotary factors of positions 0..T
   std::vector<float*> eh;   // L_E + 1 residual streams
   std::vector<EncBuf> enc;  // every layer, or one (checkpointing: each layer recomputed from eh)
@@ -1392,6 +1489,17 @@ void plan(const rlt_config& c, int B, int T, bool ck, Arena& A, Bufs& u) {
   u.geo = A.f(M * hd); u.geq = A.f(M * hd); u.gek = A.f(M * hd); u.gev = A.f(M * hd); u.Dq = A.f(M * H);
   u.part_n = (int64_t)kMaxSplits * B * std::max({d, hd, f, 2 * d, 3 * hd, 2 * f, (int64_t)c.vocab});
   u.part = A.f(u.part_n);
+  // weight-gradient slices: room for 4 slices of the largest weight matrix (fewer slices when a
+  // product would need more), at most 256 M floats
+  u.wpart_n = std::min<int64_t>((int64_t)4 * std::max({hd * d, f * d, d * d, (int64_t)c.vocab * d}),
+                                (int64_t)256 << 20);
+  u.wpart = A.f(u.wpart_n);
+  u.cpart_n = (M + kColRows - 1) / kColRows * d;
+  u.cpart = A.f(u.cpart_n);
+  u.tcnt = reinterpret_cast<int*>(A.f(c.vocab));
+  u.tstart = reinterpret_cast<int*>(A.f(c.vocab));
+  u.tfill = reinterpret_cast<int*>(A.f(c.vocab));
+  u.torder = reinterpret_cast<int*>(A.f(M));
   u.rope_tab = reinterpret_cast<float2*>(A.f((int64_t)2 * (T + 1) * (c.d_head / 2)));
   for (int l = 0; l < c.L_E; ++l) {
     u.qkv_e.push_back(A.f(3 * hd * d));
@@ -1429,6 +1537,10 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
   plan(cf, B, T, checkpoint, A, u);
   c.part = u.part;
   c.part_cap = u.part_n;
+  c.wpart = u.wpart;
+  c.wpart_cap = u.wpart_n;
+  c.cpart = u.cpart;
+  c.cpart_cap = u.cpart_n;
   c.rope_tab = u.rope_tab;
   const bool ck = checkpoint;
   const int M = B * T, d = cf.d, H = cf.n_heads, dh = cf.d_head, hd = H * dh, f = cf.ffn, V = cf.vocab;
@@ -1812,8 +1924,12 @@ hipError_t replay_grad(const rlt_config& cf, const std::map<std::string, const f
     gh = u.gh;
   }
   {
-    const int64_t n = (int64_t)M * d;
-    g_embed_bwd<<<blocks(n), 256, 0, c.st>>>(B, T, d, tokens, gh, g("emb"));
+    fill(c, reinterpret_cast<float*>(u.tcnt), V, 0.f);   // zero bits: integer zeros
+    g_tok_hist<<<blocks(M), 256, 0, c.st>>>(M, B, T, tokens, u.tcnt);
+    g_tok_scan<<<1, 1024, 0, c.st>>>(V, u.tcnt, u.tstart);
+    hipMemcpyAsync(u.tfill, u.tstart, sizeof(int) * V, hipMemcpyDeviceToDevice, c.st);
+    g_tok_place<<<1, 1024, 0, c.st>>>(M, B, T, tokens, u.tfill, u.torder);
+    g_embed_sum<<<blocks((int64_t)V * d), 256, 0, c.st>>>(V, d, u.tstart, u.tcnt, u.torder, gh, g("emb"));
     c.check();
   }
   return c.err;
