@@ -102,6 +102,9 @@ struct EpArgs {
   // Row-invariant arithmetic: every row count takes the decode kernel, whose per-row sums
   // run in the same order whatever M is (a row's result does not depend on the batch).
   int row_invariant = 0;
+  // The model's weights exceed the last-level cache: decode GEMMs of one row block load them
+  // with the nontemporal hint.
+  int stream_w = 0;
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.

@@ -183,8 +183,9 @@ constexpr int skinny_unroll() {
 }
 
 // XS: two-term X (each row K hi terms, then K lo terms): every weight chunk loaded once feeds
-// the MFMAs of both terms.
-template <typename T, Ep E, int NMB, int TPW, bool XS>
+// the MFMAs of both terms. NT: weight loads with the nontemporal hint (launches of one row
+// block whose weights stream once per step from a set larger than the last-level cache).
+template <typename T, Ep E, int NMB, int TPW, bool XS, bool NT = false>
 __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__ X, int64_t ldx,
                                                            const T* __restrict__ W, int M, int N, int K,
                                                            EpArgs a) {
@@ -240,8 +241,8 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
       if (c < nch) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          wa[u][t][0] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + c * 1024);
-          wa[u][t][1] = *reinterpret_cast<const uint4*>(wp + (int64_t)t * 16 * K + c * 1024 + 512);
+          wa[u][t][0] = ld16<NT>(wp + (int64_t)t * 16 * K + c * 1024);
+          wa[u][t][1] = ld16<NT>(wp + (int64_t)t * 16 * K + c * 1024 + 512);
         }
 #pragma unroll
         for (int j = 0; j < NMB; ++j) {
@@ -698,7 +699,7 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     // workgroup's bytes (TPW weight tiles + the X rows it reads) at the per-CU rate.
     const dim3 blk(kSkW * WAVE);
     const int64_t xs = a.x_split ? 2 : 1, e = sizeof(T);
-    static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}, {4, 4}};
+    static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
     int best_t = 1, best_n = 1;
     int64_t best_cost = -1;
     int ov_t = 0, ov_n = 0;
@@ -706,7 +707,6 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     for (const auto& c : cand) {
       const int tpw = c[0], nmb = c[1];
       if (tpw > 1 && N % (16 * tpw) != 0) continue;   // one tile per workgroup covers a ragged N
-      if (tpw * nmb > 8) continue;                     // 4 x 4 only on request
       const int64_t wgs = (int64_t)((N + 16 * tpw - 1) / (16 * tpw)) * ((M + 16 * nmb - 1) / (16 * nmb));
       const int64_t rows = std::min(16 * nmb, M);
       const int64_t bytes = (int64_t)tpw * 16 * K * e + rows * K * e * xs;
@@ -717,19 +717,24 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
         best_n = nmb;
       }
     }
-    if (ov_t && (ov_t == 1 || N % (16 * ov_t) == 0)) {
+    if (ov_t && ov_t * ov_n <= 8 && (ov_t == 1 || N % (16 * ov_t) == 0)) {
       best_t = ov_t;
       best_n = ov_n;
     }
     const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n));
+    // nontemporal weight loads only when no other row block of this launch reads the same
+    // tiles (measured at the paper shape: B 1 5.52 -> 5.20 ms per step; at B 64, with two row
+    // blocks, the hint made the second read miss the cache: 4% slower)
+    const bool nt = a.stream_w && grid.y == 1 && a.x_split;
 #define RLT_SKINNY(NMB_, TPW_)                                                                                   \
   if (best_n == NMB_ && best_t == TPW_) {                                                                        \
-    if (a.x_split) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+    if (nt) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+    else if (a.x_split) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
     else hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, false>), grid, blk, 0, st, x, ldx, w, M, N, K, a);   \
     return;                                                                                                      \
   }
     RLT_SKINNY(1, 1) RLT_SKINNY(2, 1) RLT_SKINNY(4, 1) RLT_SKINNY(1, 2) RLT_SKINNY(2, 2) RLT_SKINNY(4, 2)
-    RLT_SKINNY(1, 4) RLT_SKINNY(2, 4) RLT_SKINNY(4, 4)
+    RLT_SKINNY(1, 4) RLT_SKINNY(2, 4)
 #undef RLT_SKINNY
   } else if (large_gemm_enabled() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);

@@ -464,6 +464,7 @@ void timed(rlt_model* m, int kind, hipStream_t st, F&& launch) {
 void mgemm(rlt_model* m, int kind, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
            int K, hipStream_t st) {
   a.row_invariant = m->batch_invariant;
+  a.stream_w = (int64_t)m->arena_bytes > kStreamBytes;
   timed(m, kind, st, [&] { gemm(dt, ep, a, X, ldx, W, M, N, K, st); });
 }
 
