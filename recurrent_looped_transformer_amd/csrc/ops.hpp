@@ -105,10 +105,20 @@ struct EpArgs {
   // The model's weights exceed the last-level cache: decode GEMMs of one row block load them
   // with the nontemporal hint.
   int stream_w = 0;
+  // Split-K workspace of the decode GEMM (one launch at a time per workspace): the partial
+  // 16x16 tiles of every K split ([split][row block][tile group][tile][lane] f32x4). Without
+  // it (kpart null) every launch runs unsplit.
+  float* kpart = nullptr;
+  int64_t kpart_n = 0;        // floats
+  // Decode tile shape forced by the caller (TPW, NMB, K splits; TPW 0: the cost model's choice),
+  // taken where the shape admits it.
+  int tile_ov[3] = {0, 0, 1};
 };
 
 // Largest row count the decode GEMM takes; folded RMSNorm is available up to it.
 constexpr int kSkinnyMaxRows = 512;
+// Most K splits of a decode GEMM.
+constexpr int kMaxKSplit = 4;
 
 // GEMM: Y[m, n] = sum_k X[m, k] * W[n, k]  (X act rows with leading dim ldx; W packed [N, K]:
 // tile-major for bf16, row-major for fp32), Y consumed by the epilogue. bf16: MFMA; fp32:

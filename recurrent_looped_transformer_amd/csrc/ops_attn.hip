@@ -196,17 +196,21 @@ __global__ __launch_bounds__(DH) void attn_combine_k(AttnArgs a, int S) {
 // so a long prefix gets more blocks than a short one), one round of at most 256 blocks in
 // all; the pieces are combined by attn_combine_k. Measured on the medium-LM decode (16
 // heads, dh 128, t 2048): 8 rows split 16 ways ran 6.7 us slower per launch than unsplit (the
-// extra launch and per-block overheads outweigh the occupancy), so only launches of one or
-// two rows split.
-constexpr int kSplitMinKeys = 1024, kSplitMaxBlocks = 32, kSplitPiece = 256, kSplitRound = 256;
+// extra launch and per-block overheads outweigh the occupancy), so launches of more than
+// kSplitMaxBlocks blocks split only into pieces of at least kSplitLongPiece keys, when they
+// would otherwise leave CUs idle (paper shape, 32 heads, t 8192: 2 rows unsplit streamed the
+// memory at 2.9 TB/s on 64 blocks, 4 rows at 5.0 TB/s on 128).
+constexpr int kSplitMinKeys = 1024, kSplitMaxBlocks = 32, kSplitPiece = 256, kSplitRound = 256,
+              kSplitLongPiece = 2048;
 static_assert(kSplitRound <= kAttnSplitBlocks, "split workspace");
 template <typename T, int DH>
 static void launch_attn(const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
   const int blocks = a.H * a.B * a.nq;
   int S = 1;
-  if (a.split_ws && a.n_max >= kSplitMinKeys && blocks <= kSplitMaxBlocks) {
+  if (a.split_ws && a.n_max >= kSplitMinKeys && blocks < kSplitRound) {
     S = std::min({(a.n_max + kSplitPiece - 1) / kSplitPiece, kSplitRound / blocks, a.split_max});
+    if (blocks > kSplitMaxBlocks) S = std::min(S, a.n_max / kSplitLongPiece);
     S = std::max(S, 1);
     a.split_keys = (a.n_max + S - 1) / S;
     S = (a.n_max + a.split_keys - 1) / a.split_keys;
@@ -267,6 +271,8 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 // exactly the B operand layout of the 16x16x16 MFMA used for O^T += V^T P^T, so
 // probabilities never leave registers; each K or V^T fragment read from LDS feeds the four
 // query blocks of the wave. Softmax statistics are fp32 per query, online over key tiles.
+// (Pairing two 16-key sub-tiles into one 16x16x32 product per 32 keys measured 5% slower
+// at the paper-shape encode: the operands have to be gathered into adjacent registers.)
 namespace rlt {
 
 // QB query blocks of 16 per wave: up to 4 (2 for bf16 at dh 128: register budget); short

@@ -175,6 +175,15 @@ __device__ __forceinline__ float epilogue(const EpArgs& a, int m, int n, float v
 // weight slice is in flight at once for K up to kSkW * U * 64; every activation fragment a
 // wave loads feeds the TPW weight tiles (fewer re-reads of X when N is large). Partial tiles
 // meet in LDS. A row's sums run in the same order for every TPW, NMB and M.
+//
+// K split (gridDim.z = S > 1): workgroup z takes the z-th run of K / 64 / S chunks and stores
+// its reduced tiles, unscaled, to the split-K workspace; skinny_reduce then adds the S partial
+// tiles of every output tile in split order 0 .. S-1 and runs the row scale and epilogue.
+// With many rows every workgroup reads all of them for its K range, so cutting K cuts the
+// activation bytes each workgroup reads per weight byte (at 64 two-term rows, 128 activation
+// rows per weight tile). (One kernel whose last-arriving workgroup finished the tiles, after
+// a device-scope release of its partials, measured 3x slower at the paper shape: each
+// release writes back the L2 of its XCD.)
 constexpr int kSkW = 8;
 
 template <int TPW, int NMB>
@@ -182,10 +191,61 @@ constexpr int skinny_unroll() {
   return TPW + NMB <= 2 ? 8 : (TPW + NMB <= 4 ? 4 : (TPW + NMB <= 6 ? 2 : 1));
 }
 
+// Row scales of the folded RMSNorm (consumer side) of rows m0 .. m0 + 16 NMB - 1 into rsl:
+// wave w reduces rows w, w + kSkW, ... from the float4 partial sums ssr it loaded.
+template <int NMB>
+__device__ __forceinline__ void skinny_scales(const EpArgs& a, const float4* ssr, float* rsl, int wave, int lane) {
+  constexpr int RPW = NMB * 16 / kSkW;
+  const float live = lane * 4 < a.rs_n ? 1.f : 0.f;
+  float tt[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) tt[i] = wave_sum_dpp((ssr[i].x + ssr[i].y + ssr[i].z + ssr[i].w) * live);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) rsl[wave + kSkW * i] = rsqrtf(tt[i] / (float)a.rs_d + a.rs_eps);
+  }
+}
+template <int NMB>
+__device__ __forceinline__ void skinny_scale_loads(const EpArgs& a, float4* ssr, int m0, int M, int wave, int lane) {
+  constexpr int RPW = NMB * 16 / kSkW;
+  const int k4 = min(lane * 4, a.rs_n - 4);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int m = min(m0 + wave + kSkW * i, M - 1);
+    ssr[i] = *reinterpret_cast<const float4*>(a.rs_ssp + (int64_t)m * a.rs_n + k4);
+  }
+}
+
+// Epilogue of output tile o = t * NMB + j of a skinny workgroup (tiles tile0.., rows m0..):
+// lane (r, g) holds rows m0 + 16 j + r, features (tile0 + t) * 16 + 4 g .. + 3.
+template <typename T, Ep E, int NMB>
+__device__ __forceinline__ void skinny_finish(const EpArgs& a, int M, int N, int tile0, int m0, int r, int g,
+                                              const float* rsl, int o, f32x4 sum, const EpPre* pp) {
+  const int t = o / NMB, j = o % NMB;
+  const int m = m0 + j * 16 + r;
+  const int n = (tile0 + t) * 16 + 4 * g;
+  const float sc = a.rs_ssp ? rsl[j * 16 + r] : 1.f;
+  float ss = 0.f;
+  if (m < M && n < N) {
+    float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
+    ss = epilogue<T, E, true>(a, m, n, v, pp);
+  }
+  if constexpr (E == Ep::Residual || E == Ep::Merge) {
+    if (a.fold_zb) {
+      // lanes r, r+16, r+32, r+48 hold the tile's features of row m (16, or 8 for Merge)
+      ss += __shfl_xor(ss, 16, WAVE);
+      ss += __shfl_xor(ss, 32, WAVE);
+      if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + tile0 + t] = ss;
+    }
+  }
+}
+
 // XS: two-term X (each row K hi terms, then K lo terms): every weight chunk loaded once feeds
 // the MFMAs of both terms. NT: weight loads with the nontemporal hint (launches of one row
 // block whose weights stream once per step from a set larger than the last-level cache).
-template <typename T, Ep E, int NMB, int TPW, bool XS, bool NT = false>
+// KS: a K-split launch (its own instances: the unsplit ones keep compile-time chunk bounds,
+// measured 10% faster at one row than with the split bounds read from the grid).
+template <typename T, Ep E, int NMB, int TPW, bool XS, bool NT = false, bool KS = false>
 __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__ X, int64_t ldx,
                                                            const T* __restrict__ W, int M, int N, int K,
                                                            EpArgs a) {
@@ -204,21 +264,16 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
   // folded RMSNorm of the input rows: fetch the partial sums now (one float4 per lane and
   // row, no branches: rs_n is a multiple of 4), reduce after the main loop
   // (the loaded values stay untouched until then, so no wait is placed before the weight loads)
+  // (a split launch stores unscaled partial tiles: the scales belong to skinny_reduce)
+  const int ks = KS ? gridDim.z : 1;
   float4 ssr[RPW];
-  if (a.rs_ssp) {
-    const int k4 = min(lane * 4, a.rs_n - 4);
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int m = min(m0 + wave + kSkW * i, M - 1);
-      ssr[i] = *reinterpret_cast<const float4*>(a.rs_ssp + (int64_t)m * a.rs_n + k4);
-    }
-  }
+  if (a.rs_ssp && ks == 1) skinny_scale_loads<NMB>(a, ssr, m0, M, wave, lane);
 
   // the epilogue waves' operands (residual row, gain, rotary factors) are requested first;
   // in reduction pass p, wave w < NOB finishes output tile o = p NOB + w, (t, j) = (o / NMB,
   // o % NMB); the first pass's operands are prefetched
   EpPre pre{};
-  if (wave < NOB) {
+  if (wave < NOB && ks == 1) {
     const int em = m0 + (wave % NMB) * 16 + r, en = (tile0 + wave / NMB) * 16 + 4 * g;
     if (em < M && en < N) pre = ep_prefetch<E, true>(a, em, en);
   }
@@ -233,12 +288,14 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     for (int j = 0; j < NMB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // two-term X: the lo terms of chunk c lie at chunk c + nch of the row
   const int nch = K / 64;
-  for (int c0 = wave; c0 < nch; c0 += kSkW * U) {
+  const int cpk = KS ? nch / ks : nch;            // chunks per K split
+  const int cb = KS ? blockIdx.z * cpk : 0, ce = KS ? cb + cpk : nch;
+  for (int c0 = cb + wave; c0 < ce; c0 += kSkW * U) {
     uint4 wa[U][TPW][2], xb[U][NMB][2], xl[XS ? U : 1][NMB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kSkW;
-      if (c < nch) {
+      if (c < ce) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           wa[u][t][0] = ld16<NT>(wp + (int64_t)t * 16 * K + c * 1024);
@@ -257,7 +314,7 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + u * kSkW < nch) {
+      if (c0 + u * kSkW < ce) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -272,16 +329,11 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
       }
     }
   }
-  if (a.rs_ssp) {
-    const float live = lane * 4 < a.rs_n ? 1.f : 0.f;
-    float tt[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) tt[i] = wave_sum_dpp((ssr[i].x + ssr[i].y + ssr[i].z + ssr[i].w) * live);
-    if (lane == 0) {
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) rsl[wave + kSkW * i] = rsqrtf(tt[i] / (float)a.rs_d + a.rs_eps);
-    }
-  }
+  if (a.rs_ssp && ks == 1) skinny_scales<NMB>(a, ssr, rsl, wave, lane);
+  // partial tile o of split z of this workgroup's (row block, tile group), one f32x4 per lane
+  const int64_t grp = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t zstride = (int64_t)gridDim.y * gridDim.x * NO * WAVE;
+  f32x4* part = reinterpret_cast<f32x4*>(a.kpart) + grp * NO * WAVE + lane;
 #pragma unroll
   for (int p = 0; p < NO / NOB; ++p) {
     if (p > 0) __syncthreads();   // the previous pass has read red
@@ -293,27 +345,39 @@ __global__ __launch_bounds__(kSkW * WAVE) void gemm_skinny(const T* __restrict__
     __syncthreads();
     if (wave < NOB) {
       const int o = p * NOB + wave;
-      const int t = o / NMB, j = o % NMB;
       f32x4 sum = red[0][wave][lane];
 #pragma unroll
       for (int w = 1; w < kSkW; ++w) sum += red[w][wave][lane];
-      const int m = m0 + j * 16 + r;
-      const int n = (tile0 + t) * 16 + 4 * g;
-      const float sc = a.rs_ssp ? rsl[j * 16 + r] : 1.f;
-      float ss = 0.f;
-      if (m < M && n < N) {
-        float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
-        ss = epilogue<T, E, true>(a, m, n, v, p == 0 ? &pre : nullptr);
-      }
-      if constexpr (E == Ep::Residual || E == Ep::Merge) {
-        if (a.fold_zb) {
-          // lanes r, r+16, r+32, r+48 hold the tile's features of row m (16, or 8 for Merge)
-          ss += __shfl_xor(ss, 16, WAVE);
-          ss += __shfl_xor(ss, 32, WAVE);
-          if (g == 0 && m < M) a.fold_ssp[(int64_t)m * (N / 16) + tile0 + t] = ss;
-        }
-      }
+      if (ks > 1) part[blockIdx.z * zstride + (int64_t)o * WAVE] = sum;
+      else skinny_finish<T, E, NMB>(a, M, N, tile0, m0, r, g, rsl, o, sum, p == 0 ? &pre : nullptr);
     }
+  }
+}
+
+// Second kernel of a split launch (same grid x, y and block as gemm_skinny): adds the ks
+// partial tiles of each output tile in split order and runs the row scale and epilogue.
+template <typename T, Ep E, int NMB, int TPW>
+__global__ __launch_bounds__(kSkW * WAVE) void skinny_reduce(int M, int N, int ks, EpArgs a) {
+  constexpr int NO = TPW * NMB;
+  constexpr int RPW = NMB * 16 / kSkW;
+  __shared__ float rsl[NMB * 16];
+  const int tile0 = blockIdx.x * TPW;
+  const int m0 = blockIdx.y * (NMB * 16);
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  if (a.rs_ssp) {
+    float4 ssr[RPW];
+    skinny_scale_loads<NMB>(a, ssr, m0, M, wave, lane);
+    skinny_scales<NMB>(a, ssr, rsl, wave, lane);
+    __syncthreads();
+  }
+  const int64_t grp = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t zstride = (int64_t)gridDim.y * gridDim.x * NO * WAVE;
+  const f32x4* part = reinterpret_cast<const f32x4*>(a.kpart) + grp * NO * WAVE + lane;
+  for (int o = wave; o < NO; o += kSkW) {
+    f32x4 sum = part[(int64_t)o * WAVE];
+    for (int z = 1; z < ks; ++z) sum += part[z * zstride + (int64_t)o * WAVE];
+    skinny_finish<T, E, NMB>(a, M, N, tile0, m0, r, g, rsl, o, sum, nullptr);
   }
 }
 
@@ -668,19 +732,6 @@ static bool large_gemm_enabled() {
   return state == 1;
 }
 
-// RLT_SKINNY_TILE=<TPW>x<NMB> (one of the candidates below) makes every decode GEMM whose N
-// admits it take that tile shape instead of the cost model's choice (tile measurements).
-static void skinny_override(int& tpw, int& nmb) {
-  static const int v = [] {
-    const char* env = getenv("RLT_SKINNY_TILE");
-    int t = 0, n = 0;
-    if (env && sscanf(env, "%dx%d", &t, &n) == 2) return t * 16 + n;
-    return 0;
-  }();
-  tpw = v / 16;
-  nmb = v % 16;
-}
-
 template <typename T, Ep E>
 static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W, int M, int N, int K,
                      hipStream_t st) {
@@ -693,42 +744,67 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
     const int nt = mid_tiles;
     hipLaunchKernelGGL((gemm_mid<T, E>), dim3(nt), dim3(256), 0, st, x, ldx, w, M, N, K, a);
   } else if (M <= kSkinnyMaxRows || a.fold_zb || a.rs_ssp || a.row_invariant) {
-    // Tiles per workgroup (TPW) and row blocks (NMB) from a cost model fitted to MI355X
-    // measurements of this kernel: one workgroup per CU at a time, each round of up to 256
-    // workgroups costs a memory latency (~70 KB of per-CU transfer time) plus its
-    // workgroup's bytes (TPW weight tiles + the X rows it reads) at the per-CU rate.
+    // Tiles per workgroup (TPW), row blocks (NMB) and K splits (S) from a cost model fitted to
+    // MI355X measurements of this kernel: one workgroup per CU at a time, each round of up to
+    // 256 workgroups costs a memory latency (~70 KB of per-CU transfer time) plus its
+    // workgroup's bytes (TPW weight tiles + the X rows it reads, over its K range) at the
+    // per-CU rate.
     const dim3 blk(kSkW * WAVE);
     const int64_t xs = a.x_split ? 2 : 1, e = sizeof(T);
+    const int nch = K / 64;
+    // (4 x 4 tiles measured slower than 4 x 2 with two row blocks at 64 two-term rows: four
+    // reduction passes and 160 registers)
     static const int cand[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {2, 2}, {2, 4}, {4, 1}, {4, 2}};
-    int best_t = 1, best_n = 1;
+    int best_t = 1, best_n = 1, best_s = 1;
     int64_t best_cost = -1;
-    int ov_t = 0, ov_n = 0;
-    skinny_override(ov_t, ov_n);
+    auto fits = [&](int tpw, int nmb, int ks) {
+      if (tpw > 1 && N % (16 * tpw) != 0) return false;   // one tile per workgroup covers a ragged N
+      if (ks == 1) return true;
+      // split launches: row-invariant arithmetic keeps one K order; every split gets a chunk per wave
+      if (a.row_invariant || !a.kpart || nch % ks != 0 || nch / ks < kSkW) return false;
+      const int64_t gx = (N + 16 * tpw - 1) / (16 * tpw), gy = (M + 16 * nmb - 1) / (16 * nmb);
+      return (int64_t)ks * gy * gx * tpw * nmb * 256 <= a.kpart_n;
+    };
     for (const auto& c : cand) {
       const int tpw = c[0], nmb = c[1];
-      if (tpw > 1 && N % (16 * tpw) != 0) continue;   // one tile per workgroup covers a ragged N
-      const int64_t wgs = (int64_t)((N + 16 * tpw - 1) / (16 * tpw)) * ((M + 16 * nmb - 1) / (16 * nmb));
-      const int64_t rows = std::min(16 * nmb, M);
-      const int64_t bytes = (int64_t)tpw * 16 * K * e + rows * K * e * xs;
-      const int64_t cost = ((wgs + 255) / 256) * (70 * 1024 + bytes);
-      if (best_cost < 0 || cost < best_cost) {
-        best_cost = cost;
-        best_t = tpw;
-        best_n = nmb;
+      for (int ks = 1; ks <= kMaxKSplit; ks *= 2) {
+        if (!fits(tpw, nmb, ks)) continue;
+        const int64_t wgs = (int64_t)((N + 16 * tpw - 1) / (16 * tpw)) * ((M + 16 * nmb - 1) / (16 * nmb)) * ks;
+        const int64_t rows = std::min(16 * nmb, M);
+        const int64_t bytes = ((int64_t)tpw * 16 * K * e + rows * K * e * xs) / ks;
+        int64_t cost = ((wgs + 255) / 256) * (70 * 1024 + bytes);
+        // a split launch adds the reduce kernel: a dependent launch and its memory latency, and
+        // the partial tiles written and read back
+        if (ks > 1) cost += 2 * 70 * 1024 + (int64_t)(ks + 1) * tpw * nmb * 1024;
+        if (best_cost < 0 || cost < best_cost) {
+          best_cost = cost;
+          best_t = tpw;
+          best_n = nmb;
+          best_s = ks;
+        }
       }
     }
-    if (ov_t && ov_t * ov_n <= 8 && (ov_t == 1 || N % (16 * ov_t) == 0)) {
+    const int ov_t = a.tile_ov[0], ov_n = a.tile_ov[1], ov_s = a.tile_ov[2];
+    bool ov_ok = false;   // only the compiled tile shapes
+    for (const auto& c : cand) ov_ok = ov_ok || (c[0] == ov_t && c[1] == ov_n);
+    if (ov_ok && ov_s >= 1 && ov_s <= kMaxKSplit && fits(ov_t, ov_n, ov_s)) {
       best_t = ov_t;
       best_n = ov_n;
+      best_s = ov_s;
     }
-    const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n));
+    const dim3 grid((N + 16 * best_t - 1) / (16 * best_t), (M + 16 * best_n - 1) / (16 * best_n), best_s);
     // nontemporal weight loads only when no other row block of this launch reads the same
     // tiles (measured at the paper shape: B 1 5.52 -> 5.20 ms per step; at B 64, with two row
     // blocks, the hint made the second read miss the cache: 4% slower)
     const bool nt = a.stream_w && grid.y == 1 && a.x_split;
 #define RLT_SKINNY(NMB_, TPW_)                                                                                   \
   if (best_n == NMB_ && best_t == TPW_) {                                                                        \
-    if (nt) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+    if (best_s > 1) {                                                                                            \
+      if (nt) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true, true, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+      else if (a.x_split) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true, false, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+      else hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, false, false, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
+      hipLaunchKernelGGL((skinny_reduce<T, E, NMB_, TPW_>), dim3(grid.x, grid.y), blk, 0, st, M, N, best_s, a);  \
+    } else if (nt) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
     else if (a.x_split) hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, true>), grid, blk, 0, st, x, ldx, w, M, N, K, a); \
     else hipLaunchKernelGGL((gemm_skinny<T, E, NMB_, TPW_, false>), grid, blk, 0, st, x, ldx, w, M, N, K, a);   \
     return;                                                                                                      \

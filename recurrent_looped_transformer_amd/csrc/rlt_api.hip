@@ -8,6 +8,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <stdexcept>
@@ -98,6 +100,7 @@ struct rlt_model {
   uint64_t wdigest = 0;   // digest of the packed parameter values (identifies a snapshot's weights)
   int scan_mode = 0;
   int batch_invariant = 0;   // every kernel's per-row arithmetic independent of batch and pass shape
+  int tile_ov[3] = {0, 0, 1};   // decode GEMM tile override (TPW, NMB, K splits) from RLT_SKINNY_TILE
   int n_states = 0;
   // kernel timers (measurement): launches of each kind bracketed by events on their stream
   bool timing = false;
@@ -169,6 +172,8 @@ struct rlt_state {
   int32_t* rtok = nullptr;            // [B] tokens of the rows that move
   float* s_bak = nullptr;             // [B][d] s before a per-row step
   float* attn_ws = nullptr;           // [kMaxSlices][kAttnSplitBlocks][dh + 2] key-split partials
+  float* kpart = nullptr;             // [kMaxSlices][kpart_slice] split-K partial tiles of decode GEMMs
+  int64_t kpart_slice = 0;
   void* samp_ws = nullptr;            // chunk statistics of the generation sampler
   int* rp_host = nullptr;             // pinned [kStage][3][B] staging of rp_dev
   hipEvent_t rp_ev[kStage] = {};
@@ -461,9 +466,17 @@ void timed(rlt_model* m, int kind, hipStream_t st, F&& launch) {
   m->timed[kind].push_back({ev[0], ev[1]});
 }
 
-void mgemm(rlt_model* m, int kind, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx, const void* W, int M, int N,
-           int K, hipStream_t st) {
+// slice: the concurrent batch slice the launch belongs to (its own split-K workspace)
+void mgemm(rlt_model* m, rlt_state* s, int slice, int kind, Dt dt, Ep ep, EpArgs a, const void* X, int64_t ldx,
+           const void* W, int M, int N, int K, hipStream_t st) {
   a.row_invariant = m->batch_invariant;
+  a.tile_ov[0] = m->tile_ov[0];
+  a.tile_ov[1] = m->tile_ov[1];
+  a.tile_ov[2] = m->tile_ov[2];
+  if (s->kpart) {
+    a.kpart = s->kpart + (int64_t)slice * s->kpart_slice;
+    a.kpart_n = s->kpart_slice;
+  }
   a.stream_w = (int64_t)m->arena_bytes > kStreamBytes;
   timed(m, kind, st, [&] { gemm(dt, ep, a, X, ldx, W, M, N, K, st); });
 }
@@ -512,7 +525,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         at.k = s->ekv_k; at.v = s->ekv_v; at.kv_bstride = (int64_t)H * T * dh; at.cap = T; at.kv_lo = s->ekv_lo;
       }
       a.kv.ring = 0;
-      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
+      mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::QKV, a, s->exa, ad, L.wqkv, rows, 3 * hd, d, st);
       at.q = s->eq; at.ldq = ahd; at.q_lo = shd; at.ring = 0; at.out = s->eao; at.ldo = ahd; at.out_split = shd;
       at.B = nb; at.nq = T; at.H = H; at.dh = dh; at.pos0 = t0; at.window = 0;
       at.scale = 1.f / std::sqrt((float)dh);
@@ -521,11 +534,11 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         if (!(T >= 16 && !m->batch_invariant && attn_prefill(dt, at, st))) attn_decode(dt, at, st);
       });
       EpArgs r; r.resid = h; r.rmap = hm; r.x_split = A > 1;
-      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
+      mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->eao, ahd, L.wo, rows, d, hd, st);
       rmsnorm(dt, h, hm, L.n2, s->exa, ad, rows, d, c.rms_eps, st, sd);
       EpArgs sw; sw.out = s->ehid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
-      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
+      mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::SwiGLU, sw, s->exa, ad, L.w13, rows, 2 * f, d, st);
+      mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::Residual, r, s->ehid, af, L.w2, rows, d, f, st);
     }
     if (c.L_D > 0) {
       // memory: k^g = RoPE(W^g_K RMSNorm_E(e)), v^g = W^g_V RMSNorm_E(e)  (eq 2.1-2.2)
@@ -536,7 +549,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
         const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
         a.kv.k = (char*)s->mem_k + go; a.kv.v = (char*)s->mem_v + go; a.kv.cap = Tm; a.kv.ring = 0;
         a.x_split = A > 1;
-        mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
+        mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::MemKV, a, s->exa, ad, m->wkv[g], rows, 2 * hd, d, st);
       }
     }
     if (c.variant != RLT_V0) {
@@ -544,7 +557,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       rmsnorm(dt, h, hm, nullptr, s->exa, ad, rows, d, 0.f, st, sd);
       EpArgs a; a.resid = s->gpre + ((int64_t)b0 * Tm + t0) * d; a.rmap = hm; a.bias = m->bg;
       a.x_split = A > 1;
-      mgemm(m, RLT_TIME_ENCODER_GEMM, dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
+      mgemm(m, s, 0, RLT_TIME_ENCODER_GEMM, dt, Ep::Bias, a, s->exa, ad, m->wg_e, rows, d, d, st);
     }
   }
   check_launch();
@@ -633,7 +646,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     if (merge_fold) {
       a.fold_zb = sb.xa; a.fold_ld = ad; a.out_split = sd; a.fold_ssp = sb.dssp; a.fold_gain = m->dec[0].n1;
     }
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::Merge, a, sb.xs, ad, m->wsr, B, 2 * d, d, st);
   }
   const float scale = 1.f / std::sqrt((float)dh);
   auto norm_in = [&](EpArgs& a, const float* gain) {
@@ -660,7 +673,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     a.x_split = A > 1; a.pos_dev = pos_dev; a.row_pos = rp;
     const int64_t ro = (int64_t)l * s->B * H * s->R * dh * m->esz;   // layer stride spans every sequence
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
@@ -680,13 +693,13 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     });
     EpArgs r; r.resid = sb.z; r.rmap = zm; r.x_split = A > 1;
     fold_out(r, L.n2);
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r, sb.ao, ahd, L.wo, rows, d, hd, st);
     // cross-attention to the prefix memory M_<=t of this layer's group
     EpArgs qx;
     norm_in(qx, L.n2);
     qx.out = sb.q; qx.ldo = hd; qx.rope = s->rope; qx.dh = dh; qx.tn = np; qx.pos0 = t0; qx.x_split = A > 1;
     qx.pos_dev = pos_dev; qx.row_pos = rp;
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::RopeQ, qx, sb.xa, ad, L.xq, rows, hd, d, st);
     const int g = c.groups == 1 ? 0 : l;
     const int64_t go = (int64_t)g * s->B * H * Tm * dh * m->esz;
     at.k = (char*)sb.mem_k + go; at.v = (char*)sb.mem_v + go; at.kv_bstride = (int64_t)H * Tm * dh;
@@ -700,12 +713,12 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     });
     EpArgs r2; r2.resid = sb.z; r2.rmap = zm; r2.x_split = A > 1;
     fold_out(r2, L.n3);
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r2, sb.ao, ahd, L.xo, rows, d, hd, st);
     // SwiGLU FFN
     EpArgs sw;
     norm_in(sw, L.n3);
     sw.out = sb.hid; sw.ldo = af; sw.out_split = sf; sw.x_split = A > 1;
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::SwiGLU, sw, sb.xa, ad, L.w13, rows, 2 * f, d, st);
     EpArgs r3; r3.resid = sb.z; r3.rmap = zm; r3.x_split = A > 1;
     fold_out(r3, l + 1 < c.L_D ? m->dec[l + 1].n1 : nullptr);
     if (l + 1 == c.L_D) {
@@ -717,7 +730,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
         r3.fold_zb = sb.xs; r3.fold_ld = ad; r3.out_split = sd; r3.fold_ssp = sb.sssp; r3.fold_gain = m->ns;
       }
     }
-    mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
+    mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::Residual, r3, sb.hid, af, L.w2, rows, d, f, st);
   }
   if (c.L_D == 0) {
     // s_t = the last position's output of every sequence
@@ -743,7 +756,7 @@ struct ScanOut {
 // Readout of buffered positions c0 .. c0+n-1 (scan-relative) of sequences b0 .. b0+nb-1, held in
 // sbuf [B][kReadoutPositions][d] (or at src with sequence stride src_sb).
 void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStream_t st, int b0, int nb,
-             const float* src = nullptr, int64_t src_sb = 0) {
+             const float* src = nullptr, int64_t src_sb = 0, int slice = 0) {
   const rlt_config& c = m->cfg;
   const Dt dt = m->dt;
   const int d = c.d, V = c.vocab;
@@ -760,7 +773,7 @@ void readout(rlt_model* m, rlt_state* s, int c0, int n, const ScanOut& o, hipStr
   if (!o.logits && !o.lp) return;
   rmsnorm(dt, src, sm, m->nO, xr, A * d, rows, d, c.rms_eps, st, A > 1 ? d : 0);
   EpArgs a; a.out = lbuf; a.ldo = V; a.x_split = A > 1;
-  mgemm(m, RLT_TIME_DECODER_GEMM, dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
+  mgemm(m, s, slice, RLT_TIME_DECODER_GEMM, dt, Ep::StoreF32, a, xr, A * d, m->wout, rows, V, d, st);
   if (o.logits) {
     RowMap dm; dm.tn = n; dm.sb = o.ld_b * V; dm.st = V;
     copy_rows(lbuf, contiguous(V), o.logits + ((int64_t)b0 * o.ld_b + c0) * V, dm, rows, V, st);
@@ -947,7 +960,7 @@ void do_scan(rlt_model* m, rlt_state* s, int T, const ScanOut& o, hipStream_t st
   int done = 0;
   auto flush = [&] {
     if (buffered > 0)
-      for (int k = 0; k < ns; ++k) readout(m, s, c0, buffered, o, ss[k], sl[k].b0, sl[k].B);
+      for (int k = 0; k < ns; ++k) readout(m, s, c0, buffered, o, ss[k], sl[k].b0, sl[k].B, nullptr, 0, k);
     c0 += buffered;
     buffered = 0;
   };
@@ -1157,6 +1170,16 @@ int rlt_create(const rlt_config* cfg, const rlt_tensor* weights, int n_weights, 
       m->act = cfg->dtype == RLT_FP16X2 ? 2 : 1;
       m->esz = cfg->dtype == RLT_FP32 ? 4 : 2;
       m->hd = cfg->n_heads * cfg->d_head;
+      // RLT_SKINNY_TILE=<TPW>x<NMB>[x<S>]: every decode GEMM of this model whose shape admits it
+      // takes that tile shape and K split count instead of the cost model's (tile measurements)
+      if (const char* env = getenv("RLT_SKINNY_TILE")) {
+        int t = 0, n = 0, z = 1;
+        if (sscanf(env, "%dx%dx%d", &t, &n, &z) >= 2) {
+          m->tile_ov[0] = t;
+          m->tile_ov[1] = n;
+          m->tile_ov[2] = z;
+        }
+      }
       size_t total = 0;
       layout_model(m, nullptr, &total);
       if (hipMalloc(&m->arena, total) != hipSuccess) fail(RLT_ERR_OOM, "weight arena allocation failed");
@@ -1304,6 +1327,14 @@ int rlt_state_create(rlt_model* m, int batch, int max_len, int keep_encoder_cach
       s->rtok = (int32_t*)dev_alloc(s, sizeof(int32_t) * B, 5);
       s->s_bak = (float*)dev_alloc(s, sizeof(float) * B * d, 5);
       s->attn_ws = (float*)dev_alloc(s, sizeof(float) * kMaxSlices * kAttnSplitBlocks * (dh + 2), 5);
+      if (m->dt != Dt::F32) {
+        // split-K workspace per slice: kMaxKSplit partial copies of the widest decode GEMM output
+        // (rows of a decoder pass or an encoder step, at most 32 MB; wider launches run unsplit)
+        const int64_t kr = (std::min<int64_t>(std::max<int64_t>(rows, B), kSkinnyMaxRows) + 63) / 64 * 64;
+        const int64_t kn = (std::max({3 * hd, 2 * f, 2 * d}) + 63) / 64 * 64;
+        s->kpart_slice = std::min<int64_t>((int64_t)kMaxKSplit * kr * kn, (int64_t)8 << 20);
+        s->kpart = (float*)dev_alloc(s, sizeof(float) * kMaxSlices * s->kpart_slice, 5);
+      }
       s->samp_ws = dev_alloc(s, (size_t)sample_workspace_bytes((int)B, (int)V), 5);
       HIPCHK(hipHostMalloc((void**)&s->rp_host, sizeof(int) * kStage * 3 * B, hipHostMallocDefault));
       for (int k = 0; k < kStage; ++k) HIPCHK(hipEventCreateWithFlags(&s->rp_ev[k], hipEventDisableTiming));
