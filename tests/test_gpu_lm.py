@@ -7,17 +7,17 @@ arithmetic on the GPU path with two-term (hi + lo) fp16 GEMM activation inputs.
 
 - Replay of all 2304 positions at B = 32 in the benchmark's launch configuration,
   checked on sampled outputs against the oracle: rows 0-1 at positions 1-64 and
-  row 0 at positions 1-2052 (tests/golden/medium_lm*.npz, written by
+  row 0 at positions 1-2304 (tests/golden/medium_lm*.npz, written by
   tests/golden/make_golden.py from the oracle alone).
 - Generation: prefill of the 2048-token prompt with the encoder cache kept, then
   256 rlt_step calls, each consuming the stream's next token (teacher forcing:
-  the tokens come from the seeded stream, never from the GPU). Row 0's step logits
-  at positions 2049-2052 are compared with the oracle on every id; every row's
-  step log-probs and argmax with the full-size replay (serving-split invariance).
+  the tokens come from the seeded stream, never from the GPU). Row 0's prefill and step
+  logits at positions 2045-2304 are compared with the oracle; every row's step log-probs
+  and argmax with the full-size replay (serving-split invariance).
 
-The stored oracle logits are the first 64 ids at every position, every id at the
-last 8 positions, and the 8 largest per position (the oracle's argmax is the first of
-them). Bar: max abs logit error <= 2e-2 and the GPU's argmax identical to the oracle's
+The stored oracle logits are the first 64 ids at every position, every id at positions
+2045-2052 and 2297-2304, and the 8 largest per position (the oracle's argmax is the first
+of them). Bar: max abs logit error <= 2e-2 and the GPU's argmax identical to the oracle's
 (no tie rule) on >= 99.9% of the compared positions.
 """
 import os
@@ -34,6 +34,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 CFG = CONFIGS["medium_lm"]
 TOL = 2e-2            # 16-bit path vs oracle, max abs logit / log-prob error
 TOL_GPU_GPU = 4e-2    # two 16-bit GPU paths, each within TOL of the oracle
+T_GEN = 2304          # positions of row 0 in the long golden
 
 
 def load(name):
@@ -54,21 +55,35 @@ def raw_argmax(gpu_argmax, top_idx):
 
 
 def compare_rows(tag, lg_rows, lp_rows, s_rows, g):
-    """lg_rows: GPU logits [R, P, V] (cuda), lp_rows [R, P-1] (cuda), s_rows [R, d] vs golden g."""
-    head = lg_rows[:, :, :64].cpu().numpy()
-    tail = lg_rows[:, -8:, :].cpu().numpy()
-    err_h = float(np.max(np.abs(head - g["logits_head"])))
-    err_t = float(np.max(np.abs(tail - g["logits_tail"])))
-    err = max(err_h, err_t)
-    raw = raw_argmax(lg_rows.argmax(-1).cpu().numpy(), g["top8_idx"])
+    """lg_rows: GPU logits [R, P, V] (cuda) of positions 1..P, lp_rows [R, P-1] (cuda), s_rows
+    [R, d] vs golden g of the same rows and positions."""
+    err, raw = compare_at(tag, lg_rows.cpu().numpy(), g, list(range(1, lg_rows.shape[1] + 1)))
     lp_err = float(np.max(np.abs(lp_rows.cpu().numpy() - g["logprob"])))
     s_err = float(np.max(np.abs(s_rows.cpu().numpy() - g["s_last"])))
-    print(f"[parity] {tag}: logits err first-64 ids {err_h:.3e}, last-8 positions all ids {err_t:.3e}; "
-          f"raw argmax agreement {raw:.5f} over {g['top8_idx'][..., 0].size} positions; log-prob err "
-          f"{lp_err:.3e}; s_T err {s_err:.3e}", flush=True)
+    print(f"[parity] {tag}: log-prob err {lp_err:.3e}; s_T err {s_err:.3e}", flush=True)
     assert err <= TOL
     assert raw >= 0.999
     assert lp_err <= TOL
+
+
+def compare_at(tag, lg, g, positions):
+    """lg: GPU logits [R, n, V] (numpy) at the given 1-based positions vs golden g: the first 64
+    ids and the argmax everywhere, every id where g stores them (full_at_pos, the last 8)."""
+    idx = np.asarray(positions) - 1
+    T = g["logits_head"].shape[1]
+    err_h = float(np.max(np.abs(lg[:, :, :64] - g["logits_head"][:, idx])))
+    err_f = 0.0
+    full = list(zip(g["full_at_pos"], np.moveaxis(g["logits_full_at"], 1, 0))) if "full_at_pos" in g else []
+    full += list(zip(range(T - 7, T + 1), np.moveaxis(g["logits_tail"], 1, 0)))
+    n_full = 0
+    for p, ref in full:
+        if int(p) in positions:
+            err_f = max(err_f, float(np.max(np.abs(lg[:, positions.index(int(p))] - ref))))
+            n_full += 1
+    raw = raw_argmax(lg.argmax(-1), g["top8_idx"][:, idx])
+    print(f"[parity] {tag}: logits err first-64 ids {err_h:.3e}, every id at {n_full} stored positions "
+          f"{err_f:.3e}; raw argmax agreement {raw:.5f} over {lg.shape[0] * lg.shape[1]} positions", flush=True)
+    return max(err_h, err_f), raw
 
 
 @pytest.fixture(scope="module")
@@ -78,7 +93,7 @@ def lm():
     tokens = make_tokens(CFG)                          # [32, 2304]
     assert tokens.shape == (CFG.batch, CFG.seq_len + CFG.gen_len)
     assert np.array_equal(tokens[:2, :64], g64["tokens"]), "seeded token stream changed"
-    assert np.array_equal(tokens[:1, :2052], ggen["tokens"]), "seeded token stream changed"
+    assert np.array_equal(tokens[:1, :T_GEN], ggen["tokens"]), "seeded token stream changed"
     P = make_params(CFG)
     assert np.array_equal(param_probe(P), g64["param_probe"]), "seeded parameter draw changed"
     print(f"[case] medium_lm B={tokens.shape[0]} T={tokens.shape[1]}: creating model", flush=True)
@@ -114,7 +129,8 @@ def test_lm_replay_full_size_vs_oracle(lm, replay):
     _, _, g64, ggen = lm
     lg, lp, s = replay["lg"], replay["lp"], replay["s"]
     compare_rows("medium_lm replay rows 0-1 x positions 1-64", lg[:2, :64], lp[:2, :63], s[:2, 63], g64)
-    compare_rows("medium_lm replay row 0 x positions 1-2052", lg[:1, :2052], lp[:1, :2051], s[:1, 2051], ggen)
+    compare_rows("medium_lm replay row 0 x positions 1-2304", lg[:1, :T_GEN], lp[:1, :T_GEN - 1], s[:1, T_GEN - 1],
+                 ggen)
 
 
 def test_lm_replay_entry_point_full_size(lm, replay):
@@ -125,7 +141,7 @@ def test_lm_replay_entry_point_full_size(lm, replay):
     lp2, _ = m.replay(st, torch.as_tensor(tokens).cuda())
     torch.cuda.synchronize()
     d = float((lp2 - replay["lp"][:, :-1]).abs().max())
-    e = float(np.max(np.abs(lp2[:1, :2051].cpu().numpy() - ggen["logprob"])))
+    e = float(np.max(np.abs(lp2[:1, :T_GEN - 1].cpu().numpy() - ggen["logprob"])))
     print(f"[parity] medium_lm rlt_replay vs scan log-probs max diff {d:.3e}; row 0 vs oracle {e:.3e}", flush=True)
     assert d == 0.0
     assert e <= TOL
@@ -148,12 +164,12 @@ def test_lm_generation_steps_full_size(lm, replay):
     lg_step = torch.stack(steps, dim=1)                      # positions p+1 .. T
     assert rlt.rlt_state_positions(st) == (T, T)
 
-    # oracle, every id: prefill positions 2045-2048 and step positions 2049-2052 of row 0
-    tail = torch.cat([lg_pre[:1, p - 4:], lg_step[:1, :4]], dim=1).cpu().numpy()
-    err = float(np.max(np.abs(tail - ggen["logits_tail"])))
-    print(f"[parity] medium_lm row 0 positions 2045-2052 (prefill + rlt_step) vs oracle, every id: "
-          f"max abs err {err:.3e}", flush=True)
+    # oracle, row 0: the last prefill positions 2045-2048 and every step position 2049-2304
+    lg0 = torch.cat([lg_pre[:1, p - 4:], lg_step[:1]], dim=1).cpu().numpy()
+    err, raw = compare_at(f"medium_lm row 0 prefill + rlt_step positions {p - 3}-{T}", lg0, ggen,
+                          list(range(p - 3, T + 1)))
     assert err <= TOL
+    assert raw >= 0.999
 
     # serving-split invariance at full size: step chain vs replay, every row and step
     rep = replay["lg"][:, p:]
@@ -171,11 +187,11 @@ def test_lm_generation_steps_full_size(lm, replay):
 def test_lm_single_row_long_context(lm):
     """Row 0 alone (B = 1: 16 attention blocks per launch, so every memory or window range of
     512 keys or more is cut into 128-key pieces whose partial softmax sums are combined
-    afterwards): replay of positions 1-2052 against the oracle, and prefill 2048 + 4 rlt_step
-    (the encoder-cache attention of the steps is split too) against the oracle at 2045-2052."""
+    afterwards): replay of positions 1-2304 against the oracle, and prefill 2048 + 8 rlt_step
+    (the encoder-cache attention of the steps is split too) against the oracle at 2045-2056."""
     m, tokens, _, ggen = lm
-    T = 2052
-    print("[case] medium_lm B=1 T=2052 (key-split attention)", flush=True)
+    T = T_GEN
+    print(f"[case] medium_lm B=1 T={T} (key-split attention)", flush=True)
     x = torch.as_tensor(np.ascontiguousarray(tokens[:1, :T])).cuda()
     st = m.state(1, T, keep_encoder_cache=True)
     nxt = torch.full((1, T), -1, dtype=torch.int32, device="cuda")
@@ -186,16 +202,15 @@ def test_lm_single_row_long_context(lm):
     rlt.rlt_encode(m.h, st, x)
     rlt.rlt_decode_scan(m.h, st, T, logits=lg, next_logprob=lp, next_tokens=nxt, s_out=s)
     torch.cuda.synchronize()
-    compare_rows("medium_lm B=1 replay positions 1-2052", lg, lp[:, :T - 1], s[:, T - 1], ggen)
+    compare_rows(f"medium_lm B=1 replay positions 1-{T}", lg, lp[:, :T - 1], s[:, T - 1], ggen)
     del lg, s
     p = 2048
     st2 = m.state(1, T, keep_encoder_cache=True)
     pre = torch.empty((1, p, CFG.vocab), dtype=torch.float32, device="cuda")
     rlt.rlt_encode(m.h, st2, x[:, :p].contiguous())
     rlt.rlt_decode_scan(m.h, st2, p, logits=pre)
-    steps = [m.step(st2, x[:, i].contiguous()) for i in range(p, T)]
-    tail = torch.cat([pre[:, p - 4:], torch.stack(steps, dim=1)], dim=1).cpu().numpy()
-    err = float(np.max(np.abs(tail - ggen["logits_tail"])))
-    print(f"[parity] medium_lm B=1 positions 2045-2052 (prefill + rlt_step) vs oracle, every id: {err:.3e}",
-          flush=True)
+    steps = [m.step(st2, x[:, i].contiguous()) for i in range(p, p + 8)]
+    lg0 = torch.cat([pre[:, p - 4:], torch.stack(steps, dim=1)], dim=1).cpu().numpy()
+    err, raw = compare_at("medium_lm B=1 prefill + rlt_step positions 2045-2056", lg0, ggen, list(range(p - 3, p + 9)))
     assert err <= TOL
+    assert raw >= 0.999
