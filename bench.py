@@ -715,6 +715,8 @@ def main():
                          "t = 32 and the prompt length of each shape; prints one JSON line per point")
     ap.add_argument("--sweep-shapes", default="algo_bf16,medium_lm,paper_shared")
     ap.add_argument("--sweep-batches", default="1,2,4,8")
+    ap.add_argument("--sweep-positions", default="32,prompt",
+                    help="decoder positions of the sweep points (\"prompt\": the shape's prompt length)")
     ap.add_argument("--generate", action="store_true",
                     help="time rlt_generate (on-device sampling with recorded log-probabilities) and the sampler")
     ap.add_argument("--snapshot", action="store_true",
@@ -738,7 +740,8 @@ def main():
     if args.sweep == "decode":
         from recurrent_looped_transformer_amd.synth import CONFIGS
         shapes = [x for x in args.sweep_shapes.split(",") if x]
-        pos = {n: [32, CONFIGS[n].seq_len] for n in shapes}
+        pos = {n: [CONFIGS[n].seq_len if p == "prompt" else int(p) for p in args.sweep_positions.split(",") if p]
+               for n in shapes}
         decode_sweep(shapes, [int(b) for b in args.sweep_batches.split(",")], pos)
         return
     if args.copy_probe:

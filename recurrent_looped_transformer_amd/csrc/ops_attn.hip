@@ -452,9 +452,9 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 // and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Same tiling as above with both
 // terms of a key / value tile in LDS (4 stages: buffer x term); at most two query blocks per
 // wave (register budget).
-template <typename T, int DH, int QB>
-__global__ __launch_bounds__(256) void flash_prefill_x2_k(AttnArgs a) {
-  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = 4 * QW;
+template <typename T, int DH, int QB, int NW = 4>
+__global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = NW * QW;
   constexpr int PARTS = DH / 8;
   constexpr int LOADERS = 16 * PARTS;
   __shared__ __align__(16) uint4 sK[2][2][BK][KP];           // [buffer][term]
@@ -655,7 +655,7 @@ static void launch_flash(const AttnArgs& a, hipStream_t st) {
     if (a.nq <= 512) {
       hipLaunchKernelGGL((flash_prefill_x2_k<T, DH, 1>), dim3((a.nq + 63) / 64, a.H, a.B), dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL((flash_prefill_x2_k<T, DH, 2>), dim3((a.nq + 127) / 128, a.H, a.B), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((flash_prefill_x2_k<T, DH, 1, 8>), dim3((a.nq + 127) / 128, a.H, a.B), dim3(512), 0, st, a);
     }
     return;
   }

@@ -154,14 +154,24 @@ void advance_scan_pos(int* p, int np, hipStream_t st) {
   hipLaunchKernelGGL(advance_scan_pos_k, dim3(1), dim3(1), 0, st, p, np);
 }
 
+// Grid-stride (a dispatch holds fewer than 2^32 work-items, and ring buffers of large
+// states exceed that many words): 16-byte stores over the aligned body, words at the ends.
 __global__ void fill_zero_k(uint32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t mis = (int64_t)((16 - ((uintptr_t)p & 15)) & 15) / 4;   // words before a 16-byte boundary
+  const int64_t head = mis < n ? mis : n;
+  const int64_t n4 = (n - head) / 4;
+  uint4* q = reinterpret_cast<uint4*>(p + head);
+  for (int64_t i = t; i < n4; i += stride) q[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t i = t; i < head; i += stride) p[i] = 0u;
+  for (int64_t i = head + 4 * n4 + t; i < n; i += stride) p[i] = 0u;
 }
 
 void fill_zero_u32(void* p, int64_t n, hipStream_t st) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(fill_zero_k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (uint32_t*)p, n);
+  const int64_t blocks = std::min<int64_t>((n / 4 + 255) / 256 + 1, 16384);
+  hipLaunchKernelGGL(fill_zero_k, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p, n);
 }
 
 __global__ void broadcast_row_k(const float* __restrict__ s0, float* __restrict__ s, int B, int d) {
