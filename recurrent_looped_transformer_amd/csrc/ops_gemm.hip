@@ -484,6 +484,27 @@ __global__ __launch_bounds__(256) void gemm_tiled(const T* __restrict__ X, int64
 constexpr int kBT = 256;                 // tile rows (both operands)
 constexpr int kBK = 64;                  // k per stage
 
+// Output tile of workgroup `pid`. Workgroups are dispatched to the 8 XCDs round-robin (pid
+// mod 8), so XCD x gets a contiguous run of tile indices q (the runs' lengths differ by at
+// most one when 8 does not divide the tile count); within the run, tiles are walked in groups
+// of kGroupM row tiles, every column tile of the group before the next group. The ~32
+// workgroups an XCD runs at once then cover about 8 row tiles x 4 column tiles and share their
+// activation and weight slices in its L2, instead of 32 row tiles of one column tile (each
+// activation slice read once per column tile).
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void large_tile(int pid, int ntm, int ntn, int& tm, int& tn) {
+  const int nt = ntm * ntn;
+  const int x = pid % 8, i = pid / 8;
+  const int per = nt / 8, rem = nt % 8;
+  const int q = x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+  const int span = kGroupM * ntn;                 // tiles of one group of row tiles
+  const int first = (q / span) * kGroupM;
+  const int gsize = min(ntm - first, kGroupM);
+  const int r = q % span;
+  tm = first + r % gsize;
+  tn = r / gsize;
+}
+
 // Eight waves (2 x 4, each 128 rows x 64 features) rather than four (2 x 2, 128 x 128): two
 // waves per SIMD hide each other's LDS waits and barriers (measured +7-13%, e.g. 1014 against
 // 915 TFLOP/s at M 32768, N 2048, K 5632; the result is the same bit for bit).
@@ -510,10 +531,8 @@ __global__ __launch_bounds__(512) void gemm_large(const T* __restrict__ X, int64
   const int wm = (wave >> 2) * 128;
   const int wn = (wave & 3) * 64;
   const int ntm = (M + kBT - 1) / kBT, ntn = (N + kBT - 1) / kBT;
-  const int nt = ntm * ntn;
-  int pid = blockIdx.x;
-  if (nt % 8 == 0) pid = (pid % 8) * (nt / 8) + pid / 8;
-  const int tm = pid % ntm, tn = pid / ntm;
+  int tm, tn;
+  large_tile(blockIdx.x, ntm, ntn, tm, tn);
   const int m0 = tm * kBT, n0 = tn * kBT;
   const int nkw = K / kBK;
   const int nk = 2 * (a.x_split ? 2 * nkw : nkw);   // half-slice stages (a multiple of 2)
@@ -522,9 +541,12 @@ __global__ __launch_bounds__(512) void gemm_large(const T* __restrict__ X, int64
   const T* wbase = W + (int64_t)(n0 / 16 + wave * CPW) * 16 * K + lane * 8;
   const int xrow0 = m0 + wave * CPW * 16 + r;
   const T* xbase = X + g * 16;
+  // two-term X: the hi and lo stages of each k slice follow each other (hi 0, lo 0, hi 1, ...),
+  // so the second copy of a weight slice comes from L2
   auto issue = [&](int st_, uint4* sb) {
-    const int kt = st_ >> 1, h = st_ & 1;
-    const int kw = kt < nkw ? kt : kt - nkw;
+    const int p = st_ >> 1, h = st_ & 1;
+    const int kw = a.x_split ? p >> 1 : p;
+    const int kt = a.x_split && (p & 1) ? nkw + kw : kw;   // X column slice (lo terms after the hi)
     uint4* d = sb + wave * CPW * 64;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
