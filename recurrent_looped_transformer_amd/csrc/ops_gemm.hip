@@ -614,6 +614,103 @@ __global__ __launch_bounds__(512) void gemm_large(const T* __restrict__ X, int64
   }
 }
 
+// Two-term X (each row K hi terms, then K lo terms): the tiles and copies of gemm_large, but a
+// stage holds one weight half-slice and both terms' activation half-slices (48 KB), so every
+// weight fragment read from LDS feeds the MFMAs of both terms: 64 MFMAs per wave, one barrier
+// and 20 fragment reads per stage (two stages, two barriers and 24 reads before). Ring of
+// three stages requested two ahead (144 KB of LDS).
+template <typename T, Ep E>
+__global__ __launch_bounds__(512) void gemm_large_x2(const T* __restrict__ X, int64_t ldx, const T* __restrict__ W,
+                                                     int M, int N, int K, EpArgs a) {
+  // [W 1024 uint4 | X hi 1024 uint4 | X lo 1024 uint4] each, distinct objects (see gemm_large)
+  __shared__ uint4 sb0[3072], sb1[3072], sb2[3072];
+  constexpr int NI = 4;
+  constexpr int CPW = 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = (wave >> 2) * 128;
+  const int wn = (wave & 3) * 64;
+  const int ntm = (M + kBT - 1) / kBT, ntn = (N + kBT - 1) / kBT;
+  int tm, tn;
+  large_tile(blockIdx.x, ntm, ntn, tm, tn);
+  const int m0 = tm * kBT, n0 = tn * kBT;
+  const int nkw = K / kBK;
+  const int nk = 2 * nkw;   // half-slice stages
+
+  const T* wbase = W + (int64_t)(n0 / 16 + wave * CPW) * 16 * K + lane * 8;
+  const int xrow0 = m0 + wave * CPW * 16 + r;
+  const T* xbase = X + g * 16;
+  auto issue = [&](int st_, uint4* sb) {
+    const int kw = st_ >> 1, h = st_ & 1;
+    uint4* d = sb + wave * CPW * 64;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const T* wsrc = wbase + (int64_t)i * 16 * K + h * 512 + (int64_t)kw * 1024;
+      const int row = min(xrow0 + i * 16, M - 1);
+      const T* xsrc = xbase + (int64_t)row * ldx + h * 8 + (int64_t)kw * kBK;
+      __builtin_amdgcn_global_load_lds((const void*)wsrc, (__attribute__((address_space(3))) void*)(d + i * 64), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)xsrc, (__attribute__((address_space(3))) void*)(d + 1024 + i * 64),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc + (int64_t)nkw * kBK),
+                                       (__attribute__((address_space(3))) void*)(d + 2048 + i * 64), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // stage s: wait for this wave's copies of s (the next stage's 3 CPW copies may still be in
+  // flight), a bare barrier, request stage s + 2 into the buffer stage s - 1 used, multiply
+  auto stage = [&](int s, const uint4* cur, uint4* nxt) {
+    if (s + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + 2 < nk) issue(s + 2, nxt);
+    const uint4* sw = cur + (wn / 16) * 64;
+    uint4 af[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) af[i] = sw[i * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {   // hi, then lo terms of the rows
+      const uint4* sx = cur + 1024 * (1 + t) + (wm / 16) * 64;
+      uint4 bfr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bfr[j] = sx[j * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32<T>(af[i], bfr[j], acc[i][j]);
+    }
+  };
+  issue(0, sb0);
+  if (1 < nk) issue(1, sb1);
+  for (int s = 0; s < nk; s += 3) {
+    stage(s, sb0, sb2);
+    if (s + 1 < nk) stage(s + 1, sb1, sb0);
+    if (s + 2 < nk) stage(s + 2, sb2, sb1);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = n0 + wn + i * 16 + 4 * g;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + wm + j * 16 + r;
+      if (m < M) {
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        epilogue<T, E>(a, m, n, v);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ mid (decode, M >= 256)
 // Decode GEMMs with a few hundred rows and a wide output are MFMA work, not weight
 // streaming: 128 x 128 output tile per workgroup of 4 waves (2 x 2, each 64 x 64 = 4 x 4 MFMA
@@ -836,7 +933,8 @@ static void launch16(const EpArgs& a, const void* X, int64_t ldx, const void* W,
 #undef RLT_SKINNY
   } else if (large_gemm_enabled() && K % kBK == 0) {
     const int nt = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-    hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
+    if (a.x_split) hipLaunchKernelGGL((gemm_large_x2<T, E>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
+    else hipLaunchKernelGGL((gemm_large<T, E>), dim3(nt), dim3(512), 0, st, x, ldx, w, M, N, K, a);
   } else {
     hipLaunchKernelGGL((gemm_tiled<T, E>), dim3((N + TB - 1) / TB, (M + TB - 1) / TB), dim3(256), 0, st, x, ldx, w,
                        M, N, K, a);
