@@ -319,18 +319,25 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
 
   // staging: thread t < LOADERS owns keys 4 jq .. 4 jq + 3 (jq = t / PARTS), 16-byte chunk part
+  // of K, and keys 4 jv .. 4 jv + 3 (jv = t % 16), chunk pv = t / 16 of V: the V^T writes of
+  // a wave then spread over every LDS bank (with the K mapping, the 16 chunks of a wave's
+  // rows fell on two bank groups: 8-way conflicts)
   const int jq = tid / PARTS, part = tid % PARTS;
+  const int jv = tid % 16, pv = tid / 16;
   uint4 rk[4], rv[4];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = k0 + 4 * jq + e;
+      const int p = k0 + 4 * jq + e, q = k0 + 4 * jv + e;
       rk[e] = make_uint4(0, 0, 0, 0);
       rv[e] = make_uint4(0, 0, 0, 0);
       if (tid < LOADERS && p <= kmax) {
         const int slot = a.ring ? (p - 1) % a.cap : p - 1;
         rk[e] = *reinterpret_cast<const uint4*>(Kb + (int64_t)slot * DH + part * 8);
-        rv[e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + part * 8);
+      }
+      if (tid < LOADERS && q <= kmax) {
+        const int slot = a.ring ? (q - 1) % a.cap : q - 1;
+        rv[e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + pv * 8);
       }
     }
   };
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
         uint2 t;
         t.x = ((w[0][e >> 1] >> sh) & 0xffffu) | (((w[1][e >> 1] >> sh) & 0xffffu) << 16);
         t.y = ((w[2][e >> 1] >> sh) & 0xffffu) | (((w[3][e >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sVt[buf][part * 8 + e][4 * jq]) = t;
+        *reinterpret_cast<uint2*>(&sVt[buf][pv * 8 + e][4 * jv]) = t;
       }
     }
   };
@@ -496,12 +503,14 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
 
+  // K and V staged by different thread mappings (see flash_prefill_k): conflict-free V^T writes
   const int jq = tid / PARTS, part = tid % PARTS;
+  const int jv = tid % 16, pv = tid / 16;
   uint4 rk[2][4], rv[2][4];                                   // [term][key]
   auto gload = [&](int k0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = k0 + 4 * jq + e;
+      const int p = k0 + 4 * jq + e, q = k0 + 4 * jv + e;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         rk[t][e] = make_uint4(0, 0, 0, 0);
@@ -511,8 +520,12 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
         const int slot = a.ring ? (p - 1) % a.cap : p - 1;
         const int64_t off = (int64_t)slot * DH + part * 8;
         rk[0][e] = *reinterpret_cast<const uint4*>(Kb + off);
-        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + off);
         rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + off);
+      }
+      if (tid < LOADERS && q <= kmax) {
+        const int slot = a.ring ? (q - 1) % a.cap : q - 1;
+        const int64_t off = (int64_t)slot * DH + pv * 8;
+        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + off);
         rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + off);
       }
     }
@@ -533,7 +546,7 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
           uint2 u;
           u.x = ((w[0][e >> 1] >> sh) & 0xffffu) | (((w[1][e >> 1] >> sh) & 0xffffu) << 16);
           u.y = ((w[2][e >> 1] >> sh) & 0xffffu) | (((w[3][e >> 1] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<uint2*>(&sVt[buf][t][part * 8 + e][4 * jq]) = u;
+          *reinterpret_cast<uint2*>(&sVt[buf][t][pv * 8 + e][4 * jv]) = u;
         }
       }
     }
