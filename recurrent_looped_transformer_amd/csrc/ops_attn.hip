@@ -277,9 +277,12 @@ namespace rlt {
 
 // QB query blocks of 16 per wave: up to 4 (2 for bf16 at dh 128: register budget); short
 // sequences take one so that the grid keeps enough workgroups.
+// Row pitches: KP = DH / 8 + 1 uint4 per K row (the 16 rows a fragment read touches start 4
+// banks apart); VP = BK + 4 halves per V^T row (136 bytes: the 16 rows of a PV fragment read
+// start 34 banks apart, distinct bank pairs — a pitch of 72 put rows c and c + 8 on one pair).
 template <typename T, int DH, int QB>
 __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
-  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = 4 * QW;
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 4, QW = 16 * QB, QBLK = 4 * QW;
   constexpr int PARTS = DH / 8;                      // 16-byte chunks of a key row
   constexpr int LOADERS = 16 * PARTS;                // threads that stage a tile: 4 keys x 8 values each
   __shared__ __align__(16) uint4 sK[2][BK][KP];
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 // wave (register budget).
 template <typename T, int DH, int QB, int NW = 4>
 __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
-  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 8, QW = 16 * QB, QBLK = NW * QW;
+  constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 4, QW = 16 * QB, QBLK = NW * QW;
   constexpr int PARTS = DH / 8;
   constexpr int LOADERS = 16 * PARTS;
   __shared__ __align__(16) uint4 sK[2][2][BK][KP];           // [buffer][term]
