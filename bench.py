@@ -543,16 +543,18 @@ def mem_attn_bytes(cfg, B: int, t: int) -> float:
 def decode_bench(args, cfg, prompt: int):
     """Decoder transitions at position ~prompt for the whole batch, plus the encoder prefill.
 
-    Encodes prompt + warmup + steps tokens per row (timed: encoder tok/s), seeks the decoder
-    to position `prompt` (the window rings cleared, the memory of every encoded position
-    real: rlt_state_seek), runs `warmup` transitions, then times `steps` transitions with HIP
-    events, the cross-attention launches among them on their own event timers. A step is one
+    Encodes prompt + warmup + 2 steps tokens per row (timed: encoder tok/s), seeks the
+    decoder to position `prompt` (the window rings cleared, the memory of every encoded
+    position real: rlt_state_seek), runs `warmup` transitions, then times `steps` transitions
+    with HIP events around the whole run (the value). A second run of `steps` transitions with
+    the per-kernel event timers on gives the step breakdown and the cross-attention's
+    per-launch duration (the timers' own events would slow the first run). A step is one
     batched transition (merge, L_D blocks, readout with fp32 logits) of every row."""
     import torch
     from recurrent_looped_transformer_amd import rlt
     from recurrent_looped_transformer_amd.synth import make_params, make_tokens
     B, K, Wm = cfg.batch, args.steps, args.warmup
-    T = prompt + Wm + K
+    T = prompt + Wm + 2 * K
     t0 = time.perf_counter()
     P = make_params(cfg, bf16_storage=cfg.d >= 4096)
     torch.cuda.set_device(0)
@@ -564,7 +566,6 @@ def decode_bench(args, cfg, prompt: int):
     stream = torch.cuda.current_stream()
     lg = torch.empty((B, K, cfg.vocab), dtype=torch.float32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    rlt.rlt_kernel_timing(model.h, True)
     torch.cuda.synchronize()
     ev[0].record(stream)
     rlt.rlt_encode(model.h, st, x)
@@ -572,13 +573,9 @@ def decode_bench(args, cfg, prompt: int):
     torch.cuda.synchronize()
     enc_ms = ev[0].elapsed_time(ev[1])
     print(f"[bench] encode of {B} x {T} tokens: {enc_ms:.0f} ms", flush=True)
-    for k in range(5):
-        rlt.rlt_kernel_time(model.h, k)          # clear the encoder's timers
     rlt.rlt_state_seek(model.h, st, prompt)
     if Wm:
         rlt.rlt_decode_scan(model.h, st, Wm)
-    for k in range(5):
-        rlt.rlt_kernel_time(model.h, k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ev[2].record(stream)
@@ -587,15 +584,20 @@ def decode_bench(args, cfg, prompt: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t1
     scan_ms = ev[2].elapsed_time(ev[3])
+    # second run with the per-kernel timers (breakdown, dominant kernel's launch duration)
+    rlt.rlt_kernel_timing(model.h, True)
+    rlt.rlt_decode_scan(model.h, st, K, logits=lg)
+    torch.cuda.synchronize()
     att_ms, att_n = rlt.rlt_kernel_time(model.h, rlt.TIME_MEMORY_ATTN)
     win_ms, win_n = rlt.rlt_kernel_time(model.h, rlt.TIME_WINDOW_ATTN)
     gem_ms, gem_n = rlt.rlt_kernel_time(model.h, rlt.TIME_DECODER_GEMM)
     rlt.rlt_kernel_timing(model.h, False)
     assert att_n == K * cfg.L_D, (att_n, K * cfg.L_D)
     pos = list(range(prompt + Wm + 1, prompt + Wm + K + 1))
+    pos2 = list(range(prompt + Wm + K + 1, prompt + Wm + 2 * K + 1))
     ms_step = scan_ms / K
     sb = scan_bytes(cfg, B, K, t_start=prompt + Wm)
-    att_bytes = float(np.mean([mem_attn_bytes(cfg, B, t) for t in pos]))
+    att_bytes = float(np.mean([mem_attn_bytes(cfg, B, t) for t in pos2]))
     att_avg = att_ms / att_n
     ach = att_bytes / (att_avg / 1e3) / 1e9
     ef = encoder_flops(cfg, B, T)
@@ -633,7 +635,9 @@ def decode_bench(args, cfg, prompt: int):
                           "unit": "GB/s", "frac": sb / (scan_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                           "algorithmic_bytes_per_step": sb / K},
         "step_breakdown_ms": {"memory_attention": att_ms / K, "window_attention": win_ms / K,
-                              "gemms": gem_ms / K, "launches_per_step": (att_n + win_n + gem_n) / K},
+                              "gemms": gem_ms / K, "launches_per_step": (att_n + win_n + gem_n) / K,
+                              "positions": [pos2[0], pos2[-1]],
+                              "note": "a second run of the same number of steps with per-kernel event timers"},
         "encoder_tok_s": B * T / (enc_ms / 1e3), "encoder_ms": enc_ms, "encoder_tokens": B * T,
         "encoder_tflops": ef / (enc_ms / 1e3) / 1e12,
         "encoder_mfma_frac": ef / (enc_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -692,7 +696,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="paper_shared")
+    ap.add_argument("--config", default=None,
+                    help="workload (default: paper_shared for the decoder-transition line; algo_bf16 for "
+                         "--replay, --grad, --ragged, --generate and --snapshot)")
     ap.add_argument("--replay", action="store_true",
                     help="time whole replays (encode + scan over every position + log-probs) instead of "
                          "decoder transitions at the prompt's end")
@@ -755,6 +761,9 @@ def main():
     from recurrent_looped_transformer_amd import rlt
     from recurrent_looped_transformer_amd.synth import CONFIGS, make_params, make_tokens
 
+    if args.config is None:
+        side = args.replay or args.grad or args.ragged or args.generate or args.snapshot
+        args.config = "algo_bf16" if side else "paper_shared"
     cfg = CONFIGS[args.config]
     if args.batch:
         cfg = cfg.replace(batch=args.batch)
