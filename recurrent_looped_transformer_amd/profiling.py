@@ -18,8 +18,8 @@
     python -m recurrent_looped_transformer_amd.profiling run-decode OUT [bench args...]
         (on the MI355X host) the default measurement of bench.py (decoder transitions at the
         prompt's end): --kernel-trace --stats over `bench.py --steps 3 --warmup 1 --no-cpu ...`,
-        --pmc FETCH_SIZE and --pmc WRITE_SIZE over `bench.py --steps 1 --warmup 0 --no-cpu ...`,
-        and the copy probe for both counters
+        --pmc FETCH_SIZE and --pmc WRITE_SIZE over `bench.py --steps 1 --warmup 0 --no-cpu ...`
+        on the decoder's kernels only (--kernel-include-regex), and the copy probe for both
     python -m recurrent_looped_transformer_amd.profiling summarize-decode OUT NAME [bench args...]
         writes profiles/kernels_NAME.md (kernel table, counters of the decoder's kernels per
         dispatch) and profiles/traffic_memattn_NAME.json (HBM bytes per launch of the memory
@@ -233,12 +233,15 @@ def run_decode(out_dir: str, bench_args):
     for big in glob.glob(os.path.join(out_dir, "trace", "**", "*kernel_trace.csv"), recursive=True):
         os.remove(big)
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        _rocprof(out_dir, c.lower(), ["--pmc", c], ["--steps", "1", "--warmup", "0", "--no-cpu"] + bench_args,
-                 lg(c.lower()))
+        # counters on the decoder's kernels only (the transition's GEMMs and attention): the encode
+        # that precedes the transitions runs uninstrumented
+        _rocprof(out_dir, c.lower(), ["--pmc", c, "--kernel-include-regex", DECODE_KERNELS],
+                 ["--steps", "1", "--warmup", "0", "--no-cpu"] + bench_args, lg(c.lower()))
         _rocprof(out_dir, "copy_" + c.lower(), ["--pmc", c], ["--copy-probe", str(COPY_BYTES)], lg("copy_" + c.lower()))
 
 
-MEM_ATTN = re.compile(r"attn_decode_k<[^,]+, \d+, false, 1(, false)?>")
+DECODE_KERNELS = "attn_decode_k|gemm_skinny|skinny_reduce"
+MEM_ATTN = re.compile(r"attn_decode_k<[^,]+, \d+, false, 1(, false(, (true|false))?)?>")   # any NT instance
 
 
 def summarize_decode(out_dir: str, name: str, bench_args):
@@ -271,14 +274,15 @@ def summarize_decode(out_dir: str, name: str, bench_args):
              "Commands (R = repository root on the MI355X host; every file run is committed):", "",
              f"    python -m recurrent_looped_transformer_amd.profiling run-decode OUT {cmd}",
              "    (rocprofv3 --kernel-trace --stats ... -- python3 R/bench.py --steps 3 --warmup 1 --no-cpu ARGS;",
-             "     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 R/bench.py --steps 1 --warmup 0 --no-cpu ARGS;",
+             f"     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE --kernel-include-regex '{DECODE_KERNELS}' ... -- "
+             "python3 R/bench.py --steps 1 --warmup 0 --no-cpu ARGS;",
              f"     the same counters over python3 R/bench.py --copy-probe {COPY_BYTES})",
              f"    python -m recurrent_looped_transformer_amd.profiling summarize-decode OUT {name} {cmd}", "",
              f"Library sha256 prefix: {lib_sha()}", "",
              f"Counter scale: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f} (a {COPY_BYTES >> 20} MiB copy reads "
              f"{max(copy_f):.0f} / writes {max(copy_w):.0f} KiB of counter).", "",
              "rocprofv3 --stats over the whole run (one encode of the prompt, then 1 warm-up + 3 timed decoder "
-             "steps; the encoder's kernels carry most of the total):", "",
+             "steps + 3 more with bench.py's per-kernel timers; the encoder's kernels carry most of the total):", "",
              "| kernel | calls | total ms | mean us | share | decode HBM read KiB/dispatch | "
              "decode HBM write KiB/dispatch |", "|---|---|---|---|---|---|---|"]
     for r in stats[:24]:
