@@ -267,12 +267,14 @@ void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st) {
 // queries as 2 blocks of 16 per wave at dh 128) of one (sequence, head); keys and values stream through LDS in tiles of 64 positions, double
 // buffered (the next tile's loads are in registers while the current one computes; V is
 // stored transposed, 4 keys per 8-byte write). Each wave computes S^T = K Q^T with 16x16x32
-// MFMAs: lane l then holds the scores of keys 4g..4g+3 (g = l / 16) of query l % 16, which is
-// exactly the B operand layout of the 16x16x16 MFMA used for O^T += V^T P^T, so
-// probabilities never leave registers; each K or V^T fragment read from LDS feeds the four
-// query blocks of the wave. Softmax statistics are fp32 per query, online over key tiles.
-// (Pairing two 16-key sub-tiles into one 16x16x32 product per 32 keys measured 5% slower
-// at the paper-shape encode: the operands have to be gathered into adjacent registers.)
+// MFMAs: lane l then holds the scores of 4 keys of query l % 16. Key rows sit in LDS in a
+// permuted order (LDS row 32 p + 16 h + 4 a + i holds key 32 p + 8 a + 4 h + i), so that over
+// two adjacent 16-key sub-tiles lane l holds keys 8g..8g+7 (g = l / 16) of a 32-key half: exactly
+// the B operand of the 16x16x32 MFMA for O^T += V^T P^T, so probabilities never leave
+// registers, and the weighted sum takes one product per 32 keys (two 16x16x16 products issue
+// at half the rate on this part). Each K or V^T fragment read from LDS feeds the query blocks
+// of the wave. Softmax statistics are fp32 per query, online over key tiles, in base 2 with
+// log2(e) folded into the score scale; tiles that every query of a wave sees whole skip the mask.
 namespace rlt {
 
 // QB query blocks of 16 per wave: up to 4 (2 for bf16 at dh 128: register budget); short
@@ -288,7 +290,8 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   __shared__ __align__(16) uint4 sK[2][BK][KP];
   __shared__ __align__(16) uint16_t sVt[2][DH][VP];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int g = lane >> 4, c = lane & 15;
   const int q0 = qb * QBLK + wave * QW;              // first query (within this call) of the wave
   uint4 qf[QB][DH / 32];
@@ -315,9 +318,12 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
     m_run[j] = -INFINITY;
     l_run[j] = 0.f;
   }
+  const float scale2 = a.scale * 1.4426950408889634f;     // scores in base 2
   const int qlast = min(a.nq, (qb + 1) * QBLK);        // queries of this block: [qb*QBLK, qlast)
   const int kmax = a.pos0 + qlast;                       // last key position any query here needs
   const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * QBLK - a.window + 1) : 1;
+  const bool wave_full_q = q0 + QW <= a.nq;              // the wave's queries all valid
+  const int wq_first = a.pos0 + 1 + q0, wq_last = a.pos0 + q0 + QW;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
 
@@ -327,27 +333,37 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   // rows fell on two bank groups: 8-way conflicts)
   const int jq = tid / PARTS, part = tid % PARTS;
   const int jv = tid % 16, pv = tid / 16;
+  // LDS row of key 4 jq (the permuted key order of the two-term kernel below)
+  const int krow = 32 * (jq >> 3) + 16 * (jq & 1) + 4 * ((jq >> 1) & 3);
   uint4 rk[4], rv[4];
+  // positions past kmax load the row of kmax (valid data: their scores are masked, so they
+  // weigh zero); a ring slot is the tile's first slot (one scalar modulo) plus the key's
+  // offset, wrapped once (the launch guarantees cap >= BK)
+  // (the staging registers are defined on every path: otherwise they are kept in scratch)
   auto gload = [&](int k0) {
+    const int s0 = a.ring ? (k0 - 1) % a.cap : k0 - 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = k0 + 4 * jq + e, q = k0 + 4 * jv + e;
       rk[e] = make_uint4(0, 0, 0, 0);
       rv[e] = make_uint4(0, 0, 0, 0);
-      if (tid < LOADERS && p <= kmax) {
-        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-        rk[e] = *reinterpret_cast<const uint4*>(Kb + (int64_t)slot * DH + part * 8);
-      }
-      if (tid < LOADERS && q <= kmax) {
-        const int slot = a.ring ? (q - 1) % a.cap : q - 1;
-        rv[e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)slot * DH + pv * 8);
+    }
+    if (tid < LOADERS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int sp = s0 + min(4 * jq + e, kmax - k0), sq = s0 + min(4 * jv + e, kmax - k0);
+        if (a.ring) {
+          sp = sp >= a.cap ? sp - a.cap : sp;
+          sq = sq >= a.cap ? sq - a.cap : sq;
+        }
+        rk[e] = *reinterpret_cast<const uint4*>(Kb + (int64_t)sp * DH + part * 8);
+        rv[e] = *reinterpret_cast<const uint4*>(Vb + (int64_t)sq * DH + pv * 8);
       }
     }
   };
   auto lstore = [&](int buf) {
     if (tid < LOADERS) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sK[buf][4 * jq + e][part] = rk[e];
+      for (int e = 0; e < 4; ++e) sK[buf][krow + e][part] = rk[e];
       const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w}, {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
                                 {rv[2].x, rv[2].y, rv[2].z, rv[2].w}, {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
 #pragma unroll
@@ -368,10 +384,10 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   for (int k0 = kmin; k0 <= kmax; k0 += BK) {
     const bool more = k0 + BK <= kmax;
     if (more) gload(k0 + BK);
-    float s[QB][4][4];
-    float tmax[QB];
-#pragma unroll
-    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);   // the next tile's loads stay ahead of this tile's work
+    const bool whole = wave_full_q && k0 + BK - 1 <= wq_first && (a.window <= 0 || k0 > wq_last - a.window);
+    // all score products first (no branch between them), then the mask
+    f32x4 sacc[QB][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint4 kf[DH / 32];
@@ -382,16 +398,37 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < DH / 32; ++kc) acc = mfma16x16x32<T>(kf[kc], qf[j][kc], acc);
+        sacc[j][st] = acc;
+      }
+    }
+    float s[QB][4][4];
+    float tmax[QB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kp = k0 + st * 16 + 4 * g + i;
-          const bool ok = qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
-          s[j][st][i] = ok ? acc[i] * a.scale : -INFINITY;
-          tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const f32x4 acc = sacc[j][st];
+        if (whole) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[j][st][i] = acc[i] * scale2;
+            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kp = k0 + 32 * (st >> 1) + 8 * g + 4 * (st & 1) + i;   // permuted key rows
+            const bool ok =
+                qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
+            s[j][st][i] = ok ? acc[i] * scale2 : -INFINITY;
+            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+          }
         }
       }
     }
-    uint2 pb[QB][4];
+    uint4 pb[QB][2];                             // [query block][32-key half]: keys 8 g .. 8 g + 7
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float tm = fmaxf(tmax[j], __shfl_xor(tmax[j], 16, WAVE));
@@ -399,34 +436,39 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
       const float m_new = fmaxf(m_run[j], tm);
       // branch-free: a column with nothing visible yet keeps l = 0 and o = 0 (exp(-inf) = 0)
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __expf(m_run[j] - m_use);
+      const float corr = __builtin_amdgcn_exp2f(m_run[j] - m_use);
       l_run[j] *= corr;
 #pragma unroll
       for (int i = 0; i < DH / 16; ++i) o[j][i] *= corr;
       float lsum = 0.f;
+      uint32_t w[4][2];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __expf(s[j][st][i] - m_use);
+          pv[i] = __builtin_amdgcn_exp2f(s[j][st][i] - m_use);
           lsum += pv[i];
         }
-        pb[j][st].x = pack2<T>(pv[0], pv[1]);
-        pb[j][st].y = pack2<T>(pv[2], pv[3]);
+        w[st][0] = pack2<T>(pv[0], pv[1]);
+        w[st][1] = pack2<T>(pv[2], pv[3]);
       }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) pb[j][p] = make_uint4(w[2 * p][0], w[2 * p][1], w[2 * p + 1][0], w[2 * p + 1][1]);
       lsum += __shfl_xor(lsum, 16, WAVE);
       lsum += __shfl_xor(lsum, 32, WAVE);
       l_run[j] += lsum;
       m_run[j] = m_new;
     }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) {
-        const uint2 av = *reinterpret_cast<const uint2*>(&sVt[buf][db * 16 + c][st * 16 + 4 * g]);
+        const uint16_t* r0 = &sVt[buf][db * 16 + c][p * 32 + 8 * g];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(r0), v1 = *reinterpret_cast<const uint2*>(r0 + 4);
+        const uint4 av = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-        for (int j = 0; j < QB; ++j) o[j][db] = mfma16x16x16<T>(av, pb[j][st], o[j][db]);
+        for (int j = 0; j < QB; ++j) o[j][db] = mfma16x16x32<T>(av, pb[j][p], o[j][db]);
       }
     }
     if (more) lstore(buf ^ 1);   // buffer buf ^ 1 was last read before the previous barrier
@@ -459,9 +501,11 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 // Two-term operands (q_lo, kv_lo > 0): every query, key and value is hi + lo in the 16-bit
 // type. Scores take three MFMA products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
 // below the fp32 rounding of the sum), the probabilities are split into hi + lo in registers
-// and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Same tiling as above with both
-// terms of a key / value tile in LDS (4 stages: buffer x term); at most two query blocks per
-// wave (register budget).
+// and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Both terms of a key / value tile
+// sit in LDS (4 stages: buffer x term); at most two query blocks per wave (register budget).
+//
+// Key order, weighted-sum products and softmax as in flash_prefill_k (one 16x16x32 product per
+// 32 keys instead of two 16x16x16: the MFMA-busy counter of this kernel fell by a third).
 template <typename T, int DH, int QB, int NW = 4>
 __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 4, QW = 16 * QB, QBLK = NW * QW;
@@ -470,7 +514,8 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   __shared__ __align__(16) uint4 sK[2][2][BK][KP];           // [buffer][term]
   __shared__ __align__(16) uint16_t sVt[2][2][DH][VP];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int g = lane >> 4, c = lane & 15;
   const int q0 = qb * QBLK + wave * QW;
   uint4 qh[QB][DH / 32], ql[QB][DH / 32];
@@ -500,36 +545,45 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
     m_run[j] = -INFINITY;
     l_run[j] = 0.f;
   }
+  const float scale2 = a.scale * 1.4426950408889634f;     // scores in base 2
   const int qlast = min(a.nq, (qb + 1) * QBLK);
   const int kmax = a.pos0 + qlast;
   const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * QBLK - a.window + 1) : 1;
+  // the wave's queries: positions pos0 + 1 + q0 .. pos0 + q0 + QW, all valid or not
+  const bool wave_full_q = q0 + QW <= a.nq;
+  const int wq_first = a.pos0 + 1 + q0, wq_last = a.pos0 + q0 + QW;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
 
   // K and V staged by different thread mappings (see flash_prefill_k): conflict-free V^T writes
   const int jq = tid / PARTS, part = tid % PARTS;
   const int jv = tid % 16, pv = tid / 16;
+  // LDS row of key 4 jq (keys 4 jq .. 4 jq + 3 land on consecutive rows)
+  const int krow = 32 * (jq >> 3) + 16 * (jq & 1) + 4 * ((jq >> 1) & 3);
   uint4 rk[2][4], rv[2][4];                                   // [term][key]
+  // positions past kmax load the row of kmax (valid data: their scores are masked, so they
+  // weigh zero); a ring slot is the tile's first slot (one scalar modulo) plus the key's
+  // offset, wrapped once (the launch guarantees cap >= BK)
+  // (the staging registers are defined on every path: otherwise they are kept in scratch)
   auto gload = [&](int k0) {
+    const int s0 = a.ring ? (k0 - 1) % a.cap : k0 - 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = k0 + 4 * jq + e, q = k0 + 4 * jv + e;
+      rk[0][e] = rk[1][e] = rv[0][e] = rv[1][e] = make_uint4(0, 0, 0, 0);
+    }
+    if (tid < LOADERS) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        rk[t][e] = make_uint4(0, 0, 0, 0);
-        rv[t][e] = make_uint4(0, 0, 0, 0);
-      }
-      if (tid < LOADERS && p <= kmax) {
-        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
-        const int64_t off = (int64_t)slot * DH + part * 8;
-        rk[0][e] = *reinterpret_cast<const uint4*>(Kb + off);
-        rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + off);
-      }
-      if (tid < LOADERS && q <= kmax) {
-        const int slot = a.ring ? (q - 1) % a.cap : q - 1;
-        const int64_t off = (int64_t)slot * DH + pv * 8;
-        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + off);
-        rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + off);
+      for (int e = 0; e < 4; ++e) {
+        int sp = s0 + min(4 * jq + e, kmax - k0), sq = s0 + min(4 * jv + e, kmax - k0);
+        if (a.ring) {
+          sp = sp >= a.cap ? sp - a.cap : sp;
+          sq = sq >= a.cap ? sq - a.cap : sq;
+        }
+        const int64_t offk = (int64_t)sp * DH + part * 8, offv = (int64_t)sq * DH + pv * 8;
+        rk[0][e] = *reinterpret_cast<const uint4*>(Kb + offk);
+        rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + offk);
+        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + offv);
+        rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + offv);
       }
     }
   };
@@ -538,7 +592,7 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sK[buf][t][4 * jq + e][part] = rk[t][e];
+        for (int e = 0; e < 4; ++e) sK[buf][t][krow + e][part] = rk[t][e];
         const uint32_t w[4][4] = {{rv[t][0].x, rv[t][0].y, rv[t][0].z, rv[t][0].w},
                                   {rv[t][1].x, rv[t][1].y, rv[t][1].z, rv[t][1].w},
                                   {rv[t][2].x, rv[t][2].y, rv[t][2].z, rv[t][2].w},
@@ -562,10 +616,12 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   for (int k0 = kmin; k0 <= kmax; k0 += BK) {
     const bool more = k0 + BK <= kmax;
     if (more) gload(k0 + BK);
-    float s[QB][4][4];
-    float tmax[QB];
-#pragma unroll
-    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);   // the next tile's loads stay ahead of this tile's work
+    // every key of the tile visible to every query of the wave
+    const bool whole = wave_full_q && k0 + BK - 1 <= wq_first && (a.window <= 0 || k0 > wq_last - a.window);
+    // all score products first (independent accumulators per sub-tile, no branch between
+    // them), then the mask
+    f32x4 sacc[QB][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint4 kh[DH / 32], kl[DH / 32];
@@ -583,41 +639,69 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
           acc = mfma16x16x32<T>(kh[kc], ql[j][kc], acc);
           acc = mfma16x16x32<T>(kh[kc], qh[j][kc], acc);
         }
+        sacc[j][st] = acc;
+      }
+    }
+    float s[QB][4][4];
+    float tmax[QB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kp = k0 + st * 16 + 4 * g + i;
-          const bool ok = qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
-          s[j][st][i] = ok ? acc[i] * a.scale : -INFINITY;
-          tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const f32x4 acc = sacc[j][st];
+        if (whole) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[j][st][i] = acc[i] * scale2;
+            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // lane (g, c), sub-tile st: key 32 (st / 2) + 8 g + 4 (st % 2) + i of the tile
+            const int kp = k0 + 32 * (st >> 1) + 8 * g + 4 * (st & 1) + i;
+            const bool ok =
+                qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
+            s[j][st][i] = ok ? acc[i] * scale2 : -INFINITY;
+            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
+          }
         }
       }
     }
-    uint2 pbh[QB][4], pbl[QB][4];
+    uint4 pbh[QB][2], pbl[QB][2];                // [query block][32-key half]: keys 8 g .. 8 g + 7
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float tm = fmaxf(tmax[j], __shfl_xor(tmax[j], 16, WAVE));
       tm = fmaxf(tm, __shfl_xor(tm, 32, WAVE));
       const float m_new = fmaxf(m_run[j], tm);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __expf(m_run[j] - m_use);
+      const float corr = __builtin_amdgcn_exp2f(m_run[j] - m_use);
       l_run[j] *= corr;
 #pragma unroll
       for (int i = 0; i < DH / 16; ++i) o[j][i] *= corr;
       float lsum = 0.f;
+      uint32_t wh[4][2], wl[4][2];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float ph[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __expf(s[j][st][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(s[j][st][i] - m_use);
           lsum += pv;
           ph[i] = Elem<T>::round(pv);
           pl[i] = pv - ph[i];
         }
-        pbh[j][st].x = pack2<T>(ph[0], ph[1]);
-        pbh[j][st].y = pack2<T>(ph[2], ph[3]);
-        pbl[j][st].x = pack2<T>(pl[0], pl[1]);
-        pbl[j][st].y = pack2<T>(pl[2], pl[3]);
+        wh[st][0] = pack2<T>(ph[0], ph[1]);
+        wh[st][1] = pack2<T>(ph[2], ph[3]);
+        wl[st][0] = pack2<T>(pl[0], pl[1]);
+        wl[st][1] = pack2<T>(pl[2], pl[3]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        pbh[j][p] = make_uint4(wh[2 * p][0], wh[2 * p][1], wh[2 * p + 1][0], wh[2 * p + 1][1]);
+        pbl[j][p] = make_uint4(wl[2 * p][0], wl[2 * p][1], wl[2 * p + 1][0], wl[2 * p + 1][1]);
       }
       lsum += __shfl_xor(lsum, 16, WAVE);
       lsum += __shfl_xor(lsum, 32, WAVE);
@@ -625,16 +709,21 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
       m_run[j] = m_new;
     }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) {
-        const uint2 vh = *reinterpret_cast<const uint2*>(&sVt[buf][0][db * 16 + c][st * 16 + 4 * g]);
-        const uint2 vl = *reinterpret_cast<const uint2*>(&sVt[buf][1][db * 16 + c][st * 16 + 4 * g]);
+        // two 8-byte reads per term (rows of 68 halves: the 16 rows of a read fall on distinct
+        // bank pairs; 16-byte reads of 16-byte aligned rows measured twice the bank conflicts)
+        const uint16_t* r0 = &sVt[buf][0][db * 16 + c][p * 32 + 8 * g];
+        const uint16_t* r1 = &sVt[buf][1][db * 16 + c][p * 32 + 8 * g];
+        const uint2 h0 = *reinterpret_cast<const uint2*>(r0), h1 = *reinterpret_cast<const uint2*>(r0 + 4);
+        const uint2 l0 = *reinterpret_cast<const uint2*>(r1), l1 = *reinterpret_cast<const uint2*>(r1 + 4);
+        const uint4 vh = make_uint4(h0.x, h0.y, h1.x, h1.y), vl = make_uint4(l0.x, l0.y, l1.x, l1.y);
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-          o[j][db] = mfma16x16x16<T>(vl, pbh[j][st], o[j][db]);
-          o[j][db] = mfma16x16x16<T>(vh, pbl[j][st], o[j][db]);
-          o[j][db] = mfma16x16x16<T>(vh, pbh[j][st], o[j][db]);
+          o[j][db] = mfma16x16x32<T>(vl, pbh[j][p], o[j][db]);
+          o[j][db] = mfma16x16x32<T>(vh, pbl[j][p], o[j][db]);
+          o[j][db] = mfma16x16x32<T>(vh, pbh[j][p], o[j][db]);
         }
       }
     }
@@ -690,6 +779,7 @@ static void launch_flash(const AttnArgs& a, hipStream_t st) {
 
 bool attn_prefill(Dt dt, const AttnArgs& a, hipStream_t st) {
   if ((a.dh != 64 && a.dh != 128) || dt == Dt::F32) return false;
+  if (a.ring && a.cap < 64) return false;   // a tile's ring slots wrap at most once
   if (dt == Dt::BF16) {
     if (a.dh == 64) launch_flash<bf16_t, 64>(a, st);
     else launch_flash<bf16_t, 128>(a, st);
