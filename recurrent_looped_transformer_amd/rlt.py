@@ -180,10 +180,26 @@ def rlt_destroy(model) -> None:
     _check(load().rlt_destroy(model))
 
 
+# Rows of every live state: a buffer passed with a state must hold exactly that many rows (the
+# library reads and writes [rows, ...] through plain pointers, so a shorter tensor would be
+# accessed out of bounds on the device).
+_STATE_ROWS: Dict[int, int] = {}
+
+
+def _rows(state, *tensors) -> None:
+    rows = _STATE_ROWS.get(state.value if isinstance(state, ctypes.c_void_p) else int(state))
+    if rows is None:
+        return
+    for t in tensors:
+        if t is not None and (t.dim() == 0 or t.shape[0] != rows):
+            raise ValueError(f"a tensor of shape {tuple(t.shape)} passed with a state of {rows} rows")
+
+
 def rlt_state_create(model, batch: int, max_len: int, keep_encoder_cache: bool = True) -> ctypes.c_void_p:
     out = ctypes.c_void_p()
     _check(load().rlt_state_create(model, batch, max_len, 1 if keep_encoder_cache else 0,
                                    ctypes.c_void_p(_stream()), ctypes.byref(out)))
+    _STATE_ROWS[out.value] = batch
     return out
 
 
@@ -193,6 +209,7 @@ def rlt_state_reset(model, state) -> None:
 
 def rlt_state_destroy(state) -> None:
     _check(load().rlt_state_destroy(state))
+    _STATE_ROWS.pop(state.value if isinstance(state, ctypes.c_void_p) else int(state), None)
 
 
 def rlt_state_bytes(state) -> list:
@@ -238,21 +255,25 @@ def rlt_set_batch_invariant(model, on: bool) -> None:
 
 def rlt_encode(model, state, tokens: torch.Tensor) -> None:
     assert tokens.dtype == torch.int32 and tokens.dim() == 2
+    _rows(state, tokens)
     _check(load().rlt_encode(model, state, _ptr(tokens), tokens.shape[1], ctypes.c_void_p(_stream())))
 
 
 def rlt_decode_scan(model, state, T: int, logits=None, next_logprob=None, next_tokens=None, s_out=None) -> None:
+    _rows(state, logits, next_logprob, next_tokens, s_out)
     _check(load().rlt_decode_scan(model, state, T, _ptr(logits), _ptr(next_logprob), _ptr(next_tokens),
                                   _ptr(s_out), ctypes.c_void_p(_stream())))
 
 
 def rlt_step(model, state, tokens: torch.Tensor, logits: torch.Tensor) -> None:
     assert tokens.dtype == torch.int32 and tokens.dim() == 1
+    _rows(state, tokens, logits)
     _check(load().rlt_step(model, state, _ptr(tokens), _ptr(logits), ctypes.c_void_p(_stream())))
 
 
 def rlt_replay(model, state, tokens: torch.Tensor, logprob: torch.Tensor, s_out=None) -> None:
     assert tokens.dtype == torch.int32 and tokens.dim() == 2
+    _rows(state, tokens, logprob, s_out)
     _check(load().rlt_replay(model, state, _ptr(tokens), tokens.shape[1], _ptr(logprob), _ptr(s_out),
                              ctypes.c_void_p(_stream())))
 
@@ -285,6 +306,7 @@ def rlt_sample_noalloc(logits: torch.Tensor, temperature: float, seed: int, step
 def rlt_generate(model, state, first: torch.Tensor, n: int, temperature: float, seed: int, step0: int,
                  tokens: torch.Tensor, logprob: torch.Tensor, logits: Optional[torch.Tensor] = None) -> None:
     assert first.dtype == torch.int32 and first.dim() == 1 and tokens.dtype == torch.int32
+    _rows(state, first, tokens, logprob, logits)
     _check(load().rlt_generate(model, state, _ptr(first), n, temperature, seed, step0, _ptr(tokens), _ptr(logprob),
                                _ptr(logits), ctypes.c_void_p(_stream())))
 
@@ -325,6 +347,7 @@ def _host_i32(vals) -> ctypes.Array:
 def rlt_step_rows(model, state, tokens: torch.Tensor, active, logits: torch.Tensor) -> None:
     """One position for the rows with active[b] (host sequence of B flags), each at its own position."""
     assert tokens.dtype == torch.int32 and tokens.dim() == 1 and logits.dtype == torch.float32
+    _rows(state, tokens, logits)
     _check(load().rlt_step_rows(model, state, _ptr(tokens), _host_i32(active), _ptr(logits),
                                 ctypes.c_void_p(_stream())))
 

@@ -110,3 +110,25 @@ def test_replay_grad_workspace_and_host_checks(lib):
     assert ck < 0.5 * full
     # null tokens / workspace: rejected before touching the device
     assert lib.rlt_replay_grad(ctypes.byref(cs), None, 0, None, 0, None, 2, 16, None, None, 0, None, 0, None) == -1
+
+
+def test_binding_rejects_tensors_with_other_row_counts():
+    """A buffer passed with a state must hold the state's rows: the library accesses [rows, ...]
+    through plain pointers, so the binding refuses a shorter (or longer) tensor on the host."""
+    import ctypes
+
+    import torch
+
+    from recurrent_looped_transformer_amd import rlt
+    h = ctypes.c_void_p(0x1000)                    # a registered handle; nothing is called
+    rlt._STATE_ROWS[h.value] = 4
+    try:
+        rlt._rows(h, torch.zeros(4, 7), None, torch.zeros(4))
+        with pytest.raises(ValueError):
+            rlt._rows(h, torch.zeros(3, 1100, dtype=torch.int32))
+        with pytest.raises(ValueError):
+            rlt._rows(h, torch.zeros(4, 7), torch.zeros(5, 7))
+        with pytest.raises(ValueError):
+            rlt.rlt_replay(None, h, torch.zeros(3, 9, dtype=torch.int32), torch.zeros(3, 8))
+    finally:
+        rlt._STATE_ROWS.pop(h.value, None)
