@@ -229,6 +229,9 @@ struct AttnArgs {
                                 // last-level cache holds)
   int memory = 0;               // 1: the decoder's cross-attention over the memory (its own kernel
                                 // instance, so profiles report it apart from the window attention)
+  int wide = 0;                 // 1: a launch with no more blocks than CUs may take blocks of 512
+                                // threads (a row's summation order then depends on the launch size:
+                                // unset in batch-invariant mode)
 };
 void attn_decode(Dt dt, const AttnArgs& a, hipStream_t st);
 // 16-bit many-query attention with MFMA (dh 64 or 128); returns false when the type or shape is

@@ -23,11 +23,14 @@ namespace rlt {
 // X2: two-term query, keys and values (q_lo, kv_lo): each operand is hi + lo in fp32.
 // NT: keys and values read with the nontemporal hint (launches that stream more than the
 // last-level cache holds).
-template <typename T, int DH, bool SPLIT, int MEM, bool X2 = false, bool NT = false>
-__global__ __launch_bounds__(256) void attn_decode_k(AttnArgs a) {
+// NTH: threads per block (256; 512 when a launch leaves at least half the CUs without a block:
+// twice the keys in flight per block — medium-LM decode, t 2048: B 8 2033 -> 1957 us per step,
+// B 1 1575 -> 1548 us; at the paper shape, whose launches fill every CU, no faster).
+template <typename T, int DH, bool SPLIT, int MEM, bool X2 = false, bool NT = false, int NTH = 256>
+__global__ __launch_bounds__(NTH) void attn_decode_k(AttnArgs a) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int G = DH / VEC;              // lanes per key
-  constexpr int NG = 256 / G;              // keys in flight per block per round
+  constexpr int NG = NTH / G;              // keys in flight per block per round
   constexpr int UNR = X2 ? 4 : 8;
   __shared__ float part[NG * DH];
   __shared__ float ml[2 * NG];
@@ -191,6 +194,25 @@ __global__ __launch_bounds__(DH) void attn_combine_k(AttnArgs a, int S) {
   store_act<T>(op, a.out_split, num / den);
 }
 
+template <typename T, int DH, int NTH>
+static void launch_attn_variant(const AttnArgs& a, dim3 grid, int S, bool x2, bool nt, hipStream_t st) {
+  const dim3 blk(NTH);
+  if (S > 1) {
+    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, true, false, NTH>), grid, blk, 0, st, a);
+    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1, false, true, NTH>), grid, blk, 0, st, a);
+    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1, false, false, NTH>), grid, blk, 0, st, a);
+    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, false, true, NTH>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, false, false, NTH>), grid, blk, 0, st, a);
+    hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
+  } else {
+    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, true, false, NTH>), grid, blk, 0, st, a);
+    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1, false, true, NTH>), grid, blk, 0, st, a);
+    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1, false, false, NTH>), grid, blk, 0, st, a);
+    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, false, true, NTH>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, false, false, NTH>), grid, blk, 0, st, a);
+  }
+}
+
 // Key splits: when the launch has at most kSplitMaxBlocks (head, query) blocks and its longest
 // key range is long, every range is cut into pieces of split_keys keys (the same for every row,
 // so a long prefix gets more blocks than a short one), one round of at most 256 blocks in
@@ -216,24 +238,15 @@ static void launch_attn(const AttnArgs& a0, hipStream_t st) {
     S = (a.n_max + a.split_keys - 1) / a.split_keys;
   }
   // the memory attention runs its own instance of the same code (MEM = 1): a separate symbol;
-  // two-term operands (the encoder's, 16-bit types) take the X2 instances
+  // two-term operands (the encoder's, 16-bit types) take the X2 instances. Launches of at most
+  // 128 blocks take blocks of 512 threads when the caller allows it (not in batch-invariant
+  // mode: a row's arithmetic must not depend on the batch)
   const dim3 grid(a.H, a.B * a.nq, S);
   const bool x2 = !__is_same(T, float) && (a.q_lo > 0 || a.kv_lo > 0);
   const bool nt = a.stream != 0 && !x2;
-  if (S > 1) {
-    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, true>), grid, dim3(256), 0, st, a);
-    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1, false, true>), grid, dim3(256), 0, st, a);
-    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 1>), grid, dim3(256), 0, st, a);
-    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0, false, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_k<T, DH, true, 0>), grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((attn_combine_k<T, DH>), dim3(a.H, a.B * a.nq), dim3(DH), 0, st, a, S);
-  } else {
-    if (x2) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, true>), grid, dim3(256), 0, st, a);
-    else if (a.memory && nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1, false, true>), grid, dim3(256), 0, st, a);
-    else if (a.memory) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 1>), grid, dim3(256), 0, st, a);
-    else if (nt) hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0, false, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_k<T, DH, false, 0>), grid, dim3(256), 0, st, a);
-  }
+  const bool wide = DH >= 64 && a.wide && (int64_t)grid.x * grid.y * grid.z <= 128;
+  if (wide) launch_attn_variant<T, DH, 512>(a, grid, S, x2, nt, st);
+  else launch_attn_variant<T, DH, 256>(a, grid, S, x2, nt, st);
 }
 
 template <typename T>
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
   // rows fell on two bank groups: 8-way conflicts)
   const int jq = tid / PARTS, part = tid % PARTS;
   const int jv = tid % 16, pv = tid / 16;
-  // LDS row of key 4 jq (the permuted key order of the two-term kernel below)
+  // LDS row of key 4 jq in the permuted key order described above
   const int krow = 32 * (jq >> 3) + 16 * (jq & 1) + 4 * ((jq >> 1) & 3);
   uint4 rk[4], rv[4];
   // positions past kmax load the row of kmax (valid data: their scores are masked, so they
@@ -499,13 +512,14 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 }
 
 // Two-term operands (q_lo, kv_lo > 0): every query, key and value is hi + lo in the 16-bit
-// type. Scores take three MFMA products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
+// type. (This kernel keeps key rows in natural order and the 16x16x16 weighted sum: the key
+// permutation, 16x16x32 weighted sum and whole-tile path of the one-term kernel cut its
+// MFMA-busy cycles by a third but measured 1.2% slower on the paper-shape encode and no faster
+// on the medium-LM encode; its time is not set by the MFMA count.) Scores take three MFMA products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
 // below the fp32 rounding of the sum), the probabilities are split into hi + lo in registers
-// and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Both terms of a key / value tile
-// sit in LDS (4 stages: buffer x term); at most two query blocks per wave (register budget).
-//
-// Key order, weighted-sum products and softmax as in flash_prefill_k (one 16x16x32 product per
-// 32 keys instead of two 16x16x16: the MFMA-busy counter of this kernel fell by a third).
+// and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Same tiling as above with both
+// terms of a key / value tile in LDS (4 stages: buffer x term); at most two query blocks per
+// wave (register budget).
 template <typename T, int DH, int QB, int NW = 4>
 __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   constexpr int BK = 64, KP = DH / 8 + 1, VP = BK + 4, QW = 16 * QB, QBLK = NW * QW;
@@ -514,8 +528,7 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   __shared__ __align__(16) uint4 sK[2][2][BK][KP];           // [buffer][term]
   __shared__ __align__(16) uint16_t sVt[2][2][DH][VP];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int g = lane >> 4, c = lane & 15;
   const int q0 = qb * QBLK + wave * QW;
   uint4 qh[QB][DH / 32], ql[QB][DH / 32];
@@ -545,45 +558,36 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
     m_run[j] = -INFINITY;
     l_run[j] = 0.f;
   }
-  const float scale2 = a.scale * 1.4426950408889634f;     // scores in base 2
   const int qlast = min(a.nq, (qb + 1) * QBLK);
   const int kmax = a.pos0 + qlast;
   const int kmin = a.window > 0 ? max(1, a.pos0 + 1 + qb * QBLK - a.window + 1) : 1;
-  // the wave's queries: positions pos0 + 1 + q0 .. pos0 + q0 + QW, all valid or not
-  const bool wave_full_q = q0 + QW <= a.nq;
-  const int wq_first = a.pos0 + 1 + q0, wq_last = a.pos0 + q0 + QW;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)b * a.kv_bstride + (int64_t)h * a.cap * DH;
 
   // K and V staged by different thread mappings (see flash_prefill_k): conflict-free V^T writes
   const int jq = tid / PARTS, part = tid % PARTS;
   const int jv = tid % 16, pv = tid / 16;
-  // LDS row of key 4 jq (keys 4 jq .. 4 jq + 3 land on consecutive rows)
-  const int krow = 32 * (jq >> 3) + 16 * (jq & 1) + 4 * ((jq >> 1) & 3);
   uint4 rk[2][4], rv[2][4];                                   // [term][key]
-  // positions past kmax load the row of kmax (valid data: their scores are masked, so they
-  // weigh zero); a ring slot is the tile's first slot (one scalar modulo) plus the key's
-  // offset, wrapped once (the launch guarantees cap >= BK)
-  // (the staging registers are defined on every path: otherwise they are kept in scratch)
   auto gload = [&](int k0) {
-    const int s0 = a.ring ? (k0 - 1) % a.cap : k0 - 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      rk[0][e] = rk[1][e] = rv[0][e] = rv[1][e] = make_uint4(0, 0, 0, 0);
-    }
-    if (tid < LOADERS) {
+      const int p = k0 + 4 * jq + e, q = k0 + 4 * jv + e;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int sp = s0 + min(4 * jq + e, kmax - k0), sq = s0 + min(4 * jv + e, kmax - k0);
-        if (a.ring) {
-          sp = sp >= a.cap ? sp - a.cap : sp;
-          sq = sq >= a.cap ? sq - a.cap : sq;
-        }
-        const int64_t offk = (int64_t)sp * DH + part * 8, offv = (int64_t)sq * DH + pv * 8;
-        rk[0][e] = *reinterpret_cast<const uint4*>(Kb + offk);
-        rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + offk);
-        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + offv);
-        rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + offv);
+      for (int t = 0; t < 2; ++t) {
+        rk[t][e] = make_uint4(0, 0, 0, 0);
+        rv[t][e] = make_uint4(0, 0, 0, 0);
+      }
+      if (tid < LOADERS && p <= kmax) {
+        const int slot = a.ring ? (p - 1) % a.cap : p - 1;
+        const int64_t off = (int64_t)slot * DH + part * 8;
+        rk[0][e] = *reinterpret_cast<const uint4*>(Kb + off);
+        rk[1][e] = *reinterpret_cast<const uint4*>(Kb + a.kv_lo + off);
+      }
+      if (tid < LOADERS && q <= kmax) {
+        const int slot = a.ring ? (q - 1) % a.cap : q - 1;
+        const int64_t off = (int64_t)slot * DH + pv * 8;
+        rv[0][e] = *reinterpret_cast<const uint4*>(Vb + off);
+        rv[1][e] = *reinterpret_cast<const uint4*>(Vb + a.kv_lo + off);
       }
     }
   };
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sK[buf][t][krow + e][part] = rk[t][e];
+        for (int e = 0; e < 4; ++e) sK[buf][t][4 * jq + e][part] = rk[t][e];
         const uint32_t w[4][4] = {{rv[t][0].x, rv[t][0].y, rv[t][0].z, rv[t][0].w},
                                   {rv[t][1].x, rv[t][1].y, rv[t][1].z, rv[t][1].w},
                                   {rv[t][2].x, rv[t][2].y, rv[t][2].z, rv[t][2].w},
@@ -616,12 +620,10 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
   for (int k0 = kmin; k0 <= kmax; k0 += BK) {
     const bool more = k0 + BK <= kmax;
     if (more) gload(k0 + BK);
-    __builtin_amdgcn_sched_barrier(0);   // the next tile's loads stay ahead of this tile's work
-    // every key of the tile visible to every query of the wave
-    const bool whole = wave_full_q && k0 + BK - 1 <= wq_first && (a.window <= 0 || k0 > wq_last - a.window);
-    // all score products first (independent accumulators per sub-tile, no branch between
-    // them), then the mask
-    f32x4 sacc[QB][4];
+    float s[QB][4][4];
+    float tmax[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint4 kh[DH / 32], kl[DH / 32];
@@ -639,69 +641,41 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
           acc = mfma16x16x32<T>(kh[kc], ql[j][kc], acc);
           acc = mfma16x16x32<T>(kh[kc], qh[j][kc], acc);
         }
-        sacc[j][st] = acc;
-      }
-    }
-    float s[QB][4][4];
-    float tmax[QB];
 #pragma unroll
-    for (int j = 0; j < QB; ++j) tmax[j] = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        const f32x4 acc = sacc[j][st];
-        if (whole) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            s[j][st][i] = acc[i] * scale2;
-            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // lane (g, c), sub-tile st: key 32 (st / 2) + 8 g + 4 (st % 2) + i of the tile
-            const int kp = k0 + 32 * (st >> 1) + 8 * g + 4 * (st & 1) + i;
-            const bool ok =
-                qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
-            s[j][st][i] = ok ? acc[i] * scale2 : -INFINITY;
-            tmax[j] = fmaxf(tmax[j], s[j][st][i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int kp = k0 + st * 16 + 4 * g + i;
+          const bool ok = qvalid[j] && kp <= qpos[j] && kp <= kmax && (a.window <= 0 || kp > qpos[j] - a.window);
+          s[j][st][i] = ok ? acc[i] * a.scale : -INFINITY;
+          tmax[j] = fmaxf(tmax[j], s[j][st][i]);
         }
       }
     }
-    uint4 pbh[QB][2], pbl[QB][2];                // [query block][32-key half]: keys 8 g .. 8 g + 7
+    uint2 pbh[QB][4], pbl[QB][4];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float tm = fmaxf(tmax[j], __shfl_xor(tmax[j], 16, WAVE));
       tm = fmaxf(tm, __shfl_xor(tm, 32, WAVE));
       const float m_new = fmaxf(m_run[j], tm);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __builtin_amdgcn_exp2f(m_run[j] - m_use);
+      const float corr = __expf(m_run[j] - m_use);
       l_run[j] *= corr;
 #pragma unroll
       for (int i = 0; i < DH / 16; ++i) o[j][i] *= corr;
       float lsum = 0.f;
-      uint32_t wh[4][2], wl[4][2];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float ph[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(s[j][st][i] - m_use);
+          const float pv = __expf(s[j][st][i] - m_use);
           lsum += pv;
           ph[i] = Elem<T>::round(pv);
           pl[i] = pv - ph[i];
         }
-        wh[st][0] = pack2<T>(ph[0], ph[1]);
-        wh[st][1] = pack2<T>(ph[2], ph[3]);
-        wl[st][0] = pack2<T>(pl[0], pl[1]);
-        wl[st][1] = pack2<T>(pl[2], pl[3]);
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        pbh[j][p] = make_uint4(wh[2 * p][0], wh[2 * p][1], wh[2 * p + 1][0], wh[2 * p + 1][1]);
-        pbl[j][p] = make_uint4(wl[2 * p][0], wl[2 * p][1], wl[2 * p + 1][0], wl[2 * p + 1][1]);
+        pbh[j][st].x = pack2<T>(ph[0], ph[1]);
+        pbh[j][st].y = pack2<T>(ph[2], ph[3]);
+        pbl[j][st].x = pack2<T>(pl[0], pl[1]);
+        pbl[j][st].y = pack2<T>(pl[2], pl[3]);
       }
       lsum += __shfl_xor(lsum, 16, WAVE);
       lsum += __shfl_xor(lsum, 32, WAVE);
@@ -709,21 +683,16 @@ __global__ __launch_bounds__(NW * WAVE) void flash_prefill_x2_k(AttnArgs a) {
       m_run[j] = m_new;
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) {
-        // two 8-byte reads per term (rows of 68 halves: the 16 rows of a read fall on distinct
-        // bank pairs; 16-byte reads of 16-byte aligned rows measured twice the bank conflicts)
-        const uint16_t* r0 = &sVt[buf][0][db * 16 + c][p * 32 + 8 * g];
-        const uint16_t* r1 = &sVt[buf][1][db * 16 + c][p * 32 + 8 * g];
-        const uint2 h0 = *reinterpret_cast<const uint2*>(r0), h1 = *reinterpret_cast<const uint2*>(r0 + 4);
-        const uint2 l0 = *reinterpret_cast<const uint2*>(r1), l1 = *reinterpret_cast<const uint2*>(r1 + 4);
-        const uint4 vh = make_uint4(h0.x, h0.y, h1.x, h1.y), vl = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        const uint2 vh = *reinterpret_cast<const uint2*>(&sVt[buf][0][db * 16 + c][st * 16 + 4 * g]);
+        const uint2 vl = *reinterpret_cast<const uint2*>(&sVt[buf][1][db * 16 + c][st * 16 + 4 * g]);
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-          o[j][db] = mfma16x16x32<T>(vl, pbh[j][p], o[j][db]);
-          o[j][db] = mfma16x16x32<T>(vh, pbl[j][p], o[j][db]);
-          o[j][db] = mfma16x16x32<T>(vh, pbh[j][p], o[j][db]);
+          o[j][db] = mfma16x16x16<T>(vl, pbh[j][st], o[j][db]);
+          o[j][db] = mfma16x16x16<T>(vh, pbl[j][st], o[j][db]);
+          o[j][db] = mfma16x16x16<T>(vh, pbh[j][st], o[j][db]);
         }
       }
     }

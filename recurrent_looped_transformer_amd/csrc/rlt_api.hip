@@ -513,6 +513,7 @@ void do_encode(rlt_model* m, rlt_state* s, const int32_t* tokens, int T, hipStre
       a.tn = T; a.pos0 = t0; a.x_split = A > 1; a.row_pos = rp;
       AttnArgs at;
       at.row_pos = rp;
+      at.wide = !m->batch_invariant;
       if (s->enc_k) {
         const int64_t lo = (int64_t)l * s->B * H * Tm * dh;
         a.kv.k = (char*)s->enc_k + lo * m->esz; a.kv.v = (char*)s->enc_v + lo * m->esz;
@@ -675,6 +676,7 @@ void decoder_pass(rlt_model* m, rlt_state* s, int t0, int np, hipStream_t st, co
     a.kv.k = (char*)sb.ring_k + ro; a.kv.v = (char*)sb.ring_v + ro; a.kv.cap = s->R; a.kv.ring = 1;
     mgemm(m, s, sb.slice, RLT_TIME_DECODER_GEMM, dt, Ep::QKV, a, sb.xa, ad, L.wqkv, rows, 3 * hd, d, st);
     AttnArgs at;
+    at.wide = !m->batch_invariant;
     at.q = sb.q; at.ldq = hd; at.k = a.kv.k; at.v = a.kv.v; at.kv_bstride = (int64_t)H * s->R * dh;
     at.cap = s->R; at.ring = 1; at.out = sb.ao; at.ldo = ahd; at.out_split = shd;
     at.B = B; at.nq = np; at.H = H; at.dh = dh;

@@ -241,7 +241,7 @@ def run_decode(out_dir: str, bench_args):
 
 
 DECODE_KERNELS = "attn_decode_k|gemm_skinny|skinny_reduce"
-MEM_ATTN = re.compile(r"attn_decode_k<[^,]+, \d+, false, 1(, false(, (true|false))?)?>")   # any NT instance
+MEM_ATTN = re.compile(r"attn_decode_k<[^,]+, \d+, false, 1(, false(, (true|false)(, \d+)?)?)?>")   # any NT / block size
 
 
 def summarize_decode(out_dir: str, name: str, bench_args):
