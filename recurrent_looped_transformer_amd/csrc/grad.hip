@@ -912,22 +912,35 @@ __global__ __launch_bounds__(256) void g_attn_fwd(int nq, int B, int tq0, int wi
   q.x *= scale; q.y *= scale; q.z *= scale; q.w *= scale;
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = lo + gi; j <= tq; j += NG) {
-    const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
-    float4 k, v;
-    if (kv_k && j == tq) {   // the row this launch produces (group-uniform branch)
-      k = kt;
-      v = vt;
-    } else {
-      k = ld4(K + ro);
-      v = ld4(Vv + ro);
+  // a group's keys lo + gi, lo + gi + NG, ... in that order, kU of them loaded before any is
+  // used (the loads of a chunk in flight together; the arithmetic order is unchanged)
+  constexpr int kU = 4;
+  for (int j0 = lo + gi; j0 <= tq; j0 += kU * NG) {
+    float4 kk[kU], vv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u * NG;
+      kk[u] = vv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j > tq) continue;
+      if (kv_k && j == tq) {   // the row this launch produces (group-uniform branch)
+        kk[u] = kt;
+        vv[u] = vt;
+      } else {
+        const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
+        kk[u] = ld4(K + ro);
+        vv[u] = ld4(Vv + ro);
+      }
     }
-    const float sc = gsum<G>(dot4(q, k));
-    const float mn = fmaxf(m, sc);
-    const float c = __expf(m - mn), p = __expf(sc - mn);
-    l = l * c + p;
-    acc = fma4(p, v, make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c));
-    m = mn;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (j0 + u * NG > tq) continue;   // group-uniform
+      const float sc = gsum<G>(dot4(q, kk[u]));
+      const float mn = fmaxf(m, sc);
+      const float c = __expf(m - mn), p = __expf(sc - mn);
+      l = l * c + p;
+      acc = fma4(p, vv[u], make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c));
+      m = mn;
+    }
   }
   pacc[tid] = acc;
   if (gl == 0) { pm[gi] = m; pl[gi] = l; }
@@ -997,17 +1010,37 @@ __global__ __launch_bounds__(256) void g_attn_bwd_q(int nq, int B, int tq0, int 
   const float D = gsum<G>(dot4(go, ld4(O + qo)));
   const float L = lse[(int64_t)r * H + h];
   float4 dq = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = lo + gi; j <= tq; j += NG) {
-    const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
-    const float4 k = ld4(K + ro), v = ld4(Vv + ro);
-    const float p = __expf(gsum<G>(dot4(q, k)) - L);
-    const float ds = p * (gsum<G>(dot4(go, v)) - D);
-    dq = fma4(ds, k, dq);
-    if (KV) {
-      float4 nk = fma4(ds, q, ld4(dK + ro));
-      if (rot == 2 && j == tq) nk = rope_inv4<DH>(nk, gl, tq + 1, tab);   // the whole group takes j == tq
-      st4(dK + ro, nk);
-      st4(dV + ro, fma4(p, go, ld4(dV + ro)));
+  // a group's keys in order, kU of them (and their gradient rows) loaded before any is used
+  constexpr int kU = 4;
+  for (int j0 = lo + gi; j0 <= tq; j0 += kU * NG) {
+    float4 kk[kU], vv[kU], gk[kU], gv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u * NG;
+      kk[u] = vv[u] = gk[u] = gv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j > tq) continue;
+      const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
+      kk[u] = ld4(K + ro);
+      vv[u] = ld4(Vv + ro);
+      if (KV) {   // rows of other keys: no other query of this launch touches them
+        gk[u] = ld4(dK + ro);
+        gv[u] = ld4(dV + ro);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u * NG;
+      if (j > tq) continue;   // group-uniform
+      const float p = __expf(gsum<G>(dot4(q, kk[u])) - L);
+      const float ds = p * (gsum<G>(dot4(go, vv[u])) - D);
+      dq = fma4(ds, kk[u], dq);
+      if (KV) {
+        const int64_t ro = ((int64_t)j * B + b) * hd + h * DH + gl * 4;
+        float4 nk = fma4(ds, q, gk[u]);
+        if (rot == 2 && j == tq) nk = rope_inv4<DH>(nk, gl, tq + 1, tab);   // the whole group takes j == tq
+        st4(dK + ro, nk);
+        st4(dV + ro, fma4(p, go, gv[u]));
+      }
     }
   }
   pdq[tid] = dq;
