@@ -515,7 +515,8 @@ __global__ __launch_bounds__(256) void flash_prefill_k(AttnArgs a) {
 // type. (This kernel keeps key rows in natural order and the 16x16x16 weighted sum: the key
 // permutation, 16x16x32 weighted sum and whole-tile path of the one-term kernel cut its
 // MFMA-busy cycles by a third but measured 1.2% slower on the paper-shape encode and no faster
-// on the medium-LM encode; its time is not set by the MFMA count.) Scores take three MFMA products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
+// on the medium-LM encode; its time is not set by the MFMA count.) Scores take three MFMA
+// products (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi; the lo * lo term is
 // below the fp32 rounding of the sum), the probabilities are split into hi + lo in registers
 // and the weighted sum takes V_hi P_hi + V_hi P_lo + V_lo P_hi. Same tiling as above with both
 // terms of a key / value tile in LDS (4 stages: buffer x term); at most two query blocks per
